@@ -1,0 +1,159 @@
+"""CPU oracle (plain C, float64, single-threaded) — TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The HIP product path never calls it and shares
+no code with it; ``oracle.c`` names the passage each function follows and the
+readings taken where the source page is silent.
+
+Functions take a :class:`matrix_free_pcg_amd.workloads.Problem` (inputs only)
+and numpy float64 fields of shape (ny, nz, nx).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_default = None
+
+OK, NOT_CONVERGED, ERR_INVALID, ERR_BREAKDOWN = 0, 1, -1, -2
+
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile an oracle source file with gcc into a shared library."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (always, when force)."""
+    if force or not os.path.exists(_LIB):
+        compile_source(SOURCE, _LIB)
+    return _LIB
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i = ctypes.c_int
+        d = ctypes.c_double
+        lib.orc_apply_A.argtypes = [i, i, i, d, dp, dp, dp, dp]
+        lib.orc_apply_A.restype = None
+        lib.orc_precond.argtypes = [i, i, i, d, dp, dp, dp, dp]
+        lib.orc_precond.restype = i
+        lib.orc_dot.argtypes = [ctypes.c_size_t, dp, dp]
+        lib.orc_dot.restype = d
+        lib.orc_alpha_T.argtypes = [i, i, dp, i, i]
+        lib.orc_alpha_T.restype = d
+        lib.orc_pcg.argtypes = [i, i, i, d, dp, dp, dp, dp, d, i, dp,
+                                ctypes.POINTER(ctypes.c_int), i, dp, dp, dp]
+        lib.orc_pcg.restype = i
+        self.lib = lib
+        self.path = path
+
+    @staticmethod
+    def _field(a, prob) -> np.ndarray:
+        a = np.ascontiguousarray(a, dtype=np.float64)
+        if a.size != prob.n:
+            raise ValueError(f"field has {a.size} entries, grid needs {prob.n}")
+        return a.reshape(prob.ny, prob.nz, prob.nx)
+
+    @staticmethod
+    def _coeffs(prob):
+        az = np.ascontiguousarray(prob.alpha_z_face, dtype=np.float64)
+        if az.shape != (prob.nz + 1,):
+            raise ValueError("alpha_z_face must have nz+1 entries")
+        return az, prob.alpha_h_field()
+
+    def apply_A(self, prob, x) -> np.ndarray:
+        """y = A x (matrix-free 7-point stencil)."""
+        x = self._field(x, prob)
+        az, ah = self._coeffs(prob)
+        y = np.empty_like(x)
+        self.lib.orc_apply_A(prob.nx, prob.ny, prob.nz, prob.delta, _ptr(az), _ptr(ah), _ptr(x), _ptr(y))
+        return y
+
+    def precond(self, prob, r) -> np.ndarray:
+        """z = M^{-1} r (Thomas algorithm, one tridiagonal system per column)."""
+        r = self._field(r, prob)
+        az, ah = self._coeffs(prob)
+        z = np.empty_like(r)
+        st = self.lib.orc_precond(prob.nx, prob.ny, prob.nz, prob.delta, _ptr(az), _ptr(ah), _ptr(r), _ptr(z))
+        if st != OK:
+            raise FloatingPointError("zero pivot in the column solve")
+        return z
+
+    def dot(self, a, b) -> float:
+        a = np.ascontiguousarray(a, dtype=np.float64).ravel()
+        b = np.ascontiguousarray(b, dtype=np.float64).ravel()
+        return self.lib.orc_dot(a.size, _ptr(a), _ptr(b))
+
+    def alpha_T(self, prob, i: int, j: int) -> float:
+        ah = prob.alpha_h_field()
+        return self.lib.orc_alpha_T(prob.nx, prob.ny, _ptr(ah), i, j)
+
+    def pcg(self, prob, b, x0=None, tol: float = 1e-10, maxit: int = 500, ntrace: int = 0):
+        """Textbook PCG.  Returns dict(x, iters, hist, status[, trace_r, trace_z, trace_p])."""
+        b = self._field(b, prob)
+        x = np.zeros_like(b) if x0 is None else self._field(x0, prob).copy()
+        az, ah = self._coeffs(prob)
+        hist = np.zeros(max(1, maxit + 1))
+        iters = ctypes.c_int(0)
+        ntr = max(0, min(ntrace, maxit + 1))
+        tr = [np.zeros((ntr,) + b.shape) for _ in range(3)] if ntr > 0 else [np.zeros(1)] * 3
+        st = self.lib.orc_pcg(prob.nx, prob.ny, prob.nz, prob.delta, _ptr(az), _ptr(ah), _ptr(b),
+                              _ptr(x), float(tol), int(maxit), _ptr(hist), ctypes.byref(iters), ntr,
+                              _ptr(tr[0]), _ptr(tr[1]), _ptr(tr[2]))
+        out = dict(x=x, iters=iters.value, hist=hist[: iters.value + 1].copy(), status=st)
+        if ntr > 0:
+            out.update(trace_r=tr[0], trace_z=tr[1], trace_p=tr[2])
+        return out
+
+
+def default() -> Oracle:
+    """The oracle built from oracle.c (rebuilt when the source is newer)."""
+    global _default
+    with _lock:
+        if _default is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(SOURCE):
+                build(force=True)
+            _default = Oracle(_LIB)
+        return _default
+
+
+def apply_A(prob, x):
+    return default().apply_A(prob, x)
+
+
+def precond(prob, r):
+    return default().precond(prob, r)
+
+
+def dot(a, b):
+    return default().dot(a, b)
+
+
+def alpha_T(prob, i, j):
+    return default().alpha_T(prob, i, j)
+
+
+def pcg(prob, b, x0=None, tol=1e-10, maxit=500, ntrace=0):
+    return default().pcg(prob, b, x0, tol, maxit, ntrace)

@@ -1,0 +1,241 @@
+/*
+ * CPU oracle for the matrix-free PCG solve of the anisotropic
+ * pressure-correction equation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header or table with the HIP
+ * library.
+ *
+ * Source: E. Mueller, X. Guo, R. Scheichl, S. Shi, "Matrix-free GPU
+ * implementation of a preconditioned conjugate gradient solver for
+ * anisotropic elliptic PDEs" (2013).  Each function names the passage it
+ * follows.  Deliberately plain: single thread, float64, no blocking, no
+ * fusion, compiled with -O2 -ffp-contract=off.
+ *
+ * Readings taken where the page is silent or garbled (each is also listed in
+ * the design notes):
+ *  - operator signs: the symmetric positive definite 7-point operator
+ *      (A u) = delta*u + sum over the 6 faces of coeff_face*(u - u_neighbour)
+ *    (section 3 eqs. (5)-(8) and eq. (18) with |T|=d_k=1, a'_k=delta and the
+ *    off-diagonal couplings negative);
+ *  - boundaries: periodic in i and j; zero-flux faces at the bottom and the
+ *    top of every column (face 0 and face nz carry no coupling);
+ *  - a horizontal face coefficient is the arithmetic mean of the two cells'
+ *    alpha_h values, so A is symmetric;
+ *  - the preconditioner M keeps A's column blocks A_T (tridiagonal, with the
+ *    full horizontal diagonal alpha_T on its diagonal) and drops only the
+ *    couplings between columns (section 4.2, before eq. (19));
+ *  - PCG is the textbook loop (section 4.1); it stops after the first CG step
+ *    with ||r_k||/||r_0|| < tol (strict) or r_k == 0 (section 4.3, Algorithm 1
+ *    with tau disabled); a step count is a count of x-updates;
+ *  - dot products use Neumaier-compensated sequential summation in memory
+ *    order.
+ *
+ * Field layout: l = i + nx*(k + nz*j) (section 6.1, eq. (22)); the horizontal
+ * coefficient field is indexed [j*nx + i].  The algorithm is indifferent to
+ * the order; this order is used so that no conversion is needed.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_NOT_CONVERGED 1
+#define ORC_ERR_INVALID (-1)
+#define ORC_ERR_BREAKDOWN (-2)
+
+static size_t at(int nx, int nz, int i, int j, int k)
+{
+    return (size_t)i + (size_t)nx * ((size_t)k + (size_t)nz * (size_t)j);
+}
+
+/* Horizontal face coefficients of cell (i,j): mean of the two cells sharing
+ * the face (section 3, eqs. (6)-(7): alpha_{T,T'} is one symmetric value per
+ * edge; here its value is the mean of the two cells' alpha_h). */
+static double face_xp(int nx, const double *ah, int i, int j)
+{
+    int ip = (i + 1) % nx;
+    return 0.5 * (ah[(size_t)j * nx + i] + ah[(size_t)j * nx + ip]);
+}
+static double face_xm(int nx, const double *ah, int i, int j)
+{
+    int im = (i + nx - 1) % nx;
+    return 0.5 * (ah[(size_t)j * nx + i] + ah[(size_t)j * nx + im]);
+}
+static double face_yp(int nx, int ny, const double *ah, int i, int j)
+{
+    int jp = (j + 1) % ny;
+    return 0.5 * (ah[(size_t)j * nx + i] + ah[(size_t)jp * nx + i]);
+}
+static double face_ym(int nx, int ny, const double *ah, int i, int j)
+{
+    int jm = (j + ny - 1) % ny;
+    return 0.5 * (ah[(size_t)j * nx + i] + ah[(size_t)jm * nx + i]);
+}
+
+/* alpha_T: sum of the horizontal couplings of one column (section 3, eq. (7)). */
+double orc_alpha_T(int nx, int ny, const double *ah, int i, int j)
+{
+    return face_xp(nx, ah, i, j) + face_xm(nx, ah, i, j)
+         + face_yp(nx, ny, ah, i, j) + face_ym(nx, ny, ah, i, j);
+}
+
+/* y = A x: the matrix-free 7-point stencil, recomputing every coefficient
+ * (section 4.2, eq. (18), read with the signs above). */
+void orc_apply_A(int nx, int ny, int nz, double delta, const double *az,
+                 const double *ah, const double *x, double *y)
+{
+    for (int j = 0; j < ny; ++j)
+        for (int k = 0; k < nz; ++k)
+            for (int i = 0; i < nx; ++i) {
+                int ip = (i + 1) % nx, im = (i + nx - 1) % nx;
+                int jp = (j + 1) % ny, jm = (j + ny - 1) % ny;
+                double u = x[at(nx, nz, i, j, k)];
+                double acc = delta * u;
+                acc += face_xp(nx, ah, i, j) * (u - x[at(nx, nz, ip, j, k)]);
+                acc += face_xm(nx, ah, i, j) * (u - x[at(nx, nz, im, j, k)]);
+                acc += face_yp(nx, ny, ah, i, j) * (u - x[at(nx, nz, i, jp, k)]);
+                acc += face_ym(nx, ny, ah, i, j) * (u - x[at(nx, nz, i, jm, k)]);
+                if (k < nz - 1)
+                    acc += az[k + 1] * (u - x[at(nx, nz, i, j, k + 1)]);
+                if (k > 0)
+                    acc += az[k] * (u - x[at(nx, nz, i, j, k - 1)]);
+                y[at(nx, nz, i, j, k)] = acc;
+            }
+}
+
+/* z = M^{-1} r with M = blockdiag over columns of A_T (section 4.2, eq. (19)):
+ * one independent tridiagonal solve per column by the Thomas algorithm
+ * (forward elimination with an auxiliary vector, then back substitution, as
+ * in the cited Numerical Recipes routine).  No pivoting: every column matrix
+ * is strictly diagonally dominant when delta > 0.  Returns ORC_ERR_BREAKDOWN
+ * if a pivot is zero. */
+int orc_precond(int nx, int ny, int nz, double delta, const double *az,
+                const double *ah, const double *r, double *z)
+{
+    double *gam = (double *)malloc(sizeof(double) * (size_t)(nz > 0 ? nz : 1));
+    if (!gam)
+        return ORC_ERR_INVALID;
+    int status = ORC_OK;
+    for (int j = 0; j < ny; ++j)
+        for (int i = 0; i < nx; ++i) {
+            double aT = orc_alpha_T(nx, ny, ah, i, j);
+            /* row k: sub*z[k-1] + diag*z[k] + sup*z[k+1] = r[k] */
+            double diag0 = delta + aT + (nz > 1 ? az[1] : 0.0);
+            double bet = diag0;
+            if (bet == 0.0) { status = ORC_ERR_BREAKDOWN; }
+            z[at(nx, nz, i, j, 0)] = r[at(nx, nz, i, j, 0)] / bet;
+            for (int k = 1; k < nz; ++k) {
+                double sub = -az[k];
+                double sup_prev = -az[k];           /* super-diagonal of row k-1 */
+                double up = (k < nz - 1) ? az[k + 1] : 0.0;
+                double diag = delta + aT + az[k] + up;
+                gam[k] = sup_prev / bet;
+                bet = diag - sub * gam[k];
+                if (bet == 0.0) { status = ORC_ERR_BREAKDOWN; }
+                z[at(nx, nz, i, j, k)] =
+                    (r[at(nx, nz, i, j, k)] - sub * z[at(nx, nz, i, j, k - 1)]) / bet;
+            }
+            for (int k = nz - 2; k >= 0; --k)
+                z[at(nx, nz, i, j, k)] -= gam[k + 1] * z[at(nx, nz, i, j, k + 1)];
+        }
+    free(gam);
+    return status;
+}
+
+/* Neumaier-compensated dot product in memory order. */
+double orc_dot(size_t n, const double *a, const double *b)
+{
+    double s = 0.0, c = 0.0;
+    for (size_t l = 0; l < n; ++l) {
+        double t = a[l] * b[l];
+        double u = s + t;
+        if (fabs(s) >= fabs(t))
+            c += (s - u) + t;
+        else
+            c += (t - u) + s;
+        s = u;
+    }
+    return s + c;
+}
+
+/* Preconditioned conjugate gradients, textbook form (section 4.1: Krylov
+ * space of r_0, A-orthogonal search directions, left preconditioning with M).
+ * Same iterates, in exact arithmetic, as the interleaved loop of section 4.3
+ * (Algorithm 1), which only reorders the same updates into two grid passes.
+ *
+ *   x      in: x0, out: last iterate
+ *   hist   out: ||r_k||_2 for k = 0..iters (length >= maxit+1)
+ *   trace  optional (may be NULL): the first ntrace iterates of r, z and p are
+ *          copied to trace_r/z/p[t*n ...] (t = 0..ntrace-1) for invariant checks
+ * Returns ORC_OK, ORC_NOT_CONVERGED or ORC_ERR_BREAKDOWN.
+ */
+int orc_pcg(int nx, int ny, int nz, double delta, const double *az, const double *ah,
+            const double *b, double *x, double tol, int maxit,
+            double *hist, int *iters_out,
+            int ntrace, double *trace_r, double *trace_z, double *trace_p)
+{
+    size_t n = (size_t)nx * ny * nz;
+    double *r = (double *)malloc(sizeof(double) * n);
+    double *z = (double *)malloc(sizeof(double) * n);
+    double *p = (double *)malloc(sizeof(double) * n);
+    double *q = (double *)malloc(sizeof(double) * n);
+    int status = ORC_NOT_CONVERGED;
+    int it = 0;
+    if (!r || !z || !p || !q) {
+        status = ORC_ERR_INVALID;
+        goto done;
+    }
+    /* r0 = b - A x0 */
+    orc_apply_A(nx, ny, nz, delta, az, ah, x, q);
+    for (size_t l = 0; l < n; ++l)
+        r[l] = b[l] - q[l];
+    double R0 = sqrt(orc_dot(n, r, r));
+    hist[0] = R0;
+    if (!isfinite(R0)) { status = ORC_ERR_BREAKDOWN; goto done; }
+    if (R0 == 0.0) { status = ORC_OK; goto done; }
+
+    if (orc_precond(nx, ny, nz, delta, az, ah, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+    memcpy(p, z, sizeof(double) * n);
+    double rho = orc_dot(n, r, z);
+    if (!(rho > 0.0) || !isfinite(rho)) { status = ORC_ERR_BREAKDOWN; goto done; }
+    if (ntrace > 0) {
+        memcpy(trace_r, r, sizeof(double) * n);
+        memcpy(trace_z, z, sizeof(double) * n);
+        memcpy(trace_p, p, sizeof(double) * n);
+    }
+
+    for (int k = 1; k <= maxit; ++k) {
+        orc_apply_A(nx, ny, nz, delta, az, ah, p, q);
+        double sigma = orc_dot(n, p, q);
+        if (!(sigma > 0.0) || !isfinite(sigma)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double alpha = rho / sigma;
+        for (size_t l = 0; l < n; ++l) x[l] += alpha * p[l];
+        for (size_t l = 0; l < n; ++l) r[l] -= alpha * q[l];
+        double R = sqrt(orc_dot(n, r, r));
+        hist[k] = R;
+        it = k;
+        if (!isfinite(R)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        if (R == 0.0 || R / R0 < tol) { status = ORC_OK; goto done; }
+        if (k == maxit) break;
+        if (orc_precond(nx, ny, nz, delta, az, ah, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double rho_new = orc_dot(n, r, z);
+        if (!(rho_new > 0.0) || !isfinite(rho_new)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double beta = rho_new / rho;
+        rho = rho_new;
+        for (size_t l = 0; l < n; ++l) p[l] = z[l] + beta * p[l];
+        if (k < ntrace) {
+            memcpy(trace_r + (size_t)k * n, r, sizeof(double) * n);
+            memcpy(trace_z + (size_t)k * n, z, sizeof(double) * n);
+            memcpy(trace_p + (size_t)k * n, p, sizeof(double) * n);
+        }
+    }
+    status = ORC_NOT_CONVERGED;
+done:
+    if (iters_out) *iters_out = it;
+    free(r); free(z); free(p); free(q);
+    return status;
+}

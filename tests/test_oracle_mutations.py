@@ -1,0 +1,60 @@
+"""Planted mistakes in copies of the CPU oracle must each fail a pin.
+
+Every mutation below is a plausible slip (a dropped term, a wrong sign or
+index, a wrong face value, a wrong scalar in the Krylov step).  The copy is
+compiled on the CPU with the same flags as the oracle and the full pin set
+of oracle_pins.py is run against it; the test passes only if some pin fails.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+MUTATIONS = {
+    "stencil_drop_ym": ("acc += face_ym(nx, ny, ah, i, j) * (u - x[at(nx, nz, i, jm, k)]);", ""),
+    "stencil_vertical_sign": ("acc += az[k + 1] * (u - x[at(nx, nz, i, j, k + 1)]);",
+                              "acc -= az[k + 1] * (u - x[at(nx, nz, i, j, k + 1)]);"),
+    "stencil_no_wrap": ("int ip = (i + 1) % nx, im = (i + nx - 1) % nx;",
+                        "int ip = (i + 1 < nx) ? i + 1 : i, im = (i + nx - 1) % nx;"),
+    "stencil_face_index": ("acc += az[k + 1] * (u - x[at(nx, nz, i, j, k + 1)]);",
+                           "acc += az[k] * (u - x[at(nx, nz, i, j, k + 1)]);"),
+    "face_not_mean": ("return 0.5 * (ah[(size_t)j * nx + i] + ah[(size_t)j * nx + ip]);",
+                      "(void)ip; return ah[(size_t)j * nx + i];"),
+    "precond_drop_alphaT": ("double aT = orc_alpha_T(nx, ny, ah, i, j);", "double aT = 0.0;"),
+    "precond_back_sign": ("z[at(nx, nz, i, j, k)] -= gam[k + 1] * z[at(nx, nz, i, j, k + 1)];",
+                          "z[at(nx, nz, i, j, k)] += gam[k + 1] * z[at(nx, nz, i, j, k + 1)];"),
+    "precond_upper_face": ("double up = (k < nz - 1) ? az[k + 1] : 0.0;",
+                           "double up = (k < nz - 1) ? az[k] : 0.0;"),
+    "pcg_beta_inverted": ("double beta = rho_new / rho;", "double beta = rho / rho_new;"),
+    "pcg_alpha_wrong_dot": ("double alpha = rho / sigma;", "double alpha = rho / orc_dot(n, q, q);"),
+    "pcg_x_sign": ("for (size_t l = 0; l < n; ++l) x[l] += alpha * p[l];",
+                   "for (size_t l = 0; l < n; ++l) x[l] -= alpha * p[l];"),
+    "pcg_r_uses_p": ("for (size_t l = 0; l < n; ++l) r[l] -= alpha * q[l];",
+                     "for (size_t l = 0; l < n; ++l) r[l] -= alpha * p[l];"),
+    "pcg_extra_step": ("for (int k = 1; k <= maxit; ++k) {", "for (int k = 1; k <= maxit + 1; ++k) {"),
+    "pcg_p_no_beta": ("for (size_t l = 0; l < n; ++l) p[l] = z[l] + beta * p[l];",
+                      "for (size_t l = 0; l < n; ++l) p[l] = z[l];"),
+    "pcg_residual_sign": ("r[l] = b[l] - q[l];", "r[l] = b[l] + q[l];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old}"
+    mutated = src.replace(old, new, 1)
+    path = os.path.join(tmp_path, "mut.c")
+    with open(path, "w") as f:
+        f.write(mutated)
+    lib = oracle.compile_source(path, os.path.join(tmp_path, "libmut.so"))
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, FloatingPointError, ValueError, Exception) as e:  # noqa: B014
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutation {name}"
