@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Throughput benchmark: PCG iterations/s and achieved HBM bandwidth on one MI355X.
+
+One step = one complete solve of the 1024x1024x128 float64 workload (graded
+alpha_z, horizontally varying alpha_h, seeded uniform right-hand side) to
+||r||/||r0|| < 1e-10 from x0 = 0: coefficient set-up already done at handle
+creation, then initial residual, the interleaved PCG iterations and the final
+x update.  Inputs are resident in device memory before the timed region.
+
+Prints one JSON line (see the "roofline" and "cpu_baseline" objects).
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+Options for profiling helpers:
+  --copy-calibration   run only a plain 1 GiB device copy (counter calibration)
+  --no-cpu-baseline    skip timing the CPU oracle
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+METRIC = "PCG iterations/s + achieved HBM GB/s (% roofline), fp64 1024×1024×128"
+
+# Algorithmic bytes per grid point of each pass (float64 = 8 B; each vector
+# read or written once per pass; stencil halos and coefficients not counted).
+BYTES_PER_POINT = {
+    "fused_prec": 32,   # read r, q; write r, z
+    "fused_spmv": 56,   # read x, p, q, z; write x, p, q
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4])
+    ap.add_argument("--variant", default="interleaved", choices=["interleaved", "standard"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of exactly 1 GiB (read 1 GiB, write 1 GiB),
+    for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 27
+    a = torch.ones(n, dtype=torch.float64, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    reps = 20
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t) / reps
+    print(json.dumps({"copy_bytes_read": n * 8, "copy_bytes_written": n * 8,
+                      "copy_ms": dt * 1e3, "copy_GBps": 2 * n * 8 / dt / 1e9}), flush=True)
+
+
+def cpu_baseline(w, steps):
+    """The CPU oracle (single thread) on a bounded sample of the same workload:
+    `steps` CG steps of the full problem, timed around the oracle's step loop
+    (its set-up pass r0 = b - A x0, z0 = M^-1 r0 is not counted)."""
+    import oracle
+    t0 = time.perf_counter()
+    res = oracle.pcg(w.problem, w.rhs, tol=0.0, maxit=steps)
+    total = time.perf_counter() - t0
+    per = res["loop_seconds"] / max(1, res["iters"])
+    return {"value": round(1.0 / per, 4), "unit": "iterations/s", "cores": 1, "kind": "oracle",
+            "sample": f"{res['iters']} CG steps of the {w.name} workload (single-threaded C, "
+                      f"-O2), timed around the step loop; {total:.1f} s of CPU time in all",
+            "s_per_iteration": round(per, 3)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the multi-GPU path is a design, not a build", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import matrix_free_pcg_amd as mf
+    from matrix_free_pcg_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = time.perf_counter()
+    w = W.make_workload(args.config)
+    prob = w.problem
+    if w.rhs is None:
+        raise SystemExit("bench supports workloads with a stored right-hand side")
+    log(f"[bench] {w.name}: inputs generated in {time.perf_counter() - t:.1f}s")
+    n = prob.n
+    b = torch.from_numpy(w.rhs).to(dev)
+    x = torch.zeros_like(b)
+    stream = torch.cuda.current_stream()
+    h = mf.pcg_create(prob, stream)
+    ws = torch.empty(mf.pcg_solve_workspace_bytes(h, w.maxit), dtype=torch.uint8, device=dev)
+    solve = mf.pcg_solve if args.variant == "interleaved" else mf.pcg_solve_standard
+    torch.cuda.synchronize()
+
+    for s in range(args.warmup):
+        x.zero_()
+        res = solve(h, b, x, w.tol, w.maxit, ws)
+        log(f"[bench] warmup {s}: iters={res['iters']} status={res['status']}")
+
+    mf.pcg_profile_reset(h)
+    mf.pcg_profile_enable(h, True)
+    iters = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        x.zero_()
+        res = solve(h, b, x, w.tol, w.maxit, ws)
+        iters.append(res["iters"])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    mf.pcg_profile_enable(h, False)
+    total_iters = int(sum(iters))
+    log(f"[bench] timed: {args.steps} solves, {total_iters} iterations in {elapsed:.3f}s")
+
+    kern = {}
+    names = {"fused_prec": mf.PCG_KID_FUSED_PREC, "fused_spmv": mf.PCG_KID_FUSED_SPMV,
+             "apply_A": mf.PCG_KID_APPLY_A, "precond": mf.PCG_KID_PRECOND, "vector": mf.PCG_KID_VECTOR}
+    for name, kid in names.items():
+        ms, cnt = mf.pcg_profile_read(h, kid)
+        if cnt:
+            avg = ms / cnt
+            ent = {"launches": cnt, "avg_ms": avg, "total_ms": ms}
+            if name in BYTES_PER_POINT:
+                ent["bytes_per_launch"] = BYTES_PER_POINT[name] * n
+                ent["GBps"] = BYTES_PER_POINT[name] * n / (avg * 1e-3) / 1e9
+            kern[name] = ent
+
+    # true residual of the last solve, with the library's own stencil
+    r = torch.empty_like(b)
+    mf.pcg_apply_A(h, x, r)
+    torch.cuda.synchronize()
+    true_rel = float(torch.linalg.vector_norm(b - r) / torch.linalg.vector_norm(b))
+    mf.pcg_destroy(h)
+
+    per_iter_bytes = sum(BYTES_PER_POINT.values()) * n
+    it_s = total_iters / elapsed
+    dom = max((k for k in kern if k in BYTES_PER_POINT), key=lambda k: kern[k]["total_ms"], default=None)
+    roofline = None
+    if dom is not None:
+        ach = kern[dom]["GBps"]
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                    "bytes_per_launch": kern[dom]["bytes_per_launch"],
+                    "avg_launch_ms": round(kern[dom]["avg_ms"], 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(it_s, 2),
+        "unit": "iterations/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": w.name, "nx": prob.nx, "ny": prob.ny, "nz": prob.nz,
+                   "tol": w.tol, "variant": args.variant,
+                   "iterations_per_solve": iters, "status": res["status"],
+                   "final_rel_res": res["final_rel_res"], "true_rel_res": true_rel},
+        "hbm_GBps_per_iteration": round(per_iter_bytes * it_s / 1e9, 1),
+        "hbm_frac_per_iteration": round(per_iter_bytes * it_s / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes_per_point_per_iteration": sum(BYTES_PER_POINT.values()),
+        "kernels": kern,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        t = time.perf_counter()
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
+        log(f"[bench] cpu baseline in {time.perf_counter() - t:.1f}s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * mfpcg.h - C ABI of the matrix-free preconditioned conjugate gradient
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The library solves A x = b for the 3-D anisotropic elliptic
+ * pressure-correction operator of E. Mueller, X. Guo, R. Scheichl, S. Shi,
+ * "Matrix-free GPU implementation of a preconditioned conjugate gradient
+ * solver for anisotropic elliptic PDEs" (2013), on a flat nx*ny*nz grid:
+ *
+ *   (A u)_ijk = delta*u_ijk
+ *             + sum over the 4 horizontal faces of c_face*(u_ijk - u_nb)
+ *             + alpha_z[k+1]*(u_ijk - u_i,j,k+1) + alpha_z[k]*(u_ijk - u_i,j,k-1)
+ *
+ * (section 3, eqs. (5)-(8), and the stencil of section 4.2, eq. (18), with
+ * |T| = d_k = 1), periodic in i and j, zero-flux at the bottom and top of
+ * each column.  A horizontal face coefficient is the mean of the alpha_h
+ * values of the two cells it separates.  The preconditioner M keeps the
+ * column blocks A_T of A (tridiagonal, eq. (8)) and drops the couplings
+ * between columns (section 4.2, eq. (19)); it is inverted column by column
+ * with the Thomas algorithm.
+ *
+ * Field layout (all device vectors): float64, linear index
+ *   l = i + nx*(k + nz*j)
+ * i.e. the first horizontal index runs fastest (section 6.1, eq. (22)); a
+ * torch tensor of shape [ny, nz, nx].
+ *
+ * Memory: every pointer named *_dev is device memory on the device that was
+ * current when the handle was created; *_host pointers are host memory.  The
+ * caller owns all vectors and the solve workspace.  The handle owns only
+ * small coefficient tables: O(nz + (1 + ceil(nz/L)) * nx*ny) doubles,
+ * allocated at pcg_create and freed at pcg_destroy.
+ *
+ * Streams: every call is ordered on the handle's HIP stream (the one passed
+ * to pcg_create, or pcg_set_stream).  pcg_apply_A and pcg_precond are
+ * asynchronous; the solves block the calling thread until the result is
+ * known.
+ *
+ * Errors: functions return PCG_OK (0), PCG_NOT_CONVERGED (+1, solves only),
+ * or a negative code; pcg_last_error() then describes the failure.  Invalid
+ * arguments are detected on the host before any work is queued.
+ *
+ * Thread safety: one handle must not be used from two threads at once.
+ */
+#ifndef MFPCG_H
+#define MFPCG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PCG_OK 0
+#define PCG_NOT_CONVERGED 1
+#define PCG_ERR_INVALID (-1)     /* bad argument, grid or coefficients       */
+#define PCG_ERR_BREAKDOWN (-2)   /* sigma <= 0, kappa <= 0 or a non-finite scalar */
+#define PCG_ERR_HIP (-3)         /* HIP runtime error (see pcg_last_error)   */
+#define PCG_ERR_UNSUPPORTED (-4) /* grid outside the supported range          */
+
+#define PCG_AH_CONST 0 /* alpha_h(i,j) = alpha_h_const                          */
+#define PCG_AH_FIELD 1 /* alpha_h(i,j) = alpha_h_field[j*nx + i] (host array)   */
+
+typedef struct pcg_handle pcg_handle;
+
+/* Grid: nx, ny >= 1 (periodic), 1 <= nz <= 512. */
+typedef struct {
+    int32_t nx, ny, nz;
+} pcg_grid;
+
+/* Operator coefficients (section 3, eqs. (5)-(8); section 4.2, eq. (17)).
+ *   delta         zero-order term, > 0
+ *   alpha_z_face  HOST, nz+1 entries; face f lies between cells f-1 and f;
+ *                 every entry >= 0 and faces 0 and nz must be 0 (no flux)
+ *   alpha_h_kind  PCG_AH_CONST or PCG_AH_FIELD
+ *   alpha_h_const used when kind == PCG_AH_CONST, >= 0
+ *   alpha_h_field HOST, ny*nx entries [j*nx + i], each >= 0, when kind ==
+ *                 PCG_AH_FIELD
+ * All values are copied at pcg_create; the caller may free them after. */
+typedef struct {
+    double delta;
+    const double *alpha_z_face;
+    int32_t alpha_h_kind;
+    double alpha_h_const;
+    const double *alpha_h_field;
+} pcg_coeffs;
+
+/* Create a handle for one grid and operator (section 6: the coefficient
+ * vectors are copied to the device once).  hip_stream: a hipStream_t, or
+ * NULL for the null stream.  Returns PCG_ERR_INVALID for bad arguments,
+ * PCG_ERR_UNSUPPORTED for nz > 512, PCG_ERR_HIP if a table allocation fails.
+ * *out is NULL on failure. */
+int pcg_create(const pcg_grid *grid, const pcg_coeffs *coeffs, void *hip_stream,
+               pcg_handle **out);
+
+/* Release the handle and its tables (waits for its stream).  NULL is a no-op. */
+int pcg_destroy(pcg_handle *h);
+
+/* Change the stream later calls are ordered on. */
+int pcg_set_stream(pcg_handle *h, void *hip_stream);
+
+/* y = A x, the matrix-free stencil that recomputes its coefficients in every
+ * cell (section 4.2, eq. (18)).  x_dev, y_dev: N = nx*ny*nz doubles each,
+ * must not overlap.  Asynchronous. */
+int pcg_apply_A(pcg_handle *h, const double *x_dev, double *y_dev);
+
+/* z = M^{-1} r, one tridiagonal (Thomas) solve per vertical column
+ * (section 4.2, eq. (19)).  r_dev, z_dev: N doubles each, must not overlap.
+ * Asynchronous. */
+int pcg_precond(pcg_handle *h, const double *r_dev, double *z_dev);
+
+/* Bytes of device workspace a solve with this maxit needs (four N-vectors,
+ * per-workgroup partial sums, the scalar state and the residual history). */
+size_t pcg_solve_workspace_bytes(const pcg_handle *h, int32_t maxit);
+
+/* Solve A x = b by PCG with the interleaved loop of section 4.3
+ * (Algorithm 1): per iteration one fused preconditioner pass (Appendix A,
+ * Algorithm 3: r -= alpha q, z = M^{-1} r, <r,r>, <r,z>) and one fused
+ * stencil pass (Algorithm 2: x += alpha p, p = z + beta p, q = A z + beta q,
+ * <p,q>), each followed by a deterministic reduction.
+ *   b_dev          right-hand side, N doubles
+ *   x_dev          in: initial guess x0; out: the last iterate.  Must not
+ *                  alias b_dev or the workspace.
+ *   tol            stop after the first step with ||r_k||/||r_0|| < tol
+ *                  (2-norms of the unpreconditioned residual) or r_k = 0;
+ *                  tol <= 0 runs exactly maxit steps
+ *   maxit          >= 0, maximum number of CG steps (x updates)
+ *   workspace_dev  >= pcg_solve_workspace_bytes(h, maxit) bytes, 256-byte
+ *                  aligned; contents on entry are ignored
+ *   iters_out      (may be NULL) number of CG steps taken
+ *   hist_host      (may be NULL) ||r_k||_2 for k = 0..iters; needs maxit+1
+ *                  entries
+ *   hist_len_out   (may be NULL) iters + 1 (entries written)
+ *   final_rel_res  (may be NULL) hist[iters]/hist[0] (0 when r_0 = 0)
+ * Returns PCG_OK, PCG_NOT_CONVERGED (maxit reached; x is the last iterate),
+ * PCG_ERR_BREAKDOWN (x holds the iterate before the failing step),
+ * PCG_ERR_INVALID or PCG_ERR_HIP.  Blocks until done. */
+int pcg_solve(pcg_handle *h, const double *b_dev, double *x_dev, double tol, int32_t maxit,
+              void *workspace_dev, size_t workspace_bytes, int32_t *iters_out,
+              double *hist_host, int32_t *hist_len_out, double *final_rel_res);
+
+/* Same contract as pcg_solve, computed by the standard (non-interleaved)
+ * PCG of section 4.1: separate stencil, preconditioner and vector-update
+ * passes, each vector update fused with its dot product (section 6: the
+ * stand-alone kernels plus level-1 BLAS operations). */
+int pcg_solve_standard(pcg_handle *h, const double *b_dev, double *x_dev, double tol,
+                       int32_t maxit, void *workspace_dev, size_t workspace_bytes,
+                       int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
+                       double *final_rel_res);
+
+/* Per-kernel timing with HIP events on the handle's stream (off by default).
+ * While enabled, every launch of the kernels below is bracketed by events;
+ * pcg_profile_read returns the accumulated milliseconds and launch count of
+ * one kernel id since the last pcg_profile_reset. */
+#define PCG_KID_FUSED_PREC 0   /* interleaved preconditioner pass          */
+#define PCG_KID_FUSED_SPMV 1   /* interleaved stencil pass                 */
+#define PCG_KID_APPLY_A 2      /* stand-alone y = A x (and standard q = A p) */
+#define PCG_KID_PRECOND 3      /* stand-alone z = M^{-1} r (and standard)    */
+#define PCG_KID_VECTOR 4       /* standard-PCG vector updates               */
+#define PCG_KID_COUNT 5
+int pcg_profile_enable(pcg_handle *h, int32_t enable);
+int pcg_profile_reset(pcg_handle *h);
+int pcg_profile_read(const pcg_handle *h, int32_t kernel_id, double *ms_total,
+                     int64_t *launches);
+
+/* Human-readable description of the last error on this handle (or of the
+ * last failed pcg_create when h is NULL).  Never NULL. */
+const char *pcg_last_error(const pcg_handle *h);
+
+/* Library version string. */
+const char *pcg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MFPCG_H */

@@ -1,0 +1,21 @@
+"""Matrix-free PCG for the anisotropic pressure-correction equation on AMD MI355X.
+
+The solver lives in a HIP shared library with a C ABI (include/mfpcg.h); the
+functions exported here are its ctypes binding (same names) plus the seeded
+synthetic workloads.  Importing this package does not load the library; the
+first call does, and raises if it has not been built.
+"""
+from . import workloads  # noqa: F401
+from ._abi import (PCG_ERR_BREAKDOWN, PCG_ERR_HIP, PCG_ERR_INVALID, PCG_ERR_UNSUPPORTED,  # noqa: F401
+                   PCG_KID_APPLY_A, PCG_KID_FUSED_PREC, PCG_KID_FUSED_SPMV, PCG_KID_PRECOND,
+                   PCG_KID_VECTOR, PCG_NOT_CONVERGED, PCG_OK, Handle, PcgError, pcg_apply_A,
+                   pcg_create, pcg_destroy, pcg_last_error, pcg_precond, pcg_profile_enable,
+                   pcg_profile_read, pcg_profile_reset, pcg_set_stream, pcg_solve,
+                   pcg_solve_standard, pcg_solve_workspace_bytes, pcg_version)
+
+__all__ = [
+    "workloads", "Handle", "PcgError", "pcg_create", "pcg_destroy", "pcg_set_stream",
+    "pcg_apply_A", "pcg_precond", "pcg_solve", "pcg_solve_standard",
+    "pcg_solve_workspace_bytes", "pcg_profile_enable", "pcg_profile_reset",
+    "pcg_profile_read", "pcg_last_error", "pcg_version",
+]

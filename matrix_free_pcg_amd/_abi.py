@@ -1,0 +1,265 @@
+"""ctypes binding of the C ABI in include/mfpcg.h (argument marshalling only).
+
+Every function here has the name of the C entry point it calls.  Device
+vectors are torch float64 CUDA tensors of shape [ny, nz, nx] (or any
+contiguous tensor with nx*ny*nz elements); the stream is torch's current
+stream unless one is given.  Nothing here computes any part of the method:
+if the HIP library is missing the calls raise, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+from . import build as _build
+
+PCG_OK = 0
+PCG_NOT_CONVERGED = 1
+PCG_ERR_INVALID = -1
+PCG_ERR_BREAKDOWN = -2
+PCG_ERR_HIP = -3
+PCG_ERR_UNSUPPORTED = -4
+
+PCG_AH_CONST = 0
+PCG_AH_FIELD = 1
+
+PCG_KID_FUSED_PREC = 0
+PCG_KID_FUSED_SPMV = 1
+PCG_KID_APPLY_A = 2
+PCG_KID_PRECOND = 3
+PCG_KID_VECTOR = 4
+PCG_KID_COUNT = 5
+
+EXPORTED = [
+    "pcg_create", "pcg_destroy", "pcg_set_stream", "pcg_apply_A", "pcg_precond",
+    "pcg_solve_workspace_bytes", "pcg_solve", "pcg_solve_standard", "pcg_profile_enable",
+    "pcg_profile_reset", "pcg_profile_read", "pcg_last_error", "pcg_version",
+]
+
+
+class PcgError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+class pcg_grid(ctypes.Structure):
+    _fields_ = [("nx", ctypes.c_int32), ("ny", ctypes.c_int32), ("nz", ctypes.c_int32)]
+
+
+class pcg_coeffs(ctypes.Structure):
+    _fields_ = [
+        ("delta", ctypes.c_double),
+        ("alpha_z_face", ctypes.POINTER(ctypes.c_double)),
+        ("alpha_h_kind", ctypes.c_int32),
+        ("alpha_h_const", ctypes.c_double),
+        ("alpha_h_field", ctypes.POINTER(ctypes.c_double)),
+    ]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def load():
+    """Load libmfpcg.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = _build.LIB
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"HIP library not built: {path} is missing (run __graft_entry__.build() "
+                "or python -m matrix_free_pcg_amd.build)")
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        dp = ctypes.POINTER(ctypes.c_double)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        H = ctypes.c_void_p
+        lib.pcg_create.argtypes = [ctypes.POINTER(pcg_grid), ctypes.POINTER(pcg_coeffs), vp, ctypes.POINTER(H)]
+        lib.pcg_create.restype = ctypes.c_int
+        lib.pcg_destroy.argtypes = [H]
+        lib.pcg_destroy.restype = ctypes.c_int
+        lib.pcg_set_stream.argtypes = [H, vp]
+        lib.pcg_set_stream.restype = ctypes.c_int
+        lib.pcg_apply_A.argtypes = [H, vp, vp]
+        lib.pcg_apply_A.restype = ctypes.c_int
+        lib.pcg_precond.argtypes = [H, vp, vp]
+        lib.pcg_precond.restype = ctypes.c_int
+        lib.pcg_solve_workspace_bytes.argtypes = [H, ctypes.c_int32]
+        lib.pcg_solve_workspace_bytes.restype = ctypes.c_size_t
+        for name in ("pcg_solve", "pcg_solve_standard"):
+            f = getattr(lib, name)
+            f.argtypes = [H, vp, vp, ctypes.c_double, ctypes.c_int32, vp, ctypes.c_size_t,
+                          i32p, dp, i32p, dp]
+            f.restype = ctypes.c_int
+        lib.pcg_profile_enable.argtypes = [H, ctypes.c_int32]
+        lib.pcg_profile_enable.restype = ctypes.c_int
+        lib.pcg_profile_reset.argtypes = [H]
+        lib.pcg_profile_reset.restype = ctypes.c_int
+        lib.pcg_profile_read.argtypes = [H, ctypes.c_int32, dp, ctypes.POINTER(ctypes.c_int64)]
+        lib.pcg_profile_read.restype = ctypes.c_int
+        lib.pcg_last_error.argtypes = [H]
+        lib.pcg_last_error.restype = ctypes.c_char_p
+        lib.pcg_version.argtypes = []
+        lib.pcg_version.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev_ptr(t, n: int, name: str) -> int:
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != torch.float64 or not t.is_cuda:
+        raise TypeError(f"{name} must be a float64 CUDA tensor (got {t.dtype} on {t.device})")
+    if not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name} must be contiguous with {n} elements (got {tuple(t.shape)})")
+    return t.data_ptr()
+
+
+def pcg_last_error(h=None) -> str:
+    return load().pcg_last_error(h).decode()
+
+
+def pcg_version() -> str:
+    return load().pcg_version().decode()
+
+
+def _check(h, rc: int, allow=(PCG_OK,)) -> int:
+    if rc in allow:
+        return rc
+    raise PcgError(rc, pcg_last_error(h))
+
+
+class Handle:
+    """An open pcg_handle plus the grid it was created for."""
+
+    def __init__(self, ptr: int, nx: int, ny: int, nz: int, device):
+        self.ptr = ptr
+        self.nx, self.ny, self.nz = nx, ny, nz
+        self.n = nx * ny * nz
+        self.device = device
+
+    def __repr__(self):
+        return f"Handle({self.nx}x{self.ny}x{self.nz})"
+
+
+def pcg_create(problem, stream=None) -> Handle:
+    """Create a handle for a :class:`workloads.Problem` on the current CUDA device."""
+    import torch
+    lib = load()
+    g = pcg_grid(problem.nx, problem.ny, problem.nz)
+    az = np.ascontiguousarray(problem.alpha_z_face, dtype=np.float64)
+    if az.shape != (problem.nz + 1,):
+        raise ValueError("alpha_z_face must have nz+1 entries")
+    c = pcg_coeffs()
+    c.delta = float(problem.delta)
+    c.alpha_z_face = az.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    keep = [az]
+    if problem.alpha_h_is_const():
+        c.alpha_h_kind = PCG_AH_CONST
+        c.alpha_h_const = float(problem.alpha_h)
+        c.alpha_h_field = ctypes.POINTER(ctypes.c_double)()
+    else:
+        ah = np.ascontiguousarray(problem.alpha_h_field(), dtype=np.float64)
+        if ah.shape != (problem.ny, problem.nx):
+            raise ValueError("alpha_h field must have shape (ny, nx)")
+        keep.append(ah)
+        c.alpha_h_kind = PCG_AH_FIELD
+        c.alpha_h_const = 0.0
+        c.alpha_h_field = ah.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    out = ctypes.c_void_p()
+    rc = lib.pcg_create(ctypes.byref(g), ctypes.byref(c), ctypes.c_void_p(_stream_ptr(stream)),
+                        ctypes.byref(out))
+    del keep
+    if rc != PCG_OK:
+        raise PcgError(rc, pcg_last_error(None))
+    return Handle(out.value, problem.nx, problem.ny, problem.nz, torch.cuda.current_device())
+
+
+def pcg_destroy(h: Handle) -> None:
+    if h is not None and h.ptr:
+        load().pcg_destroy(h.ptr)
+        h.ptr = None
+
+
+def pcg_set_stream(h: Handle, stream) -> None:
+    _check(h.ptr, load().pcg_set_stream(h.ptr, ctypes.c_void_p(_stream_ptr(stream))))
+
+
+def pcg_apply_A(h: Handle, x, y) -> None:
+    """y = A x (asynchronous on the handle's stream)."""
+    rc = load().pcg_apply_A(h.ptr, _dev_ptr(x, h.n, "x"), _dev_ptr(y, h.n, "y"))
+    _check(h.ptr, rc)
+
+
+def pcg_precond(h: Handle, r, z) -> None:
+    """z = M^{-1} r (asynchronous on the handle's stream)."""
+    rc = load().pcg_precond(h.ptr, _dev_ptr(r, h.n, "r"), _dev_ptr(z, h.n, "z"))
+    _check(h.ptr, rc)
+
+
+def pcg_solve_workspace_bytes(h: Handle, maxit: int) -> int:
+    return int(load().pcg_solve_workspace_bytes(h.ptr, int(maxit)))
+
+
+def _solve(fn, h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
+    import torch
+    need = pcg_solve_workspace_bytes(h, maxit)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a CUDA tensor of >= {need} bytes")
+    hist = np.zeros(max(1, maxit + 1), dtype=np.float64)
+    iters = ctypes.c_int32(0)
+    hlen = ctypes.c_int32(0)
+    rel = ctypes.c_double(0.0)
+    rc = fn(h.ptr, _dev_ptr(b, h.n, "b"), _dev_ptr(x, h.n, "x"), float(tol), int(maxit),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            ctypes.byref(iters), hist.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+            ctypes.byref(hlen), ctypes.byref(rel))
+    _check(h.ptr, rc, allow=(PCG_OK, PCG_NOT_CONVERGED, PCG_ERR_BREAKDOWN))
+    return dict(status=rc, iters=iters.value, hist=hist[: hlen.value].copy(),
+                final_rel_res=rel.value,
+                error=pcg_last_error(h.ptr) if rc == PCG_ERR_BREAKDOWN else "")
+
+
+def pcg_solve(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
+    """Interleaved PCG (x in: x0, out: solution).  Returns status, iters, hist, final_rel_res."""
+    return _solve(load().pcg_solve, h, b, x, tol, maxit, workspace)
+
+
+def pcg_solve_standard(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
+    """Standard (non-interleaved) PCG; same contract as pcg_solve."""
+    return _solve(load().pcg_solve_standard, h, b, x, tol, maxit, workspace)
+
+
+def pcg_profile_enable(h: Handle, enable: bool = True) -> None:
+    _check(h.ptr, load().pcg_profile_enable(h.ptr, 1 if enable else 0))
+
+
+def pcg_profile_reset(h: Handle) -> None:
+    _check(h.ptr, load().pcg_profile_reset(h.ptr))
+
+
+def pcg_profile_read(h: Handle, kid: int):
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check(h.ptr, load().pcg_profile_read(h.ptr, int(kid), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,690 @@
+// Device kernels of the matrix-free PCG solver for gfx950 (MI355X).
+//
+// Method: E. Mueller, X. Guo, R. Scheichl, S. Shi, "Matrix-free GPU
+// implementation of a preconditioned conjugate gradient solver for
+// anisotropic elliptic PDEs" (2013).
+//
+// Work decomposition shared by every grid pass ("tile geometry"):
+//   * a tile is 64 consecutive columns i0..i0+63 of one row j;
+//   * a workgroup owns one tile and has P waves; wave s owns the vertical
+//     segment k in [s*L, min(nz, (s+1)*L)) of the tile's 64 columns, one
+//     column per lane;
+//   * with the layout l = i + nx*(k + nz*j) (section 6.1, eq. (22)) every
+//     wave-wide access at fixed (j, k) is 64 consecutive doubles (512 B);
+//   * hardware workgroup ids are renumbered so that each of the 8 XCDs (which
+//     receive workgroups round-robin) walks a contiguous run of tiles, j
+//     fastest: the j-1 / j+1 neighbour rows a stencil tile reads are then
+//     being read by workgroups on the same XCD, i.e. from the same L2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfpcg {
+
+constexpr int kWave = 64;
+constexpr int kMaxP = 16;   // waves (segments) per workgroup
+constexpr int kXcds = 8;
+
+// Operator description passed by value to every kernel.
+struct Op {
+    int nx, ny, nz;
+    int L, P;              // column segment length and count (P = ceil(nz/L))
+    double delta;
+    const double *az;      // nz+1 vertical face coefficients (faces 0, nz are 0)
+    const double *ah;      // ny*nx per-column alpha_h
+    const double *phib;    // (P-1)*ny*nx: Thomas auxiliary value phi at k = s*L-1
+};
+
+// Scalar state of one solve, in device memory (one writer: the reduce kernels).
+struct SolveState {
+    double alpha, beta, kappa_old, R0, R, sigma, kappa, pad0;
+    int32_t k, done, fixup, status, iters, pad1, pad2, pad3;
+};
+
+// Copy of the stop decision that the reduce kernel writes to pinned host memory.
+struct HostStatus {
+    int32_t k, done, status, iters;
+    double R, pad;
+};
+
+enum : int32_t { ST_OK = 0, ST_NOT_CONVERGED = 1, ST_BREAKDOWN = -2 };
+
+__device__ __forceinline__ int tile_of_block(int block, int nblocks)
+{
+    // XCD-aware renumbering: blocks block = 8q + x run on XCD x; give XCD x the
+    // contiguous tile range [start(x), start(x) + count(x)).
+    const int per = nblocks / kXcds, rem = nblocks % kXcds;
+    const int x = block % kXcds, q = block / kXcds;
+    return x * per + (x < rem ? x : rem) + q;
+}
+
+__device__ __forceinline__ size_t lin(const Op &o, int i, int j, int k)
+{
+    return (size_t)i + (size_t)o.nx * ((size_t)k + (size_t)o.nz * (size_t)j);
+}
+
+// Horizontal face coefficients of column (i, j): mean of the two cells'
+// alpha_h (the symmetric per-edge alpha_{T,T'} of section 3, eqs. (6)-(7)).
+struct Faces {
+    double xp, xm, yp, ym;
+    __device__ __forceinline__ double sum() const { return (xp + xm) + (yp + ym); }
+};
+
+__device__ __forceinline__ Faces column_faces(const Op &o, int i, int j)
+{
+    const int ip = (i + 1 == o.nx) ? 0 : i + 1;
+    const int im = (i == 0) ? o.nx - 1 : i - 1;
+    const int jp = (j + 1 == o.ny) ? 0 : j + 1;
+    const int jm = (j == 0) ? o.ny - 1 : j - 1;
+    const double c = o.ah[(size_t)j * o.nx + i];
+    Faces f;
+    f.xp = 0.5 * (c + o.ah[(size_t)j * o.nx + ip]);
+    f.xm = 0.5 * (c + o.ah[(size_t)j * o.nx + im]);
+    f.yp = 0.5 * (c + o.ah[(size_t)jp * o.nx + i]);
+    f.ym = 0.5 * (c + o.ah[(size_t)jm * o.nx + i]);
+    return f;
+}
+
+// Thomas pivot of level k (section 4.2, eq. (19); Appendix A, Algorithm 3):
+// D_k = diag_k - sub_k * phi_{k-1} with diag_k = delta + alpha_T + lo + up,
+// sub_k = -lo, phi_{k-1} = super_{k-1} / D_{k-1}.
+__device__ __forceinline__ double thomas_pivot(double delta, double aT, double lo, double up,
+                                               double phi_prev)
+{
+    return ((delta + aT) + (lo + up)) + lo * phi_prev;
+}
+
+// ---------------------------------------------------------------------------
+// Wave and workgroup reductions (deterministic: fixed shuffle tree, fixed
+// order over waves).
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+template <int NV>
+__device__ __forceinline__ void block_partials(double (&v)[NV], int s, int P, int lane,
+                                               double (*sh)[4], double *out)
+{
+#pragma unroll
+    for (int a = 0; a < NV; ++a)
+        v[a] = wave_sum(v[a]);
+    if (lane == 0) {
+#pragma unroll
+        for (int a = 0; a < NV; ++a)
+            sh[s][a] = v[a];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int a = 0; a < NV; ++a) {
+            double t = 0.0;
+            for (int w = 0; w < P; ++w)
+                t += sh[w][a];
+            out[a] = t;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Column solve z = M^{-1} r, one tridiagonal system per column (section 4.2,
+// eq. (19)), optionally fused with the residual update and the two dot
+// products of the interleaved preconditioner kernel (Appendix A,
+// Algorithm 3): r <- r - alpha q, <r,r>, <r,z>.
+//
+// The serial Thomas recurrence of a column is split over the P waves of the
+// workgroup (wave s: levels [s*L, s*L+len)).  It stays the same elimination:
+//  * the pivots D_k and multipliers phi_k do not depend on the data; wave s
+//    restarts their recurrence from phi_{s*L-1}, precomputed once per column
+//    at set-up (Op::phib), so it reproduces the serial pivots;
+//  * the forward-eliminated right-hand side z'_k is affine in the value z'
+//    entering the segment: z'_e = z''_e + mu_e * z'_in (z'' and mu computed
+//    locally); a scan over the waves through LDS gives every wave its true
+//    inflow, after which it recomputes its z'_k exactly;
+//  * back substitution z_k = z'_k - phi_k z_{k+1} is affine in the value
+//    above the segment: z_k = zh_k + H_k * z_top; a second scan, top down,
+//    gives every wave its z_top.
+// Per lane only three length-L arrays live in registers (r, 1/D, z').
+template <int L, bool UPDATE, bool DOTS>
+__global__ __launch_bounds__(1024) void k_column_solve(const double *__restrict__ rin,
+                                                       const double *__restrict__ q,
+                                                       double *__restrict__ rout,
+                                                       double *__restrict__ z, Op o,
+                                                       const SolveState *__restrict__ st,
+                                                       int first, double *__restrict__ partials)
+{
+    __shared__ double sh_a[kMaxP][kWave];
+    __shared__ double sh_b[kMaxP][kWave];
+    __shared__ double sh_red[kMaxP][4];
+
+    if (st != nullptr && st->done)
+        return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int P = o.P;
+    const int tile = tile_of_block(blockIdx.x, gridDim.x);
+    const int ntx = (o.nx + kWave - 1) / kWave;
+    const int it = tile / o.ny;
+    const int j = tile - it * o.ny;
+    (void)ntx;
+    const int i = it * kWave + lane;
+    const bool ok = i < o.nx;
+    const int ic = ok ? i : o.nx - 1;
+    const double aT = column_faces(o, ic, j).sum();
+    const int k0 = s * L;
+    const int len = min(L, o.nz - k0);
+    const size_t base = lin(o, ic, j, 0);
+    const size_t ks = (size_t)o.nx;
+    const double alpha = (UPDATE && !first) ? st->alpha : 0.0;
+
+    double rr[L], iD[L], zp[L];
+    double r2 = 0.0;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        double v = 0.0;
+        if (t < len && ok) {
+            const size_t l = base + (size_t)(k0 + t) * ks;
+            v = rin[l];
+            if (UPDATE && !first)
+                v = v - alpha * q[l];
+        }
+        rr[t] = v;
+        r2 += v * v;
+    }
+    if (UPDATE && !first && ok) {
+#pragma unroll
+        for (int t = 0; t < L; ++t)
+            if (t < len)
+                rout[base + (size_t)(k0 + t) * ks] = rr[t];
+    }
+
+    // Local forward sweep: pivots from the true incoming phi, z'' with zero inflow.
+    const size_t ncol = (size_t)o.nx * o.ny;
+    double phi = (s > 0) ? o.phib[(size_t)(s - 1) * ncol + (size_t)j * o.nx + ic] : 0.0;
+    double zpp = 0.0, mu = 1.0;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        if (t < len) {
+            const int k = k0 + t;
+            const double lo = o.az[k], up = o.az[k + 1];
+            const double inv = 1.0 / thomas_pivot(o.delta, aT, lo, up, phi);
+            iD[t] = inv;
+            phi = -up * inv;
+            zpp = (rr[t] + lo * zpp) * inv;
+            mu = (lo * inv) * mu;
+        } else {
+            iD[t] = 0.0;
+        }
+    }
+    sh_a[s][lane] = zpp;
+    sh_b[s][lane] = mu;
+    __syncthreads();
+    double zin = 0.0;
+    for (int w = 0; w < s; ++w)
+        zin = sh_a[w][lane] + sh_b[w][lane] * zin;
+
+    // Forward sweep again with the true inflow: z'_k of the serial algorithm.
+    double prev = zin;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        if (t < len) {
+            const double lo = o.az[k0 + t];
+            prev = (rr[t] + lo * prev) * iD[t];
+            zp[t] = prev;
+        }
+    }
+    // Local back substitution with zero value above the segment.
+    double znext = 0.0, H = 1.0;
+#pragma unroll
+    for (int t = L - 1; t >= 0; --t) {
+        if (t < len) {
+            const double up = o.az[k0 + t + 1];
+            const double ph = -up * iD[t];
+            znext = zp[t] - ph * znext;
+            H = -ph * H;
+            zp[t] = znext;
+        }
+    }
+    __syncthreads();   // every wave has finished reading the first scan
+    sh_a[s][lane] = znext;   // zh at the segment's first level
+    sh_b[s][lane] = H;       // response of that level to the value above
+    __syncthreads();
+    double ztop = 0.0;
+    for (int w = P - 1; w > s; --w)
+        ztop = sh_a[w][lane] + sh_b[w][lane] * ztop;
+
+    double kap = 0.0;
+    H = 1.0;
+#pragma unroll
+    for (int t = L - 1; t >= 0; --t) {
+        if (t < len) {
+            const double up = o.az[k0 + t + 1];
+            H = (up * iD[t]) * H;
+            const double zv = zp[t] + ztop * H;
+            kap += rr[t] * zv;
+            if (ok)
+                z[base + (size_t)(k0 + t) * ks] = zv;
+        }
+    }
+    if (DOTS) {
+        double v[2] = {r2, kap};
+        double out[2];
+        block_partials<2>(v, s, P, lane, sh_red, out);
+        if (threadIdx.x == 0) {
+            partials[2 * (size_t)tile + 0] = out[0];
+            partials[2 * (size_t)tile + 1] = out[1];
+        }
+    }
+}
+
+// Set-up: the Thomas multipliers phi_k at every segment boundary of every
+// column (data independent; computed once per operator).
+__global__ void k_setup_phib(Op o, double *__restrict__ phib)
+{
+    const size_t ncol = (size_t)o.nx * o.ny;
+    const size_t col = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (col >= ncol)
+        return;
+    const int j = (int)(col / o.nx);
+    const int i = (int)(col - (size_t)j * o.nx);
+    const double aT = column_faces(o, i, j).sum();
+    double phi = 0.0;
+    for (int k = 0; k < o.nz; ++k) {
+        const double lo = o.az[k], up = o.az[k + 1];
+        const double inv = 1.0 / thomas_pivot(o.delta, aT, lo, up, phi);
+        phi = -up * inv;
+        const int kk = k + 1;
+        if (kk % o.L == 0 && kk / o.L < o.P)
+            phib[(size_t)(kk / o.L - 1) * ncol + col] = phi;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stencil passes (section 4.2, eq. (18)): the 7-point operator recomputed in
+// every cell from the per-column face coefficients and the per-level alpha_z.
+enum : int {
+    SP_FIRST = 0,   // p = z, q = A z, <p,q>             (first interleaved pass)
+    SP_FUSED = 1,   // x += alpha p, p = z + beta p, q = A z + beta q, <p,q> (Algorithm 2)
+    SP_APPLY = 2,   // y = A x
+    SP_RESID = 3,   // y = b - A x
+    SP_APPLY_DOT = 4 // y = A x, <x, y>  (standard PCG: q = A p, sigma)
+};
+
+template <int L, int MODE>
+__global__ __launch_bounds__(1024) void k_stencil(const double *__restrict__ zin,
+                                                  const double *__restrict__ bvec,
+                                                  double *__restrict__ u, double *__restrict__ p,
+                                                  double *__restrict__ y, Op o,
+                                                  const SolveState *__restrict__ st,
+                                                  double *__restrict__ partials)
+{
+    __shared__ double sh_red[kMaxP][4];
+    double alpha = 0.0, beta = 0.0;
+    bool fixup_only = false;
+    if (MODE == SP_FIRST || MODE == SP_FUSED || MODE == SP_APPLY_DOT) {
+        if (st->done) {
+            if (MODE != SP_FUSED || !st->fixup)
+                return;
+            fixup_only = true;
+        }
+        alpha = st->alpha;
+        beta = st->beta;
+    }
+    const int lane = threadIdx.x & (kWave - 1);
+    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tile = tile_of_block(blockIdx.x, gridDim.x);
+    const int it = tile / o.ny;
+    const int j = tile - it * o.ny;
+    const int i = it * kWave + lane;
+    const bool ok = i < o.nx;
+    const int ic = ok ? i : o.nx - 1;
+    const int k0 = s * L;
+    const int len = min(L, o.nz - k0);
+    const size_t ks = (size_t)o.nx;
+    const size_t base = lin(o, ic, j, 0);
+
+    if (MODE == SP_FUSED && fixup_only) {
+        // The stop test passed in this iteration: only the pending update
+        // x += alpha p of the last step remains (Algorithm 1 exits before it).
+        if (ok) {
+            for (int t = 0; t < len; ++t) {
+                const size_t l = base + (size_t)(k0 + t) * ks;
+                u[l] = u[l] + alpha * p[l];
+            }
+        }
+        return;
+    }
+
+    const Faces f = column_faces(o, ic, j);
+    const int ip = (ic + 1 == o.nx) ? 0 : ic + 1;
+    const int im = (ic == 0) ? o.nx - 1 : ic - 1;
+    const int jp = (j + 1 == o.ny) ? 0 : j + 1;
+    const int jm = (j == 0) ? o.ny - 1 : j - 1;
+    const size_t bxp = lin(o, ip, j, 0), bxm = lin(o, im, j, 0);
+    const size_t byp = lin(o, ic, jp, 0), bym = lin(o, ic, jm, 0);
+
+    double acc = 0.0;
+    double zc = zin[base + (size_t)k0 * ks];
+    double zm = (k0 > 0) ? zin[base + (size_t)(k0 - 1) * ks] : zc;
+#pragma unroll 4
+    for (int t = 0; t < len; ++t) {
+        const int k = k0 + t;
+        const size_t off = (size_t)k * ks;
+        const double zn = (k + 1 < o.nz) ? zin[base + off + ks] : zc;
+        const double lo = o.az[k], up = o.az[k + 1];
+        double Az = o.delta * zc;
+        Az += f.xp * (zc - zin[bxp + off]);
+        Az += f.xm * (zc - zin[bxm + off]);
+        Az += f.yp * (zc - zin[byp + off]);
+        Az += f.ym * (zc - zin[bym + off]);
+        Az += up * (zc - zn);
+        Az += lo * (zc - zm);
+        const size_t l = base + off;
+        if (MODE == SP_FIRST) {
+            if (ok) {
+                p[l] = zc;
+                y[l] = Az;
+                acc += zc * Az;
+            }
+        } else if (MODE == SP_FUSED) {
+            if (ok) {
+                const double po = p[l];
+                const double qo = y[l];
+                u[l] = u[l] + alpha * po;
+                const double pn = zc + beta * po;
+                const double qn = Az + beta * qo;
+                p[l] = pn;
+                y[l] = qn;
+                acc += pn * qn;
+            }
+        } else if (MODE == SP_APPLY) {
+            if (ok)
+                y[l] = Az;
+        } else if (MODE == SP_RESID) {
+            if (ok)
+                y[l] = bvec[l] - Az;
+        } else {   // SP_APPLY_DOT
+            if (ok) {
+                y[l] = Az;
+                acc += zc * Az;
+            }
+        }
+        zm = zc;
+        zc = zn;
+    }
+    if (MODE == SP_FIRST || MODE == SP_FUSED || MODE == SP_APPLY_DOT) {
+        double v[1] = {acc};
+        double out[1];
+        block_partials<1>(v, s, o.P, lane, sh_red, out);
+        if (threadIdx.x == 0)
+            partials[2 * (size_t)tile] = out[0];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Vector passes of the standard PCG loop, each fused with its dot product.
+// x += alpha p ; r -= alpha q ; <r,r>
+template <int L>
+__global__ __launch_bounds__(1024) void k_update_xr(double *__restrict__ x,
+                                                    const double *__restrict__ p,
+                                                    double *__restrict__ r,
+                                                    const double *__restrict__ q, Op o,
+                                                    const SolveState *__restrict__ st,
+                                                    double *__restrict__ partials)
+{
+    __shared__ double sh_red[kMaxP][4];
+    if (st->done)
+        return;
+    const double alpha = st->alpha;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tile = tile_of_block(blockIdx.x, gridDim.x);
+    const int it = tile / o.ny;
+    const int j = tile - it * o.ny;
+    const int i = it * kWave + lane;
+    const bool ok = i < o.nx;
+    const int k0 = s * L;
+    const int len = min(L, o.nz - k0);
+    double acc = 0.0;
+    if (ok) {
+        const size_t base = lin(o, i, j, 0);
+#pragma unroll 4
+        for (int t = 0; t < len; ++t) {
+            const size_t l = base + (size_t)(k0 + t) * o.nx;
+            x[l] = x[l] + alpha * p[l];
+            const double rn = r[l] - alpha * q[l];
+            r[l] = rn;
+            acc += rn * rn;
+        }
+    }
+    double v[1] = {acc};
+    double out[1];
+    block_partials<1>(v, s, o.P, lane, sh_red, out);
+    if (threadIdx.x == 0)
+        partials[2 * (size_t)tile] = out[0];
+}
+
+// p = z + beta p   (p = z on the first step)
+template <int L>
+__global__ __launch_bounds__(1024) void k_update_p(double *__restrict__ p,
+                                                   const double *__restrict__ z, Op o,
+                                                   const SolveState *__restrict__ st, int first)
+{
+    if (st->done)
+        return;
+    const double beta = st->beta;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tile = tile_of_block(blockIdx.x, gridDim.x);
+    const int it = tile / o.ny;
+    const int j = tile - it * o.ny;
+    const int i = it * kWave + lane;
+    if (i >= o.nx)
+        return;
+    const int k0 = s * L;
+    const int len = min(L, o.nz - k0);
+    const size_t base = lin(o, i, j, 0);
+#pragma unroll 4
+    for (int t = 0; t < len; ++t) {
+        const size_t l = base + (size_t)(k0 + t) * o.nx;
+        p[l] = first ? z[l] : z[l] + beta * p[l];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reductions of the per-workgroup partial sums (fixed order: deterministic)
+// and the scalar recurrences of PCG (section 4.3, Algorithm 1).
+constexpr int kRedThreads = 256;
+
+template <int NV>
+__device__ __forceinline__ void sum_partials(const double *__restrict__ partials, int nparts,
+                                             int first_value, double (&tot)[NV])
+{
+    __shared__ double sh[NV][kRedThreads];
+    const int tid = threadIdx.x;
+    double acc[NV];
+#pragma unroll
+    for (int a = 0; a < NV; ++a)
+        acc[a] = 0.0;
+    for (int t = tid; t < nparts; t += kRedThreads) {
+#pragma unroll
+        for (int a = 0; a < NV; ++a)
+            acc[a] += partials[2 * (size_t)t + first_value + a];
+    }
+#pragma unroll
+    for (int a = 0; a < NV; ++a)
+        sh[a][tid] = acc[a];
+    __syncthreads();
+    for (int w = kRedThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) {
+#pragma unroll
+            for (int a = 0; a < NV; ++a)
+                sh[a][tid] += sh[a][tid + w];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int a = 0; a < NV; ++a)
+        tot[a] = sh[a][0];
+}
+
+__device__ __forceinline__ void finish(SolveState *st, int32_t status, int32_t fixup)
+{
+    st->done = 1;
+    st->status = status;
+    st->fixup = fixup;
+}
+
+__device__ __forceinline__ void publish(const SolveState *st, HostStatus *hs, int k)
+{
+    if (hs) {
+        volatile HostStatus *v = hs;
+        v->R = st->R;
+        v->iters = st->iters;
+        v->status = st->status;
+        v->done = st->done;
+        v->k = k;
+    }
+}
+
+// After the preconditioner pass of step k: ||r_k||, the stop test, beta.
+// Used by both loops (the standard loop passes kappa from its own pass).
+__global__ __launch_bounds__(kRedThreads) void k_reduce_rz(const double *__restrict__ partials,
+                                                           int nparts, SolveState *st,
+                                                           double *__restrict__ hist, int k,
+                                                           int maxit, double tol,
+                                                           HostStatus *hs)
+{
+    if (st->done) {
+        if (threadIdx.x == 0)
+            publish(st, hs, k);
+        return;
+    }
+    double tot[2];
+    sum_partials<2>(partials, nparts, 0, tot);
+    if (threadIdx.x != 0)
+        return;
+    const double R = sqrt(tot[0]);
+    const double kappa = tot[1];
+    st->R = R;
+    st->kappa = kappa;
+    hist[k] = R;
+    if (k == 0) {
+        st->R0 = R;
+        st->iters = 0;
+        st->alpha = 0.0;
+        if (!isfinite(R))
+            finish(st, ST_BREAKDOWN, 0);
+        else if (R == 0.0)
+            finish(st, ST_OK, 0);
+        else if (maxit == 0)
+            finish(st, ST_NOT_CONVERGED, 0);
+        else if (!(kappa > 0.0) || !isfinite(kappa))
+            finish(st, ST_BREAKDOWN, 0);
+        else {
+            st->beta = 0.0;
+            st->kappa_old = kappa;
+        }
+    } else {
+        st->iters = k;
+        if (!isfinite(R))
+            finish(st, ST_BREAKDOWN, 1);
+        else if (R == 0.0 || R / st->R0 < tol)
+            finish(st, ST_OK, 1);
+        else if (k == maxit)
+            finish(st, ST_NOT_CONVERGED, 1);
+        else if (!(kappa > 0.0) || !isfinite(kappa))
+            finish(st, ST_BREAKDOWN, 1);
+        else {
+            st->beta = kappa / st->kappa_old;
+            st->kappa_old = kappa;
+        }
+    }
+    publish(st, hs, k);
+}
+
+// After the stencil pass: sigma = <p, A p>, alpha = kappa / sigma.
+__global__ __launch_bounds__(kRedThreads) void k_reduce_sigma(const double *__restrict__ partials,
+                                                              int nparts, SolveState *st,
+                                                              int iters_if_breakdown)
+{
+    if (st->done) {
+        if (threadIdx.x == 0)
+            st->fixup = 0;
+        return;
+    }
+    double tot[1];
+    sum_partials<1>(partials, nparts, 0, tot);
+    if (threadIdx.x != 0)
+        return;
+    const double sigma = tot[0];
+    st->sigma = sigma;
+    if (!(sigma > 0.0) || !isfinite(sigma)) {
+        st->iters = iters_if_breakdown;
+        finish(st, ST_BREAKDOWN, 0);
+    } else {
+        st->alpha = st->kappa_old / sigma;
+    }
+}
+
+// Standard loop, after x += alpha p, r -= alpha q: ||r_k|| and the stop test.
+__global__ __launch_bounds__(kRedThreads) void k_reduce_rr(const double *__restrict__ partials,
+                                                           int nparts, SolveState *st,
+                                                           double *__restrict__ hist, int k,
+                                                           int maxit, double tol, HostStatus *hs)
+{
+    if (st->done) {
+        if (threadIdx.x == 0)
+            publish(st, hs, k);
+        return;
+    }
+    double tot[1];
+    sum_partials<1>(partials, nparts, 0, tot);
+    if (threadIdx.x != 0)
+        return;
+    const double R = sqrt(tot[0]);
+    st->R = R;
+    hist[k] = R;
+    st->iters = k;
+    if (!isfinite(R))
+        finish(st, ST_BREAKDOWN, 0);
+    else if (R == 0.0 || R / st->R0 < tol)
+        finish(st, ST_OK, 0);
+    else if (k == maxit)
+        finish(st, ST_NOT_CONVERGED, 0);
+    publish(st, hs, k);
+}
+
+// Standard loop, after z = M^{-1} r: kappa = <r,z>, beta = kappa / kappa_old.
+__global__ __launch_bounds__(kRedThreads) void k_reduce_kappa(const double *__restrict__ partials,
+                                                              int nparts, SolveState *st)
+{
+    if (st->done)
+        return;
+    double tot[1];
+    sum_partials<1>(partials, nparts, 1, tot);
+    if (threadIdx.x != 0)
+        return;
+    const double kappa = tot[0];
+    st->kappa = kappa;
+    if (!(kappa > 0.0) || !isfinite(kappa)) {
+        finish(st, ST_BREAKDOWN, 0);
+    } else {
+        st->beta = kappa / st->kappa_old;
+        st->kappa_old = kappa;
+    }
+}
+
+__global__ void k_init_state(SolveState *st)
+{
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        SolveState z = {};
+        *st = z;
+    }
+}
+
+}   // namespace mfpcg

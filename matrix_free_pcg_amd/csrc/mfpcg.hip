@@ -1,0 +1,669 @@
+// Host side of the matrix-free PCG library: argument checking, the handle,
+// the workspace layout, kernel launches and the two PCG loops.  See
+// include/mfpcg.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mfpcg.h"
+#include "kernels.hpp"
+
+using namespace mfpcg;
+
+namespace {
+
+thread_local std::string g_create_error = "no error";
+
+struct EventPair {
+    hipEvent_t a, b;
+    int kid;
+    int tag;   // iteration index of the launch (or -1)
+};
+
+}   // namespace
+
+struct pcg_handle {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    Op op{};
+    int ntx = 0;           // tiles along i
+    int ntiles = 0;        // workgroups of every grid pass
+    size_t n = 0;          // nx*ny*nz
+    double *d_az = nullptr, *d_ah = nullptr, *d_phib = nullptr;
+    HostStatus *h_status = nullptr;   // pinned host memory written by the reduce kernels
+    std::string err = "no error";
+    bool profiling = false;
+    double prof_ms[PCG_KID_COUNT] = {};
+    int64_t prof_n[PCG_KID_COUNT] = {};
+    std::vector<hipEvent_t> free_events;
+    std::vector<EventPair> pending;
+};
+
+namespace {
+
+int fail(pcg_handle *h, int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (h)
+        h->err = buf;
+    else
+        g_create_error = buf;
+    return code;
+}
+
+#define HIP_TRY(h, call)                                                                     \
+    do {                                                                                     \
+        hipError_t e_ = (call);                                                              \
+        if (e_ != hipSuccess)                                                                \
+            return fail((h), PCG_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_));     \
+    } while (0)
+
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Column segment length: the smallest of 4, 8, 16, 32 that splits nz into at
+// most 8 segments (16 for nz > 128).
+int choose_L(int nz)
+{
+    if (nz <= 32) return 4;
+    if (nz <= 64) return 8;
+    if (nz <= 256) return 16;
+    return 32;
+}
+
+struct Workspace {
+    double *r, *z, *p, *q, *partials, *hist;
+    SolveState *state;
+};
+
+size_t workspace_layout(const pcg_handle *h, int32_t maxit, char *base, Workspace *w)
+{
+    const size_t vec = align256(h->n * sizeof(double));
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    size_t o_r = take(vec), o_z = take(vec), o_p = take(vec), o_q = take(vec);
+    size_t o_part = take((size_t)h->ntiles * 2 * sizeof(double));
+    size_t o_state = take(sizeof(SolveState));
+    size_t o_hist = take((size_t)(maxit + 1) * sizeof(double));
+    if (w && base) {
+        w->r = (double *)(base + o_r);
+        w->z = (double *)(base + o_z);
+        w->p = (double *)(base + o_p);
+        w->q = (double *)(base + o_q);
+        w->partials = (double *)(base + o_part);
+        w->state = (SolveState *)(base + o_state);
+        w->hist = (double *)(base + o_hist);
+    }
+    return off;
+}
+
+// ---- per-kernel event timing ------------------------------------------------
+hipEvent_t take_event(pcg_handle *h)
+{
+    if (!h->free_events.empty()) {
+        hipEvent_t e = h->free_events.back();
+        h->free_events.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess)
+        return nullptr;
+    return e;
+}
+
+struct Timed {
+    pcg_handle *h;
+    EventPair ev{};
+    bool on;
+    Timed(pcg_handle *hh, int kid, int tag) : h(hh), on(hh->profiling)
+    {
+        if (!on) return;
+        ev.a = take_event(h);
+        ev.b = take_event(h);
+        ev.kid = kid;
+        ev.tag = tag;
+        if (!ev.a || !ev.b) { on = false; return; }
+        hipEventRecord(ev.a, h->stream);
+    }
+    ~Timed()
+    {
+        if (!on) return;
+        hipEventRecord(ev.b, h->stream);
+        h->pending.push_back(ev);
+    }
+};
+
+// Fold the recorded event pairs into the totals (the stream must be idle).
+// Launches tagged `skip_tag` of kernel `skip_kid` are dropped (the final
+// stencil pass of a solve, which only applies the pending x update).
+void drain_events(pcg_handle *h, int skip_kid = -1, int skip_tag = -2)
+{
+    for (auto &e : h->pending) {
+        float ms = 0.f;
+        if (!(e.kid == skip_kid && e.tag == skip_tag) && hipEventElapsedTime(&ms, e.a, e.b) == hipSuccess) {
+            h->prof_ms[e.kid] += ms;
+            h->prof_n[e.kid] += 1;
+        }
+        h->free_events.push_back(e.a);
+        h->free_events.push_back(e.b);
+    }
+    h->pending.clear();
+}
+
+// ---- launch helpers (template dispatch on the segment length) ---------------
+template <int L>
+void launch_column(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
+                   const SolveState *st, int first, double *partials, bool update, bool dots)
+{
+    dim3 grid(h->ntiles), block(kWave * h->op.P);
+    if (update)
+        k_column_solve<L, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
+    else if (dots)
+        k_column_solve<L, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
+    else
+        k_column_solve<L, false, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
+}
+
+void column(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
+            const SolveState *st, int first, double *partials, bool update, bool dots)
+{
+    switch (h->op.L) {
+    case 4: launch_column<4>(h, rin, q, rout, z, st, first, partials, update, dots); break;
+    case 8: launch_column<8>(h, rin, q, rout, z, st, first, partials, update, dots); break;
+    case 16: launch_column<16>(h, rin, q, rout, z, st, first, partials, update, dots); break;
+    default: launch_column<32>(h, rin, q, rout, z, st, first, partials, update, dots); break;
+    }
+}
+
+template <int L>
+void launch_stencil(pcg_handle *h, int mode, const double *zin, const double *b, double *u,
+                    double *p, double *y, const SolveState *st, double *partials)
+{
+    dim3 grid(h->ntiles), block(kWave * h->op.P);
+    switch (mode) {
+    case SP_FIRST: k_stencil<L, SP_FIRST><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
+    case SP_FUSED: k_stencil<L, SP_FUSED><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
+    case SP_APPLY: k_stencil<L, SP_APPLY><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
+    case SP_RESID: k_stencil<L, SP_RESID><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
+    default: k_stencil<L, SP_APPLY_DOT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
+    }
+}
+
+void stencil(pcg_handle *h, int mode, const double *zin, const double *b, double *u, double *p,
+             double *y, const SolveState *st, double *partials)
+{
+    switch (h->op.L) {
+    case 4: launch_stencil<4>(h, mode, zin, b, u, p, y, st, partials); break;
+    case 8: launch_stencil<8>(h, mode, zin, b, u, p, y, st, partials); break;
+    case 16: launch_stencil<16>(h, mode, zin, b, u, p, y, st, partials); break;
+    default: launch_stencil<32>(h, mode, zin, b, u, p, y, st, partials); break;
+    }
+}
+
+template <int L>
+void launch_update_xr(pcg_handle *h, double *x, const double *p, double *r, const double *q,
+                      const SolveState *st, double *partials)
+{
+    k_update_xr<L><<<dim3(h->ntiles), dim3(kWave * h->op.P), 0, h->stream>>>(x, p, r, q, h->op, st, partials);
+}
+template <int L>
+void launch_update_p(pcg_handle *h, double *p, const double *z, const SolveState *st, int first)
+{
+    k_update_p<L><<<dim3(h->ntiles), dim3(kWave * h->op.P), 0, h->stream>>>(p, z, h->op, st, first);
+}
+void update_xr(pcg_handle *h, double *x, const double *p, double *r, const double *q,
+               const SolveState *st, double *partials)
+{
+    switch (h->op.L) {
+    case 4: launch_update_xr<4>(h, x, p, r, q, st, partials); break;
+    case 8: launch_update_xr<8>(h, x, p, r, q, st, partials); break;
+    case 16: launch_update_xr<16>(h, x, p, r, q, st, partials); break;
+    default: launch_update_xr<32>(h, x, p, r, q, st, partials); break;
+    }
+}
+void update_p(pcg_handle *h, double *p, const double *z, const SolveState *st, int first)
+{
+    switch (h->op.L) {
+    case 4: launch_update_p<4>(h, p, z, st, first); break;
+    case 8: launch_update_p<8>(h, p, z, st, first); break;
+    case 16: launch_update_p<16>(h, p, z, st, first); break;
+    default: launch_update_p<32>(h, p, z, st, first); break;
+    }
+}
+
+int check_vectors(pcg_handle *h, const void *a, const void *b, const char *what)
+{
+    if (!a || !b)
+        return fail(h, PCG_ERR_INVALID, "%s: null device pointer", what);
+    const size_t bytes = h->n * sizeof(double);
+    const char *pa = (const char *)a, *pb = (const char *)b;
+    if (pa < pb + bytes && pb < pa + bytes)
+        return fail(h, PCG_ERR_INVALID, "%s: input and output overlap", what);
+    return PCG_OK;
+}
+
+int set_device(pcg_handle *h)
+{
+    HIP_TRY(h, hipSetDevice(h->device));
+    return PCG_OK;
+}
+
+struct SolveArgs {
+    const double *b;
+    double *x;
+    double tol;
+    int32_t maxit;
+    void *ws;
+    size_t ws_bytes;
+    int32_t *iters_out;
+    double *hist_host;
+    int32_t *hist_len_out;
+    double *final_rel;
+};
+
+int solve_prologue(pcg_handle *h, const SolveArgs &a, Workspace *w, const char *who)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    if (a.maxit < 0)
+        return fail(h, PCG_ERR_INVALID, "%s: maxit must be >= 0", who);
+    if (std::isnan(a.tol))
+        return fail(h, PCG_ERR_INVALID, "%s: tol is NaN", who);
+    int rc = check_vectors(h, a.b, a.x, who);
+    if (rc != PCG_OK)
+        return rc;
+    if (!a.ws)
+        return fail(h, PCG_ERR_INVALID, "%s: null workspace", who);
+    if (((uintptr_t)a.ws & 255u) != 0)
+        return fail(h, PCG_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
+    const size_t need = workspace_layout(h, a.maxit, nullptr, nullptr);
+    if (a.ws_bytes < need)
+        return fail(h, PCG_ERR_INVALID, "%s: workspace has %zu bytes, needs %zu", who, a.ws_bytes, need);
+    const char *ws = (const char *)a.ws, *xb = (const char *)a.x;
+    const size_t vb = h->n * sizeof(double);
+    if (xb < ws + need && ws < xb + vb)
+        return fail(h, PCG_ERR_INVALID, "%s: x overlaps the workspace", who);
+    const char *bb = (const char *)a.b;
+    if (bb < ws + need && ws < bb + vb)
+        return fail(h, PCG_ERR_INVALID, "%s: b overlaps the workspace", who);
+    rc = set_device(h);
+    if (rc != PCG_OK)
+        return rc;
+    workspace_layout(h, a.maxit, (char *)a.ws, w);
+    return PCG_OK;
+}
+
+int solve_epilogue(pcg_handle *h, const SolveArgs &a, const Workspace &w, int skip_kid, int skip_tag)
+{
+    HIP_TRY(h, hipStreamSynchronize(h->stream));
+    HIP_TRY(h, hipGetLastError());
+    if (h->profiling)
+        drain_events(h, skip_kid, skip_tag);
+    SolveState st;
+    HIP_TRY(h, hipMemcpy(&st, w.state, sizeof st, hipMemcpyDeviceToHost));
+    const int iters = st.iters;
+    if (a.iters_out)
+        *a.iters_out = iters;
+    if (a.hist_host && iters >= 0) {
+        const int cnt = (st.status == ST_BREAKDOWN && iters == 0 && !std::isfinite(st.R0)) ? 1 : iters + 1;
+        HIP_TRY(h, hipMemcpy(a.hist_host, w.hist, (size_t)cnt * sizeof(double), hipMemcpyDeviceToHost));
+        if (a.hist_len_out)
+            *a.hist_len_out = cnt;
+    } else if (a.hist_len_out) {
+        *a.hist_len_out = iters + 1;
+    }
+    if (a.final_rel) {
+        double hk = 0.0;
+        HIP_TRY(h, hipMemcpy(&hk, w.hist + iters, sizeof(double), hipMemcpyDeviceToHost));
+        *a.final_rel = (st.R0 == 0.0) ? 0.0 : hk / st.R0;
+    }
+    if (st.status == ST_OK)
+        return PCG_OK;
+    if (st.status == ST_NOT_CONVERGED)
+        return PCG_NOT_CONVERGED;
+    return fail(h, PCG_ERR_BREAKDOWN, "PCG breakdown after %d steps (sigma = %g, kappa = %g, |r| = %g)",
+                iters, st.sigma, st.kappa, st.R);
+}
+
+}   // namespace
+
+// ============================================================================
+extern "C" {
+
+const char *pcg_version(void) { return "mfpcg 0.1 (gfx950, fp64)"; }
+
+const char *pcg_last_error(const pcg_handle *h)
+{
+    return h ? h->err.c_str() : g_create_error.c_str();
+}
+
+int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_handle **out)
+{
+    if (!out)
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: out is NULL");
+    *out = nullptr;
+    if (!grid || !c)
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: null grid or coefficients");
+    const int nx = grid->nx, ny = grid->ny, nz = grid->nz;
+    if (nx < 1 || ny < 1 || nz < 1)
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: grid %d x %d x %d must be positive", nx, ny, nz);
+    if (nz > 512)
+        return fail(nullptr, PCG_ERR_UNSUPPORTED, "pcg_create: nz = %d > 512 is not supported", nz);
+    const size_t ntx = ((size_t)nx + kWave - 1) / kWave;
+    if (ntx * (size_t)ny > (size_t)0x7fffffff)
+        return fail(nullptr, PCG_ERR_UNSUPPORTED, "pcg_create: too many columns");
+    if (!(c->delta > 0.0) || !std::isfinite(c->delta))
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: delta must be finite and > 0");
+    if (!c->alpha_z_face)
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: alpha_z_face is NULL");
+    for (int f = 0; f <= nz; ++f) {
+        const double v = c->alpha_z_face[f];
+        if (!(v >= 0.0) || !std::isfinite(v))
+            return fail(nullptr, PCG_ERR_INVALID, "pcg_create: alpha_z_face[%d] = %g must be finite and >= 0", f, v);
+    }
+    if (c->alpha_z_face[0] != 0.0 || c->alpha_z_face[nz] != 0.0)
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: faces 0 and nz carry no flux and must be 0");
+    const size_t ncol = (size_t)nx * ny;
+    std::vector<double> ah(ncol);
+    if (c->alpha_h_kind == PCG_AH_CONST) {
+        if (!(c->alpha_h_const >= 0.0) || !std::isfinite(c->alpha_h_const))
+            return fail(nullptr, PCG_ERR_INVALID, "pcg_create: alpha_h_const must be finite and >= 0");
+        for (auto &v : ah) v = c->alpha_h_const;
+    } else if (c->alpha_h_kind == PCG_AH_FIELD) {
+        if (!c->alpha_h_field)
+            return fail(nullptr, PCG_ERR_INVALID, "pcg_create: alpha_h_field is NULL");
+        for (size_t t = 0; t < ncol; ++t) {
+            const double v = c->alpha_h_field[t];
+            if (!(v >= 0.0) || !std::isfinite(v))
+                return fail(nullptr, PCG_ERR_INVALID, "pcg_create: alpha_h_field[%zu] = %g must be finite and >= 0", t, v);
+            ah[t] = v;
+        }
+    } else {
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: unknown alpha_h_kind %d", c->alpha_h_kind);
+    }
+
+    pcg_handle *h = new pcg_handle();
+    auto bail = [&](int code) {
+        g_create_error = h->err;
+        pcg_destroy(h);
+        return code;
+    };
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        h->err = "pcg_create: hipGetDevice failed";
+        return bail(PCG_ERR_HIP);
+    }
+    h->stream = (hipStream_t)hip_stream;
+    const int L = choose_L(nz);
+    const int P = (nz + L - 1) / L;
+    h->ntx = (int)ntx;
+    h->ntiles = (int)(ntx * ny);
+    h->n = ncol * (size_t)nz;
+    h->op.nx = nx;
+    h->op.ny = ny;
+    h->op.nz = nz;
+    h->op.L = L;
+    h->op.P = P;
+    h->op.delta = c->delta;
+    hipError_t e;
+    if ((e = hipMalloc(&h->d_az, sizeof(double) * (nz + 1))) != hipSuccess ||
+        (e = hipMalloc(&h->d_ah, sizeof(double) * ncol)) != hipSuccess ||
+        (e = hipMalloc(&h->d_phib, sizeof(double) * ncol * (size_t)(P > 1 ? P - 1 : 1))) != hipSuccess ||
+        (e = hipHostMalloc((void **)&h->h_status, sizeof(HostStatus), hipHostMallocCoherent)) != hipSuccess) {
+        h->err = std::string("pcg_create: allocation failed: ") + hipGetErrorString(e);
+        return bail(PCG_ERR_HIP);
+    }
+    memset(h->h_status, 0, sizeof(HostStatus));
+    if ((e = hipMemcpyAsync(h->d_az, c->alpha_z_face, sizeof(double) * (nz + 1), hipMemcpyHostToDevice, h->stream)) != hipSuccess ||
+        (e = hipMemcpyAsync(h->d_ah, ah.data(), sizeof(double) * ncol, hipMemcpyHostToDevice, h->stream)) != hipSuccess) {
+        h->err = std::string("pcg_create: copy failed: ") + hipGetErrorString(e);
+        return bail(PCG_ERR_HIP);
+    }
+    h->op.az = h->d_az;
+    h->op.ah = h->d_ah;
+    h->op.phib = h->d_phib;
+    if (P > 1) {
+        const int threads = 256;
+        const size_t blocks = (ncol + threads - 1) / threads;
+        k_setup_phib<<<dim3((unsigned)blocks), dim3(threads), 0, h->stream>>>(h->op, h->d_phib);
+    }
+    if ((e = hipStreamSynchronize(h->stream)) != hipSuccess || (e = hipGetLastError()) != hipSuccess) {
+        h->err = std::string("pcg_create: set-up failed: ") + hipGetErrorString(e);
+        return bail(PCG_ERR_HIP);
+    }
+    *out = h;
+    return PCG_OK;
+}
+
+int pcg_destroy(pcg_handle *h)
+{
+    if (!h)
+        return PCG_OK;
+    hipSetDevice(h->device);
+    if (h->stream || h->d_az)
+        hipStreamSynchronize(h->stream);
+    for (auto &e : h->pending) {
+        hipEventDestroy(e.a);
+        hipEventDestroy(e.b);
+    }
+    for (auto e : h->free_events)
+        hipEventDestroy(e);
+    if (h->d_az) hipFree(h->d_az);
+    if (h->d_ah) hipFree(h->d_ah);
+    if (h->d_phib) hipFree(h->d_phib);
+    if (h->h_status) hipHostFree(h->h_status);
+    delete h;
+    return PCG_OK;
+}
+
+int pcg_set_stream(pcg_handle *h, void *hip_stream)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    h->stream = (hipStream_t)hip_stream;
+    return PCG_OK;
+}
+
+int pcg_apply_A(pcg_handle *h, const double *x, double *y)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    int rc = check_vectors(h, x, y, "pcg_apply_A");
+    if (rc != PCG_OK)
+        return rc;
+    if ((rc = set_device(h)) != PCG_OK)
+        return rc;
+    {
+        Timed t(h, PCG_KID_APPLY_A, -1);
+        stencil(h, SP_APPLY, x, nullptr, nullptr, nullptr, y, nullptr, nullptr);
+    }
+    HIP_TRY(h, hipGetLastError());
+    return PCG_OK;
+}
+
+int pcg_precond(pcg_handle *h, const double *r, double *z)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    int rc = check_vectors(h, r, z, "pcg_precond");
+    if (rc != PCG_OK)
+        return rc;
+    if ((rc = set_device(h)) != PCG_OK)
+        return rc;
+    {
+        Timed t(h, PCG_KID_PRECOND, -1);
+        column(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, false, false);
+    }
+    HIP_TRY(h, hipGetLastError());
+    return PCG_OK;
+}
+
+size_t pcg_solve_workspace_bytes(const pcg_handle *h, int32_t maxit)
+{
+    if (!h || maxit < 0)
+        return 0;
+    return workspace_layout(h, maxit, nullptr, nullptr);
+}
+
+int pcg_solve(pcg_handle *h, const double *b, double *x, double tol, int32_t maxit, void *ws,
+              size_t ws_bytes, int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
+              double *final_rel)
+{
+    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    Workspace w{};
+    int rc = solve_prologue(h, a, &w, "pcg_solve");
+    if (rc != PCG_OK)
+        return rc;
+    HostStatus *hs = nullptr;
+    HIP_TRY(h, hipHostGetDevicePointer((void **)&hs, h->h_status, 0));
+    h->h_status->done = 0;
+    const int np = h->ntiles;
+    k_init_state<<<1, 64, 0, h->stream>>>(w.state);
+    // a2: r0 = b - A x0
+    stencil(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
+    hipEvent_t ev = nullptr;
+    HIP_TRY(h, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    int last = 0;
+    for (int k = 0; k <= maxit; ++k) {
+        // a3: r -= alpha q; z = M^{-1} r; partial <r,r>, <r,z>   (Algorithm 3)
+        {
+            Timed t(h, PCG_KID_FUSED_PREC, k);
+            column(h, w.r, w.q, w.r, w.z, w.state, k == 0, w.partials, true, true);
+        }
+        // a4: ||r_k||, stop test, beta
+        k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state, w.hist, k, maxit, tol, hs);
+        hipEventRecord(ev, h->stream);
+        // a5: x += alpha p; p = z + beta p; q = A z + beta q; partial <p,q>  (Algorithm 2)
+        //     (only x += alpha p once the stop test has passed: a7)
+        {
+            Timed t(h, PCG_KID_FUSED_SPMV, k);
+            stencil(h, k == 0 ? SP_FIRST : SP_FUSED, w.z, nullptr, x, w.p, w.q, w.state, w.partials);
+        }
+        // a6: sigma, alpha
+        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state, k);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) {
+            hipEventDestroy(ev);
+            return fail(h, PCG_ERR_HIP, "pcg_solve: launch failed: %s", hipGetErrorString(e));
+        }
+        e = hipEventSynchronize(ev);
+        if (e != hipSuccess) {
+            hipEventDestroy(ev);
+            return fail(h, PCG_ERR_HIP, "pcg_solve: hipEventSynchronize: %s", hipGetErrorString(e));
+        }
+        last = k;
+        if (((volatile HostStatus *)h->h_status)->done)
+            break;
+    }
+    hipEventDestroy(ev);
+    return solve_epilogue(h, a, w, PCG_KID_FUSED_SPMV, last);
+}
+
+int pcg_solve_standard(pcg_handle *h, const double *b, double *x, double tol, int32_t maxit,
+                       void *ws, size_t ws_bytes, int32_t *iters_out, double *hist_host,
+                       int32_t *hist_len_out, double *final_rel)
+{
+    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    Workspace w{};
+    int rc = solve_prologue(h, a, &w, "pcg_solve_standard");
+    if (rc != PCG_OK)
+        return rc;
+    HostStatus *hs = nullptr;
+    HIP_TRY(h, hipHostGetDevicePointer((void **)&hs, h->h_status, 0));
+    h->h_status->done = 0;
+    const int np = h->ntiles;
+    hipEvent_t ev = nullptr;
+    HIP_TRY(h, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    k_init_state<<<1, 64, 0, h->stream>>>(w.state);
+    stencil(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
+    {
+        Timed t(h, PCG_KID_PRECOND, 0);
+        column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, false, true);
+    }
+    k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state, w.hist, 0, maxit, tol, hs);
+    {
+        Timed t(h, PCG_KID_VECTOR, 0);
+        update_p(h, w.p, w.z, w.state, 1);
+    }
+    hipEventRecord(ev, h->stream);
+    hipError_t e = hipEventSynchronize(ev);
+    bool done = (e == hipSuccess) && ((volatile HostStatus *)h->h_status)->done;
+    for (int k = 1; e == hipSuccess && !done && k <= maxit; ++k) {
+        {   // q = A p ; sigma = <p,q>
+            Timed t(h, PCG_KID_APPLY_A, k);
+            stencil(h, SP_APPLY_DOT, w.p, nullptr, nullptr, nullptr, w.q, w.state, w.partials);
+        }
+        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state, k - 1);
+        {   // x += alpha p ; r -= alpha q ; <r,r>
+            Timed t(h, PCG_KID_VECTOR, k);
+            update_xr(h, x, w.p, w.r, w.q, w.state, w.partials);
+        }
+        k_reduce_rr<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state, w.hist, k, maxit, tol, hs);
+        hipEventRecord(ev, h->stream);
+        {   // z = M^{-1} r ; kappa = <r,z>
+            Timed t(h, PCG_KID_PRECOND, k);
+            column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, false, true);
+        }
+        k_reduce_kappa<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state);
+        {   // p = z + beta p
+            Timed t(h, PCG_KID_VECTOR, k);
+            update_p(h, w.p, w.z, w.state, 0);
+        }
+        e = hipGetLastError();
+        if (e == hipSuccess)
+            e = hipEventSynchronize(ev);
+        done = (e == hipSuccess) && ((volatile HostStatus *)h->h_status)->done;
+    }
+    hipEventDestroy(ev);
+    if (e != hipSuccess)
+        return fail(h, PCG_ERR_HIP, "pcg_solve_standard: %s", hipGetErrorString(e));
+    return solve_epilogue(h, a, w, -1, -2);
+}
+
+int pcg_profile_enable(pcg_handle *h, int32_t enable)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    h->profiling = enable != 0;
+    return PCG_OK;
+}
+
+int pcg_profile_reset(pcg_handle *h)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    if (!h->pending.empty()) {
+        HIP_TRY(h, hipStreamSynchronize(h->stream));
+        drain_events(h);
+    }
+    for (int t = 0; t < PCG_KID_COUNT; ++t) {
+        h->prof_ms[t] = 0.0;
+        h->prof_n[t] = 0;
+    }
+    return PCG_OK;
+}
+
+int pcg_profile_read(const pcg_handle *hc, int32_t kid, double *ms_total, int64_t *launches)
+{
+    pcg_handle *h = const_cast<pcg_handle *>(hc);
+    if (!h || kid < 0 || kid >= PCG_KID_COUNT)
+        return PCG_ERR_INVALID;
+    if (!h->pending.empty()) {
+        HIP_TRY(h, hipStreamSynchronize(h->stream));
+        drain_events(h);
+    }
+    if (ms_total)
+        *ms_total = h->prof_ms[kid];
+    if (launches)
+        *launches = h->prof_n[kid];
+    return PCG_OK;
+}
+
+}   // extern "C"

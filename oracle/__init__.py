@@ -66,6 +66,8 @@ class Oracle:
         lib.orc_pcg.argtypes = [i, i, i, d, dp, dp, dp, dp, d, i, dp,
                                 ctypes.POINTER(ctypes.c_int), i, dp, dp, dp]
         lib.orc_pcg.restype = i
+        lib.orc_last_loop_seconds.argtypes = []
+        lib.orc_last_loop_seconds.restype = d
         self.lib = lib
         self.path = path
 
@@ -122,7 +124,8 @@ class Oracle:
         st = self.lib.orc_pcg(prob.nx, prob.ny, prob.nz, prob.delta, _ptr(az), _ptr(ah), _ptr(b),
                               _ptr(x), float(tol), int(maxit), _ptr(hist), ctypes.byref(iters), ntr,
                               _ptr(tr[0]), _ptr(tr[1]), _ptr(tr[2]))
-        out = dict(x=x, iters=iters.value, hist=hist[: iters.value + 1].copy(), status=st)
+        out = dict(x=x, iters=iters.value, hist=hist[: iters.value + 1].copy(), status=st,
+                   loop_seconds=self.lib.orc_last_loop_seconds())
         if ntr > 0:
             out.update(trace_r=tr[0], trace_z=tr[1], trace_p=tr[2])
         return out

@@ -36,11 +36,13 @@
  * coefficient field is indexed [j*nx + i].  The algorithm is indifferent to
  * the order; this order is used so that no conversion is needed.
  */
+#define _POSIX_C_SOURCE 199309L
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <time.h>
 
 #define ORC_OK 0
 #define ORC_NOT_CONVERGED 1
@@ -146,6 +148,18 @@ int orc_precond(int nx, int ny, int nz, double delta, const double *az,
     return status;
 }
 
+/* Wall time of the CG-step loop of the last orc_pcg call (timing only; used
+ * to report the oracle's seconds per step without its set-up pass). */
+static double g_loop_seconds = 0.0;
+double orc_last_loop_seconds(void) { return g_loop_seconds; }
+
+static double now_seconds(void)
+{
+    struct timespec ts;
+    clock_gettime(CLOCK_MONOTONIC, &ts);
+    return (double)ts.tv_sec + 1e-9 * (double)ts.tv_nsec;
+}
+
 /* Neumaier-compensated dot product in memory order. */
 double orc_dot(size_t n, const double *a, const double *b)
 {
@@ -185,6 +199,7 @@ int orc_pcg(int nx, int ny, int nz, double delta, const double *az, const double
     double *q = (double *)malloc(sizeof(double) * n);
     int status = ORC_NOT_CONVERGED;
     int it = 0;
+    double t_loop = 0.0;
     if (!r || !z || !p || !q) {
         status = ORC_ERR_INVALID;
         goto done;
@@ -208,7 +223,10 @@ int orc_pcg(int nx, int ny, int nz, double delta, const double *az, const double
         memcpy(trace_p, p, sizeof(double) * n);
     }
 
+    t_loop = now_seconds();
+    g_loop_seconds = 0.0;
     for (int k = 1; k <= maxit; ++k) {
+        g_loop_seconds = now_seconds() - t_loop;
         orc_apply_A(nx, ny, nz, delta, az, ah, p, q);
         double sigma = orc_dot(n, p, q);
         if (!(sigma > 0.0) || !isfinite(sigma)) { status = ORC_ERR_BREAKDOWN; goto done; }
@@ -235,6 +253,7 @@ int orc_pcg(int nx, int ny, int nz, double delta, const double *az, const double
     }
     status = ORC_NOT_CONVERGED;
 done:
+    if (it > 0) g_loop_seconds = now_seconds() - t_loop;
     if (iters_out) *iters_out = it;
     free(r); free(z); free(p); free(q);
     return status;

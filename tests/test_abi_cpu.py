@@ -1,0 +1,126 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/mfpcg.h declares, and rejects invalid arguments before any GPU work."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from matrix_free_pcg_amd import _abi
+from matrix_free_pcg_amd import build as hipbuild
+
+HEADER = os.path.join(hipbuild.INCLUDE, "mfpcg.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hipbuild.LIB) or hipbuild.is_stale():
+        hipbuild.build()
+    return _abi.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pcg_[a-zA-Z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_contract():
+    names = declared_functions()
+    for required in ("pcg_create", "pcg_destroy", "pcg_apply_A", "pcg_precond", "pcg_solve",
+                     "pcg_last_error", "pcg_solve_workspace_bytes"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(_abi.EXPORTED) == names
+
+
+def test_version_and_error_strings(lib):
+    assert "gfx950" in _abi.pcg_version()
+    assert isinstance(_abi.pcg_last_error(None), str)
+
+
+def _create(lib, nx, ny, nz, delta, az, kind=0, hconst=1.0, field=None):
+    g = _abi.pcg_grid(nx, ny, nz)
+    c = _abi.pcg_coeffs()
+    c.delta = delta
+    az = np.ascontiguousarray(az, dtype=np.float64)
+    c.alpha_z_face = az.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    c.alpha_h_kind = kind
+    c.alpha_h_const = hconst
+    if field is not None:
+        field = np.ascontiguousarray(field, dtype=np.float64)
+        c.alpha_h_field = field.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    out = ctypes.c_void_p()
+    rc = lib.pcg_create(ctypes.byref(g), ctypes.byref(c), None, ctypes.byref(out))
+    return rc, out.value, (az, field)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("delta_zero", _abi.PCG_ERR_INVALID),
+    ("delta_nan", _abi.PCG_ERR_INVALID),
+    ("face_negative", _abi.PCG_ERR_INVALID),
+    ("boundary_face", _abi.PCG_ERR_INVALID),
+    ("nz_zero", _abi.PCG_ERR_INVALID),
+    ("nx_negative", _abi.PCG_ERR_INVALID),
+    ("nz_too_big", _abi.PCG_ERR_UNSUPPORTED),
+    ("alpha_h_negative", _abi.PCG_ERR_INVALID),
+    ("field_negative", _abi.PCG_ERR_INVALID),
+    ("field_null", _abi.PCG_ERR_INVALID),
+    ("bad_kind", _abi.PCG_ERR_INVALID),
+])
+def test_create_rejects_invalid_arguments(lib, case, expect):
+    nz = 8
+    az = np.zeros(nz + 1)
+    az[1:nz] = 10.0
+    args = dict(nx=4, ny=4, nz=nz, delta=1e-2, az=az)
+    if case == "delta_zero":
+        args["delta"] = 0.0
+    elif case == "delta_nan":
+        args["delta"] = float("nan")
+    elif case == "face_negative":
+        az[3] = -1.0
+    elif case == "boundary_face":
+        az[0] = 1.0
+    elif case == "nz_zero":
+        args["nz"] = 0
+        args["az"] = np.zeros(1)
+    elif case == "nx_negative":
+        args["nx"] = -3
+    elif case == "nz_too_big":
+        args["nz"] = 513
+        args["az"] = np.zeros(514)
+    elif case == "alpha_h_negative":
+        args["hconst"] = -0.5
+    elif case == "field_negative":
+        f = np.ones((4, 4))
+        f[2, 1] = -1.0
+        args.update(kind=1, field=f)
+    elif case == "field_null":
+        args.update(kind=1)
+    elif case == "bad_kind":
+        args.update(kind=7)
+    rc, h, _keep = _create(lib, **args)
+    assert rc == expect
+    assert h is None
+    assert len(_abi.pcg_last_error(None)) > 0
+
+
+def test_null_handle_calls_are_invalid(lib):
+    assert lib.pcg_apply_A(None, None, None) == _abi.PCG_ERR_INVALID
+    assert lib.pcg_precond(None, None, None) == _abi.PCG_ERR_INVALID
+    assert lib.pcg_destroy(None) == _abi.PCG_OK
+    assert lib.pcg_solve_workspace_bytes(None, 10) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(hipbuild, "LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_abi, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _abi.load()

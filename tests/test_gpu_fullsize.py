@@ -1,0 +1,153 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (1024x1024x128 with graded alpha_z and varying alpha_h;
+512x512x128 manufactured solution).
+
+The oracle cannot finish a full solve at these sizes within a test, so the
+solve is checked by what it can compute: the whole stencil and column solve
+(one pass each), the first CG steps exactly, and the true residual
+||b - A x|| of the GPU solution evaluated by the oracle's stencil.
+"""
+import time
+
+import numpy as np
+import pytest
+
+import matrix_free_pcg_amd as mf
+import oracle
+from gpu_helpers import EPS, apply_tol, precond_tol, require_gpu, to_dev, to_host
+from matrix_free_pcg_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+@pytest.fixture(scope="module")
+def cfg4():
+    t = time.time()
+    w = W.make_workload(4)
+    print(f"\n[cfg4] inputs generated in {time.time() - t:.1f}s", flush=True)
+    return w
+
+
+def test_cfg4_apply_A_full(dev, cfg4):
+    import torch
+    prob = cfg4.problem
+    x = W.uniform_field(prob.nx, prob.ny, prob.nz, 101)
+    h = mf.pcg_create(prob)
+    try:
+        xd = to_dev(x, dev)
+        yd = torch.empty_like(xd)
+        mf.pcg_apply_A(h, xd, yd)
+        torch.cuda.synchronize()
+        y = to_host(yd)
+        del xd, yd
+    finally:
+        mf.pcg_destroy(h)
+    ref = oracle.apply_A(prob, x)
+    err = np.abs(y - ref).max()
+    assert err <= apply_tol(prob, x), err
+
+
+def test_cfg4_precond_full(dev, cfg4):
+    import torch
+    prob = cfg4.problem
+    r = cfg4.rhs
+    h = mf.pcg_create(prob)
+    try:
+        rd = to_dev(r, dev)
+        zd = torch.empty_like(rd)
+        mf.pcg_precond(h, rd, zd)
+        torch.cuda.synchronize()
+        z = to_host(zd)
+        del rd, zd
+    finally:
+        mf.pcg_destroy(h)
+    ref = oracle.precond(prob, r)
+    err = np.abs(z - ref).max()
+    assert err <= precond_tol(prob, ref), (err, precond_tol(prob, ref))
+
+
+def test_cfg4_first_steps_full(dev, cfg4):
+    """Three CG steps at full size: history and iterate against the oracle."""
+    import torch
+    prob = cfg4.problem
+    h = mf.pcg_create(prob)
+    try:
+        bd = to_dev(cfg4.rhs, dev)
+        xd = torch.zeros_like(bd)
+        res = mf.pcg_solve(h, bd, xd, 0.0, 3)
+        torch.cuda.synchronize()
+        xg = to_host(xd)
+        del bd, xd
+    finally:
+        mf.pcg_destroy(h)
+    t = time.time()
+    ref = oracle.pcg(prob, cfg4.rhs, tol=0.0, maxit=3)
+    print(f"[cfg4] oracle 3 steps: {time.time() - t:.1f}s", flush=True)
+    assert res["iters"] == ref["iters"] == 3
+    assert np.allclose(res["hist"], ref["hist"], rtol=1e-11, atol=0), (res["hist"], ref["hist"])
+    rel = np.linalg.norm(xg - ref["x"]) / np.linalg.norm(ref["x"])
+    assert rel <= 1e-11, rel
+
+
+def _true_residual(prob, b, x):
+    r = b - oracle.apply_A(prob, x)
+    return np.linalg.norm(r) / np.linalg.norm(b)
+
+
+def test_cfg4_full_solve_true_residual(dev, cfg4):
+    """Full solve to tol 1e-10 (the benchmark's step); the oracle's stencil
+    evaluates the true residual of the returned iterate.  The gap between the
+    recursively updated residual and the true one is rounding; it is bounded
+    here by 1e-10 (the stop test) plus 64 eps * iters * S / ||b|| with S the
+    stencil's term bound for x."""
+    import torch
+    prob = cfg4.problem
+    h = mf.pcg_create(prob)
+    try:
+        bd = to_dev(cfg4.rhs, dev)
+        xd = torch.zeros_like(bd)
+        res = mf.pcg_solve(h, bd, xd, cfg4.tol, cfg4.maxit)
+        torch.cuda.synchronize()
+        xg = to_host(xd)
+        del bd, xd
+    finally:
+        mf.pcg_destroy(h)
+    assert res["status"] == mf.PCG_OK, res
+    assert res["final_rel_res"] < cfg4.tol
+    tr = _true_residual(prob, cfg4.rhs, xg)
+    S = (prob.delta + 8 * prob.alpha_h_field().max() + 4 * prob.alpha_z_face.max()) * np.linalg.norm(xg)
+    bound = cfg4.tol + 64 * EPS * res["iters"] * S / np.linalg.norm(cfg4.rhs)
+    print(f"[cfg4] iters={res['iters']} recursive={res['final_rel_res']:.3e} true={tr:.3e} bound={bound:.3e}",
+          flush=True)
+    assert tr <= bound, (tr, bound)
+
+
+def test_cfg3_manufactured_full(dev):
+    """512x512x128, b = A x_true: the solve recovers x_true to within the
+    condition-number bound of tol, and its true residual is small."""
+    import torch
+    w = W.make_workload(3)
+    prob = w.problem
+    b = oracle.apply_A(prob, w.x_true)
+    h = mf.pcg_create(prob)
+    try:
+        bd = to_dev(b, dev)
+        xd = torch.zeros_like(bd)
+        res = mf.pcg_solve(h, bd, xd, w.tol, w.maxit)
+        torch.cuda.synchronize()
+        xg = to_host(xd)
+        del bd, xd
+    finally:
+        mf.pcg_destroy(h)
+    assert res["status"] == mf.PCG_OK, res
+    err = np.linalg.norm(xg - w.x_true) / np.linalg.norm(w.x_true)
+    kappa = (prob.delta + 8 * 1.0 + 4 * prob.alpha_z_face.max()) / prob.delta
+    tr = _true_residual(prob, b, xg)
+    print(f"[cfg3] iters={res['iters']} err={err:.3e} true-res={tr:.3e}", flush=True)
+    assert err <= kappa * w.tol
+    assert tr <= 1e-8
