@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--fixed-iterations", type=int, default=0,
+                    help="run exactly N CG steps per solve (tol 0) instead of solving to 1e-10")
     return ap.parse_args()
 
 
@@ -118,13 +120,16 @@ def main():
     x = torch.zeros_like(b)
     stream = torch.cuda.current_stream()
     h = mf.pcg_create(prob, stream)
-    ws = torch.empty(mf.pcg_solve_workspace_bytes(h, w.maxit), dtype=torch.uint8, device=dev)
+    tol, maxit = w.tol, w.maxit
+    if args.fixed_iterations > 0:
+        tol, maxit = 0.0, args.fixed_iterations
+    ws = torch.empty(mf.pcg_solve_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
     solve = mf.pcg_solve if args.variant == "interleaved" else mf.pcg_solve_standard
     torch.cuda.synchronize()
 
     for s in range(args.warmup):
         x.zero_()
-        res = solve(h, b, x, w.tol, w.maxit, ws)
+        res = solve(h, b, x, tol, maxit, ws)
         log(f"[bench] warmup {s}: iters={res['iters']} status={res['status']}")
 
     mf.pcg_profile_reset(h)
@@ -134,7 +139,7 @@ def main():
     t0 = time.perf_counter()
     for s in range(args.steps):
         x.zero_()
-        res = solve(h, b, x, w.tol, w.maxit, ws)
+        res = solve(h, b, x, tol, maxit, ws)
         iters.append(res["iters"])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -187,7 +192,7 @@ def main():
         "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": w.name, "nx": prob.nx, "ny": prob.ny, "nz": prob.nz,
-                   "tol": w.tol, "variant": args.variant,
+                   "tol": tol, "maxit": maxit, "variant": args.variant,
                    "iterations_per_solve": iters, "status": res["status"],
                    "final_rel_res": res["final_rel_res"], "true_rel_res": true_rel},
         "hbm_GBps_per_iteration": round(per_iter_bytes * it_s / 1e9, 1),

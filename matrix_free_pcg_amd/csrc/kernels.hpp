@@ -4,17 +4,23 @@
 // implementation of a preconditioned conjugate gradient solver for
 // anisotropic elliptic PDEs" (2013).
 //
-// Work decomposition shared by every grid pass ("tile geometry"):
-//   * a tile is 64 consecutive columns i0..i0+63 of one row j;
-//   * a workgroup owns one tile and has P waves; wave s owns the vertical
-//     segment k in [s*L, min(nz, (s+1)*L)) of the tile's 64 columns, one
-//     column per lane;
-//   * with the layout l = i + nx*(k + nz*j) (section 6.1, eq. (22)) every
-//     wave-wide access at fixed (j, k) is 64 consecutive doubles (512 B);
-//   * hardware workgroup ids are renumbered so that each of the 8 XCDs (which
-//     receive workgroups round-robin) walks a contiguous run of tiles, j
-//     fastest: the j-1 / j+1 neighbour rows a stencil tile reads are then
-//     being read by workgroups on the same XCD, i.e. from the same L2.
+// Field layout l = i + nx*(k + nz*j) (section 6.1, eq. (22)): a wave-wide
+// access to consecutive i at fixed (j, k) is contiguous.
+//
+// Two work decompositions:
+//  * column passes (the Thomas solve): a workgroup owns C consecutive columns
+//    of one row j and all their levels; thread (c, s) owns column c and the
+//    vertical segment k in [s*L, min(nz, (s+1)*L)).
+//  * sweep passes (stencil and vector updates): a workgroup owns 64
+//    consecutive columns of one row j over Ws*Ls consecutive levels; each
+//    wave sweeps Ls levels with one column per lane, so per-column work (the
+//    face coefficients) is done once per Ls points.
+// Tiles are numbered with j faster than the i-tile (k-tile fastest of all in
+// sweep passes): at any moment every XCD works on the same few rows j, and
+// the j-1 / j+1 and k-1 / k+1 neighbours of a tile are read by workgroups
+// that run at the same time.  Hardware workgroup ids are renumbered so that
+// each of the 8 XCDs (which receive workgroups round-robin) walks one
+// contiguous run of tiles and those neighbours are served by its own L2.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,17 +29,18 @@
 namespace mfpcg {
 
 constexpr int kWave = 64;
-constexpr int kMaxP = 16;   // waves (segments) per workgroup
+constexpr int kMaxThreads = 1024;
 constexpr int kXcds = 8;
 
-// Operator description passed by value to every kernel.
+// Operator and launch geometry, passed by value to every kernel.
 struct Op {
     int nx, ny, nz;
-    int L, P;              // column segment length and count (P = ceil(nz/L))
+    int L, P, C, ntc;      // column passes: segment length, segments, columns per tile, tiles along i
+    int Ls, Ws, nkt;       // sweep passes: levels per wave, waves per tile, tiles along k
     double delta;
     const double *az;      // nz+1 vertical face coefficients (faces 0, nz are 0)
     const double *ah;      // ny*nx per-column alpha_h
-    const double *phib;    // (P-1)*ny*nx: Thomas auxiliary value phi at k = s*L-1
+    const double *phib;    // (P-1)*ny*nx: Thomas multiplier phi at k = s*L-1
 };
 
 // Scalar state of one solve, in device memory (one writer: the reduce kernels).
@@ -52,8 +59,8 @@ enum : int32_t { ST_OK = 0, ST_NOT_CONVERGED = 1, ST_BREAKDOWN = -2 };
 
 __device__ __forceinline__ int tile_of_block(int block, int nblocks)
 {
-    // XCD-aware renumbering: blocks block = 8q + x run on XCD x; give XCD x the
-    // contiguous tile range [start(x), start(x) + count(x)).
+    // Blocks 8q + x run on XCD x; give XCD x the contiguous tile range
+    // [start(x), start(x) + count(x)).
     const int per = nblocks / kXcds, rem = nblocks % kXcds;
     const int x = block % kXcds, q = block / kXcds;
     return x * per + (x < rem ? x : rem) + q;
@@ -96,8 +103,8 @@ __device__ __forceinline__ double thomas_pivot(double delta, double aT, double l
 }
 
 // ---------------------------------------------------------------------------
-// Wave and workgroup reductions (deterministic: fixed shuffle tree, fixed
-// order over waves).
+// Deterministic reductions: fixed shuffle tree in a wave, fixed order over the
+// waves of a workgroup.
 __device__ __forceinline__ double wave_sum(double v)
 {
 #pragma unroll
@@ -106,25 +113,28 @@ __device__ __forceinline__ double wave_sum(double v)
     return v;
 }
 
+// Sum NV per-thread values over the workgroup; thread 0 gets the totals.
 template <int NV>
-__device__ __forceinline__ void block_partials(double (&v)[NV], int s, int P, int lane,
-                                               double (*sh)[4], double *out)
+__device__ __forceinline__ void block_sum(double (&v)[NV], double (*sh)[NV], double (&out)[NV])
 {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
 #pragma unroll
     for (int a = 0; a < NV; ++a)
         v[a] = wave_sum(v[a]);
     if (lane == 0) {
 #pragma unroll
         for (int a = 0; a < NV; ++a)
-            sh[s][a] = v[a];
+            sh[w][a] = v[a];
     }
     __syncthreads();
     if (threadIdx.x == 0) {
 #pragma unroll
         for (int a = 0; a < NV; ++a) {
             double t = 0.0;
-            for (int w = 0; w < P; ++w)
-                t += sh[w][a];
+            for (int q = 0; q < nw; ++q)
+                t += sh[q][a];
             out[a] = t;
         }
     }
@@ -136,50 +146,67 @@ __device__ __forceinline__ void block_partials(double (&v)[NV], int s, int P, in
 // products of the interleaved preconditioner kernel (Appendix A,
 // Algorithm 3): r <- r - alpha q, <r,r>, <r,z>.
 //
-// The serial Thomas recurrence of a column is split over the P waves of the
-// workgroup (wave s: levels [s*L, s*L+len)).  It stays the same elimination:
-//  * the pivots D_k and multipliers phi_k do not depend on the data; wave s
-//    restarts their recurrence from phi_{s*L-1}, precomputed once per column
-//    at set-up (Op::phib), so it reproduces the serial pivots;
+// The serial Thomas recurrence of a column is split over the P segment
+// threads that own it.  It stays the same elimination:
+//  * the pivots D_k and multipliers phi_k do not depend on the data; segment
+//    s restarts their recurrence from phi_{s*L-1}, precomputed once per
+//    column at set-up (Op::phib), so it reproduces the serial pivots;
 //  * the forward-eliminated right-hand side z'_k is affine in the value z'
 //    entering the segment: z'_e = z''_e + mu_e * z'_in (z'' and mu computed
-//    locally); a scan over the waves through LDS gives every wave its true
-//    inflow, after which it recomputes its z'_k exactly;
+//    locally); a scan over the segments through LDS gives every segment its
+//    true inflow, after which it recomputes its z'_k exactly;
 //  * back substitution z_k = z'_k - phi_k z_{k+1} is affine in the value
 //    above the segment: z_k = zh_k + H_k * z_top; a second scan, top down,
-//    gives every wave its z_top.
-// Per lane only three length-L arrays live in registers (r, 1/D, z').
-template <int L, bool UPDATE, bool DOTS>
-__global__ __launch_bounds__(1024) void k_column_solve(const double *__restrict__ rin,
-                                                       const double *__restrict__ q,
-                                                       double *__restrict__ rout,
-                                                       double *__restrict__ z, Op o,
-                                                       const SolveState *__restrict__ st,
-                                                       int first, double *__restrict__ partials)
+//    gives every segment its z_top.
+// Per thread only three length-L arrays live in registers (r, 1/D, z').
+// Block: C * P threads rounded up to a multiple of 64 (extra threads idle).
+template <int L, int C, bool UPDATE, bool DOTS>
+__global__ __launch_bounds__(kMaxThreads) void k_column_solve(
+    const double *__restrict__ rin, const double *__restrict__ q, double *__restrict__ rout,
+    double *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
+    double *__restrict__ partials)
 {
-    __shared__ double sh_a[kMaxP][kWave];
-    __shared__ double sh_b[kMaxP][kWave];
-    __shared__ double sh_red[kMaxP][4];
+    __shared__ double sh_a[kMaxThreads];
+    __shared__ double sh_b[kMaxThreads];
+    __shared__ double sh_red[kMaxThreads / kWave][2];
 
     if (st != nullptr && st->done)
         return;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x;
+    const int c = tid % C;
+    // with 64 columns a wave owns one segment: keep s in a scalar register
+    const int s = (C == kWave) ? __builtin_amdgcn_readfirstlane(tid / C) : tid / C;
     const int P = o.P;
+    const bool active = s < P;
     const int tile = tile_of_block(blockIdx.x, gridDim.x);
-    const int ntx = (o.nx + kWave - 1) / kWave;
     const int it = tile / o.ny;
     const int j = tile - it * o.ny;
-    (void)ntx;
-    const int i = it * kWave + lane;
-    const bool ok = i < o.nx;
-    const int ic = ok ? i : o.nx - 1;
+    const int i = it * C + c;
+    const bool ok = active && i < o.nx;
+    const int ic = i < o.nx ? i : o.nx - 1;
     const double aT = column_faces(o, ic, j).sum();
     const int k0 = s * L;
-    const int len = min(L, o.nz - k0);
+    const int len = active ? min(L, o.nz - k0) : 0;
     const size_t base = lin(o, ic, j, 0);
     const size_t ks = (size_t)o.nx;
     const double alpha = (UPDATE && !first) ? st->alpha : 0.0;
+
+    // The segment's vertical face coefficients: face(t) couples levels
+    // k0+t-1 and k0+t (face(0) below the segment, face(len) above it).  With
+    // 64 columns the segment is wave-uniform and the loads are scalar; with
+    // 32 a wave holds two segments and a register copy avoids reloading them.
+    double fz[L + 1];
+    if constexpr (C != kWave) {
+#pragma unroll
+        for (int t = 0; t <= L; ++t)
+            fz[t] = (t <= len) ? o.az[k0 + t] : 0.0;
+    }
+    auto face = [&](int t) -> double {
+        if constexpr (C == kWave)
+            return o.az[k0 + t];
+        else
+            return fz[t];
+    };
 
     double rr[L], iD[L], zp[L];
     double r2 = 0.0;
@@ -204,13 +231,12 @@ __global__ __launch_bounds__(1024) void k_column_solve(const double *__restrict_
 
     // Local forward sweep: pivots from the true incoming phi, z'' with zero inflow.
     const size_t ncol = (size_t)o.nx * o.ny;
-    double phi = (s > 0) ? o.phib[(size_t)(s - 1) * ncol + (size_t)j * o.nx + ic] : 0.0;
+    double phi = (s > 0 && active) ? o.phib[(size_t)(s - 1) * ncol + (size_t)j * o.nx + ic] : 0.0;
     double zpp = 0.0, mu = 1.0;
 #pragma unroll
     for (int t = 0; t < L; ++t) {
         if (t < len) {
-            const int k = k0 + t;
-            const double lo = o.az[k], up = o.az[k + 1];
+            const double lo = face(t), up = face(t + 1);
             const double inv = 1.0 / thomas_pivot(o.delta, aT, lo, up, phi);
             iD[t] = inv;
             phi = -up * inv;
@@ -220,19 +246,21 @@ __global__ __launch_bounds__(1024) void k_column_solve(const double *__restrict_
             iD[t] = 0.0;
         }
     }
-    sh_a[s][lane] = zpp;
-    sh_b[s][lane] = mu;
+    if (active) {
+        sh_a[s * C + c] = zpp;
+        sh_b[s * C + c] = mu;
+    }
     __syncthreads();
     double zin = 0.0;
-    for (int w = 0; w < s; ++w)
-        zin = sh_a[w][lane] + sh_b[w][lane] * zin;
+    for (int w = 0; w < s && active; ++w)
+        zin = sh_a[w * C + c] + sh_b[w * C + c] * zin;
 
     // Forward sweep again with the true inflow: z'_k of the serial algorithm.
     double prev = zin;
 #pragma unroll
     for (int t = 0; t < L; ++t) {
         if (t < len) {
-            const double lo = o.az[k0 + t];
+            const double lo = face(t);
             prev = (rr[t] + lo * prev) * iD[t];
             zp[t] = prev;
         }
@@ -242,27 +270,30 @@ __global__ __launch_bounds__(1024) void k_column_solve(const double *__restrict_
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
         if (t < len) {
-            const double up = o.az[k0 + t + 1];
+            const double up = face(t + 1);
             const double ph = -up * iD[t];
             znext = zp[t] - ph * znext;
             H = -ph * H;
             zp[t] = znext;
         }
     }
-    __syncthreads();   // every wave has finished reading the first scan
-    sh_a[s][lane] = znext;   // zh at the segment's first level
-    sh_b[s][lane] = H;       // response of that level to the value above
+    __syncthreads();   // every thread has finished reading the first scan
+    if (active) {
+        sh_a[s * C + c] = znext;   // zh at the segment's first level
+        sh_b[s * C + c] = H;       // response of that level to the value above
+    }
     __syncthreads();
     double ztop = 0.0;
-    for (int w = P - 1; w > s; --w)
-        ztop = sh_a[w][lane] + sh_b[w][lane] * ztop;
+    if (active)
+        for (int w = P - 1; w > s; --w)
+            ztop = sh_a[w * C + c] + sh_b[w * C + c] * ztop;
 
     double kap = 0.0;
     H = 1.0;
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
         if (t < len) {
-            const double up = o.az[k0 + t + 1];
+            const double up = face(t + 1);
             H = (up * iD[t]) * H;
             const double zv = zp[t] + ztop * H;
             kap += rr[t] * zv;
@@ -273,8 +304,8 @@ __global__ __launch_bounds__(1024) void k_column_solve(const double *__restrict_
     if (DOTS) {
         double v[2] = {r2, kap};
         double out[2];
-        block_partials<2>(v, s, P, lane, sh_red, out);
-        if (threadIdx.x == 0) {
+        block_sum<2>(v, sh_red, out);
+        if (tid == 0) {
             partials[2 * (size_t)tile + 0] = out[0];
             partials[2 * (size_t)tile + 1] = out[1];
         }
@@ -304,25 +335,52 @@ __global__ void k_setup_phib(Op o, double *__restrict__ phib)
 }
 
 // ---------------------------------------------------------------------------
-// Stencil passes (section 4.2, eq. (18)): the 7-point operator recomputed in
-// every cell from the per-column face coefficients and the per-level alpha_z.
-enum : int {
-    SP_FIRST = 0,   // p = z, q = A z, <p,q>             (first interleaved pass)
-    SP_FUSED = 1,   // x += alpha p, p = z + beta p, q = A z + beta q, <p,q> (Algorithm 2)
-    SP_APPLY = 2,   // y = A x
-    SP_RESID = 3,   // y = b - A x
-    SP_APPLY_DOT = 4 // y = A x, <x, y>  (standard PCG: q = A p, sigma)
+// Sweep passes.
+struct Sweep {
+    int i, j, k0, len, ic;
+    bool ok;
+    int tile;
 };
 
-template <int L, int MODE>
-__global__ __launch_bounds__(1024) void k_stencil(const double *__restrict__ zin,
-                                                  const double *__restrict__ bvec,
-                                                  double *__restrict__ u, double *__restrict__ p,
-                                                  double *__restrict__ y, Op o,
-                                                  const SolveState *__restrict__ st,
-                                                  double *__restrict__ partials)
+// Wave w of the workgroup sweeps levels [k0, k0 + len) of column i of row j.
+__device__ __forceinline__ Sweep sweep_of_thread(const Op &o, int Ls)
 {
-    __shared__ double sh_red[kMaxP][4];
+    Sweep sw;
+    sw.tile = tile_of_block(blockIdx.x, gridDim.x);
+    const int kt = sw.tile % o.nkt;
+    const int r = sw.tile / o.nkt;
+    sw.j = r % o.ny;
+    const int it = r / o.ny;
+    sw.i = it * kWave + (threadIdx.x & (kWave - 1));
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    sw.k0 = (kt * o.Ws + w) * Ls;
+    sw.len = max(0, min(Ls, o.nz - sw.k0));
+    sw.ok = sw.i < o.nx;
+    sw.ic = sw.ok ? sw.i : o.nx - 1;
+    return sw;
+}
+
+enum : int {
+    SP_FIRST = 0,     // p = z, q = A z, <p,q>             (first interleaved pass)
+    SP_FUSED = 1,     // x += alpha p, p = z + beta p, q = A z + beta q, <p,q> (Algorithm 2)
+    SP_APPLY = 2,     // y = A x
+    SP_RESID = 3,     // y = b - A x
+    SP_APPLY_DOT = 4  // y = A x, <x, y>  (standard PCG: q = A p, sigma)
+};
+
+// Stencil passes (section 4.2, eq. (18)): the 7-point operator recomputed in
+// every cell from the column's face coefficients and the level's alpha_z.
+// Block: 64 * Ws threads.
+template <int Ls, int MODE>
+__global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restrict__ zin,
+                                                         const double *__restrict__ bvec,
+                                                         double *__restrict__ u,
+                                                         double *__restrict__ p,
+                                                         double *__restrict__ y, Op o,
+                                                         const SolveState *__restrict__ st,
+                                                         double *__restrict__ partials)
+{
+    __shared__ double sh_red[kMaxThreads / kWave][1];
     double alpha = 0.0, beta = 0.0;
     bool fixup_only = false;
     if (MODE == SP_FIRST || MODE == SP_FUSED || MODE == SP_APPLY_DOT) {
@@ -334,127 +392,105 @@ __global__ __launch_bounds__(1024) void k_stencil(const double *__restrict__ zin
         alpha = st->alpha;
         beta = st->beta;
     }
-    const int lane = threadIdx.x & (kWave - 1);
-    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tile = tile_of_block(blockIdx.x, gridDim.x);
-    const int it = tile / o.ny;
-    const int j = tile - it * o.ny;
-    const int i = it * kWave + lane;
-    const bool ok = i < o.nx;
-    const int ic = ok ? i : o.nx - 1;
-    const int k0 = s * L;
-    const int len = min(L, o.nz - k0);
+    const Sweep sw = sweep_of_thread(o, Ls);
     const size_t ks = (size_t)o.nx;
-    const size_t base = lin(o, ic, j, 0);
+    const size_t base = lin(o, sw.ic, sw.j, 0);
 
     if (MODE == SP_FUSED && fixup_only) {
         // The stop test passed in this iteration: only the pending update
         // x += alpha p of the last step remains (Algorithm 1 exits before it).
-        if (ok) {
-            for (int t = 0; t < len; ++t) {
-                const size_t l = base + (size_t)(k0 + t) * ks;
+        if (sw.ok) {
+            for (int t = 0; t < sw.len; ++t) {
+                const size_t l = base + (size_t)(sw.k0 + t) * ks;
                 u[l] = u[l] + alpha * p[l];
             }
         }
         return;
     }
 
-    const Faces f = column_faces(o, ic, j);
-    const int ip = (ic + 1 == o.nx) ? 0 : ic + 1;
-    const int im = (ic == 0) ? o.nx - 1 : ic - 1;
-    const int jp = (j + 1 == o.ny) ? 0 : j + 1;
-    const int jm = (j == 0) ? o.ny - 1 : j - 1;
-    const size_t bxp = lin(o, ip, j, 0), bxm = lin(o, im, j, 0);
-    const size_t byp = lin(o, ic, jp, 0), bym = lin(o, ic, jm, 0);
-
     double acc = 0.0;
-    double zc = zin[base + (size_t)k0 * ks];
-    double zm = (k0 > 0) ? zin[base + (size_t)(k0 - 1) * ks] : zc;
+    if (sw.len > 0) {
+        const Faces f = column_faces(o, sw.ic, sw.j);
+        const int ip = (sw.ic + 1 == o.nx) ? 0 : sw.ic + 1;
+        const int im = (sw.ic == 0) ? o.nx - 1 : sw.ic - 1;
+        const int jp = (sw.j + 1 == o.ny) ? 0 : sw.j + 1;
+        const int jm = (sw.j == 0) ? o.ny - 1 : sw.j - 1;
+        const size_t bxp = lin(o, ip, sw.j, 0), bxm = lin(o, im, sw.j, 0);
+        const size_t byp = lin(o, sw.ic, jp, 0), bym = lin(o, sw.ic, jm, 0);
+        double zc = zin[base + (size_t)sw.k0 * ks];
+        double zm = (sw.k0 > 0) ? zin[base + (size_t)(sw.k0 - 1) * ks] : zc;
 #pragma unroll 4
-    for (int t = 0; t < len; ++t) {
-        const int k = k0 + t;
-        const size_t off = (size_t)k * ks;
-        const double zn = (k + 1 < o.nz) ? zin[base + off + ks] : zc;
-        const double lo = o.az[k], up = o.az[k + 1];
-        double Az = o.delta * zc;
-        Az += f.xp * (zc - zin[bxp + off]);
-        Az += f.xm * (zc - zin[bxm + off]);
-        Az += f.yp * (zc - zin[byp + off]);
-        Az += f.ym * (zc - zin[bym + off]);
-        Az += up * (zc - zn);
-        Az += lo * (zc - zm);
-        const size_t l = base + off;
-        if (MODE == SP_FIRST) {
-            if (ok) {
-                p[l] = zc;
-                y[l] = Az;
-                acc += zc * Az;
+        for (int t = 0; t < sw.len; ++t) {
+            const int k = sw.k0 + t;
+            const size_t off = (size_t)k * ks;
+            const double zn = (k + 1 < o.nz) ? zin[base + off + ks] : zc;
+            const double lo = o.az[k], up = o.az[k + 1];
+            double Az = o.delta * zc;
+            Az += f.xp * (zc - zin[bxp + off]);
+            Az += f.xm * (zc - zin[bxm + off]);
+            Az += f.yp * (zc - zin[byp + off]);
+            Az += f.ym * (zc - zin[bym + off]);
+            Az += up * (zc - zn);
+            Az += lo * (zc - zm);
+            const size_t l = base + off;
+            if (sw.ok) {
+                if (MODE == SP_FIRST) {
+                    p[l] = zc;
+                    y[l] = Az;
+                    acc += zc * Az;
+                } else if (MODE == SP_FUSED) {
+                    const double po = p[l];
+                    const double qo = y[l];
+                    u[l] = u[l] + alpha * po;
+                    const double pn = zc + beta * po;
+                    const double qn = Az + beta * qo;
+                    p[l] = pn;
+                    y[l] = qn;
+                    acc += pn * qn;
+                } else if (MODE == SP_APPLY) {
+                    y[l] = Az;
+                } else if (MODE == SP_RESID) {
+                    y[l] = bvec[l] - Az;
+                } else {   // SP_APPLY_DOT
+                    y[l] = Az;
+                    acc += zc * Az;
+                }
             }
-        } else if (MODE == SP_FUSED) {
-            if (ok) {
-                const double po = p[l];
-                const double qo = y[l];
-                u[l] = u[l] + alpha * po;
-                const double pn = zc + beta * po;
-                const double qn = Az + beta * qo;
-                p[l] = pn;
-                y[l] = qn;
-                acc += pn * qn;
-            }
-        } else if (MODE == SP_APPLY) {
-            if (ok)
-                y[l] = Az;
-        } else if (MODE == SP_RESID) {
-            if (ok)
-                y[l] = bvec[l] - Az;
-        } else {   // SP_APPLY_DOT
-            if (ok) {
-                y[l] = Az;
-                acc += zc * Az;
-            }
+            zm = zc;
+            zc = zn;
         }
-        zm = zc;
-        zc = zn;
     }
     if (MODE == SP_FIRST || MODE == SP_FUSED || MODE == SP_APPLY_DOT) {
         double v[1] = {acc};
         double out[1];
-        block_partials<1>(v, s, o.P, lane, sh_red, out);
+        block_sum<1>(v, sh_red, out);
         if (threadIdx.x == 0)
-            partials[2 * (size_t)tile] = out[0];
+            partials[2 * (size_t)sw.tile] = out[0];
     }
 }
 
-// ---------------------------------------------------------------------------
-// Vector passes of the standard PCG loop, each fused with its dot product.
+// Vector passes of the standard PCG loop, each fused with its dot product
+// (sweep geometry).
 // x += alpha p ; r -= alpha q ; <r,r>
-template <int L>
-__global__ __launch_bounds__(1024) void k_update_xr(double *__restrict__ x,
-                                                    const double *__restrict__ p,
-                                                    double *__restrict__ r,
-                                                    const double *__restrict__ q, Op o,
-                                                    const SolveState *__restrict__ st,
-                                                    double *__restrict__ partials)
+template <int Ls>
+__global__ __launch_bounds__(kMaxThreads) void k_update_xr(double *__restrict__ x,
+                                                           const double *__restrict__ p,
+                                                           double *__restrict__ r,
+                                                           const double *__restrict__ q, Op o,
+                                                           const SolveState *__restrict__ st,
+                                                           double *__restrict__ partials)
 {
-    __shared__ double sh_red[kMaxP][4];
+    __shared__ double sh_red[kMaxThreads / kWave][1];
     if (st->done)
         return;
     const double alpha = st->alpha;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tile = tile_of_block(blockIdx.x, gridDim.x);
-    const int it = tile / o.ny;
-    const int j = tile - it * o.ny;
-    const int i = it * kWave + lane;
-    const bool ok = i < o.nx;
-    const int k0 = s * L;
-    const int len = min(L, o.nz - k0);
+    const Sweep sw = sweep_of_thread(o, Ls);
     double acc = 0.0;
-    if (ok) {
-        const size_t base = lin(o, i, j, 0);
+    if (sw.ok) {
+        const size_t base = lin(o, sw.i, sw.j, 0);
 #pragma unroll 4
-        for (int t = 0; t < len; ++t) {
-            const size_t l = base + (size_t)(k0 + t) * o.nx;
+        for (int t = 0; t < sw.len; ++t) {
+            const size_t l = base + (size_t)(sw.k0 + t) * o.nx;
             x[l] = x[l] + alpha * p[l];
             const double rn = r[l] - alpha * q[l];
             r[l] = rn;
@@ -463,42 +499,66 @@ __global__ __launch_bounds__(1024) void k_update_xr(double *__restrict__ x,
     }
     double v[1] = {acc};
     double out[1];
-    block_partials<1>(v, s, o.P, lane, sh_red, out);
+    block_sum<1>(v, sh_red, out);
     if (threadIdx.x == 0)
-        partials[2 * (size_t)tile] = out[0];
+        partials[2 * (size_t)sw.tile] = out[0];
 }
 
 // p = z + beta p   (p = z on the first step)
-template <int L>
-__global__ __launch_bounds__(1024) void k_update_p(double *__restrict__ p,
-                                                   const double *__restrict__ z, Op o,
-                                                   const SolveState *__restrict__ st, int first)
+template <int Ls>
+__global__ __launch_bounds__(kMaxThreads) void k_update_p(double *__restrict__ p,
+                                                          const double *__restrict__ z, Op o,
+                                                          const SolveState *__restrict__ st,
+                                                          int first)
 {
     if (st->done)
         return;
     const double beta = st->beta;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tile = tile_of_block(blockIdx.x, gridDim.x);
-    const int it = tile / o.ny;
-    const int j = tile - it * o.ny;
-    const int i = it * kWave + lane;
-    if (i >= o.nx)
+    const Sweep sw = sweep_of_thread(o, Ls);
+    if (!sw.ok)
         return;
-    const int k0 = s * L;
-    const int len = min(L, o.nz - k0);
-    const size_t base = lin(o, i, j, 0);
+    const size_t base = lin(o, sw.i, sw.j, 0);
 #pragma unroll 4
-    for (int t = 0; t < len; ++t) {
-        const size_t l = base + (size_t)(k0 + t) * o.nx;
+    for (int t = 0; t < sw.len; ++t) {
+        const size_t l = base + (size_t)(sw.k0 + t) * o.nx;
         p[l] = first ? z[l] : z[l] + beta * p[l];
     }
 }
 
 // ---------------------------------------------------------------------------
-// Reductions of the per-workgroup partial sums (fixed order: deterministic)
-// and the scalar recurrences of PCG (section 4.3, Algorithm 1).
+// Reductions of the per-workgroup partial sums (entries are pairs; fixed
+// order: deterministic) and the scalar recurrences of PCG (section 4.3,
+// Algorithm 1).
 constexpr int kRedThreads = 256;
+
+// Stage 1: block b sums pairs [b*per, min(n, (b+1)*per)) into out[2b], out[2b+1].
+__global__ __launch_bounds__(kRedThreads) void k_sum_stage(const double *__restrict__ in, int n,
+                                                           int per, double *__restrict__ out)
+{
+    __shared__ double sh[2][kRedThreads];
+    const int tid = threadIdx.x;
+    const int lo = blockIdx.x * per;
+    const int hi = min(n, lo + per);
+    double a0 = 0.0, a1 = 0.0;
+    for (int t = lo + tid; t < hi; t += kRedThreads) {
+        a0 += in[2 * (size_t)t];
+        a1 += in[2 * (size_t)t + 1];
+    }
+    sh[0][tid] = a0;
+    sh[1][tid] = a1;
+    __syncthreads();
+    for (int w = kRedThreads / 2; w > 0; w >>= 1) {
+        if (tid < w) {
+            sh[0][tid] += sh[0][tid + w];
+            sh[1][tid] += sh[1][tid + w];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        out[2 * (size_t)blockIdx.x] = sh[0][0];
+        out[2 * (size_t)blockIdx.x + 1] = sh[1][0];
+    }
+}
 
 template <int NV>
 __device__ __forceinline__ void sum_partials(const double *__restrict__ partials, int nparts,

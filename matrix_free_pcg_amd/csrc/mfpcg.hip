@@ -6,6 +6,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -31,8 +33,9 @@ struct pcg_handle {
     int device = 0;
     hipStream_t stream = nullptr;
     Op op{};
-    int ntx = 0;           // tiles along i
-    int ntiles = 0;        // workgroups of every grid pass
+    int col_tiles = 0;     // workgroups of a column pass
+    int col_threads = 0;   // threads per column-pass workgroup
+    int pt_tiles = 0;      // workgroups of a point pass
     size_t n = 0;          // nx*ny*nz
     double *d_az = nullptr, *d_ah = nullptr, *d_phib = nullptr;
     HostStatus *h_status = nullptr;   // pinned host memory written by the reduce kernels
@@ -69,28 +72,64 @@ int fail(pcg_handle *h, int code, const char *fmt, ...)
 
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-// Column segment length: the smallest of 4, 8, 16, 32 that splits nz into at
-// most 8 segments (16 for nz > 128).
-int choose_L(int nz)
+// Column-pass geometry: C columns per workgroup and the segment length L
+// (default: the smallest of 8, 16, 32 with C * ceil(nz / L) <= 1024).
+// Sweep-pass geometry: Ls levels per wave, Ws waves per workgroup (default
+// Ls = 4, Ws = min(8, ceil(nz / 4))).  MFPCG_COL_L, MFPCG_COL_C, MFPCG_ST_L
+// and MFPCG_ST_W override the choice (tuning).
+int env_int(const char *name, int dflt)
 {
-    if (nz <= 32) return 4;
-    if (nz <= 64) return 8;
-    if (nz <= 256) return 16;
-    return 32;
+    const char *v = getenv(name);
+    return (v && *v) ? atoi(v) : dflt;
 }
 
+struct Geometry {
+    int L, C, Ls, Ws;
+};
+
+bool choose_geometry(int nz, Geometry *g, std::string *why)
+{
+    g->C = env_int("MFPCG_COL_C", 64);
+    if (g->C != 32 && g->C != 64) { *why = "MFPCG_COL_C must be 32 or 64"; return false; }
+    int l = env_int("MFPCG_COL_L", 0);
+    if (l == 0) {
+        for (int cand : {8, 16, 32}) {
+            if ((size_t)g->C * ((nz + cand - 1) / cand) <= (size_t)kMaxThreads) { l = cand; break; }
+        }
+        if (l == 0) { *why = "nz too large for the column solve"; return false; }
+    }
+    if (l != 4 && l != 8 && l != 16 && l != 32) { *why = "MFPCG_COL_L must be 4, 8, 16 or 32"; return false; }
+    if ((size_t)g->C * ((nz + l - 1) / l) > (size_t)kMaxThreads) { *why = "column workgroup exceeds 1024 threads"; return false; }
+    g->L = l;
+    g->Ls = env_int("MFPCG_ST_L", 4);
+    if (g->Ls != 4 && g->Ls != 8 && g->Ls != 16 && g->Ls != 32) { *why = "MFPCG_ST_L must be 4, 8, 16 or 32"; return false; }
+    const int need = (nz + g->Ls - 1) / g->Ls;
+    g->Ws = env_int("MFPCG_ST_W", std::min(8, need));
+    if (g->Ws < 1 || g->Ws > 16) { *why = "MFPCG_ST_W must be in 1..16"; return false; }
+    return true;
+}
+
+// Partial sums: a pass writes one pair per workgroup; above kDirect pairs a
+// first stage folds them per 1024 into at most kStageMax pairs.
+constexpr int kDirect = 4096;
+constexpr int kStagePer = 1024;
+
+int stage_blocks(int nparts) { return nparts <= kDirect ? 0 : (nparts + kStagePer - 1) / kStagePer; }
+
 struct Workspace {
-    double *r, *z, *p, *q, *partials, *hist;
+    double *r, *z, *p, *q, *partials, *stage, *hist;
     SolveState *state;
 };
 
 size_t workspace_layout(const pcg_handle *h, int32_t maxit, char *base, Workspace *w)
 {
     const size_t vec = align256(h->n * sizeof(double));
+    const int np = std::max(h->col_tiles, h->pt_tiles);
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     size_t o_r = take(vec), o_z = take(vec), o_p = take(vec), o_q = take(vec);
-    size_t o_part = take((size_t)h->ntiles * 2 * sizeof(double));
+    size_t o_part = take((size_t)np * 2 * sizeof(double));
+    size_t o_stage = take((size_t)std::max(1, stage_blocks(np)) * 2 * sizeof(double));
     size_t o_state = take(sizeof(SolveState));
     size_t o_hist = take((size_t)(maxit + 1) * sizeof(double));
     if (w && base) {
@@ -99,10 +138,25 @@ size_t workspace_layout(const pcg_handle *h, int32_t maxit, char *base, Workspac
         w->p = (double *)(base + o_p);
         w->q = (double *)(base + o_q);
         w->partials = (double *)(base + o_part);
+        w->stage = (double *)(base + o_stage);
         w->state = (SolveState *)(base + o_state);
         w->hist = (double *)(base + o_hist);
     }
     return off;
+}
+
+// Fold `n` partial pairs to a count the single-workgroup reduce kernels read
+// quickly; returns the array they should read and its length.
+const double *fold_partials(pcg_handle *h, const Workspace &w, int n, int *n_out)
+{
+    const int nb = stage_blocks(n);
+    if (nb == 0) {
+        *n_out = n;
+        return w.partials;
+    }
+    k_sum_stage<<<dim3(nb), dim3(kRedThreads), 0, h->stream>>>(w.partials, n, kStagePer, w.stage);
+    *n_out = nb;
+    return w.stage;
 }
 
 // ---- per-kernel event timing ------------------------------------------------
@@ -158,49 +212,59 @@ void drain_events(pcg_handle *h, int skip_kid = -1, int skip_tag = -2)
     h->pending.clear();
 }
 
-// ---- launch helpers (template dispatch on the segment length) ---------------
-template <int L>
-void launch_column(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
-                   const SolveState *st, int first, double *partials, bool update, bool dots)
+// ---- launch helpers (template dispatch on the column geometry) ---------------
+template <int L, int C>
+void launch_column_lc(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
+                      const SolveState *st, int first, double *partials, bool update, bool dots)
 {
-    dim3 grid(h->ntiles), block(kWave * h->op.P);
+    dim3 grid(h->col_tiles), block(h->col_threads);
     if (update)
-        k_column_solve<L, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
+        k_column_solve<L, C, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
     else if (dots)
-        k_column_solve<L, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
+        k_column_solve<L, C, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
     else
-        k_column_solve<L, false, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
+        k_column_solve<L, C, false, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
+}
+
+template <int C>
+void launch_column_c(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
+                     const SolveState *st, int first, double *partials, bool update, bool dots)
+{
+    switch (h->op.L) {
+    case 4: launch_column_lc<4, C>(h, rin, q, rout, z, st, first, partials, update, dots); break;
+    case 8: launch_column_lc<8, C>(h, rin, q, rout, z, st, first, partials, update, dots); break;
+    case 16: launch_column_lc<16, C>(h, rin, q, rout, z, st, first, partials, update, dots); break;
+    default: launch_column_lc<32, C>(h, rin, q, rout, z, st, first, partials, update, dots); break;
+    }
 }
 
 void column(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
             const SolveState *st, int first, double *partials, bool update, bool dots)
 {
-    switch (h->op.L) {
-    case 4: launch_column<4>(h, rin, q, rout, z, st, first, partials, update, dots); break;
-    case 8: launch_column<8>(h, rin, q, rout, z, st, first, partials, update, dots); break;
-    case 16: launch_column<16>(h, rin, q, rout, z, st, first, partials, update, dots); break;
-    default: launch_column<32>(h, rin, q, rout, z, st, first, partials, update, dots); break;
-    }
+    if (h->op.C == 64)
+        launch_column_c<64>(h, rin, q, rout, z, st, first, partials, update, dots);
+    else
+        launch_column_c<32>(h, rin, q, rout, z, st, first, partials, update, dots);
 }
 
-template <int L>
+template <int Ls>
 void launch_stencil(pcg_handle *h, int mode, const double *zin, const double *b, double *u,
                     double *p, double *y, const SolveState *st, double *partials)
 {
-    dim3 grid(h->ntiles), block(kWave * h->op.P);
+    dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
     switch (mode) {
-    case SP_FIRST: k_stencil<L, SP_FIRST><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
-    case SP_FUSED: k_stencil<L, SP_FUSED><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
-    case SP_APPLY: k_stencil<L, SP_APPLY><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
-    case SP_RESID: k_stencil<L, SP_RESID><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
-    default: k_stencil<L, SP_APPLY_DOT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
+    case SP_FIRST: k_stencil<Ls, SP_FIRST><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
+    case SP_FUSED: k_stencil<Ls, SP_FUSED><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
+    case SP_APPLY: k_stencil<Ls, SP_APPLY><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
+    case SP_RESID: k_stencil<Ls, SP_RESID><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
+    default: k_stencil<Ls, SP_APPLY_DOT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
     }
 }
 
 void stencil(pcg_handle *h, int mode, const double *zin, const double *b, double *u, double *p,
              double *y, const SolveState *st, double *partials)
 {
-    switch (h->op.L) {
+    switch (h->op.Ls) {
     case 4: launch_stencil<4>(h, mode, zin, b, u, p, y, st, partials); break;
     case 8: launch_stencil<8>(h, mode, zin, b, u, p, y, st, partials); break;
     case 16: launch_stencil<16>(h, mode, zin, b, u, p, y, st, partials); break;
@@ -208,35 +272,38 @@ void stencil(pcg_handle *h, int mode, const double *zin, const double *b, double
     }
 }
 
-template <int L>
-void launch_update_xr(pcg_handle *h, double *x, const double *p, double *r, const double *q,
-                      const SolveState *st, double *partials)
+template <int Ls>
+void launch_vec(pcg_handle *h, int which, double *x, const double *p, double *r, const double *q,
+                const SolveState *st, double *partials, int first)
 {
-    k_update_xr<L><<<dim3(h->ntiles), dim3(kWave * h->op.P), 0, h->stream>>>(x, p, r, q, h->op, st, partials);
+    dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
+    if (which == 0)
+        k_update_xr<Ls><<<grid, block, 0, h->stream>>>(x, p, r, q, h->op, st, partials);
+    else
+        k_update_p<Ls><<<grid, block, 0, h->stream>>>(r, q, h->op, st, first);
 }
-template <int L>
-void launch_update_p(pcg_handle *h, double *p, const double *z, const SolveState *st, int first)
+
+void vec(pcg_handle *h, int which, double *x, const double *p, double *r, const double *q,
+         const SolveState *st, double *partials, int first)
 {
-    k_update_p<L><<<dim3(h->ntiles), dim3(kWave * h->op.P), 0, h->stream>>>(p, z, h->op, st, first);
+    switch (h->op.Ls) {
+    case 4: launch_vec<4>(h, which, x, p, r, q, st, partials, first); break;
+    case 8: launch_vec<8>(h, which, x, p, r, q, st, partials, first); break;
+    case 16: launch_vec<16>(h, which, x, p, r, q, st, partials, first); break;
+    default: launch_vec<32>(h, which, x, p, r, q, st, partials, first); break;
+    }
 }
+
 void update_xr(pcg_handle *h, double *x, const double *p, double *r, const double *q,
                const SolveState *st, double *partials)
 {
-    switch (h->op.L) {
-    case 4: launch_update_xr<4>(h, x, p, r, q, st, partials); break;
-    case 8: launch_update_xr<8>(h, x, p, r, q, st, partials); break;
-    case 16: launch_update_xr<16>(h, x, p, r, q, st, partials); break;
-    default: launch_update_xr<32>(h, x, p, r, q, st, partials); break;
-    }
+    vec(h, 0, x, p, r, q, st, partials, 0);
 }
+
+// p = z + beta p: the second kernel takes (p, z) in the (r, q) slots.
 void update_p(pcg_handle *h, double *p, const double *z, const SolveState *st, int first)
 {
-    switch (h->op.L) {
-    case 4: launch_update_p<4>(h, p, z, st, first); break;
-    case 8: launch_update_p<8>(h, p, z, st, first); break;
-    case 16: launch_update_p<16>(h, p, z, st, first); break;
-    default: launch_update_p<32>(h, p, z, st, first); break;
-    }
+    vec(h, 1, nullptr, nullptr, p, z, st, nullptr, first);
 }
 
 int check_vectors(pcg_handle *h, const void *a, const void *b, const char *what)
@@ -357,9 +424,16 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
         return fail(nullptr, PCG_ERR_INVALID, "pcg_create: grid %d x %d x %d must be positive", nx, ny, nz);
     if (nz > 512)
         return fail(nullptr, PCG_ERR_UNSUPPORTED, "pcg_create: nz = %d > 512 is not supported", nz);
+    Geometry g{};
+    std::string why;
+    if (!choose_geometry(nz, &g, &why))
+        return fail(nullptr, PCG_ERR_UNSUPPORTED, "pcg_create: %s (nz = %d)", why.c_str(), nz);
+    const int L = g.L, C = g.C;
     const size_t ntx = ((size_t)nx + kWave - 1) / kWave;
-    if (ntx * (size_t)ny > (size_t)0x7fffffff)
-        return fail(nullptr, PCG_ERR_UNSUPPORTED, "pcg_create: too many columns");
+    const size_t ntc = ((size_t)nx + C - 1) / C;
+    const size_t nkt = ((size_t)nz + (size_t)g.Ls * g.Ws - 1) / ((size_t)g.Ls * g.Ws);
+    if (ntx * nkt * (size_t)ny > (size_t)0x7fffffff || ntc * (size_t)ny > (size_t)0x7fffffff)
+        return fail(nullptr, PCG_ERR_UNSUPPORTED, "pcg_create: too many tiles");
     if (!(c->delta > 0.0) || !std::isfinite(c->delta))
         return fail(nullptr, PCG_ERR_INVALID, "pcg_create: delta must be finite and > 0");
     if (!c->alpha_z_face)
@@ -401,16 +475,21 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
         return bail(PCG_ERR_HIP);
     }
     h->stream = (hipStream_t)hip_stream;
-    const int L = choose_L(nz);
     const int P = (nz + L - 1) / L;
-    h->ntx = (int)ntx;
-    h->ntiles = (int)(ntx * ny);
+    h->col_tiles = (int)(ntc * ny);
+    h->col_threads = ((C * P + kWave - 1) / kWave) * kWave;
+    h->pt_tiles = (int)(ntx * nkt * ny);
     h->n = ncol * (size_t)nz;
     h->op.nx = nx;
     h->op.ny = ny;
     h->op.nz = nz;
     h->op.L = L;
     h->op.P = P;
+    h->op.C = C;
+    h->op.ntc = (int)ntc;
+    h->op.Ls = g.Ls;
+    h->op.Ws = g.Ws;
+    h->op.nkt = (int)nkt;
     h->op.delta = c->delta;
     hipError_t e;
     if ((e = hipMalloc(&h->d_az, sizeof(double) * (nz + 1))) != hipSuccess ||
@@ -524,7 +603,6 @@ int pcg_solve(pcg_handle *h, const double *b, double *x, double tol, int32_t max
     HostStatus *hs = nullptr;
     HIP_TRY(h, hipHostGetDevicePointer((void **)&hs, h->h_status, 0));
     h->h_status->done = 0;
-    const int np = h->ntiles;
     k_init_state<<<1, 64, 0, h->stream>>>(w.state);
     // a2: r0 = b - A x0
     stencil(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
@@ -532,13 +610,16 @@ int pcg_solve(pcg_handle *h, const double *b, double *x, double tol, int32_t max
     HIP_TRY(h, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
     int last = 0;
     for (int k = 0; k <= maxit; ++k) {
+        int nred = 0;
+        const double *red = nullptr;
         // a3: r -= alpha q; z = M^{-1} r; partial <r,r>, <r,z>   (Algorithm 3)
         {
             Timed t(h, PCG_KID_FUSED_PREC, k);
             column(h, w.r, w.q, w.r, w.z, w.state, k == 0, w.partials, true, true);
         }
         // a4: ||r_k||, stop test, beta
-        k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state, w.hist, k, maxit, tol, hs);
+        red = fold_partials(h, w, h->col_tiles, &nred);
+        k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, w.hist, k, maxit, tol, hs);
         hipEventRecord(ev, h->stream);
         // a5: x += alpha p; p = z + beta p; q = A z + beta q; partial <p,q>  (Algorithm 2)
         //     (only x += alpha p once the stop test has passed: a7)
@@ -547,7 +628,8 @@ int pcg_solve(pcg_handle *h, const double *b, double *x, double tol, int32_t max
             stencil(h, k == 0 ? SP_FIRST : SP_FUSED, w.z, nullptr, x, w.p, w.q, w.state, w.partials);
         }
         // a6: sigma, alpha
-        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state, k);
+        red = fold_partials(h, w, h->pt_tiles, &nred);
+        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) {
             hipEventDestroy(ev);
@@ -578,16 +660,18 @@ int pcg_solve_standard(pcg_handle *h, const double *b, double *x, double tol, in
     HostStatus *hs = nullptr;
     HIP_TRY(h, hipHostGetDevicePointer((void **)&hs, h->h_status, 0));
     h->h_status->done = 0;
-    const int np = h->ntiles;
     hipEvent_t ev = nullptr;
     HIP_TRY(h, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    int nred = 0;
+    const double *red = nullptr;
     k_init_state<<<1, 64, 0, h->stream>>>(w.state);
     stencil(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
     {
         Timed t(h, PCG_KID_PRECOND, 0);
         column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, false, true);
     }
-    k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state, w.hist, 0, maxit, tol, hs);
+    red = fold_partials(h, w, h->col_tiles, &nred);
+    k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, w.hist, 0, maxit, tol, hs);
     {
         Timed t(h, PCG_KID_VECTOR, 0);
         update_p(h, w.p, w.z, w.state, 1);
@@ -600,18 +684,21 @@ int pcg_solve_standard(pcg_handle *h, const double *b, double *x, double tol, in
             Timed t(h, PCG_KID_APPLY_A, k);
             stencil(h, SP_APPLY_DOT, w.p, nullptr, nullptr, nullptr, w.q, w.state, w.partials);
         }
-        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state, k - 1);
+        red = fold_partials(h, w, h->pt_tiles, &nred);
+        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k - 1);
         {   // x += alpha p ; r -= alpha q ; <r,r>
             Timed t(h, PCG_KID_VECTOR, k);
             update_xr(h, x, w.p, w.r, w.q, w.state, w.partials);
         }
-        k_reduce_rr<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state, w.hist, k, maxit, tol, hs);
+        red = fold_partials(h, w, h->pt_tiles, &nred);
+        k_reduce_rr<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, w.hist, k, maxit, tol, hs);
         hipEventRecord(ev, h->stream);
         {   // z = M^{-1} r ; kappa = <r,z>
             Timed t(h, PCG_KID_PRECOND, k);
             column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, false, true);
         }
-        k_reduce_kappa<<<1, kRedThreads, 0, h->stream>>>(w.partials, np, w.state);
+        red = fold_partials(h, w, h->col_tiles, &nred);
+        k_reduce_kappa<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state);
         {   // p = z + beta p
             Timed t(h, PCG_KID_VECTOR, k);
             update_p(h, w.p, w.z, w.state, 0);
