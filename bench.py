@@ -36,8 +36,30 @@ BYTES_PER_POINT = {
 }
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fused_passes_varying-1024x1024x128.json")
+KERNEL_SOURCE = os.path.join(ROOT, "matrix_free_pcg_amd", "csrc", "kernels.hpp")
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when
+    that summary was taken on a different kernel source or workload."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if rec.get("source_sha256") != sha or workload not in os.path.basename(TRAFFIC_FILE):
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else int(round(k["traffic_bytes"]))
 
 
 def parse():
@@ -174,7 +196,9 @@ def main():
     if dom is not None:
         ach = kern[dom]["GBps"]
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                    "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(dom, w.name),
+                    "traffic_unit": "bytes per launch", "kernel": dom,
                     "bytes_per_launch": kern[dom]["bytes_per_launch"],
                     "avg_launch_ms": round(kern[dom]["avg_ms"], 4)}
 
