@@ -67,7 +67,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="5 = explicit-vs-matrix-free comparison at 2048x2048x128 (50 fixed steps)")
     ap.add_argument("--variant", default="interleaved", choices=["interleaved", "standard"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
@@ -112,6 +113,62 @@ def cpu_baseline(w, steps):
             "s_per_iteration": round(per, 3)}
 
 
+CSR_BYTES_PER_ROW = 108   # 7 x (8 B value + 4 B column) + row pointer + x + y (8 B each)
+
+
+def explicit_comparison(args):
+    """2048x2048x128: 50 fixed CG steps matrix-free (interleaved) and explicit
+    (CSR matrix + stored column matrices, standard loop), and the isolated
+    operator application both ways.  One JSON line."""
+    import torch
+    import matrix_free_pcg_amd as mf
+    from matrix_free_pcg_amd import workloads as W
+    dev = torch.device("cuda:0")
+    t = time.perf_counter()
+    w = W.make_workload(5)
+    prob = w.problem
+    n = prob.n
+    log(f"[bench] {w.name}: inputs generated in {time.perf_counter() - t:.1f}s")
+    b = torch.from_numpy(w.rhs).to(dev)
+    x = torch.zeros_like(b)
+    h = mf.pcg_create(prob, torch.cuda.current_stream())
+    t = time.perf_counter()
+    C = mf.pcg_csr_assemble(h)
+    tri = mf.pcg_tridiag_assemble(h)
+    torch.cuda.synchronize()
+    t_asm = time.perf_counter() - t
+    ws = torch.empty(mf.pcg_solve_workspace_bytes(h, w.maxit), dtype=torch.uint8, device=dev)
+    out = {"workload": w.name, "steps": w.maxit, "nnz": C.col.numel(), "csr_assembly_s": round(t_asm, 3)}
+    for name, fn in (("matrix_free", lambda: mf.pcg_solve(h, b, x, 0.0, w.maxit, ws)),
+                     ("explicit", lambda: mf.pcg_solve_csr(h, C, tri, b, x, 0.0, w.maxit, ws))):
+        x.zero_()
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            x.zero_()
+            res = fn()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        out[name] = {"s_per_solve": round(dt, 4), "iterations_per_s": round(w.maxit / dt, 2),
+                     "final_rel_res": res["final_rel_res"]}
+    y = torch.empty_like(b)
+    mf.pcg_profile_reset(h)
+    mf.pcg_profile_enable(h, True)
+    for _ in range(10):
+        mf.pcg_apply_A(h, b, y)
+        mf.pcg_csr_spmv(h, C, b, y)
+    ms_mf, n_mf = mf.pcg_profile_read(h, mf.PCG_KID_APPLY_A)
+    ms_csr, n_csr = mf.pcg_profile_read(h, mf.PCG_KID_CSR_SPMV)
+    mf.pcg_profile_enable(h, False)
+    a_mf, a_csr = ms_mf / n_mf, ms_csr / n_csr
+    out["spmv"] = {"matrix_free_ms": round(a_mf, 4), "matrix_free_GBps": round(16 * n / a_mf / 1e6, 1),
+                   "csr_ms": round(a_csr, 4), "csr_GBps": round(CSR_BYTES_PER_ROW * n / a_csr / 1e6, 1),
+                   "speedup_matrix_free": round(a_csr / a_mf, 2)}
+    mf.pcg_destroy(h)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -124,6 +181,10 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+
+    if args.config == 5:
+        explicit_comparison(args)
         return
 
     import matrix_free_pcg_amd as mf

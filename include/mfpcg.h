@@ -148,6 +148,47 @@ int pcg_solve_standard(pcg_handle *h, const double *b_dev, double *x_dev, double
                        int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
                        double *final_rel_res);
 
+/* ---- Explicit (matrix-stored) comparison path, section 6.2 ----------------
+ * The same operator assembled as a CSR matrix and the preconditioner's column
+ * matrices stored as three vectors, solved with the standard PCG loop.  Rows
+ * and vectors follow the field layout; a row holds the diagonal, its distinct
+ * horizontal neighbours and the vertical neighbours that exist, columns
+ * ascending.  Requires N < 2^31 (int32 column indices), else
+ * PCG_ERR_UNSUPPORTED.  All arrays are caller-owned device memory. */
+
+/* Number of stored entries of the CSR matrix (host computation). */
+int pcg_csr_nnz(const pcg_handle *h, int64_t *nnz);
+
+/* Assemble the CSR matrix on the device: row_ptr_dev (N+1 int64), col_dev
+ * (nnz int32), val_dev (nnz doubles).  Asynchronous. */
+int pcg_csr_assemble(pcg_handle *h, int64_t *row_ptr_dev, int32_t *col_dev, double *val_dev);
+
+/* y = A x with the assembled CSR matrix (one row per thread).  Asynchronous. */
+int pcg_csr_spmv(pcg_handle *h, const int64_t *row_ptr_dev, const int32_t *col_dev,
+                 const double *val_dev, const double *x_dev, double *y_dev);
+
+/* Assemble M's column matrices as tri_dev = [sub | diag | sup] (3N doubles,
+ * each in field layout; sub is 0 at k = 0 and sup at k = nz-1) and factor
+ * them (pcg_tridiag_factor).  Asynchronous. */
+int pcg_tridiag_assemble(pcg_handle *h, double *tri_dev);
+
+/* Compute the handle's segment-boundary multipliers of the stored column
+ * matrices tri_dev; call again after changing tri_dev.  Allocates a table of
+ * (ceil(nz/L)-1)*nx*ny doubles in the handle on first use.  Asynchronous. */
+int pcg_tridiag_factor(pcg_handle *h, const double *tri_dev);
+
+/* z = M^{-1} r with the stored column matrices (factored first).
+ * Asynchronous. */
+int pcg_tridiag_precond(pcg_handle *h, const double *tri_dev, const double *r_dev, double *z_dev);
+
+/* Standard PCG (section 4.1) with the CSR matrix and the stored column
+ * matrices; arguments and results as pcg_solve. */
+int pcg_solve_csr(pcg_handle *h, const int64_t *row_ptr_dev, const int32_t *col_dev,
+                  const double *val_dev, const double *tri_dev, const double *b_dev,
+                  double *x_dev, double tol, int32_t maxit, void *workspace_dev,
+                  size_t workspace_bytes, int32_t *iters_out, double *hist_host,
+                  int32_t *hist_len_out, double *final_rel_res);
+
 /* Per-kernel timing with HIP events on the handle's stream (off by default).
  * While enabled, every launch of the kernels below is bracketed by events;
  * pcg_profile_read returns the accumulated milliseconds and launch count of
@@ -157,7 +198,8 @@ int pcg_solve_standard(pcg_handle *h, const double *b_dev, double *x_dev, double
 #define PCG_KID_APPLY_A 2      /* stand-alone y = A x (and standard q = A p) */
 #define PCG_KID_PRECOND 3      /* stand-alone z = M^{-1} r (and standard)    */
 #define PCG_KID_VECTOR 4       /* standard-PCG vector updates               */
-#define PCG_KID_COUNT 5
+#define PCG_KID_CSR_SPMV 5     /* stand-alone CSR y = A x                    */
+#define PCG_KID_COUNT 6
 int pcg_profile_enable(pcg_handle *h, int32_t enable);
 int pcg_profile_reset(pcg_handle *h);
 int pcg_profile_read(const pcg_handle *h, int32_t kernel_id, double *ms_total,

@@ -31,12 +31,15 @@ PCG_KID_FUSED_SPMV = 1
 PCG_KID_APPLY_A = 2
 PCG_KID_PRECOND = 3
 PCG_KID_VECTOR = 4
-PCG_KID_COUNT = 5
+PCG_KID_CSR_SPMV = 5
+PCG_KID_COUNT = 6
 
 EXPORTED = [
     "pcg_create", "pcg_destroy", "pcg_set_stream", "pcg_apply_A", "pcg_precond",
     "pcg_solve_workspace_bytes", "pcg_solve", "pcg_solve_standard", "pcg_profile_enable",
     "pcg_profile_reset", "pcg_profile_read", "pcg_last_error", "pcg_version",
+    "pcg_csr_nnz", "pcg_csr_assemble", "pcg_csr_spmv", "pcg_tridiag_assemble",
+    "pcg_tridiag_factor", "pcg_tridiag_precond", "pcg_solve_csr",
 ]
 
 
@@ -111,6 +114,21 @@ def load():
         lib.pcg_last_error.restype = ctypes.c_char_p
         lib.pcg_version.argtypes = []
         lib.pcg_version.restype = ctypes.c_char_p
+        lib.pcg_csr_nnz.argtypes = [H, ctypes.POINTER(ctypes.c_int64)]
+        lib.pcg_csr_nnz.restype = ctypes.c_int
+        lib.pcg_csr_assemble.argtypes = [H, vp, vp, vp]
+        lib.pcg_csr_assemble.restype = ctypes.c_int
+        lib.pcg_csr_spmv.argtypes = [H, vp, vp, vp, vp, vp]
+        lib.pcg_csr_spmv.restype = ctypes.c_int
+        lib.pcg_tridiag_assemble.argtypes = [H, vp]
+        lib.pcg_tridiag_assemble.restype = ctypes.c_int
+        lib.pcg_tridiag_factor.argtypes = [H, vp]
+        lib.pcg_tridiag_factor.restype = ctypes.c_int
+        lib.pcg_tridiag_precond.argtypes = [H, vp, vp, vp]
+        lib.pcg_tridiag_precond.restype = ctypes.c_int
+        lib.pcg_solve_csr.argtypes = [H, vp, vp, vp, vp, vp, vp, ctypes.c_double, ctypes.c_int32,
+                                      vp, ctypes.c_size_t, i32p, dp, i32p, dp]
+        lib.pcg_solve_csr.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -263,3 +281,83 @@ def pcg_profile_read(h: Handle, kid: int):
     n = ctypes.c_int64(0)
     _check(h.ptr, load().pcg_profile_read(h.ptr, int(kid), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+# ---- explicit (CSR + stored tridiagonal) comparison path --------------------
+
+def _dev_tensor(t, numel: int, dtype_name: str, name: str) -> int:
+    import torch
+    dt = getattr(torch, dtype_name)
+    if not isinstance(t, torch.Tensor) or t.dtype != dt or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dtype_name} CUDA tensor")
+    if not t.is_contiguous() or t.numel() != numel:
+        raise ValueError(f"{name} must be contiguous with {numel} elements (got {t.numel()})")
+    return t.data_ptr()
+
+
+def pcg_csr_nnz(h: Handle) -> int:
+    nnz = ctypes.c_int64(0)
+    _check(h.ptr, load().pcg_csr_nnz(h.ptr, ctypes.byref(nnz)))
+    return nnz.value
+
+
+class Csr:
+    """Device CSR matrix of the operator: row_ptr (int64, N+1), col (int32), val (float64)."""
+
+    def __init__(self, row_ptr, col, val):
+        self.row_ptr, self.col, self.val = row_ptr, col, val
+
+
+def pcg_csr_assemble(h: Handle, device=None) -> Csr:
+    """Allocate (torch) and assemble the CSR matrix on the device."""
+    import torch
+    nnz = pcg_csr_nnz(h)
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    rp = torch.empty(h.n + 1, dtype=torch.int64, device=dev)
+    col = torch.empty(nnz, dtype=torch.int32, device=dev)
+    val = torch.empty(nnz, dtype=torch.float64, device=dev)
+    _check(h.ptr, load().pcg_csr_assemble(h.ptr, rp.data_ptr(), col.data_ptr(), val.data_ptr()))
+    return Csr(rp, col, val)
+
+
+def _csr_ptrs(h: Handle, A: Csr):
+    nnz = A.col.numel()
+    return (_dev_tensor(A.row_ptr, h.n + 1, "int64", "row_ptr"),
+            _dev_tensor(A.col, nnz, "int32", "col"),
+            _dev_tensor(A.val, nnz, "float64", "val"))
+
+
+def pcg_csr_spmv(h: Handle, A: Csr, x, y) -> None:
+    """y = A x with the CSR matrix (asynchronous)."""
+    rp, col, val = _csr_ptrs(h, A)
+    _check(h.ptr, load().pcg_csr_spmv(h.ptr, rp, col, val, _dev_ptr(x, h.n, "x"), _dev_ptr(y, h.n, "y")))
+
+
+def pcg_tridiag_assemble(h: Handle, device=None):
+    """Allocate (torch, 3N doubles = [sub | diag | sup]) and assemble + factor M's column matrices."""
+    import torch
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    tri = torch.empty(3 * h.n, dtype=torch.float64, device=dev)
+    _check(h.ptr, load().pcg_tridiag_assemble(h.ptr, tri.data_ptr()))
+    return tri
+
+
+def pcg_tridiag_factor(h: Handle, tri) -> None:
+    _check(h.ptr, load().pcg_tridiag_factor(h.ptr, _dev_tensor(tri, 3 * h.n, "float64", "tri")))
+
+
+def pcg_tridiag_precond(h: Handle, tri, r, z) -> None:
+    """z = M^{-1} r with the stored column matrices (asynchronous)."""
+    _check(h.ptr, load().pcg_tridiag_precond(h.ptr, _dev_tensor(tri, 3 * h.n, "float64", "tri"),
+                                             _dev_ptr(r, h.n, "r"), _dev_ptr(z, h.n, "z")))
+
+
+def pcg_solve_csr(h: Handle, A: Csr, tri, b, x, tol: float, maxit: int, workspace=None) -> dict:
+    """Standard PCG with the CSR matrix and the stored column matrices."""
+    lib = load()
+    rp, col, val = _csr_ptrs(h, A)
+    tp = _dev_tensor(tri, 3 * h.n, "float64", "tri")
+
+    def fn(hp, bp, xp, tol_, maxit_, wsp, wsb, it, hist, hlen, rel):
+        return lib.pcg_solve_csr(hp, rp, col, val, tp, bp, xp, tol_, maxit_, wsp, wsb, it, hist, hlen, rel)
+    return _solve(fn, h, b, x, tol, maxit, workspace)

@@ -160,11 +160,17 @@ __device__ __forceinline__ void block_sum(double (&v)[NV], double (*sh)[NV], dou
 //    gives every segment its z_top.
 // Per thread only three length-L arrays live in registers (r, 1/D, z').
 // Block: C * P threads rounded up to a multiple of 64 (extra threads idle).
-template <int L, int C, bool UPDATE, bool DOTS>
+//
+// STORED: the explicit variant of section 6.2 -- the column matrices are read
+// from three stored vectors tri = [sub | diag | sup] (N each, field layout)
+// instead of being recomputed, and the boundary multipliers come from a
+// table computed from those vectors (phib_tab).
+template <int L, int C, bool UPDATE, bool DOTS, bool STORED>
 __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     const double *__restrict__ rin, const double *__restrict__ q, double *__restrict__ rout,
     double *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
-    double *__restrict__ partials)
+    double *__restrict__ partials, const double *__restrict__ tri,
+    const double *__restrict__ phib_tab)
 {
     __shared__ double sh_a[kMaxThreads];
     __shared__ double sh_b[kMaxThreads];
@@ -207,6 +213,25 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         else
             return fz[t];
     };
+    // stored coefficients of the segment's levels: lo = -sub, up = -sup, diag
+    double slo[STORED ? L : 1], sup_[STORED ? L : 1], sdg[STORED ? L : 1];
+    if constexpr (STORED) {
+        const size_t n = (size_t)o.nx * o.ny * o.nz;
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            const size_t l = base + (size_t)(k0 + t) * ks;
+            const bool in = t < len;
+            slo[t] = in ? -tri[l] : 0.0;
+            sdg[t] = in ? tri[n + l] : 1.0;
+            sup_[t] = in ? -tri[2 * n + l] : 0.0;
+        }
+    }
+    auto lo_at = [&](int t) -> double {
+        if constexpr (STORED) return slo[t]; else return face(t);
+    };
+    auto up_at = [&](int t) -> double {
+        if constexpr (STORED) return sup_[t]; else return face(t + 1);
+    };
 
     double rr[L], iD[L], zp[L];
     double r2 = 0.0;
@@ -231,13 +256,18 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
 
     // Local forward sweep: pivots from the true incoming phi, z'' with zero inflow.
     const size_t ncol = (size_t)o.nx * o.ny;
-    double phi = (s > 0 && active) ? o.phib[(size_t)(s - 1) * ncol + (size_t)j * o.nx + ic] : 0.0;
+    double phi = (s > 0 && active) ? phib_tab[(size_t)(s - 1) * ncol + (size_t)j * o.nx + ic] : 0.0;
     double zpp = 0.0, mu = 1.0;
 #pragma unroll
     for (int t = 0; t < L; ++t) {
         if (t < len) {
-            const double lo = face(t), up = face(t + 1);
-            const double inv = 1.0 / thomas_pivot(o.delta, aT, lo, up, phi);
+            const double lo = lo_at(t), up = up_at(t);
+            double D;
+            if constexpr (STORED)
+                D = sdg[t] + lo * phi;
+            else
+                D = thomas_pivot(o.delta, aT, lo, up, phi);
+            const double inv = 1.0 / D;
             iD[t] = inv;
             phi = -up * inv;
             zpp = (rr[t] + lo * zpp) * inv;
@@ -260,7 +290,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
 #pragma unroll
     for (int t = 0; t < L; ++t) {
         if (t < len) {
-            const double lo = face(t);
+            const double lo = lo_at(t);
             prev = (rr[t] + lo * prev) * iD[t];
             zp[t] = prev;
         }
@@ -270,7 +300,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
         if (t < len) {
-            const double up = face(t + 1);
+            const double up = up_at(t);
             const double ph = -up * iD[t];
             znext = zp[t] - ph * znext;
             H = -ph * H;
@@ -293,7 +323,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
         if (t < len) {
-            const double up = face(t + 1);
+            const double up = up_at(t);
             H = (up * iD[t]) * H;
             const double zv = zp[t] + ztop * H;
             kap += rr[t] * zv;
@@ -331,6 +361,52 @@ __global__ void k_setup_phib(Op o, double *__restrict__ phib)
         const int kk = k + 1;
         if (kk % o.L == 0 && kk / o.L < o.P)
             phib[(size_t)(kk / o.L - 1) * ncol + col] = phi;
+    }
+}
+
+// Set-up of the explicit variant: the same boundary multipliers computed from
+// stored column matrices tri = [sub | diag | sup].
+__global__ void k_setup_phib_stored(Op o, const double *__restrict__ tri, double *__restrict__ phib)
+{
+    const size_t ncol = (size_t)o.nx * o.ny;
+    const size_t n = ncol * o.nz;
+    const size_t col = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (col >= ncol)
+        return;
+    const int j = (int)(col / o.nx);
+    const int i = (int)(col - (size_t)j * o.nx);
+    double phi = 0.0;
+    for (int k = 0; k < o.nz; ++k) {
+        const size_t l = lin(o, i, j, k);
+        const double lo = -tri[l];
+        const double inv = 1.0 / (tri[n + l] + lo * phi);
+        phi = tri[2 * n + l] * inv;   // super-diagonal / pivot
+        const int kk = k + 1;
+        if (kk % o.L == 0 && kk / o.L < o.P)
+            phib[(size_t)(kk / o.L - 1) * ncol + col] = phi;
+    }
+}
+
+// Assembly of the stored column matrices of M (section 6.2: the tridiagonal
+// matrix of the preconditioner kept as three vectors of length N):
+// sub = -alpha_z[k], diag = delta + alpha_T + alpha_z[k] + alpha_z[k+1],
+// sup = -alpha_z[k+1] (zero couplings at the bottom and top faces).
+__global__ void k_tridiag_assemble(Op o, double *__restrict__ tri)
+{
+    const size_t ncol = (size_t)o.nx * o.ny;
+    const size_t n = ncol * o.nz;
+    const size_t col = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (col >= ncol)
+        return;
+    const int j = (int)(col / o.nx);
+    const int i = (int)(col - (size_t)j * o.nx);
+    const double aT = column_faces(o, i, j).sum();
+    for (int k = 0; k < o.nz; ++k) {
+        const size_t l = lin(o, i, j, k);
+        const double lo = o.az[k], up = o.az[k + 1];
+        tri[l] = -lo;
+        tri[n + l] = (o.delta + aT) + (lo + up);
+        tri[2 * n + l] = -up;
     }
 }
 
@@ -522,6 +598,152 @@ __global__ __launch_bounds__(kMaxThreads) void k_update_p(double *__restrict__ p
     for (int t = 0; t < sw.len; ++t) {
         const size_t l = base + (size_t)(sw.k0 + t) * o.nx;
         p[l] = first ? z[l] : z[l] + beta * p[l];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Explicit operator in CSR form (section 6.2: the same 7-point operator stored
+// as a compressed-sparse-row matrix).  Rows follow the field layout; a row
+// holds the diagonal, its distinct horizontal neighbours (two per direction,
+// one when the periodic direction has 2 cells, none when it has 1) and the
+// vertical neighbours that exist; columns ascending.  The row length depends
+// only on k, so row_ptr has a closed form and needs no scan.
+struct CsrShape {
+    int hx, hy;    // distinct horizontal neighbours per direction
+    int base;      // 1 + hx + hy
+};
+
+__device__ __forceinline__ int csr_vert(int k, int nz) { return (k > 0) + (k < nz - 1); }
+__device__ __forceinline__ int64_t csr_vert_prefix(int k, int nz)
+{
+    // sum over k' < k of csr_vert(k')
+    return (int64_t)max(0, k - 1) + (int64_t)min(k, nz - 1);
+}
+
+__device__ __forceinline__ int64_t csr_row_start(const Op &o, const CsrShape &cs, int i, int j, int k)
+{
+    const int64_t l = (int64_t)lin(o, i, j, k);
+    const int64_t V = csr_vert_prefix(o.nz, o.nz);
+    return l * cs.base + (int64_t)j * o.nx * V + (int64_t)o.nx * csr_vert_prefix(k, o.nz) +
+           (int64_t)i * csr_vert(k, o.nz);
+}
+
+// Fill row_ptr (N+1), col (nnz) and val (nnz).  Sweep geometry.
+template <int Ls>
+__global__ __launch_bounds__(kMaxThreads) void k_csr_assemble(Op o, CsrShape cs,
+                                                              int64_t *__restrict__ row_ptr,
+                                                              int32_t *__restrict__ col,
+                                                              double *__restrict__ val)
+{
+    const Sweep sw = sweep_of_thread(o, Ls);
+    if (!sw.ok || sw.len <= 0)
+        return;
+    const int i = sw.i, j = sw.j;
+    const Faces f = column_faces(o, i, j);
+    const int ip = (i + 1 == o.nx) ? 0 : i + 1;
+    const int im = (i == 0) ? o.nx - 1 : i - 1;
+    const int jp = (j + 1 == o.ny) ? 0 : j + 1;
+    const int jm = (j == 0) ? o.ny - 1 : j - 1;
+    for (int t = 0; t < sw.len; ++t) {
+        const int k = sw.k0 + t;
+        const double lo = o.az[k], up = o.az[k + 1];
+        int32_t cc[7];
+        double vv[7];
+        int m = 0;
+        double diag = o.delta;
+        if (cs.hx == 2) {
+            cc[m] = (int32_t)lin(o, ip, j, k); vv[m++] = -f.xp;
+            cc[m] = (int32_t)lin(o, im, j, k); vv[m++] = -f.xm;
+            diag += f.xp + f.xm;
+        } else if (cs.hx == 1) {
+            cc[m] = (int32_t)lin(o, ip, j, k); vv[m++] = -(f.xp + f.xm);
+            diag += f.xp + f.xm;
+        }
+        if (cs.hy == 2) {
+            cc[m] = (int32_t)lin(o, i, jp, k); vv[m++] = -f.yp;
+            cc[m] = (int32_t)lin(o, i, jm, k); vv[m++] = -f.ym;
+            diag += f.yp + f.ym;
+        } else if (cs.hy == 1) {
+            cc[m] = (int32_t)lin(o, i, jp, k); vv[m++] = -(f.yp + f.ym);
+            diag += f.yp + f.ym;
+        }
+        if (k > 0) {
+            cc[m] = (int32_t)lin(o, i, j, k - 1); vv[m++] = -lo;
+            diag += lo;
+        }
+        if (k < o.nz - 1) {
+            cc[m] = (int32_t)lin(o, i, j, k + 1); vv[m++] = -up;
+            diag += up;
+        }
+        cc[m] = (int32_t)lin(o, i, j, k);
+        vv[m++] = diag;
+        // insertion sort by column (at most 7 entries)
+        for (int a = 1; a < m; ++a) {
+            const int32_t ck = cc[a];
+            const double vk = vv[a];
+            int b = a - 1;
+            while (b >= 0 && cc[b] > ck) {
+                cc[b + 1] = cc[b];
+                vv[b + 1] = vv[b];
+                --b;
+            }
+            cc[b + 1] = ck;
+            vv[b + 1] = vk;
+        }
+        const int64_t start = csr_row_start(o, cs, i, j, k);
+        const int64_t l = (int64_t)lin(o, i, j, k);
+        row_ptr[l] = start;
+        for (int a = 0; a < m; ++a) {
+            col[start + a] = cc[a];
+            val[start + a] = vv[a];
+        }
+        if (l == (int64_t)o.nx * o.ny * o.nz - 1)
+            row_ptr[l + 1] = start + m;
+    }
+}
+
+enum : int { CSR_APPLY = 0, CSR_RESID = 1, CSR_APPLY_DOT = 2 };
+
+// y = A x from the CSR matrix (one row per thread, sweep geometry); RESID:
+// y = b - A x; APPLY_DOT: also <x, y> per workgroup.
+template <int Ls, int MODE>
+__global__ __launch_bounds__(kMaxThreads) void k_csr_spmv(const int64_t *__restrict__ row_ptr,
+                                                          const int32_t *__restrict__ col,
+                                                          const double *__restrict__ val,
+                                                          const double *__restrict__ x,
+                                                          const double *__restrict__ bvec,
+                                                          double *__restrict__ y, Op o,
+                                                          const SolveState *__restrict__ st,
+                                                          double *__restrict__ partials)
+{
+    __shared__ double sh_red[kMaxThreads / kWave][1];
+    if (MODE == CSR_APPLY_DOT && st->done)
+        return;
+    const Sweep sw = sweep_of_thread(o, Ls);
+    double acc = 0.0;
+    if (sw.ok) {
+        const size_t base = lin(o, sw.i, sw.j, 0);
+        for (int t = 0; t < sw.len; ++t) {
+            const size_t l = base + (size_t)(sw.k0 + t) * o.nx;
+            const int64_t e0 = row_ptr[l], e1 = row_ptr[l + 1];
+            double s = 0.0;
+            for (int64_t e = e0; e < e1; ++e)
+                s += val[e] * x[col[e]];
+            if (MODE == CSR_RESID) {
+                y[l] = bvec[l] - s;
+            } else {
+                y[l] = s;
+                if (MODE == CSR_APPLY_DOT)
+                    acc += x[l] * s;
+            }
+        }
+    }
+    if (MODE == CSR_APPLY_DOT) {
+        double v[1] = {acc};
+        double out[1];
+        block_sum<1>(v, sh_red, out);
+        if (threadIdx.x == 0)
+            partials[2 * (size_t)sw.tile] = out[0];
     }
 }
 

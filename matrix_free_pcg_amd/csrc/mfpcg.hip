@@ -38,6 +38,8 @@ struct pcg_handle {
     int pt_tiles = 0;      // workgroups of a point pass
     size_t n = 0;          // nx*ny*nz
     double *d_az = nullptr, *d_ah = nullptr, *d_phib = nullptr;
+    double *d_phib_tri = nullptr;     // boundary multipliers of the last factored stored tridiagonal
+    CsrShape csr{};
     HostStatus *h_status = nullptr;   // pinned host memory written by the reduce kernels
     std::string err = "no error";
     bool profiling = false;
@@ -215,36 +217,46 @@ void drain_events(pcg_handle *h, int skip_kid = -1, int skip_tag = -2)
 // ---- launch helpers (template dispatch on the column geometry) ---------------
 template <int L, int C>
 void launch_column_lc(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
-                      const SolveState *st, int first, double *partials, bool update, bool dots)
+                      const SolveState *st, int first, double *partials, bool update, bool dots,
+                      const double *tri)
 {
     dim3 grid(h->col_tiles), block(h->col_threads);
-    if (update)
-        k_column_solve<L, C, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
+    const Op &o = h->op;
+    if (tri) {
+        if (dots)
+            k_column_solve<L, C, false, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
+        else
+            k_column_solve<L, C, false, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
+    } else if (update)
+        k_column_solve<L, C, true, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
     else if (dots)
-        k_column_solve<L, C, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
+        k_column_solve<L, C, false, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
     else
-        k_column_solve<L, C, false, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, h->op, st, first, partials);
+        k_column_solve<L, C, false, false, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
 }
 
 template <int C>
 void launch_column_c(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
-                     const SolveState *st, int first, double *partials, bool update, bool dots)
+                     const SolveState *st, int first, double *partials, bool update, bool dots,
+                     const double *tri)
 {
     switch (h->op.L) {
-    case 4: launch_column_lc<4, C>(h, rin, q, rout, z, st, first, partials, update, dots); break;
-    case 8: launch_column_lc<8, C>(h, rin, q, rout, z, st, first, partials, update, dots); break;
-    case 16: launch_column_lc<16, C>(h, rin, q, rout, z, st, first, partials, update, dots); break;
-    default: launch_column_lc<32, C>(h, rin, q, rout, z, st, first, partials, update, dots); break;
+    case 4: launch_column_lc<4, C>(h, rin, q, rout, z, st, first, partials, update, dots, tri); break;
+    case 8: launch_column_lc<8, C>(h, rin, q, rout, z, st, first, partials, update, dots, tri); break;
+    case 16: launch_column_lc<16, C>(h, rin, q, rout, z, st, first, partials, update, dots, tri); break;
+    default: launch_column_lc<32, C>(h, rin, q, rout, z, st, first, partials, update, dots, tri); break;
     }
 }
 
+// z = M^{-1} r; tri != nullptr selects the stored (explicit) column matrices.
 void column(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
-            const SolveState *st, int first, double *partials, bool update, bool dots)
+            const SolveState *st, int first, double *partials, bool update, bool dots,
+            const double *tri = nullptr)
 {
     if (h->op.C == 64)
-        launch_column_c<64>(h, rin, q, rout, z, st, first, partials, update, dots);
+        launch_column_c<64>(h, rin, q, rout, z, st, first, partials, update, dots, tri);
     else
-        launch_column_c<32>(h, rin, q, rout, z, st, first, partials, update, dots);
+        launch_column_c<32>(h, rin, q, rout, z, st, first, partials, update, dots, tri);
 }
 
 template <int Ls>
@@ -304,6 +316,48 @@ void update_xr(pcg_handle *h, double *x, const double *p, double *r, const doubl
 void update_p(pcg_handle *h, double *p, const double *z, const SolveState *st, int first)
 {
     vec(h, 1, nullptr, nullptr, p, z, st, nullptr, first);
+}
+
+template <int Ls>
+void launch_csr(pcg_handle *h, int mode, const int64_t *rp, const int32_t *col, const double *val,
+                const double *x, const double *b, double *y, const SolveState *st, double *partials)
+{
+    dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
+    if (mode == CSR_APPLY)
+        k_csr_spmv<Ls, CSR_APPLY><<<grid, block, 0, h->stream>>>(rp, col, val, x, b, y, h->op, st, partials);
+    else if (mode == CSR_RESID)
+        k_csr_spmv<Ls, CSR_RESID><<<grid, block, 0, h->stream>>>(rp, col, val, x, b, y, h->op, st, partials);
+    else
+        k_csr_spmv<Ls, CSR_APPLY_DOT><<<grid, block, 0, h->stream>>>(rp, col, val, x, b, y, h->op, st, partials);
+}
+
+void csr_spmv(pcg_handle *h, int mode, const int64_t *rp, const int32_t *col, const double *val,
+              const double *x, const double *b, double *y, const SolveState *st, double *partials)
+{
+    switch (h->op.Ls) {
+    case 4: launch_csr<4>(h, mode, rp, col, val, x, b, y, st, partials); break;
+    case 8: launch_csr<8>(h, mode, rp, col, val, x, b, y, st, partials); break;
+    case 16: launch_csr<16>(h, mode, rp, col, val, x, b, y, st, partials); break;
+    default: launch_csr<32>(h, mode, rp, col, val, x, b, y, st, partials); break;
+    }
+}
+
+void csr_assemble(pcg_handle *h, int64_t *rp, int32_t *col, double *val)
+{
+    dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
+    switch (h->op.Ls) {
+    case 4: k_csr_assemble<4><<<grid, block, 0, h->stream>>>(h->op, h->csr, rp, col, val); break;
+    case 8: k_csr_assemble<8><<<grid, block, 0, h->stream>>>(h->op, h->csr, rp, col, val); break;
+    case 16: k_csr_assemble<16><<<grid, block, 0, h->stream>>>(h->op, h->csr, rp, col, val); break;
+    default: k_csr_assemble<32><<<grid, block, 0, h->stream>>>(h->op, h->csr, rp, col, val); break;
+    }
+}
+
+int64_t csr_nnz(const pcg_handle *h)
+{
+    const int64_t ncol = (int64_t)h->op.nx * h->op.ny;
+    const int64_t V = 2 * (int64_t)h->op.nz - 2;
+    return (int64_t)h->n * h->csr.base + ncol * V;
 }
 
 int check_vectors(pcg_handle *h, const void *a, const void *b, const char *what)
@@ -487,6 +541,9 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
     h->op.P = P;
     h->op.C = C;
     h->op.ntc = (int)ntc;
+    h->csr.hx = nx == 1 ? 0 : (nx == 2 ? 1 : 2);
+    h->csr.hy = ny == 1 ? 0 : (ny == 2 ? 1 : 2);
+    h->csr.base = 1 + h->csr.hx + h->csr.hy;
     h->op.Ls = g.Ls;
     h->op.Ws = g.Ws;
     h->op.nkt = (int)nkt;
@@ -537,6 +594,7 @@ int pcg_destroy(pcg_handle *h)
     if (h->d_az) hipFree(h->d_az);
     if (h->d_ah) hipFree(h->d_ah);
     if (h->d_phib) hipFree(h->d_phib);
+    if (h->d_phib_tri) hipFree(h->d_phib_tri);
     if (h->h_status) hipHostFree(h->h_status);
     delete h;
     return PCG_OK;
@@ -648,27 +706,45 @@ int pcg_solve(pcg_handle *h, const double *b, double *x, double tol, int32_t max
     return solve_epilogue(h, a, w, PCG_KID_FUSED_SPMV, last);
 }
 
-int pcg_solve_standard(pcg_handle *h, const double *b, double *x, double tol, int32_t maxit,
-                       void *ws, size_t ws_bytes, int32_t *iters_out, double *hist_host,
-                       int32_t *hist_len_out, double *final_rel)
+}   // extern "C"
+
+namespace {
+
+// The explicit operator of section 6.2 (CSR matrix + stored column matrices),
+// or none for the matrix-free operator.
+struct Explicit {
+    const int64_t *row_ptr;
+    const int32_t *col;
+    const double *val;
+    const double *tri;
+};
+
+// Standard PCG (section 4.1): q = A p with sigma; x, r updates with <r,r>;
+// z = M^{-1} r with <r,z>; p = z + beta p.  The host reads the stop decision
+// after the r update while the preconditioner pass already runs.
+int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const Explicit *ex,
+                  const char *who)
 {
-    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
-    Workspace w{};
-    int rc = solve_prologue(h, a, &w, "pcg_solve_standard");
-    if (rc != PCG_OK)
-        return rc;
     HostStatus *hs = nullptr;
     HIP_TRY(h, hipHostGetDevicePointer((void **)&hs, h->h_status, 0));
     h->h_status->done = 0;
     hipEvent_t ev = nullptr;
     HIP_TRY(h, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    const double *b = a.b;
+    double *x = a.x;
+    const int32_t maxit = a.maxit;
+    const double tol = a.tol;
+    const double *tri = ex ? ex->tri : nullptr;
     int nred = 0;
     const double *red = nullptr;
     k_init_state<<<1, 64, 0, h->stream>>>(w.state);
-    stencil(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
+    if (ex)
+        csr_spmv(h, CSR_RESID, ex->row_ptr, ex->col, ex->val, x, b, w.r, nullptr, nullptr);
+    else
+        stencil(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
     {
         Timed t(h, PCG_KID_PRECOND, 0);
-        column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, false, true);
+        column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, false, true, tri);
     }
     red = fold_partials(h, w, h->col_tiles, &nred);
     k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, w.hist, 0, maxit, tol, hs);
@@ -682,7 +758,10 @@ int pcg_solve_standard(pcg_handle *h, const double *b, double *x, double tol, in
     for (int k = 1; e == hipSuccess && !done && k <= maxit; ++k) {
         {   // q = A p ; sigma = <p,q>
             Timed t(h, PCG_KID_APPLY_A, k);
-            stencil(h, SP_APPLY_DOT, w.p, nullptr, nullptr, nullptr, w.q, w.state, w.partials);
+            if (ex)
+                csr_spmv(h, CSR_APPLY_DOT, ex->row_ptr, ex->col, ex->val, w.p, nullptr, w.q, w.state, w.partials);
+            else
+                stencil(h, SP_APPLY_DOT, w.p, nullptr, nullptr, nullptr, w.q, w.state, w.partials);
         }
         red = fold_partials(h, w, h->pt_tiles, &nred);
         k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k - 1);
@@ -695,7 +774,7 @@ int pcg_solve_standard(pcg_handle *h, const double *b, double *x, double tol, in
         hipEventRecord(ev, h->stream);
         {   // z = M^{-1} r ; kappa = <r,z>
             Timed t(h, PCG_KID_PRECOND, k);
-            column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, false, true);
+            column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, false, true, tri);
         }
         red = fold_partials(h, w, h->col_tiles, &nred);
         k_reduce_kappa<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state);
@@ -710,8 +789,158 @@ int pcg_solve_standard(pcg_handle *h, const double *b, double *x, double tol, in
     }
     hipEventDestroy(ev);
     if (e != hipSuccess)
-        return fail(h, PCG_ERR_HIP, "pcg_solve_standard: %s", hipGetErrorString(e));
+        return fail(h, PCG_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
     return solve_epilogue(h, a, w, -1, -2);
+}
+
+int csr_supported(pcg_handle *h, const char *who)
+{
+    if (h->n >= (size_t)0x7fffffff)
+        return fail(h, PCG_ERR_UNSUPPORTED, "%s: N = %zu >= 2^31 does not fit int32 column indices", who, h->n);
+    return PCG_OK;
+}
+
+int check_explicit(pcg_handle *h, const Explicit &ex, const char *who)
+{
+    if (!ex.row_ptr || !ex.col || !ex.val || !ex.tri)
+        return fail(h, PCG_ERR_INVALID, "%s: null CSR or tridiagonal pointer", who);
+    if (!h->d_phib_tri && h->op.P > 1)
+        return fail(h, PCG_ERR_INVALID, "%s: the stored tridiagonal has not been factored (pcg_tridiag_factor)", who);
+    return csr_supported(h, who);
+}
+
+}   // namespace
+
+extern "C" {
+
+int pcg_solve_standard(pcg_handle *h, const double *b, double *x, double tol, int32_t maxit,
+                       void *ws, size_t ws_bytes, int32_t *iters_out, double *hist_host,
+                       int32_t *hist_len_out, double *final_rel)
+{
+    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    Workspace w{};
+    int rc = solve_prologue(h, a, &w, "pcg_solve_standard");
+    if (rc != PCG_OK)
+        return rc;
+    return standard_loop(h, a, w, nullptr, "pcg_solve_standard");
+}
+
+int pcg_csr_nnz(const pcg_handle *hc, int64_t *nnz)
+{
+    pcg_handle *h = const_cast<pcg_handle *>(hc);
+    if (!h || !nnz)
+        return PCG_ERR_INVALID;
+    int rc = csr_supported(h, "pcg_csr_nnz");
+    if (rc != PCG_OK)
+        return rc;
+    *nnz = csr_nnz(h);
+    return PCG_OK;
+}
+
+int pcg_csr_assemble(pcg_handle *h, int64_t *row_ptr, int32_t *col, double *val)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    if (!row_ptr || !col || !val)
+        return fail(h, PCG_ERR_INVALID, "pcg_csr_assemble: null pointer");
+    int rc = csr_supported(h, "pcg_csr_assemble");
+    if (rc != PCG_OK || (rc = set_device(h)) != PCG_OK)
+        return rc;
+    csr_assemble(h, row_ptr, col, val);
+    HIP_TRY(h, hipGetLastError());
+    return PCG_OK;
+}
+
+int pcg_csr_spmv(pcg_handle *h, const int64_t *row_ptr, const int32_t *col, const double *val,
+                 const double *x, double *y)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    if (!row_ptr || !col || !val)
+        return fail(h, PCG_ERR_INVALID, "pcg_csr_spmv: null CSR pointer");
+    int rc = check_vectors(h, x, y, "pcg_csr_spmv");
+    if (rc != PCG_OK || (rc = csr_supported(h, "pcg_csr_spmv")) != PCG_OK || (rc = set_device(h)) != PCG_OK)
+        return rc;
+    {
+        Timed t(h, PCG_KID_CSR_SPMV, -1);
+        csr_spmv(h, CSR_APPLY, row_ptr, col, val, x, nullptr, y, nullptr, nullptr);
+    }
+    HIP_TRY(h, hipGetLastError());
+    return PCG_OK;
+}
+
+int pcg_tridiag_factor(pcg_handle *h, const double *tri)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    if (!tri)
+        return fail(h, PCG_ERR_INVALID, "pcg_tridiag_factor: null pointer");
+    int rc = set_device(h);
+    if (rc != PCG_OK)
+        return rc;
+    const size_t ncol = (size_t)h->op.nx * h->op.ny;
+    if (!h->d_phib_tri)
+        HIP_TRY(h, hipMalloc(&h->d_phib_tri, sizeof(double) * ncol * (size_t)(h->op.P > 1 ? h->op.P - 1 : 1)));
+    if (h->op.P > 1) {
+        const int threads = 256;
+        k_setup_phib_stored<<<dim3((unsigned)((ncol + threads - 1) / threads)), dim3(threads), 0, h->stream>>>(h->op, tri, h->d_phib_tri);
+    }
+    HIP_TRY(h, hipGetLastError());
+    return PCG_OK;
+}
+
+int pcg_tridiag_assemble(pcg_handle *h, double *tri)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    if (!tri)
+        return fail(h, PCG_ERR_INVALID, "pcg_tridiag_assemble: null pointer");
+    int rc = set_device(h);
+    if (rc != PCG_OK)
+        return rc;
+    const size_t ncol = (size_t)h->op.nx * h->op.ny;
+    const int threads = 256;
+    k_tridiag_assemble<<<dim3((unsigned)((ncol + threads - 1) / threads)), dim3(threads), 0, h->stream>>>(h->op, tri);
+    HIP_TRY(h, hipGetLastError());
+    return pcg_tridiag_factor(h, tri);
+}
+
+int pcg_tridiag_precond(pcg_handle *h, const double *tri, const double *r, double *z)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    int rc = check_vectors(h, r, z, "pcg_tridiag_precond");
+    if (rc != PCG_OK || (rc = set_device(h)) != PCG_OK)
+        return rc;
+    if (!tri)
+        return fail(h, PCG_ERR_INVALID, "pcg_tridiag_precond: null pointer");
+    if (!h->d_phib_tri && h->op.P > 1)
+        return fail(h, PCG_ERR_INVALID, "pcg_tridiag_precond: call pcg_tridiag_factor first");
+    {
+        Timed t(h, PCG_KID_PRECOND, -1);
+        column(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, false, false, tri);
+    }
+    HIP_TRY(h, hipGetLastError());
+    return PCG_OK;
+}
+
+int pcg_solve_csr(pcg_handle *h, const int64_t *row_ptr, const int32_t *col, const double *val,
+                  const double *tri, const double *b, double *x, double tol, int32_t maxit,
+                  void *ws, size_t ws_bytes, int32_t *iters_out, double *hist_host,
+                  int32_t *hist_len_out, double *final_rel)
+{
+    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    if (!h)
+        return PCG_ERR_INVALID;
+    Explicit ex{row_ptr, col, val, tri};
+    int rc = check_explicit(h, ex, "pcg_solve_csr");
+    if (rc != PCG_OK)
+        return rc;
+    Workspace w{};
+    rc = solve_prologue(h, a, &w, "pcg_solve_csr");
+    if (rc != PCG_OK)
+        return rc;
+    return standard_loop(h, a, w, &ex, "pcg_solve_csr");
 }
 
 int pcg_profile_enable(pcg_handle *h, int32_t enable)

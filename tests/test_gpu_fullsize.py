@@ -151,3 +151,55 @@ def test_cfg3_manufactured_full(dev):
     print(f"[cfg3] iters={res['iters']} err={err:.3e} true-res={tr:.3e}", flush=True)
     assert err <= kappa * w.tol
     assert tr <= 1e-8
+
+
+def test_cfg5_explicit_path_full(dev):
+    """2048x2048x128 with the 1024^2 operator: the CSR matrix applied to a field
+    against the oracle's stencil (every element), the first 2 explicit CG steps
+    against the oracle, and the 50-step iterates of the matrix-free
+    (interleaved) and explicit (CSR + stored tridiagonal) solves."""
+    import torch
+    t = time.time()
+    w = W.make_workload(5)
+    prob = w.problem
+    print(f"\n[cfg5] inputs generated in {time.time() - t:.1f}s", flush=True)
+    h = mf.pcg_create(prob)
+    try:
+        C = mf.pcg_csr_assemble(h)
+        tri = mf.pcg_tridiag_assemble(h)
+        torch.cuda.synchronize()
+        print(f"[cfg5] nnz = {C.col.numel()}", flush=True)
+        bd = to_dev(w.rhs, dev)
+        yd = torch.empty_like(bd)
+        mf.pcg_csr_spmv(h, C, bd, yd)
+        torch.cuda.synchronize()
+        y = to_host(yd)
+        del yd
+        ws = torch.empty(mf.pcg_solve_workspace_bytes(h, 50), dtype=torch.uint8, device=dev)
+        x2 = torch.zeros_like(bd)
+        res2 = mf.pcg_solve_csr(h, C, tri, bd, x2, 0.0, 2, ws)
+        x2h = to_host(x2)
+        del x2
+        xm = torch.zeros_like(bd)
+        resm = mf.pcg_solve(h, bd, xm, 0.0, 50, ws)
+        xc = torch.zeros_like(bd)
+        resc = mf.pcg_solve_csr(h, C, tri, bd, xc, 0.0, 50, ws)
+        torch.cuda.synchronize()
+        d50 = float(torch.linalg.vector_norm(xm - xc) / torch.linalg.vector_norm(xc))
+        del xm, xc, ws, bd, C, tri
+    finally:
+        mf.pcg_destroy(h)
+    print(f"[cfg5] 50 steps: mf hist[-1]/hist[0]={resm['final_rel_res']:.3e} "
+          f"csr={resc['final_rel_res']:.3e} rel-L2(x_mf, x_csr)={d50:.2e}", flush=True)
+    assert resm["iters"] == resc["iters"] == 50
+    assert d50 <= 1e-10
+    assert np.allclose(resm["hist"], resc["hist"], rtol=1e-8, atol=0)
+    t = time.time()
+    yref = oracle.apply_A(prob, w.rhs)
+    assert np.abs(y - yref).max() <= apply_tol(prob, w.rhs)
+    del y, yref
+    ref = oracle.pcg(prob, w.rhs, tol=0.0, maxit=2)
+    print(f"[cfg5] oracle apply + 2 steps: {time.time() - t:.1f}s", flush=True)
+    assert res2["iters"] == ref["iters"] == 2
+    assert np.allclose(res2["hist"], ref["hist"], rtol=1e-11, atol=0)
+    assert np.linalg.norm(x2h - ref["x"]) <= 1e-11 * np.linalg.norm(ref["x"])
