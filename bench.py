@@ -30,9 +30,16 @@ METRIC = "PCG iterations/s + achieved HBM GB/s (% roofline), fp64 1024×1024×12
 
 # Algorithmic bytes per grid point of each pass (float64 = 8 B; each vector
 # read or written once per pass; stencil halos and coefficients not counted).
-BYTES_PER_POINT = {
-    "fused_prec": 32,   # read r, q; write r, z
-    "fused_spmv": 56,   # read x, p, q, z; write x, p, q
+BYTES_PER_POINT_BY_VARIANT = {
+    "interleaved": {                 # Algorithms 2-3 as printed: 88 B per point per iteration
+        "fused_prec": 32,            # read r, q; write r, z
+        "fused_spmv": 56,            # read x, p, q, z; write x, p, q
+    },
+    "interleaved_no_q": {            # q never stored: 72 B
+        "fused_prec": 32,            # read r, p; write r, z
+        "fused_spmv": 40,            # read x, p, z; write x, p
+    },
+    "standard": {},
 }
 
 
@@ -44,7 +51,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, variant: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when
     that summary was taken on a different kernel source or workload."""
@@ -56,7 +63,8 @@ def measured_traffic(kernel: str, workload: str):
             sha = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    if rec.get("source_sha256") != sha or workload not in os.path.basename(TRAFFIC_FILE):
+    if (rec.get("source_sha256") != sha or rec.get("variant") != variant
+            or workload not in os.path.basename(TRAFFIC_FILE)):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else int(round(k["traffic_bytes"]))
@@ -69,7 +77,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
                     help="5 = explicit-vs-matrix-free comparison at 2048x2048x128 (50 fixed steps)")
-    ap.add_argument("--variant", default="interleaved", choices=["interleaved", "standard"])
+    ap.add_argument("--variant", default="interleaved", choices=["interleaved", "interleaved_no_q", "standard"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -207,7 +215,9 @@ def main():
     if args.fixed_iterations > 0:
         tol, maxit = 0.0, args.fixed_iterations
     ws = torch.empty(mf.pcg_solve_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
-    solve = mf.pcg_solve if args.variant == "interleaved" else mf.pcg_solve_standard
+    solve = {"interleaved": mf.pcg_solve, "interleaved_no_q": mf.pcg_solve_no_q,
+             "standard": mf.pcg_solve_standard}[args.variant]
+    BYTES_PER_POINT = BYTES_PER_POINT_BY_VARIANT[args.variant]
     torch.cuda.synchronize()
 
     for s in range(args.warmup):
@@ -250,7 +260,7 @@ def main():
     true_rel = float(torch.linalg.vector_norm(b - r) / torch.linalg.vector_norm(b))
     mf.pcg_destroy(h)
 
-    per_iter_bytes = sum(BYTES_PER_POINT.values()) * n
+    per_iter_bytes = sum(BYTES_PER_POINT.values()) * n if BYTES_PER_POINT else None
     it_s = total_iters / elapsed
     dom = max((k for k in kern if k in BYTES_PER_POINT), key=lambda k: kern[k]["total_ms"], default=None)
     roofline = None
@@ -258,7 +268,7 @@ def main():
         ach = kern[dom]["GBps"]
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(dom, w.name),
+                    "traffic": measured_traffic(dom, w.name, args.variant),
                     "traffic_unit": "bytes per launch", "kernel": dom,
                     "bytes_per_launch": kern[dom]["bytes_per_launch"],
                     "avg_launch_ms": round(kern[dom]["avg_ms"], 4)}
@@ -280,9 +290,9 @@ def main():
                    "tol": tol, "maxit": maxit, "variant": args.variant,
                    "iterations_per_solve": iters, "status": res["status"],
                    "final_rel_res": res["final_rel_res"], "true_rel_res": true_rel},
-        "hbm_GBps_per_iteration": round(per_iter_bytes * it_s / 1e9, 1),
-        "hbm_frac_per_iteration": round(per_iter_bytes * it_s / 1e9 / HBM_PEAK_GBS, 4),
-        "bytes_per_point_per_iteration": sum(BYTES_PER_POINT.values()),
+        "hbm_GBps_per_iteration": round(per_iter_bytes * it_s / 1e9, 1) if per_iter_bytes else None,
+        "hbm_frac_per_iteration": round(per_iter_bytes * it_s / 1e9 / HBM_PEAK_GBS, 4) if per_iter_bytes else None,
+        "bytes_per_point_per_iteration": sum(BYTES_PER_POINT.values()) if per_iter_bytes else None,
         "kernels": kern,
         "roofline": roofline,
         "cpu_baseline": None,

@@ -117,7 +117,8 @@ size_t pcg_solve_workspace_bytes(const pcg_handle *h, int32_t maxit);
  * (Algorithm 1): per iteration one fused preconditioner pass (Appendix A,
  * Algorithm 3: r -= alpha q, z = M^{-1} r, <r,r>, <r,z>) and one fused
  * stencil pass (Algorithm 2: x += alpha p, p = z + beta p, q = A z + beta q,
- * <p,q>), each followed by a deterministic reduction.
+ * <p,q>), each followed by a deterministic reduction; 88 bytes per point per
+ * iteration (read r, q, x, p, q, z; write r, z, x, p, q).
  *   b_dev          right-hand side, N doubles
  *   x_dev          in: initial guess x0; out: the last iterate.  Must not
  *                  alias b_dev or the workspace.
@@ -138,6 +139,14 @@ size_t pcg_solve_workspace_bytes(const pcg_handle *h, int32_t maxit);
 int pcg_solve(pcg_handle *h, const double *b_dev, double *x_dev, double tol, int32_t maxit,
               void *workspace_dev, size_t workspace_bytes, int32_t *iters_out,
               double *hist_host, int32_t *hist_len_out, double *final_rel_res);
+
+/* Same contract as pcg_solve, with q never stored: the preconditioner pass
+ * recomputes A p from p and its neighbours, and the stencil pass forms
+ * <p_new, A z + beta A p_old> (72 bytes per point per iteration; two stencils
+ * of neighbour reads per iteration instead of one). */
+int pcg_solve_no_q(pcg_handle *h, const double *b_dev, double *x_dev, double tol, int32_t maxit,
+                   void *workspace_dev, size_t workspace_bytes, int32_t *iters_out,
+                   double *hist_host, int32_t *hist_len_out, double *final_rel_res);
 
 /* Same contract as pcg_solve, computed by the standard (non-interleaved)
  * PCG of section 4.1: separate stencil, preconditioner and vector-update

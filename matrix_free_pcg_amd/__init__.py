@@ -11,13 +11,13 @@ from ._abi import (PCG_ERR_BREAKDOWN, PCG_ERR_HIP, PCG_ERR_INVALID, PCG_ERR_UNSU
                    PCG_KID_VECTOR, PCG_NOT_CONVERGED, PCG_OK, Handle, PcgError, pcg_apply_A,
                    pcg_create, pcg_destroy, pcg_last_error, pcg_precond, pcg_profile_enable,
                    pcg_profile_read, pcg_profile_reset, pcg_set_stream, pcg_solve,
-                   pcg_solve_standard, pcg_solve_workspace_bytes, pcg_version,
+                   pcg_solve_standard, pcg_solve_no_q, pcg_solve_workspace_bytes, pcg_version,
                    PCG_KID_CSR_SPMV, Csr, pcg_csr_nnz, pcg_csr_assemble, pcg_csr_spmv,
                    pcg_tridiag_assemble, pcg_tridiag_factor, pcg_tridiag_precond, pcg_solve_csr)
 
 __all__ = [
     "workloads", "Handle", "PcgError", "pcg_create", "pcg_destroy", "pcg_set_stream",
-    "pcg_apply_A", "pcg_precond", "pcg_solve", "pcg_solve_standard",
+    "pcg_apply_A", "pcg_precond", "pcg_solve", "pcg_solve_standard", "pcg_solve_no_q",
     "pcg_solve_workspace_bytes", "pcg_profile_enable", "pcg_profile_reset",
     "pcg_profile_read", "pcg_last_error", "pcg_version", "Csr", "pcg_csr_nnz",
     "pcg_csr_assemble", "pcg_csr_spmv", "pcg_tridiag_assemble", "pcg_tridiag_factor",

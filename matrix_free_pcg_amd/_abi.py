@@ -36,7 +36,8 @@ PCG_KID_COUNT = 6
 
 EXPORTED = [
     "pcg_create", "pcg_destroy", "pcg_set_stream", "pcg_apply_A", "pcg_precond",
-    "pcg_solve_workspace_bytes", "pcg_solve", "pcg_solve_standard", "pcg_profile_enable",
+    "pcg_solve_workspace_bytes", "pcg_solve", "pcg_solve_standard", "pcg_solve_no_q",
+    "pcg_profile_enable",
     "pcg_profile_reset", "pcg_profile_read", "pcg_last_error", "pcg_version",
     "pcg_csr_nnz", "pcg_csr_assemble", "pcg_csr_spmv", "pcg_tridiag_assemble",
     "pcg_tridiag_factor", "pcg_tridiag_precond", "pcg_solve_csr",
@@ -99,7 +100,7 @@ def load():
         lib.pcg_precond.restype = ctypes.c_int
         lib.pcg_solve_workspace_bytes.argtypes = [H, ctypes.c_int32]
         lib.pcg_solve_workspace_bytes.restype = ctypes.c_size_t
-        for name in ("pcg_solve", "pcg_solve_standard"):
+        for name in ("pcg_solve", "pcg_solve_standard", "pcg_solve_no_q"):
             f = getattr(lib, name)
             f.argtypes = [H, vp, vp, ctypes.c_double, ctypes.c_int32, vp, ctypes.c_size_t,
                           i32p, dp, i32p, dp]
@@ -259,8 +260,14 @@ def _solve(fn, h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
 
 
 def pcg_solve(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
-    """Interleaved PCG (x in: x0, out: solution).  Returns status, iters, hist, final_rel_res."""
+    """Interleaved PCG, Algorithms 1-3 (x in: x0, out: solution).
+    Returns status, iters, hist, final_rel_res."""
     return _solve(load().pcg_solve, h, b, x, tol, maxit, workspace)
+
+
+def pcg_solve_no_q(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
+    """Interleaved PCG without storing q (A p recomputed; 72 B per point per iteration)."""
+    return _solve(load().pcg_solve_no_q, h, b, x, tol, maxit, workspace)
 
 
 def pcg_solve_standard(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:

@@ -165,7 +165,15 @@ __device__ __forceinline__ void block_sum(double (&v)[NV], double (*sh)[NV], dou
 // from three stored vectors tri = [sub | diag | sup] (N each, field layout)
 // instead of being recomputed, and the boundary multipliers come from a
 // table computed from those vectors (phib_tab).
-template <int L, int C, bool UPDATE, bool DOTS, bool STORED>
+//
+// UPD selects the residual update done while loading r:
+//   UPD_NONE  none (stand-alone preconditioner, standard loop),
+//   UPD_Q     r -= alpha q, q stored by the previous stencil pass (Algorithm 3),
+//   UPD_AP    r -= alpha (A p), the product recomputed from p and its
+//             neighbours, so that q never has to be stored.
+enum : int { UPD_NONE = 0, UPD_Q = 1, UPD_AP = 2 };
+
+template <int L, int C, int UPD, bool DOTS, bool STORED>
 __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     const double *__restrict__ rin, const double *__restrict__ q, double *__restrict__ rout,
     double *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
@@ -190,12 +198,13 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     const int i = it * C + c;
     const bool ok = active && i < o.nx;
     const int ic = i < o.nx ? i : o.nx - 1;
-    const double aT = column_faces(o, ic, j).sum();
+    const Faces fc = column_faces(o, ic, j);
+    const double aT = fc.sum();
     const int k0 = s * L;
     const int len = active ? min(L, o.nz - k0) : 0;
     const size_t base = lin(o, ic, j, 0);
     const size_t ks = (size_t)o.nx;
-    const double alpha = (UPDATE && !first) ? st->alpha : 0.0;
+    const double alpha = (UPD != UPD_NONE && !first) ? st->alpha : 0.0;
 
     // The segment's vertical face coefficients: face(t) couples levels
     // k0+t-1 and k0+t (face(0) below the segment, face(len) above it).  With
@@ -235,19 +244,80 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
 
     double rr[L], iD[L], zp[L];
     double r2 = 0.0;
+    if constexpr (UPD == UPD_AP) {
+        // q = p; (A p) at the segment's levels.  Load phase first (r, p at
+        // levels k0-1..k0+L clamped to the grid, p at j-1 and j+1; with 64
+        // columns per wave p at i-1 / i+1 comes from the adjacent lanes except
+        // at the tile edges and the periodic wrap), then the products.
+        const bool do_ap = !first && len > 0;
+        const int lane = tid & (kWave - 1);
+        const int ip = (ic + 1 == o.nx) ? 0 : ic + 1;
+        const int im = (ic == 0) ? o.nx - 1 : ic - 1;
+        const int jp = (j + 1 == o.ny) ? 0 : j + 1;
+        const int jm = (j == 0) ? o.ny - 1 : j - 1;
+        const size_t bxp = lin(o, ip, j, 0), bxm = lin(o, im, j, 0);
+        const size_t byp = lin(o, ic, jp, 0), bym = lin(o, ic, jm, 0);
+        constexpr bool kShfl = C == kWave;
+        const bool needL = !kShfl || lane == 0;
+        const bool needR = !kShfl || lane == kWave - 1 || ic + 1 >= o.nx;
+        auto lev = [&](int k) { return (size_t)min(max(k, 0), o.nz - 1) * ks; };
+        double pv[L + 2], pyp[L], pym[L], pxl[L], pxr[L];
+        if (do_ap) {
 #pragma unroll
-    for (int t = 0; t < L; ++t) {
-        double v = 0.0;
-        if (t < len && ok) {
-            const size_t l = base + (size_t)(k0 + t) * ks;
-            v = rin[l];
-            if (UPDATE && !first)
-                v = v - alpha * q[l];
+            for (int t = 0; t < L + 2; ++t)
+                pv[t] = q[base + lev(k0 - 1 + t)];
+#pragma unroll
+            for (int t = 0; t < L; ++t) {
+                const size_t off = lev(k0 + t);
+                pyp[t] = q[byp + off];
+                pym[t] = q[bym + off];
+                pxl[t] = needL ? q[bxm + off] : 0.0;
+                pxr[t] = needR ? q[bxp + off] : 0.0;
+            }
         }
-        rr[t] = v;
-        r2 += v * v;
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            double v = 0.0;
+            if (t < len && ok)
+                v = rin[base + (size_t)(k0 + t) * ks];
+            if (do_ap && t < len) {
+                const double pc = pv[t + 1];
+                double pl = pxl[t], pr = pxr[t];
+                if constexpr (kShfl) {
+                    const double pl_s = __shfl_up(pc, 1, kWave);
+                    const double pr_s = __shfl_down(pc, 1, kWave);
+                    pl = needL ? pl : pl_s;
+                    pr = needR ? pr : pr_s;
+                }
+                const double lo = face(t), up = face(t + 1);
+                double Ap = o.delta * pc;
+                Ap += fc.xp * (pc - pr);
+                Ap += fc.xm * (pc - pl);
+                Ap += fc.yp * (pc - pyp[t]);
+                Ap += fc.ym * (pc - pym[t]);
+                Ap += up * (pc - pv[t + 2]);
+                Ap += lo * (pc - pv[t]);
+                if (ok)
+                    v = v - alpha * Ap;
+            }
+            rr[t] = v;
+            r2 += v * v;
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            double v = 0.0;
+            if (t < len && ok) {
+                const size_t l = base + (size_t)(k0 + t) * ks;
+                v = rin[l];
+                if (UPD == UPD_Q && !first)
+                    v = v - alpha * q[l];
+            }
+            rr[t] = v;
+            r2 += v * v;
+        }
     }
-    if (UPDATE && !first && ok) {
+    if (UPD != UPD_NONE && !first && ok) {
 #pragma unroll
         for (int t = 0; t < L; ++t)
             if (t < len)
@@ -441,12 +511,17 @@ enum : int {
     SP_FUSED = 1,     // x += alpha p, p = z + beta p, q = A z + beta q, <p,q> (Algorithm 2)
     SP_APPLY = 2,     // y = A x
     SP_RESID = 3,     // y = b - A x
-    SP_APPLY_DOT = 4  // y = A x, <x, y>  (standard PCG: q = A p, sigma)
+    SP_APPLY_DOT = 4, // y = A x, <x, y>  (standard PCG: q = A p, sigma)
+    SP_FIRST_AP = 5,  // p = z, <z, A z>                    (no q stored)
+    SP_FUSED_AP = 6   // x += alpha p, p_new = z + beta p, <p_new, A z + beta A p>  (no q stored)
 };
 
 // Stencil passes (section 4.2, eq. (18)): the 7-point operator recomputed in
 // every cell from the column's face coefficients and the level's alpha_z.
 // Block: 64 * Ws threads.
+// SP_FIRST_AP / SP_FUSED_AP read the old search direction from p (with its
+// neighbours) and write the new one to p_out, a different buffer: an in-place
+// update would let a neighbour read an already-updated value.
 template <int Ls, int MODE>
 __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restrict__ zin,
                                                          const double *__restrict__ bvec,
@@ -454,14 +529,18 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
                                                          double *__restrict__ p,
                                                          double *__restrict__ y, Op o,
                                                          const SolveState *__restrict__ st,
-                                                         double *__restrict__ partials)
+                                                         double *__restrict__ partials,
+                                                         double *__restrict__ p_out)
 {
     __shared__ double sh_red[kMaxThreads / kWave][1];
     double alpha = 0.0, beta = 0.0;
     bool fixup_only = false;
-    if (MODE == SP_FIRST || MODE == SP_FUSED || MODE == SP_APPLY_DOT) {
+    constexpr bool kDot = MODE == SP_FIRST || MODE == SP_FUSED || MODE == SP_APPLY_DOT ||
+                          MODE == SP_FIRST_AP || MODE == SP_FUSED_AP;
+    constexpr bool kFused = MODE == SP_FUSED || MODE == SP_FUSED_AP;
+    if (kDot) {
         if (st->done) {
-            if (MODE != SP_FUSED || !st->fixup)
+            if (!kFused || !st->fixup)
                 return;
             fixup_only = true;
         }
@@ -472,7 +551,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
     const size_t ks = (size_t)o.nx;
     const size_t base = lin(o, sw.ic, sw.j, 0);
 
-    if (MODE == SP_FUSED && fixup_only) {
+    if (kFused && fixup_only) {
         // The stop test passed in this iteration: only the pending update
         // x += alpha p of the last step remains (Algorithm 1 exits before it).
         if (sw.ok) {
@@ -487,56 +566,124 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
     double acc = 0.0;
     if (sw.len > 0) {
         const Faces f = column_faces(o, sw.ic, sw.j);
+        const int lane = threadIdx.x & (kWave - 1);
         const int ip = (sw.ic + 1 == o.nx) ? 0 : sw.ic + 1;
         const int im = (sw.ic == 0) ? o.nx - 1 : sw.ic - 1;
         const int jp = (sw.j + 1 == o.ny) ? 0 : sw.j + 1;
         const int jm = (sw.j == 0) ? o.ny - 1 : sw.j - 1;
         const size_t bxp = lin(o, ip, sw.j, 0), bxm = lin(o, im, sw.j, 0);
         const size_t byp = lin(o, sw.ic, jp, 0), bym = lin(o, sw.ic, jm, 0);
-        double zc = zin[base + (size_t)sw.k0 * ks];
-        double zm = (sw.k0 > 0) ? zin[base + (size_t)(sw.k0 - 1) * ks] : zc;
-#pragma unroll 4
-        for (int t = 0; t < sw.len; ++t) {
-            const int k = sw.k0 + t;
-            const size_t off = (size_t)k * ks;
-            const double zn = (k + 1 < o.nz) ? zin[base + off + ks] : zc;
-            const double lo = o.az[k], up = o.az[k + 1];
-            double Az = o.delta * zc;
-            Az += f.xp * (zc - zin[bxp + off]);
-            Az += f.xm * (zc - zin[bxm + off]);
-            Az += f.yp * (zc - zin[byp + off]);
-            Az += f.ym * (zc - zin[bym + off]);
-            Az += up * (zc - zn);
-            Az += lo * (zc - zm);
-            const size_t l = base + off;
-            if (sw.ok) {
-                if (MODE == SP_FIRST) {
-                    p[l] = zc;
-                    y[l] = Az;
-                    acc += zc * Az;
-                } else if (MODE == SP_FUSED) {
-                    const double po = p[l];
-                    const double qo = y[l];
-                    u[l] = u[l] + alpha * po;
-                    const double pn = zc + beta * po;
-                    const double qn = Az + beta * qo;
-                    p[l] = pn;
-                    y[l] = qn;
-                    acc += pn * qn;
-                } else if (MODE == SP_APPLY) {
-                    y[l] = Az;
-                } else if (MODE == SP_RESID) {
-                    y[l] = bvec[l] - Az;
-                } else {   // SP_APPLY_DOT
-                    y[l] = Az;
-                    acc += zc * Az;
+        const int k0 = sw.k0, len = sw.len;
+        // i-1 is lane-1 except for lane 0; i+1 is lane+1 except for lane 63 and
+        // for the last column of the grid (periodic wrap).  Those lanes load
+        // their neighbour; the others take it from the adjacent lane.
+        const bool needL = lane == 0;
+        const bool needR = lane == kWave - 1 || sw.ic + 1 >= o.nx;
+        auto lev = [&](int k) { return (size_t)min(max(k, 0), o.nz - 1) * ks; };
+
+        // Load phase: every value of the wave's Ls levels is requested before
+        // any is used, so a wave waits for one memory round trip, not Ls.
+        constexpr bool kAp = MODE == SP_FUSED_AP;
+        double zv[Ls + 2], zyp[Ls], zym[Ls], zxl[Ls], zxr[Ls];
+        double pv[kAp ? Ls + 2 : 1], pyp[kAp ? Ls : 1], pym[kAp ? Ls : 1], pxl[kAp ? Ls : 1], pxr[kAp ? Ls : 1];
+        double uo[Ls], po[Ls], qo[Ls];
+#pragma unroll
+        for (int t = 0; t < Ls + 2; ++t) {
+            const size_t off = lev(k0 - 1 + t);   // levels k0-1 .. k0+Ls, clamped to the grid
+            zv[t] = zin[base + off];
+            if constexpr (kAp)
+                pv[t] = p[base + off];
+        }
+#pragma unroll
+        for (int t = 0; t < Ls; ++t) {
+            const size_t off = lev(k0 + t);
+            zyp[t] = zin[byp + off];
+            zym[t] = zin[bym + off];
+            zxl[t] = needL ? zin[bxm + off] : 0.0;
+            zxr[t] = needR ? zin[bxp + off] : 0.0;
+            if constexpr (kAp) {
+                pyp[t] = p[byp + off];
+                pym[t] = p[bym + off];
+                pxl[t] = needL ? p[bxm + off] : 0.0;
+                pxr[t] = needR ? p[bxp + off] : 0.0;
+            }
+            if constexpr (MODE == SP_FUSED || MODE == SP_FUSED_AP)
+                uo[t] = u[base + off];
+            if constexpr (MODE == SP_FUSED)
+                po[t] = p[base + off];
+            if constexpr (MODE == SP_FUSED)
+                qo[t] = y[base + off];
+            if constexpr (MODE == SP_RESID)
+                qo[t] = bvec[base + off];
+        }
+
+        // Compute phase.
+#pragma unroll
+        for (int t = 0; t < Ls; ++t) {
+            if (t < len) {
+                const int k = k0 + t;
+                const double lo = o.az[k], up = o.az[k + 1];
+                const double zc = zv[t + 1];
+                const double zl_s = __shfl_up(zc, 1, kWave);
+                const double zr_s = __shfl_down(zc, 1, kWave);
+                const double zl = needL ? zxl[t] : zl_s;
+                const double zr = needR ? zxr[t] : zr_s;
+                // k = 0 / nz-1: the clamped neighbour is zc itself and lo / up is 0
+                double Az = o.delta * zc;
+                Az += f.xp * (zc - zr);
+                Az += f.xm * (zc - zl);
+                Az += f.yp * (zc - zyp[t]);
+                Az += f.ym * (zc - zym[t]);
+                Az += up * (zc - zv[t + 2]);
+                Az += lo * (zc - zv[t]);
+                const size_t l = base + (size_t)k * ks;
+                if constexpr (kAp) {
+                    const double pc = pv[t + 1];
+                    const double pl_s = __shfl_up(pc, 1, kWave);
+                    const double pr_s = __shfl_down(pc, 1, kWave);
+                    const double pl = needL ? pxl[t] : pl_s;
+                    const double pr = needR ? pxr[t] : pr_s;
+                    double Ap = o.delta * pc;
+                    Ap += f.xp * (pc - pr);
+                    Ap += f.xm * (pc - pl);
+                    Ap += f.yp * (pc - pyp[t]);
+                    Ap += f.ym * (pc - pym[t]);
+                    Ap += up * (pc - pv[t + 2]);
+                    Ap += lo * (pc - pv[t]);
+                    if (sw.ok) {
+                        u[l] = uo[t] + alpha * pc;
+                        const double pnew = zc + beta * pc;
+                        p_out[l] = pnew;
+                        acc += pnew * (Az + beta * Ap);
+                    }
+                } else if (sw.ok) {
+                    if (MODE == SP_FIRST) {
+                        p[l] = zc;
+                        y[l] = Az;
+                        acc += zc * Az;
+                    } else if (MODE == SP_FUSED) {
+                        u[l] = uo[t] + alpha * po[t];
+                        const double pn = zc + beta * po[t];
+                        const double qn = Az + beta * qo[t];
+                        p[l] = pn;
+                        y[l] = qn;
+                        acc += pn * qn;
+                    } else if (MODE == SP_APPLY) {
+                        y[l] = Az;
+                    } else if (MODE == SP_RESID) {
+                        y[l] = qo[t] - Az;
+                    } else if (MODE == SP_APPLY_DOT) {
+                        y[l] = Az;
+                        acc += zc * Az;
+                    } else if (MODE == SP_FIRST_AP) {
+                        p_out[l] = zc;
+                        acc += zc * Az;
+                    }
                 }
             }
-            zm = zc;
-            zc = zn;
         }
     }
-    if (MODE == SP_FIRST || MODE == SP_FUSED || MODE == SP_APPLY_DOT) {
+    if (kDot) {
         double v[1] = {acc};
         double out[1];
         block_sum<1>(v, sh_red, out);

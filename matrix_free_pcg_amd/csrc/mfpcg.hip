@@ -76,8 +76,8 @@ inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // Column-pass geometry: C columns per workgroup and the segment length L
 // (default: the smallest of 8, 16, 32 with C * ceil(nz / L) <= 1024).
-// Sweep-pass geometry: Ls levels per wave, Ws waves per workgroup (default
-// Ls = 4, Ws = min(8, ceil(nz / 4))).  MFPCG_COL_L, MFPCG_COL_C, MFPCG_ST_L
+// Sweep-pass geometry: Ls levels per wave (1, 2, 4 or 8), Ws waves per
+// workgroup (default Ls = 4, Ws = min(4, ceil(nz / 4))).  MFPCG_COL_L, MFPCG_COL_C, MFPCG_ST_L
 // and MFPCG_ST_W override the choice (tuning).
 int env_int(const char *name, int dflt)
 {
@@ -104,9 +104,9 @@ bool choose_geometry(int nz, Geometry *g, std::string *why)
     if ((size_t)g->C * ((nz + l - 1) / l) > (size_t)kMaxThreads) { *why = "column workgroup exceeds 1024 threads"; return false; }
     g->L = l;
     g->Ls = env_int("MFPCG_ST_L", 4);
-    if (g->Ls != 4 && g->Ls != 8 && g->Ls != 16 && g->Ls != 32) { *why = "MFPCG_ST_L must be 4, 8, 16 or 32"; return false; }
+    if (g->Ls != 1 && g->Ls != 2 && g->Ls != 4 && g->Ls != 8) { *why = "MFPCG_ST_L must be 1, 2, 4 or 8"; return false; }
     const int need = (nz + g->Ls - 1) / g->Ls;
-    g->Ws = env_int("MFPCG_ST_W", std::min(8, need));
+    g->Ws = env_int("MFPCG_ST_W", std::min(4, need));
     if (g->Ws < 1 || g->Ws > 16) { *why = "MFPCG_ST_W must be in 1..16"; return false; }
     return true;
 }
@@ -217,70 +217,76 @@ void drain_events(pcg_handle *h, int skip_kid = -1, int skip_tag = -2)
 // ---- launch helpers (template dispatch on the column geometry) ---------------
 template <int L, int C>
 void launch_column_lc(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
-                      const SolveState *st, int first, double *partials, bool update, bool dots,
+                      const SolveState *st, int first, double *partials, int upd, bool dots,
                       const double *tri)
 {
     dim3 grid(h->col_tiles), block(h->col_threads);
     const Op &o = h->op;
     if (tri) {
         if (dots)
-            k_column_solve<L, C, false, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
+            k_column_solve<L, C, UPD_NONE, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
         else
-            k_column_solve<L, C, false, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
-    } else if (update)
-        k_column_solve<L, C, true, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
+            k_column_solve<L, C, UPD_NONE, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
+    } else if (upd == UPD_Q)
+        k_column_solve<L, C, UPD_Q, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
+    else if (upd == UPD_AP)
+        k_column_solve<L, C, UPD_AP, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
     else if (dots)
-        k_column_solve<L, C, false, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
+        k_column_solve<L, C, UPD_NONE, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
     else
-        k_column_solve<L, C, false, false, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
+        k_column_solve<L, C, UPD_NONE, false, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
 }
 
 template <int C>
 void launch_column_c(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
-                     const SolveState *st, int first, double *partials, bool update, bool dots,
+                     const SolveState *st, int first, double *partials, int upd, bool dots,
                      const double *tri)
 {
     switch (h->op.L) {
-    case 4: launch_column_lc<4, C>(h, rin, q, rout, z, st, first, partials, update, dots, tri); break;
-    case 8: launch_column_lc<8, C>(h, rin, q, rout, z, st, first, partials, update, dots, tri); break;
-    case 16: launch_column_lc<16, C>(h, rin, q, rout, z, st, first, partials, update, dots, tri); break;
-    default: launch_column_lc<32, C>(h, rin, q, rout, z, st, first, partials, update, dots, tri); break;
+    case 4: launch_column_lc<4, C>(h, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
+    case 8: launch_column_lc<8, C>(h, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
+    case 16: launch_column_lc<16, C>(h, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
+    default: launch_column_lc<32, C>(h, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
     }
 }
 
-// z = M^{-1} r; tri != nullptr selects the stored (explicit) column matrices.
+// z = M^{-1} r; upd selects the fused residual update (UPD_*); tri != nullptr
+// selects the stored (explicit) column matrices.
 void column(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
-            const SolveState *st, int first, double *partials, bool update, bool dots,
+            const SolveState *st, int first, double *partials, int upd, bool dots,
             const double *tri = nullptr)
 {
     if (h->op.C == 64)
-        launch_column_c<64>(h, rin, q, rout, z, st, first, partials, update, dots, tri);
+        launch_column_c<64>(h, rin, q, rout, z, st, first, partials, upd, dots, tri);
     else
-        launch_column_c<32>(h, rin, q, rout, z, st, first, partials, update, dots, tri);
+        launch_column_c<32>(h, rin, q, rout, z, st, first, partials, upd, dots, tri);
 }
 
 template <int Ls>
 void launch_stencil(pcg_handle *h, int mode, const double *zin, const double *b, double *u,
-                    double *p, double *y, const SolveState *st, double *partials)
+                    double *p, double *y, const SolveState *st, double *partials, double *p_out)
 {
     dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
+    const Op &o = h->op;
     switch (mode) {
-    case SP_FIRST: k_stencil<Ls, SP_FIRST><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
-    case SP_FUSED: k_stencil<Ls, SP_FUSED><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
-    case SP_APPLY: k_stencil<Ls, SP_APPLY><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
-    case SP_RESID: k_stencil<Ls, SP_RESID><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
-    default: k_stencil<Ls, SP_APPLY_DOT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, h->op, st, partials); break;
+    case SP_FIRST: k_stencil<Ls, SP_FIRST><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_FUSED: k_stencil<Ls, SP_FUSED><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_APPLY: k_stencil<Ls, SP_APPLY><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_RESID: k_stencil<Ls, SP_RESID><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_APPLY_DOT: k_stencil<Ls, SP_APPLY_DOT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_FIRST_AP: k_stencil<Ls, SP_FIRST_AP><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    default: k_stencil<Ls, SP_FUSED_AP><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
     }
 }
 
 void stencil(pcg_handle *h, int mode, const double *zin, const double *b, double *u, double *p,
-             double *y, const SolveState *st, double *partials)
+             double *y, const SolveState *st, double *partials, double *p_out = nullptr)
 {
     switch (h->op.Ls) {
-    case 4: launch_stencil<4>(h, mode, zin, b, u, p, y, st, partials); break;
-    case 8: launch_stencil<8>(h, mode, zin, b, u, p, y, st, partials); break;
-    case 16: launch_stencil<16>(h, mode, zin, b, u, p, y, st, partials); break;
-    default: launch_stencil<32>(h, mode, zin, b, u, p, y, st, partials); break;
+    case 1: launch_stencil<1>(h, mode, zin, b, u, p, y, st, partials, p_out); break;
+    case 2: launch_stencil<2>(h, mode, zin, b, u, p, y, st, partials, p_out); break;
+    case 4: launch_stencil<4>(h, mode, zin, b, u, p, y, st, partials, p_out); break;
+    default: launch_stencil<8>(h, mode, zin, b, u, p, y, st, partials, p_out); break;
     }
 }
 
@@ -299,10 +305,10 @@ void vec(pcg_handle *h, int which, double *x, const double *p, double *r, const 
          const SolveState *st, double *partials, int first)
 {
     switch (h->op.Ls) {
+    case 1: launch_vec<1>(h, which, x, p, r, q, st, partials, first); break;
+    case 2: launch_vec<2>(h, which, x, p, r, q, st, partials, first); break;
     case 4: launch_vec<4>(h, which, x, p, r, q, st, partials, first); break;
-    case 8: launch_vec<8>(h, which, x, p, r, q, st, partials, first); break;
-    case 16: launch_vec<16>(h, which, x, p, r, q, st, partials, first); break;
-    default: launch_vec<32>(h, which, x, p, r, q, st, partials, first); break;
+    default: launch_vec<8>(h, which, x, p, r, q, st, partials, first); break;
     }
 }
 
@@ -335,10 +341,10 @@ void csr_spmv(pcg_handle *h, int mode, const int64_t *rp, const int32_t *col, co
               const double *x, const double *b, double *y, const SolveState *st, double *partials)
 {
     switch (h->op.Ls) {
+    case 1: launch_csr<1>(h, mode, rp, col, val, x, b, y, st, partials); break;
+    case 2: launch_csr<2>(h, mode, rp, col, val, x, b, y, st, partials); break;
     case 4: launch_csr<4>(h, mode, rp, col, val, x, b, y, st, partials); break;
-    case 8: launch_csr<8>(h, mode, rp, col, val, x, b, y, st, partials); break;
-    case 16: launch_csr<16>(h, mode, rp, col, val, x, b, y, st, partials); break;
-    default: launch_csr<32>(h, mode, rp, col, val, x, b, y, st, partials); break;
+    default: launch_csr<8>(h, mode, rp, col, val, x, b, y, st, partials); break;
     }
 }
 
@@ -346,10 +352,10 @@ void csr_assemble(pcg_handle *h, int64_t *rp, int32_t *col, double *val)
 {
     dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
     switch (h->op.Ls) {
+    case 1: k_csr_assemble<1><<<grid, block, 0, h->stream>>>(h->op, h->csr, rp, col, val); break;
+    case 2: k_csr_assemble<2><<<grid, block, 0, h->stream>>>(h->op, h->csr, rp, col, val); break;
     case 4: k_csr_assemble<4><<<grid, block, 0, h->stream>>>(h->op, h->csr, rp, col, val); break;
-    case 8: k_csr_assemble<8><<<grid, block, 0, h->stream>>>(h->op, h->csr, rp, col, val); break;
-    case 16: k_csr_assemble<16><<<grid, block, 0, h->stream>>>(h->op, h->csr, rp, col, val); break;
-    default: k_csr_assemble<32><<<grid, block, 0, h->stream>>>(h->op, h->csr, rp, col, val); break;
+    default: k_csr_assemble<8><<<grid, block, 0, h->stream>>>(h->op, h->csr, rp, col, val); break;
     }
 }
 
@@ -636,7 +642,7 @@ int pcg_precond(pcg_handle *h, const double *r, double *z)
         return rc;
     {
         Timed t(h, PCG_KID_PRECOND, -1);
-        column(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, false, false);
+        column(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, UPD_NONE, false);
     }
     HIP_TRY(h, hipGetLastError());
     return PCG_OK;
@@ -649,18 +655,26 @@ size_t pcg_solve_workspace_bytes(const pcg_handle *h, int32_t maxit)
     return workspace_layout(h, maxit, nullptr, nullptr);
 }
 
-int pcg_solve(pcg_handle *h, const double *b, double *x, double tol, int32_t maxit, void *ws,
-              size_t ws_bytes, int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
-              double *final_rel)
+}   // extern "C"
+
+namespace {
+
+// The interleaved loop of section 4.3, Algorithm 1.  ap = false: Algorithms 2
+// and 3 as printed (q = A z + beta q stored by the stencil pass, r -= alpha q
+// in the preconditioner pass).  ap = true: q is never stored -- the
+// preconditioner pass recomputes A p from p and the stencil pass forms
+// <p_new, A z + beta A p_old>; p alternates between two buffers (the stencil
+// pass reads the old direction around each point while writing the new one).
+int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool ap, const char *who)
 {
-    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
-    Workspace w{};
-    int rc = solve_prologue(h, a, &w, "pcg_solve");
-    if (rc != PCG_OK)
-        return rc;
     HostStatus *hs = nullptr;
     HIP_TRY(h, hipHostGetDevicePointer((void **)&hs, h->h_status, 0));
     h->h_status->done = 0;
+    const double *b = a.b;
+    double *x = a.x;
+    const int32_t maxit = a.maxit;
+    const double tol = a.tol;
+    double *pbuf[2] = {w.p, w.q};
     k_init_state<<<1, 64, 0, h->stream>>>(w.state);
     // a2: r0 = b - A x0
     stencil(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
@@ -670,20 +684,29 @@ int pcg_solve(pcg_handle *h, const double *b, double *x, double tol, int32_t max
     for (int k = 0; k <= maxit; ++k) {
         int nred = 0;
         const double *red = nullptr;
-        // a3: r -= alpha q; z = M^{-1} r; partial <r,r>, <r,z>   (Algorithm 3)
+        // search direction read this iteration (ap: written by the previous one)
+        double *pin = ap ? pbuf[(k + 1) & 1] : w.q;
+        double *pcur = ap ? pbuf[(k + 1) & 1] : w.p;
+        double *pnext = ap ? pbuf[k & 1] : nullptr;
+        // a3: r -= alpha q (or alpha A p); z = M^{-1} r; partial <r,r>, <r,z>  (Algorithm 3)
         {
             Timed t(h, PCG_KID_FUSED_PREC, k);
-            column(h, w.r, w.q, w.r, w.z, w.state, k == 0, w.partials, true, true);
+            column(h, w.r, pin, w.r, w.z, w.state, k == 0, w.partials, ap ? UPD_AP : UPD_Q, true);
         }
         // a4: ||r_k||, stop test, beta
         red = fold_partials(h, w, h->col_tiles, &nred);
         k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, w.hist, k, maxit, tol, hs);
         hipEventRecord(ev, h->stream);
-        // a5: x += alpha p; p = z + beta p; q = A z + beta q; partial <p,q>  (Algorithm 2)
-        //     (only x += alpha p once the stop test has passed: a7)
+        // a5: x += alpha p; p = z + beta p; q = A z + beta q (or A p_new on the
+        //     fly); partial <p,q>  (Algorithm 2); only x += alpha p once the
+        //     stop test has passed (a7)
         {
             Timed t(h, PCG_KID_FUSED_SPMV, k);
-            stencil(h, k == 0 ? SP_FIRST : SP_FUSED, w.z, nullptr, x, w.p, w.q, w.state, w.partials);
+            if (ap)
+                stencil(h, k == 0 ? SP_FIRST_AP : SP_FUSED_AP, w.z, nullptr, x, pcur, nullptr, w.state,
+                        w.partials, pnext);
+            else
+                stencil(h, k == 0 ? SP_FIRST : SP_FUSED, w.z, nullptr, x, w.p, w.q, w.state, w.partials);
         }
         // a6: sigma, alpha
         red = fold_partials(h, w, h->pt_tiles, &nred);
@@ -691,12 +714,12 @@ int pcg_solve(pcg_handle *h, const double *b, double *x, double tol, int32_t max
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) {
             hipEventDestroy(ev);
-            return fail(h, PCG_ERR_HIP, "pcg_solve: launch failed: %s", hipGetErrorString(e));
+            return fail(h, PCG_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
         }
         e = hipEventSynchronize(ev);
         if (e != hipSuccess) {
             hipEventDestroy(ev);
-            return fail(h, PCG_ERR_HIP, "pcg_solve: hipEventSynchronize: %s", hipGetErrorString(e));
+            return fail(h, PCG_ERR_HIP, "%s: hipEventSynchronize: %s", who, hipGetErrorString(e));
         }
         last = k;
         if (((volatile HostStatus *)h->h_status)->done)
@@ -704,6 +727,34 @@ int pcg_solve(pcg_handle *h, const double *b, double *x, double tol, int32_t max
     }
     hipEventDestroy(ev);
     return solve_epilogue(h, a, w, PCG_KID_FUSED_SPMV, last);
+}
+
+}   // namespace
+
+extern "C" {
+
+int pcg_solve(pcg_handle *h, const double *b, double *x, double tol, int32_t maxit, void *ws,
+              size_t ws_bytes, int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
+              double *final_rel)
+{
+    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    Workspace w{};
+    int rc = solve_prologue(h, a, &w, "pcg_solve");
+    if (rc != PCG_OK)
+        return rc;
+    return interleaved_loop(h, a, w, false, "pcg_solve");
+}
+
+int pcg_solve_no_q(pcg_handle *h, const double *b, double *x, double tol, int32_t maxit, void *ws,
+                   size_t ws_bytes, int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
+                   double *final_rel)
+{
+    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    Workspace w{};
+    int rc = solve_prologue(h, a, &w, "pcg_solve_no_q");
+    if (rc != PCG_OK)
+        return rc;
+    return interleaved_loop(h, a, w, true, "pcg_solve_no_q");
 }
 
 }   // extern "C"
@@ -744,7 +795,7 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
         stencil(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
     {
         Timed t(h, PCG_KID_PRECOND, 0);
-        column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, false, true, tri);
+        column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, UPD_NONE, true, tri);
     }
     red = fold_partials(h, w, h->col_tiles, &nred);
     k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, w.hist, 0, maxit, tol, hs);
@@ -774,7 +825,7 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
         hipEventRecord(ev, h->stream);
         {   // z = M^{-1} r ; kappa = <r,z>
             Timed t(h, PCG_KID_PRECOND, k);
-            column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, false, true, tri);
+            column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, UPD_NONE, true, tri);
         }
         red = fold_partials(h, w, h->col_tiles, &nred);
         k_reduce_kappa<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state);
@@ -918,7 +969,7 @@ int pcg_tridiag_precond(pcg_handle *h, const double *tri, const double *r, doubl
         return fail(h, PCG_ERR_INVALID, "pcg_tridiag_precond: call pcg_tridiag_factor first");
     {
         Timed t(h, PCG_KID_PRECOND, -1);
-        column(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, false, false, tri);
+        column(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, UPD_NONE, false, tri);
     }
     HIP_TRY(h, hipGetLastError());
     return PCG_OK;

@@ -76,14 +76,18 @@ def test_precond_matches_oracle(dev, label, make):
     assert np.array_equal(to_host(rd), r)   # input untouched
 
 
+SOLVERS = {"interleaved": mf.pcg_solve, "no_q": mf.pcg_solve_no_q,
+           "standard": mf.pcg_solve_standard}
+VARIANTS = list(SOLVERS)
+
+
 def _solve_both(prob, b, tol, maxit, dev, variant="interleaved", x0=None):
     import torch
     h = mf.pcg_create(prob)
     try:
         bd = to_dev(b, dev)
         xd = to_dev(np.zeros_like(b) if x0 is None else x0, dev)
-        fn = mf.pcg_solve if variant == "interleaved" else mf.pcg_solve_standard
-        res = fn(h, bd, xd, tol, maxit)
+        res = SOLVERS[variant](h, bd, xd, tol, maxit)
         torch.cuda.synchronize()
         xg = to_host(xd)
     finally:
@@ -165,7 +169,7 @@ def _rhs(w):
     return oracle.apply_A(w.problem, w.x_true)   # oracle side builds its b; the same b is given to both
 
 
-@pytest.mark.parametrize("variant", ["interleaved", "standard"])
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("label,make,drift", SOLVE_CASES, ids=[c[0] for c in SOLVE_CASES])
 def test_solve_matches_oracle(dev, label, make, drift, variant):
     w = make()
@@ -176,7 +180,7 @@ def test_solve_matches_oracle(dev, label, make, drift, variant):
     print(f"{label} {variant}: iters gpu={res['iters']} oracle={ref['iters']} rel-L2={rel:.2e}")
 
 
-@pytest.mark.parametrize("variant", ["interleaved", "standard"])
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("steps", [0, 1, 2, 5])
 def test_first_steps_match_oracle(dev, steps, variant):
     """Fixed step counts (tol = 0): iterate and history after k steps, tight."""
@@ -218,12 +222,12 @@ def test_solve_is_deterministic(dev):
     assert np.array_equal(outs[0][0], outs[1][0])
 
 
-@pytest.mark.parametrize("variant", ["interleaved", "standard"])
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_edge_cases(dev, variant):
     import torch
     w = W.make_workload(4, scale_xy=(33, 5), nz=9)
     prob = w.problem
-    fn = mf.pcg_solve if variant == "interleaved" else mf.pcg_solve_standard
+    fn = SOLVERS[variant]
     h = mf.pcg_create(prob)
     try:
         # r0 = 0: no steps, x = x0, converged
