@@ -28,19 +28,45 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 METRIC = "PCG iterations/s + achieved HBM GB/s (% roofline), fp64 1024×1024×128"
 
-# Algorithmic bytes per grid point of each pass (float64 = 8 B; each vector
-# read or written once per pass; stencil halos and coefficients not counted).
-BYTES_PER_POINT_BY_VARIANT = {
-    "interleaved": {                 # Algorithms 2-3 as printed: 88 B per point per iteration
-        "fused_prec": 32,            # read r, q; write r, z
-        "fused_spmv": 56,            # read x, p, q, z; write x, p, q
-    },
-    "interleaved_no_q": {            # q never stored: 72 B
-        "fused_prec": 32,            # read r, p; write r, z
-        "fused_spmv": 40,            # read x, p, z; write x, p
-    },
-    "standard": {},
-}
+# Algorithmic bytes per grid point of each launch of a pass (float64 = 8 B;
+# each vector read or written once per pass; stencil halos and coefficients
+# not counted), as a function of the step k the launch belongs to.
+#   interleaved: Algorithms 2-3, x updated every second step.
+#     fused_prec  k = 0: read r, write z (16); k >= 1: read r, q, write r, z (32)
+#     fused_spmv  k = 0: read z, write p, q (24); odd k: read z, p, q, write p, q
+#                 (40); even k >= 2: also read x and the previous p, write x (64)
+#     -> 84 B per point per step in steady state
+#   interleaved_no_q: q never stored.
+#     fused_prec  k = 0: 16; k >= 1: read r, p, write r, z (32)
+#     fused_spmv  k = 0: read z, write p (16); k >= 1: read x, p, z, write x, p (40)
+#     -> 72 B per point per step
+def _bytes_interleaved(kernel, k):
+    if kernel == "fused_prec":
+        return 16 if k == 0 else 32
+    return 24 if k == 0 else (40 if k % 2 else 64)
+
+
+def _bytes_no_q(kernel, k):
+    if kernel == "fused_prec":
+        return 16 if k == 0 else 32
+    return 16 if k == 0 else 40
+
+
+BYTES_BY_VARIANT = {"interleaved": (_bytes_interleaved, 84), "interleaved_no_q": (_bytes_no_q, 72)}
+
+
+def pass_bytes(variant, kernel, iters, n):
+    """Total algorithmic bytes and launch count of the timed launches of one
+    pass over solves that took `iters` steps each: the preconditioner pass runs
+    at k = 0..K, the stencil pass at k = 0..K-1 (its launch at k = K only
+    applies the pending x update and is not timed)."""
+    f = BYTES_BY_VARIANT[variant][0]
+    tot = cnt = 0
+    for K in iters:
+        ks = range(K + 1) if kernel == "fused_prec" else range(K)
+        tot += sum(f(kernel, k) for k in ks) * n
+        cnt += len(ks)
+    return tot, cnt
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fused_passes_varying-1024x1024x128.json")
@@ -217,7 +243,7 @@ def main():
     ws = torch.empty(mf.pcg_solve_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
     solve = {"interleaved": mf.pcg_solve, "interleaved_no_q": mf.pcg_solve_no_q,
              "standard": mf.pcg_solve_standard}[args.variant]
-    BYTES_PER_POINT = BYTES_PER_POINT_BY_VARIANT[args.variant]
+    has_bytes = args.variant in BYTES_BY_VARIANT
     torch.cuda.synchronize()
 
     for s in range(args.warmup):
@@ -248,9 +274,12 @@ def main():
         if cnt:
             avg = ms / cnt
             ent = {"launches": cnt, "avg_ms": avg, "total_ms": ms}
-            if name in BYTES_PER_POINT:
-                ent["bytes_per_launch"] = BYTES_PER_POINT[name] * n
-                ent["GBps"] = BYTES_PER_POINT[name] * n / (avg * 1e-3) / 1e9
+            if has_bytes and name in ("fused_prec", "fused_spmv"):
+                tot, nl = pass_bytes(args.variant, name, iters, n)
+                if nl != cnt:
+                    raise SystemExit(f"{name}: {cnt} timed launches, expected {nl}")
+                ent["bytes_per_launch"] = tot / nl          # average over the timed launches
+                ent["GBps"] = tot / (ms * 1e-3) / 1e9
             kern[name] = ent
 
     # true residual of the last solve, with the library's own stencil
@@ -260,9 +289,11 @@ def main():
     true_rel = float(torch.linalg.vector_norm(b - r) / torch.linalg.vector_norm(b))
     mf.pcg_destroy(h)
 
-    per_iter_bytes = sum(BYTES_PER_POINT.values()) * n if BYTES_PER_POINT else None
     it_s = total_iters / elapsed
-    dom = max((k for k in kern if k in BYTES_PER_POINT), key=lambda k: kern[k]["total_ms"], default=None)
+    # every timed pass's algorithmic bytes over the whole timed region
+    all_bytes = (sum(pass_bytes(args.variant, kname, iters, n)[0] for kname in ("fused_prec", "fused_spmv"))
+                 if has_bytes else None)
+    dom = max((k for k in kern if "GBps" in kern[k]), key=lambda k: kern[k]["total_ms"], default=None)
     roofline = None
     if dom is not None:
         ach = kern[dom]["GBps"]
@@ -270,7 +301,7 @@ def main():
                     "frac": round(ach / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic(dom, w.name, args.variant),
                     "traffic_unit": "bytes per launch", "kernel": dom,
-                    "bytes_per_launch": kern[dom]["bytes_per_launch"],
+                    "bytes_per_launch": round(kern[dom]["bytes_per_launch"]),
                     "avg_launch_ms": round(kern[dom]["avg_ms"], 4)}
 
     out = {
@@ -290,9 +321,10 @@ def main():
                    "tol": tol, "maxit": maxit, "variant": args.variant,
                    "iterations_per_solve": iters, "status": res["status"],
                    "final_rel_res": res["final_rel_res"], "true_rel_res": true_rel},
-        "hbm_GBps_per_iteration": round(per_iter_bytes * it_s / 1e9, 1) if per_iter_bytes else None,
-        "hbm_frac_per_iteration": round(per_iter_bytes * it_s / 1e9 / HBM_PEAK_GBS, 4) if per_iter_bytes else None,
-        "bytes_per_point_per_iteration": sum(BYTES_PER_POINT.values()) if per_iter_bytes else None,
+        # algorithmic bytes of both passes over the whole timed region / its wall time
+        "hbm_GBps_whole_solve": round(all_bytes / elapsed / 1e9, 1) if all_bytes else None,
+        "hbm_frac_whole_solve": round(all_bytes / elapsed / 1e9 / HBM_PEAK_GBS, 4) if all_bytes else None,
+        "bytes_per_point_per_iteration": BYTES_BY_VARIANT[args.variant][1] if has_bytes else None,
         "kernels": kern,
         "roofline": roofline,
         "cpu_baseline": None,

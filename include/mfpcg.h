@@ -109,7 +109,7 @@ int pcg_apply_A(pcg_handle *h, const double *x_dev, double *y_dev);
  * Asynchronous. */
 int pcg_precond(pcg_handle *h, const double *r_dev, double *z_dev);
 
-/* Bytes of device workspace a solve with this maxit needs (four N-vectors,
+/* Bytes of device workspace a solve with this maxit needs (five N-vectors,
  * per-workgroup partial sums, the scalar state and the residual history). */
 size_t pcg_solve_workspace_bytes(const pcg_handle *h, int32_t maxit);
 
@@ -117,8 +117,13 @@ size_t pcg_solve_workspace_bytes(const pcg_handle *h, int32_t maxit);
  * (Algorithm 1): per iteration one fused preconditioner pass (Appendix A,
  * Algorithm 3: r -= alpha q, z = M^{-1} r, <r,r>, <r,z>) and one fused
  * stencil pass (Algorithm 2: x += alpha p, p = z + beta p, q = A z + beta q,
- * <p,q>), each followed by a deterministic reduction; 88 bytes per point per
- * iteration (read r, q, x, p, q, z; write r, z, x, p, q).
+ * <p,q>), each followed by a deterministic reduction.  The x update of every
+ * odd step is deferred to the next stencil pass, which applies both terms
+ * (x + alpha_{k-1} p_{k-1} + alpha_k p_k, the same sum as two updates), so x
+ * is read and written every second step; the two latest directions live in
+ * two workspace vectors.  84 bytes per point per step (preconditioner pass:
+ * read r, q, write r, z; stencil pass: read z, p, q, write p, q, and every
+ * second step also read x and the older p, write x).
  *   b_dev          right-hand side, N doubles
  *   x_dev          in: initial guess x0; out: the last iterate.  Must not
  *                  alias b_dev or the workspace.

@@ -45,7 +45,7 @@ struct Op {
 
 // Scalar state of one solve, in device memory (one writer: the reduce kernels).
 struct SolveState {
-    double alpha, beta, kappa_old, R0, R, sigma, kappa, pad0;
+    double alpha, beta, kappa_old, R0, R, sigma, kappa, alpha_prev;
     int32_t k, done, fixup, status, iters, pad1, pad2, pad3;
 };
 
@@ -412,6 +412,189 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     }
 }
 
+// Loads and stores at a wave-uniform base plus a 32-bit per-lane byte offset:
+// the base stays in scalar registers and the address needs no 64-bit vector
+// arithmetic.
+__device__ __forceinline__ double ld_at(const double *base, unsigned boff)
+{
+    return *(const double *)((const char *)base + boff);
+}
+__device__ __forceinline__ void st_at(double *base, unsigned boff, double v)
+{
+    *(double *)((char *)base + boff) = v;
+}
+
+// The column solve of k_column_solve (same elimination, same segment scans)
+// for grids whose tiles are all whole: nx a multiple of 64 and nz a multiple
+// of L, so every thread owns L levels of an existing column and the code is
+// straight-line.  Thread (lane, wave s): column it*64 + lane, segment s.
+// The segment inflow / outflow scans read the other segments' affine maps as
+// (offset, slope) pairs from LDS without branches, so the reads are not
+// serialised behind the recurrence.
+template <int L, int UPD, bool DOTS>
+__global__ __launch_bounds__(kMaxThreads) void k_column_full(
+    const double *__restrict__ rin, const double *__restrict__ q, double *__restrict__ rout,
+    double *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
+    double *__restrict__ partials)
+{
+    constexpr int kSeg = kMaxThreads / kWave;
+    __shared__ double2 sh_ab[kMaxThreads];
+    __shared__ double sh_red[kSeg][2];
+
+    if (st != nullptr && st->done)
+        return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int P = o.P;
+    const int nx = o.nx;
+    const int tile = tile_of_block(blockIdx.x, gridDim.x);
+    const int it = tile / o.ny;
+    const int j = tile - it * o.ny;
+    const int i = it * kWave + lane;
+    const Faces fc = column_faces(o, i, j);
+    const double aT = fc.sum();
+    const int k0 = s * L;
+    const unsigned c8 = (unsigned)i * 8u;
+    const size_t row0 = ((size_t)j * o.nz + k0) * nx;   // level k0 of row j (uniform)
+    const double alpha = (UPD != UPD_NONE && !first) ? st->alpha : 0.0;
+    const double *az = o.az + k0;                       // az[t]: face below level k0+t
+
+    double rr[L];
+    double r2 = 0.0;
+    if (UPD == UPD_Q && !first) {
+        double qv[L];
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            rr[t] = ld_at(rin + row0 + (size_t)t * nx, c8);
+            qv[t] = ld_at(q + row0 + (size_t)t * nx, c8);
+        }
+#pragma unroll
+        for (int t = 0; t < L; ++t)
+            rr[t] = rr[t] - alpha * qv[t];
+    } else if (UPD == UPD_AP && !first) {
+        // r -= alpha (A p): p at levels k0-1 .. k0+L (clamped to the grid),
+        // at j-1 and j+1, and at i-1 / i+1 from the adjacent lanes (lanes 0
+        // and 63 load theirs: one load with two active lanes per level).
+        const int jp = (j + 1 == o.ny) ? 0 : j + 1;
+        const int jm = (j == 0) ? o.ny - 1 : j - 1;
+        const size_t rowp = ((size_t)jp * o.nz + k0) * nx, rowm = ((size_t)jm * o.nz + k0) * nx;
+        const int ie = lane == 0 ? (i == 0 ? nx - 1 : i - 1) : (i + 1 == nx ? 0 : i + 1);
+        const unsigned e8 = (unsigned)ie * 8u;
+        const bool edge = lane == 0 || lane == kWave - 1;
+        const int kb = k0 > 0 ? -1 : 0;                      // level below, clamped
+        const int ka = k0 + L < o.nz ? L : L - 1;            // level above, clamped
+        double pv[L + 2], pyp[L], pym[L], pe[L];
+        pv[0] = ld_at(q + row0 + (ptrdiff_t)kb * nx, c8);
+        pv[L + 1] = ld_at(q + row0 + (size_t)ka * nx, c8);
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            rr[t] = ld_at(rin + row0 + (size_t)t * nx, c8);
+            pv[t + 1] = ld_at(q + row0 + (size_t)t * nx, c8);
+            pyp[t] = ld_at(q + rowp + (size_t)t * nx, c8);
+            pym[t] = ld_at(q + rowm + (size_t)t * nx, c8);
+            pe[t] = edge ? ld_at(q + row0 + (size_t)t * nx, e8) : 0.0;
+        }
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            const double pc = pv[t + 1];
+            const double pl_s = __shfl_up(pc, 1, kWave);
+            const double pr_s = __shfl_down(pc, 1, kWave);
+            const double pl = lane == 0 ? pe[t] : pl_s;
+            const double pr = lane == kWave - 1 ? pe[t] : pr_s;
+            double Ap = o.delta * pc;
+            Ap += fc.xp * (pc - pr);
+            Ap += fc.xm * (pc - pl);
+            Ap += fc.yp * (pc - pyp[t]);
+            Ap += fc.ym * (pc - pym[t]);
+            Ap += az[t + 1] * (pc - pv[t + 2]);
+            Ap += az[t] * (pc - pv[t]);
+            rr[t] = rr[t] - alpha * Ap;
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < L; ++t)
+            rr[t] = ld_at(rin + row0 + (size_t)t * nx, c8);
+    }
+#pragma unroll
+    for (int t = 0; t < L; ++t)
+        r2 += rr[t] * rr[t];
+    if (UPD != UPD_NONE && !first) {
+#pragma unroll
+        for (int t = 0; t < L; ++t)
+            st_at(rout + row0 + (size_t)t * nx, c8, rr[t]);
+    }
+
+    // Local forward sweep: pivots from the true incoming phi, z'' with zero inflow.
+    const size_t ncol = (size_t)nx * o.ny;
+    double phi = s > 0 ? o.phib[(size_t)(s - 1) * ncol + (size_t)j * nx + i] : 0.0;
+    double iD[L], zp[L];
+    double zpp = 0.0, mu = 1.0;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        const double lo = az[t], up = az[t + 1];
+        const double inv = 1.0 / thomas_pivot(o.delta, aT, lo, up, phi);
+        iD[t] = inv;
+        phi = -up * inv;
+        zpp = (rr[t] + lo * zpp) * inv;
+        mu = (lo * inv) * mu;
+    }
+    sh_ab[s * kWave + lane] = make_double2(zpp, mu);
+    __syncthreads();
+    double zin = 0.0;
+#pragma unroll
+    for (int w = 0; w < kSeg - 1; ++w) {
+        const double2 ab = sh_ab[w * kWave + lane];
+        const double nz_ = ab.x + ab.y * zin;
+        zin = w < s ? nz_ : zin;
+    }
+
+    // Forward sweep again with the true inflow, then the local back
+    // substitution with zero value above the segment.
+    double prev = zin;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+        prev = (rr[t] + az[t] * prev) * iD[t];
+        zp[t] = prev;
+    }
+    double znext = 0.0, H = 1.0;
+#pragma unroll
+    for (int t = L - 1; t >= 0; --t) {
+        const double ph = -az[t + 1] * iD[t];
+        znext = zp[t] - ph * znext;
+        H = -ph * H;
+        zp[t] = znext;
+    }
+    __syncthreads();   // every wave has finished reading the first scan
+    sh_ab[s * kWave + lane] = make_double2(znext, H);
+    __syncthreads();
+    double ztop = 0.0;
+#pragma unroll
+    for (int w = kSeg - 1; w > 0; --w) {
+        const double2 ab = sh_ab[w * kWave + lane];
+        const double nt = ab.x + ab.y * ztop;
+        ztop = (w > s && w < P) ? nt : ztop;
+    }
+
+    double kap = 0.0;
+    H = 1.0;
+#pragma unroll
+    for (int t = L - 1; t >= 0; --t) {
+        H = (az[t + 1] * iD[t]) * H;
+        const double zv = zp[t] + ztop * H;
+        kap += rr[t] * zv;
+        st_at(z + row0 + (size_t)t * nx, c8, zv);
+    }
+    if (DOTS) {
+        double v[2] = {r2, kap};
+        double out[2];
+        block_sum<2>(v, sh_red, out);
+        if (threadIdx.x == 0) {
+            partials[2 * (size_t)tile + 0] = out[0];
+            partials[2 * (size_t)tile + 1] = out[1];
+        }
+    }
+}
+
 // Set-up: the Thomas multipliers phi_k at every segment boundary of every
 // column (data independent; computed once per operator).
 __global__ void k_setup_phib(Op o, double *__restrict__ phib)
@@ -508,12 +691,15 @@ __device__ __forceinline__ Sweep sweep_of_thread(const Op &o, int Ls)
 
 enum : int {
     SP_FIRST = 0,     // p = z, q = A z, <p,q>             (first interleaved pass)
-    SP_FUSED = 1,     // x += alpha p, p = z + beta p, q = A z + beta q, <p,q> (Algorithm 2)
     SP_APPLY = 2,     // y = A x
     SP_RESID = 3,     // y = b - A x
     SP_APPLY_DOT = 4, // y = A x, <x, y>  (standard PCG: q = A p, sigma)
     SP_FIRST_AP = 5,  // p = z, <z, A z>                    (no q stored)
-    SP_FUSED_AP = 6   // x += alpha p, p_new = z + beta p, <p_new, A z + beta A p>  (no q stored)
+    SP_FUSED_AP = 6,  // x += alpha p, p_new = z + beta p, <p_new, A z + beta A p>  (no q stored)
+    SP_FUSED_NOX = 7, // Algorithm 2 with the x update deferred: p_new = z + beta p (to
+                      //   p_out), q = A z + beta q, <p_new, q>
+    SP_FUSED_X2 = 8   // SP_FUSED_NOX plus both pending x updates:
+                      //   x += alpha_prev p_prev (read from p_out) + alpha p
 };
 
 // Stencil passes (section 4.2, eq. (18)): the 7-point operator recomputed in
@@ -522,7 +708,15 @@ enum : int {
 // SP_FIRST_AP / SP_FUSED_AP read the old search direction from p (with its
 // neighbours) and write the new one to p_out, a different buffer: an in-place
 // update would let a neighbour read an already-updated value.
-template <int Ls, int MODE>
+// SP_FUSED_NOX / SP_FUSED_X2 update x every second step (the stencil pass of
+// an odd step skips it, the next one applies both terms in one read and write
+// of x): p alternates between two buffers so that the older direction is still
+// there; p_out holds it on entry and receives the new one (each point is read
+// before it is written by the same thread, and p has no neighbour reads here).
+// FULL: every tile is whole (nx a multiple of 64, nz a multiple of Ws * Ls),
+// so no level or column guard is needed and the two edge lanes of a wave load
+// their outside neighbours (i-1 for lane 0, i+1 for lane 63) with one load.
+template <int Ls, int MODE, bool FULL>
 __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restrict__ zin,
                                                          const double *__restrict__ bvec,
                                                          double *__restrict__ u,
@@ -535,17 +729,25 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
     __shared__ double sh_red[kMaxThreads / kWave][1];
     double alpha = 0.0, beta = 0.0;
     bool fixup_only = false;
-    constexpr bool kDot = MODE == SP_FIRST || MODE == SP_FUSED || MODE == SP_APPLY_DOT ||
-                          MODE == SP_FIRST_AP || MODE == SP_FUSED_AP;
-    constexpr bool kFused = MODE == SP_FUSED || MODE == SP_FUSED_AP;
+    constexpr bool kDot = MODE == SP_FIRST || MODE == SP_APPLY_DOT ||
+                          MODE == SP_FIRST_AP || MODE == SP_FUSED_AP || MODE == SP_FUSED_NOX ||
+                          MODE == SP_FUSED_X2;
+    constexpr bool kFused = MODE == SP_FUSED_AP || MODE == SP_FUSED_NOX ||
+                            MODE == SP_FUSED_X2;
+    constexpr bool kX2 = MODE == SP_FUSED_X2;
+    double alpha_prev = 0.0;
+    int fixup = 0;
     if (kDot) {
         if (st->done) {
-            if (!kFused || !st->fixup)
+            fixup = st->fixup;
+            if (!kFused || !fixup)
                 return;
             fixup_only = true;
         }
         alpha = st->alpha;
         beta = st->beta;
+        if (kX2)
+            alpha_prev = st->alpha_prev;
     }
     const Sweep sw = sweep_of_thread(o, Ls);
     const size_t ks = (size_t)o.nx;
@@ -553,11 +755,18 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
 
     if (kFused && fixup_only) {
         // The stop test passed in this iteration: only the pending update
-        // x += alpha p of the last step remains (Algorithm 1 exits before it).
+        // x += alpha p of the last step remains (Algorithm 1 exits before it),
+        // preceded in SP_FUSED_X2 by the deferred one of the step before
+        // (fixup 2: that deferred term alone, after a breakdown).
         if (sw.ok) {
             for (int t = 0; t < sw.len; ++t) {
                 const size_t l = base + (size_t)(sw.k0 + t) * ks;
-                u[l] = u[l] + alpha * p[l];
+                double v = u[l];
+                if (kX2)
+                    v = v + alpha_prev * p_out[l];
+                if (!kX2 || fixup == 1)
+                    v = v + alpha * p[l];
+                u[l] = v;
             }
         }
         return;
@@ -578,7 +787,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
         // for the last column of the grid (periodic wrap).  Those lanes load
         // their neighbour; the others take it from the adjacent lane.
         const bool needL = lane == 0;
-        const bool needR = lane == kWave - 1 || sw.ic + 1 >= o.nx;
+        const bool needR = FULL ? lane == kWave - 1 : (lane == kWave - 1 || sw.ic + 1 >= o.nx);
+        const size_t bxe = needL ? bxm : bxp;   // FULL: the edge lanes' outside neighbour
         auto lev = [&](int k) { return (size_t)min(max(k, 0), o.nz - 1) * ks; };
 
         // Load phase: every value of the wave's Ls levels is requested before
@@ -586,7 +796,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
         constexpr bool kAp = MODE == SP_FUSED_AP;
         double zv[Ls + 2], zyp[Ls], zym[Ls], zxl[Ls], zxr[Ls];
         double pv[kAp ? Ls + 2 : 1], pyp[kAp ? Ls : 1], pym[kAp ? Ls : 1], pxl[kAp ? Ls : 1], pxr[kAp ? Ls : 1];
-        double uo[Ls], po[Ls], qo[Ls];
+        double uo[Ls], po[Ls], qo[Ls], p2[kX2 ? Ls : 1];
 #pragma unroll
         for (int t = 0; t < Ls + 2; ++t) {
             const size_t off = lev(k0 - 1 + t);   // levels k0-1 .. k0+Ls, clamped to the grid
@@ -599,19 +809,31 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
             const size_t off = lev(k0 + t);
             zyp[t] = zin[byp + off];
             zym[t] = zin[bym + off];
-            zxl[t] = needL ? zin[bxm + off] : 0.0;
-            zxr[t] = needR ? zin[bxp + off] : 0.0;
+            if constexpr (FULL) {
+                zxl[t] = (needL || needR) ? zin[bxe + off] : 0.0;
+                zxr[t] = zxl[t];
+            } else {
+                zxl[t] = needL ? zin[bxm + off] : 0.0;
+                zxr[t] = needR ? zin[bxp + off] : 0.0;
+            }
             if constexpr (kAp) {
                 pyp[t] = p[byp + off];
                 pym[t] = p[bym + off];
-                pxl[t] = needL ? p[bxm + off] : 0.0;
-                pxr[t] = needR ? p[bxp + off] : 0.0;
+                if constexpr (FULL) {
+                    pxl[t] = (needL || needR) ? p[bxe + off] : 0.0;
+                    pxr[t] = pxl[t];
+                } else {
+                    pxl[t] = needL ? p[bxm + off] : 0.0;
+                    pxr[t] = needR ? p[bxp + off] : 0.0;
+                }
             }
-            if constexpr (MODE == SP_FUSED || MODE == SP_FUSED_AP)
+            if constexpr (MODE == SP_FUSED_AP || kX2)
                 uo[t] = u[base + off];
-            if constexpr (MODE == SP_FUSED)
+            if constexpr (MODE == SP_FUSED_NOX || kX2)
                 po[t] = p[base + off];
-            if constexpr (MODE == SP_FUSED)
+            if constexpr (kX2)
+                p2[t] = p_out[base + off];
+            if constexpr (MODE == SP_FUSED_NOX || kX2)
                 qo[t] = y[base + off];
             if constexpr (MODE == SP_RESID)
                 qo[t] = bvec[base + off];
@@ -620,7 +842,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
         // Compute phase.
 #pragma unroll
         for (int t = 0; t < Ls; ++t) {
-            if (t < len) {
+            if (FULL || t < len) {
                 const int k = k0 + t;
                 const double lo = o.az[k], up = o.az[k + 1];
                 const double zc = zv[t + 1];
@@ -650,22 +872,23 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
                     Ap += f.ym * (pc - pym[t]);
                     Ap += up * (pc - pv[t + 2]);
                     Ap += lo * (pc - pv[t]);
-                    if (sw.ok) {
+                    if (FULL || sw.ok) {
                         u[l] = uo[t] + alpha * pc;
                         const double pnew = zc + beta * pc;
                         p_out[l] = pnew;
                         acc += pnew * (Az + beta * Ap);
                     }
-                } else if (sw.ok) {
+                } else if (FULL || sw.ok) {
                     if (MODE == SP_FIRST) {
                         p[l] = zc;
                         y[l] = Az;
                         acc += zc * Az;
-                    } else if (MODE == SP_FUSED) {
-                        u[l] = uo[t] + alpha * po[t];
+                    } else if (MODE == SP_FUSED_NOX || kX2) {
+                        if constexpr (kX2)
+                            u[l] = (uo[t] + alpha_prev * p2[t]) + alpha * po[t];
                         const double pn = zc + beta * po[t];
                         const double qn = Az + beta * qo[t];
-                        p[l] = pn;
+                        p_out[l] = pn;
                         y[l] = qn;
                         acc += pn * qn;
                     } else if (MODE == SP_APPLY) {
@@ -1036,10 +1259,13 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce_rz(const double *__restr
     publish(st, hs, k);
 }
 
-// After the stencil pass: sigma = <p, A p>, alpha = kappa / sigma.
+// After the stencil pass: sigma = <p, A p>, alpha = kappa / sigma (the
+// previous alpha is kept for a deferred x update).  deferred != 0: the x
+// update of this step was deferred (see SP_FUSED_NOX), so a breakdown here
+// leaves fixup = 2 for the next stencil pass to apply it alone.
 __global__ __launch_bounds__(kRedThreads) void k_reduce_sigma(const double *__restrict__ partials,
                                                               int nparts, SolveState *st,
-                                                              int iters_if_breakdown)
+                                                              int iters_if_breakdown, int deferred)
 {
     if (st->done) {
         if (threadIdx.x == 0)
@@ -1054,8 +1280,14 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce_sigma(const double *__re
     st->sigma = sigma;
     if (!(sigma > 0.0) || !isfinite(sigma)) {
         st->iters = iters_if_breakdown;
-        finish(st, ST_BREAKDOWN, 0);
+        if (deferred) {
+            st->alpha_prev = st->alpha;
+            finish(st, ST_BREAKDOWN, 2);
+        } else {
+            finish(st, ST_BREAKDOWN, 0);
+        }
     } else {
+        st->alpha_prev = st->alpha;
         st->alpha = st->kappa_old / sigma;
     }
 }

@@ -35,7 +35,9 @@ struct pcg_handle {
     Op op{};
     int col_tiles = 0;     // workgroups of a column pass
     int col_threads = 0;   // threads per column-pass workgroup
+    bool col_full = false; // every column tile whole (nx % 64 == 0, nz % L == 0, 64 columns)
     int pt_tiles = 0;      // workgroups of a point pass
+    bool pt_full = false;  // every sweep tile whole (nx % 64 == 0, nz % (Ws * Ls) == 0)
     size_t n = 0;          // nx*ny*nz
     double *d_az = nullptr, *d_ah = nullptr, *d_phib = nullptr;
     double *d_phib_tri = nullptr;     // boundary multipliers of the last factored stored tridiagonal
@@ -78,7 +80,8 @@ inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // (default: the smallest of 8, 16, 32 with C * ceil(nz / L) <= 1024).
 // Sweep-pass geometry: Ls levels per wave (1, 2, 4 or 8), Ws waves per
 // workgroup (default Ls = 4, Ws = min(4, ceil(nz / 4))).  MFPCG_COL_L, MFPCG_COL_C, MFPCG_ST_L
-// and MFPCG_ST_W override the choice (tuning).
+// and MFPCG_ST_W override the choice (tuning); MFPCG_COL_FULL=0 and MFPCG_ST_FULL=0
+// disable the whole-tile kernels.
 int env_int(const char *name, int dflt)
 {
     const char *v = getenv(name);
@@ -119,7 +122,7 @@ constexpr int kStagePer = 1024;
 int stage_blocks(int nparts) { return nparts <= kDirect ? 0 : (nparts + kStagePer - 1) / kStagePer; }
 
 struct Workspace {
-    double *r, *z, *p, *q, *partials, *stage, *hist;
+    double *r, *z, *p, *q, *p2, *partials, *stage, *hist;
     SolveState *state;
 };
 
@@ -129,7 +132,7 @@ size_t workspace_layout(const pcg_handle *h, int32_t maxit, char *base, Workspac
     const int np = std::max(h->col_tiles, h->pt_tiles);
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-    size_t o_r = take(vec), o_z = take(vec), o_p = take(vec), o_q = take(vec);
+    size_t o_r = take(vec), o_z = take(vec), o_p = take(vec), o_q = take(vec), o_p2 = take(vec);
     size_t o_part = take((size_t)np * 2 * sizeof(double));
     size_t o_stage = take((size_t)std::max(1, stage_blocks(np)) * 2 * sizeof(double));
     size_t o_state = take(sizeof(SolveState));
@@ -139,6 +142,7 @@ size_t workspace_layout(const pcg_handle *h, int32_t maxit, char *base, Workspac
         w->z = (double *)(base + o_z);
         w->p = (double *)(base + o_p);
         w->q = (double *)(base + o_q);
+        w->p2 = (double *)(base + o_p2);
         w->partials = (double *)(base + o_part);
         w->stage = (double *)(base + o_stage);
         w->state = (SolveState *)(base + o_state);
@@ -187,12 +191,12 @@ struct Timed {
         ev.kid = kid;
         ev.tag = tag;
         if (!ev.a || !ev.b) { on = false; return; }
-        hipEventRecord(ev.a, h->stream);
+        (void)hipEventRecord(ev.a, h->stream);
     }
     ~Timed()
     {
         if (!on) return;
-        hipEventRecord(ev.b, h->stream);
+        (void)hipEventRecord(ev.b, h->stream);
         h->pending.push_back(ev);
     }
 };
@@ -222,6 +226,19 @@ void launch_column_lc(pcg_handle *h, const double *rin, const double *q, double 
 {
     dim3 grid(h->col_tiles), block(h->col_threads);
     const Op &o = h->op;
+    if constexpr (C == kWave) {
+        if (!tri && h->col_full) {
+            if (upd == UPD_Q)
+                k_column_full<L, UPD_Q, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials);
+            else if (upd == UPD_AP)
+                k_column_full<L, UPD_AP, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials);
+            else if (dots)
+                k_column_full<L, UPD_NONE, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials);
+            else
+                k_column_full<L, UPD_NONE, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials);
+            return;
+        }
+    }
     if (tri) {
         if (dots)
             k_column_solve<L, C, UPD_NONE, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
@@ -262,21 +279,32 @@ void column(pcg_handle *h, const double *rin, const double *q, double *rout, dou
         launch_column_c<32>(h, rin, q, rout, z, st, first, partials, upd, dots, tri);
 }
 
-template <int Ls>
-void launch_stencil(pcg_handle *h, int mode, const double *zin, const double *b, double *u,
-                    double *p, double *y, const SolveState *st, double *partials, double *p_out)
+template <int Ls, bool FULL>
+void launch_stencil_f(pcg_handle *h, int mode, const double *zin, const double *b, double *u,
+                      double *p, double *y, const SolveState *st, double *partials, double *p_out)
 {
     dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
     const Op &o = h->op;
     switch (mode) {
-    case SP_FIRST: k_stencil<Ls, SP_FIRST><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_FUSED: k_stencil<Ls, SP_FUSED><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_APPLY: k_stencil<Ls, SP_APPLY><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_RESID: k_stencil<Ls, SP_RESID><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_APPLY_DOT: k_stencil<Ls, SP_APPLY_DOT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_FIRST_AP: k_stencil<Ls, SP_FIRST_AP><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    default: k_stencil<Ls, SP_FUSED_AP><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_FIRST: k_stencil<Ls, SP_FIRST, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_APPLY: k_stencil<Ls, SP_APPLY, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_RESID: k_stencil<Ls, SP_RESID, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_APPLY_DOT: k_stencil<Ls, SP_APPLY_DOT, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_FIRST_AP: k_stencil<Ls, SP_FIRST_AP, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_FUSED_NOX: k_stencil<Ls, SP_FUSED_NOX, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_FUSED_X2: k_stencil<Ls, SP_FUSED_X2, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    default: k_stencil<Ls, SP_FUSED_AP, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
     }
+}
+
+template <int Ls>
+void launch_stencil(pcg_handle *h, int mode, const double *zin, const double *b, double *u,
+                    double *p, double *y, const SolveState *st, double *partials, double *p_out)
+{
+    if (h->pt_full)
+        launch_stencil_f<Ls, true>(h, mode, zin, b, u, p, y, st, partials, p_out);
+    else
+        launch_stencil_f<Ls, false>(h, mode, zin, b, u, p, y, st, partials, p_out);
 }
 
 void stencil(pcg_handle *h, int mode, const double *zin, const double *b, double *u, double *p,
@@ -538,7 +566,9 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
     const int P = (nz + L - 1) / L;
     h->col_tiles = (int)(ntc * ny);
     h->col_threads = ((C * P + kWave - 1) / kWave) * kWave;
+    h->col_full = C == kWave && nx % kWave == 0 && nz % L == 0 && env_int("MFPCG_COL_FULL", 1) != 0;
     h->pt_tiles = (int)(ntx * nkt * ny);
+    h->pt_full = nx % kWave == 0 && nz % (g.Ls * g.Ws) == 0 && env_int("MFPCG_ST_FULL", 1) != 0;
     h->n = ncol * (size_t)nz;
     h->op.nx = nx;
     h->op.ny = ny;
@@ -588,20 +618,20 @@ int pcg_destroy(pcg_handle *h)
 {
     if (!h)
         return PCG_OK;
-    hipSetDevice(h->device);
+    (void)hipSetDevice(h->device);
     if (h->stream || h->d_az)
-        hipStreamSynchronize(h->stream);
+        (void)hipStreamSynchronize(h->stream);
     for (auto &e : h->pending) {
-        hipEventDestroy(e.a);
-        hipEventDestroy(e.b);
+        (void)hipEventDestroy(e.a);
+        (void)hipEventDestroy(e.b);
     }
     for (auto e : h->free_events)
-        hipEventDestroy(e);
-    if (h->d_az) hipFree(h->d_az);
-    if (h->d_ah) hipFree(h->d_ah);
-    if (h->d_phib) hipFree(h->d_phib);
-    if (h->d_phib_tri) hipFree(h->d_phib_tri);
-    if (h->h_status) hipHostFree(h->h_status);
+        (void)hipEventDestroy(e);
+    if (h->d_az) (void)hipFree(h->d_az);
+    if (h->d_ah) (void)hipFree(h->d_ah);
+    if (h->d_phib) (void)hipFree(h->d_phib);
+    if (h->d_phib_tri) (void)hipFree(h->d_phib_tri);
+    if (h->h_status) (void)hipHostFree(h->h_status);
     delete h;
     return PCG_OK;
 }
@@ -661,10 +691,14 @@ namespace {
 
 // The interleaved loop of section 4.3, Algorithm 1.  ap = false: Algorithms 2
 // and 3 as printed (q = A z + beta q stored by the stencil pass, r -= alpha q
-// in the preconditioner pass).  ap = true: q is never stored -- the
-// preconditioner pass recomputes A p from p and the stencil pass forms
-// <p_new, A z + beta A p_old>; p alternates between two buffers (the stencil
-// pass reads the old direction around each point while writing the new one).
+// in the preconditioner pass), with the x update of every odd step deferred to
+// the next stencil pass, which applies both terms (x is read and written every
+// second step: 84 instead of 88 bytes per point per step); the directions
+// alternate between p and p2 so that the deferred one is still there.
+// ap = true: q is never stored -- the preconditioner pass recomputes A p from
+// p and the stencil pass forms <p_new, A z + beta A p_old>; p alternates
+// between two buffers (the stencil pass reads the old direction around each
+// point while writing the new one).
 int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool ap, const char *who)
 {
     HostStatus *hs = nullptr;
@@ -674,7 +708,7 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
     double *x = a.x;
     const int32_t maxit = a.maxit;
     const double tol = a.tol;
-    double *pbuf[2] = {w.p, w.q};
+    double *pbuf[2] = {w.p, ap ? w.q : w.p2};
     k_init_state<<<1, 64, 0, h->stream>>>(w.state);
     // a2: r0 = b - A x0
     stencil(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
@@ -684,10 +718,11 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
     for (int k = 0; k <= maxit; ++k) {
         int nred = 0;
         const double *red = nullptr;
-        // search direction read this iteration (ap: written by the previous one)
+        // search direction read this iteration (written by the previous one)
+        // and the buffer of the new one
         double *pin = ap ? pbuf[(k + 1) & 1] : w.q;
-        double *pcur = ap ? pbuf[(k + 1) & 1] : w.p;
-        double *pnext = ap ? pbuf[k & 1] : nullptr;
+        double *pcur = pbuf[(k + 1) & 1];
+        double *pnext = pbuf[k & 1];
         // a3: r -= alpha q (or alpha A p); z = M^{-1} r; partial <r,r>, <r,z>  (Algorithm 3)
         {
             Timed t(h, PCG_KID_FUSED_PREC, k);
@@ -696,7 +731,7 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
         // a4: ||r_k||, stop test, beta
         red = fold_partials(h, w, h->col_tiles, &nred);
         k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, w.hist, k, maxit, tol, hs);
-        hipEventRecord(ev, h->stream);
+        (void)hipEventRecord(ev, h->stream);
         // a5: x += alpha p; p = z + beta p; q = A z + beta q (or A p_new on the
         //     fly); partial <p,q>  (Algorithm 2); only x += alpha p once the
         //     stop test has passed (a7)
@@ -705,27 +740,30 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
             if (ap)
                 stencil(h, k == 0 ? SP_FIRST_AP : SP_FUSED_AP, w.z, nullptr, x, pcur, nullptr, w.state,
                         w.partials, pnext);
+            else if (k == 0)
+                stencil(h, SP_FIRST, w.z, nullptr, x, pnext, w.q, w.state, w.partials);
             else
-                stencil(h, k == 0 ? SP_FIRST : SP_FUSED, w.z, nullptr, x, w.p, w.q, w.state, w.partials);
+                stencil(h, (k & 1) ? SP_FUSED_NOX : SP_FUSED_X2, w.z, nullptr, x, pcur, w.q, w.state,
+                        w.partials, pnext);
         }
         // a6: sigma, alpha
         red = fold_partials(h, w, h->pt_tiles, &nred);
-        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k);
+        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k, !ap && (k & 1));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) {
-            hipEventDestroy(ev);
+            (void)hipEventDestroy(ev);
             return fail(h, PCG_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
         }
         e = hipEventSynchronize(ev);
         if (e != hipSuccess) {
-            hipEventDestroy(ev);
+            (void)hipEventDestroy(ev);
             return fail(h, PCG_ERR_HIP, "%s: hipEventSynchronize: %s", who, hipGetErrorString(e));
         }
         last = k;
         if (((volatile HostStatus *)h->h_status)->done)
             break;
     }
-    hipEventDestroy(ev);
+    (void)hipEventDestroy(ev);
     return solve_epilogue(h, a, w, PCG_KID_FUSED_SPMV, last);
 }
 
@@ -803,7 +841,7 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
         Timed t(h, PCG_KID_VECTOR, 0);
         update_p(h, w.p, w.z, w.state, 1);
     }
-    hipEventRecord(ev, h->stream);
+    (void)hipEventRecord(ev, h->stream);
     hipError_t e = hipEventSynchronize(ev);
     bool done = (e == hipSuccess) && ((volatile HostStatus *)h->h_status)->done;
     for (int k = 1; e == hipSuccess && !done && k <= maxit; ++k) {
@@ -815,14 +853,14 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
                 stencil(h, SP_APPLY_DOT, w.p, nullptr, nullptr, nullptr, w.q, w.state, w.partials);
         }
         red = fold_partials(h, w, h->pt_tiles, &nred);
-        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k - 1);
+        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k - 1, 0);
         {   // x += alpha p ; r -= alpha q ; <r,r>
             Timed t(h, PCG_KID_VECTOR, k);
             update_xr(h, x, w.p, w.r, w.q, w.state, w.partials);
         }
         red = fold_partials(h, w, h->pt_tiles, &nred);
         k_reduce_rr<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, w.hist, k, maxit, tol, hs);
-        hipEventRecord(ev, h->stream);
+        (void)hipEventRecord(ev, h->stream);
         {   // z = M^{-1} r ; kappa = <r,z>
             Timed t(h, PCG_KID_PRECOND, k);
             column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, UPD_NONE, true, tri);
@@ -838,7 +876,7 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
             e = hipEventSynchronize(ev);
         done = (e == hipSuccess) && ((volatile HostStatus *)h->h_status)->done;
     }
-    hipEventDestroy(ev);
+    (void)hipEventDestroy(ev);
     if (e != hipSuccess)
         return fail(h, PCG_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
     return solve_epilogue(h, a, w, -1, -2);

@@ -27,6 +27,12 @@ GRIDS = [
     ("cfg4-2x2x1", lambda: W.config_problem(4, scale_xy=(2, 2), nz=1)),
     ("cfg2-3x1x2", lambda: W.config_problem(2, scale_xy=(3, 1), nz=2)),
     ("cfg4-64x2x33", lambda: W.config_problem(4, scale_xy=(64, 2), nz=33)),
+    # whole tiles (nx a multiple of 64, nz of the segment length): the
+    # straight-line kernels, with 16, 1, 16 and 16 segments of 8, 8, 16, 32 levels
+    ("cfg4-128x3x128", lambda: W.config_problem(4, scale_xy=(128, 3), nz=128)),
+    ("cfg4-64x1x8", lambda: W.config_problem(4, scale_xy=(64, 1), nz=8)),
+    ("cfg2-192x2x256", lambda: W.config_problem(2, scale_xy=(192, 2), nz=256)),
+    ("cfg4-64x2x512", lambda: W.config_problem(4, scale_xy=(64, 2), nz=512)),
 ]
 
 
@@ -160,6 +166,7 @@ SOLVE_CASES = [
     ("cfg3-64x48x32", lambda: W.make_workload(3, scale_xy=(64, 48), nz=32), True),
     ("cfg4-70x45x40", lambda: W.make_workload(4, scale_xy=(70, 45), nz=40), False),
     ("cfg4-130x20x128", lambda: W.make_workload(4, scale_xy=(130, 20), nz=128), False),
+    ("cfg4-128x24x64", lambda: W.make_workload(4, scale_xy=(128, 24), nz=64), False),
 ]
 
 
@@ -289,3 +296,43 @@ def test_profile_counts_launches(dev):
         assert mf.pcg_profile_read(h, mf.PCG_KID_FUSED_PREC) == (0.0, 0)
     finally:
         mf.pcg_destroy(h)
+
+
+def test_whole_tile_kernels_match_generic(dev, monkeypatch):
+    """On a grid of whole tiles the straight-line kernels run by default; with
+    MFPCG_COL_FULL=0 / MFPCG_ST_FULL=0 (read at pcg_create) the guarded ones do.
+    Both compute the same elimination and stencil: apply_A, precond and 5 CG
+    steps of each variant agree to rounding."""
+    import torch
+    w = W.make_workload(4, scale_xy=(128, 6), nz=64)
+    prob = w.problem
+    x = W.uniform_field(prob.nx, prob.ny, prob.nz, 11)
+
+    def run(full):
+        monkeypatch.setenv("MFPCG_COL_FULL", "1" if full else "0")
+        monkeypatch.setenv("MFPCG_ST_FULL", "1" if full else "0")
+        h = mf.pcg_create(prob)
+        try:
+            xd = to_dev(x, dev)
+            y, z = torch.empty_like(xd), torch.empty_like(xd)
+            mf.pcg_apply_A(h, xd, y)
+            mf.pcg_precond(h, xd, z)
+            out = {"y": to_host(y), "z": to_host(z)}
+            for name, fn in SOLVERS.items():
+                bd = to_dev(w.rhs, dev)
+                xs = torch.zeros_like(bd)
+                res = fn(h, bd, xs, 0.0, 5)
+                out[name] = (to_host(xs), res["hist"])
+            torch.cuda.synchronize()
+            return out
+        finally:
+            mf.pcg_destroy(h)
+
+    a, b = run(True), run(False)
+    assert np.abs(a["y"] - b["y"]).max() <= apply_tol(prob, x)
+    assert np.abs(a["z"] - b["z"]).max() <= precond_tol(prob, b["z"])
+    for name in SOLVERS:
+        xa, ha = a[name]
+        xb, hb = b[name]
+        assert np.allclose(ha, hb, rtol=1e-12, atol=0), name
+        assert np.linalg.norm(xa - xb) <= 1e-12 * np.linalg.norm(xb), name
