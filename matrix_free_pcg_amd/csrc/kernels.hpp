@@ -15,12 +15,15 @@
 //    consecutive columns of one row j over Ws*Ls consecutive levels; each
 //    wave sweeps Ls levels with one column per lane, so per-column work (the
 //    face coefficients) is done once per Ls points.
-// Tiles are numbered with j faster than the i-tile (k-tile fastest of all in
-// sweep passes): at any moment every XCD works on the same few rows j, and
-// the j-1 / j+1 and k-1 / k+1 neighbours of a tile are read by workgroups
-// that run at the same time.  Hardware workgroup ids are renumbered so that
-// each of the 8 XCDs (which receive workgroups round-robin) walks one
-// contiguous run of tiles and those neighbours are served by its own L2.
+// Hardware workgroup ids are renumbered so that each of the 8 XCDs (which
+// receive workgroups round-robin) walks one contiguous run of tiles, and tiles
+// are numbered so that the neighbours a tile reads are read by workgroups of
+// the same XCD at about the same time (served by its L2):
+//  * column passes: j faster than the i-tile;
+//  * sweep passes: the i-tiles are grouped in strips of sg tiles (one strip
+//    per XCD); within a strip the k-tile is fastest, then the i-tile, then j.
+//    The j-1 / j+1, k-1 / k+1 and (inside the strip) i-1 / i+1 neighbours of
+//    a tile are read within a few tiles of it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,6 +40,7 @@ struct Op {
     int nx, ny, nz;
     int L, P, C, ntc;      // column passes: segment length, segments, columns per tile, tiles along i
     int Ls, Ws, nkt;       // sweep passes: levels per wave, waves per tile, tiles along k
+    int ntx, sg;           // sweep passes: 64-column tiles along i, tiles per i-strip
     double delta;
     const double *az;      // nz+1 vertical face coefficients (faces 0, nz are 0)
     const double *ah;      // ny*nx per-column alpha_h
@@ -676,10 +680,15 @@ __device__ __forceinline__ Sweep sweep_of_thread(const Op &o, int Ls)
 {
     Sweep sw;
     sw.tile = tile_of_block(blockIdx.x, gridDim.x);
-    const int kt = sw.tile % o.nkt;
-    const int r = sw.tile / o.nkt;
-    sw.j = r % o.ny;
-    const int it = r / o.ny;
+    // strip g holds i-tiles [g*sg, g*sg + gw); the last strip may be narrower
+    const int per_strip = o.sg * o.ny * o.nkt;
+    const int g = sw.tile / per_strip;
+    const int rem = sw.tile - g * per_strip;
+    const int gw = min(o.sg, o.ntx - g * o.sg);
+    const int kt = rem % o.nkt;
+    const int r = rem / o.nkt;
+    sw.j = r / gw;
+    const int it = g * o.sg + (r - sw.j * gw);
     sw.i = it * kWave + (threadIdx.x & (kWave - 1));
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     sw.k0 = (kt * o.Ws + w) * Ls;

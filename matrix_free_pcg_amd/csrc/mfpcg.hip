@@ -583,6 +583,9 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
     h->op.Ls = g.Ls;
     h->op.Ws = g.Ws;
     h->op.nkt = (int)nkt;
+    h->op.ntx = (int)ntx;
+    // one strip of i-tiles per XCD (MFPCG_ST_STRIP overrides; 1 = i-tile slowest)
+    h->op.sg = std::max(1, std::min((int)ntx, env_int("MFPCG_ST_STRIP", (int)((ntx + kXcds - 1) / kXcds))));
     h->op.delta = c->delta;
     hipError_t e;
     if ((e = hipMalloc(&h->d_az, sizeof(double) * (nz + 1))) != hipSuccess ||
