@@ -55,17 +55,33 @@ def _bytes_no_q(kernel, k):
 BYTES_BY_VARIANT = {"interleaved": (_bytes_interleaved, 84), "interleaved_no_q": (_bytes_no_q, 72)}
 
 
+def step_class(variant, kernel, k):
+    """Launches of a pass with the same work per point: the first step, and
+    (interleaved stencil pass) odd / even steps, else the rest."""
+    if k == 0:
+        return "first"
+    if variant == "interleaved" and kernel == "fused_spmv":
+        return "odd" if k % 2 else "even"
+    return "rest"
+
+
+def timed_steps(kernel, iters):
+    """Step index k of every timed launch of a pass, over solves of `iters`
+    steps each: the preconditioner pass runs at k = 0..K, the stencil pass at
+    k = 0..K-1 (its launch at k = K only applies the pending x update and is
+    not timed)."""
+    for K in iters:
+        yield from (range(K + 1) if kernel == "fused_prec" else range(K))
+
+
 def pass_bytes(variant, kernel, iters, n):
     """Total algorithmic bytes and launch count of the timed launches of one
-    pass over solves that took `iters` steps each: the preconditioner pass runs
-    at k = 0..K, the stencil pass at k = 0..K-1 (its launch at k = K only
-    applies the pending x update and is not timed)."""
+    pass over solves that took `iters` steps each."""
     f = BYTES_BY_VARIANT[variant][0]
     tot = cnt = 0
-    for K in iters:
-        ks = range(K + 1) if kernel == "fused_prec" else range(K)
-        tot += sum(f(kernel, k) for k in ks) * n
-        cnt += len(ks)
+    for k in timed_steps(kernel, iters):
+        tot += f(kernel, k) * n
+        cnt += 1
     return tot, cnt
 
 
@@ -77,10 +93,11 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def measured_traffic(kernel: str, workload: str, variant: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when
-    that summary was taken on a different kernel source or workload."""
+def measured_traffic(kernel: str, workload: str, variant: str, iters):
+    """HBM bytes per launch of a pass from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE per dispatch, calibrated on a plain copy,
+    per step class), averaged over the same launches as the timing; None when
+    that summary was taken on a different kernel source, variant or workload."""
     import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
@@ -89,11 +106,19 @@ def measured_traffic(kernel: str, workload: str, variant: str):
             sha = hashlib.sha256(f.read()).hexdigest()
     except OSError:
         return None
-    if (rec.get("source_sha256") != sha or rec.get("variant") != variant
-            or workload not in os.path.basename(TRAFFIC_FILE)):
+    if rec.get("source_sha256") != sha or rec.get("variant") != variant or rec.get("workload") != workload:
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else int(round(k["traffic_bytes"]))
+    classes = rec.get("passes", {}).get(kernel)
+    if not classes:
+        return None
+    tot = cnt = 0
+    for k in timed_steps(kernel, iters):
+        c = classes.get(step_class(variant, kernel, k))
+        if c is None:
+            return None
+        tot += c["traffic_bytes"]
+        cnt += 1
+    return int(round(tot / cnt)) if cnt else None
 
 
 def parse():
@@ -299,7 +324,7 @@ def main():
         ach = kern[dom]["GBps"]
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(dom, w.name, args.variant),
+                    "traffic": measured_traffic(dom, w.name, args.variant, iters),
                     "traffic_unit": "bytes per launch", "kernel": dom,
                     "bytes_per_launch": round(kern[dom]["bytes_per_launch"]),
                     "avg_launch_ms": round(kern[dom]["avg_ms"], 4)}

@@ -19,7 +19,8 @@
 // receive workgroups round-robin) walks one contiguous run of tiles, and tiles
 // are numbered so that the neighbours a tile reads are read by workgroups of
 // the same XCD at about the same time (served by its L2):
-//  * column passes: j faster than the i-tile;
+//  * column passes: the i-tiles are grouped in strips of csg tiles (one strip
+//    per XCD); within a strip the i-tile is faster than j;
 //  * sweep passes: the i-tiles are grouped in strips of sg tiles (one strip
 //    per XCD); within a strip the k-tile is fastest, then the i-tile, then j.
 //    The j-1 / j+1, k-1 / k+1 and (inside the strip) i-1 / i+1 neighbours of
@@ -41,6 +42,7 @@ struct Op {
     int L, P, C, ntc;      // column passes: segment length, segments, columns per tile, tiles along i
     int Ls, Ws, nkt;       // sweep passes: levels per wave, waves per tile, tiles along k
     int ntx, sg;           // sweep passes: 64-column tiles along i, tiles per i-strip
+    int csg;               // column passes: tiles per i-strip
     double delta;
     const double *az;      // nz+1 vertical face coefficients (faces 0, nz are 0)
     const double *ah;      // ny*nx per-column alpha_h
@@ -68,6 +70,23 @@ __device__ __forceinline__ int tile_of_block(int block, int nblocks)
     const int per = nblocks / kXcds, rem = nblocks % kXcds;
     const int x = block % kXcds, q = block / kXcds;
     return x * per + (x < rem ? x : rem) + q;
+}
+
+// Column-pass tile -> (i-tile, j): strips of csg i-tiles, the i-tile faster
+// than j inside a strip (csg = 1: j fastest).
+struct ColTile {
+    int it, j;
+};
+__device__ __forceinline__ ColTile col_tile(const Op &o, int tile)
+{
+    const int per_strip = o.csg * o.ny;
+    const int g = tile / per_strip;
+    const int rem = tile - g * per_strip;
+    const int gw = min(o.csg, o.ntc - g * o.csg);
+    ColTile ct;
+    ct.j = rem / gw;
+    ct.it = g * o.csg + (rem - ct.j * gw);
+    return ct;
 }
 
 __device__ __forceinline__ size_t lin(const Op &o, int i, int j, int k)
@@ -197,8 +216,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     const int P = o.P;
     const bool active = s < P;
     const int tile = tile_of_block(blockIdx.x, gridDim.x);
-    const int it = tile / o.ny;
-    const int j = tile - it * o.ny;
+    const ColTile ct = col_tile(o, tile);
+    const int it = ct.it, j = ct.j;
     const int i = it * C + c;
     const bool ok = active && i < o.nx;
     const int ic = i < o.nx ? i : o.nx - 1;
@@ -452,8 +471,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     const int P = o.P;
     const int nx = o.nx;
     const int tile = tile_of_block(blockIdx.x, gridDim.x);
-    const int it = tile / o.ny;
-    const int j = tile - it * o.ny;
+    const ColTile ct = col_tile(o, tile);
+    const int it = ct.it, j = ct.j;
     const int i = it * kWave + lane;
     const Faces fc = column_faces(o, i, j);
     const double aT = fc.sum();

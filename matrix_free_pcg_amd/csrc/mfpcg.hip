@@ -81,7 +81,8 @@ inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // Sweep-pass geometry: Ls levels per wave (1, 2, 4 or 8), Ws waves per
 // workgroup (default Ls = 4, Ws = min(4, ceil(nz / 4))).  MFPCG_COL_L, MFPCG_COL_C, MFPCG_ST_L
 // and MFPCG_ST_W override the choice (tuning); MFPCG_COL_FULL=0 and MFPCG_ST_FULL=0
-// disable the whole-tile kernels.
+// disable the whole-tile kernels; MFPCG_COL_STRIP and MFPCG_ST_STRIP set the
+// i-strip widths of the tile order (default: one strip per XCD).
 int env_int(const char *name, int dflt)
 {
     const char *v = getenv(name);
@@ -586,6 +587,7 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
     h->op.ntx = (int)ntx;
     // one strip of i-tiles per XCD (MFPCG_ST_STRIP overrides; 1 = i-tile slowest)
     h->op.sg = std::max(1, std::min((int)ntx, env_int("MFPCG_ST_STRIP", (int)((ntx + kXcds - 1) / kXcds))));
+    h->op.csg = std::max(1, std::min((int)ntc, env_int("MFPCG_COL_STRIP", (int)((ntc + kXcds - 1) / kXcds))));
     h->op.delta = c->delta;
     hipError_t e;
     if ((e = hipMalloc(&h->d_az, sizeof(double) * (nz + 1))) != hipSuccess ||
