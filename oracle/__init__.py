@@ -6,7 +6,8 @@ no code with it; ``oracle.c`` names the passage each function follows and the
 readings taken where the source page is silent.
 
 Functions take a :class:`matrix_free_pcg_amd.workloads.Problem` (inputs only)
-and numpy float64 fields of shape (ny, nz, nx).
+and numpy float64 fields of shape (ny, nz, nx); the ``*_f32`` functions take
+and return float32 fields (binary32 arithmetic, readings in ``oracle.c``).
 """
 from __future__ import annotations
 
@@ -47,6 +48,10 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def _fptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
 class Oracle:
     """ctypes view of one compiled oracle library."""
 
@@ -68,6 +73,19 @@ class Oracle:
         lib.orc_pcg.restype = i
         lib.orc_last_loop_seconds.argtypes = []
         lib.orc_last_loop_seconds.restype = d
+        fp = ctypes.POINTER(ctypes.c_float)
+        f = ctypes.c_float
+        ip = ctypes.POINTER(ctypes.c_int)
+        lib.orc_apply_A_f32.argtypes = [i, i, i, f, fp, fp, fp, fp]
+        lib.orc_apply_A_f32.restype = None
+        lib.orc_precond_f32.argtypes = [i, i, i, f, fp, fp, fp, fp]
+        lib.orc_precond_f32.restype = i
+        lib.orc_dot_f32.argtypes = [ctypes.c_size_t, fp, fp]
+        lib.orc_dot_f32.restype = d
+        lib.orc_pcg_f32.argtypes = [i, i, i, d, dp, dp, fp, fp, d, i, dp, ip]
+        lib.orc_pcg_f32.restype = i
+        lib.orc_pcg_mixed.argtypes = [i, i, i, d, dp, dp, dp, dp, d, i, dp, ip]
+        lib.orc_pcg_mixed.restype = i
         self.lib = lib
         self.path = path
 
@@ -102,6 +120,62 @@ class Oracle:
         if st != OK:
             raise FloatingPointError("zero pivot in the column solve")
         return z
+
+    @staticmethod
+    def _field32(a, prob) -> np.ndarray:
+        a = np.ascontiguousarray(a, dtype=np.float32)
+        if a.size != prob.n:
+            raise ValueError(f"field has {a.size} entries, grid needs {prob.n}")
+        return a.reshape(prob.ny, prob.nz, prob.nx)
+
+    def _coeffs32(self, prob):
+        az, ah = self._coeffs(prob)
+        return np.float32(prob.delta), az.astype(np.float32), np.ascontiguousarray(ah, dtype=np.float32)
+
+    def apply_A_f32(self, prob, x) -> np.ndarray:
+        """y = A x in binary32 (coefficients rounded to binary32)."""
+        x = self._field32(x, prob)
+        d32, az, ah = self._coeffs32(prob)
+        y = np.empty_like(x)
+        self.lib.orc_apply_A_f32(prob.nx, prob.ny, prob.nz, float(d32), _fptr(az), _fptr(ah), _fptr(x), _fptr(y))
+        return y
+
+    def precond_f32(self, prob, r) -> np.ndarray:
+        """z = M^{-1} r in binary32 (Thomas algorithm per column)."""
+        r = self._field32(r, prob)
+        d32, az, ah = self._coeffs32(prob)
+        z = np.empty_like(r)
+        st = self.lib.orc_precond_f32(prob.nx, prob.ny, prob.nz, float(d32), _fptr(az), _fptr(ah), _fptr(r), _fptr(z))
+        if st != OK:
+            raise FloatingPointError("zero pivot in the column solve")
+        return z
+
+    def dot_f32(self, a, b) -> float:
+        a = np.ascontiguousarray(a, dtype=np.float32).ravel()
+        b = np.ascontiguousarray(b, dtype=np.float32).ravel()
+        return self.lib.orc_dot_f32(a.size, _fptr(a), _fptr(b))
+
+    def pcg_f32(self, prob, b, x0=None, tol: float = 1e-5, maxit: int = 500):
+        """PCG in binary32.  Returns dict(x (float32), iters, hist (float64), status)."""
+        b = self._field32(b, prob)
+        x = np.zeros_like(b) if x0 is None else self._field32(x0, prob).copy()
+        az, ah = self._coeffs(prob)
+        hist = np.zeros(max(1, maxit + 1))
+        iters = ctypes.c_int(0)
+        st = self.lib.orc_pcg_f32(prob.nx, prob.ny, prob.nz, prob.delta, _ptr(az), _ptr(ah), _fptr(b),
+                                  _fptr(x), float(tol), int(maxit), _ptr(hist), ctypes.byref(iters))
+        return dict(x=x, iters=iters.value, hist=hist[: iters.value + 1].copy(), status=st)
+
+    def pcg_mixed(self, prob, b, x0=None, tol: float = 1e-10, maxit: int = 500):
+        """Binary64 PCG with the preconditioner applied in binary32."""
+        b = self._field(b, prob)
+        x = np.zeros_like(b) if x0 is None else self._field(x0, prob).copy()
+        az, ah = self._coeffs(prob)
+        hist = np.zeros(max(1, maxit + 1))
+        iters = ctypes.c_int(0)
+        st = self.lib.orc_pcg_mixed(prob.nx, prob.ny, prob.nz, prob.delta, _ptr(az), _ptr(ah), _ptr(b),
+                                    _ptr(x), float(tol), int(maxit), _ptr(hist), ctypes.byref(iters))
+        return dict(x=x, iters=iters.value, hist=hist[: iters.value + 1].copy(), status=st)
 
     def dot(self, a, b) -> float:
         a = np.ascontiguousarray(a, dtype=np.float64).ravel()
@@ -160,3 +234,23 @@ def alpha_T(prob, i, j):
 
 def pcg(prob, b, x0=None, tol=1e-10, maxit=500, ntrace=0):
     return default().pcg(prob, b, x0, tol, maxit, ntrace)
+
+
+def apply_A_f32(prob, x):
+    return default().apply_A_f32(prob, x)
+
+
+def precond_f32(prob, r):
+    return default().precond_f32(prob, r)
+
+
+def dot_f32(a, b):
+    return default().dot_f32(a, b)
+
+
+def pcg_f32(prob, b, x0=None, tol=1e-5, maxit=500):
+    return default().pcg_f32(prob, b, x0, tol, maxit)
+
+
+def pcg_mixed(prob, b, x0=None, tol=1e-10, maxit=500):
+    return default().pcg_mixed(prob, b, x0, tol, maxit)

@@ -258,3 +258,237 @@ done:
     free(r); free(z); free(p); free(q);
     return status;
 }
+
+/* ======================================================================
+ * Single precision (section 7 measures the solver in single and in double
+ * precision).  Readings (also in the design notes):
+ *  - fp32 PCG: every vector (x, r, z, p, q), the stencil, the Thomas solve
+ *    and the vector updates in binary32, with the coefficients delta, alpha_z,
+ *    alpha_h rounded to binary32 and the face means and alpha_T formed in
+ *    binary32; the dot products <r,r>, <r,z>, <p,q> are sums of the exact
+ *    products of the binary32 values, accumulated in binary64; the scalars
+ *    alpha = rho/sigma, beta = rho'/rho and the stop test are binary64, and
+ *    alpha, beta are rounded to binary32 where they scale a vector;
+ *  - mixed: the binary64 PCG above whose preconditioner rounds r to binary32,
+ *    solves the column systems in binary32 (as in fp32 PCG) and widens z
+ *    exactly back to binary64.
+ * Compiled with -ffp-contract=off: every float operation is rounded once. */
+
+static float face_f32(const float *ah, size_t a, size_t b)
+{
+    return 0.5f * (ah[a] + ah[b]);
+}
+
+/* alpha_T in binary32 (section 3, eq. (7)), faces as in face_xp .. face_ym. */
+static float alpha_T_f32(int nx, int ny, const float *ah, int i, int j)
+{
+    size_t c = (size_t)j * nx + i;
+    float xp = face_f32(ah, c, (size_t)j * nx + (i + 1) % nx);
+    float xm = face_f32(ah, c, (size_t)j * nx + (i + nx - 1) % nx);
+    float yp = face_f32(ah, c, (size_t)((j + 1) % ny) * nx + i);
+    float ym = face_f32(ah, c, (size_t)((j + ny - 1) % ny) * nx + i);
+    return xp + xm + yp + ym;
+}
+
+/* y = A x in binary32 (section 4.2, eq. (18)); same terms and order as
+ * orc_apply_A. */
+void orc_apply_A_f32(int nx, int ny, int nz, float delta, const float *az,
+                     const float *ah, const float *x, float *y)
+{
+    for (int j = 0; j < ny; ++j)
+        for (int k = 0; k < nz; ++k)
+            for (int i = 0; i < nx; ++i) {
+                int ip = (i + 1) % nx, im = (i + nx - 1) % nx;
+                int jp = (j + 1) % ny, jm = (j + ny - 1) % ny;
+                size_t c = (size_t)j * nx + i;
+                float u = x[at(nx, nz, i, j, k)];
+                float acc = delta * u;
+                acc += face_f32(ah, c, (size_t)j * nx + ip) * (u - x[at(nx, nz, ip, j, k)]);
+                acc += face_f32(ah, c, (size_t)j * nx + im) * (u - x[at(nx, nz, im, j, k)]);
+                acc += face_f32(ah, c, (size_t)jp * nx + i) * (u - x[at(nx, nz, i, jp, k)]);
+                acc += face_f32(ah, c, (size_t)jm * nx + i) * (u - x[at(nx, nz, i, jm, k)]);
+                if (k < nz - 1)
+                    acc += az[k + 1] * (u - x[at(nx, nz, i, j, k + 1)]);
+                if (k > 0)
+                    acc += az[k] * (u - x[at(nx, nz, i, j, k - 1)]);
+                y[at(nx, nz, i, j, k)] = acc;
+            }
+}
+
+/* z = M^{-1} r in binary32 (section 4.2, eq. (19)): the Thomas algorithm of
+ * orc_precond with every operation in binary32. */
+int orc_precond_f32(int nx, int ny, int nz, float delta, const float *az,
+                    const float *ah, const float *r, float *z)
+{
+    float *gam = (float *)malloc(sizeof(float) * (size_t)(nz > 0 ? nz : 1));
+    if (!gam)
+        return ORC_ERR_INVALID;
+    int status = ORC_OK;
+    for (int j = 0; j < ny; ++j)
+        for (int i = 0; i < nx; ++i) {
+            float aT = alpha_T_f32(nx, ny, ah, i, j);
+            float bet = delta + aT + (nz > 1 ? az[1] : 0.0f);
+            if (bet == 0.0f) { status = ORC_ERR_BREAKDOWN; }
+            z[at(nx, nz, i, j, 0)] = r[at(nx, nz, i, j, 0)] / bet;
+            for (int k = 1; k < nz; ++k) {
+                float sub = -az[k];
+                float sup_prev = -az[k];
+                float up = (k < nz - 1) ? az[k + 1] : 0.0f;
+                float diag = delta + aT + az[k] + up;
+                gam[k] = sup_prev / bet;
+                bet = diag - sub * gam[k];
+                if (bet == 0.0f) { status = ORC_ERR_BREAKDOWN; }
+                z[at(nx, nz, i, j, k)] =
+                    (r[at(nx, nz, i, j, k)] - sub * z[at(nx, nz, i, j, k - 1)]) / bet;
+            }
+            for (int k = nz - 2; k >= 0; --k)
+                z[at(nx, nz, i, j, k)] -= gam[k + 1] * z[at(nx, nz, i, j, k + 1)];
+        }
+    free(gam);
+    return status;
+}
+
+/* <a,b> of binary32 vectors: exact products, Neumaier-compensated binary64 sum. */
+double orc_dot_f32(size_t n, const float *a, const float *b)
+{
+    double s = 0.0, c = 0.0;
+    for (size_t l = 0; l < n; ++l) {
+        double t = (double)a[l] * (double)b[l];
+        double u = s + t;
+        if (fabs(s) >= fabs(t))
+            c += (s - u) + t;
+        else
+            c += (t - u) + s;
+        s = u;
+    }
+    return s + c;
+}
+
+/* Coefficients rounded to binary32 (az: nz+1 faces, ah: nx*ny). */
+static int round_coeffs(int nx, int ny, int nz, const double *az, const double *ah,
+                        float **az32, float **ah32)
+{
+    size_t ncol = (size_t)nx * ny;
+    *az32 = (float *)malloc(sizeof(float) * (size_t)(nz + 1));
+    *ah32 = (float *)malloc(sizeof(float) * ncol);
+    if (!*az32 || !*ah32)
+        return ORC_ERR_INVALID;
+    for (int f = 0; f <= nz; ++f) (*az32)[f] = (float)az[f];
+    for (size_t c = 0; c < ncol; ++c) (*ah32)[c] = (float)ah[c];
+    return ORC_OK;
+}
+
+/* PCG in binary32 (the textbook loop of orc_pcg with the readings above). */
+int orc_pcg_f32(int nx, int ny, int nz, double delta, const double *az, const double *ah,
+                const float *b, float *x, double tol, int maxit, double *hist, int *iters_out)
+{
+    size_t n = (size_t)nx * ny * nz;
+    float *r = (float *)malloc(sizeof(float) * n);
+    float *z = (float *)malloc(sizeof(float) * n);
+    float *p = (float *)malloc(sizeof(float) * n);
+    float *q = (float *)malloc(sizeof(float) * n);
+    float *az32 = NULL, *ah32 = NULL;
+    int status = ORC_NOT_CONVERGED, it = 0;
+    const float d32 = (float)delta;
+    if (!r || !z || !p || !q || round_coeffs(nx, ny, nz, az, ah, &az32, &ah32) != ORC_OK) {
+        status = ORC_ERR_INVALID;
+        goto done;
+    }
+    orc_apply_A_f32(nx, ny, nz, d32, az32, ah32, x, q);
+    for (size_t l = 0; l < n; ++l)
+        r[l] = b[l] - q[l];
+    double R0 = sqrt(orc_dot_f32(n, r, r));
+    hist[0] = R0;
+    if (!isfinite(R0)) { status = ORC_ERR_BREAKDOWN; goto done; }
+    if (R0 == 0.0) { status = ORC_OK; goto done; }
+    if (orc_precond_f32(nx, ny, nz, d32, az32, ah32, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+    memcpy(p, z, sizeof(float) * n);
+    double rho = orc_dot_f32(n, r, z);
+    if (!(rho > 0.0) || !isfinite(rho)) { status = ORC_ERR_BREAKDOWN; goto done; }
+    for (int k = 1; k <= maxit; ++k) {
+        orc_apply_A_f32(nx, ny, nz, d32, az32, ah32, p, q);
+        double sigma = orc_dot_f32(n, p, q);
+        if (!(sigma > 0.0) || !isfinite(sigma)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        const float alpha = (float)(rho / sigma);
+        for (size_t l = 0; l < n; ++l) x[l] += alpha * p[l];
+        for (size_t l = 0; l < n; ++l) r[l] -= alpha * q[l];
+        double R = sqrt(orc_dot_f32(n, r, r));
+        hist[k] = R;
+        it = k;
+        if (!isfinite(R)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        if (R == 0.0 || R / R0 < tol) { status = ORC_OK; goto done; }
+        if (k == maxit) break;
+        if (orc_precond_f32(nx, ny, nz, d32, az32, ah32, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double rho_new = orc_dot_f32(n, r, z);
+        if (!(rho_new > 0.0) || !isfinite(rho_new)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        const float beta = (float)(rho_new / rho);
+        rho = rho_new;
+        for (size_t l = 0; l < n; ++l) p[l] = z[l] + beta * p[l];
+    }
+    status = ORC_NOT_CONVERGED;
+done:
+    if (iters_out) *iters_out = it;
+    free(r); free(z); free(p); free(q); free(az32); free(ah32);
+    return status;
+}
+
+/* PCG in binary64 with the preconditioner applied in binary32 (readings
+ * above): the loop of orc_pcg, z = widen(M32^{-1} round32(r)). */
+int orc_pcg_mixed(int nx, int ny, int nz, double delta, const double *az, const double *ah,
+                  const double *b, double *x, double tol, int maxit, double *hist, int *iters_out)
+{
+    size_t n = (size_t)nx * ny * nz;
+    double *r = (double *)malloc(sizeof(double) * n);
+    double *z = (double *)malloc(sizeof(double) * n);
+    double *p = (double *)malloc(sizeof(double) * n);
+    double *q = (double *)malloc(sizeof(double) * n);
+    float *r32 = (float *)malloc(sizeof(float) * n);
+    float *z32 = (float *)malloc(sizeof(float) * n);
+    float *az32 = NULL, *ah32 = NULL;
+    int status = ORC_NOT_CONVERGED, it = 0;
+    const float d32 = (float)delta;
+    if (!r || !z || !p || !q || !r32 || !z32 || round_coeffs(nx, ny, nz, az, ah, &az32, &ah32) != ORC_OK) {
+        status = ORC_ERR_INVALID;
+        goto done;
+    }
+    orc_apply_A(nx, ny, nz, delta, az, ah, x, q);
+    for (size_t l = 0; l < n; ++l)
+        r[l] = b[l] - q[l];
+    double R0 = sqrt(orc_dot(n, r, r));
+    hist[0] = R0;
+    if (!isfinite(R0)) { status = ORC_ERR_BREAKDOWN; goto done; }
+    if (R0 == 0.0) { status = ORC_OK; goto done; }
+    for (size_t l = 0; l < n; ++l) r32[l] = (float)r[l];
+    if (orc_precond_f32(nx, ny, nz, d32, az32, ah32, r32, z32) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+    for (size_t l = 0; l < n; ++l) z[l] = (double)z32[l];
+    memcpy(p, z, sizeof(double) * n);
+    double rho = orc_dot(n, r, z);
+    if (!(rho > 0.0) || !isfinite(rho)) { status = ORC_ERR_BREAKDOWN; goto done; }
+    for (int k = 1; k <= maxit; ++k) {
+        orc_apply_A(nx, ny, nz, delta, az, ah, p, q);
+        double sigma = orc_dot(n, p, q);
+        if (!(sigma > 0.0) || !isfinite(sigma)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double alpha = rho / sigma;
+        for (size_t l = 0; l < n; ++l) x[l] += alpha * p[l];
+        for (size_t l = 0; l < n; ++l) r[l] -= alpha * q[l];
+        double R = sqrt(orc_dot(n, r, r));
+        hist[k] = R;
+        it = k;
+        if (!isfinite(R)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        if (R == 0.0 || R / R0 < tol) { status = ORC_OK; goto done; }
+        if (k == maxit) break;
+        for (size_t l = 0; l < n; ++l) r32[l] = (float)r[l];
+        if (orc_precond_f32(nx, ny, nz, d32, az32, ah32, r32, z32) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+        for (size_t l = 0; l < n; ++l) z[l] = (double)z32[l];
+        double rho_new = orc_dot(n, r, z);
+        if (!(rho_new > 0.0) || !isfinite(rho_new)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double beta = rho_new / rho;
+        rho = rho_new;
+        for (size_t l = 0; l < n; ++l) p[l] = z[l] + beta * p[l];
+    }
+    status = ORC_NOT_CONVERGED;
+done:
+    if (iters_out) *iters_out = it;
+    free(r); free(z); free(p); free(q); free(r32); free(z32); free(az32); free(ah32);
+    return status;
+}

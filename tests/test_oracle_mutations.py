@@ -37,6 +37,11 @@ MUTATIONS = {
     "pcg_p_no_beta": ("for (size_t l = 0; l < n; ++l) p[l] = z[l] + beta * p[l];",
                       "for (size_t l = 0; l < n; ++l) p[l] = z[l];"),
     "pcg_residual_sign": ("r[l] = b[l] - q[l];", "r[l] = b[l] + q[l];"),
+    "f32_stencil_drop_xm": ("acc += face_f32(ah, c, (size_t)j * nx + im) * (u - x[at(nx, nz, im, j, k)]);", ""),
+    "f32_precond_back_sign": ("z[at(nx, nz, i, j, k)] -= gam[k + 1] * z[at(nx, nz, i, j, k + 1)];\n        }\n    free(gam);\n    return status;\n}\n\n/* <a,b> of binary32",
+                              "z[at(nx, nz, i, j, k)] += gam[k + 1] * z[at(nx, nz, i, j, k + 1)];\n        }\n    free(gam);\n    return status;\n}\n\n/* <a,b> of binary32"),
+    "f32_pcg_beta_inverted": ("const float beta = (float)(rho_new / rho);", "const float beta = (float)(rho / rho_new);"),
+    "mixed_stale_residual": ("        for (size_t l = 0; l < n; ++l) r32[l] = (float)r[l];", ""),
 }
 
 
