@@ -40,6 +40,13 @@ METRIC = "PCG iterations/s + achieved HBM GB/s (% roofline), fp64 1024×1024×12
 #     fused_prec  k = 0: 16; k >= 1: read r, p, write r, z (32)
 #     fused_spmv  k = 0: read z, write p (16); k >= 1: read x, p, z, write x, p (40)
 #     -> 72 B per point per step
+#   f32: the interleaved loop with every vector in binary32 (4 B): half of
+#     the interleaved figures -> 42 B per point per step
+#   mixed: binary64 vectors, z in binary32:
+#     fused_prec  k = 0: read r, write z (12); k >= 1: read r, q, write r, z (28)
+#     fused_spmv  k = 0: read z, write p, q (20); odd k: read z, p, q, write p, q
+#                 (36); even k: also read x and the older p, write x (60)
+#     -> 76 B per point per step
 def _bytes_interleaved(kernel, k):
     if kernel == "fused_prec":
         return 16 if k == 0 else 32
@@ -52,7 +59,18 @@ def _bytes_no_q(kernel, k):
     return 16 if k == 0 else 40
 
 
-BYTES_BY_VARIANT = {"interleaved": (_bytes_interleaved, 84), "interleaved_no_q": (_bytes_no_q, 72)}
+def _bytes_f32(kernel, k):
+    return _bytes_interleaved(kernel, k) // 2
+
+
+def _bytes_mixed(kernel, k):
+    if kernel == "fused_prec":
+        return 12 if k == 0 else 28
+    return 20 if k == 0 else (36 if k % 2 else 60)
+
+
+BYTES_BY_VARIANT = {"interleaved": (_bytes_interleaved, 84), "interleaved_no_q": (_bytes_no_q, 72),
+                    "f32": (_bytes_f32, 42), "mixed": (_bytes_mixed, 76)}
 
 
 def step_class(variant, kernel, k):
@@ -60,7 +78,7 @@ def step_class(variant, kernel, k):
     (interleaved stencil pass) odd / even steps, else the rest."""
     if k == 0:
         return "first"
-    if variant == "interleaved" and kernel == "fused_spmv":
+    if variant in ("interleaved", "f32", "mixed") and kernel == "fused_spmv":
         return "odd" if k % 2 else "even"
     return "rest"
 
@@ -128,7 +146,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
                     help="5 = explicit-vs-matrix-free comparison at 2048x2048x128 (50 fixed steps)")
-    ap.add_argument("--variant", default="interleaved", choices=["interleaved", "interleaved_no_q", "standard"])
+    ap.add_argument("--variant", default="interleaved",
+                    choices=["interleaved", "interleaved_no_q", "standard", "f32", "mixed"],
+                    help="f32: every vector in binary32, to tol 1e-5 (the workload's 1e-10 is below "
+                         "binary32 rounding); mixed: binary64 with the preconditioner in binary32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -258,16 +279,18 @@ def main():
         raise SystemExit("bench supports workloads with a stored right-hand side")
     log(f"[bench] {w.name}: inputs generated in {time.perf_counter() - t:.1f}s")
     n = prob.n
-    b = torch.from_numpy(w.rhs).to(dev)
+    vdtype = np.float32 if args.variant == "f32" else np.float64
+    b = torch.from_numpy(w.rhs.astype(vdtype)).to(dev)
     x = torch.zeros_like(b)
     stream = torch.cuda.current_stream()
     h = mf.pcg_create(prob, stream)
-    tol, maxit = w.tol, w.maxit
+    tol, maxit = (1e-5 if args.variant == "f32" else w.tol), w.maxit
     if args.fixed_iterations > 0:
         tol, maxit = 0.0, args.fixed_iterations
     ws = torch.empty(mf.pcg_solve_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
     solve = {"interleaved": mf.pcg_solve, "interleaved_no_q": mf.pcg_solve_no_q,
-             "standard": mf.pcg_solve_standard}[args.variant]
+             "standard": mf.pcg_solve_standard, "f32": mf.pcg_solve_f32,
+             "mixed": mf.pcg_solve_mixed}[args.variant]
     has_bytes = args.variant in BYTES_BY_VARIANT
     torch.cuda.synchronize()
 
@@ -308,10 +331,11 @@ def main():
             kern[name] = ent
 
     # true residual of the last solve, with the library's own stencil
-    r = torch.empty_like(b)
-    mf.pcg_apply_A(h, x, r)
+    xb, bb = x.double(), b.double()
+    r = torch.empty_like(bb)
+    mf.pcg_apply_A(h, xb, r)
     torch.cuda.synchronize()
-    true_rel = float(torch.linalg.vector_norm(b - r) / torch.linalg.vector_norm(b))
+    true_rel = float(torch.linalg.vector_norm(bb - r) / torch.linalg.vector_norm(bb))
     mf.pcg_destroy(h)
 
     it_s = total_iters / elapsed
@@ -340,7 +364,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64",
+        "dtype": {"f32": "f32", "mixed": "f64 (preconditioner f32)"}.get(args.variant, "f64"),
         "data": "synthetic",
         "config": {"workload": w.name, "nx": prob.nx, "ny": prob.ny, "nz": prob.nz,
                    "tol": tol, "maxit": maxit, "variant": args.variant,

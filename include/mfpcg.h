@@ -153,6 +153,42 @@ int pcg_solve_no_q(pcg_handle *h, const double *b_dev, double *x_dev, double tol
                    void *workspace_dev, size_t workspace_bytes, int32_t *iters_out,
                    double *hist_host, int32_t *hist_len_out, double *final_rel_res);
 
+/* ---- Single precision (section 7 runs the solver in single and in double
+ * precision) -------------------------------------------------------------
+ * The same operator and preconditioner with the coefficients (kept in
+ * binary64 by the handle) rounded to binary32 where they are used.  In every
+ * entry point below the dot products <r,r>, <r,z>, <p,q> accumulate in binary64
+ * and the scalars alpha, beta and the stop test are binary64 (alpha and beta
+ * are rounded to binary32 where they scale a binary32 vector). */
+
+/* y = A x in binary32 (eq. (18)); x_dev, y_dev: N floats each, must not
+ * overlap.  Asynchronous. */
+int pcg_apply_A_f32(pcg_handle *h, const float *x_dev, float *y_dev);
+
+/* z = M^{-1} r in binary32 (eq. (19)), one Thomas solve per column with
+ * binary32 pivots; r_dev, z_dev: N floats each, must not overlap.
+ * Asynchronous. */
+int pcg_precond_f32(pcg_handle *h, const float *r_dev, float *z_dev);
+
+/* The interleaved solve of pcg_solve with every vector (b, x and the
+ * workspace's r, z, p, q) in binary32: 42 bytes per point per step.  b_dev,
+ * x_dev: N floats.  The workspace is the one pcg_solve_workspace_bytes sizes
+ * (binary32 vectors use the front of each slot); tol below the binary32
+ * rounding level of the residual (about 1e-6 relative) is not reached.
+ * Returns as pcg_solve. */
+int pcg_solve_f32(pcg_handle *h, const float *b_dev, float *x_dev, double tol, int32_t maxit,
+                  void *workspace_dev, size_t workspace_bytes, int32_t *iters_out,
+                  double *hist_host, int32_t *hist_len_out, double *final_rel_res);
+
+/* pcg_solve with the preconditioner applied in binary32: the preconditioner
+ * pass rounds the (binary64) residual to binary32, solves the column systems
+ * in binary32 and stores z in binary32; the stencil pass widens z exactly.
+ * Everything else is binary64: 76 bytes per point per step.  Same contract
+ * and arguments as pcg_solve. */
+int pcg_solve_mixed(pcg_handle *h, const double *b_dev, double *x_dev, double tol, int32_t maxit,
+                    void *workspace_dev, size_t workspace_bytes, int32_t *iters_out,
+                    double *hist_host, int32_t *hist_len_out, double *final_rel_res);
+
 /* Same contract as pcg_solve, computed by the standard (non-interleaved)
  * PCG of section 4.1: separate stencil, preconditioner and vector-update
  * passes, each vector update fused with its dot product (section 6: the

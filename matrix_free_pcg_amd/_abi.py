@@ -41,6 +41,7 @@ EXPORTED = [
     "pcg_profile_reset", "pcg_profile_read", "pcg_last_error", "pcg_version",
     "pcg_csr_nnz", "pcg_csr_assemble", "pcg_csr_spmv", "pcg_tridiag_assemble",
     "pcg_tridiag_factor", "pcg_tridiag_precond", "pcg_solve_csr",
+    "pcg_apply_A_f32", "pcg_precond_f32", "pcg_solve_f32", "pcg_solve_mixed",
 ]
 
 
@@ -100,7 +101,12 @@ def load():
         lib.pcg_precond.restype = ctypes.c_int
         lib.pcg_solve_workspace_bytes.argtypes = [H, ctypes.c_int32]
         lib.pcg_solve_workspace_bytes.restype = ctypes.c_size_t
-        for name in ("pcg_solve", "pcg_solve_standard", "pcg_solve_no_q"):
+        lib.pcg_apply_A_f32.argtypes = [H, vp, vp]
+        lib.pcg_apply_A_f32.restype = ctypes.c_int
+        lib.pcg_precond_f32.argtypes = [H, vp, vp]
+        lib.pcg_precond_f32.restype = ctypes.c_int
+        for name in ("pcg_solve", "pcg_solve_standard", "pcg_solve_no_q", "pcg_solve_f32",
+                     "pcg_solve_mixed"):
             f = getattr(lib, name)
             f.argtypes = [H, vp, vp, ctypes.c_double, ctypes.c_int32, vp, ctypes.c_size_t,
                           i32p, dp, i32p, dp]
@@ -141,12 +147,12 @@ def _stream_ptr(stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _dev_ptr(t, n: int, name: str) -> int:
+def _dev_ptr(t, n: int, name: str, dtype_name: str = "float64") -> int:
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if t.dtype != torch.float64 or not t.is_cuda:
-        raise TypeError(f"{name} must be a float64 CUDA tensor (got {t.dtype} on {t.device})")
+    if t.dtype != getattr(torch, dtype_name) or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dtype_name} CUDA tensor (got {t.dtype} on {t.device})")
     if not t.is_contiguous() or t.numel() != n:
         raise ValueError(f"{name} must be contiguous with {n} elements (got {tuple(t.shape)})")
     return t.data_ptr()
@@ -238,7 +244,7 @@ def pcg_solve_workspace_bytes(h: Handle, maxit: int) -> int:
     return int(load().pcg_solve_workspace_bytes(h.ptr, int(maxit)))
 
 
-def _solve(fn, h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
+def _solve(fn, h: Handle, b, x, tol: float, maxit: int, workspace=None, dtype_name="float64") -> dict:
     import torch
     need = pcg_solve_workspace_bytes(h, maxit)
     if workspace is None:
@@ -249,7 +255,7 @@ def _solve(fn, h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
     iters = ctypes.c_int32(0)
     hlen = ctypes.c_int32(0)
     rel = ctypes.c_double(0.0)
-    rc = fn(h.ptr, _dev_ptr(b, h.n, "b"), _dev_ptr(x, h.n, "x"), float(tol), int(maxit),
+    rc = fn(h.ptr, _dev_ptr(b, h.n, "b", dtype_name), _dev_ptr(x, h.n, "x", dtype_name), float(tol), int(maxit),
             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             ctypes.byref(iters), hist.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
             ctypes.byref(hlen), ctypes.byref(rel))
@@ -273,6 +279,28 @@ def pcg_solve_no_q(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> d
 def pcg_solve_standard(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
     """Standard (non-interleaved) PCG; same contract as pcg_solve."""
     return _solve(load().pcg_solve_standard, h, b, x, tol, maxit, workspace)
+
+
+def pcg_apply_A_f32(h: Handle, x, y) -> None:
+    """y = A x in binary32 (float32 tensors; asynchronous on the handle's stream)."""
+    rc = load().pcg_apply_A_f32(h.ptr, _dev_ptr(x, h.n, "x", "float32"), _dev_ptr(y, h.n, "y", "float32"))
+    _check(h.ptr, rc)
+
+
+def pcg_precond_f32(h: Handle, r, z) -> None:
+    """z = M^{-1} r in binary32 (float32 tensors; asynchronous)."""
+    rc = load().pcg_precond_f32(h.ptr, _dev_ptr(r, h.n, "r", "float32"), _dev_ptr(z, h.n, "z", "float32"))
+    _check(h.ptr, rc)
+
+
+def pcg_solve_f32(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
+    """Interleaved PCG in binary32 (float32 b, x; binary64 dots and scalars)."""
+    return _solve(load().pcg_solve_f32, h, b, x, tol, maxit, workspace, "float32")
+
+
+def pcg_solve_mixed(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
+    """Interleaved binary64 PCG with the column preconditioner in binary32."""
+    return _solve(load().pcg_solve_mixed, h, b, x, tol, maxit, workspace)
 
 
 def pcg_profile_enable(h: Handle, enable: bool = True) -> None:

@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mfpcg {
 
 constexpr int kWave = 64;
@@ -94,36 +96,61 @@ __device__ __forceinline__ size_t lin(const Op &o, int i, int j, int k)
     return (size_t)i + (size_t)o.nx * ((size_t)k + (size_t)o.nz * (size_t)j);
 }
 
-// Horizontal face coefficients of column (i, j): mean of the two cells'
-// alpha_h (the symmetric per-edge alpha_{T,T'} of section 3, eqs. (6)-(7)).
-struct Faces {
-    double xp, xm, yp, ym;
-    __device__ __forceinline__ double sum() const { return (xp + xm) + (yp + ym); }
-};
+// Precision.  Every kernel is written for two element types: TV, the type of
+// the solver's vectors r, q, x, p, b and of their arithmetic, and TZ (or TI
+// for a stencil's operand), the type of z and of the column solve.  binary64
+// throughout is <double, double>; the single-precision runs of section 7 are
+// <float, float>; binary64 PCG with a binary32 preconditioner is
+// <double, float>.  The coefficients are kept in binary64 and rounded to the
+// arithmetic type where they are used; dot products always accumulate in
+// binary64.
 
-__device__ __forceinline__ Faces column_faces(const Op &o, int i, int j)
+// Horizontal face coefficients of column (i, j): mean of the two cells'
+// alpha_h (the symmetric per-edge alpha_{T,T'} of section 3, eqs. (6)-(7)),
+// formed in T.
+template <typename T>
+struct FacesT {
+    T xp, xm, yp, ym;
+    __device__ __forceinline__ T sum() const { return (xp + xm) + (yp + ym); }
+};
+using Faces = FacesT<double>;
+
+template <typename T>
+__device__ __forceinline__ FacesT<T> column_faces_t(const Op &o, int i, int j)
 {
     const int ip = (i + 1 == o.nx) ? 0 : i + 1;
     const int im = (i == 0) ? o.nx - 1 : i - 1;
     const int jp = (j + 1 == o.ny) ? 0 : j + 1;
     const int jm = (j == 0) ? o.ny - 1 : j - 1;
-    const double c = o.ah[(size_t)j * o.nx + i];
-    Faces f;
-    f.xp = 0.5 * (c + o.ah[(size_t)j * o.nx + ip]);
-    f.xm = 0.5 * (c + o.ah[(size_t)j * o.nx + im]);
-    f.yp = 0.5 * (c + o.ah[(size_t)jp * o.nx + i]);
-    f.ym = 0.5 * (c + o.ah[(size_t)jm * o.nx + i]);
+    const T c = (T)o.ah[(size_t)j * o.nx + i];
+    const T half = (T)0.5;
+    FacesT<T> f;
+    f.xp = half * (c + (T)o.ah[(size_t)j * o.nx + ip]);
+    f.xm = half * (c + (T)o.ah[(size_t)j * o.nx + im]);
+    f.yp = half * (c + (T)o.ah[(size_t)jp * o.nx + i]);
+    f.ym = half * (c + (T)o.ah[(size_t)jm * o.nx + i]);
     return f;
+}
+
+__device__ __forceinline__ Faces column_faces(const Op &o, int i, int j)
+{
+    return column_faces_t<double>(o, i, j);
 }
 
 // Thomas pivot of level k (section 4.2, eq. (19); Appendix A, Algorithm 3):
 // D_k = diag_k - sub_k * phi_{k-1} with diag_k = delta + alpha_T + lo + up,
 // sub_k = -lo, phi_{k-1} = super_{k-1} / D_{k-1}.
-__device__ __forceinline__ double thomas_pivot(double delta, double aT, double lo, double up,
-                                               double phi_prev)
+template <typename T>
+__device__ __forceinline__ T thomas_pivot(T delta, T aT, T lo, T up, T phi_prev)
 {
     return ((delta + aT) + (lo + up)) + lo * phi_prev;
 }
+
+// (offset, slope) of a segment's affine map, exchanged through LDS
+template <typename T>
+struct __align__(2 * sizeof(T)) Pair {
+    T a, b;
+};
 
 // Streams that a pass reads or writes exactly once per element go through
 // non-temporal loads and stores, so that they do not displace the lines that
@@ -211,15 +238,18 @@ __device__ __forceinline__ void block_sum(double (&v)[NV], double (*sh)[NV], dou
 //             neighbours, so that q never has to be stored.
 enum : int { UPD_NONE = 0, UPD_Q = 1, UPD_AP = 2 };
 
-template <int L, int C, int UPD, bool DOTS, bool STORED>
+template <int L, int C, int UPD, bool DOTS, bool STORED, typename TV = double, typename TZ = double>
 __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
-    const double *__restrict__ rin, const double *__restrict__ q, double *__restrict__ rout,
-    double *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
+    const TV *__restrict__ rin, const TV *__restrict__ q, TV *__restrict__ rout,
+    TZ *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
     double *__restrict__ partials, const double *__restrict__ tri,
-    const double *__restrict__ phib_tab)
+    const TZ *__restrict__ phib_tab)
 {
-    __shared__ double sh_a[kMaxThreads];
-    __shared__ double sh_b[kMaxThreads];
+    static_assert((UPD != UPD_AP && !STORED) ||
+                      (std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
+                  "the stored-matrix and recomputed-Ap forms are binary64 only");
+    __shared__ TZ sh_a[kMaxThreads];
+    __shared__ TZ sh_b[kMaxThreads];
     __shared__ double sh_red[kMaxThreads / kWave][2];
 
     if (st != nullptr && st->done)
@@ -236,32 +266,33 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     const int i = it * C + c;
     const bool ok = active && i < o.nx;
     const int ic = i < o.nx ? i : o.nx - 1;
-    const Faces fc = column_faces(o, ic, j);
-    const double aT = fc.sum();
+    const FacesT<TZ> fc = column_faces_t<TZ>(o, ic, j);
+    const TZ aT = fc.sum();
+    const TZ delta = (TZ)o.delta;
     const int k0 = s * L;
     const int len = active ? min(L, o.nz - k0) : 0;
     const size_t base = lin(o, ic, j, 0);
     const size_t ks = (size_t)o.nx;
-    const double alpha = (UPD != UPD_NONE && !first) ? st->alpha : 0.0;
+    const TV alpha = (UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0;
 
     // The segment's vertical face coefficients: face(t) couples levels
     // k0+t-1 and k0+t (face(0) below the segment, face(len) above it).  With
     // 64 columns the segment is wave-uniform and the loads are scalar; with
     // 32 a wave holds two segments and a register copy avoids reloading them.
-    double fz[L + 1];
+    TZ fz[L + 1];
     if constexpr (C != kWave) {
 #pragma unroll
         for (int t = 0; t <= L; ++t)
-            fz[t] = (t <= len) ? o.az[k0 + t] : 0.0;
+            fz[t] = (t <= len) ? (TZ)o.az[k0 + t] : (TZ)0;
     }
-    auto face = [&](int t) -> double {
+    auto face = [&](int t) -> TZ {
         if constexpr (C == kWave)
-            return o.az[k0 + t];
+            return (TZ)o.az[k0 + t];
         else
             return fz[t];
     };
     // stored coefficients of the segment's levels: lo = -sub, up = -sup, diag
-    double slo[STORED ? L : 1], sup_[STORED ? L : 1], sdg[STORED ? L : 1];
+    TZ slo[STORED ? L : 1], sup_[STORED ? L : 1], sdg[STORED ? L : 1];
     if constexpr (STORED) {
         const size_t n = (size_t)o.nx * o.ny * o.nz;
 #pragma unroll
@@ -273,14 +304,15 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
             sup_[t] = in ? -ld_s(tri + 2 * n + l) : 0.0;
         }
     }
-    auto lo_at = [&](int t) -> double {
+    auto lo_at = [&](int t) -> TZ {
         if constexpr (STORED) return slo[t]; else return face(t);
     };
-    auto up_at = [&](int t) -> double {
+    auto up_at = [&](int t) -> TZ {
         if constexpr (STORED) return sup_[t]; else return face(t + 1);
     };
 
-    double rr[L], iD[L], zp[L];
+    TV rr[L];
+    TZ iD[L], zp[L];
     double r2 = 0.0;
     if constexpr (UPD == UPD_AP) {
         // q = p; (A p) at the segment's levels.  Load phase first (r, p at
@@ -344,7 +376,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     } else {
 #pragma unroll
         for (int t = 0; t < L; ++t) {
-            double v = 0.0;
+            TV v = (TV)0;
             if (t < len && ok) {
                 const size_t l = base + (size_t)(k0 + t) * ks;
                 v = ld_s(rin + l);
@@ -352,7 +384,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
                     v = v - alpha * ld_s(q + l);
             }
             rr[t] = v;
-            r2 += v * v;
+            r2 += (double)v * (double)v;
         }
     }
     if (UPD != UPD_NONE && !first && ok) {
@@ -362,26 +394,27 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
                 st_s(rout + base + (size_t)(k0 + t) * ks, rr[t]);
     }
 
-    // Local forward sweep: pivots from the true incoming phi, z'' with zero inflow.
+    // Local forward sweep: pivots from the true incoming phi, z'' with zero
+    // inflow; the right-hand side rounded to TZ.
     const size_t ncol = (size_t)o.nx * o.ny;
-    double phi = (s > 0 && active) ? ld_s(phib_tab + (size_t)(s - 1) * ncol + (size_t)j * o.nx + ic) : 0.0;
-    double zpp = 0.0, mu = 1.0;
+    TZ phi = (s > 0 && active) ? ld_s(phib_tab + (size_t)(s - 1) * ncol + (size_t)j * o.nx + ic) : (TZ)0;
+    TZ zpp = 0, mu = 1;
 #pragma unroll
     for (int t = 0; t < L; ++t) {
         if (t < len) {
-            const double lo = lo_at(t), up = up_at(t);
-            double D;
+            const TZ lo = lo_at(t), up = up_at(t);
+            TZ D;
             if constexpr (STORED)
                 D = sdg[t] + lo * phi;
             else
-                D = thomas_pivot(o.delta, aT, lo, up, phi);
-            const double inv = 1.0 / D;
+                D = thomas_pivot(delta, aT, lo, up, phi);
+            const TZ inv = (TZ)1 / D;
             iD[t] = inv;
             phi = -up * inv;
-            zpp = (rr[t] + lo * zpp) * inv;
+            zpp = ((TZ)rr[t] + lo * zpp) * inv;
             mu = (lo * inv) * mu;
         } else {
-            iD[t] = 0.0;
+            iD[t] = 0;
         }
     }
     if (active) {
@@ -389,27 +422,27 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         sh_b[s * C + c] = mu;
     }
     __syncthreads();
-    double zin = 0.0;
+    TZ zin = 0;
     for (int w = 0; w < s && active; ++w)
         zin = sh_a[w * C + c] + sh_b[w * C + c] * zin;
 
     // Forward sweep again with the true inflow: z'_k of the serial algorithm.
-    double prev = zin;
+    TZ prev = zin;
 #pragma unroll
     for (int t = 0; t < L; ++t) {
         if (t < len) {
-            const double lo = lo_at(t);
-            prev = (rr[t] + lo * prev) * iD[t];
+            const TZ lo = lo_at(t);
+            prev = ((TZ)rr[t] + lo * prev) * iD[t];
             zp[t] = prev;
         }
     }
     // Local back substitution with zero value above the segment.
-    double znext = 0.0, H = 1.0;
+    TZ znext = 0, H = 1;
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
         if (t < len) {
-            const double up = up_at(t);
-            const double ph = -up * iD[t];
+            const TZ up = up_at(t);
+            const TZ ph = -up * iD[t];
             znext = zp[t] - ph * znext;
             H = -ph * H;
             zp[t] = znext;
@@ -421,20 +454,20 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         sh_b[s * C + c] = H;       // response of that level to the value above
     }
     __syncthreads();
-    double ztop = 0.0;
+    TZ ztop = 0;
     if (active)
         for (int w = P - 1; w > s; --w)
             ztop = sh_a[w * C + c] + sh_b[w * C + c] * ztop;
 
     double kap = 0.0;
-    H = 1.0;
+    H = 1;
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
         if (t < len) {
-            const double up = up_at(t);
+            const TZ up = up_at(t);
             H = (up * iD[t]) * H;
-            const double zv = zp[t] + ztop * H;
-            kap += rr[t] * zv;
+            const TZ zv = zp[t] + ztop * H;
+            kap += (double)rr[t] * (double)zv;
             if (ok)
                 st_s(z + base + (size_t)(k0 + t) * ks, zv);
         }
@@ -453,13 +486,15 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
 // Loads and stores at a wave-uniform base plus a 32-bit per-lane byte offset:
 // the base stays in scalar registers and the address needs no 64-bit vector
 // arithmetic.
-__device__ __forceinline__ double ld_at(const double *base, unsigned boff)
+template <typename T>
+__device__ __forceinline__ T ld_at(const T *base, unsigned boff)
 {
-    return ld_s((const double *)((const char *)base + boff));
+    return ld_s((const T *)((const char *)base + boff));
 }
-__device__ __forceinline__ void st_at(double *base, unsigned boff, double v)
+template <typename T>
+__device__ __forceinline__ void st_at(T *base, unsigned boff, T v)
 {
-    st_s((double *)((char *)base + boff), v);
+    st_s((T *)((char *)base + boff), v);
 }
 
 // The column solve of k_column_solve (same elimination, same segment scans)
@@ -469,14 +504,16 @@ __device__ __forceinline__ void st_at(double *base, unsigned boff, double v)
 // The segment inflow / outflow scans read the other segments' affine maps as
 // (offset, slope) pairs from LDS without branches, so the reads are not
 // serialised behind the recurrence.
-template <int L, int UPD, bool DOTS>
+template <int L, int UPD, bool DOTS, typename TV = double, typename TZ = double>
 __global__ __launch_bounds__(kMaxThreads) void k_column_full(
-    const double *__restrict__ rin, const double *__restrict__ q, double *__restrict__ rout,
-    double *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
-    double *__restrict__ partials)
+    const TV *__restrict__ rin, const TV *__restrict__ q, TV *__restrict__ rout,
+    TZ *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
+    double *__restrict__ partials, const TZ *__restrict__ phib)
 {
+    static_assert(UPD != UPD_AP || (std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
+                  "the recomputed-Ap form is binary64 only");
     constexpr int kSeg = kMaxThreads / kWave;
-    __shared__ double2 sh_ab[kMaxThreads];
+    __shared__ Pair<TZ> sh_ab[kMaxThreads];
     __shared__ double sh_red[kSeg][2];
 
     if (st != nullptr && st->done)
@@ -489,22 +526,24 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     const ColTile ct = col_tile(o, tile);
     const int it = ct.it, j = ct.j;
     const int i = it * kWave + lane;
-    const Faces fc = column_faces(o, i, j);
-    const double aT = fc.sum();
+    const FacesT<TZ> fz = column_faces_t<TZ>(o, i, j);
+    const TZ aT = fz.sum();
+    const TZ delta = (TZ)o.delta;
     const int k0 = s * L;
-    const unsigned c8 = (unsigned)i * 8u;
+    const unsigned cv = (unsigned)i * (unsigned)sizeof(TV);   // lane's byte offset in a TV row
+    const unsigned cz = (unsigned)i * (unsigned)sizeof(TZ);   // ... in a TZ row
     const size_t row0 = ((size_t)j * o.nz + k0) * nx;   // level k0 of row j (uniform)
-    const double alpha = (UPD != UPD_NONE && !first) ? st->alpha : 0.0;
+    const TV alpha = (UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0;
     const double *az = o.az + k0;                       // az[t]: face below level k0+t
 
-    double rr[L];
+    TV rr[L];
     double r2 = 0.0;
     if (UPD == UPD_Q && !first) {
-        double qv[L];
+        TV qv[L];
 #pragma unroll
         for (int t = 0; t < L; ++t) {
-            rr[t] = ld_at(rin + row0 + (size_t)t * nx, c8);
-            qv[t] = ld_at(q + row0 + (size_t)t * nx, c8);
+            rr[t] = ld_at(rin + row0 + (size_t)t * nx, cv);
+            qv[t] = ld_at(q + row0 + (size_t)t * nx, cv);
         }
 #pragma unroll
         for (int t = 0; t < L; ++t)
@@ -513,6 +552,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         // r -= alpha (A p): p at levels k0-1 .. k0+L (clamped to the grid),
         // at j-1 and j+1, and at i-1 / i+1 from the adjacent lanes (lanes 0
         // and 63 load theirs: one load with two active lanes per level).
+        const Faces fc = column_faces(o, i, j);
         const int jp = (j + 1 == o.ny) ? 0 : j + 1;
         const int jm = (j == 0) ? o.ny - 1 : j - 1;
         const size_t rowp = ((size_t)jp * o.nz + k0) * nx, rowm = ((size_t)jm * o.nz + k0) * nx;
@@ -522,14 +562,14 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         const int kb = k0 > 0 ? -1 : 0;                      // level below, clamped
         const int ka = k0 + L < o.nz ? L : L - 1;            // level above, clamped
         double pv[L + 2], pyp[L], pym[L], pe[L];
-        pv[0] = ld_at(q + row0 + (ptrdiff_t)kb * nx, c8);
-        pv[L + 1] = ld_at(q + row0 + (size_t)ka * nx, c8);
+        pv[0] = ld_at(q + row0 + (ptrdiff_t)kb * nx, cv);
+        pv[L + 1] = ld_at(q + row0 + (size_t)ka * nx, cv);
 #pragma unroll
         for (int t = 0; t < L; ++t) {
-            rr[t] = ld_at(rin + row0 + (size_t)t * nx, c8);
-            pv[t + 1] = ld_at(q + row0 + (size_t)t * nx, c8);
-            pyp[t] = ld_at(q + rowp + (size_t)t * nx, c8);
-            pym[t] = ld_at(q + rowm + (size_t)t * nx, c8);
+            rr[t] = ld_at(rin + row0 + (size_t)t * nx, cv);
+            pv[t + 1] = ld_at(q + row0 + (size_t)t * nx, cv);
+            pyp[t] = ld_at(q + rowp + (size_t)t * nx, cv);
+            pym[t] = ld_at(q + rowm + (size_t)t * nx, cv);
             pe[t] = edge ? ld_at(q + row0 + (size_t)t * nx, e8) : 0.0;
         }
 #pragma unroll
@@ -551,76 +591,77 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     } else {
 #pragma unroll
         for (int t = 0; t < L; ++t)
-            rr[t] = ld_at(rin + row0 + (size_t)t * nx, c8);
+            rr[t] = ld_at(rin + row0 + (size_t)t * nx, cv);
     }
 #pragma unroll
     for (int t = 0; t < L; ++t)
-        r2 += rr[t] * rr[t];
+        r2 += (double)rr[t] * (double)rr[t];
     if (UPD != UPD_NONE && !first) {
 #pragma unroll
         for (int t = 0; t < L; ++t)
-            st_at(rout + row0 + (size_t)t * nx, c8, rr[t]);
+            st_at(rout + row0 + (size_t)t * nx, cv, rr[t]);
     }
 
-    // Local forward sweep: pivots from the true incoming phi, z'' with zero inflow.
+    // Local forward sweep: pivots from the true incoming phi, z'' with zero
+    // inflow; the right-hand side rounded to TZ.
     const size_t ncol = (size_t)nx * o.ny;
-    double phi = s > 0 ? ld_s(o.phib + (size_t)(s - 1) * ncol + (size_t)j * nx + i) : 0.0;
-    double iD[L], zp[L];
-    double zpp = 0.0, mu = 1.0;
+    TZ phi = s > 0 ? ld_s(phib + (size_t)(s - 1) * ncol + (size_t)j * nx + i) : (TZ)0;
+    TZ iD[L], zp[L];
+    TZ zpp = 0, mu = 1;
 #pragma unroll
     for (int t = 0; t < L; ++t) {
-        const double lo = az[t], up = az[t + 1];
-        const double inv = 1.0 / thomas_pivot(o.delta, aT, lo, up, phi);
+        const TZ lo = (TZ)az[t], up = (TZ)az[t + 1];
+        const TZ inv = (TZ)1 / thomas_pivot(delta, aT, lo, up, phi);
         iD[t] = inv;
         phi = -up * inv;
-        zpp = (rr[t] + lo * zpp) * inv;
+        zpp = ((TZ)rr[t] + lo * zpp) * inv;
         mu = (lo * inv) * mu;
     }
-    sh_ab[s * kWave + lane] = make_double2(zpp, mu);
+    sh_ab[s * kWave + lane] = Pair<TZ>{zpp, mu};
     __syncthreads();
-    double zin = 0.0;
+    TZ zin = 0;
 #pragma unroll
     for (int w = 0; w < kSeg - 1; ++w) {
-        const double2 ab = sh_ab[w * kWave + lane];
-        const double nz_ = ab.x + ab.y * zin;
+        const Pair<TZ> ab = sh_ab[w * kWave + lane];
+        const TZ nz_ = ab.a + ab.b * zin;
         zin = w < s ? nz_ : zin;
     }
 
     // Forward sweep again with the true inflow, then the local back
     // substitution with zero value above the segment.
-    double prev = zin;
+    TZ prev = zin;
 #pragma unroll
     for (int t = 0; t < L; ++t) {
-        prev = (rr[t] + az[t] * prev) * iD[t];
+        prev = ((TZ)rr[t] + (TZ)az[t] * prev) * iD[t];
         zp[t] = prev;
     }
-    double znext = 0.0, H = 1.0;
+    TZ znext = 0, H = 1;
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
-        const double ph = -az[t + 1] * iD[t];
+        const TZ ph = -(TZ)az[t + 1] * iD[t];
         znext = zp[t] - ph * znext;
         H = -ph * H;
         zp[t] = znext;
     }
     __syncthreads();   // every wave has finished reading the first scan
-    sh_ab[s * kWave + lane] = make_double2(znext, H);
+    sh_ab[s * kWave + lane] = Pair<TZ>{znext, H};
     __syncthreads();
-    double ztop = 0.0;
+    TZ ztop = 0;
 #pragma unroll
     for (int w = kSeg - 1; w > 0; --w) {
-        const double2 ab = sh_ab[w * kWave + lane];
-        const double nt = ab.x + ab.y * ztop;
+        const Pair<TZ> ab = sh_ab[w * kWave + lane];
+        const TZ nt = ab.a + ab.b * ztop;
         ztop = (w > s && w < P) ? nt : ztop;
     }
 
     double kap = 0.0;
-    H = 1.0;
+    H = 1;
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
-        H = (az[t + 1] * iD[t]) * H;
-        const double zv = zp[t] + ztop * H;
-        kap += rr[t] * zv;
-        st_at(z + row0 + (size_t)t * nx, c8, zv);
+        H = ((TZ)az[t + 1] * iD[t]) * H;
+        const TZ zv = zp[t] + ztop * H;
+        kap += (double)rr[t] * (double)zv;
+        st_at(z + row0 + (size_t)t * nx, cz, zv);
     }
     if (DOTS) {
         double v[2] = {r2, kap};
@@ -634,8 +675,9 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
 }
 
 // Set-up: the Thomas multipliers phi_k at every segment boundary of every
-// column (data independent; computed once per operator).
-__global__ void k_setup_phib(Op o, double *__restrict__ phib)
+// column (data independent; computed once per operator and precision, in T).
+template <typename T>
+__global__ void k_setup_phib(Op o, T *__restrict__ phib)
 {
     const size_t ncol = (size_t)o.nx * o.ny;
     const size_t col = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -643,11 +685,12 @@ __global__ void k_setup_phib(Op o, double *__restrict__ phib)
         return;
     const int j = (int)(col / o.nx);
     const int i = (int)(col - (size_t)j * o.nx);
-    const double aT = column_faces(o, i, j).sum();
-    double phi = 0.0;
+    const T aT = column_faces_t<T>(o, i, j).sum();
+    const T delta = (T)o.delta;
+    T phi = 0;
     for (int k = 0; k < o.nz; ++k) {
-        const double lo = o.az[k], up = o.az[k + 1];
-        const double inv = 1.0 / thomas_pivot(o.delta, aT, lo, up, phi);
+        const T lo = (T)o.az[k], up = (T)o.az[k + 1];
+        const T inv = (T)1 / thomas_pivot(delta, aT, lo, up, phi);
         phi = -up * inv;
         const int kk = k + 1;
         if (kk % o.L == 0 && kk / o.L < o.P)
@@ -759,18 +802,21 @@ enum : int {
 // FULL: every tile is whole (nx a multiple of 64, nz a multiple of Ws * Ls),
 // so no level or column guard is needed and the two edge lanes of a wave load
 // their outside neighbours (i-1 for lane 0, i+1 for lane 63) with one load.
-template <int Ls, int MODE, bool FULL>
-__global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restrict__ zin,
-                                                         const double *__restrict__ bvec,
-                                                         double *__restrict__ u,
-                                                         double *__restrict__ p,
-                                                         double *__restrict__ y, Op o,
+template <int Ls, int MODE, bool FULL, typename TV = double, typename TI = double>
+__global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ zin,
+                                                         const TV *__restrict__ bvec,
+                                                         TV *__restrict__ u,
+                                                         TV *__restrict__ p,
+                                                         TV *__restrict__ y, Op o,
                                                          const SolveState *__restrict__ st,
                                                          double *__restrict__ partials,
-                                                         double *__restrict__ p_out)
+                                                         TV *__restrict__ p_out)
 {
+    static_assert((MODE != SP_FIRST_AP && MODE != SP_FUSED_AP) ||
+                      (std::is_same<TV, double>::value && std::is_same<TI, double>::value),
+                  "the q-free forms are binary64 only");
     __shared__ double sh_red[kMaxThreads / kWave][1];
-    double alpha = 0.0, beta = 0.0;
+    TV alpha = 0, beta = 0;
     bool fixup_only = false;
     constexpr bool kDot = MODE == SP_FIRST || MODE == SP_APPLY_DOT ||
                           MODE == SP_FIRST_AP || MODE == SP_FUSED_AP || MODE == SP_FUSED_NOX ||
@@ -778,7 +824,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
     constexpr bool kFused = MODE == SP_FUSED_AP || MODE == SP_FUSED_NOX ||
                             MODE == SP_FUSED_X2;
     constexpr bool kX2 = MODE == SP_FUSED_X2;
-    double alpha_prev = 0.0;
+    TV alpha_prev = 0;
     int fixup = 0;
     if (kDot) {
         if (st->done) {
@@ -787,10 +833,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
                 return;
             fixup_only = true;
         }
-        alpha = st->alpha;
-        beta = st->beta;
+        alpha = (TV)st->alpha;
+        beta = (TV)st->beta;
         if (kX2)
-            alpha_prev = st->alpha_prev;
+            alpha_prev = (TV)st->alpha_prev;
     }
     const Sweep sw = sweep_of_thread(o, Ls);
     const size_t ks = (size_t)o.nx;
@@ -804,7 +850,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
         if (sw.ok) {
             for (int t = 0; t < sw.len; ++t) {
                 const size_t l = base + (size_t)(sw.k0 + t) * ks;
-                double v = u[l];
+                TV v = u[l];
                 if (kX2)
                     v = v + alpha_prev * p_out[l];
                 if (!kX2 || fixup == 1)
@@ -817,7 +863,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
 
     double acc = 0.0;
     if (sw.len > 0) {
-        const Faces f = column_faces(o, sw.ic, sw.j);
+        const FacesT<TV> f = column_faces_t<TV>(o, sw.ic, sw.j);
+        const TV delta = (TV)o.delta;
         const int lane = threadIdx.x & (kWave - 1);
         const int ip = (sw.ic + 1 == o.nx) ? 0 : sw.ic + 1;
         const int im = (sw.ic == 0) ? o.nx - 1 : sw.ic - 1;
@@ -837,27 +884,27 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
         // Load phase: every value of the wave's Ls levels is requested before
         // any is used, so a wave waits for one memory round trip, not Ls.
         constexpr bool kAp = MODE == SP_FUSED_AP;
-        double zv[Ls + 2], zyp[Ls], zym[Ls], zxl[Ls], zxr[Ls];
-        double pv[kAp ? Ls + 2 : 1], pyp[kAp ? Ls : 1], pym[kAp ? Ls : 1], pxl[kAp ? Ls : 1], pxr[kAp ? Ls : 1];
-        double uo[Ls], po[Ls], qo[Ls], p2[kX2 ? Ls : 1];
+        TV zv[Ls + 2], zyp[Ls], zym[Ls], zxl[Ls], zxr[Ls];   // the operand, widened to TV
+        TV pv[kAp ? Ls + 2 : 1], pyp[kAp ? Ls : 1], pym[kAp ? Ls : 1], pxl[kAp ? Ls : 1], pxr[kAp ? Ls : 1];
+        TV uo[Ls], po[Ls], qo[Ls], p2[kX2 ? Ls : 1];
 #pragma unroll
         for (int t = 0; t < Ls + 2; ++t) {
             const size_t off = lev(k0 - 1 + t);   // levels k0-1 .. k0+Ls, clamped to the grid
-            zv[t] = zin[base + off];
+            zv[t] = (TV)zin[base + off];
             if constexpr (kAp)
                 pv[t] = p[base + off];
         }
 #pragma unroll
         for (int t = 0; t < Ls; ++t) {
             const size_t off = lev(k0 + t);
-            zyp[t] = zin[byp + off];
-            zym[t] = zin[bym + off];
+            zyp[t] = (TV)zin[byp + off];
+            zym[t] = (TV)zin[bym + off];
             if constexpr (FULL) {
-                zxl[t] = (needL || needR) ? zin[bxe + off] : 0.0;
+                zxl[t] = (needL || needR) ? (TV)zin[bxe + off] : (TV)0;
                 zxr[t] = zxl[t];
             } else {
-                zxl[t] = needL ? zin[bxm + off] : 0.0;
-                zxr[t] = needR ? zin[bxp + off] : 0.0;
+                zxl[t] = needL ? (TV)zin[bxm + off] : (TV)0;
+                zxr[t] = needR ? (TV)zin[bxp + off] : (TV)0;
             }
             if constexpr (kAp) {
                 pyp[t] = p[byp + off];
@@ -887,14 +934,14 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
         for (int t = 0; t < Ls; ++t) {
             if (FULL || t < len) {
                 const int k = k0 + t;
-                const double lo = o.az[k], up = o.az[k + 1];
-                const double zc = zv[t + 1];
-                const double zl_s = __shfl_up(zc, 1, kWave);
-                const double zr_s = __shfl_down(zc, 1, kWave);
-                const double zl = needL ? zxl[t] : zl_s;
-                const double zr = needR ? zxr[t] : zr_s;
+                const TV lo = (TV)o.az[k], up = (TV)o.az[k + 1];
+                const TV zc = zv[t + 1];
+                const TV zl_s = __shfl_up(zc, 1, kWave);
+                const TV zr_s = __shfl_down(zc, 1, kWave);
+                const TV zl = needL ? zxl[t] : zl_s;
+                const TV zr = needR ? zxr[t] : zr_s;
                 // k = 0 / nz-1: the clamped neighbour is zc itself and lo / up is 0
-                double Az = o.delta * zc;
+                TV Az = delta * zc;
                 Az += f.xp * (zc - zr);
                 Az += f.xm * (zc - zl);
                 Az += f.yp * (zc - zyp[t]);
@@ -925,25 +972,25 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const double *__restric
                     if (MODE == SP_FIRST) {
                         st_s(p + l, zc);
                         st_s(y + l, Az);
-                        acc += zc * Az;
+                        acc += (double)zc * (double)Az;
                     } else if (MODE == SP_FUSED_NOX || kX2) {
                         if constexpr (kX2)
                             st_s(u + l, (uo[t] + alpha_prev * p2[t]) + alpha * po[t]);
-                        const double pn = zc + beta * po[t];
-                        const double qn = Az + beta * qo[t];
+                        const TV pn = zc + beta * po[t];
+                        const TV qn = Az + beta * qo[t];
                         st_s(p_out + l, pn);
                         st_s(y + l, qn);
-                        acc += pn * qn;
+                        acc += (double)pn * (double)qn;
                     } else if (MODE == SP_APPLY) {
                         st_s(y + l, Az);
                     } else if (MODE == SP_RESID) {
                         st_s(y + l, qo[t] - Az);
                     } else if (MODE == SP_APPLY_DOT) {
                         st_s(y + l, Az);
-                        acc += zc * Az;
+                        acc += (double)zc * (double)Az;
                     } else if (MODE == SP_FIRST_AP) {
                         st_s(p_out + l, zc);
-                        acc += zc * Az;
+                        acc += (double)zc * (double)Az;
                     }
                 }
             }

@@ -10,6 +10,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/mfpcg.h"
@@ -41,6 +42,7 @@ struct pcg_handle {
     size_t n = 0;          // nx*ny*nz
     double *d_az = nullptr, *d_ah = nullptr, *d_phib = nullptr;
     double *d_phib_tri = nullptr;     // boundary multipliers of the last factored stored tridiagonal
+    float *d_phib32 = nullptr;        // boundary multipliers in binary32 (single-precision solves)
     CsrShape csr{};
     HostStatus *h_status = nullptr;   // pinned host memory written by the reduce kernels
     std::string err = "no error";
@@ -220,43 +222,64 @@ void drain_events(pcg_handle *h, int skip_kid = -1, int skip_tag = -2)
 }
 
 // ---- launch helpers (template dispatch on the column geometry) ---------------
-template <int L, int C>
-void launch_column_lc(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
+// TV: type of r, q (and of the stencil pass's vectors); TZ: type of z and of
+// the column solve.  <double, double> is the binary64 solver; <float, float>
+// and <double, float> only need the fused preconditioner pass and the
+// stand-alone solve.
+template <typename T> const T *phib_of(const pcg_handle *h);
+template <> const double *phib_of<double>(const pcg_handle *h) { return h->d_phib; }
+template <> const float *phib_of<float>(const pcg_handle *h) { return h->d_phib32; }
+
+template <typename TV, typename TZ>
+constexpr bool kBinary64 = std::is_same<TV, double>::value && std::is_same<TZ, double>::value;
+
+template <int L, int C, typename TV, typename TZ>
+void launch_column_lc(pcg_handle *h, const TV *rin, const TV *q, TV *rout, TZ *z,
                       const SolveState *st, int first, double *partials, int upd, bool dots,
                       const double *tri)
 {
     dim3 grid(h->col_tiles), block(h->col_threads);
     const Op &o = h->op;
+    const TZ *phib = phib_of<TZ>(h);
+    constexpr bool kD = kBinary64<TV, TZ>;
     if constexpr (C == kWave) {
         if (!tri && h->col_full) {
             if (upd == UPD_Q)
-                k_column_full<L, UPD_Q, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials);
-            else if (upd == UPD_AP)
-                k_column_full<L, UPD_AP, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials);
-            else if (dots)
-                k_column_full<L, UPD_NONE, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials);
-            else
-                k_column_full<L, UPD_NONE, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials);
+                k_column_full<L, UPD_Q, true, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib);
+            else if (!dots)
+                k_column_full<L, UPD_NONE, false, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib);
+            else if constexpr (kD) {
+                if (upd == UPD_AP)
+                    k_column_full<L, UPD_AP, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib);
+                else
+                    k_column_full<L, UPD_NONE, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib);
+            }
             return;
         }
     }
-    if (tri) {
-        if (dots)
-            k_column_solve<L, C, UPD_NONE, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
+    if constexpr (kD) {
+        if (tri) {
+            if (dots)
+                k_column_solve<L, C, UPD_NONE, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
+            else
+                k_column_solve<L, C, UPD_NONE, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
+            return;
+        }
+    }
+    if (upd == UPD_Q)
+        k_column_solve<L, C, UPD_Q, true, false, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib);
+    else if (!dots)
+        k_column_solve<L, C, UPD_NONE, false, false, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib);
+    else if constexpr (kD) {
+        if (upd == UPD_AP)
+            k_column_solve<L, C, UPD_AP, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib);
         else
-            k_column_solve<L, C, UPD_NONE, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
-    } else if (upd == UPD_Q)
-        k_column_solve<L, C, UPD_Q, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
-    else if (upd == UPD_AP)
-        k_column_solve<L, C, UPD_AP, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
-    else if (dots)
-        k_column_solve<L, C, UPD_NONE, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
-    else
-        k_column_solve<L, C, UPD_NONE, false, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, o.phib);
+            k_column_solve<L, C, UPD_NONE, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib);
+    }
 }
 
-template <int C>
-void launch_column_c(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
+template <int C, typename TV, typename TZ>
+void launch_column_c(pcg_handle *h, const TV *rin, const TV *q, TV *rout, TZ *z,
                      const SolveState *st, int first, double *partials, int upd, bool dots,
                      const double *tri)
 {
@@ -269,8 +292,9 @@ void launch_column_c(pcg_handle *h, const double *rin, const double *q, double *
 }
 
 // z = M^{-1} r; upd selects the fused residual update (UPD_*); tri != nullptr
-// selects the stored (explicit) column matrices.
-void column(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
+// selects the stored (explicit) column matrices (binary64 only).
+template <typename TV, typename TZ>
+void column(pcg_handle *h, const TV *rin, const TV *q, TV *rout, TZ *z,
             const SolveState *st, int first, double *partials, int upd, bool dots,
             const double *tri = nullptr)
 {
@@ -280,27 +304,48 @@ void column(pcg_handle *h, const double *rin, const double *q, double *rout, dou
         launch_column_c<32>(h, rin, q, rout, z, st, first, partials, upd, dots, tri);
 }
 
-template <int Ls, bool FULL>
-void launch_stencil_f(pcg_handle *h, int mode, const double *zin, const double *b, double *u,
-                      double *p, double *y, const SolveState *st, double *partials, double *p_out)
+// TV: the vectors' type; TI: the stencil operand's (z from a TZ column pass,
+// or x).  <double, double> has every mode; <float, float> the modes of the
+// single-precision solve and apply_A; <double, float> the stencil passes of
+// the solve with a binary32 preconditioner.
+template <int Ls, bool FULL, typename TV, typename TI>
+void launch_stencil_f(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, TV *p, TV *y,
+                      const SolveState *st, double *partials, TV *p_out)
 {
     dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
     const Op &o = h->op;
+    constexpr bool kSame = std::is_same<TV, TI>::value;
+    constexpr bool kD = kBinary64<TV, TI>;
     switch (mode) {
-    case SP_FIRST: k_stencil<Ls, SP_FIRST, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_APPLY: k_stencil<Ls, SP_APPLY, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_RESID: k_stencil<Ls, SP_RESID, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_APPLY_DOT: k_stencil<Ls, SP_APPLY_DOT, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_FIRST_AP: k_stencil<Ls, SP_FIRST_AP, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_FUSED_NOX: k_stencil<Ls, SP_FUSED_NOX, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_FUSED_X2: k_stencil<Ls, SP_FUSED_X2, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    default: k_stencil<Ls, SP_FUSED_AP, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_FIRST: k_stencil<Ls, SP_FIRST, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_FUSED_NOX: k_stencil<Ls, SP_FUSED_NOX, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_FUSED_X2: k_stencil<Ls, SP_FUSED_X2, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_APPLY:
+        if constexpr (kSame)
+            k_stencil<Ls, SP_APPLY, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+        break;
+    case SP_RESID:
+        if constexpr (kSame)
+            k_stencil<Ls, SP_RESID, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+        break;
+    case SP_APPLY_DOT:
+        if constexpr (kD)
+            k_stencil<Ls, SP_APPLY_DOT, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+        break;
+    case SP_FIRST_AP:
+        if constexpr (kD)
+            k_stencil<Ls, SP_FIRST_AP, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+        break;
+    default:
+        if constexpr (kD)
+            k_stencil<Ls, SP_FUSED_AP, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+        break;
     }
 }
 
-template <int Ls>
-void launch_stencil(pcg_handle *h, int mode, const double *zin, const double *b, double *u,
-                    double *p, double *y, const SolveState *st, double *partials, double *p_out)
+template <int Ls, typename TV, typename TI>
+void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, TV *p, TV *y,
+                    const SolveState *st, double *partials, TV *p_out)
 {
     if (h->pt_full)
         launch_stencil_f<Ls, true>(h, mode, zin, b, u, p, y, st, partials, p_out);
@@ -308,8 +353,9 @@ void launch_stencil(pcg_handle *h, int mode, const double *zin, const double *b,
         launch_stencil_f<Ls, false>(h, mode, zin, b, u, p, y, st, partials, p_out);
 }
 
-void stencil(pcg_handle *h, int mode, const double *zin, const double *b, double *u, double *p,
-             double *y, const SolveState *st, double *partials, double *p_out = nullptr)
+template <typename TV, typename TI>
+void stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, TV *p, TV *y,
+             const SolveState *st, double *partials, TV *p_out = nullptr)
 {
     switch (h->op.Ls) {
     case 1: launch_stencil<1>(h, mode, zin, b, u, p, y, st, partials, p_out); break;
@@ -395,11 +441,12 @@ int64_t csr_nnz(const pcg_handle *h)
     return (int64_t)h->n * h->csr.base + ncol * V;
 }
 
-int check_vectors(pcg_handle *h, const void *a, const void *b, const char *what)
+int check_vectors(pcg_handle *h, const void *a, const void *b, const char *what,
+                  size_t elem = sizeof(double))
 {
     if (!a || !b)
         return fail(h, PCG_ERR_INVALID, "%s: null device pointer", what);
-    const size_t bytes = h->n * sizeof(double);
+    const size_t bytes = h->n * elem;
     const char *pa = (const char *)a, *pb = (const char *)b;
     if (pa < pb + bytes && pb < pa + bytes)
         return fail(h, PCG_ERR_INVALID, "%s: input and output overlap", what);
@@ -413,8 +460,9 @@ int set_device(pcg_handle *h)
 }
 
 struct SolveArgs {
-    const double *b;
-    double *x;
+    const void *b;   // device vectors of elem-byte elements
+    void *x;
+    size_t elem;
     double tol;
     int32_t maxit;
     void *ws;
@@ -433,7 +481,7 @@ int solve_prologue(pcg_handle *h, const SolveArgs &a, Workspace *w, const char *
         return fail(h, PCG_ERR_INVALID, "%s: maxit must be >= 0", who);
     if (std::isnan(a.tol))
         return fail(h, PCG_ERR_INVALID, "%s: tol is NaN", who);
-    int rc = check_vectors(h, a.b, a.x, who);
+    int rc = check_vectors(h, a.b, a.x, who, a.elem);
     if (rc != PCG_OK)
         return rc;
     if (!a.ws)
@@ -444,7 +492,7 @@ int solve_prologue(pcg_handle *h, const SolveArgs &a, Workspace *w, const char *
     if (a.ws_bytes < need)
         return fail(h, PCG_ERR_INVALID, "%s: workspace has %zu bytes, needs %zu", who, a.ws_bytes, need);
     const char *ws = (const char *)a.ws, *xb = (const char *)a.x;
-    const size_t vb = h->n * sizeof(double);
+    const size_t vb = h->n * a.elem;
     if (xb < ws + need && ws < xb + vb)
         return fail(h, PCG_ERR_INVALID, "%s: x overlaps the workspace", who);
     const char *bb = (const char *)a.b;
@@ -593,6 +641,7 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
     if ((e = hipMalloc(&h->d_az, sizeof(double) * (nz + 1))) != hipSuccess ||
         (e = hipMalloc(&h->d_ah, sizeof(double) * ncol)) != hipSuccess ||
         (e = hipMalloc(&h->d_phib, sizeof(double) * ncol * (size_t)(P > 1 ? P - 1 : 1))) != hipSuccess ||
+        (e = hipMalloc(&h->d_phib32, sizeof(float) * ncol * (size_t)(P > 1 ? P - 1 : 1))) != hipSuccess ||
         (e = hipHostMalloc((void **)&h->h_status, sizeof(HostStatus), hipHostMallocCoherent)) != hipSuccess) {
         h->err = std::string("pcg_create: allocation failed: ") + hipGetErrorString(e);
         return bail(PCG_ERR_HIP);
@@ -609,7 +658,8 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
     if (P > 1) {
         const int threads = 256;
         const size_t blocks = (ncol + threads - 1) / threads;
-        k_setup_phib<<<dim3((unsigned)blocks), dim3(threads), 0, h->stream>>>(h->op, h->d_phib);
+        k_setup_phib<double><<<dim3((unsigned)blocks), dim3(threads), 0, h->stream>>>(h->op, h->d_phib);
+        k_setup_phib<float><<<dim3((unsigned)blocks), dim3(threads), 0, h->stream>>>(h->op, h->d_phib32);
     }
     if ((e = hipStreamSynchronize(h->stream)) != hipSuccess || (e = hipGetLastError()) != hipSuccess) {
         h->err = std::string("pcg_create: set-up failed: ") + hipGetErrorString(e);
@@ -635,6 +685,7 @@ int pcg_destroy(pcg_handle *h)
     if (h->d_az) (void)hipFree(h->d_az);
     if (h->d_ah) (void)hipFree(h->d_ah);
     if (h->d_phib) (void)hipFree(h->d_phib);
+    if (h->d_phib32) (void)hipFree(h->d_phib32);
     if (h->d_phib_tri) (void)hipFree(h->d_phib_tri);
     if (h->h_status) (void)hipHostFree(h->h_status);
     delete h;
@@ -660,7 +711,41 @@ int pcg_apply_A(pcg_handle *h, const double *x, double *y)
         return rc;
     {
         Timed t(h, PCG_KID_APPLY_A, -1);
-        stencil(h, SP_APPLY, x, nullptr, nullptr, nullptr, y, nullptr, nullptr);
+        stencil<double, double>(h, SP_APPLY, x, nullptr, nullptr, nullptr, y, nullptr, nullptr);
+    }
+    HIP_TRY(h, hipGetLastError());
+    return PCG_OK;
+}
+
+int pcg_apply_A_f32(pcg_handle *h, const float *x, float *y)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    int rc = check_vectors(h, x, y, "pcg_apply_A_f32", sizeof(float));
+    if (rc != PCG_OK)
+        return rc;
+    if ((rc = set_device(h)) != PCG_OK)
+        return rc;
+    {
+        Timed t(h, PCG_KID_APPLY_A, -1);
+        stencil<float, float>(h, SP_APPLY, x, nullptr, nullptr, nullptr, y, nullptr, nullptr);
+    }
+    HIP_TRY(h, hipGetLastError());
+    return PCG_OK;
+}
+
+int pcg_precond_f32(pcg_handle *h, const float *r, float *z)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    int rc = check_vectors(h, r, z, "pcg_precond_f32", sizeof(float));
+    if (rc != PCG_OK)
+        return rc;
+    if ((rc = set_device(h)) != PCG_OK)
+        return rc;
+    {
+        Timed t(h, PCG_KID_PRECOND, -1);
+        column<float, float>(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, UPD_NONE, false);
     }
     HIP_TRY(h, hipGetLastError());
     return PCG_OK;
@@ -677,7 +762,7 @@ int pcg_precond(pcg_handle *h, const double *r, double *z)
         return rc;
     {
         Timed t(h, PCG_KID_PRECOND, -1);
-        column(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, UPD_NONE, false);
+        column<double, double>(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, UPD_NONE, false);
     }
     HIP_TRY(h, hipGetLastError());
     return PCG_OK;
@@ -704,19 +789,28 @@ namespace {
 // p and the stencil pass forms <p_new, A z + beta A p_old>; p alternates
 // between two buffers (the stencil pass reads the old direction around each
 // point while writing the new one).
+// TV, TZ: see the launch helpers; ap only for binary64.
+template <typename TV, typename TZ>
 int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool ap, const char *who)
 {
+    constexpr bool kD = kBinary64<TV, TZ>;
+    if (ap && !kD)
+        return fail(h, PCG_ERR_UNSUPPORTED, "%s: the q-free loop is binary64 only", who);
     HostStatus *hs = nullptr;
     HIP_TRY(h, hipHostGetDevicePointer((void **)&hs, h->h_status, 0));
     h->h_status->done = 0;
-    const double *b = a.b;
-    double *x = a.x;
+    const TV *b = (const TV *)a.b;
+    TV *x = (TV *)a.x;
     const int32_t maxit = a.maxit;
     const double tol = a.tol;
-    double *pbuf[2] = {w.p, ap ? w.q : w.p2};
+    // the workspace's vector slots hold binary64 vectors; narrower types use
+    // the front of each slot
+    TV *r = (TV *)w.r, *q = (TV *)w.q;
+    TZ *z = (TZ *)w.z;
+    TV *pbuf[2] = {(TV *)w.p, ap ? (TV *)w.q : (TV *)w.p2};
     k_init_state<<<1, 64, 0, h->stream>>>(w.state);
     // a2: r0 = b - A x0
-    stencil(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
+    stencil<TV, TV>(h, SP_RESID, x, b, nullptr, nullptr, r, nullptr, nullptr);
     hipEvent_t ev = nullptr;
     HIP_TRY(h, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
     int last = 0;
@@ -725,13 +819,13 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
         const double *red = nullptr;
         // search direction read this iteration (written by the previous one)
         // and the buffer of the new one
-        double *pin = ap ? pbuf[(k + 1) & 1] : w.q;
-        double *pcur = pbuf[(k + 1) & 1];
-        double *pnext = pbuf[k & 1];
+        TV *pin = ap ? pbuf[(k + 1) & 1] : q;
+        TV *pcur = pbuf[(k + 1) & 1];
+        TV *pnext = pbuf[k & 1];
         // a3: r -= alpha q (or alpha A p); z = M^{-1} r; partial <r,r>, <r,z>  (Algorithm 3)
         {
             Timed t(h, PCG_KID_FUSED_PREC, k);
-            column(h, w.r, pin, w.r, w.z, w.state, k == 0, w.partials, ap ? UPD_AP : UPD_Q, true);
+            column<TV, TZ>(h, r, pin, r, z, w.state, k == 0, w.partials, ap ? UPD_AP : UPD_Q, true);
         }
         // a4: ||r_k||, stop test, beta
         red = fold_partials(h, w, h->col_tiles, &nred);
@@ -742,14 +836,16 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
         //     stop test has passed (a7)
         {
             Timed t(h, PCG_KID_FUSED_SPMV, k);
-            if (ap)
-                stencil(h, k == 0 ? SP_FIRST_AP : SP_FUSED_AP, w.z, nullptr, x, pcur, nullptr, w.state,
-                        w.partials, pnext);
-            else if (k == 0)
-                stencil(h, SP_FIRST, w.z, nullptr, x, pnext, w.q, w.state, w.partials);
-            else
-                stencil(h, (k & 1) ? SP_FUSED_NOX : SP_FUSED_X2, w.z, nullptr, x, pcur, w.q, w.state,
-                        w.partials, pnext);
+            if (ap) {
+                if constexpr (kD)
+                    stencil<TV, TZ>(h, k == 0 ? SP_FIRST_AP : SP_FUSED_AP, z, nullptr, x, pcur, nullptr,
+                                    w.state, w.partials, pnext);
+            } else if (k == 0) {
+                stencil<TV, TZ>(h, SP_FIRST, z, nullptr, x, pnext, q, w.state, w.partials);
+            } else {
+                stencil<TV, TZ>(h, (k & 1) ? SP_FUSED_NOX : SP_FUSED_X2, z, nullptr, x, pcur, q, w.state,
+                                w.partials, pnext);
+            }
         }
         // a6: sigma, alpha
         red = fold_partials(h, w, h->pt_tiles, &nred);
@@ -780,24 +876,48 @@ int pcg_solve(pcg_handle *h, const double *b, double *x, double tol, int32_t max
               size_t ws_bytes, int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
               double *final_rel)
 {
-    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    SolveArgs a{b, x, sizeof(double), tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
     Workspace w{};
     int rc = solve_prologue(h, a, &w, "pcg_solve");
     if (rc != PCG_OK)
         return rc;
-    return interleaved_loop(h, a, w, false, "pcg_solve");
+    return interleaved_loop<double, double>(h, a, w, false, "pcg_solve");
 }
 
 int pcg_solve_no_q(pcg_handle *h, const double *b, double *x, double tol, int32_t maxit, void *ws,
                    size_t ws_bytes, int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
                    double *final_rel)
 {
-    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    SolveArgs a{b, x, sizeof(double), tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
     Workspace w{};
     int rc = solve_prologue(h, a, &w, "pcg_solve_no_q");
     if (rc != PCG_OK)
         return rc;
-    return interleaved_loop(h, a, w, true, "pcg_solve_no_q");
+    return interleaved_loop<double, double>(h, a, w, true, "pcg_solve_no_q");
+}
+
+int pcg_solve_f32(pcg_handle *h, const float *b, float *x, double tol, int32_t maxit, void *ws,
+                  size_t ws_bytes, int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
+                  double *final_rel)
+{
+    SolveArgs a{b, x, sizeof(float), tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    Workspace w{};
+    int rc = solve_prologue(h, a, &w, "pcg_solve_f32");
+    if (rc != PCG_OK)
+        return rc;
+    return interleaved_loop<float, float>(h, a, w, false, "pcg_solve_f32");
+}
+
+int pcg_solve_mixed(pcg_handle *h, const double *b, double *x, double tol, int32_t maxit, void *ws,
+                    size_t ws_bytes, int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
+                    double *final_rel)
+{
+    SolveArgs a{b, x, sizeof(double), tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    Workspace w{};
+    int rc = solve_prologue(h, a, &w, "pcg_solve_mixed");
+    if (rc != PCG_OK)
+        return rc;
+    return interleaved_loop<double, float>(h, a, w, false, "pcg_solve_mixed");
 }
 
 }   // extern "C"
@@ -824,8 +944,8 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
     h->h_status->done = 0;
     hipEvent_t ev = nullptr;
     HIP_TRY(h, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
-    const double *b = a.b;
-    double *x = a.x;
+    const double *b = (const double *)a.b;
+    double *x = (double *)a.x;
     const int32_t maxit = a.maxit;
     const double tol = a.tol;
     const double *tri = ex ? ex->tri : nullptr;
@@ -835,10 +955,10 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
     if (ex)
         csr_spmv(h, CSR_RESID, ex->row_ptr, ex->col, ex->val, x, b, w.r, nullptr, nullptr);
     else
-        stencil(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
+        stencil<double, double>(h, SP_RESID, x, b, nullptr, nullptr, w.r, nullptr, nullptr);
     {
         Timed t(h, PCG_KID_PRECOND, 0);
-        column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, UPD_NONE, true, tri);
+        column<double, double>(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, UPD_NONE, true, tri);
     }
     red = fold_partials(h, w, h->col_tiles, &nred);
     k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, w.hist, 0, maxit, tol, hs);
@@ -855,7 +975,7 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
             if (ex)
                 csr_spmv(h, CSR_APPLY_DOT, ex->row_ptr, ex->col, ex->val, w.p, nullptr, w.q, w.state, w.partials);
             else
-                stencil(h, SP_APPLY_DOT, w.p, nullptr, nullptr, nullptr, w.q, w.state, w.partials);
+                stencil<double, double>(h, SP_APPLY_DOT, w.p, nullptr, nullptr, nullptr, w.q, w.state, w.partials);
         }
         red = fold_partials(h, w, h->pt_tiles, &nred);
         k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k - 1, 0);
@@ -868,7 +988,7 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
         (void)hipEventRecord(ev, h->stream);
         {   // z = M^{-1} r ; kappa = <r,z>
             Timed t(h, PCG_KID_PRECOND, k);
-            column(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, UPD_NONE, true, tri);
+            column<double, double>(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, UPD_NONE, true, tri);
         }
         red = fold_partials(h, w, h->col_tiles, &nred);
         k_reduce_kappa<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state);
@@ -911,7 +1031,7 @@ int pcg_solve_standard(pcg_handle *h, const double *b, double *x, double tol, in
                        void *ws, size_t ws_bytes, int32_t *iters_out, double *hist_host,
                        int32_t *hist_len_out, double *final_rel)
 {
-    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    SolveArgs a{b, x, sizeof(double), tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
     Workspace w{};
     int rc = solve_prologue(h, a, &w, "pcg_solve_standard");
     if (rc != PCG_OK)
@@ -1012,7 +1132,7 @@ int pcg_tridiag_precond(pcg_handle *h, const double *tri, const double *r, doubl
         return fail(h, PCG_ERR_INVALID, "pcg_tridiag_precond: call pcg_tridiag_factor first");
     {
         Timed t(h, PCG_KID_PRECOND, -1);
-        column(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, UPD_NONE, false, tri);
+        column<double, double>(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, UPD_NONE, false, tri);
     }
     HIP_TRY(h, hipGetLastError());
     return PCG_OK;
@@ -1023,7 +1143,7 @@ int pcg_solve_csr(pcg_handle *h, const int64_t *row_ptr, const int32_t *col, con
                   void *ws, size_t ws_bytes, int32_t *iters_out, double *hist_host,
                   int32_t *hist_len_out, double *final_rel)
 {
-    SolveArgs a{b, x, tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    SolveArgs a{b, x, sizeof(double), tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
     if (!h)
         return PCG_ERR_INVALID;
     Explicit ex{row_ptr, col, val, tri};

@@ -23,7 +23,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pcg_[a-zA-Z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pcg_[A-Za-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_contract():
