@@ -121,9 +121,71 @@ class Problem:
 
 
 @dataclasses.dataclass
+class GeneralProblem:
+    """Operator coefficients in the general tensor-product form of section 3,
+    eqs. (5)-(8), as inputs only (no solver arithmetic):
+
+      ``a``, ``d``      per level (nz): the zero-order term and the factor of the
+                        horizontal couplings;
+      ``beta_face``     nz+1 vertical face coefficients (faces 0 and nz are 0);
+      ``area``          (ny, nx): |T| of every column;
+      ``alpha_x``       (ny, nx): the edge coefficient between (i, j) and
+                        (i+1 mod nx, j);
+      ``alpha_y``       (ny, nx): between (i, j) and (i, j+1 mod ny).
+    """
+    nx: int
+    ny: int
+    nz: int
+    a: np.ndarray
+    d: np.ndarray
+    beta_face: np.ndarray
+    area: np.ndarray
+    alpha_x: np.ndarray
+    alpha_y: np.ndarray
+
+    @property
+    def n(self) -> int:
+        return self.nx * self.ny * self.nz
+
+
+def general_problem(nx: int, ny: int, nz: int, seed: int) -> GeneralProblem:
+    """Seeded general-coefficient operator: a synthetic stand-in for the thin
+    spherical shell of the paper's model problem (its own parameters are not
+    recoverable from the page).  Vertical faces r_f = 1 + 0.02 (f/nz)^2
+    (finer near the ground); with cell thicknesses h_k, mean thickness hb and
+    mid-points m_k: a_k = 1e-3 h_k / hb, d_k = h_k / hb, interior
+    beta_f = 1e4 r_f^2 hb / (m_f - m_{f-1}).  The area is that of a gnomonic
+    panel cell, (1 + x^2 + y^2)^(-3/2) at the cell centre (x, y) in [-1, 1]^2,
+    times 1 + 0.1 sin(...); the edge coefficients are 1 + 0.25 * products of
+    sinusoids; phases from the generator keyed ``seed ^ 0x5A``."""
+    u = uniform01(seed ^ 0x5A, np.arange(6, dtype=np.uint64))
+    ph = 2.0 * math.pi * u
+    f = np.arange(nz + 1, dtype=np.float64)
+    r = 1.0 + 0.02 * (f / nz) ** 2
+    h = np.diff(r)
+    hb = h.mean()
+    m = 0.5 * (r[:-1] + r[1:])
+    a = 1e-3 * h / hb
+    d = h / hb
+    beta = np.zeros(nz + 1)
+    if nz > 1:
+        beta[1:nz] = 1e4 * r[1:nz] ** 2 * hb / np.diff(m)
+    i = np.arange(nx, dtype=np.float64)
+    j = np.arange(ny, dtype=np.float64)
+    x = -1.0 + (2.0 * i + 1.0) / nx
+    y = -1.0 + (2.0 * j + 1.0) / ny
+    area = (1.0 + x[None, :] ** 2 + y[:, None] ** 2) ** -1.5
+    area = area * (1.0 + 0.1 * np.sin(2.0 * math.pi * j[:, None] / ny + ph[0]) * np.sin(2.0 * math.pi * i[None, :] / nx + ph[1]))
+    ax = 1.0 + 0.25 * np.cos(2.0 * math.pi * (i[None, :] + 0.5) / nx + ph[2]) * np.sin(2.0 * math.pi * j[:, None] / ny + ph[3])
+    ay = 1.0 + 0.25 * np.sin(2.0 * math.pi * i[None, :] / nx + ph[4]) * np.cos(2.0 * math.pi * (j[:, None] + 0.5) / ny + ph[5])
+    return GeneralProblem(nx, ny, nz, a, d, beta, np.ascontiguousarray(area), np.ascontiguousarray(ax),
+                          np.ascontiguousarray(ay))
+
+
+@dataclasses.dataclass
 class Workload:
     name: str
-    problem: Problem
+    problem: object                  # Problem, or GeneralProblem for the general workload
     rhs: Optional[np.ndarray]        # b, or None when b = A x_true (each side applies its own A)
     x_true: Optional[np.ndarray]     # manufactured solution, when there is one
     tol: float
@@ -184,18 +246,21 @@ CONFIG_NAMES = {
     3: "manufactured-512x512x128",
     4: "varying-1024x1024x128",
     5: "csr-vs-mf-2048x2048x128",
+    6: "general-1024x1024x128",
 }
 
 
-def config_problem(cfg: int, scale_xy: Optional[tuple] = None, nz: Optional[int] = None) -> Problem:
-    """Operator of workload `cfg` (1..5); `scale_xy`/`nz` override the grid (same recipe)."""
+def config_problem(cfg: int, scale_xy: Optional[tuple] = None, nz: Optional[int] = None):
+    """Operator of workload `cfg` (1..6); `scale_xy`/`nz` override the grid (same recipe)."""
     dims = {1: (32, 32, 16), 2: (128, 128, 64), 3: (512, 512, 128),
-            4: (1024, 1024, 128), 5: (2048, 2048, 128)}[cfg]
+            4: (1024, 1024, 128), 5: (2048, 2048, 128), 6: (1024, 1024, 128)}[cfg]
     nx, ny, z = dims
     if scale_xy is not None:
         nx, ny = scale_xy
     if nz is not None:
         z = nz
+    if cfg == 6:
+        return general_problem(nx, ny, z, 6)
     if cfg == 1:
         return Problem(nx, ny, z, 1e-2, constant_faces(z, 1e3), 1.0)
     if cfg == 2:
@@ -207,7 +272,7 @@ def config_problem(cfg: int, scale_xy: Optional[tuple] = None, nz: Optional[int]
 
 
 def make_workload(cfg: int, scale_xy: Optional[tuple] = None, nz: Optional[int] = None) -> Workload:
-    """Seeded workload `cfg` (1..5), optionally on a smaller grid with the same recipe."""
+    """Seeded workload `cfg` (1..6), optionally on a smaller grid with the same recipe."""
     prob = config_problem(cfg, scale_xy, nz)
     nx, ny, z = prob.nx, prob.ny, prob.nz
     name = CONFIG_NAMES[cfg] if scale_xy is None and nz is None else f"cfg{cfg}-{nx}x{ny}x{z}"
@@ -221,4 +286,6 @@ def make_workload(cfg: int, scale_xy: Optional[tuple] = None, nz: Optional[int] 
         return Workload(name, prob, None, smooth_field(nx, ny, z, 3), 1e-10, 5000)
     if cfg == 4:
         return Workload(name, prob, uniform_field(nx, ny, z, 4), None, 1e-10, 5000)
+    if cfg == 6:
+        return Workload(name, prob, uniform_field(nx, ny, z, 6), None, 1e-10, 5000)
     return Workload(name, prob, gaussian_field(nx, ny, z, 5), None, 0.0, 50, fixed_iterations=True)

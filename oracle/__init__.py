@@ -86,6 +86,13 @@ class Oracle:
         lib.orc_pcg_f32.restype = i
         lib.orc_pcg_mixed.argtypes = [i, i, i, d, dp, dp, dp, dp, d, i, dp, ip]
         lib.orc_pcg_mixed.restype = i
+        gen = [i, i, i, dp, dp, dp, dp, dp, dp]
+        lib.orc_apply_A_gen.argtypes = gen + [dp, dp]
+        lib.orc_apply_A_gen.restype = None
+        lib.orc_precond_gen.argtypes = gen + [dp, dp]
+        lib.orc_precond_gen.restype = i
+        lib.orc_pcg_gen.argtypes = gen + [dp, dp, d, i, dp, ip]
+        lib.orc_pcg_gen.restype = i
         self.lib = lib
         self.path = path
 
@@ -177,6 +184,51 @@ class Oracle:
                                     _ptr(x), float(tol), int(maxit), _ptr(hist), ctypes.byref(iters))
         return dict(x=x, iters=iters.value, hist=hist[: iters.value + 1].copy(), status=st)
 
+    @staticmethod
+    def _gen(gp):
+        """Coefficient arrays of a GeneralProblem (float64, contiguous, checked)."""
+        nz, ncol = gp.nz, gp.nx * gp.ny
+        arrs = []
+        for name, size in (("a", nz), ("d", nz), ("beta_face", nz + 1), ("area", ncol),
+                           ("alpha_x", ncol), ("alpha_y", ncol)):
+            v = np.ascontiguousarray(getattr(gp, name), dtype=np.float64).ravel()
+            if v.size != size:
+                raise ValueError(f"{name} has {v.size} entries, needs {size}")
+            arrs.append(v)
+        return arrs
+
+    def _gen_args(self, gp):
+        arrs = self._gen(gp)
+        return (gp.nx, gp.ny, gp.nz, *[_ptr(v) for v in arrs]), arrs
+
+    def apply_A_gen(self, gp, x) -> np.ndarray:
+        """y = A x for general tensor-product coefficients (eqs. (5)-(8))."""
+        x = self._field(x, gp)
+        args, keep = self._gen_args(gp)
+        y = np.empty_like(x)
+        self.lib.orc_apply_A_gen(*args, _ptr(x), _ptr(y))
+        return y
+
+    def precond_gen(self, gp, r) -> np.ndarray:
+        """z = M^{-1} r for general coefficients (Thomas per column)."""
+        r = self._field(r, gp)
+        args, keep = self._gen_args(gp)
+        z = np.empty_like(r)
+        if self.lib.orc_precond_gen(*args, _ptr(r), _ptr(z)) != OK:
+            raise FloatingPointError("zero pivot in the column solve")
+        return z
+
+    def pcg_gen(self, gp, b, x0=None, tol: float = 1e-10, maxit: int = 500):
+        """Textbook PCG with general coefficients.  Returns dict(x, iters, hist, status)."""
+        b = self._field(b, gp)
+        x = np.zeros_like(b) if x0 is None else self._field(x0, gp).copy()
+        args, keep = self._gen_args(gp)
+        hist = np.zeros(max(1, maxit + 1))
+        iters = ctypes.c_int(0)
+        st = self.lib.orc_pcg_gen(*args, _ptr(b), _ptr(x), float(tol), int(maxit), _ptr(hist),
+                                  ctypes.byref(iters))
+        return dict(x=x, iters=iters.value, hist=hist[: iters.value + 1].copy(), status=st)
+
     def dot(self, a, b) -> float:
         a = np.ascontiguousarray(a, dtype=np.float64).ravel()
         b = np.ascontiguousarray(b, dtype=np.float64).ravel()
@@ -254,3 +306,15 @@ def pcg_f32(prob, b, x0=None, tol=1e-5, maxit=500):
 
 def pcg_mixed(prob, b, x0=None, tol=1e-10, maxit=500):
     return default().pcg_mixed(prob, b, x0, tol, maxit)
+
+
+def apply_A_gen(gp, x):
+    return default().apply_A_gen(gp, x)
+
+
+def precond_gen(gp, r):
+    return default().precond_gen(gp, r)
+
+
+def pcg_gen(gp, b, x0=None, tol=1e-10, maxit=500):
+    return default().pcg_gen(gp, b, x0, tol, maxit)

@@ -492,3 +492,141 @@ done:
     free(r); free(z); free(p); free(q); free(r32); free(z32); free(az32); free(ah32);
     return status;
 }
+
+/* ======================================================================
+ * General tensor-product coefficients (section 3, eqs. (5)-(8)), read with
+ * the signs of the symmetric positive definite operator as above:
+ *   (A u)_{T,k} = |T| a_k u_{T,k}
+ *               + d_k sum_{T' in N(T)} alpha_{T,T'} (u_{T,k} - u_{T',k})
+ *               + |T| ( beta_{k+1} (u_{T,k} - u_{T,k+1}) + beta_k (u_{T,k} - u_{T,k-1}) )
+ * with the tridiagonal column block A_T = |T| diag(a) + alpha_T diag(d) +
+ * |T| (vertical second difference with face coefficients beta), eq. (8), the
+ * diagonal horizontal blocks A_{T,T'} = -alpha_{T,T'} diag(d), eq. (6), and
+ * alpha_T = sum of alpha_{T,T'}, eq. (7).  Faces 0 and nz carry no flux
+ * (beta_0 = beta_nz = 0).  On the logically rectangular periodic grid the
+ * edge coefficients are two fields: ax[j*nx + i] between (i, j) and
+ * (i+1 mod nx, j), ay[j*nx + i] between (i, j) and (i, j+1 mod ny).  The
+ * preconditioner keeps A_T and drops the A_{T,T'} (section 4.2). */
+
+static double gen_alpha_T(int nx, int ny, const double *ax, const double *ay, int i, int j)
+{
+    int im = (i + nx - 1) % nx, jm = (j + ny - 1) % ny;
+    return ax[(size_t)j * nx + i] + ax[(size_t)j * nx + im]
+         + ay[(size_t)j * nx + i] + ay[(size_t)jm * nx + i];
+}
+
+/* y = A x for the general coefficients (eqs. (5)-(8)). */
+void orc_apply_A_gen(int nx, int ny, int nz, const double *a, const double *d, const double *beta,
+                     const double *area, const double *ax, const double *ay,
+                     const double *x, double *y)
+{
+    for (int j = 0; j < ny; ++j)
+        for (int k = 0; k < nz; ++k)
+            for (int i = 0; i < nx; ++i) {
+                int ip = (i + 1) % nx, im = (i + nx - 1) % nx;
+                int jp = (j + 1) % ny, jm = (j + ny - 1) % ny;
+                double T = area[(size_t)j * nx + i];
+                double u = x[at(nx, nz, i, j, k)];
+                double acc = T * a[k] * u;
+                double hor = ax[(size_t)j * nx + i] * (u - x[at(nx, nz, ip, j, k)]);
+                hor += ax[(size_t)j * nx + im] * (u - x[at(nx, nz, im, j, k)]);
+                hor += ay[(size_t)j * nx + i] * (u - x[at(nx, nz, i, jp, k)]);
+                hor += ay[(size_t)jm * nx + i] * (u - x[at(nx, nz, i, jm, k)]);
+                acc += d[k] * hor;
+                if (k < nz - 1)
+                    acc += T * beta[k + 1] * (u - x[at(nx, nz, i, j, k + 1)]);
+                if (k > 0)
+                    acc += T * beta[k] * (u - x[at(nx, nz, i, j, k - 1)]);
+                y[at(nx, nz, i, j, k)] = acc;
+            }
+}
+
+/* z = M^{-1} r, M = blockdiag(A_T) for the general coefficients: one Thomas
+ * solve per column (eq. (19)); diagonal |T| a_k + alpha_T d_k + |T| (beta_k +
+ * beta_{k+1}), off-diagonals -|T| beta. */
+int orc_precond_gen(int nx, int ny, int nz, const double *a, const double *d, const double *beta,
+                    const double *area, const double *ax, const double *ay,
+                    const double *r, double *z)
+{
+    double *gam = (double *)malloc(sizeof(double) * (size_t)(nz > 0 ? nz : 1));
+    if (!gam)
+        return ORC_ERR_INVALID;
+    int status = ORC_OK;
+    for (int j = 0; j < ny; ++j)
+        for (int i = 0; i < nx; ++i) {
+            double aT = gen_alpha_T(nx, ny, ax, ay, i, j);
+            double T = area[(size_t)j * nx + i];
+            double up0 = (nz > 1) ? T * beta[1] : 0.0;
+            double bet = T * a[0] + aT * d[0] + up0;
+            if (bet == 0.0) { status = ORC_ERR_BREAKDOWN; }
+            z[at(nx, nz, i, j, 0)] = r[at(nx, nz, i, j, 0)] / bet;
+            for (int k = 1; k < nz; ++k) {
+                double sub = -T * beta[k];
+                double sup_prev = -T * beta[k];
+                double up = (k < nz - 1) ? T * beta[k + 1] : 0.0;
+                double diag = T * a[k] + aT * d[k] + T * beta[k] + up;
+                gam[k] = sup_prev / bet;
+                bet = diag - sub * gam[k];
+                if (bet == 0.0) { status = ORC_ERR_BREAKDOWN; }
+                z[at(nx, nz, i, j, k)] =
+                    (r[at(nx, nz, i, j, k)] - sub * z[at(nx, nz, i, j, k - 1)]) / bet;
+            }
+            for (int k = nz - 2; k >= 0; --k)
+                z[at(nx, nz, i, j, k)] -= gam[k + 1] * z[at(nx, nz, i, j, k + 1)];
+        }
+    free(gam);
+    return status;
+}
+
+/* Textbook PCG (as orc_pcg) with the general operator and preconditioner. */
+int orc_pcg_gen(int nx, int ny, int nz, const double *a, const double *d, const double *beta,
+                const double *area, const double *ax, const double *ay,
+                const double *b, double *x, double tol, int maxit, double *hist, int *iters_out)
+{
+    size_t n = (size_t)nx * ny * nz;
+    double *r = (double *)malloc(sizeof(double) * n);
+    double *z = (double *)malloc(sizeof(double) * n);
+    double *p = (double *)malloc(sizeof(double) * n);
+    double *q = (double *)malloc(sizeof(double) * n);
+    int status = ORC_NOT_CONVERGED, it = 0;
+    if (!r || !z || !p || !q) {
+        status = ORC_ERR_INVALID;
+        goto done;
+    }
+    orc_apply_A_gen(nx, ny, nz, a, d, beta, area, ax, ay, x, q);
+    for (size_t l = 0; l < n; ++l)
+        r[l] = b[l] - q[l];
+    double R0 = sqrt(orc_dot(n, r, r));
+    hist[0] = R0;
+    if (!isfinite(R0)) { status = ORC_ERR_BREAKDOWN; goto done; }
+    if (R0 == 0.0) { status = ORC_OK; goto done; }
+    if (orc_precond_gen(nx, ny, nz, a, d, beta, area, ax, ay, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+    memcpy(p, z, sizeof(double) * n);
+    double rho = orc_dot(n, r, z);
+    if (!(rho > 0.0) || !isfinite(rho)) { status = ORC_ERR_BREAKDOWN; goto done; }
+    for (int k = 1; k <= maxit; ++k) {
+        orc_apply_A_gen(nx, ny, nz, a, d, beta, area, ax, ay, p, q);
+        double sigma = orc_dot(n, p, q);
+        if (!(sigma > 0.0) || !isfinite(sigma)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double alpha = rho / sigma;
+        for (size_t l = 0; l < n; ++l) x[l] += alpha * p[l];
+        for (size_t l = 0; l < n; ++l) r[l] -= alpha * q[l];
+        double R = sqrt(orc_dot(n, r, r));
+        hist[k] = R;
+        it = k;
+        if (!isfinite(R)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        if (R == 0.0 || R / R0 < tol) { status = ORC_OK; goto done; }
+        if (k == maxit) break;
+        if (orc_precond_gen(nx, ny, nz, a, d, beta, area, ax, ay, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double rho_new = orc_dot(n, r, z);
+        if (!(rho_new > 0.0) || !isfinite(rho_new)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double beta_cg = rho_new / rho;
+        rho = rho_new;
+        for (size_t l = 0; l < n; ++l) p[l] = z[l] + beta_cg * p[l];
+    }
+    status = ORC_NOT_CONVERGED;
+done:
+    if (iters_out) *iters_out = it;
+    free(r); free(z); free(p); free(q);
+    return status;
+}

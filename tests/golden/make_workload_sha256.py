@@ -28,8 +28,12 @@ def digest(a) -> str:
 def fingerprints(cfg: int):
     w = W.make_workload(cfg)
     p = w.problem
-    rows = [(w.name, "alpha_z_face", (p.nz + 1,), digest(p.alpha_z_face)),
-            (w.name, "alpha_h", (p.ny, p.nx), digest(p.alpha_h_field()))]
+    if isinstance(p, W.GeneralProblem):
+        rows = [(w.name, name, np.shape(getattr(p, name)), digest(getattr(p, name)))
+                for name in ("a", "d", "beta_face", "area", "alpha_x", "alpha_y")]
+    else:
+        rows = [(w.name, "alpha_z_face", (p.nz + 1,), digest(p.alpha_z_face)),
+                (w.name, "alpha_h", (p.ny, p.nx), digest(p.alpha_h_field()))]
     if w.rhs is not None:
         rows.append((w.name, "rhs", w.rhs.shape, digest(w.rhs)))
     if w.x_true is not None:

@@ -42,6 +42,12 @@ MUTATIONS = {
                               "z[at(nx, nz, i, j, k)] += gam[k + 1] * z[at(nx, nz, i, j, k + 1)];\n        }\n    free(gam);\n    return status;\n}\n\n/* <a,b> of binary32"),
     "f32_pcg_beta_inverted": ("const float beta = (float)(rho_new / rho);", "const float beta = (float)(rho / rho_new);"),
     "mixed_stale_residual": ("        for (size_t l = 0; l < n; ++l) r32[l] = (float)r[l];", ""),
+    "gen_drop_d": ("acc += d[k] * hor;", "acc += hor;"),
+    "gen_x_edge_index": ("hor += ax[(size_t)j * nx + im] * (u - x[at(nx, nz, im, j, k)]);",
+                         "hor += ax[(size_t)j * nx + i] * (u - x[at(nx, nz, im, j, k)]);"),
+    "gen_precond_no_area": ("double sub = -T * beta[k];", "double sub = -beta[k];"),
+    "gen_alphaT_missing_edge": ("return ax[(size_t)j * nx + i] + ax[(size_t)j * nx + im]",
+                                "return ax[(size_t)j * nx + i] + 0.0 * ax[(size_t)j * nx + im]"),
 }
 
 

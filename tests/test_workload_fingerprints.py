@@ -1,5 +1,5 @@
 """The seeded input generator reproduces the recorded fingerprints of all
-five workloads (tests/golden/workload_sha256.txt, written by
+six workloads (tests/golden/workload_sha256.txt, written by
 tests/golden/make_workload_sha256.py)."""
 import importlib.util
 import os
@@ -29,7 +29,7 @@ def _recorded():
     return rec
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_workload_arrays_match_fingerprints(cfg):
     mk = _maker()
     rec = _recorded()
