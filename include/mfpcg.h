@@ -86,12 +86,44 @@ typedef struct {
 } pcg_coeffs;
 
 /* Create a handle for one grid and operator (section 6: the coefficient
- * vectors are copied to the device once).  hip_stream: a hipStream_t, or
+ * vectors are copied to the device once).  The operator is the special case
+ * of the general form below with |T| = 1, a_k = delta, d_k = 1, beta = alpha_z
+ * and the edge coefficient between two cells the mean of their alpha_h.  hip_stream: a hipStream_t, or
  * NULL for the null stream.  Returns PCG_ERR_INVALID for bad arguments,
  * PCG_ERR_UNSUPPORTED for nz > 512, PCG_ERR_HIP if a table allocation fails.
  * *out is NULL on failure. */
 int pcg_create(const pcg_grid *grid, const pcg_coeffs *coeffs, void *hip_stream,
                pcg_handle **out);
+
+/* The operator with general tensor-product coefficients (section 3,
+ * eqs. (5)-(8), with the signs of a symmetric positive definite operator):
+ *   (A u)_{T,k} = |T| a_k u_{T,k} + d_k sum_{T'} alpha_{T,T'} (u_{T,k} - u_{T',k})
+ *               + |T| (beta_{k+1} (u_{T,k} - u_{T,k+1}) + beta_k (u_{T,k} - u_{T,k-1}))
+ * and M = its column blocks A_T (the couplings between columns dropped).
+ *   a          HOST, nz entries, each finite and > 0 (zero-order term)
+ *   d          HOST, nz entries, each finite and >= 0 (factor of the
+ *              horizontal couplings at level k)
+ *   beta_face  HOST, nz+1 entries, each finite and >= 0; face f lies between
+ *              levels f-1 and f; faces 0 and nz must be 0 (no flux)
+ *   area       HOST, ny*nx entries [j*nx + i], each finite and > 0 (|T|)
+ *   alpha_x    HOST, ny*nx entries: the edge between (i, j) and
+ *              (i+1 mod nx, j), each finite and >= 0
+ *   alpha_y    HOST, ny*nx entries: the edge between (i, j) and
+ *              (i, j+1 mod ny), each finite and >= 0
+ * All values are copied at creation; the caller may free them after. */
+typedef struct {
+    const double *a;
+    const double *d;
+    const double *beta_face;
+    const double *area;
+    const double *alpha_x;
+    const double *alpha_y;
+} pcg_coeffs_general;
+
+/* As pcg_create, for general coefficients.  Every other entry point works
+ * on the handle unchanged (binary64, binary32, mixed, explicit path). */
+int pcg_create_general(const pcg_grid *grid, const pcg_coeffs_general *coeffs, void *hip_stream,
+                       pcg_handle **out);
 
 /* Release the handle and its tables (waits for its stream).  NULL is a no-op. */
 int pcg_destroy(pcg_handle *h);

@@ -41,7 +41,7 @@ EXPORTED = [
     "pcg_profile_reset", "pcg_profile_read", "pcg_last_error", "pcg_version",
     "pcg_csr_nnz", "pcg_csr_assemble", "pcg_csr_spmv", "pcg_tridiag_assemble",
     "pcg_tridiag_factor", "pcg_tridiag_precond", "pcg_solve_csr",
-    "pcg_apply_A_f32", "pcg_precond_f32", "pcg_solve_f32", "pcg_solve_mixed",
+    "pcg_apply_A_f32", "pcg_precond_f32", "pcg_solve_f32", "pcg_solve_mixed", "pcg_create_general",
 ]
 
 
@@ -53,6 +53,11 @@ class PcgError(RuntimeError):
 
 class pcg_grid(ctypes.Structure):
     _fields_ = [("nx", ctypes.c_int32), ("ny", ctypes.c_int32), ("nz", ctypes.c_int32)]
+
+
+class pcg_coeffs_general(ctypes.Structure):
+    _fields_ = [(name, ctypes.POINTER(ctypes.c_double))
+                for name in ("a", "d", "beta_face", "area", "alpha_x", "alpha_y")]
 
 
 class pcg_coeffs(ctypes.Structure):
@@ -91,6 +96,9 @@ def load():
         H = ctypes.c_void_p
         lib.pcg_create.argtypes = [ctypes.POINTER(pcg_grid), ctypes.POINTER(pcg_coeffs), vp, ctypes.POINTER(H)]
         lib.pcg_create.restype = ctypes.c_int
+        lib.pcg_create_general.argtypes = [ctypes.POINTER(pcg_grid), ctypes.POINTER(pcg_coeffs_general), vp,
+                                           ctypes.POINTER(H)]
+        lib.pcg_create_general.restype = ctypes.c_int
         lib.pcg_destroy.argtypes = [H]
         lib.pcg_destroy.restype = ctypes.c_int
         lib.pcg_set_stream.argtypes = [H, vp]
@@ -185,9 +193,37 @@ class Handle:
         return f"Handle({self.nx}x{self.ny}x{self.nz})"
 
 
-def pcg_create(problem, stream=None) -> Handle:
-    """Create a handle for a :class:`workloads.Problem` on the current CUDA device."""
+def _create_general(problem, stream) -> Handle:
     import torch
+    lib = load()
+    g = pcg_grid(problem.nx, problem.ny, problem.nz)
+    ncol = problem.nx * problem.ny
+    c = pcg_coeffs_general()
+    keep = []
+    for name, size in (("a", problem.nz), ("d", problem.nz), ("beta_face", problem.nz + 1),
+                       ("area", ncol), ("alpha_x", ncol), ("alpha_y", ncol)):
+        v = np.ascontiguousarray(getattr(problem, name), dtype=np.float64).ravel()
+        if v.size != size:
+            raise ValueError(f"{name} must have {size} entries (got {v.size})")
+        keep.append(v)
+        setattr(c, name, v.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    out = ctypes.c_void_p()
+    rc = lib.pcg_create_general(ctypes.byref(g), ctypes.byref(c), ctypes.c_void_p(_stream_ptr(stream)),
+                                ctypes.byref(out))
+    del keep
+    if rc != PCG_OK:
+        raise PcgError(rc, pcg_last_error(None))
+    return Handle(out.value, problem.nx, problem.ny, problem.nz, torch.cuda.current_device())
+
+
+def pcg_create(problem, stream=None) -> Handle:
+    """Create a handle for a :class:`workloads.Problem` (pcg_create) or a
+    :class:`workloads.GeneralProblem` (pcg_create_general) on the current
+    CUDA device."""
+    import torch
+    from .workloads import GeneralProblem
+    if isinstance(problem, GeneralProblem):
+        return _create_general(problem, stream)
     lib = load()
     g = pcg_grid(problem.nx, problem.ny, problem.nz)
     az = np.ascontiguousarray(problem.alpha_z_face, dtype=np.float64)

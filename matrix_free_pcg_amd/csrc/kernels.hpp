@@ -45,9 +45,16 @@ struct Op {
     int Ls, Ws, nkt;       // sweep passes: levels per wave, waves per tile, tiles along k
     int ntx, sg;           // sweep passes: 64-column tiles along i, tiles per i-strip
     int csg;               // column passes: tiles per i-strip
-    double delta;
-    const double *az;      // nz+1 vertical face coefficients (faces 0, nz are 0)
-    const double *ah;      // ny*nx per-column alpha_h
+    // The operator in the general tensor-product form of section 3, eqs.
+    // (5)-(8) (symmetric positive definite signs):
+    //   (A u)_{T,k} = |T| a_k u + d_k sum_{T'} alpha_{T,T'} (u - u_{T'})
+    //               + |T| (beta_{k+1} (u - u_{k+1}) + beta_k (u - u_{k-1}))
+    const double *az;      // nz+1 vertical face coefficients beta (faces 0, nz are 0)
+    const double *lev_a;   // nz: zero-order coefficient a_k
+    const double *lev_d;   // nz: factor d_k of the horizontal couplings
+    const double *area;    // ny*nx: |T| per column
+    const double *ex;      // ny*nx: edge coefficient between (i, j) and (i+1 mod nx, j)
+    const double *ey;      // ny*nx: edge coefficient between (i, j) and (i, j+1 mod ny)
     const double *phib;    // (P-1)*ny*nx: Thomas multiplier phi at k = s*L-1
 };
 
@@ -105,12 +112,12 @@ __device__ __forceinline__ size_t lin(const Op &o, int i, int j, int k)
 // arithmetic type where they are used; dot products always accumulate in
 // binary64.
 
-// Horizontal face coefficients of column (i, j): mean of the two cells'
-// alpha_h (the symmetric per-edge alpha_{T,T'} of section 3, eqs. (6)-(7)),
-// formed in T.
+// Horizontal edge coefficients alpha_{T,T'} of column (i, j) (section 3,
+// eqs. (6)-(7)) and its area |T|, in T.  sum() is alpha_T.
 template <typename T>
 struct FacesT {
     T xp, xm, yp, ym;
+    T area;
     __device__ __forceinline__ T sum() const { return (xp + xm) + (yp + ym); }
 };
 using Faces = FacesT<double>;
@@ -118,17 +125,15 @@ using Faces = FacesT<double>;
 template <typename T>
 __device__ __forceinline__ FacesT<T> column_faces_t(const Op &o, int i, int j)
 {
-    const int ip = (i + 1 == o.nx) ? 0 : i + 1;
     const int im = (i == 0) ? o.nx - 1 : i - 1;
-    const int jp = (j + 1 == o.ny) ? 0 : j + 1;
     const int jm = (j == 0) ? o.ny - 1 : j - 1;
-    const T c = (T)o.ah[(size_t)j * o.nx + i];
-    const T half = (T)0.5;
+    const size_t c = (size_t)j * o.nx + i;
     FacesT<T> f;
-    f.xp = half * (c + (T)o.ah[(size_t)j * o.nx + ip]);
-    f.xm = half * (c + (T)o.ah[(size_t)j * o.nx + im]);
-    f.yp = half * (c + (T)o.ah[(size_t)jp * o.nx + i]);
-    f.ym = half * (c + (T)o.ah[(size_t)jm * o.nx + i]);
+    f.xp = (T)o.ex[c];
+    f.xm = (T)o.ex[(size_t)j * o.nx + im];
+    f.yp = (T)o.ey[c];
+    f.ym = (T)o.ey[(size_t)jm * o.nx + i];
+    f.area = (T)o.area[c];
     return f;
 }
 
@@ -137,13 +142,40 @@ __device__ __forceinline__ Faces column_faces(const Op &o, int i, int j)
     return column_faces_t<double>(o, i, j);
 }
 
+// The parts of the column matrix A_T (eq. (8)) at level k of a column with
+// edges f: the diagonal's zero-order and horizontal part |T| a_k + d_k alpha_T,
+// and the vertical couplings lo = |T| beta_k (to k-1), up = |T| beta_{k+1}.
+template <typename T>
+__device__ __forceinline__ T diag_base(const Op &o, const FacesT<T> &f, T aT, int k)
+{
+    return f.area * (T)o.lev_a[k] + (T)o.lev_d[k] * aT;
+}
+
 // Thomas pivot of level k (section 4.2, eq. (19); Appendix A, Algorithm 3):
-// D_k = diag_k - sub_k * phi_{k-1} with diag_k = delta + alpha_T + lo + up,
+// D_k = diag_k - sub_k * phi_{k-1} with diag_k = base + lo + up,
 // sub_k = -lo, phi_{k-1} = super_{k-1} / D_{k-1}.
 template <typename T>
-__device__ __forceinline__ T thomas_pivot(T delta, T aT, T lo, T up, T phi_prev)
+__device__ __forceinline__ T thomas_pivot(T base, T lo, T up, T phi_prev)
 {
-    return ((delta + aT) + (lo + up)) + lo * phi_prev;
+    return (base + (lo + up)) + lo * phi_prev;
+}
+
+// One row of the stencil (eq. (18) in the general form): c the cell, its
+// i-1 / i+1, j-1 / j+1 and k-1 / k+1 neighbours; za = |T| a_k, dk = d_k,
+// lo / up the area-scaled vertical couplings.
+template <typename T>
+__device__ __forceinline__ T stencil_row(const FacesT<T> &f, T za, T dk, T lo, T up, T c, T xm, T xp,
+                                         T ym, T yp, T km, T kp)
+{
+    T hor = f.xp * (c - xp);
+    hor += f.xm * (c - xm);
+    hor += f.yp * (c - yp);
+    hor += f.ym * (c - ym);
+    T acc = za * c;
+    acc += dk * hor;
+    acc += up * (c - kp);
+    acc += lo * (c - km);
+    return acc;
 }
 
 // (offset, slope) of a segment's affine map, exchanged through LDS
@@ -268,7 +300,6 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     const int ic = i < o.nx ? i : o.nx - 1;
     const FacesT<TZ> fc = column_faces_t<TZ>(o, ic, j);
     const TZ aT = fc.sum();
-    const TZ delta = (TZ)o.delta;
     const int k0 = s * L;
     const int len = active ? min(L, o.nz - k0) : 0;
     const size_t base = lin(o, ic, j, 0);
@@ -285,11 +316,12 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         for (int t = 0; t <= L; ++t)
             fz[t] = (t <= len) ? (TZ)o.az[k0 + t] : (TZ)0;
     }
+    // area-scaled vertical coupling across face(t)
     auto face = [&](int t) -> TZ {
         if constexpr (C == kWave)
-            return (TZ)o.az[k0 + t];
+            return fc.area * (TZ)o.az[k0 + t];
         else
-            return fz[t];
+            return fc.area * fz[t];
     };
     // stored coefficients of the segment's levels: lo = -sub, up = -sup, diag
     TZ slo[STORED ? L : 1], sup_[STORED ? L : 1], sdg[STORED ? L : 1];
@@ -360,13 +392,9 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
                     pr = needR ? pr : pr_s;
                 }
                 const double lo = face(t), up = face(t + 1);
-                double Ap = o.delta * pc;
-                Ap += fc.xp * (pc - pr);
-                Ap += fc.xm * (pc - pl);
-                Ap += fc.yp * (pc - pyp[t]);
-                Ap += fc.ym * (pc - pym[t]);
-                Ap += up * (pc - pv[t + 2]);
-                Ap += lo * (pc - pv[t]);
+                const int k = k0 + t;
+                const double Ap = stencil_row<double>(fc, fc.area * o.lev_a[k], o.lev_d[k], lo, up, pc, pl, pr,
+                                                      pym[t], pyp[t], pv[t], pv[t + 2]);
                 if (ok)
                     v = v - alpha * Ap;
             }
@@ -407,7 +435,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
             if constexpr (STORED)
                 D = sdg[t] + lo * phi;
             else
-                D = thomas_pivot(delta, aT, lo, up, phi);
+                D = thomas_pivot(diag_base(o, fc, aT, k0 + t), lo, up, phi);
             const TZ inv = (TZ)1 / D;
             iD[t] = inv;
             phi = -up * inv;
@@ -528,13 +556,14 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     const int i = it * kWave + lane;
     const FacesT<TZ> fz = column_faces_t<TZ>(o, i, j);
     const TZ aT = fz.sum();
-    const TZ delta = (TZ)o.delta;
     const int k0 = s * L;
     const unsigned cv = (unsigned)i * (unsigned)sizeof(TV);   // lane's byte offset in a TV row
     const unsigned cz = (unsigned)i * (unsigned)sizeof(TZ);   // ... in a TZ row
     const size_t row0 = ((size_t)j * o.nz + k0) * nx;   // level k0 of row j (uniform)
     const TV alpha = (UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0;
     const double *az = o.az + k0;                       // az[t]: face below level k0+t
+    // area-scaled vertical couplings: vz(t) couples levels k0+t-1 and k0+t
+    auto vz = [&](int t) -> TZ { return fz.area * (TZ)az[t]; };
 
     TV rr[L];
     double r2 = 0.0;
@@ -579,13 +608,9 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
             const double pr_s = __shfl_down(pc, 1, kWave);
             const double pl = lane == 0 ? pe[t] : pl_s;
             const double pr = lane == kWave - 1 ? pe[t] : pr_s;
-            double Ap = o.delta * pc;
-            Ap += fc.xp * (pc - pr);
-            Ap += fc.xm * (pc - pl);
-            Ap += fc.yp * (pc - pyp[t]);
-            Ap += fc.ym * (pc - pym[t]);
-            Ap += az[t + 1] * (pc - pv[t + 2]);
-            Ap += az[t] * (pc - pv[t]);
+            const double Ap = stencil_row<double>(fc, fc.area * o.lev_a[k0 + t], o.lev_d[k0 + t],
+                                                  fc.area * az[t], fc.area * az[t + 1], pc, pl, pr, pym[t],
+                                                  pyp[t], pv[t], pv[t + 2]);
             rr[t] = rr[t] - alpha * Ap;
         }
     } else {
@@ -610,8 +635,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     TZ zpp = 0, mu = 1;
 #pragma unroll
     for (int t = 0; t < L; ++t) {
-        const TZ lo = (TZ)az[t], up = (TZ)az[t + 1];
-        const TZ inv = (TZ)1 / thomas_pivot(delta, aT, lo, up, phi);
+        const TZ lo = vz(t), up = vz(t + 1);
+        const TZ inv = (TZ)1 / thomas_pivot(diag_base(o, fz, aT, k0 + t), lo, up, phi);
         iD[t] = inv;
         phi = -up * inv;
         zpp = ((TZ)rr[t] + lo * zpp) * inv;
@@ -632,13 +657,13 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     TZ prev = zin;
 #pragma unroll
     for (int t = 0; t < L; ++t) {
-        prev = ((TZ)rr[t] + (TZ)az[t] * prev) * iD[t];
+        prev = ((TZ)rr[t] + vz(t) * prev) * iD[t];
         zp[t] = prev;
     }
     TZ znext = 0, H = 1;
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
-        const TZ ph = -(TZ)az[t + 1] * iD[t];
+        const TZ ph = -vz(t + 1) * iD[t];
         znext = zp[t] - ph * znext;
         H = -ph * H;
         zp[t] = znext;
@@ -658,7 +683,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     H = 1;
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
-        H = ((TZ)az[t + 1] * iD[t]) * H;
+        H = (vz(t + 1) * iD[t]) * H;
         const TZ zv = zp[t] + ztop * H;
         kap += (double)rr[t] * (double)zv;
         st_at(z + row0 + (size_t)t * nx, cz, zv);
@@ -685,12 +710,12 @@ __global__ void k_setup_phib(Op o, T *__restrict__ phib)
         return;
     const int j = (int)(col / o.nx);
     const int i = (int)(col - (size_t)j * o.nx);
-    const T aT = column_faces_t<T>(o, i, j).sum();
-    const T delta = (T)o.delta;
+    const FacesT<T> f = column_faces_t<T>(o, i, j);
+    const T aT = f.sum();
     T phi = 0;
     for (int k = 0; k < o.nz; ++k) {
-        const T lo = (T)o.az[k], up = (T)o.az[k + 1];
-        const T inv = (T)1 / thomas_pivot(delta, aT, lo, up, phi);
+        const T lo = f.area * (T)o.az[k], up = f.area * (T)o.az[k + 1];
+        const T inv = (T)1 / thomas_pivot(diag_base(o, f, aT, k), lo, up, phi);
         phi = -up * inv;
         const int kk = k + 1;
         if (kk % o.L == 0 && kk / o.L < o.P)
@@ -723,8 +748,8 @@ __global__ void k_setup_phib_stored(Op o, const double *__restrict__ tri, double
 
 // Assembly of the stored column matrices of M (section 6.2: the tridiagonal
 // matrix of the preconditioner kept as three vectors of length N):
-// sub = -alpha_z[k], diag = delta + alpha_T + alpha_z[k] + alpha_z[k+1],
-// sup = -alpha_z[k+1] (zero couplings at the bottom and top faces).
+// sub = -|T| beta_k, diag = |T| a_k + d_k alpha_T + |T| (beta_k + beta_{k+1}),
+// sup = -|T| beta_{k+1} (zero couplings at the bottom and top faces).
 __global__ void k_tridiag_assemble(Op o, double *__restrict__ tri)
 {
     const size_t ncol = (size_t)o.nx * o.ny;
@@ -734,12 +759,13 @@ __global__ void k_tridiag_assemble(Op o, double *__restrict__ tri)
         return;
     const int j = (int)(col / o.nx);
     const int i = (int)(col - (size_t)j * o.nx);
-    const double aT = column_faces(o, i, j).sum();
+    const Faces f = column_faces(o, i, j);
+    const double aT = f.sum();
     for (int k = 0; k < o.nz; ++k) {
         const size_t l = lin(o, i, j, k);
-        const double lo = o.az[k], up = o.az[k + 1];
+        const double lo = f.area * o.az[k], up = f.area * o.az[k + 1];
         tri[l] = -lo;
-        tri[n + l] = (o.delta + aT) + (lo + up);
+        tri[n + l] = diag_base(o, f, aT, k) + (lo + up);
         tri[2 * n + l] = -up;
     }
 }
@@ -864,7 +890,6 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
     double acc = 0.0;
     if (sw.len > 0) {
         const FacesT<TV> f = column_faces_t<TV>(o, sw.ic, sw.j);
-        const TV delta = (TV)o.delta;
         const int lane = threadIdx.x & (kWave - 1);
         const int ip = (sw.ic + 1 == o.nx) ? 0 : sw.ic + 1;
         const int im = (sw.ic == 0) ? o.nx - 1 : sw.ic - 1;
@@ -934,20 +959,15 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
         for (int t = 0; t < Ls; ++t) {
             if (FULL || t < len) {
                 const int k = k0 + t;
-                const TV lo = (TV)o.az[k], up = (TV)o.az[k + 1];
+                const TV lo = f.area * (TV)o.az[k], up = f.area * (TV)o.az[k + 1];
+                const TV za = f.area * (TV)o.lev_a[k], dk = (TV)o.lev_d[k];
                 const TV zc = zv[t + 1];
                 const TV zl_s = __shfl_up(zc, 1, kWave);
                 const TV zr_s = __shfl_down(zc, 1, kWave);
                 const TV zl = needL ? zxl[t] : zl_s;
                 const TV zr = needR ? zxr[t] : zr_s;
                 // k = 0 / nz-1: the clamped neighbour is zc itself and lo / up is 0
-                TV Az = delta * zc;
-                Az += f.xp * (zc - zr);
-                Az += f.xm * (zc - zl);
-                Az += f.yp * (zc - zyp[t]);
-                Az += f.ym * (zc - zym[t]);
-                Az += up * (zc - zv[t + 2]);
-                Az += lo * (zc - zv[t]);
+                const TV Az = stencil_row(f, za, dk, lo, up, zc, zl, zr, zym[t], zyp[t], zv[t], zv[t + 2]);
                 const size_t l = base + (size_t)k * ks;
                 if constexpr (kAp) {
                     const double pc = pv[t + 1];
@@ -955,13 +975,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
                     const double pr_s = __shfl_down(pc, 1, kWave);
                     const double pl = needL ? pxl[t] : pl_s;
                     const double pr = needR ? pxr[t] : pr_s;
-                    double Ap = o.delta * pc;
-                    Ap += f.xp * (pc - pr);
-                    Ap += f.xm * (pc - pl);
-                    Ap += f.yp * (pc - pyp[t]);
-                    Ap += f.ym * (pc - pym[t]);
-                    Ap += up * (pc - pv[t + 2]);
-                    Ap += lo * (pc - pv[t]);
+                    const double Ap = stencil_row<double>(f, za, dk, lo, up, pc, pl, pr, pym[t], pyp[t], pv[t],
+                                                          pv[t + 2]);
                     if (FULL || sw.ok) {
                         st_s(u + l, uo[t] + alpha * pc);
                         const double pnew = zc + beta * pc;
@@ -1106,26 +1121,27 @@ __global__ __launch_bounds__(kMaxThreads) void k_csr_assemble(Op o, CsrShape cs,
     const int jm = (j == 0) ? o.ny - 1 : j - 1;
     for (int t = 0; t < sw.len; ++t) {
         const int k = sw.k0 + t;
-        const double lo = o.az[k], up = o.az[k + 1];
+        const double lo = f.area * o.az[k], up = f.area * o.az[k + 1];
+        const double dk = o.lev_d[k];
         int32_t cc[7];
         double vv[7];
         int m = 0;
-        double diag = o.delta;
+        double diag = f.area * o.lev_a[k];
         if (cs.hx == 2) {
-            cc[m] = (int32_t)lin(o, ip, j, k); vv[m++] = -f.xp;
-            cc[m] = (int32_t)lin(o, im, j, k); vv[m++] = -f.xm;
-            diag += f.xp + f.xm;
+            cc[m] = (int32_t)lin(o, ip, j, k); vv[m++] = -dk * f.xp;
+            cc[m] = (int32_t)lin(o, im, j, k); vv[m++] = -dk * f.xm;
+            diag += dk * (f.xp + f.xm);
         } else if (cs.hx == 1) {
-            cc[m] = (int32_t)lin(o, ip, j, k); vv[m++] = -(f.xp + f.xm);
-            diag += f.xp + f.xm;
+            cc[m] = (int32_t)lin(o, ip, j, k); vv[m++] = -dk * (f.xp + f.xm);
+            diag += dk * (f.xp + f.xm);
         }
         if (cs.hy == 2) {
-            cc[m] = (int32_t)lin(o, i, jp, k); vv[m++] = -f.yp;
-            cc[m] = (int32_t)lin(o, i, jm, k); vv[m++] = -f.ym;
-            diag += f.yp + f.ym;
+            cc[m] = (int32_t)lin(o, i, jp, k); vv[m++] = -dk * f.yp;
+            cc[m] = (int32_t)lin(o, i, jm, k); vv[m++] = -dk * f.ym;
+            diag += dk * (f.yp + f.ym);
         } else if (cs.hy == 1) {
-            cc[m] = (int32_t)lin(o, i, jp, k); vv[m++] = -(f.yp + f.ym);
-            diag += f.yp + f.ym;
+            cc[m] = (int32_t)lin(o, i, jp, k); vv[m++] = -dk * (f.yp + f.ym);
+            diag += dk * (f.yp + f.ym);
         }
         if (k > 0) {
             cc[m] = (int32_t)lin(o, i, j, k - 1); vv[m++] = -lo;

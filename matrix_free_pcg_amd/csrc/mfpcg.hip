@@ -40,7 +40,8 @@ struct pcg_handle {
     int pt_tiles = 0;      // workgroups of a point pass
     bool pt_full = false;  // every sweep tile whole (nx % 64 == 0, nz % (Ws * Ls) == 0)
     size_t n = 0;          // nx*ny*nz
-    double *d_az = nullptr, *d_ah = nullptr, *d_phib = nullptr;
+    double *d_az = nullptr, *d_phib = nullptr;
+    double *d_coef = nullptr;         // lev_a, lev_d (nz each), area, ex, ey (ny*nx each)
     double *d_phib_tri = nullptr;     // boundary multipliers of the last factored stored tridiagonal
     float *d_phib32 = nullptr;        // boundary multipliers in binary32 (single-precision solves)
     CsrShape csr{};
@@ -549,58 +550,59 @@ const char *pcg_last_error(const pcg_handle *h)
     return h ? h->err.c_str() : g_create_error.c_str();
 }
 
-int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_handle **out)
+}   // extern "C"
+
+namespace {
+
+// The operator in the general form the kernels read (see Op in kernels.hpp).
+struct HostCoeffs {
+    std::vector<double> a, d, beta, area, ex, ey;
+};
+
+// Geometry checks shared by both create functions.
+int check_grid(const char *who, const pcg_grid *grid, Geometry *g)
 {
-    if (!out)
-        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: out is NULL");
-    *out = nullptr;
-    if (!grid || !c)
-        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: null grid or coefficients");
     const int nx = grid->nx, ny = grid->ny, nz = grid->nz;
     if (nx < 1 || ny < 1 || nz < 1)
-        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: grid %d x %d x %d must be positive", nx, ny, nz);
+        return fail(nullptr, PCG_ERR_INVALID, "%s: grid %d x %d x %d must be positive", who, nx, ny, nz);
     if (nz > 512)
-        return fail(nullptr, PCG_ERR_UNSUPPORTED, "pcg_create: nz = %d > 512 is not supported", nz);
-    Geometry g{};
+        return fail(nullptr, PCG_ERR_UNSUPPORTED, "%s: nz = %d > 512 is not supported", who, nz);
     std::string why;
-    if (!choose_geometry(nz, &g, &why))
-        return fail(nullptr, PCG_ERR_UNSUPPORTED, "pcg_create: %s (nz = %d)", why.c_str(), nz);
+    if (!choose_geometry(nz, g, &why))
+        return fail(nullptr, PCG_ERR_UNSUPPORTED, "%s: %s (nz = %d)", who, why.c_str(), nz);
+    const size_t ntx = ((size_t)nx + kWave - 1) / kWave;
+    const size_t ntc = ((size_t)nx + g->C - 1) / g->C;
+    const size_t nkt = ((size_t)nz + (size_t)g->Ls * g->Ws - 1) / ((size_t)g->Ls * g->Ws);
+    if (ntx * nkt * (size_t)ny > (size_t)0x7fffffff || ntc * (size_t)ny > (size_t)0x7fffffff)
+        return fail(nullptr, PCG_ERR_UNSUPPORTED, "%s: too many tiles", who);
+    return PCG_OK;
+}
+
+// Each entry of v[0..n) finite and >= lo (strictly > lo when strict).
+int check_array(const char *who, const char *name, const double *v, size_t n, bool strict)
+{
+    if (!v)
+        return fail(nullptr, PCG_ERR_INVALID, "%s: %s is NULL", who, name);
+    for (size_t t = 0; t < n; ++t) {
+        const double x = v[t];
+        if (!std::isfinite(x) || (strict ? !(x > 0.0) : !(x >= 0.0)))
+            return fail(nullptr, PCG_ERR_INVALID, "%s: %s[%zu] = %g must be finite and %s 0", who, name, t, x,
+                        strict ? ">" : ">=");
+    }
+    return PCG_OK;
+}
+
+// Allocate the handle, copy the coefficients and compute the Thomas
+// multipliers at the segment boundaries (binary64 and binary32 tables).
+int create_handle(const char *who, const pcg_grid *grid, const Geometry &g, const HostCoeffs &hc,
+                  void *hip_stream, pcg_handle **out)
+{
+    const int nx = grid->nx, ny = grid->ny, nz = grid->nz;
     const int L = g.L, C = g.C;
     const size_t ntx = ((size_t)nx + kWave - 1) / kWave;
     const size_t ntc = ((size_t)nx + C - 1) / C;
     const size_t nkt = ((size_t)nz + (size_t)g.Ls * g.Ws - 1) / ((size_t)g.Ls * g.Ws);
-    if (ntx * nkt * (size_t)ny > (size_t)0x7fffffff || ntc * (size_t)ny > (size_t)0x7fffffff)
-        return fail(nullptr, PCG_ERR_UNSUPPORTED, "pcg_create: too many tiles");
-    if (!(c->delta > 0.0) || !std::isfinite(c->delta))
-        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: delta must be finite and > 0");
-    if (!c->alpha_z_face)
-        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: alpha_z_face is NULL");
-    for (int f = 0; f <= nz; ++f) {
-        const double v = c->alpha_z_face[f];
-        if (!(v >= 0.0) || !std::isfinite(v))
-            return fail(nullptr, PCG_ERR_INVALID, "pcg_create: alpha_z_face[%d] = %g must be finite and >= 0", f, v);
-    }
-    if (c->alpha_z_face[0] != 0.0 || c->alpha_z_face[nz] != 0.0)
-        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: faces 0 and nz carry no flux and must be 0");
     const size_t ncol = (size_t)nx * ny;
-    std::vector<double> ah(ncol);
-    if (c->alpha_h_kind == PCG_AH_CONST) {
-        if (!(c->alpha_h_const >= 0.0) || !std::isfinite(c->alpha_h_const))
-            return fail(nullptr, PCG_ERR_INVALID, "pcg_create: alpha_h_const must be finite and >= 0");
-        for (auto &v : ah) v = c->alpha_h_const;
-    } else if (c->alpha_h_kind == PCG_AH_FIELD) {
-        if (!c->alpha_h_field)
-            return fail(nullptr, PCG_ERR_INVALID, "pcg_create: alpha_h_field is NULL");
-        for (size_t t = 0; t < ncol; ++t) {
-            const double v = c->alpha_h_field[t];
-            if (!(v >= 0.0) || !std::isfinite(v))
-                return fail(nullptr, PCG_ERR_INVALID, "pcg_create: alpha_h_field[%zu] = %g must be finite and >= 0", t, v);
-            ah[t] = v;
-        }
-    } else {
-        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: unknown alpha_h_kind %d", c->alpha_h_kind);
-    }
-
     pcg_handle *h = new pcg_handle();
     auto bail = [&](int code) {
         g_create_error = h->err;
@@ -608,7 +610,7 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
         return code;
     };
     if (hipGetDevice(&h->device) != hipSuccess) {
-        h->err = "pcg_create: hipGetDevice failed";
+        h->err = std::string(who) + ": hipGetDevice failed";
         return bail(PCG_ERR_HIP);
     }
     h->stream = (hipStream_t)hip_stream;
@@ -636,24 +638,32 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
     // one strip of i-tiles per XCD (MFPCG_ST_STRIP overrides; 1 = i-tile slowest)
     h->op.sg = std::max(1, std::min((int)ntx, env_int("MFPCG_ST_STRIP", (int)((ntx + kXcds - 1) / kXcds))));
     h->op.csg = std::max(1, std::min((int)ntc, env_int("MFPCG_COL_STRIP", (int)((ntc + kXcds - 1) / kXcds))));
-    h->op.delta = c->delta;
+    const size_t ncoef = 2 * (size_t)nz + 3 * ncol;
     hipError_t e;
     if ((e = hipMalloc(&h->d_az, sizeof(double) * (nz + 1))) != hipSuccess ||
-        (e = hipMalloc(&h->d_ah, sizeof(double) * ncol)) != hipSuccess ||
+        (e = hipMalloc(&h->d_coef, sizeof(double) * ncoef)) != hipSuccess ||
         (e = hipMalloc(&h->d_phib, sizeof(double) * ncol * (size_t)(P > 1 ? P - 1 : 1))) != hipSuccess ||
         (e = hipMalloc(&h->d_phib32, sizeof(float) * ncol * (size_t)(P > 1 ? P - 1 : 1))) != hipSuccess ||
         (e = hipHostMalloc((void **)&h->h_status, sizeof(HostStatus), hipHostMallocCoherent)) != hipSuccess) {
-        h->err = std::string("pcg_create: allocation failed: ") + hipGetErrorString(e);
+        h->err = std::string(who) + ": allocation failed: " + hipGetErrorString(e);
         return bail(PCG_ERR_HIP);
     }
     memset(h->h_status, 0, sizeof(HostStatus));
-    if ((e = hipMemcpyAsync(h->d_az, c->alpha_z_face, sizeof(double) * (nz + 1), hipMemcpyHostToDevice, h->stream)) != hipSuccess ||
-        (e = hipMemcpyAsync(h->d_ah, ah.data(), sizeof(double) * ncol, hipMemcpyHostToDevice, h->stream)) != hipSuccess) {
-        h->err = std::string("pcg_create: copy failed: ") + hipGetErrorString(e);
+    std::vector<double> coef;
+    coef.reserve(ncoef);
+    for (const auto *v : {&hc.a, &hc.d, &hc.area, &hc.ex, &hc.ey})
+        coef.insert(coef.end(), v->begin(), v->end());
+    if ((e = hipMemcpy(h->d_az, hc.beta.data(), sizeof(double) * (nz + 1), hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(h->d_coef, coef.data(), sizeof(double) * ncoef, hipMemcpyHostToDevice)) != hipSuccess) {
+        h->err = std::string(who) + ": copy failed: " + hipGetErrorString(e);
         return bail(PCG_ERR_HIP);
     }
     h->op.az = h->d_az;
-    h->op.ah = h->d_ah;
+    h->op.lev_a = h->d_coef;
+    h->op.lev_d = h->d_coef + nz;
+    h->op.area = h->d_coef + 2 * (size_t)nz;
+    h->op.ex = h->op.area + ncol;
+    h->op.ey = h->op.ex + ncol;
     h->op.phib = h->d_phib;
     if (P > 1) {
         const int threads = 256;
@@ -662,11 +672,100 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
         k_setup_phib<float><<<dim3((unsigned)blocks), dim3(threads), 0, h->stream>>>(h->op, h->d_phib32);
     }
     if ((e = hipStreamSynchronize(h->stream)) != hipSuccess || (e = hipGetLastError()) != hipSuccess) {
-        h->err = std::string("pcg_create: set-up failed: ") + hipGetErrorString(e);
+        h->err = std::string(who) + ": set-up failed: " + hipGetErrorString(e);
         return bail(PCG_ERR_HIP);
     }
     *out = h;
     return PCG_OK;
+}
+
+}   // namespace
+
+extern "C" {
+
+int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_handle **out)
+{
+    const char *who = "pcg_create";
+    if (!out)
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: out is NULL");
+    *out = nullptr;
+    if (!grid || !c)
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: null grid or coefficients");
+    Geometry g{};
+    int rc = check_grid(who, grid, &g);
+    if (rc != PCG_OK)
+        return rc;
+    const int nx = grid->nx, ny = grid->ny, nz = grid->nz;
+    if (!(c->delta > 0.0) || !std::isfinite(c->delta))
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: delta must be finite and > 0");
+    if ((rc = check_array(who, "alpha_z_face", c->alpha_z_face, (size_t)nz + 1, false)) != PCG_OK)
+        return rc;
+    if (c->alpha_z_face[0] != 0.0 || c->alpha_z_face[nz] != 0.0)
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: faces 0 and nz carry no flux and must be 0");
+    const size_t ncol = (size_t)nx * ny;
+    std::vector<double> ah(ncol);
+    if (c->alpha_h_kind == PCG_AH_CONST) {
+        if (!(c->alpha_h_const >= 0.0) || !std::isfinite(c->alpha_h_const))
+            return fail(nullptr, PCG_ERR_INVALID, "pcg_create: alpha_h_const must be finite and >= 0");
+        for (auto &v : ah) v = c->alpha_h_const;
+    } else if (c->alpha_h_kind == PCG_AH_FIELD) {
+        if ((rc = check_array(who, "alpha_h_field", c->alpha_h_field, ncol, false)) != PCG_OK)
+            return rc;
+        ah.assign(c->alpha_h_field, c->alpha_h_field + ncol);
+    } else {
+        return fail(nullptr, PCG_ERR_INVALID, "pcg_create: unknown alpha_h_kind %d", c->alpha_h_kind);
+    }
+    // the special case of the general form: |T| = 1, a = delta, d = 1,
+    // beta = alpha_z, and the edge coefficient between two cells the mean of
+    // their alpha_h (section 3, eqs. (6)-(7): one symmetric value per edge)
+    HostCoeffs hc;
+    hc.a.assign(nz, c->delta);
+    hc.d.assign(nz, 1.0);
+    hc.beta.assign(c->alpha_z_face, c->alpha_z_face + nz + 1);
+    hc.area.assign(ncol, 1.0);
+    hc.ex.resize(ncol);
+    hc.ey.resize(ncol);
+    for (int j = 0; j < ny; ++j)
+        for (int i = 0; i < nx; ++i) {
+            const size_t t = (size_t)j * nx + i;
+            hc.ex[t] = 0.5 * (ah[t] + ah[(size_t)j * nx + (i + 1 == nx ? 0 : i + 1)]);
+            hc.ey[t] = 0.5 * (ah[t] + ah[(size_t)(j + 1 == ny ? 0 : j + 1) * nx + i]);
+        }
+    return create_handle(who, grid, g, hc, hip_stream, out);
+}
+
+int pcg_create_general(const pcg_grid *grid, const pcg_coeffs_general *c, void *hip_stream,
+                       pcg_handle **out)
+{
+    const char *who = "pcg_create_general";
+    if (!out)
+        return fail(nullptr, PCG_ERR_INVALID, "%s: out is NULL", who);
+    *out = nullptr;
+    if (!grid || !c)
+        return fail(nullptr, PCG_ERR_INVALID, "%s: null grid or coefficients", who);
+    Geometry g{};
+    int rc = check_grid(who, grid, &g);
+    if (rc != PCG_OK)
+        return rc;
+    const int nx = grid->nx, ny = grid->ny, nz = grid->nz;
+    const size_t ncol = (size_t)nx * ny;
+    if ((rc = check_array(who, "a", c->a, (size_t)nz, true)) != PCG_OK ||
+        (rc = check_array(who, "d", c->d, (size_t)nz, false)) != PCG_OK ||
+        (rc = check_array(who, "beta_face", c->beta_face, (size_t)nz + 1, false)) != PCG_OK ||
+        (rc = check_array(who, "area", c->area, ncol, true)) != PCG_OK ||
+        (rc = check_array(who, "alpha_x", c->alpha_x, ncol, false)) != PCG_OK ||
+        (rc = check_array(who, "alpha_y", c->alpha_y, ncol, false)) != PCG_OK)
+        return rc;
+    if (c->beta_face[0] != 0.0 || c->beta_face[nz] != 0.0)
+        return fail(nullptr, PCG_ERR_INVALID, "%s: faces 0 and nz carry no flux and must be 0", who);
+    HostCoeffs hc;
+    hc.a.assign(c->a, c->a + nz);
+    hc.d.assign(c->d, c->d + nz);
+    hc.beta.assign(c->beta_face, c->beta_face + nz + 1);
+    hc.area.assign(c->area, c->area + ncol);
+    hc.ex.assign(c->alpha_x, c->alpha_x + ncol);
+    hc.ey.assign(c->alpha_y, c->alpha_y + ncol);
+    return create_handle(who, grid, g, hc, hip_stream, out);
 }
 
 int pcg_destroy(pcg_handle *h)
@@ -683,7 +782,7 @@ int pcg_destroy(pcg_handle *h)
     for (auto e : h->free_events)
         (void)hipEventDestroy(e);
     if (h->d_az) (void)hipFree(h->d_az);
-    if (h->d_ah) (void)hipFree(h->d_ah);
+    if (h->d_coef) (void)hipFree(h->d_coef);
     if (h->d_phib) (void)hipFree(h->d_phib);
     if (h->d_phib32) (void)hipFree(h->d_phib32);
     if (h->d_phib_tri) (void)hipFree(h->d_phib_tri);

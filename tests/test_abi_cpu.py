@@ -124,3 +124,38 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _abi.load()
+
+
+@pytest.mark.parametrize("case", ["a_zero", "a_nan", "d_negative", "beta_boundary", "beta_negative",
+                                  "area_zero", "alpha_x_negative", "alpha_y_inf", "null_area"])
+def test_create_general_rejects_invalid_arguments(lib, case):
+    nx, ny, nz = 4, 3, 6
+    arrs = dict(a=np.full(nz, 1e-2), d=np.ones(nz), beta_face=np.r_[0.0, np.full(nz - 1, 5.0), 0.0],
+                area=np.ones(nx * ny), alpha_x=np.ones(nx * ny), alpha_y=np.ones(nx * ny))
+    if case == "a_zero":
+        arrs["a"][2] = 0.0
+    elif case == "a_nan":
+        arrs["a"][0] = float("nan")
+    elif case == "d_negative":
+        arrs["d"][1] = -1.0
+    elif case == "beta_boundary":
+        arrs["beta_face"][nz] = 1.0
+    elif case == "beta_negative":
+        arrs["beta_face"][3] = -2.0
+    elif case == "area_zero":
+        arrs["area"][5] = 0.0
+    elif case == "alpha_x_negative":
+        arrs["alpha_x"][0] = -0.1
+    elif case == "alpha_y_inf":
+        arrs["alpha_y"][7] = float("inf")
+    c = _abi.pcg_coeffs_general()
+    for name, v in arrs.items():
+        if case == "null_area" and name == "area":
+            continue
+        setattr(c, name, v.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    g = _abi.pcg_grid(nx, ny, nz)
+    out = ctypes.c_void_p()
+    rc = lib.pcg_create_general(ctypes.byref(g), ctypes.byref(c), None, ctypes.byref(out))
+    assert rc == _abi.PCG_ERR_INVALID
+    assert out.value is None
+    assert "pcg_create_general" in _abi.pcg_last_error(None)

@@ -203,3 +203,40 @@ def test_cfg5_explicit_path_full(dev):
     assert res2["iters"] == ref["iters"] == 2
     assert np.allclose(res2["hist"], ref["hist"], rtol=1e-11, atol=0)
     assert np.linalg.norm(x2h - ref["x"]) <= 1e-11 * np.linalg.norm(ref["x"])
+
+
+def test_general_full_size(dev):
+    """general-1024x1024x128 in the benchmark's launch configuration: the whole
+    stencil and column solve against the oracle, and the full solve's true
+    residual evaluated by the oracle's general stencil."""
+    import torch
+    from test_gpu_general import gen_column_cond, gen_scale
+    t = time.time()
+    w = W.make_workload(6)
+    gp = w.problem
+    print(f"\n[general] inputs generated in {time.time() - t:.1f}s", flush=True)
+    h = mf.pcg_create(gp)
+    try:
+        bd = to_dev(w.rhs, dev)
+        yd = torch.empty_like(bd)
+        zd = torch.empty_like(bd)
+        mf.pcg_apply_A(h, bd, yd)
+        mf.pcg_precond(h, bd, zd)
+        torch.cuda.synchronize()
+        y, z = to_host(yd), to_host(zd)
+        del yd, zd
+        xd = torch.zeros_like(bd)
+        res = mf.pcg_solve(h, bd, xd, w.tol, w.maxit)
+        torch.cuda.synchronize()
+        xg = to_host(xd)
+        del bd, xd
+    finally:
+        mf.pcg_destroy(h)
+    assert np.abs(y - oracle.apply_A_gen(gp, w.rhs)).max() <= 16 * EPS * gen_scale(gp, w.rhs)
+    zo = oracle.precond_gen(gp, w.rhs)
+    assert np.abs(z - zo).max() <= 64 * EPS * gen_column_cond(gp) * np.abs(zo).max()
+    del y, z, zo
+    assert res["status"] == mf.PCG_OK, res
+    tr = np.linalg.norm(w.rhs - oracle.apply_A_gen(gp, xg)) / np.linalg.norm(w.rhs)
+    print(f"[general] iters={res['iters']} recursive={res['final_rel_res']:.3e} true={tr:.3e}", flush=True)
+    assert tr <= 1e-8, tr

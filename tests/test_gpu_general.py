@@ -1,0 +1,180 @@
+"""GPU parity of the general tensor-product operator (section 3, eqs.
+(5)-(8): per-level a_k, d_k, beta, per-column |T|, per-edge alpha) against the
+oracle's general functions (pinned by G1-G5).  Tolerances as for the special
+operator, with the general stencil scale and column conditioning:
+  * stencil: |y_gpu - y_orc| <= 16 eps S, S = max(|T| a + 2 d (ax + ay) + 4 |T| beta) ||x||_inf
+    bounds the sum of the terms' magnitudes in any cell (counting each edge
+    from both sides);
+  * column solve: |z_gpu - z_orc| <= 64 eps kappa ||z||_inf, kappa the
+    Gershgorin bound of the column matrices' condition number;
+  * solves: iterations within 1, final iterates within rel-L2 1e-9, and the
+    residual histories while ||r|| >= 1e-6 ||r0|| within max(1e-6, 10x the
+    oracle's own spread under an ulp-level perturbation of b)."""
+import numpy as np
+import pytest
+
+import matrix_free_pcg_amd as mf
+import oracle
+from gpu_helpers import EPS, require_gpu, to_dev, to_host
+from matrix_free_pcg_amd import workloads as W
+from oracle_pins import dense_from_apply_gen, random_general
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+GRIDS = [
+    ("general-70x45x40", lambda: W.general_problem(70, 45, 40, 6)),
+    ("general-128x24x64", lambda: W.general_problem(128, 24, 64, 6)),
+    ("general-65x4x130", lambda: W.general_problem(65, 4, 130, 6)),
+    ("random-7x5x9", lambda: random_general(7, 5, 9, seed=1)),
+    ("random-1x3x4", lambda: random_general(1, 3, 4, seed=2)),
+    ("random-2x2x2", lambda: random_general(2, 2, 2, seed=3)),
+    ("random-64x2x512", lambda: random_general(64, 2, 512, seed=4)),
+]
+
+
+def gen_scale(gp, x):
+    T = gp.area
+    hor = gp.d.max() * (gp.alpha_x + np.roll(gp.alpha_x, 1, axis=1) + gp.alpha_y + np.roll(gp.alpha_y, 1, axis=0)).max()
+    return (T.max() * gp.a.max() + hor + 4 * T.max() * gp.beta_face.max()) * np.abs(x).max()
+
+
+def gen_column_cond(gp):
+    aT = gp.alpha_x + np.roll(gp.alpha_x, 1, axis=1) + gp.alpha_y + np.roll(gp.alpha_y, 1, axis=0)
+    lo = (gp.area[:, None, :] * gp.a[None, :, None] + gp.d[None, :, None] * aT[:, None, :]).min()
+    vert = gp.beta_face[:-1] + gp.beta_face[1:]
+    hi = (gp.area[:, None, :] * (gp.a + 2 * vert)[None, :, None] + gp.d[None, :, None] * aT[:, None, :]).max()
+    return hi / lo
+
+
+@pytest.mark.parametrize("label,make", GRIDS, ids=[g[0] for g in GRIDS])
+def test_general_apply_and_precond(dev, label, make):
+    import torch
+    gp = make()
+    x = W.uniform_field(gp.nx, gp.ny, gp.nz, 101)
+    r = W.gaussian_field(gp.nx, gp.ny, gp.nz, 202)
+    h = mf.pcg_create(gp)
+    try:
+        xd, rd = to_dev(x, dev), to_dev(r, dev)
+        yd = torch.full_like(xd, float("nan"))
+        zd = torch.full_like(xd, float("nan"))
+        mf.pcg_apply_A(h, xd, yd)
+        mf.pcg_precond(h, rd, zd)
+        torch.cuda.synchronize()
+        y, z = to_host(yd), to_host(zd)
+    finally:
+        mf.pcg_destroy(h)
+    yo = oracle.apply_A_gen(gp, x)
+    zo = oracle.precond_gen(gp, r)
+    assert np.abs(y - yo).max() <= 16 * EPS * gen_scale(gp, x), label
+    assert np.abs(z - zo).max() <= 64 * EPS * gen_column_cond(gp) * np.abs(zo).max(), label
+
+
+SOLVES = [
+    ("general-70x45x40", lambda: W.general_problem(70, 45, 40, 6), 6),
+    ("general-128x24x64", lambda: W.general_problem(128, 24, 64, 6), 7),
+    ("random-33x5x9", lambda: random_general(33, 5, 9, seed=5), 8),
+]
+SOLVERS = {"interleaved": mf.pcg_solve, "standard": mf.pcg_solve_standard, "no_q": mf.pcg_solve_no_q}
+
+
+@pytest.mark.parametrize("variant", list(SOLVERS))
+@pytest.mark.parametrize("label,make,seed", SOLVES, ids=[c[0] for c in SOLVES])
+def test_general_solve_matches_oracle(dev, label, make, seed, variant):
+    import torch
+    gp = make()
+    b = W.uniform_field(gp.nx, gp.ny, gp.nz, seed)
+    h = mf.pcg_create(gp)
+    try:
+        bd = to_dev(b, dev)
+        xd = torch.zeros_like(bd)
+        res = SOLVERS[variant](h, bd, xd, 1e-10, 5000)
+        torch.cuda.synchronize()
+        xg = to_host(xd)
+    finally:
+        mf.pcg_destroy(h)
+    ref = oracle.pcg_gen(gp, b, tol=1e-10, maxit=5000)
+    assert res["status"] == ref["status"] == 0, (label, res, ref["status"])
+    assert abs(res["iters"] - ref["iters"]) <= 1, (label, res["iters"], ref["iters"])
+    rel = np.linalg.norm(xg - ref["x"]) / np.linalg.norm(ref["x"])
+    u = np.random.default_rng(4242).uniform(-1.0, 1.0, size=b.shape)
+    spread = oracle.pcg_gen(gp, b * (1.0 + 2.0 ** -52 * u), tol=1e-10, maxit=5000)["hist"]
+    n = min(len(res["hist"]), len(ref["hist"]), len(spread))
+    hg, ho, hs = res["hist"][:n], ref["hist"][:n], spread[:n]
+    big = ho >= 1e-6 * ho[0]
+    dg = np.max(np.abs(hg[big] - ho[big]) / ho[big])
+    ds = np.max(np.abs(hs[big] - ho[big]) / ho[big])
+    print(f"{label} {variant}: iters gpu {res['iters']} oracle {ref['iters']} rel-L2 {rel:.2e} history {dg:.2e} (self {ds:.2e})")
+    assert rel <= 1e-9, (label, rel)
+    assert dg <= max(1e-6, 10 * ds), (label, dg, ds)
+
+
+def test_general_mixed_solve_converges(dev):
+    """Binary64 PCG with the binary32 column solve on the general operator:
+    converged (true residual by the oracle's general stencil) and within 1e-8
+    of the oracle's binary64 solution."""
+    import torch
+    gp = W.general_problem(70, 45, 40, 6)
+    b = W.uniform_field(gp.nx, gp.ny, gp.nz, 6)
+    h = mf.pcg_create(gp)
+    try:
+        bd = to_dev(b, dev)
+        xd = torch.zeros_like(bd)
+        res = mf.pcg_solve_mixed(h, bd, xd, 1e-10, 5000)
+        torch.cuda.synchronize()
+        xg = to_host(xd)
+    finally:
+        mf.pcg_destroy(h)
+    ref = oracle.pcg_gen(gp, b, tol=1e-10, maxit=5000)
+    assert res["status"] == 0
+    assert abs(res["iters"] - ref["iters"]) <= 0.2 * ref["iters"] + 2, (res["iters"], ref["iters"])
+    tr = np.linalg.norm(b - oracle.apply_A_gen(gp, xg)) / np.linalg.norm(b)
+    assert tr <= 1e-9, tr
+    assert np.linalg.norm(xg - ref["x"]) <= 1e-8 * np.linalg.norm(ref["x"])
+
+
+@pytest.mark.parametrize("nx,ny,nz", [(5, 4, 6), (1, 3, 4), (2, 2, 3)])
+def test_general_csr_matches_dense_operator(dev, nx, ny, nz):
+    import torch
+    gp = random_general(nx, ny, nz, seed=nx + 10 * ny)
+    A = dense_from_apply_gen(oracle.default(), gp)
+    h = mf.pcg_create(gp)
+    try:
+        C = mf.pcg_csr_assemble(h)
+        torch.cuda.synchronize()
+        rp, col, val = to_host(C.row_ptr), to_host(C.col), to_host(C.val)
+    finally:
+        mf.pcg_destroy(h)
+    exp_rp, exp_col, exp_val = [0], [], []
+    for l in range(gp.n):
+        nzc = np.nonzero(A[l])[0]
+        exp_col.extend(nzc.tolist())
+        exp_val.extend(A[l, nzc].tolist())
+        exp_rp.append(len(exp_col))
+    assert np.array_equal(rp, np.array(exp_rp)) and np.array_equal(col, np.array(exp_col, dtype=np.int32))
+    assert np.abs(val - np.array(exp_val)).max() <= 8 * EPS * np.abs(A).max()
+
+
+def test_general_explicit_solve_matches_oracle(dev):
+    import torch
+    gp = W.general_problem(70, 45, 40, 6)
+    b = W.uniform_field(gp.nx, gp.ny, gp.nz, 9)
+    h = mf.pcg_create(gp)
+    try:
+        C = mf.pcg_csr_assemble(h)
+        tri = mf.pcg_tridiag_assemble(h)
+        bd = to_dev(b, dev)
+        xd = torch.zeros_like(bd)
+        res = mf.pcg_solve_csr(h, C, tri, bd, xd, 1e-10, 5000)
+        torch.cuda.synchronize()
+        xg = to_host(xd)
+    finally:
+        mf.pcg_destroy(h)
+    ref = oracle.pcg_gen(gp, b, tol=1e-10, maxit=5000)
+    assert res["status"] == 0 and abs(res["iters"] - ref["iters"]) <= 1, (res["iters"], ref["iters"])
+    assert np.linalg.norm(xg - ref["x"]) <= 1e-9 * np.linalg.norm(ref["x"])
