@@ -15,6 +15,7 @@ import ctypes
 import os
 import subprocess
 import threading
+import types
 
 import numpy as np
 
@@ -93,6 +94,15 @@ class Oracle:
         lib.orc_precond_gen.restype = i
         lib.orc_pcg_gen.argtypes = gen + [dp, dp, d, i, dp, ip]
         lib.orc_pcg_gen.restype = i
+        lib.orc_mg_coarsen.argtypes = [i, i, dp, dp, dp, ip, ip, dp, dp, dp]
+        lib.orc_mg_coarsen.restype = i
+        lib.orc_mg_num_levels.argtypes = [i, i, i]
+        lib.orc_mg_num_levels.restype = i
+        mg = [i, d, i, i]
+        lib.orc_mg_vcycle.argtypes = gen + mg + [dp, dp]
+        lib.orc_mg_vcycle.restype = i
+        lib.orc_pcg_mg.argtypes = gen + mg + [dp, dp, d, i, dp, ip]
+        lib.orc_pcg_mg.restype = i
         self.lib = lib
         self.path = path
 
@@ -229,6 +239,51 @@ class Oracle:
                                   ctypes.byref(iters))
         return dict(x=x, iters=iters.value, hist=hist[: iters.value + 1].copy(), status=st)
 
+    # ---- tensor-product multigrid (readings in oracle.c) --------------------
+    def mg_coarsen(self, gp):
+        """The Galerkin coarse operator of one coarsening step, as an object
+        with the fields of a general problem; None if the level cannot be
+        coarsened."""
+        a, d, beta, area, ax, ay = self._gen(gp)
+        ncol = gp.nx * gp.ny
+        ca, cx, cy = np.zeros(ncol), np.zeros(ncol), np.zeros(ncol)
+        ncx, ncy = ctypes.c_int(0), ctypes.c_int(0)
+        if not self.lib.orc_mg_coarsen(gp.nx, gp.ny, _ptr(area), _ptr(ax), _ptr(ay), ctypes.byref(ncx),
+                                       ctypes.byref(ncy), _ptr(ca), _ptr(cx), _ptr(cy)):
+            return None
+        m = ncx.value * ncy.value
+        shape = (ncy.value, ncx.value)
+        return types.SimpleNamespace(nx=ncx.value, ny=ncy.value, nz=gp.nz, n=m * gp.nz, a=a.copy(), d=d.copy(),
+                                     beta_face=beta.copy(), area=ca[:m].reshape(shape).copy(),
+                                     alpha_x=cx[:m].reshape(shape).copy(), alpha_y=cy[:m].reshape(shape).copy())
+
+    def mg_num_levels(self, nx: int, ny: int, max_levels: int = 0) -> int:
+        return self.lib.orc_mg_num_levels(int(nx), int(ny), int(max_levels))
+
+    def mg_vcycle(self, gp, r, nu: int = 1, omega: float = 0.8, max_levels: int = 0,
+                  coarse_sweeps: int = 2) -> np.ndarray:
+        """z = B r: one V(nu, nu) cycle of the multigrid hierarchy."""
+        r = self._field(r, gp)
+        args, keep = self._gen_args(gp)
+        z = np.empty_like(r)
+        st = self.lib.orc_mg_vcycle(*args, int(nu), float(omega), int(max_levels), int(coarse_sweeps),
+                                    _ptr(r), _ptr(z))
+        if st != OK:
+            raise FloatingPointError(f"V-cycle failed ({st})")
+        return z
+
+    def pcg_mg(self, gp, b, x0=None, tol: float = 1e-10, maxit: int = 500, nu: int = 1,
+               omega: float = 0.8, max_levels: int = 0, coarse_sweeps: int = 2):
+        """Textbook PCG with one V-cycle per step.  Returns dict(x, iters, hist, status)."""
+        b = self._field(b, gp)
+        x = np.zeros_like(b) if x0 is None else self._field(x0, gp).copy()
+        args, keep = self._gen_args(gp)
+        hist = np.zeros(max(1, maxit + 1))
+        iters = ctypes.c_int(0)
+        st = self.lib.orc_pcg_mg(*args, int(nu), float(omega), int(max_levels), int(coarse_sweeps),
+                                 _ptr(b), _ptr(x), float(tol), int(maxit), _ptr(hist), ctypes.byref(iters))
+        return dict(x=x, iters=iters.value, hist=hist[: iters.value + 1].copy(), status=st)
+
     def dot(self, a, b) -> float:
         a = np.ascontiguousarray(a, dtype=np.float64).ravel()
         b = np.ascontiguousarray(b, dtype=np.float64).ravel()
@@ -318,3 +373,19 @@ def precond_gen(gp, r):
 
 def pcg_gen(gp, b, x0=None, tol=1e-10, maxit=500):
     return default().pcg_gen(gp, b, x0, tol, maxit)
+
+
+def mg_coarsen(gp):
+    return default().mg_coarsen(gp)
+
+
+def mg_num_levels(nx, ny, max_levels=0):
+    return default().mg_num_levels(nx, ny, max_levels)
+
+
+def mg_vcycle(gp, r, nu=1, omega=0.8, max_levels=0, coarse_sweeps=2):
+    return default().mg_vcycle(gp, r, nu, omega, max_levels, coarse_sweeps)
+
+
+def pcg_mg(gp, b, x0=None, tol=1e-10, maxit=500, nu=1, omega=0.8, max_levels=0, coarse_sweeps=2):
+    return default().pcg_mg(gp, b, x0, tol, maxit, nu, omega, max_levels, coarse_sweeps)

@@ -630,3 +630,279 @@ done:
     free(r); free(z); free(p); free(q);
     return status;
 }
+
+/* ======================================================================
+ * Tensor-product multigrid as the preconditioner of CG (section 2 names
+ * geometric multigrid with the vertical line relaxation as the faster CPU
+ * solver, and section 8 plans it on the GPU; the pages give no intergrid
+ * operators).  Readings (also in the design notes):
+ *  - levels: level 0 is the grid; the next level halves nx where nx is even
+ *    and > 1 and ny where ny is even and > 1, and keeps nz (horizontal
+ *    semi-coarsening: the strong vertical coupling is left to the smoother);
+ *    the hierarchy ends at a single column, at a level where neither
+ *    dimension can be halved, or after max_levels levels (0 = no limit);
+ *  - transfers: piecewise-constant prolongation P (a fine column takes its
+ *    coarse parent's value at the same level) and restriction P^T (the sum
+ *    over the children);
+ *  - coarse operator: the Galerkin product P^T A P.  It has the general
+ *    form again: a coarse column's |T| is the sum of its children's, its
+ *    edge to a coarse neighbour is the sum of the fine edges crossing that
+ *    coarse edge, a, d and beta are unchanged, and the edges of a dimension
+ *    of size 1 are zero (they would couple a column with itself, which
+ *    cancels in P^T A P);
+ *  - smoother: damped block Jacobi with the column blocks (the line
+ *    relaxation; M of the PCG preconditioner on that level):
+ *    z <- z + omega M^{-1} (f - A z);
+ *  - cycle: V(nu, nu): nu sweeps from z = 0, the coarse correction, nu
+ *    sweeps; on the coarsest level z = M^{-1} f when it is one column (exact,
+ *    its edges being zero), else coarse_sweeps sweeps from z = 0.
+ * ====================================================================== */
+
+/* Coarsening factors of an nx x ny level (1 or 2 each); 0 if neither
+ * dimension can be halved. */
+static int mg_factors(int nx, int ny, int *fx, int *fy)
+{
+    *fx = (nx > 1 && nx % 2 == 0) ? 2 : 1;
+    *fy = (ny > 1 && ny % 2 == 0) ? 2 : 1;
+    return (*fx > 1 || *fy > 1);
+}
+
+/* One Galerkin coarsening step (readings above).  The coarse arrays hold
+ * (nx/fx)*(ny/fy) entries.  Sums run over the children in the order
+ * (row b outer, column a inner).  Returns 1 and the coarse sizes, or 0 when
+ * the level cannot be coarsened. */
+int orc_mg_coarsen(int nx, int ny, const double *area, const double *ax, const double *ay,
+                   int *ncx_out, int *ncy_out, double *carea, double *cax, double *cay)
+{
+    int fx, fy;
+    if (!mg_factors(nx, ny, &fx, &fy))
+        return 0;
+    int ncx = nx / fx, ncy = ny / fy;
+    for (int J = 0; J < ncy; ++J)
+        for (int I = 0; I < ncx; ++I) {
+            double sa = 0.0, sx = 0.0, sy = 0.0;
+            for (int b = 0; b < fy; ++b)
+                for (int a = 0; a < fx; ++a)
+                    sa += area[(size_t)(fy * J + b) * nx + (fx * I + a)];
+            /* fine x-edges between columns fx*I+fx-1 and fx*I+fx (mod nx) of
+             * the children rows cross the coarse edge between I and I+1 */
+            for (int b = 0; b < fy; ++b)
+                sx += ax[(size_t)(fy * J + b) * nx + (fx * I + fx - 1)];
+            /* fine y-edges between rows fy*J+fy-1 and fy*J+fy (mod ny) */
+            for (int a = 0; a < fx; ++a)
+                sy += ay[(size_t)(fy * J + fy - 1) * nx + (fx * I + a)];
+            carea[(size_t)J * ncx + I] = sa;
+            cax[(size_t)J * ncx + I] = (ncx == 1) ? 0.0 : sx;
+            cay[(size_t)J * ncx + I] = (ncy == 1) ? 0.0 : sy;
+        }
+    *ncx_out = ncx;
+    *ncy_out = ncy;
+    return 1;
+}
+
+typedef struct {
+    int nx, ny;
+    double *area, *ax, *ay;    /* the level's coefficients (level 0: the caller's) */
+    double *f, *z;             /* right-hand side and correction (levels >= 1) */
+    double *t, *y;             /* residual and M^{-1} residual */
+    int owns;
+} mg_level;
+
+static void mg_free(mg_level *lv, int nlev)
+{
+    if (!lv)
+        return;
+    for (int l = 0; l < nlev; ++l) {
+        if (lv[l].owns) {
+            free(lv[l].area); free(lv[l].ax); free(lv[l].ay);
+        }
+        free(lv[l].f); free(lv[l].z); free(lv[l].t); free(lv[l].y);
+    }
+    free(lv);
+}
+
+/* Number of levels for an nx x ny grid (readings above). */
+int orc_mg_num_levels(int nx, int ny, int max_levels)
+{
+    int n = 1, fx, fy;
+    while ((max_levels <= 0 || n < max_levels) && nx * ny > 1 && mg_factors(nx, ny, &fx, &fy)) {
+        nx /= fx;
+        ny /= fy;
+        ++n;
+    }
+    return n;
+}
+
+static mg_level *mg_build(int nx, int ny, int nz, const double *area, const double *ax,
+                          const double *ay, int max_levels, int *nlev_out)
+{
+    int nlev = orc_mg_num_levels(nx, ny, max_levels);
+    mg_level *lv = (mg_level *)calloc((size_t)nlev, sizeof(mg_level));
+    if (!lv)
+        return NULL;
+    lv[0].nx = nx;
+    lv[0].ny = ny;
+    lv[0].area = (double *)area;
+    lv[0].ax = (double *)ax;
+    lv[0].ay = (double *)ay;
+    for (int l = 0; l < nlev; ++l) {
+        size_t ncol = (size_t)lv[l].nx * lv[l].ny, n = ncol * nz;
+        lv[l].t = (double *)malloc(sizeof(double) * n);
+        lv[l].y = (double *)malloc(sizeof(double) * n);
+        if (l > 0) {
+            lv[l].f = (double *)malloc(sizeof(double) * n);
+            lv[l].z = (double *)malloc(sizeof(double) * n);
+        }
+        if (!lv[l].t || !lv[l].y || (l > 0 && (!lv[l].f || !lv[l].z))) {
+            mg_free(lv, nlev);
+            return NULL;
+        }
+        if (l + 1 < nlev) {
+            mg_level *c = &lv[l + 1];
+            c->owns = 1;
+            c->area = (double *)malloc(sizeof(double) * ncol);
+            c->ax = (double *)malloc(sizeof(double) * ncol);
+            c->ay = (double *)malloc(sizeof(double) * ncol);
+            if (!c->area || !c->ax || !c->ay) {
+                mg_free(lv, nlev);
+                return NULL;
+            }
+            orc_mg_coarsen(lv[l].nx, lv[l].ny, lv[l].area, lv[l].ax, lv[l].ay, &c->nx, &c->ny,
+                           c->area, c->ax, c->ay);
+        }
+    }
+    *nlev_out = nlev;
+    return lv;
+}
+
+/* One smoothing sweep on level L: z <- z + omega M^{-1} (f - A z). */
+static int mg_smooth(const mg_level *L, int nz, const double *a, const double *d, const double *beta,
+                     double omega, const double *f, double *z)
+{
+    size_t n = (size_t)L->nx * L->ny * nz;
+    orc_apply_A_gen(L->nx, L->ny, nz, a, d, beta, L->area, L->ax, L->ay, z, L->t);
+    for (size_t l = 0; l < n; ++l)
+        L->t[l] = f[l] - L->t[l];
+    if (orc_precond_gen(L->nx, L->ny, nz, a, d, beta, L->area, L->ax, L->ay, L->t, L->y) != ORC_OK)
+        return ORC_ERR_BREAKDOWN;
+    for (size_t l = 0; l < n; ++l)
+        z[l] += omega * L->y[l];
+    return ORC_OK;
+}
+
+/* z = B_l f: one V(nu, nu) cycle from level l down (readings above). */
+static int mg_vcycle(const mg_level *lv, int nlev, int l, int nz, const double *a, const double *d,
+                     const double *beta, int nu, double omega, int coarse_sweeps,
+                     const double *f, double *z)
+{
+    const mg_level *L = &lv[l];
+    int nx = L->nx, ny = L->ny;
+    size_t n = (size_t)nx * ny * nz;
+    memset(z, 0, sizeof(double) * n);
+    if (l == nlev - 1) {
+        if (nx * ny == 1)
+            return orc_precond_gen(nx, ny, nz, a, d, beta, L->area, L->ax, L->ay, f, z);
+        for (int s = 0; s < coarse_sweeps; ++s)
+            if (mg_smooth(L, nz, a, d, beta, omega, f, z) != ORC_OK)
+                return ORC_ERR_BREAKDOWN;
+        return ORC_OK;
+    }
+    for (int s = 0; s < nu; ++s)
+        if (mg_smooth(L, nz, a, d, beta, omega, f, z) != ORC_OK)
+            return ORC_ERR_BREAKDOWN;
+    /* coarse right-hand side P^T (f - A z) */
+    const mg_level *C = &lv[l + 1];
+    int fx = nx / C->nx, fy = ny / C->ny;
+    orc_apply_A_gen(nx, ny, nz, a, d, beta, L->area, L->ax, L->ay, z, L->t);
+    for (size_t q = 0; q < n; ++q)
+        L->t[q] = f[q] - L->t[q];
+    memset(C->f, 0, sizeof(double) * (size_t)C->nx * C->ny * nz);
+    for (int j = 0; j < ny; ++j)
+        for (int k = 0; k < nz; ++k)
+            for (int i = 0; i < nx; ++i)
+                C->f[at(C->nx, nz, i / fx, j / fy, k)] += L->t[at(nx, nz, i, j, k)];
+    if (mg_vcycle(lv, nlev, l + 1, nz, a, d, beta, nu, omega, coarse_sweeps, C->f, C->z) != ORC_OK)
+        return ORC_ERR_BREAKDOWN;
+    /* z += P z_c */
+    for (int j = 0; j < ny; ++j)
+        for (int k = 0; k < nz; ++k)
+            for (int i = 0; i < nx; ++i)
+                z[at(nx, nz, i, j, k)] += C->z[at(C->nx, nz, i / fx, j / fy, k)];
+    for (int s = 0; s < nu; ++s)
+        if (mg_smooth(L, nz, a, d, beta, omega, f, z) != ORC_OK)
+            return ORC_ERR_BREAKDOWN;
+    return ORC_OK;
+}
+
+/* z = B r, one V-cycle of the hierarchy of the general operator. */
+int orc_mg_vcycle(int nx, int ny, int nz, const double *a, const double *d, const double *beta,
+                  const double *area, const double *ax, const double *ay, int nu, double omega,
+                  int max_levels, int coarse_sweeps, const double *r, double *z)
+{
+    int nlev = 0;
+    mg_level *lv = mg_build(nx, ny, nz, area, ax, ay, max_levels, &nlev);
+    if (!lv)
+        return ORC_ERR_INVALID;
+    int st = mg_vcycle(lv, nlev, 0, nz, a, d, beta, nu, omega, coarse_sweeps, r, z);
+    mg_free(lv, nlev);
+    return st;
+}
+
+/* Textbook PCG (as orc_pcg_gen) with one V-cycle as the preconditioner. */
+int orc_pcg_mg(int nx, int ny, int nz, const double *a, const double *d, const double *beta,
+               const double *area, const double *ax, const double *ay, int nu, double omega,
+               int max_levels, int coarse_sweeps, const double *b, double *x, double tol, int maxit,
+               double *hist, int *iters_out)
+{
+    size_t n = (size_t)nx * ny * nz;
+    int nlev = 0;
+    mg_level *lv = mg_build(nx, ny, nz, area, ax, ay, max_levels, &nlev);
+    double *r = (double *)malloc(sizeof(double) * n);
+    double *z = (double *)malloc(sizeof(double) * n);
+    double *p = (double *)malloc(sizeof(double) * n);
+    double *q = (double *)malloc(sizeof(double) * n);
+    int status = ORC_NOT_CONVERGED, it = 0;
+    double t0 = now_seconds();
+    if (!lv || !r || !z || !p || !q) {
+        status = ORC_ERR_INVALID;
+        goto done;
+    }
+    orc_apply_A_gen(nx, ny, nz, a, d, beta, area, ax, ay, x, q);
+    for (size_t l = 0; l < n; ++l)
+        r[l] = b[l] - q[l];
+    double R0 = sqrt(orc_dot(n, r, r));
+    hist[0] = R0;
+    if (!isfinite(R0)) { status = ORC_ERR_BREAKDOWN; goto done; }
+    if (R0 == 0.0) { status = ORC_OK; goto done; }
+    if (mg_vcycle(lv, nlev, 0, nz, a, d, beta, nu, omega, coarse_sweeps, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+    memcpy(p, z, sizeof(double) * n);
+    double rho = orc_dot(n, r, z);
+    if (!(rho > 0.0) || !isfinite(rho)) { status = ORC_ERR_BREAKDOWN; goto done; }
+    for (int k = 1; k <= maxit; ++k) {
+        orc_apply_A_gen(nx, ny, nz, a, d, beta, area, ax, ay, p, q);
+        double sigma = orc_dot(n, p, q);
+        if (!(sigma > 0.0) || !isfinite(sigma)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double alpha = rho / sigma;
+        for (size_t l = 0; l < n; ++l) x[l] += alpha * p[l];
+        for (size_t l = 0; l < n; ++l) r[l] -= alpha * q[l];
+        double R = sqrt(orc_dot(n, r, r));
+        hist[k] = R;
+        it = k;
+        if (!isfinite(R)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        if (R == 0.0 || R / R0 < tol) { status = ORC_OK; goto done; }
+        if (k == maxit) break;
+        if (mg_vcycle(lv, nlev, 0, nz, a, d, beta, nu, omega, coarse_sweeps, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double rho_new = orc_dot(n, r, z);
+        if (!(rho_new > 0.0) || !isfinite(rho_new)) { status = ORC_ERR_BREAKDOWN; goto done; }
+        double beta_cg = rho_new / rho;
+        rho = rho_new;
+        for (size_t l = 0; l < n; ++l) p[l] = z[l] + beta_cg * p[l];
+    }
+    status = ORC_NOT_CONVERGED;
+done:
+    g_loop_seconds = now_seconds() - t0;
+    if (iters_out) *iters_out = it;
+    mg_free(lv, nlev);
+    free(r); free(z); free(p); free(q);
+    return status;
+}

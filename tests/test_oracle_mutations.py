@@ -48,6 +48,21 @@ MUTATIONS = {
     "gen_precond_no_area": ("double sub = -T * beta[k];", "double sub = -beta[k];"),
     "gen_alphaT_missing_edge": ("return ax[(size_t)j * nx + i] + ax[(size_t)j * nx + im]",
                                 "return ax[(size_t)j * nx + i] + 0.0 * ax[(size_t)j * nx + im]"),
+    "mg_coarse_edge_index": ("sx += ax[(size_t)(fy * J + b) * nx + (fx * I + fx - 1)];",
+                             "sx += ax[(size_t)(fy * J + b) * nx + (fx * I)];"),
+    "mg_self_edge_kept": ("cax[(size_t)J * ncx + I] = (ncx == 1) ? 0.0 : sx;", "cax[(size_t)J * ncx + I] = sx;"),
+    "mg_area_not_summed": ("sa += area[(size_t)(fy * J + b) * nx + (fx * I + a)];",
+                           "sa = area[(size_t)(fy * J + b) * nx + (fx * I + a)];"),
+    "mg_restrict_average": ("C->f[at(C->nx, nz, i / fx, j / fy, k)] += L->t[at(nx, nz, i, j, k)];",
+                            "C->f[at(C->nx, nz, i / fx, j / fy, k)] += 0.25 * L->t[at(nx, nz, i, j, k)];"),
+    "mg_prolong_wrong_parent": ("+= C->z[at(C->nx, nz, i / fx, j / fy, k)];",
+                                "+= C->z[at(C->nx, nz, (i / fx + 1) % C->nx, j / fy, k)];"),
+    "mg_no_damping": ("z[l] += omega * L->y[l];", "z[l] += L->y[l];"),
+    "mg_no_post_smooth": ("""        z[at(nx, nz, i, j, k)] += C->z[at(C->nx, nz, i / fx, j / fy, k)];
+    for (int s = 0; s < nu; ++s)""", """        z[at(nx, nz, i, j, k)] += C->z[at(C->nx, nz, i / fx, j / fy, k)];
+    for (int s = 0; s < 0; ++s)"""),
+    "mg_coarsest_not_exact": ("        if (nx * ny == 1)\n            return orc_precond_gen(",
+                              "        if (nx * ny == 0)\n            return orc_precond_gen("),
 }
 
 
