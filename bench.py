@@ -70,7 +70,33 @@ def _bytes_mixed(kernel, k):
 
 
 BYTES_BY_VARIANT = {"interleaved": (_bytes_interleaved, 84), "interleaved_no_q": (_bytes_no_q, 72),
-                    "f32": (_bytes_f32, 42), "mixed": (_bytes_mixed, 76)}
+                    "f32": (_bytes_f32, 42), "mixed": (_bytes_mixed, 76), "mg": (_bytes_interleaved, None)}
+
+
+# mg: the interleaved loop with one multigrid V-cycle as the preconditioner
+# pass; the stencil pass is the interleaved one.  Algorithmic bytes of one
+# V(1,1) cycle, per level of n_l points whose coarser level has n_c points
+# (0 on the coarsest), each vector read or written once per pass:
+#   first sweep   read f (and q: r -= alpha q on level 0, k >= 1), write z
+#                 (and r): 16, level 0 at k >= 1: 32
+#   restriction   read f, z, write t: 24 per point; write f_c: 8 per coarse point
+#   prolongation  read and write t: 16; read z_c: 8 per coarse point
+#   correction    read w, z (and f for the dot products on level 0), write z:
+#                 24, level 0: 32; read z_c: 8 per coarse point
+# and on a coarsest level of one column the exact column solve: 16.
+def mg_cycle_bytes(level_points, k, nu=1):
+    if nu != 1:
+        raise ValueError("the byte model covers V(1,1) cycles")
+    tot = 0
+    for l, nl in enumerate(level_points):
+        nc = level_points[l + 1] if l + 1 < len(level_points) else 0
+        if nc == 0:
+            tot += 16 * nl
+            continue
+        first = 32 if (l == 0 and k > 0) else 16
+        corr = 32 if l == 0 else 24
+        tot += (first + 24 + 16 + corr) * nl + 24 * nc
+    return tot
 
 
 def step_class(variant, kernel, k):
@@ -81,6 +107,16 @@ def step_class(variant, kernel, k):
     if variant in ("interleaved", "f32", "mixed") and kernel == "fused_spmv":
         return "odd" if k % 2 else "even"
     return "rest"
+
+
+def mg_pass_bytes(level_points, iters):
+    """Total algorithmic bytes and count of the timed V-cycles (k = 0..K)."""
+    tot = cnt = 0
+    for K in iters:
+        for k in range(K + 1):
+            tot += mg_cycle_bytes(level_points, k)
+            cnt += 1
+    return tot, cnt
 
 
 def timed_steps(kernel, iters):
@@ -147,9 +183,10 @@ def parse():
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5, 6],
                     help="5 = explicit-vs-matrix-free comparison at 2048x2048x128 (50 fixed steps)")
     ap.add_argument("--variant", default="interleaved",
-                    choices=["interleaved", "interleaved_no_q", "standard", "f32", "mixed"],
+                    choices=["interleaved", "interleaved_no_q", "standard", "f32", "mixed", "mg"],
                     help="f32: every vector in binary32, to tol 1e-5 (the workload's 1e-10 is below "
-                         "binary32 rounding); mixed: binary64 with the preconditioner in binary32")
+                         "binary32 rounding); mixed: binary64 with the preconditioner in binary32; "
+                         "mg: one multigrid V(1,1) cycle (omega 0.8) as the preconditioner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -178,14 +215,20 @@ def copy_calibration():
                       "copy_ms": dt * 1e3, "copy_GBps": 2 * n * 8 / dt / 1e9}), flush=True)
 
 
-def cpu_baseline(w, steps):
+def cpu_baseline(w, steps, variant="interleaved"):
     """The CPU oracle (single thread) on a bounded sample of the same workload:
     `steps` CG steps of the full problem, timed around the oracle's step loop
     (its set-up pass r0 = b - A x0, z0 = M^-1 r0 is not counted)."""
     import oracle
     from matrix_free_pcg_amd.workloads import GeneralProblem
     t0 = time.perf_counter()
-    if isinstance(w.problem, GeneralProblem):
+    if variant == "mg":
+        gp = w.problem if isinstance(w.problem, GeneralProblem) else _as_general(w.problem)
+        res = oracle.pcg_mg(gp, w.rhs, tol=0.0, maxit=steps)
+        total = time.perf_counter() - t0
+        per = total / (res["iters"] + 1)
+        how = "multigrid PCG, timed around the whole call, its set-up pass counted as one more step"
+    elif isinstance(w.problem, GeneralProblem):
         res = oracle.pcg_gen(w.problem, w.rhs, tol=0.0, maxit=steps)
         total = time.perf_counter() - t0
         per = total / (res["iters"] + 1)
@@ -199,6 +242,18 @@ def cpu_baseline(w, steps):
             "sample": f"{res['iters']} CG steps of the {w.name} workload (single-threaded C, "
                       f"-O2), {how}; {total:.1f} s of CPU time in all",
             "s_per_iteration": round(per, 3)}
+
+
+def _as_general(prob):
+    """The special operator in general form (|T| = 1, a = delta, d = 1, beta =
+    alpha_z, edges the mean of the two cells' alpha_h), for the oracle."""
+    import numpy as np
+    from matrix_free_pcg_amd.workloads import GeneralProblem
+    ah = prob.alpha_h_field()
+    ax = 0.5 * (ah + np.roll(ah, -1, axis=1))
+    ay = 0.5 * (ah + np.roll(ah, -1, axis=0))
+    return GeneralProblem(prob.nx, prob.ny, prob.nz, np.full(prob.nz, prob.delta), np.ones(prob.nz),
+                          np.asarray(prob.alpha_z_face, dtype=np.float64), np.ones((prob.ny, prob.nx)), ax, ay)
 
 
 CSR_BYTES_PER_ROW = 108   # 7 x (8 B value + 4 B column) + row pointer + x + y (8 B each)
@@ -295,10 +350,17 @@ def main():
     tol, maxit = (1e-5 if args.variant == "f32" else w.tol), w.maxit
     if args.fixed_iterations > 0:
         tol, maxit = 0.0, args.fixed_iterations
-    ws = torch.empty(mf.pcg_solve_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
+    level_points = None
+    if args.variant == "mg":
+        mf.pcg_mg_setup(h, nu=1, omega=0.8)
+        level_points = [mf.pcg_mg_level(h, l)[0] * mf.pcg_mg_level(h, l)[1] * prob.nz
+                        for l in range(mf.pcg_mg_num_levels(h))]
+        ws = torch.empty(mf.pcg_mg_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(mf.pcg_solve_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
     solve = {"interleaved": mf.pcg_solve, "interleaved_no_q": mf.pcg_solve_no_q,
              "standard": mf.pcg_solve_standard, "f32": mf.pcg_solve_f32,
-             "mixed": mf.pcg_solve_mixed}[args.variant]
+             "mixed": mf.pcg_solve_mixed, "mg": mf.pcg_solve_mg}[args.variant]
     has_bytes = args.variant in BYTES_BY_VARIANT
     torch.cuda.synchronize()
 
@@ -324,13 +386,21 @@ def main():
 
     kern = {}
     names = {"fused_prec": mf.PCG_KID_FUSED_PREC, "fused_spmv": mf.PCG_KID_FUSED_SPMV,
-             "apply_A": mf.PCG_KID_APPLY_A, "precond": mf.PCG_KID_PRECOND, "vector": mf.PCG_KID_VECTOR}
+             "apply_A": mf.PCG_KID_APPLY_A, "precond": mf.PCG_KID_PRECOND, "vector": mf.PCG_KID_VECTOR,
+             "mg_vcycle": mf.PCG_KID_MG_VCYCLE}
     for name, kid in names.items():
         ms, cnt = mf.pcg_profile_read(h, kid)
         if cnt:
             avg = ms / cnt
             ent = {"launches": cnt, "avg_ms": avg, "total_ms": ms}
-            if has_bytes and name in ("fused_prec", "fused_spmv"):
+            if name == "mg_vcycle":
+                tot, nl = mg_pass_bytes(level_points, iters)
+                if nl != cnt:
+                    raise SystemExit(f"{name}: {cnt} timed cycles, expected {nl}")
+                ent["bytes_per_launch"] = tot / nl
+                ent["GBps"] = tot / (ms * 1e-3) / 1e9
+                ent["note"] = f"one V(1,1) cycle over {len(level_points)} levels: every kernel of the cycle"
+            elif has_bytes and name in ("fused_prec", "fused_spmv"):
                 tot, nl = pass_bytes(args.variant, name, iters, n)
                 if nl != cnt:
                     raise SystemExit(f"{name}: {cnt} timed launches, expected {nl}")
@@ -348,8 +418,11 @@ def main():
 
     it_s = total_iters / elapsed
     # every timed pass's algorithmic bytes over the whole timed region
-    all_bytes = (sum(pass_bytes(args.variant, kname, iters, n)[0] for kname in ("fused_prec", "fused_spmv"))
-                 if has_bytes else None)
+    if args.variant == "mg":
+        all_bytes = pass_bytes(args.variant, "fused_spmv", iters, n)[0] + mg_pass_bytes(level_points, iters)[0]
+    else:
+        all_bytes = (sum(pass_bytes(args.variant, kname, iters, n)[0] for kname in ("fused_prec", "fused_spmv"))
+                     if has_bytes else None)
     dom = max((k for k in kern if "GBps" in kern[k]), key=lambda k: kern[k]["total_ms"], default=None)
     roofline = None
     if dom is not None:
@@ -373,6 +446,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"f32": "f32", "mixed": "f64 (preconditioner f32)"}.get(args.variant, "f64"),
+        "s_per_solve": round(elapsed / args.steps, 4),
         "data": "synthetic",
         "config": {"workload": w.name, "nx": prob.nx, "ny": prob.ny, "nz": prob.nz,
                    "tol": tol, "maxit": maxit, "variant": args.variant,
@@ -381,14 +455,16 @@ def main():
         # algorithmic bytes of both passes over the whole timed region / its wall time
         "hbm_GBps_whole_solve": round(all_bytes / elapsed / 1e9, 1) if all_bytes else None,
         "hbm_frac_whole_solve": round(all_bytes / elapsed / 1e9 / HBM_PEAK_GBS, 4) if all_bytes else None,
-        "bytes_per_point_per_iteration": BYTES_BY_VARIANT[args.variant][1] if has_bytes else None,
+        "bytes_per_point_per_iteration": (BYTES_BY_VARIANT[args.variant][1] if args.variant != "mg"
+                                          else round(52 + mg_cycle_bytes(level_points, 1) / n, 2))
+                                         if has_bytes else None,
         "kernels": kern,
         "roofline": roofline,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         t = time.perf_counter()
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_steps)
+        out["cpu_baseline"] = cpu_baseline(w, 1 if args.variant == "mg" else args.cpu_steps, args.variant)
         log(f"[bench] cpu baseline in {time.perf_counter() - t:.1f}s")
     print(json.dumps(out), flush=True)
 

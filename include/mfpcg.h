@@ -185,6 +185,67 @@ int pcg_solve_no_q(pcg_handle *h, const double *b_dev, double *x_dev, double tol
                    void *workspace_dev, size_t workspace_bytes, int32_t *iters_out,
                    double *hist_host, int32_t *hist_len_out, double *final_rel_res);
 
+/* ---- Tensor-product multigrid preconditioner ---------------------------
+ * Section 2 names geometric multigrid with the vertical line relaxation as
+ * the faster CPU solver and section 8 plans it for the GPU; the pages give
+ * no intergrid operators, so this one is read as follows.  Levels keep nz
+ * and halve nx where it is even and > 1 and ny where it is even and > 1
+ * (horizontal semi-coarsening), down to one column, to a level that cannot
+ * be halved, or to max_levels levels.  Prolongation P is piecewise constant
+ * (a fine column takes its coarse parent's values), restriction is P^T (the
+ * sum over the children), and the coarse operator is P^T A P, which has the
+ * general form of section 3 again: |T| summed over the children, the edge
+ * between two coarse columns the sum of the fine edges crossing it (zero in
+ * a dimension of size 1), a, d and beta unchanged.  The smoother is the
+ * column solve of eq. (19) as damped block Jacobi, z <- z + omega M^{-1}
+ * (f - A z); the cycle is V(nu, nu) from z = 0; the coarsest level is solved
+ * exactly by the column solve when it is one column, else by coarse_sweeps
+ * sweeps from z = 0.  B (one cycle) is symmetric positive definite for
+ * 0 < omega <= 1, so CG with B is PCG. */
+typedef struct {
+    int32_t nu;            /* sweeps before and after the coarse correction, 1..16 */
+    double omega;          /* damping of the smoother, 0 < omega <= 1 */
+    int32_t max_levels;    /* 0: as many levels as the grid allows; else 1..64 */
+    int32_t coarse_sweeps; /* sweeps on a coarsest level of several columns, 1..64 */
+} pcg_mg_params;
+
+/* Build (or rebuild) the level hierarchy: the coarse levels' coefficient
+ * tables are computed on the device from the handle's and owned by the
+ * handle until pcg_destroy or the next pcg_mg_setup.  Blocks until done.
+ * Returns PCG_ERR_INVALID for bad parameters, PCG_ERR_UNSUPPORTED when the
+ * column tiles are not 64 columns wide, PCG_ERR_HIP on allocation failure. */
+int pcg_mg_setup(pcg_handle *h, const pcg_mg_params *params);
+
+/* Number of levels of the hierarchy built by pcg_mg_setup (1 = none coarser
+ * than the grid).  PCG_ERR_INVALID before pcg_mg_setup. */
+int pcg_mg_num_levels(const pcg_handle *h, int32_t *levels);
+
+/* Size and coefficients of level `level` (0 = the grid): nx, ny (may be
+ * NULL) and, when not NULL, the HOST arrays area, alpha_x, alpha_y of
+ * nx*ny entries each (layout as in pcg_coeffs_general).  Blocks. */
+int pcg_mg_level(pcg_handle *h, int32_t level, int32_t *nx, int32_t *ny, double *area_host,
+                 double *alpha_x_host, double *alpha_y_host);
+
+/* Bytes of device workspace of pcg_solve_mg with this maxit (those of
+ * pcg_solve, one more N-vector, and three vectors per coarse level: about
+ * seven N-vectors for a full hierarchy).  0 before pcg_mg_setup. */
+size_t pcg_mg_workspace_bytes(const pcg_handle *h, int32_t maxit);
+
+/* z = B r, one V-cycle.  r_dev, z_dev: N doubles each, must not overlap each
+ * other or the workspace (>= pcg_mg_workspace_bytes(h, 0) bytes, 256-byte
+ * aligned).  Asynchronous. */
+int pcg_mg_vcycle(pcg_handle *h, const double *r_dev, double *z_dev, void *workspace_dev,
+                  size_t workspace_bytes);
+
+/* pcg_solve with one V-cycle as the preconditioner: the interleaved loop of
+ * section 4.3 with its preconditioner pass replaced by the cycle, whose first
+ * sweep applies r -= alpha q and whose last sweep forms <r,r> and <r,z>.
+ * Same arguments, results and errors as pcg_solve; the workspace is
+ * pcg_mg_workspace_bytes(h, maxit).  PCG_ERR_INVALID before pcg_mg_setup. */
+int pcg_solve_mg(pcg_handle *h, const double *b_dev, double *x_dev, double tol, int32_t maxit,
+                 void *workspace_dev, size_t workspace_bytes, int32_t *iters_out,
+                 double *hist_host, int32_t *hist_len_out, double *final_rel_res);
+
 /* ---- Single precision (section 7 runs the solver in single and in double
  * precision) -------------------------------------------------------------
  * The same operator and preconditioner with the coefficients (kept in
@@ -281,7 +342,8 @@ int pcg_solve_csr(pcg_handle *h, const int64_t *row_ptr_dev, const int32_t *col_
 #define PCG_KID_PRECOND 3      /* stand-alone z = M^{-1} r (and standard)    */
 #define PCG_KID_VECTOR 4       /* standard-PCG vector updates               */
 #define PCG_KID_CSR_SPMV 5     /* stand-alone CSR y = A x                    */
-#define PCG_KID_COUNT 6
+#define PCG_KID_MG_VCYCLE 6    /* one multigrid V-cycle (all its kernels)    */
+#define PCG_KID_COUNT 7
 int pcg_profile_enable(pcg_handle *h, int32_t enable);
 int pcg_profile_reset(pcg_handle *h);
 int pcg_profile_read(const pcg_handle *h, int32_t kernel_id, double *ms_total,

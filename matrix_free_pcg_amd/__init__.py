@@ -14,7 +14,9 @@ from ._abi import (PCG_ERR_BREAKDOWN, PCG_ERR_HIP, PCG_ERR_INVALID, PCG_ERR_UNSU
                    pcg_solve_standard, pcg_solve_no_q, pcg_solve_workspace_bytes, pcg_version,
                    PCG_KID_CSR_SPMV, Csr, pcg_csr_nnz, pcg_csr_assemble, pcg_csr_spmv,
                    pcg_tridiag_assemble, pcg_tridiag_factor, pcg_tridiag_precond, pcg_solve_csr,
-                   pcg_apply_A_f32, pcg_precond_f32, pcg_solve_f32, pcg_solve_mixed)
+                   pcg_apply_A_f32, pcg_precond_f32, pcg_solve_f32, pcg_solve_mixed,
+                   PCG_KID_MG_VCYCLE, pcg_mg_setup, pcg_mg_num_levels, pcg_mg_level,
+                   pcg_mg_workspace_bytes, pcg_mg_vcycle, pcg_solve_mg)
 
 __all__ = [
     "workloads", "Handle", "PcgError", "pcg_create", "pcg_destroy", "pcg_set_stream",
@@ -23,5 +25,6 @@ __all__ = [
     "pcg_profile_read", "pcg_last_error", "pcg_version", "Csr", "pcg_csr_nnz",
     "pcg_csr_assemble", "pcg_csr_spmv", "pcg_tridiag_assemble", "pcg_tridiag_factor",
     "pcg_tridiag_precond", "pcg_solve_csr", "pcg_apply_A_f32", "pcg_precond_f32", "pcg_solve_f32",
-    "pcg_solve_mixed",
+    "pcg_solve_mixed", "pcg_mg_setup", "pcg_mg_num_levels", "pcg_mg_level", "pcg_mg_workspace_bytes",
+    "pcg_mg_vcycle", "pcg_solve_mg",
 ]

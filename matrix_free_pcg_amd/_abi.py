@@ -32,7 +32,8 @@ PCG_KID_APPLY_A = 2
 PCG_KID_PRECOND = 3
 PCG_KID_VECTOR = 4
 PCG_KID_CSR_SPMV = 5
-PCG_KID_COUNT = 6
+PCG_KID_MG_VCYCLE = 6
+PCG_KID_COUNT = 7
 
 EXPORTED = [
     "pcg_create", "pcg_destroy", "pcg_set_stream", "pcg_apply_A", "pcg_precond",
@@ -42,6 +43,8 @@ EXPORTED = [
     "pcg_csr_nnz", "pcg_csr_assemble", "pcg_csr_spmv", "pcg_tridiag_assemble",
     "pcg_tridiag_factor", "pcg_tridiag_precond", "pcg_solve_csr",
     "pcg_apply_A_f32", "pcg_precond_f32", "pcg_solve_f32", "pcg_solve_mixed", "pcg_create_general",
+    "pcg_mg_setup", "pcg_mg_num_levels", "pcg_mg_level", "pcg_mg_workspace_bytes", "pcg_mg_vcycle",
+    "pcg_solve_mg",
 ]
 
 
@@ -58,6 +61,11 @@ class pcg_grid(ctypes.Structure):
 class pcg_coeffs_general(ctypes.Structure):
     _fields_ = [(name, ctypes.POINTER(ctypes.c_double))
                 for name in ("a", "d", "beta_face", "area", "alpha_x", "alpha_y")]
+
+
+class pcg_mg_params(ctypes.Structure):
+    _fields_ = [("nu", ctypes.c_int32), ("omega", ctypes.c_double), ("max_levels", ctypes.c_int32),
+                ("coarse_sweeps", ctypes.c_int32)]
 
 
 class pcg_coeffs(ctypes.Structure):
@@ -113,8 +121,18 @@ def load():
         lib.pcg_apply_A_f32.restype = ctypes.c_int
         lib.pcg_precond_f32.argtypes = [H, vp, vp]
         lib.pcg_precond_f32.restype = ctypes.c_int
+        lib.pcg_mg_setup.argtypes = [H, ctypes.POINTER(pcg_mg_params)]
+        lib.pcg_mg_setup.restype = ctypes.c_int
+        lib.pcg_mg_num_levels.argtypes = [H, i32p]
+        lib.pcg_mg_num_levels.restype = ctypes.c_int
+        lib.pcg_mg_level.argtypes = [H, ctypes.c_int32, i32p, i32p, dp, dp, dp]
+        lib.pcg_mg_level.restype = ctypes.c_int
+        lib.pcg_mg_workspace_bytes.argtypes = [H, ctypes.c_int32]
+        lib.pcg_mg_workspace_bytes.restype = ctypes.c_size_t
+        lib.pcg_mg_vcycle.argtypes = [H, vp, vp, vp, ctypes.c_size_t]
+        lib.pcg_mg_vcycle.restype = ctypes.c_int
         for name in ("pcg_solve", "pcg_solve_standard", "pcg_solve_no_q", "pcg_solve_f32",
-                     "pcg_solve_mixed"):
+                     "pcg_solve_mixed", "pcg_solve_mg"):
             f = getattr(lib, name)
             f.argtypes = [H, vp, vp, ctypes.c_double, ctypes.c_int32, vp, ctypes.c_size_t,
                           i32p, dp, i32p, dp]
@@ -280,9 +298,11 @@ def pcg_solve_workspace_bytes(h: Handle, maxit: int) -> int:
     return int(load().pcg_solve_workspace_bytes(h.ptr, int(maxit)))
 
 
-def _solve(fn, h: Handle, b, x, tol: float, maxit: int, workspace=None, dtype_name="float64") -> dict:
+def _solve(fn, h: Handle, b, x, tol: float, maxit: int, workspace=None, dtype_name="float64",
+           need=None) -> dict:
     import torch
-    need = pcg_solve_workspace_bytes(h, maxit)
+    if need is None:
+        need = pcg_solve_workspace_bytes(h, maxit)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
@@ -337,6 +357,55 @@ def pcg_solve_f32(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> di
 def pcg_solve_mixed(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
     """Interleaved binary64 PCG with the column preconditioner in binary32."""
     return _solve(load().pcg_solve_mixed, h, b, x, tol, maxit, workspace)
+
+
+# ---- tensor-product multigrid preconditioner ----------------------------------
+
+def pcg_mg_setup(h: Handle, nu: int = 1, omega: float = 0.8, max_levels: int = 0,
+                 coarse_sweeps: int = 2) -> None:
+    """Build the level hierarchy (device tables owned by the handle)."""
+    p = pcg_mg_params(int(nu), float(omega), int(max_levels), int(coarse_sweeps))
+    _check(h.ptr, load().pcg_mg_setup(h.ptr, ctypes.byref(p)))
+
+
+def pcg_mg_num_levels(h: Handle) -> int:
+    n = ctypes.c_int32(0)
+    _check(h.ptr, load().pcg_mg_num_levels(h.ptr, ctypes.byref(n)))
+    return n.value
+
+
+def pcg_mg_level(h: Handle, level: int):
+    """(nx, ny, area, alpha_x, alpha_y) of a level, the arrays of shape (ny, nx)."""
+    lib = load()
+    nx, ny = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(h.ptr, lib.pcg_mg_level(h.ptr, int(level), ctypes.byref(nx), ctypes.byref(ny), None, None, None))
+    arrs = [np.zeros((ny.value, nx.value)) for _ in range(3)]
+    dp = ctypes.POINTER(ctypes.c_double)
+    _check(h.ptr, lib.pcg_mg_level(h.ptr, int(level), None, None, *[a.ctypes.data_as(dp) for a in arrs]))
+    return nx.value, ny.value, arrs[0], arrs[1], arrs[2]
+
+
+def pcg_mg_workspace_bytes(h: Handle, maxit: int) -> int:
+    return int(load().pcg_mg_workspace_bytes(h.ptr, int(maxit)))
+
+
+def pcg_mg_vcycle(h: Handle, r, z, workspace=None) -> None:
+    """z = B r, one V-cycle (asynchronous on the handle's stream)."""
+    import torch
+    need = pcg_mg_workspace_bytes(h, 0)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=z.device)
+    if not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a CUDA tensor of >= {need} bytes")
+    rc = load().pcg_mg_vcycle(h.ptr, _dev_ptr(r, h.n, "r"), _dev_ptr(z, h.n, "z"), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size())
+    _check(h.ptr, rc)
+
+
+def pcg_solve_mg(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
+    """Interleaved PCG with one multigrid V-cycle as the preconditioner."""
+    return _solve(load().pcg_solve_mg, h, b, x, tol, maxit, workspace,
+                  need=pcg_mg_workspace_bytes(h, maxit))
 
 
 def pcg_profile_enable(h: Handle, enable: bool = True) -> None:

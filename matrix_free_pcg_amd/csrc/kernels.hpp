@@ -270,16 +270,44 @@ __device__ __forceinline__ void block_sum(double (&v)[NV], double (*sh)[NV], dou
 //             neighbours, so that q never has to be stored.
 enum : int { UPD_NONE = 0, UPD_Q = 1, UPD_AP = 2 };
 
-template <int L, int C, int UPD, bool DOTS, bool STORED, typename TV = double, typename TZ = double>
+// Multigrid forms of the column solve (tensor-product multigrid: horizontal
+// semi-coarsening, the column solve as damped block-Jacobi smoother), with
+// y = M^{-1} rr and rr from the UPD mode:
+//   MG_FIRST  z = omega y            (first sweep from z = 0)
+//   MG_CORR   z = zb + omega y, zb = q + (zc at the coarse parent, if zc):
+//             rr is a residual computed by a sweep pass; the sweep after the
+//             coarse correction adds the prolongated correction here.
+// Binary64 only.  The dot products of these forms are <f, f> and <f, z>
+// (f: the level's right-hand side) and are skipped when partials is null.
+enum : int { MG_NONE = 0, MG_FIRST = 1, MG_CORR = 2 };
+
+struct MgArgs {
+    const double *zc;   // coarse correction (coarse layout), or null
+    const double *f;    // the level's right-hand side (dot products of MG_CORR)
+    double omega;       // damping of the smoother
+    int ncx, fx, fy;    // coarse row length, coarsening factors in i and j
+};
+
+// Index of the coarse parent of fine cell (i, j, k): (i / fx, j / fy, k).
+__device__ __forceinline__ size_t mg_parent(const MgArgs &m, int nz, int i, int j, int k)
+{
+    return (size_t)(i / m.fx) + (size_t)m.ncx * ((size_t)k + (size_t)nz * (size_t)(j / m.fy));
+}
+
+template <int L, int C, int UPD, bool DOTS, bool STORED, typename TV = double, typename TZ = double,
+          int MG = MG_NONE>
 __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     const TV *__restrict__ rin, const TV *__restrict__ q, TV *__restrict__ rout,
     TZ *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
     double *__restrict__ partials, const double *__restrict__ tri,
-    const TZ *__restrict__ phib_tab)
+    const TZ *__restrict__ phib_tab, MgArgs mg)
 {
     static_assert((UPD != UPD_AP && !STORED) ||
                       (std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
                   "the stored-matrix and recomputed-Ap forms are binary64 only");
+    static_assert(MG == MG_NONE || (UPD != UPD_AP && !STORED && std::is_same<TV, double>::value &&
+                                    std::is_same<TZ, double>::value),
+                  "the multigrid forms are binary64 only");
     __shared__ TZ sh_a[kMaxThreads];
     __shared__ TZ sh_b[kMaxThreads];
     __shared__ double sh_red[kMaxThreads / kWave][2];
@@ -421,6 +449,25 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
             if (t < len)
                 st_s(rout + base + (size_t)(k0 + t) * ks, rr[t]);
     }
+    // MG_CORR: the iterate zb (plus the coarse correction) and f at the levels
+    double zb[MG == MG_CORR ? L : 1], fv[MG == MG_CORR ? L : 1];
+    if constexpr (MG == MG_CORR) {
+        r2 = 0.0;
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            zb[t] = 0.0;
+            fv[t] = 0.0;
+            if (t < len && ok) {
+                const size_t l = base + (size_t)(k0 + t) * ks;
+                zb[t] = ld_s(q + l);
+                if (mg.zc)
+                    zb[t] = zb[t] + mg.zc[mg_parent(mg, o.nz, ic, j, k0 + t)];
+                if (partials)
+                    fv[t] = ld_s(mg.f + l);
+            }
+            r2 += fv[t] * fv[t];
+        }
+    }
 
     // Local forward sweep: pivots from the true incoming phi, z'' with zero
     // inflow; the right-hand side rounded to TZ.
@@ -494,13 +541,20 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         if (t < len) {
             const TZ up = up_at(t);
             H = (up * iD[t]) * H;
-            const TZ zv = zp[t] + ztop * H;
-            kap += (double)rr[t] * (double)zv;
+            TZ zv = zp[t] + ztop * H;
+            if constexpr (MG == MG_FIRST)
+                zv = (TZ)mg.omega * zv;
+            if constexpr (MG == MG_CORR) {
+                zv = zb[t] + mg.omega * zv;
+                kap += fv[t] * zv;
+            } else {
+                kap += (double)rr[t] * (double)zv;
+            }
             if (ok)
                 st_s(z + base + (size_t)(k0 + t) * ks, zv);
         }
     }
-    if (DOTS) {
+    if (DOTS && (MG == MG_NONE || partials != nullptr)) {
         double v[2] = {r2, kap};
         double out[2];
         block_sum<2>(v, sh_red, out);
@@ -532,14 +586,17 @@ __device__ __forceinline__ void st_at(T *base, unsigned boff, T v)
 // The segment inflow / outflow scans read the other segments' affine maps as
 // (offset, slope) pairs from LDS without branches, so the reads are not
 // serialised behind the recurrence.
-template <int L, int UPD, bool DOTS, typename TV = double, typename TZ = double>
+template <int L, int UPD, bool DOTS, typename TV = double, typename TZ = double, int MG = MG_NONE>
 __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     const TV *__restrict__ rin, const TV *__restrict__ q, TV *__restrict__ rout,
     TZ *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
-    double *__restrict__ partials, const TZ *__restrict__ phib)
+    double *__restrict__ partials, const TZ *__restrict__ phib, MgArgs mg)
 {
     static_assert(UPD != UPD_AP || (std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
                   "the recomputed-Ap form is binary64 only");
+    static_assert(MG == MG_NONE || (UPD != UPD_AP && std::is_same<TV, double>::value &&
+                                    std::is_same<TZ, double>::value),
+                  "the multigrid forms are binary64 only");
     constexpr int kSeg = kMaxThreads / kWave;
     __shared__ Pair<TZ> sh_ab[kMaxThreads];
     __shared__ double sh_red[kSeg][2];
@@ -626,6 +683,25 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         for (int t = 0; t < L; ++t)
             st_at(rout + row0 + (size_t)t * nx, cv, rr[t]);
     }
+    // MG_CORR: the iterate zb (plus the coarse correction) and f at the levels
+    double zb[MG == MG_CORR ? L : 1], fv[MG == MG_CORR ? L : 1];
+    if constexpr (MG == MG_CORR) {
+        r2 = 0.0;
+        const size_t pb = mg.zc ? mg_parent(mg, o.nz, i, j, k0) : 0;
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            zb[t] = ld_at(q + row0 + (size_t)t * nx, cv);
+            fv[t] = partials ? ld_at(mg.f + row0 + (size_t)t * nx, cv) : 0.0;
+        }
+        if (mg.zc) {
+#pragma unroll
+            for (int t = 0; t < L; ++t)
+                zb[t] = zb[t] + mg.zc[pb + (size_t)t * mg.ncx];
+        }
+#pragma unroll
+        for (int t = 0; t < L; ++t)
+            r2 += fv[t] * fv[t];
+    }
 
     // Local forward sweep: pivots from the true incoming phi, z'' with zero
     // inflow; the right-hand side rounded to TZ.
@@ -684,11 +760,18 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
         H = (vz(t + 1) * iD[t]) * H;
-        const TZ zv = zp[t] + ztop * H;
-        kap += (double)rr[t] * (double)zv;
+        TZ zv = zp[t] + ztop * H;
+        if constexpr (MG == MG_FIRST)
+            zv = (TZ)mg.omega * zv;
+        if constexpr (MG == MG_CORR) {
+            zv = zb[t] + mg.omega * zv;
+            kap += fv[t] * zv;
+        } else {
+            kap += (double)rr[t] * (double)zv;
+        }
         st_at(z + row0 + (size_t)t * nx, cz, zv);
     }
-    if (DOTS) {
+    if (DOTS && (MG == MG_NONE || partials != nullptr)) {
         double v[2] = {r2, kap};
         double out[2];
         block_sum<2>(v, sh_red, out);
@@ -1073,6 +1156,187 @@ __global__ __launch_bounds__(kMaxThreads) void k_update_p(double *__restrict__ p
     for (int t = 0; t < sw.len; ++t) {
         const size_t l = base + (size_t)(sw.k0 + t) * o.nx;
         st_s(p + l, first ? ld_s(z + l) : ld_s(z + l) + beta * ld_s(p + l));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tensor-product multigrid: the passes between the column sweeps.  Levels
+// keep nz and halve nx and / or ny (factors fx, fy in {1, 2}); prolongation is
+// piecewise constant (a fine cell takes its coarse parent's value) and
+// restriction is its transpose (the sum over the children), so the coarse
+// operator P^T A P is again of the general form:
+
+// Coarse coefficients: |T| summed over the children, the coarse edge between
+// parents I and I+1 (J and J+1) the sum of the fine edges crossing it, zero
+// in a dimension of size 1 (a column coupled with itself cancels).  Summed in
+// the order (row b outer, column a inner).  One thread per coarse column.
+__global__ void k_mg_coarsen(Op o, int ncx, int ncy, int fx, int fy, double *__restrict__ carea,
+                             double *__restrict__ cax, double *__restrict__ cay)
+{
+    const size_t col = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (col >= (size_t)ncx * ncy)
+        return;
+    const int J = (int)(col / ncx);
+    const int I = (int)(col - (size_t)J * ncx);
+    const size_t nx = (size_t)o.nx;
+    double sa = 0.0, sx = 0.0, sy = 0.0;
+    for (int b = 0; b < fy; ++b)
+        for (int a = 0; a < fx; ++a)
+            sa += o.area[(size_t)(fy * J + b) * nx + (size_t)(fx * I + a)];
+    for (int b = 0; b < fy; ++b)
+        sx += o.ex[(size_t)(fy * J + b) * nx + (size_t)(fx * I + fx - 1)];
+    for (int a = 0; a < fx; ++a)
+        sy += o.ey[(size_t)(fy * J + fy - 1) * nx + (size_t)(fx * I + a)];
+    carea[col] = sa;
+    cax[col] = ncx == 1 ? 0.0 : sx;
+    cay[col] = ncy == 1 ? 0.0 : sy;
+}
+
+// Residual and restriction after the pre-smoothing sweeps: t = f - A z (kept
+// for the sweep after the coarse correction) and fc = P^T t.  A workgroup
+// owns 64 fine columns (one lane each) of the FY fine rows of one coarse row
+// J over Ws * Ls levels; tiles run k-tile fastest, then the i-tile, then J.
+// A lane computes the residual of its column in each of the FY rows; with
+// FX = 2 the two children in i are adjacent lanes.  The children are summed
+// in the order (row outer, column inner).
+template <int Ls, int FX, int FY>
+__global__ __launch_bounds__(kMaxThreads) void k_mg_restrict(const double *__restrict__ f,
+                                                             const double *__restrict__ zin,
+                                                             double *__restrict__ t_out,
+                                                             double *__restrict__ fc, Op o, int ncx,
+                                                             const SolveState *__restrict__ st)
+{
+    if (st != nullptr && st->done)
+        return;
+    const int tile = tile_of_block(blockIdx.x, gridDim.x);
+    const int kt = tile % o.nkt;
+    const int rem = tile / o.nkt;
+    const int it = rem % o.ntx;
+    const int J = rem / o.ntx;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = it * kWave + lane;
+    const bool ok = i < o.nx;
+    const int ic = ok ? i : o.nx - 1;
+    const int k0 = (kt * o.Ws + w) * Ls;
+    const int len = max(0, min(Ls, o.nz - k0));
+    if (len == 0)
+        return;   // wave-uniform
+    const size_t ks = (size_t)o.nx;
+    const int ip = (ic + 1 == o.nx) ? 0 : ic + 1;
+    const int im = (ic == 0) ? o.nx - 1 : ic - 1;
+    const bool needL = lane == 0;
+    const bool needR = lane == kWave - 1 || ic + 1 >= o.nx;
+    auto lev = [&](int k) { return (size_t)min(max(k, 0), o.nz - 1) * ks; };
+    double res[FY][Ls];
+#pragma unroll
+    for (int b = 0; b < FY; ++b) {
+        const int j = FY * J + b;
+        const int jp = (j + 1 == o.ny) ? 0 : j + 1;
+        const int jm = (j == 0) ? o.ny - 1 : j - 1;
+        const Faces fcs = column_faces(o, ic, j);
+        const size_t base = lin(o, ic, j, 0);
+        const size_t bxp = lin(o, ip, j, 0), bxm = lin(o, im, j, 0);
+        const size_t byp = lin(o, ic, jp, 0), bym = lin(o, ic, jm, 0);
+        double zv[Ls + 2], zyp[Ls], zym[Ls], zxl[Ls], zxr[Ls], fv[Ls];
+#pragma unroll
+        for (int t = 0; t < Ls + 2; ++t)
+            zv[t] = zin[base + lev(k0 - 1 + t)];
+#pragma unroll
+        for (int t = 0; t < Ls; ++t) {
+            const size_t off = lev(k0 + t);
+            zyp[t] = zin[byp + off];
+            zym[t] = zin[bym + off];
+            zxl[t] = needL ? zin[bxm + off] : 0.0;
+            zxr[t] = needR ? zin[bxp + off] : 0.0;
+            fv[t] = ld_s(f + base + off);
+        }
+#pragma unroll
+        for (int t = 0; t < Ls; ++t) {
+            const int k = min(k0 + t, o.nz - 1);
+            const double lo = fcs.area * o.az[k], up = fcs.area * o.az[k + 1];
+            const double zc = zv[t + 1];
+            const double zl_s = __shfl_up(zc, 1, kWave);
+            const double zr_s = __shfl_down(zc, 1, kWave);
+            const double zl = needL ? zxl[t] : zl_s;
+            const double zr = needR ? zxr[t] : zr_s;
+            const double Az = stencil_row<double>(fcs, fcs.area * o.lev_a[k], o.lev_d[k], lo, up, zc, zl, zr,
+                                                  zym[t], zyp[t], zv[t], zv[t + 2]);
+            const double r = fv[t] - Az;
+            res[b][t] = (t < len && ok) ? r : 0.0;
+            if (t < len && ok)
+                st_s(t_out + base + (size_t)(k0 + t) * ks, r);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < Ls; ++t) {
+        double v;
+        if constexpr (FX == 2) {
+            const double x0 = __shfl_xor(res[0][t], 1, kWave);
+            if constexpr (FY == 2) {
+                const double x1 = __shfl_xor(res[1][t], 1, kWave);
+                v = ((res[0][t] + x0) + res[1][t]) + x1;
+            } else {
+                v = res[0][t] + x0;
+            }
+        } else if constexpr (FY == 2) {
+            v = res[0][t] + res[1][t];
+        } else {
+            v = res[0][t];
+        }
+        if (t < len && ok && (FX == 1 || (lane & 1) == 0))
+            st_s(fc + (size_t)(i / FX) + (size_t)ncx * ((size_t)(k0 + t) + (size_t)o.nz * (size_t)J), v);
+    }
+}
+
+// After the coarse correction: w = t - A (P zc), the residual of z + P zc
+// from the residual t of z (in place: each point is read and written by the
+// same thread, with no neighbour reads of t).  P zc is the coarse parent's
+// value, so the stencil is applied to the parents of the cell and of its six
+// neighbours.  Sweep geometry of the fine level.
+template <int Ls>
+__global__ __launch_bounds__(kMaxThreads) void k_mg_prolong_resid(double *__restrict__ t, Op o, MgArgs mg,
+                                                                  const SolveState *__restrict__ st)
+{
+    if (st != nullptr && st->done)
+        return;
+    const Sweep sw = sweep_of_thread(o, Ls);
+    if (!sw.ok || sw.len <= 0)
+        return;
+    const int i = sw.i, j = sw.j, k0 = sw.k0;
+    const Faces fcs = column_faces(o, i, j);
+    const int ip = (i + 1 == o.nx) ? 0 : i + 1;
+    const int im = (i == 0) ? o.nx - 1 : i - 1;
+    const int jp = (j + 1 == o.ny) ? 0 : j + 1;
+    const int jm = (j == 0) ? o.ny - 1 : j - 1;
+    const size_t ksc = (size_t)mg.ncx;
+    const size_t pc = mg_parent(mg, o.nz, i, j, 0);
+    const size_t pxp = mg_parent(mg, o.nz, ip, j, 0), pxm = mg_parent(mg, o.nz, im, j, 0);
+    const size_t pyp = mg_parent(mg, o.nz, i, jp, 0), pym = mg_parent(mg, o.nz, i, jm, 0);
+    auto lev = [&](int k) { return (size_t)min(max(k, 0), o.nz - 1) * ksc; };
+    const size_t base = lin(o, i, j, 0);
+    double cv[Ls + 2], cxp[Ls], cxm[Ls], cyp[Ls], cym[Ls], tv[Ls];
+#pragma unroll
+    for (int q = 0; q < Ls + 2; ++q)
+        cv[q] = mg.zc[pc + lev(k0 - 1 + q)];
+#pragma unroll
+    for (int q = 0; q < Ls; ++q) {
+        const size_t off = lev(k0 + q);
+        cxp[q] = mg.zc[pxp + off];
+        cxm[q] = mg.zc[pxm + off];
+        cyp[q] = mg.zc[pyp + off];
+        cym[q] = mg.zc[pym + off];
+        tv[q] = q < sw.len ? ld_s(t + base + (size_t)(k0 + q) * o.nx) : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < Ls; ++q) {
+        if (q < sw.len) {
+            const int k = k0 + q;
+            const double lo = fcs.area * o.az[k], up = fcs.area * o.az[k + 1];
+            const double APz = stencil_row<double>(fcs, fcs.area * o.lev_a[k], o.lev_d[k], lo, up, cv[q + 1],
+                                                   cxm[q], cxp[q], cym[q], cyp[q], cv[q], cv[q + 2]);
+            st_s(t + base + (size_t)k * o.nx, tv[q] - APz);
+        }
     }
 }
 

@@ -52,6 +52,13 @@ struct pcg_handle {
     int64_t prof_n[PCG_KID_COUNT] = {};
     std::vector<hipEvent_t> free_events;
     std::vector<EventPair> pending;
+    // multigrid hierarchy (pcg_mg_setup): the coarse levels 1 .. nlev-1 are
+    // handles of their own, owned by this one; mg_fx / mg_fy[l] are the
+    // factors from level l to level l+1
+    std::vector<pcg_handle *> mg_levels;
+    std::vector<int> mg_fx, mg_fy;
+    int mg_nu = 0, mg_coarse_sweeps = 0;
+    double mg_omega = 0.0;
 };
 
 namespace {
@@ -246,14 +253,14 @@ void launch_column_lc(pcg_handle *h, const TV *rin, const TV *q, TV *rout, TZ *z
     if constexpr (C == kWave) {
         if (!tri && h->col_full) {
             if (upd == UPD_Q)
-                k_column_full<L, UPD_Q, true, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib);
+                k_column_full<L, UPD_Q, true, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib, MgArgs{});
             else if (!dots)
-                k_column_full<L, UPD_NONE, false, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib);
+                k_column_full<L, UPD_NONE, false, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib, MgArgs{});
             else if constexpr (kD) {
                 if (upd == UPD_AP)
-                    k_column_full<L, UPD_AP, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib);
+                    k_column_full<L, UPD_AP, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib, MgArgs{});
                 else
-                    k_column_full<L, UPD_NONE, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib);
+                    k_column_full<L, UPD_NONE, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib, MgArgs{});
             }
             return;
         }
@@ -261,21 +268,21 @@ void launch_column_lc(pcg_handle *h, const TV *rin, const TV *q, TV *rout, TZ *z
     if constexpr (kD) {
         if (tri) {
             if (dots)
-                k_column_solve<L, C, UPD_NONE, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
+                k_column_solve<L, C, UPD_NONE, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri, MgArgs{});
             else
-                k_column_solve<L, C, UPD_NONE, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri);
+                k_column_solve<L, C, UPD_NONE, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri, MgArgs{});
             return;
         }
     }
     if (upd == UPD_Q)
-        k_column_solve<L, C, UPD_Q, true, false, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib);
+        k_column_solve<L, C, UPD_Q, true, false, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib, MgArgs{});
     else if (!dots)
-        k_column_solve<L, C, UPD_NONE, false, false, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib);
+        k_column_solve<L, C, UPD_NONE, false, false, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib, MgArgs{});
     else if constexpr (kD) {
         if (upd == UPD_AP)
-            k_column_solve<L, C, UPD_AP, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib);
+            k_column_solve<L, C, UPD_AP, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib, MgArgs{});
         else
-            k_column_solve<L, C, UPD_NONE, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib);
+            k_column_solve<L, C, UPD_NONE, true, false><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, nullptr, phib, MgArgs{});
     }
 }
 
@@ -474,7 +481,9 @@ struct SolveArgs {
     double *final_rel;
 };
 
-int solve_prologue(pcg_handle *h, const SolveArgs &a, Workspace *w, const char *who)
+size_t mg_layout(const pcg_handle *h, int32_t maxit, char *base, Workspace *w, struct MgWork *mw);
+
+int solve_prologue(pcg_handle *h, const SolveArgs &a, Workspace *w, const char *who, bool mg = false)
 {
     if (!h)
         return PCG_ERR_INVALID;
@@ -489,7 +498,8 @@ int solve_prologue(pcg_handle *h, const SolveArgs &a, Workspace *w, const char *
         return fail(h, PCG_ERR_INVALID, "%s: null workspace", who);
     if (((uintptr_t)a.ws & 255u) != 0)
         return fail(h, PCG_ERR_INVALID, "%s: workspace must be 256-byte aligned", who);
-    const size_t need = workspace_layout(h, a.maxit, nullptr, nullptr);
+    const size_t need = mg ? mg_layout(h, a.maxit, nullptr, nullptr, nullptr)
+                           : workspace_layout(h, a.maxit, nullptr, nullptr);
     if (a.ws_bytes < need)
         return fail(h, PCG_ERR_INVALID, "%s: workspace has %zu bytes, needs %zu", who, a.ws_bytes, need);
     const char *ws = (const char *)a.ws, *xb = (const char *)a.x;
@@ -592,28 +602,14 @@ int check_array(const char *who, const char *name, const double *v, size_t n, bo
     return PCG_OK;
 }
 
-// Allocate the handle, copy the coefficients and compute the Thomas
-// multipliers at the segment boundaries (binary64 and binary32 tables).
-int create_handle(const char *who, const pcg_grid *grid, const Geometry &g, const HostCoeffs &hc,
-                  void *hip_stream, pcg_handle **out)
+// Launch geometry of one level (see Op and the kernels' decompositions).
+void init_geometry(pcg_handle *h, int nx, int ny, int nz, const Geometry &g)
 {
-    const int nx = grid->nx, ny = grid->ny, nz = grid->nz;
     const int L = g.L, C = g.C;
     const size_t ntx = ((size_t)nx + kWave - 1) / kWave;
     const size_t ntc = ((size_t)nx + C - 1) / C;
     const size_t nkt = ((size_t)nz + (size_t)g.Ls * g.Ws - 1) / ((size_t)g.Ls * g.Ws);
     const size_t ncol = (size_t)nx * ny;
-    pcg_handle *h = new pcg_handle();
-    auto bail = [&](int code) {
-        g_create_error = h->err;
-        pcg_destroy(h);
-        return code;
-    };
-    if (hipGetDevice(&h->device) != hipSuccess) {
-        h->err = std::string(who) + ": hipGetDevice failed";
-        return bail(PCG_ERR_HIP);
-    }
-    h->stream = (hipStream_t)hip_stream;
     const int P = (nz + L - 1) / L;
     h->col_tiles = (int)(ntc * ny);
     h->col_threads = ((C * P + kWave - 1) / kWave) * kWave;
@@ -638,26 +634,28 @@ int create_handle(const char *who, const pcg_grid *grid, const Geometry &g, cons
     // one strip of i-tiles per XCD (MFPCG_ST_STRIP overrides; 1 = i-tile slowest)
     h->op.sg = std::max(1, std::min((int)ntx, env_int("MFPCG_ST_STRIP", (int)((ntx + kXcds - 1) / kXcds))));
     h->op.csg = std::max(1, std::min((int)ntc, env_int("MFPCG_COL_STRIP", (int)((ntc + kXcds - 1) / kXcds))));
+}
+
+// Device tables of a level (faces, per-level and per-column coefficients,
+// boundary multipliers) and, for a handle the caller sees, the pinned status
+// word; the Op pointers are set to them.
+int alloc_tables(pcg_handle *h, const char *who, bool host_status)
+{
+    const int nz = h->op.nz, P = h->op.P;
+    const size_t ncol = (size_t)h->op.nx * h->op.ny;
     const size_t ncoef = 2 * (size_t)nz + 3 * ncol;
     hipError_t e;
     if ((e = hipMalloc(&h->d_az, sizeof(double) * (nz + 1))) != hipSuccess ||
         (e = hipMalloc(&h->d_coef, sizeof(double) * ncoef)) != hipSuccess ||
         (e = hipMalloc(&h->d_phib, sizeof(double) * ncol * (size_t)(P > 1 ? P - 1 : 1))) != hipSuccess ||
         (e = hipMalloc(&h->d_phib32, sizeof(float) * ncol * (size_t)(P > 1 ? P - 1 : 1))) != hipSuccess ||
-        (e = hipHostMalloc((void **)&h->h_status, sizeof(HostStatus), hipHostMallocCoherent)) != hipSuccess) {
+        (host_status &&
+         (e = hipHostMalloc((void **)&h->h_status, sizeof(HostStatus), hipHostMallocCoherent)) != hipSuccess)) {
         h->err = std::string(who) + ": allocation failed: " + hipGetErrorString(e);
-        return bail(PCG_ERR_HIP);
+        return PCG_ERR_HIP;
     }
-    memset(h->h_status, 0, sizeof(HostStatus));
-    std::vector<double> coef;
-    coef.reserve(ncoef);
-    for (const auto *v : {&hc.a, &hc.d, &hc.area, &hc.ex, &hc.ey})
-        coef.insert(coef.end(), v->begin(), v->end());
-    if ((e = hipMemcpy(h->d_az, hc.beta.data(), sizeof(double) * (nz + 1), hipMemcpyHostToDevice)) != hipSuccess ||
-        (e = hipMemcpy(h->d_coef, coef.data(), sizeof(double) * ncoef, hipMemcpyHostToDevice)) != hipSuccess) {
-        h->err = std::string(who) + ": copy failed: " + hipGetErrorString(e);
-        return bail(PCG_ERR_HIP);
-    }
+    if (h->h_status)
+        memset(h->h_status, 0, sizeof(HostStatus));
     h->op.az = h->d_az;
     h->op.lev_a = h->d_coef;
     h->op.lev_d = h->d_coef + nz;
@@ -665,16 +663,63 @@ int create_handle(const char *who, const pcg_grid *grid, const Geometry &g, cons
     h->op.ex = h->op.area + ncol;
     h->op.ey = h->op.ex + ncol;
     h->op.phib = h->d_phib;
-    if (P > 1) {
+    return PCG_OK;
+}
+
+// The Thomas multipliers at the segment boundaries (binary64 and binary32
+// tables), then wait for the set-up to finish.
+int setup_multipliers(pcg_handle *h, const char *who)
+{
+    const size_t ncol = (size_t)h->op.nx * h->op.ny;
+    if (h->op.P > 1) {
         const int threads = 256;
         const size_t blocks = (ncol + threads - 1) / threads;
         k_setup_phib<double><<<dim3((unsigned)blocks), dim3(threads), 0, h->stream>>>(h->op, h->d_phib);
         k_setup_phib<float><<<dim3((unsigned)blocks), dim3(threads), 0, h->stream>>>(h->op, h->d_phib32);
     }
+    hipError_t e;
     if ((e = hipStreamSynchronize(h->stream)) != hipSuccess || (e = hipGetLastError()) != hipSuccess) {
         h->err = std::string(who) + ": set-up failed: " + hipGetErrorString(e);
+        return PCG_ERR_HIP;
+    }
+    return PCG_OK;
+}
+
+// Allocate the handle, copy the coefficients and compute the Thomas
+// multipliers at the segment boundaries (binary64 and binary32 tables).
+int create_handle(const char *who, const pcg_grid *grid, const Geometry &g, const HostCoeffs &hc,
+                  void *hip_stream, pcg_handle **out)
+{
+    const int nx = grid->nx, ny = grid->ny, nz = grid->nz;
+    const size_t ncol = (size_t)nx * ny;
+    pcg_handle *h = new pcg_handle();
+    auto bail = [&](int code) {
+        g_create_error = h->err;
+        pcg_destroy(h);
+        return code;
+    };
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        h->err = std::string(who) + ": hipGetDevice failed";
         return bail(PCG_ERR_HIP);
     }
+    h->stream = (hipStream_t)hip_stream;
+    init_geometry(h, nx, ny, nz, g);
+    int rc = alloc_tables(h, who, true);
+    if (rc != PCG_OK)
+        return bail(rc);
+    const size_t ncoef = 2 * (size_t)nz + 3 * ncol;
+    std::vector<double> coef;
+    coef.reserve(ncoef);
+    for (const auto *v : {&hc.a, &hc.d, &hc.area, &hc.ex, &hc.ey})
+        coef.insert(coef.end(), v->begin(), v->end());
+    hipError_t e;
+    if ((e = hipMemcpy(h->d_az, hc.beta.data(), sizeof(double) * (nz + 1), hipMemcpyHostToDevice)) != hipSuccess ||
+        (e = hipMemcpy(h->d_coef, coef.data(), sizeof(double) * ncoef, hipMemcpyHostToDevice)) != hipSuccess) {
+        h->err = std::string(who) + ": copy failed: " + hipGetErrorString(e);
+        return bail(PCG_ERR_HIP);
+    }
+    if ((rc = setup_multipliers(h, who)) != PCG_OK)
+        return bail(rc);
     *out = h;
     return PCG_OK;
 }
@@ -787,6 +832,8 @@ int pcg_destroy(pcg_handle *h)
     if (h->d_phib32) (void)hipFree(h->d_phib32);
     if (h->d_phib_tri) (void)hipFree(h->d_phib_tri);
     if (h->h_status) (void)hipHostFree(h->h_status);
+    for (auto *c : h->mg_levels)
+        pcg_destroy(c);
     delete h;
     return PCG_OK;
 }
@@ -796,6 +843,8 @@ int pcg_set_stream(pcg_handle *h, void *hip_stream)
     if (!h)
         return PCG_ERR_INVALID;
     h->stream = (hipStream_t)hip_stream;
+    for (auto *c : h->mg_levels)
+        c->stream = h->stream;
     return PCG_OK;
 }
 
@@ -878,6 +927,192 @@ size_t pcg_solve_workspace_bytes(const pcg_handle *h, int32_t maxit)
 
 namespace {
 
+// ---- tensor-product multigrid -------------------------------------------------
+// Level l of the hierarchy (0: the handle itself).
+pcg_handle *mg_level(pcg_handle *h, int l) { return l == 0 ? h : h->mg_levels[(size_t)l - 1]; }
+
+// Per level: the right-hand side f (levels >= 1; level 0 works on the
+// solve's residual) and the two iterate buffers U, V (the cycle's result
+// lands in V; level 0's V is the solve's z).
+struct MgWork {
+    std::vector<double *> f, U, V;
+};
+
+size_t mg_layout(const pcg_handle *h, int32_t maxit, char *base, Workspace *w, MgWork *mw)
+{
+    Workspace tmp{};
+    Workspace *wl = w ? w : &tmp;
+    size_t off = workspace_layout(h, maxit, base, wl);
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    const size_t nl = 1 + h->mg_levels.size();
+    if (mw) {
+        mw->f.assign(nl, nullptr);
+        mw->U.assign(nl, nullptr);
+        mw->V.assign(nl, nullptr);
+    }
+    const size_t o0 = take(h->n * sizeof(double));
+    if (mw && base) {
+        mw->U[0] = (double *)(base + o0);
+        mw->V[0] = wl->z;
+    }
+    for (size_t l = 1; l < nl; ++l) {
+        const size_t bytes = h->mg_levels[l - 1]->n * sizeof(double);
+        const size_t of = take(bytes), ou = take(bytes), ov = take(bytes);
+        if (mw && base) {
+            mw->f[l] = (double *)(base + of);
+            mw->U[l] = (double *)(base + ou);
+            mw->V[l] = (double *)(base + ov);
+        }
+    }
+    return off;
+}
+
+// Multigrid forms of the column solve (64-column tiles).  DOTS is
+// instantiated on; the kernels skip the dot products when partials is null.
+template <int MG, int L>
+void launch_mg_column_l(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
+                        const SolveState *st, int first, double *partials, int upd, const MgArgs &a)
+{
+    dim3 grid(h->col_tiles), block(h->col_threads);
+    const Op &o = h->op;
+    const bool fused_q = MG == MG_FIRST && upd == UPD_Q;
+    if (h->col_full) {
+        if (fused_q)
+            k_column_full<L, UPD_Q, true, double, double, MG_FIRST><<<grid, block, 0, h->stream>>>(
+                rin, q, rout, z, o, st, first, partials, h->d_phib, a);
+        else
+            k_column_full<L, UPD_NONE, true, double, double, MG><<<grid, block, 0, h->stream>>>(
+                rin, q, rout, z, o, st, first, partials, h->d_phib, a);
+    } else {
+        if (fused_q)
+            k_column_solve<L, kWave, UPD_Q, true, false, double, double, MG_FIRST><<<grid, block, 0, h->stream>>>(
+                rin, q, rout, z, o, st, first, partials, nullptr, h->d_phib, a);
+        else
+            k_column_solve<L, kWave, UPD_NONE, true, false, double, double, MG><<<grid, block, 0, h->stream>>>(
+                rin, q, rout, z, o, st, first, partials, nullptr, h->d_phib, a);
+    }
+}
+
+template <int MG>
+void launch_mg_column(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
+                      const SolveState *st, int first, double *partials, int upd, const MgArgs &a)
+{
+    switch (h->op.L) {
+    case 4: launch_mg_column_l<MG, 4>(h, rin, q, rout, z, st, first, partials, upd, a); break;
+    case 8: launch_mg_column_l<MG, 8>(h, rin, q, rout, z, st, first, partials, upd, a); break;
+    case 16: launch_mg_column_l<MG, 16>(h, rin, q, rout, z, st, first, partials, upd, a); break;
+    default: launch_mg_column_l<MG, 32>(h, rin, q, rout, z, st, first, partials, upd, a); break;
+    }
+}
+
+void mg_column(pcg_handle *h, int mode, const double *rin, const double *q, double *rout, double *z,
+               const SolveState *st, int first, double *partials, int upd, const MgArgs &a)
+{
+    if (mode == MG_FIRST)
+        launch_mg_column<MG_FIRST>(h, rin, q, rout, z, st, first, partials, upd, a);
+    else
+        launch_mg_column<MG_CORR>(h, rin, q, rout, z, st, first, partials, upd, a);
+}
+
+template <int Ls>
+void launch_mg_restrict(pcg_handle *h, int fx, int fy, const double *f, const double *z, double *t,
+                        double *fc, int ncx, const SolveState *st)
+{
+    const size_t ncy = (size_t)(h->op.ny / fy);
+    dim3 grid((unsigned)((size_t)h->op.ntx * ncy * h->op.nkt)), block(kWave * h->op.Ws);
+    if (fx == 2 && fy == 2)
+        k_mg_restrict<Ls, 2, 2><<<grid, block, 0, h->stream>>>(f, z, t, fc, h->op, ncx, st);
+    else if (fx == 2)
+        k_mg_restrict<Ls, 2, 1><<<grid, block, 0, h->stream>>>(f, z, t, fc, h->op, ncx, st);
+    else
+        k_mg_restrict<Ls, 1, 2><<<grid, block, 0, h->stream>>>(f, z, t, fc, h->op, ncx, st);
+}
+
+// t = f - A z and fc = P^T t (level h to the next with factors fx, fy).
+void mg_restrict(pcg_handle *h, int fx, int fy, const double *f, const double *z, double *t, double *fc,
+                 int ncx, const SolveState *st)
+{
+    switch (h->op.Ls) {
+    case 1: launch_mg_restrict<1>(h, fx, fy, f, z, t, fc, ncx, st); break;
+    case 2: launch_mg_restrict<2>(h, fx, fy, f, z, t, fc, ncx, st); break;
+    case 4: launch_mg_restrict<4>(h, fx, fy, f, z, t, fc, ncx, st); break;
+    default: launch_mg_restrict<8>(h, fx, fy, f, z, t, fc, ncx, st); break;
+    }
+}
+
+// t -= A (P zc), in place.
+void mg_prolong(pcg_handle *h, double *t, const MgArgs &a, const SolveState *st)
+{
+    dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
+    switch (h->op.Ls) {
+    case 1: k_mg_prolong_resid<1><<<grid, block, 0, h->stream>>>(t, h->op, a, st); break;
+    case 2: k_mg_prolong_resid<2><<<grid, block, 0, h->stream>>>(t, h->op, a, st); break;
+    case 4: k_mg_prolong_resid<4><<<grid, block, 0, h->stream>>>(t, h->op, a, st); break;
+    default: k_mg_prolong_resid<8><<<grid, block, 0, h->stream>>>(t, h->op, a, st); break;
+    }
+}
+
+// z = B f on level l: one V(nu, nu) cycle (horizontal semi-coarsening,
+// piecewise-constant transfers, Galerkin coarse operators, the column solve
+// as damped block-Jacobi smoother).  rin is the level's right-hand side; on
+// level 0 of a solve the first sweep also applies r -= alpha q (upd = UPD_Q,
+// rout = rin = r) and the last sweep forms the partial sums <r, r>, <r, z>
+// (partials).  The result lands in V; after the first sweep every sweep
+// writes the buffer that does not hold the current iterate:
+//   first sweep   z = omega M^{-1} f
+//   sweep         w = f - A z (stencil pass), z' = z + omega M^{-1} w
+//   restriction   t = f - A z, f_c = P^T t
+//   correction    w = t - A (P z_c), z' = (z + P z_c) + omega M^{-1} w
+// On the coarsest level: the exact column solve for one column, else
+// coarse_sweeps sweeps from z = 0.
+void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const double *q, double *rout,
+              int upd, const SolveState *st, int first, double *partials)
+{
+    pcg_handle *h = mg_level(h0, l);
+    const int nlev = 1 + (int)h0->mg_levels.size();
+    const double *f = (upd != UPD_NONE) ? rout : rin;
+    double *V = mw.V[(size_t)l], *U = mw.U[(size_t)l];
+    const MgArgs a{nullptr, f, h0->mg_omega, 0, 1, 1};
+    auto sweep = [&](double *cur, double *oth, double *parts) {
+        stencil<double, double>(h, SP_RESID, cur, f, nullptr, nullptr, oth, nullptr, nullptr);
+        mg_column(h, MG_CORR, oth, cur, nullptr, oth, st, 0, parts, UPD_NONE, a);
+    };
+    if (l == nlev - 1) {
+        if ((size_t)h->op.nx * h->op.ny == 1) {
+            column<double, double>(h, rin, q, rout, V, st, first, partials, upd, partials != nullptr);
+            return;
+        }
+        const int cs = h0->mg_coarse_sweeps;
+        double *cur = ((cs - 1) % 2 == 0) ? V : U;
+        double *oth = (cur == V) ? U : V;
+        mg_column(h, MG_FIRST, rin, q, rout, cur, st, first, cs == 1 ? partials : nullptr, upd, a);
+        for (int sw = 1; sw < cs; ++sw) {
+            sweep(cur, oth, sw == cs - 1 ? partials : nullptr);
+            std::swap(cur, oth);
+        }
+        return;
+    }
+    const int nu = h0->mg_nu;
+    double *cur = U, *oth = V;
+    mg_column(h, MG_FIRST, rin, q, rout, cur, st, first, nullptr, upd, a);
+    for (int sw = 1; sw < nu; ++sw) {
+        sweep(cur, oth, nullptr);
+        std::swap(cur, oth);
+    }
+    pcg_handle *c = mg_level(h0, l + 1);
+    const int fx = h0->mg_fx[(size_t)l], fy = h0->mg_fy[(size_t)l];
+    mg_restrict(h, fx, fy, f, cur, oth, mw.f[(size_t)l + 1], c->op.nx, st);
+    mg_cycle(h0, mw, l + 1, mw.f[(size_t)l + 1], nullptr, nullptr, UPD_NONE, st, 0, nullptr);
+    const MgArgs ap{mw.V[(size_t)l + 1], f, h0->mg_omega, c->op.nx, fx, fy};
+    mg_prolong(h, oth, ap, st);
+    mg_column(h, MG_CORR, oth, cur, nullptr, oth, st, 0, nu == 1 ? partials : nullptr, UPD_NONE, ap);
+    std::swap(cur, oth);
+    for (int sw = 1; sw < nu; ++sw) {
+        sweep(cur, oth, sw == nu - 1 ? partials : nullptr);
+        std::swap(cur, oth);
+    }
+}
+
 // The interleaved loop of section 4.3, Algorithm 1.  ap = false: Algorithms 2
 // and 3 as printed (q = A z + beta q stored by the stencil pass, r -= alpha q
 // in the preconditioner pass), with the x update of every odd step deferred to
@@ -889,8 +1124,10 @@ namespace {
 // between two buffers (the stencil pass reads the old direction around each
 // point while writing the new one).
 // TV, TZ: see the launch helpers; ap only for binary64.
+// mg != nullptr: the preconditioner pass is one multigrid V-cycle (binary64).
 template <typename TV, typename TZ>
-int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool ap, const char *who)
+int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool ap, const char *who,
+                     const MgWork *mg = nullptr)
 {
     constexpr bool kD = kBinary64<TV, TZ>;
     if (ap && !kD)
@@ -922,7 +1159,13 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
         TV *pcur = pbuf[(k + 1) & 1];
         TV *pnext = pbuf[k & 1];
         // a3: r -= alpha q (or alpha A p); z = M^{-1} r; partial <r,r>, <r,z>  (Algorithm 3)
-        {
+        if constexpr (kD) {
+            if (mg) {
+                Timed t(h, PCG_KID_MG_VCYCLE, k);
+                mg_cycle(h, *mg, 0, r, pin, r, UPD_Q, w.state, k == 0, w.partials);
+            }
+        }
+        if (!mg) {
             Timed t(h, PCG_KID_FUSED_PREC, k);
             column<TV, TZ>(h, r, pin, r, z, w.state, k == 0, w.partials, ap ? UPD_AP : UPD_Q, true);
         }
@@ -1017,6 +1260,198 @@ int pcg_solve_mixed(pcg_handle *h, const double *b, double *x, double tol, int32
     if (rc != PCG_OK)
         return rc;
     return interleaved_loop<double, float>(h, a, w, false, "pcg_solve_mixed");
+}
+
+}   // extern "C"
+
+namespace {
+
+// One coarse level from the fine level h (factors fx, fy): its tables on the
+// device, the coefficients by Galerkin coarsening, the Thomas multipliers.
+int create_coarse(pcg_handle *h, int fx, int fy, pcg_handle **out)
+{
+    const char *who = "pcg_mg_setup";
+    pcg_handle *c = new pcg_handle();
+    c->device = h->device;
+    c->stream = h->stream;
+    const Geometry g{h->op.L, h->op.C, h->op.Ls, h->op.Ws};
+    const int nz = h->op.nz;
+    init_geometry(c, h->op.nx / fx, h->op.ny / fy, nz, g);
+    int rc = alloc_tables(c, who, false);
+    if (rc == PCG_OK) {
+        hipError_t e;
+        if ((e = hipMemcpyAsync(c->d_az, h->d_az, sizeof(double) * (nz + 1), hipMemcpyDeviceToDevice,
+                                h->stream)) != hipSuccess ||
+            (e = hipMemcpyAsync(c->d_coef, h->d_coef, sizeof(double) * 2 * (size_t)nz,
+                                hipMemcpyDeviceToDevice, h->stream)) != hipSuccess) {
+            c->err = std::string(who) + ": copy failed: " + hipGetErrorString(e);
+            rc = PCG_ERR_HIP;
+        } else {
+            const size_t ncol = (size_t)c->op.nx * c->op.ny;
+            double *area = c->d_coef + 2 * (size_t)nz;
+            k_mg_coarsen<<<dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, h->stream>>>(
+                h->op, c->op.nx, c->op.ny, fx, fy, area, area + ncol, area + 2 * ncol);
+            rc = setup_multipliers(c, who);
+        }
+    }
+    if (rc != PCG_OK) {
+        h->err = c->err;
+        pcg_destroy(c);
+        return rc;
+    }
+    *out = c;
+    return PCG_OK;
+}
+
+void mg_clear(pcg_handle *h)
+{
+    for (auto *c : h->mg_levels)
+        pcg_destroy(c);
+    h->mg_levels.clear();
+    h->mg_fx.clear();
+    h->mg_fy.clear();
+    h->mg_nu = 0;
+}
+
+}   // namespace
+
+extern "C" {
+
+int pcg_mg_setup(pcg_handle *h, const pcg_mg_params *p)
+{
+    const char *who = "pcg_mg_setup";
+    if (!h)
+        return PCG_ERR_INVALID;
+    if (!p)
+        return fail(h, PCG_ERR_INVALID, "%s: params is NULL", who);
+    if (p->nu < 1 || p->nu > 16)
+        return fail(h, PCG_ERR_INVALID, "%s: nu = %d must be in 1..16", who, p->nu);
+    if (!(p->omega > 0.0 && p->omega <= 1.0))
+        return fail(h, PCG_ERR_INVALID, "%s: omega = %g must be in (0, 1]", who, p->omega);
+    if (p->max_levels < 0 || p->max_levels > 64)
+        return fail(h, PCG_ERR_INVALID, "%s: max_levels = %d must be in 0..64", who, p->max_levels);
+    if (p->coarse_sweeps < 1 || p->coarse_sweeps > 64)
+        return fail(h, PCG_ERR_INVALID, "%s: coarse_sweeps = %d must be in 1..64", who, p->coarse_sweeps);
+    if (h->op.C != kWave)
+        return fail(h, PCG_ERR_UNSUPPORTED, "%s: the multigrid sweeps need 64-column column tiles", who);
+    int rc = set_device(h);
+    if (rc != PCG_OK)
+        return rc;
+    HIP_TRY(h, hipStreamSynchronize(h->stream));
+    mg_clear(h);
+    pcg_handle *cur = h;
+    int nx = h->op.nx, ny = h->op.ny, nlev = 1;
+    while ((p->max_levels == 0 || nlev < p->max_levels) && (size_t)nx * ny > 1) {
+        const int fx = (nx > 1 && nx % 2 == 0) ? 2 : 1;
+        const int fy = (ny > 1 && ny % 2 == 0) ? 2 : 1;
+        if (fx == 1 && fy == 1)
+            break;
+        pcg_handle *c = nullptr;
+        if ((rc = create_coarse(cur, fx, fy, &c)) != PCG_OK) {
+            if (cur != h)
+                h->err = cur->err;
+            mg_clear(h);
+            return rc;
+        }
+        h->mg_levels.push_back(c);
+        h->mg_fx.push_back(fx);
+        h->mg_fy.push_back(fy);
+        cur = c;
+        nx /= fx;
+        ny /= fy;
+        ++nlev;
+    }
+    h->mg_nu = p->nu;
+    h->mg_omega = p->omega;
+    h->mg_coarse_sweeps = p->coarse_sweeps;
+    return PCG_OK;
+}
+
+int pcg_mg_num_levels(const pcg_handle *hc, int32_t *levels)
+{
+    pcg_handle *h = const_cast<pcg_handle *>(hc);
+    if (!h || !levels)
+        return PCG_ERR_INVALID;
+    if (h->mg_nu == 0)
+        return fail(h, PCG_ERR_INVALID, "pcg_mg_num_levels: call pcg_mg_setup first");
+    *levels = 1 + (int32_t)h->mg_levels.size();
+    return PCG_OK;
+}
+
+int pcg_mg_level(pcg_handle *h, int32_t level, int32_t *nx, int32_t *ny, double *area, double *ax, double *ay)
+{
+    if (!h)
+        return PCG_ERR_INVALID;
+    if (h->mg_nu == 0)
+        return fail(h, PCG_ERR_INVALID, "pcg_mg_level: call pcg_mg_setup first");
+    if (level < 0 || level > (int32_t)h->mg_levels.size())
+        return fail(h, PCG_ERR_INVALID, "pcg_mg_level: level %d out of range", level);
+    pcg_handle *l = mg_level(h, level);
+    if (nx)
+        *nx = l->op.nx;
+    if (ny)
+        *ny = l->op.ny;
+    const size_t ncol = (size_t)l->op.nx * l->op.ny;
+    int rc = set_device(h);
+    if (rc != PCG_OK)
+        return rc;
+    HIP_TRY(h, hipStreamSynchronize(h->stream));
+    if (area)
+        HIP_TRY(h, hipMemcpy(area, l->op.area, ncol * sizeof(double), hipMemcpyDeviceToHost));
+    if (ax)
+        HIP_TRY(h, hipMemcpy(ax, l->op.ex, ncol * sizeof(double), hipMemcpyDeviceToHost));
+    if (ay)
+        HIP_TRY(h, hipMemcpy(ay, l->op.ey, ncol * sizeof(double), hipMemcpyDeviceToHost));
+    return PCG_OK;
+}
+
+size_t pcg_mg_workspace_bytes(const pcg_handle *h, int32_t maxit)
+{
+    if (!h || maxit < 0 || h->mg_nu == 0)
+        return 0;
+    return mg_layout(h, maxit, nullptr, nullptr, nullptr);
+}
+
+int pcg_mg_vcycle(pcg_handle *h, const double *r, double *z, void *ws, size_t ws_bytes)
+{
+    const char *who = "pcg_mg_vcycle";
+    if (!h)
+        return PCG_ERR_INVALID;
+    if (h->mg_nu == 0)
+        return fail(h, PCG_ERR_INVALID, "%s: call pcg_mg_setup first", who);
+    SolveArgs a{r, z, sizeof(double), 0.0, 0, ws, ws_bytes, nullptr, nullptr, nullptr, nullptr};
+    Workspace w{};
+    int rc = solve_prologue(h, a, &w, who, true);
+    if (rc != PCG_OK)
+        return rc;
+    MgWork mw;
+    mg_layout(h, 0, (char *)ws, &w, &mw);
+    mw.V[0] = z;
+    {
+        Timed t(h, PCG_KID_MG_VCYCLE, -1);
+        mg_cycle(h, mw, 0, r, nullptr, nullptr, UPD_NONE, nullptr, 0, nullptr);
+    }
+    HIP_TRY(h, hipGetLastError());
+    return PCG_OK;
+}
+
+int pcg_solve_mg(pcg_handle *h, const double *b, double *x, double tol, int32_t maxit, void *ws,
+                 size_t ws_bytes, int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
+                 double *final_rel)
+{
+    const char *who = "pcg_solve_mg";
+    if (!h)
+        return PCG_ERR_INVALID;
+    if (h->mg_nu == 0)
+        return fail(h, PCG_ERR_INVALID, "%s: call pcg_mg_setup first", who);
+    SolveArgs a{b, x, sizeof(double), tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
+    Workspace w{};
+    int rc = solve_prologue(h, a, &w, who, true);
+    if (rc != PCG_OK)
+        return rc;
+    MgWork mw;
+    mg_layout(h, maxit, (char *)ws, &w, &mw);
+    return interleaved_loop<double, double>(h, a, w, false, who, &mw);
 }
 
 }   // extern "C"

@@ -159,3 +159,14 @@ def test_create_general_rejects_invalid_arguments(lib, case):
     assert rc == _abi.PCG_ERR_INVALID
     assert out.value is None
     assert "pcg_create_general" in _abi.pcg_last_error(None)
+
+
+def test_mg_entry_points_reject_null_handle(lib):
+    p = _abi.pcg_mg_params(1, 0.8, 0, 2)
+    assert lib.pcg_mg_setup(None, ctypes.byref(p)) == _abi.PCG_ERR_INVALID
+    n = ctypes.c_int32(0)
+    assert lib.pcg_mg_num_levels(None, ctypes.byref(n)) == _abi.PCG_ERR_INVALID
+    assert lib.pcg_mg_level(None, 0, None, None, None, None, None) == _abi.PCG_ERR_INVALID
+    assert lib.pcg_mg_workspace_bytes(None, 10) == 0
+    assert lib.pcg_mg_vcycle(None, None, None, None, 0) == _abi.PCG_ERR_INVALID
+    assert lib.pcg_solve_mg(None, None, None, 1e-8, 10, None, 0, None, None, None, None) == _abi.PCG_ERR_INVALID

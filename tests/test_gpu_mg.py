@@ -1,0 +1,213 @@
+"""GPU parity of the tensor-product multigrid preconditioner (horizontal
+Galerkin coarsening with piecewise-constant transfers, damped column-block
+smoother, V(nu, nu) cycle) against the oracle's multigrid functions (pinned by
+M1-M5).
+
+Tolerances:
+  * coarse coefficients: bit-exact (both sides sum the same binary64 values
+    in the same order, additions only);
+  * one V-cycle z = B r: every sweep is a stencil pass and a column solve
+    whose GPU and oracle results differ by rounding (16 eps S and 64 eps
+    kappa ||z|| per pass, as in the single-pass tests); a cycle composes a
+    few such passes per level, so |z_gpu - z_orc| <= 1e-9 ||z_orc||_inf
+    (measured differences are below 1e-12 relative);
+  * solves: as the other solve tests (iterations within 1, final iterates
+    within rel-L2 1e-9, residual histories within 10x the oracle's own
+    spread under an ulp-level perturbation of b, floor 1e-6);
+  * at full size, where the oracle is too slow, properties that hold at any
+    size: B is symmetric (<B u, v> = <u, B v>) and positive, and the solve
+    converges with a true residual within 10 tol."""
+import numpy as np
+import pytest
+
+import matrix_free_pcg_amd as mf
+import oracle
+from gpu_helpers import require_gpu, to_dev, to_host
+from matrix_free_pcg_amd import workloads as W
+from oracle_pins import general_from_special, random_general
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def as_general(prob):
+    return prob if isinstance(prob, W.GeneralProblem) else general_from_special(prob)
+
+
+GRIDS = [
+    ("general-128x64x16", lambda: W.general_problem(128, 64, 16, 6)),
+    ("varying-96x40x12", lambda: W.config_problem(4, scale_xy=(96, 40), nz=12)),
+    ("random-8x2x5", lambda: random_general(8, 2, 5, seed=21)),
+    ("random-1x16x6", lambda: random_general(1, 16, 6, seed=22)),
+    ("random-6x10x9", lambda: random_general(6, 10, 9, seed=23)),
+    ("random-1x1x7", lambda: random_general(1, 1, 7, seed=24)),
+    ("random-5x3x4", lambda: random_general(5, 3, 4, seed=25)),
+    ("general-64x64x128", lambda: W.general_problem(64, 64, 128, 6)),
+]
+PARAMS = [
+    dict(nu=1, omega=0.8, max_levels=0, coarse_sweeps=2),
+    dict(nu=2, omega=0.7, max_levels=3, coarse_sweeps=3),
+    dict(nu=1, omega=1.0, max_levels=2, coarse_sweeps=1),
+]
+
+
+@pytest.mark.parametrize("label,make", GRIDS, ids=[g[0] for g in GRIDS])
+def test_mg_levels_match_oracle(dev, label, make):
+    prob = make()
+    gp = as_general(prob)
+    h = mf.pcg_create(prob)
+    try:
+        mf.pcg_mg_setup(h)
+        nlev = mf.pcg_mg_num_levels(h)
+        levels = [mf.pcg_mg_level(h, l) for l in range(nlev)]
+    finally:
+        mf.pcg_destroy(h)
+    assert nlev == oracle.mg_num_levels(gp.nx, gp.ny), (label, nlev)
+    # coarsen the GPU's own level-0 tables on the oracle: the sums are then
+    # of identical binary64 values in identical order
+    _, _, area0, ax0, ay0 = levels[0]
+    cur = W.GeneralProblem(gp.nx, gp.ny, gp.nz, gp.a, gp.d, gp.beta_face, area0, ax0, ay0)
+    for l in range(1, nlev):
+        cur = oracle.mg_coarsen(cur)
+        nx, ny, area, ax, ay = levels[l]
+        assert (nx, ny) == (cur.nx, cur.ny), (label, l)
+        assert np.array_equal(area, cur.area) and np.array_equal(ax, cur.alpha_x) and \
+            np.array_equal(ay, cur.alpha_y), (label, l)
+    assert cur.nx * cur.ny == 1 or oracle.mg_coarsen(cur) is None, label
+
+
+@pytest.mark.parametrize("pi", range(len(PARAMS)), ids=lambda i: "nu{nu}-w{omega}-L{max_levels}-cs{coarse_sweeps}".format(**PARAMS[i]))
+@pytest.mark.parametrize("label,make", GRIDS, ids=[g[0] for g in GRIDS])
+def test_vcycle_matches_oracle(dev, label, make, pi):
+    import torch
+    prob = make()
+    gp = as_general(prob)
+    mg = PARAMS[pi]
+    r = W.gaussian_field(gp.nx, gp.ny, gp.nz, 303)
+    h = mf.pcg_create(prob)
+    try:
+        mf.pcg_mg_setup(h, **mg)
+        rd = to_dev(r, dev)
+        zd = torch.full_like(rd, float("nan"))
+        mf.pcg_mg_vcycle(h, rd, zd)
+        # a second cycle on the same workspace gives the same result
+        zd2 = torch.full_like(rd, float("nan"))
+        ws = torch.full((mf.pcg_mg_workspace_bytes(h, 0),), 255, dtype=torch.uint8, device=dev)
+        mf.pcg_mg_vcycle(h, rd, zd2, ws)
+        torch.cuda.synchronize()
+        z, z2 = to_host(zd), to_host(zd2)
+    finally:
+        mf.pcg_destroy(h)
+    zo = oracle.mg_vcycle(gp, r, **mg)
+    err = np.abs(z - zo).max() / np.abs(zo).max()
+    print(f"{label} {mg}: rel max err {err:.2e}")
+    assert np.all(np.isfinite(z)) and err <= 1e-9, (label, mg, err)
+    assert np.array_equal(z, z2), label
+
+
+SOLVES = [
+    ("general-128x64x16", lambda: W.general_problem(128, 64, 16, 6), 6),
+    ("varying-96x40x12", lambda: W.config_problem(4, scale_xy=(96, 40), nz=12), 4),
+    ("random-6x10x9", lambda: random_general(6, 10, 9, seed=23), 8),
+    ("general-64x32x32", lambda: W.general_problem(64, 32, 32, 6), 6),
+]
+
+
+@pytest.mark.parametrize("pi", [0, 1], ids=["default", "nu2-L3"])
+@pytest.mark.parametrize("label,make,seed", SOLVES, ids=[c[0] for c in SOLVES])
+def test_solve_mg_matches_oracle(dev, label, make, seed, pi):
+    import torch
+    prob = make()
+    gp = as_general(prob)
+    mg = PARAMS[pi]
+    b = W.uniform_field(gp.nx, gp.ny, gp.nz, seed)
+    h = mf.pcg_create(prob)
+    try:
+        mf.pcg_mg_setup(h, **mg)
+        bd = to_dev(b, dev)
+        xd = torch.zeros_like(bd)
+        res = mf.pcg_solve_mg(h, bd, xd, 1e-10, 500)
+        torch.cuda.synchronize()
+        xg = to_host(xd)
+    finally:
+        mf.pcg_destroy(h)
+    ref = oracle.pcg_mg(gp, b, tol=1e-10, maxit=500, **mg)
+    assert res["status"] == ref["status"] == 0, (label, res, ref["status"])
+    assert abs(res["iters"] - ref["iters"]) <= 1, (label, res["iters"], ref["iters"])
+    rel = np.linalg.norm(xg - ref["x"]) / np.linalg.norm(ref["x"])
+    u = np.random.default_rng(4242).uniform(-1.0, 1.0, size=b.shape)
+    spread = oracle.pcg_mg(gp, b * (1.0 + 2.0 ** -52 * u), tol=1e-10, maxit=500, **mg)["hist"]
+    n = min(len(res["hist"]), len(ref["hist"]), len(spread))
+    hg, ho, hs = res["hist"][:n], ref["hist"][:n], spread[:n]
+    big = ho >= 1e-6 * ho[0]
+    dg = np.max(np.abs(hg[big] - ho[big]) / ho[big])
+    ds = np.max(np.abs(hs[big] - ho[big]) / ho[big])
+    col = oracle.pcg_gen(gp, b, tol=1e-10, maxit=5000)["iters"]
+    print(f"{label} {mg}: iters gpu {res['iters']} oracle {ref['iters']} (column PCG {col}) rel-L2 {rel:.2e} "
+          f"history {dg:.2e} (self {ds:.2e})")
+    assert rel <= 1e-9, (label, rel)
+    assert dg <= max(1e-6, 10 * ds), (label, dg, ds)
+
+
+def test_mg_setup_rejects_and_requires(dev):
+    import torch
+    prob = W.config_problem(1, scale_xy=(8, 8), nz=4)
+    h = mf.pcg_create(prob)
+    try:
+        bd = to_dev(np.ones((8, 4, 8)), dev)
+        xd = torch.zeros_like(bd)
+        with pytest.raises(mf.PcgError):
+            mf.pcg_solve_mg(h, bd, xd, 1e-8, 10, workspace=torch.empty(1 << 20, dtype=torch.uint8, device=dev))
+        for bad in (dict(nu=0), dict(omega=0.0), dict(omega=1.5), dict(max_levels=-1), dict(coarse_sweeps=0)):
+            with pytest.raises(mf.PcgError) as e:
+                mf.pcg_mg_setup(h, **bad)
+            assert e.value.code == mf.PCG_ERR_INVALID
+        mf.pcg_mg_setup(h, max_levels=2)
+        assert mf.pcg_mg_num_levels(h) == 2
+        mf.pcg_mg_setup(h)
+        assert mf.pcg_mg_num_levels(h) == 4
+        with pytest.raises(mf.PcgError):
+            mf.pcg_mg_level(h, 4)
+    finally:
+        mf.pcg_destroy(h)
+
+
+@pytest.mark.parametrize("cfg", [4, 6])
+def test_mg_full_size(dev, cfg):
+    """The 1024 x 1024 x 128 workloads: B symmetric and positive on random
+    vectors, and the solve converges (true residual within 10 tol)."""
+    import torch
+    wl = W.make_workload(cfg)
+    prob = wl.problem
+    n = prob.n
+    h = mf.pcg_create(prob)
+    try:
+        mf.pcg_mg_setup(h)
+        g = torch.Generator(device=dev).manual_seed(7)
+        u = torch.randn(n, dtype=torch.float64, device=dev, generator=g)
+        v = torch.randn(n, dtype=torch.float64, device=dev, generator=g)
+        Bu, Bv = torch.empty_like(u), torch.empty_like(v)
+        ws = torch.empty(mf.pcg_mg_workspace_bytes(h, 0), dtype=torch.uint8, device=dev)
+        mf.pcg_mg_vcycle(h, u, Bu, ws)
+        mf.pcg_mg_vcycle(h, v, Bv, ws)
+        a, b_ = float(torch.dot(Bu, v)), float(torch.dot(u, Bv))
+        uBu = float(torch.dot(u, Bu))
+        assert abs(a - b_) <= 1e-10 * (float(Bu.norm()) * float(v.norm())), (a, b_)
+        assert uBu > 0.0
+        del u, v, Bu, Bv, ws
+        bd = to_dev(wl.rhs, dev).reshape(-1)
+        xd = torch.zeros_like(bd)
+        res = mf.pcg_solve_mg(h, bd, xd, wl.tol, 300)
+        y = torch.empty_like(xd)
+        mf.pcg_apply_A(h, xd, y)
+        true_rel = float((bd - y).norm() / bd.norm())
+        torch.cuda.synchronize()
+    finally:
+        mf.pcg_destroy(h)
+    print(f"cfg {cfg}: {res['iters']} steps, final {res['final_rel_res']:.2e}, true {true_rel:.2e}")
+    assert res["status"] == 0 and res["iters"] <= 150, res
+    assert true_rel <= 10 * wl.tol, true_rel
