@@ -80,8 +80,7 @@ BYTES_BY_VARIANT = {"interleaved": (_bytes_interleaved, 84), "interleaved_no_q":
 #   first sweep   read f (and q: r -= alpha q on level 0, k >= 1), write z
 #                 (and r): 16, level 0 at k >= 1: 32
 #   restriction   read f, z, write t: 24 per point; write f_c: 8 per coarse point
-#   prolongation  read and write t: 16; read z_c: 8 per coarse point
-#   correction    read w, z (and f for the dot products on level 0), write z:
+#   correction    read t, z (and f for the dot products on level 0), write z:
 #                 24, level 0: 32; read z_c: 8 per coarse point
 # and on a coarsest level of one column the exact column solve: 16.
 def mg_cycle_bytes(level_points, k, nu=1):
@@ -95,18 +94,8 @@ def mg_cycle_bytes(level_points, k, nu=1):
             continue
         first = 32 if (l == 0 and k > 0) else 16
         corr = 32 if l == 0 else 24
-        tot += (first + 24 + 16 + corr) * nl + 24 * nc
+        tot += (first + 24 + corr) * nl + 16 * nc
     return tot
-
-
-def step_class(variant, kernel, k):
-    """Launches of a pass with the same work per point: the first step, and
-    (interleaved stencil pass) odd / even steps, else the rest."""
-    if k == 0:
-        return "first"
-    if variant in ("interleaved", "f32", "mixed") and kernel == "fused_spmv":
-        return "odd" if k % 2 else "even"
-    return "rest"
 
 
 def mg_pass_bytes(level_points, iters):

@@ -272,14 +272,18 @@ enum : int { UPD_NONE = 0, UPD_Q = 1, UPD_AP = 2 };
 
 // Multigrid forms of the column solve (tensor-product multigrid: horizontal
 // semi-coarsening, the column solve as damped block-Jacobi smoother), with
-// y = M^{-1} rr and rr from the UPD mode:
-//   MG_FIRST  z = omega y            (first sweep from z = 0)
-//   MG_CORR   z = zb + omega y, zb = q + (zc at the coarse parent, if zc):
-//             rr is a residual computed by a sweep pass; the sweep after the
-//             coarse correction adds the prolongated correction here.
-// Binary64 only.  The dot products of these forms are <f, f> and <f, z>
-// (f: the level's right-hand side) and are skipped when partials is null.
-enum : int { MG_NONE = 0, MG_FIRST = 1, MG_CORR = 2 };
+// y = M^{-1} rr:
+//   MG_FIRST  rr from the UPD mode, z = omega y    (first sweep from z = 0)
+//   MG_CORR   rr = rin, a residual f - A q computed by a stencil pass;
+//             z = q + omega y                      (further sweeps)
+//   MG_POST   rr = rin - A (P zc), rin the residual t = f - A q kept by the
+//             restriction; z = (q + P zc) + omega y: the sweep after the
+//             coarse correction, with the residual of q + P zc formed from t
+//             and the coarse correction alone (no neighbour reads of q)
+// P zc is the value of the coarse parent.  Binary64 only.  The dot products
+// of MG_CORR and MG_POST are <f, f> and <f, z> (f: the level's right-hand
+// side); in every MG form they are skipped when partials is null.
+enum : int { MG_NONE = 0, MG_FIRST = 1, MG_CORR = 2, MG_POST = 3 };
 
 struct MgArgs {
     const double *zc;   // coarse correction (coarse layout), or null
@@ -308,6 +312,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     static_assert(MG == MG_NONE || (UPD != UPD_AP && !STORED && std::is_same<TV, double>::value &&
                                     std::is_same<TZ, double>::value),
                   "the multigrid forms are binary64 only");
+    static_assert(MG != MG_POST || UPD == UPD_NONE, "MG_POST reads its residual as it is");
     __shared__ TZ sh_a[kMaxThreads];
     __shared__ TZ sh_b[kMaxThreads];
     __shared__ double sh_red[kMaxThreads / kWave][2];
@@ -429,6 +434,59 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
             rr[t] = v;
             r2 += v * v;
         }
+    } else if constexpr (MG == MG_POST) {
+        // rr = t - A (P zc): the coarse parents of the column (levels k0-1 ..
+        // k0+L, clamped), of the j-1 and j+1 columns, and of the i-1 / i+1
+        // columns (from the adjacent lanes, except where a lane loads its own).
+        const bool do_it = len > 0;
+        const int lane = tid & (kWave - 1);
+        const int ip = (ic + 1 == o.nx) ? 0 : ic + 1;
+        const int im = (ic == 0) ? o.nx - 1 : ic - 1;
+        const int jp = (j + 1 == o.ny) ? 0 : j + 1;
+        const int jm = (j == 0) ? o.ny - 1 : j - 1;
+        const size_t pc = mg_parent(mg, o.nz, ic, j, 0);
+        const size_t pxp = mg_parent(mg, o.nz, ip, j, 0), pxm = mg_parent(mg, o.nz, im, j, 0);
+        const size_t pyp = mg_parent(mg, o.nz, ic, jp, 0), pym = mg_parent(mg, o.nz, ic, jm, 0);
+        constexpr bool kShfl = C == kWave;
+        const bool needL = !kShfl || lane == 0;
+        const bool needR = !kShfl || lane == kWave - 1 || ic + 1 >= o.nx;
+        const size_t ksc = (size_t)mg.ncx;
+        auto lev = [&](int k) { return (size_t)min(max(k, 0), o.nz - 1) * ksc; };
+        double cv[L + 2], cyp[L], cym[L], cxl[L], cxr[L];
+        if (do_it) {
+#pragma unroll
+            for (int t = 0; t < L + 2; ++t)
+                cv[t] = mg.zc[pc + lev(k0 - 1 + t)];
+#pragma unroll
+            for (int t = 0; t < L; ++t) {
+                const size_t off = lev(k0 + t);
+                cyp[t] = mg.zc[pyp + off];
+                cym[t] = mg.zc[pym + off];
+                cxl[t] = needL ? mg.zc[pxm + off] : 0.0;
+                cxr[t] = needR ? mg.zc[pxp + off] : 0.0;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            double v = 0.0;
+            if (t < len && ok)
+                v = ld_s(rin + base + (size_t)(k0 + t) * ks);
+            if (do_it && t < len) {
+                const double c = cv[t + 1];
+                double xl = cxl[t], xr = cxr[t];
+                if constexpr (kShfl) {
+                    const double l_s = __shfl_up(c, 1, kWave);
+                    const double r_s = __shfl_down(c, 1, kWave);
+                    xl = needL ? xl : l_s;
+                    xr = needR ? xr : r_s;
+                }
+                const int k = k0 + t;
+                const double APz = stencil_row<double>(fc, fc.area * o.lev_a[k], o.lev_d[k], face(t), face(t + 1),
+                                                       c, xl, xr, cym[t], cyp[t], cv[t], cv[t + 2]);
+                v = v - APz;
+            }
+            rr[t] = v;
+        }
     } else {
 #pragma unroll
         for (int t = 0; t < L; ++t) {
@@ -448,25 +506,6 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         for (int t = 0; t < L; ++t)
             if (t < len)
                 st_s(rout + base + (size_t)(k0 + t) * ks, rr[t]);
-    }
-    // MG_CORR: the iterate zb (plus the coarse correction) and f at the levels
-    double zb[MG == MG_CORR ? L : 1], fv[MG == MG_CORR ? L : 1];
-    if constexpr (MG == MG_CORR) {
-        r2 = 0.0;
-#pragma unroll
-        for (int t = 0; t < L; ++t) {
-            zb[t] = 0.0;
-            fv[t] = 0.0;
-            if (t < len && ok) {
-                const size_t l = base + (size_t)(k0 + t) * ks;
-                zb[t] = ld_s(q + l);
-                if (mg.zc)
-                    zb[t] = zb[t] + mg.zc[mg_parent(mg, o.nz, ic, j, k0 + t)];
-                if (partials)
-                    fv[t] = ld_s(mg.f + l);
-            }
-            r2 += fv[t] * fv[t];
-        }
     }
 
     // Local forward sweep: pivots from the true incoming phi, z'' with zero
@@ -534,7 +573,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         for (int w = P - 1; w > s; --w)
             ztop = sh_a[w * C + c] + sh_b[w * C + c] * ztop;
 
-    double kap = 0.0;
+    double kap = 0.0, r2mg = 0.0;
     H = 1;
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
@@ -544,9 +583,17 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
             TZ zv = zp[t] + ztop * H;
             if constexpr (MG == MG_FIRST)
                 zv = (TZ)mg.omega * zv;
-            if constexpr (MG == MG_CORR) {
-                zv = zb[t] + mg.omega * zv;
-                kap += fv[t] * zv;
+            if constexpr (MG == MG_CORR || MG == MG_POST) {
+                // the iterate (plus the coarse correction) and f, loaded here,
+                // after the solve, to keep the registers of the sweep low
+                const size_t l = base + (size_t)(k0 + t) * ks;
+                double zq = ok ? ld_s(q + l) : 0.0;
+                if constexpr (MG == MG_POST)
+                    zq = zq + mg.zc[mg_parent(mg, o.nz, ic, j, k0 + t)];
+                zv = zq + mg.omega * zv;
+                const double fv = (ok && partials) ? ld_s(mg.f + l) : 0.0;
+                kap += fv * zv;
+                r2mg += fv * fv;
             } else {
                 kap += (double)rr[t] * (double)zv;
             }
@@ -555,7 +602,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         }
     }
     if (DOTS && (MG == MG_NONE || partials != nullptr)) {
-        double v[2] = {r2, kap};
+        double v[2] = {(MG == MG_CORR || MG == MG_POST) ? r2mg : r2, kap};
         double out[2];
         block_sum<2>(v, sh_red, out);
         if (tid == 0) {
@@ -597,6 +644,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     static_assert(MG == MG_NONE || (UPD != UPD_AP && std::is_same<TV, double>::value &&
                                     std::is_same<TZ, double>::value),
                   "the multigrid forms are binary64 only");
+    static_assert(MG != MG_POST || UPD == UPD_NONE, "MG_POST reads its residual as it is");
     constexpr int kSeg = kMaxThreads / kWave;
     __shared__ Pair<TZ> sh_ab[kMaxThreads];
     __shared__ double sh_red[kSeg][2];
@@ -670,6 +718,52 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
                                                   pyp[t], pv[t], pv[t + 2]);
             rr[t] = rr[t] - alpha * Ap;
         }
+    } else if constexpr (MG == MG_POST) {
+        // rr = t - A (P zc): the coarse parents of the column (levels k0-1 ..
+        // k0+L, clamped), of the i-1 / i+1 columns from the adjacent lanes
+        // (lanes 0 and 63 load theirs), and of the j-1 / j+1 columns: with
+        // fy = 2 one of those is the column's own parent, so one row is loaded.
+        // Parent rows are wave-uniform; a lane adds the byte offset of its parent.
+        const int jp = (j + 1 == o.ny) ? 0 : j + 1;
+        const int jm = (j == 0) ? o.ny - 1 : j - 1;
+        const int ie = lane == 0 ? (i == 0 ? nx - 1 : i - 1) : (i + 1 == nx ? 0 : i + 1);
+        const bool edge = lane == 0 || lane == kWave - 1;
+        const size_t ksc = (size_t)mg.ncx;
+        const unsigned pl = (unsigned)(i / mg.fx) * 8u, pe = (unsigned)(ie / mg.fx) * 8u;
+        const int J = j / mg.fy;
+        const bool om = jm / mg.fy != J, op = jp / mg.fy != J;   // neighbour rows with another parent
+        auto prow = [&](int jj) { return mg.zc + ksc * ((size_t)o.nz * (size_t)(jj / mg.fy) + (size_t)k0); };
+        const double *zcc = prow(j);
+        const double *zyo = om ? prow(jm) : prow(jp);
+        const double *zy2 = prow(jp);
+        const int kb = k0 > 0 ? -1 : 0;                      // level below, clamped
+        const int ka = k0 + L < o.nz ? L : L - 1;            // level above, clamped
+        double cc[L + 2], cy[L], ce[L];
+        cc[0] = ld_at(zcc + (ptrdiff_t)kb * (ptrdiff_t)ksc, pl);
+        cc[L + 1] = ld_at(zcc + (size_t)ka * ksc, pl);
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            rr[t] = ld_at(rin + row0 + (size_t)t * nx, cv);
+            cc[t + 1] = ld_at(zcc + (size_t)t * ksc, pl);
+            cy[t] = (om || op) ? ld_at(zyo + (size_t)t * ksc, pl) : 0.0;
+            ce[t] = edge ? ld_at(zcc + (size_t)t * ksc, pe) : 0.0;
+        }
+        const Faces fc = column_faces(o, i, j);
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            const double c = cc[t + 1];
+            const double l_s = __shfl_up(c, 1, kWave);
+            const double r_s = __shfl_down(c, 1, kWave);
+            const double xl = lane == 0 ? ce[t] : l_s;
+            const double xr = lane == kWave - 1 ? ce[t] : r_s;
+            const double ym = om ? cy[t] : c;
+            double yp = c;
+            if (op)   // wave-uniform; both rows differ only when fy = 1
+                yp = om ? ld_at(zy2 + (size_t)t * ksc, pl) : cy[t];
+            const double APz = stencil_row<double>(fc, fc.area * o.lev_a[k0 + t], o.lev_d[k0 + t], fc.area * az[t],
+                                                   fc.area * az[t + 1], c, xl, xr, ym, yp, cc[t], cc[t + 2]);
+            rr[t] = rr[t] - APz;
+        }
     } else {
 #pragma unroll
         for (int t = 0; t < L; ++t)
@@ -683,24 +777,16 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         for (int t = 0; t < L; ++t)
             st_at(rout + row0 + (size_t)t * nx, cv, rr[t]);
     }
-    // MG_CORR: the iterate zb (plus the coarse correction) and f at the levels
-    double zb[MG == MG_CORR ? L : 1], fv[MG == MG_CORR ? L : 1];
+    // MG_CORR: the iterate and f, loaded with the residual (MG_POST, whose
+    // stencil on the coarse correction holds more registers in the load
+    // phase, loads them after the solve)
+    double zb[MG == MG_CORR ? L : 1], fb[MG == MG_CORR ? L : 1];
     if constexpr (MG == MG_CORR) {
-        r2 = 0.0;
-        const size_t pb = mg.zc ? mg_parent(mg, o.nz, i, j, k0) : 0;
 #pragma unroll
         for (int t = 0; t < L; ++t) {
             zb[t] = ld_at(q + row0 + (size_t)t * nx, cv);
-            fv[t] = partials ? ld_at(mg.f + row0 + (size_t)t * nx, cv) : 0.0;
+            fb[t] = partials ? ld_at(mg.f + row0 + (size_t)t * nx, cv) : 0.0;
         }
-        if (mg.zc) {
-#pragma unroll
-            for (int t = 0; t < L; ++t)
-                zb[t] = zb[t] + mg.zc[pb + (size_t)t * mg.ncx];
-        }
-#pragma unroll
-        for (int t = 0; t < L; ++t)
-            r2 += fv[t] * fv[t];
     }
 
     // Local forward sweep: pivots from the true incoming phi, z'' with zero
@@ -755,7 +841,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         ztop = (w > s && w < P) ? nt : ztop;
     }
 
-    double kap = 0.0;
+    double kap = 0.0, r2mg = 0.0;
     H = 1;
 #pragma unroll
     for (int t = L - 1; t >= 0; --t) {
@@ -763,16 +849,29 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         TZ zv = zp[t] + ztop * H;
         if constexpr (MG == MG_FIRST)
             zv = (TZ)mg.omega * zv;
-        if constexpr (MG == MG_CORR) {
-            zv = zb[t] + mg.omega * zv;
-            kap += fv[t] * zv;
+        if constexpr (MG == MG_CORR || MG == MG_POST) {
+            // the iterate (plus the coarse correction) and f, loaded here,
+            // after the solve, to keep the registers of the sweep low
+            double zq, fv;
+            if constexpr (MG == MG_CORR) {
+                zq = zb[t];
+                fv = fb[t];
+            } else {
+                zq = ld_at(q + row0 + (size_t)t * nx, cv) +
+                     ld_at(mg.zc + (size_t)mg.ncx * ((size_t)o.nz * (size_t)(j / mg.fy) + (size_t)(k0 + t)),
+                           (unsigned)(i / mg.fx) * 8u);
+                fv = partials ? ld_at(mg.f + row0 + (size_t)t * nx, cv) : 0.0;
+            }
+            zv = zq + mg.omega * zv;
+            kap += fv * zv;
+            r2mg += fv * fv;
         } else {
             kap += (double)rr[t] * (double)zv;
         }
         st_at(z + row0 + (size_t)t * nx, cz, zv);
     }
     if (DOTS && (MG == MG_NONE || partials != nullptr)) {
-        double v[2] = {r2, kap};
+        double v[2] = {(MG == MG_CORR || MG == MG_POST) ? r2mg : r2, kap};
         double out[2];
         block_sum<2>(v, sh_red, out);
         if (threadIdx.x == 0) {
@@ -1193,10 +1292,12 @@ __global__ void k_mg_coarsen(Op o, int ncx, int ncy, int fx, int fy, double *__r
 }
 
 // Residual and restriction after the pre-smoothing sweeps: t = f - A z (kept
-// for the sweep after the coarse correction) and fc = P^T t.  A workgroup
-// owns 64 fine columns (one lane each) of the FY fine rows of one coarse row
-// J over Ws * Ls levels; tiles run k-tile fastest, then the i-tile, then J.
-// A lane computes the residual of its column in each of the FY rows; with
+// for the sweep after the coarse correction, MG_POST) and fc = P^T t.  A
+// workgroup owns 64 fine columns (one lane each) of the FY fine rows of one
+// coarse row J over Ws * Ls levels; tiles run k-tile fastest, then the
+// i-tile, then J.  A lane loads the FY rows and the rows below and above
+// them once (with FY = 2 the two middle rows are each other's neighbours),
+// computes the residual of its column in each of the FY rows, and with
 // FX = 2 the two children in i are adjacent lanes.  The children are summed
 // in the order (row outer, column inner).
 template <int Ls, int FX, int FY>
@@ -1228,41 +1329,54 @@ __global__ __launch_bounds__(kMaxThreads) void k_mg_restrict(const double *__res
     const bool needL = lane == 0;
     const bool needR = lane == kWave - 1 || ic + 1 >= o.nx;
     auto lev = [&](int k) { return (size_t)min(max(k, 0), o.nz - 1) * ks; };
+    // rows: jr[0] below, jr[1 .. FY] the children, jr[FY + 1] above
+    int jr[FY + 2];
+    jr[1] = FY * J;
+    jr[0] = jr[1] == 0 ? o.ny - 1 : jr[1] - 1;
+    if constexpr (FY == 2)
+        jr[2] = jr[1] + 1;
+    jr[FY + 1] = jr[FY] + 1 == o.ny ? 0 : jr[FY] + 1;
+    double zc[FY][Ls + 2], zo[2][Ls], ze[FY][Ls], fv[FY][Ls];
+#pragma unroll
+    for (int b = 0; b < FY; ++b) {
+        const size_t base = lin(o, ic, jr[b + 1], 0);
+        const size_t bxe = lin(o, needL ? im : ip, jr[b + 1], 0);
+#pragma unroll
+        for (int t = 0; t < Ls + 2; ++t)
+            zc[b][t] = zin[base + lev(k0 - 1 + t)];
+#pragma unroll
+        for (int t = 0; t < Ls; ++t) {
+            ze[b][t] = (needL || needR) ? zin[bxe + lev(k0 + t)] : 0.0;
+            fv[b][t] = ld_s(f + base + lev(k0 + t));
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < Ls; ++t) {
+        zo[0][t] = zin[lin(o, ic, jr[0], 0) + lev(k0 + t)];
+        zo[1][t] = zin[lin(o, ic, jr[FY + 1], 0) + lev(k0 + t)];
+    }
     double res[FY][Ls];
 #pragma unroll
     for (int b = 0; b < FY; ++b) {
-        const int j = FY * J + b;
-        const int jp = (j + 1 == o.ny) ? 0 : j + 1;
-        const int jm = (j == 0) ? o.ny - 1 : j - 1;
+        const int j = jr[b + 1];
         const Faces fcs = column_faces(o, ic, j);
         const size_t base = lin(o, ic, j, 0);
-        const size_t bxp = lin(o, ip, j, 0), bxm = lin(o, im, j, 0);
-        const size_t byp = lin(o, ic, jp, 0), bym = lin(o, ic, jm, 0);
-        double zv[Ls + 2], zyp[Ls], zym[Ls], zxl[Ls], zxr[Ls], fv[Ls];
-#pragma unroll
-        for (int t = 0; t < Ls + 2; ++t)
-            zv[t] = zin[base + lev(k0 - 1 + t)];
-#pragma unroll
-        for (int t = 0; t < Ls; ++t) {
-            const size_t off = lev(k0 + t);
-            zyp[t] = zin[byp + off];
-            zym[t] = zin[bym + off];
-            zxl[t] = needL ? zin[bxm + off] : 0.0;
-            zxr[t] = needR ? zin[bxp + off] : 0.0;
-            fv[t] = ld_s(f + base + off);
-        }
 #pragma unroll
         for (int t = 0; t < Ls; ++t) {
             const int k = min(k0 + t, o.nz - 1);
             const double lo = fcs.area * o.az[k], up = fcs.area * o.az[k + 1];
-            const double zc = zv[t + 1];
-            const double zl_s = __shfl_up(zc, 1, kWave);
-            const double zr_s = __shfl_down(zc, 1, kWave);
-            const double zl = needL ? zxl[t] : zl_s;
-            const double zr = needR ? zxr[t] : zr_s;
-            const double Az = stencil_row<double>(fcs, fcs.area * o.lev_a[k], o.lev_d[k], lo, up, zc, zl, zr,
-                                                  zym[t], zyp[t], zv[t], zv[t + 2]);
-            const double r = fv[t] - Az;
+            const double c = zc[b][t + 1];
+            const double zl_s = __shfl_up(c, 1, kWave);
+            const double zr_s = __shfl_down(c, 1, kWave);
+            // a lane that needs both sides (a grid of one column) loaded one
+            // value: the same cell either way
+            const double zl = needL ? ze[b][t] : zl_s;
+            const double zr = needR ? ze[b][t] : zr_s;
+            const double ym = b == 0 ? zo[0][t] : zc[b - 1][t + 1];
+            const double yp = b == FY - 1 ? zo[1][t] : zc[b + 1][t + 1];
+            const double Az = stencil_row<double>(fcs, fcs.area * o.lev_a[k], o.lev_d[k], lo, up, c, zl, zr,
+                                                  ym, yp, zc[b][t], zc[b][t + 2]);
+            const double r = fv[b][t] - Az;
             res[b][t] = (t < len && ok) ? r : 0.0;
             if (t < len && ok)
                 st_s(t_out + base + (size_t)(k0 + t) * ks, r);
@@ -1286,57 +1400,6 @@ __global__ __launch_bounds__(kMaxThreads) void k_mg_restrict(const double *__res
         }
         if (t < len && ok && (FX == 1 || (lane & 1) == 0))
             st_s(fc + (size_t)(i / FX) + (size_t)ncx * ((size_t)(k0 + t) + (size_t)o.nz * (size_t)J), v);
-    }
-}
-
-// After the coarse correction: w = t - A (P zc), the residual of z + P zc
-// from the residual t of z (in place: each point is read and written by the
-// same thread, with no neighbour reads of t).  P zc is the coarse parent's
-// value, so the stencil is applied to the parents of the cell and of its six
-// neighbours.  Sweep geometry of the fine level.
-template <int Ls>
-__global__ __launch_bounds__(kMaxThreads) void k_mg_prolong_resid(double *__restrict__ t, Op o, MgArgs mg,
-                                                                  const SolveState *__restrict__ st)
-{
-    if (st != nullptr && st->done)
-        return;
-    const Sweep sw = sweep_of_thread(o, Ls);
-    if (!sw.ok || sw.len <= 0)
-        return;
-    const int i = sw.i, j = sw.j, k0 = sw.k0;
-    const Faces fcs = column_faces(o, i, j);
-    const int ip = (i + 1 == o.nx) ? 0 : i + 1;
-    const int im = (i == 0) ? o.nx - 1 : i - 1;
-    const int jp = (j + 1 == o.ny) ? 0 : j + 1;
-    const int jm = (j == 0) ? o.ny - 1 : j - 1;
-    const size_t ksc = (size_t)mg.ncx;
-    const size_t pc = mg_parent(mg, o.nz, i, j, 0);
-    const size_t pxp = mg_parent(mg, o.nz, ip, j, 0), pxm = mg_parent(mg, o.nz, im, j, 0);
-    const size_t pyp = mg_parent(mg, o.nz, i, jp, 0), pym = mg_parent(mg, o.nz, i, jm, 0);
-    auto lev = [&](int k) { return (size_t)min(max(k, 0), o.nz - 1) * ksc; };
-    const size_t base = lin(o, i, j, 0);
-    double cv[Ls + 2], cxp[Ls], cxm[Ls], cyp[Ls], cym[Ls], tv[Ls];
-#pragma unroll
-    for (int q = 0; q < Ls + 2; ++q)
-        cv[q] = mg.zc[pc + lev(k0 - 1 + q)];
-#pragma unroll
-    for (int q = 0; q < Ls; ++q) {
-        const size_t off = lev(k0 + q);
-        cxp[q] = mg.zc[pxp + off];
-        cxm[q] = mg.zc[pxm + off];
-        cyp[q] = mg.zc[pyp + off];
-        cym[q] = mg.zc[pym + off];
-        tv[q] = q < sw.len ? ld_s(t + base + (size_t)(k0 + q) * o.nx) : 0.0;
-    }
-#pragma unroll
-    for (int q = 0; q < Ls; ++q) {
-        if (q < sw.len) {
-            const int k = k0 + q;
-            const double lo = fcs.area * o.az[k], up = fcs.area * o.az[k + 1];
-            const double APz = stencil_row<double>(fcs, fcs.area * o.lev_a[k], o.lev_d[k], lo, up, cv[q + 1],
-                                                   cxm[q], cxp[q], cym[q], cyp[q], cv[q], cv[q + 2]);
-            st_s(t + base + (size_t)k * o.nx, tv[q] - APz);
-        }
     }
 }
 

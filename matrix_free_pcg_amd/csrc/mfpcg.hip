@@ -1010,8 +1010,10 @@ void mg_column(pcg_handle *h, int mode, const double *rin, const double *q, doub
 {
     if (mode == MG_FIRST)
         launch_mg_column<MG_FIRST>(h, rin, q, rout, z, st, first, partials, upd, a);
-    else
+    else if (mode == MG_CORR)
         launch_mg_column<MG_CORR>(h, rin, q, rout, z, st, first, partials, upd, a);
+    else
+        launch_mg_column<MG_POST>(h, rin, q, rout, z, st, first, partials, upd, a);
 }
 
 template <int Ls>
@@ -1040,18 +1042,6 @@ void mg_restrict(pcg_handle *h, int fx, int fy, const double *f, const double *z
     }
 }
 
-// t -= A (P zc), in place.
-void mg_prolong(pcg_handle *h, double *t, const MgArgs &a, const SolveState *st)
-{
-    dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
-    switch (h->op.Ls) {
-    case 1: k_mg_prolong_resid<1><<<grid, block, 0, h->stream>>>(t, h->op, a, st); break;
-    case 2: k_mg_prolong_resid<2><<<grid, block, 0, h->stream>>>(t, h->op, a, st); break;
-    case 4: k_mg_prolong_resid<4><<<grid, block, 0, h->stream>>>(t, h->op, a, st); break;
-    default: k_mg_prolong_resid<8><<<grid, block, 0, h->stream>>>(t, h->op, a, st); break;
-    }
-}
-
 // z = B f on level l: one V(nu, nu) cycle (horizontal semi-coarsening,
 // piecewise-constant transfers, Galerkin coarse operators, the column solve
 // as damped block-Jacobi smoother).  rin is the level's right-hand side; on
@@ -1062,7 +1052,8 @@ void mg_prolong(pcg_handle *h, double *t, const MgArgs &a, const SolveState *st)
 //   first sweep   z = omega M^{-1} f
 //   sweep         w = f - A z (stencil pass), z' = z + omega M^{-1} w
 //   restriction   t = f - A z, f_c = P^T t
-//   correction    w = t - A (P z_c), z' = (z + P z_c) + omega M^{-1} w
+//   correction    z' = (z + P z_c) + omega M^{-1} (t - A P z_c), one column
+//                 pass over the buffer of t
 // On the coarsest level: the exact column solve for one column, else
 // coarse_sweeps sweeps from z = 0.
 void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const double *q, double *rout,
@@ -1104,8 +1095,7 @@ void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const 
     mg_restrict(h, fx, fy, f, cur, oth, mw.f[(size_t)l + 1], c->op.nx, st);
     mg_cycle(h0, mw, l + 1, mw.f[(size_t)l + 1], nullptr, nullptr, UPD_NONE, st, 0, nullptr);
     const MgArgs ap{mw.V[(size_t)l + 1], f, h0->mg_omega, c->op.nx, fx, fy};
-    mg_prolong(h, oth, ap, st);
-    mg_column(h, MG_CORR, oth, cur, nullptr, oth, st, 0, nu == 1 ? partials : nullptr, UPD_NONE, ap);
+    mg_column(h, MG_POST, oth, cur, nullptr, oth, st, 0, nu == 1 ? partials : nullptr, UPD_NONE, ap);
     std::swap(cur, oth);
     for (int sw = 1; sw < nu; ++sw) {
         sweep(cur, oth, sw == nu - 1 ? partials : nullptr);
