@@ -211,3 +211,56 @@ def test_mg_full_size(dev, cfg):
     print(f"cfg {cfg}: {res['iters']} steps, final {res['final_rel_res']:.2e}, true {true_rel:.2e}")
     assert res["status"] == 0 and res["iters"] <= 150, res
     assert true_rel <= 10 * wl.tol, true_rel
+
+
+def test_mg_solve_edge_cases(dev):
+    """b = 0, maxit = 0, a warm start from a seeded x0, tol = 0 (fixed steps)
+    and bitwise determinism of two runs."""
+    import torch
+    prob = W.config_problem(4, scale_xy=(64, 32), nz=16)
+    gp = as_general(prob)
+    b = W.uniform_field(64, 32, 16, 44)
+    h = mf.pcg_create(prob)
+    try:
+        mf.pcg_mg_setup(h)
+        bd = to_dev(b, dev)
+        x = torch.zeros_like(bd)
+        res = mf.pcg_solve_mg(h, torch.zeros_like(bd), x, 1e-10, 100)
+        assert res["status"] == mf.PCG_OK and res["iters"] == 0 and float(x.abs().max()) == 0.0
+        res = mf.pcg_solve_mg(h, bd, x, 1e-10, 0)
+        assert res["status"] == mf.PCG_NOT_CONVERGED and res["iters"] == 0 and len(res["hist"]) == 1
+        x0 = W.uniform_field(64, 32, 16, 45)
+        x = to_dev(x0, dev)
+        warm = mf.pcg_solve_mg(h, bd, x, 1e-10, 200)
+        assert warm["status"] == mf.PCG_OK
+        x1 = x.clone()
+        xa, xb = torch.zeros_like(bd), torch.zeros_like(bd)
+        ra = mf.pcg_solve_mg(h, bd, xa, 0.0, 7)
+        rb = mf.pcg_solve_mg(h, bd, xb, 0.0, 7)
+        torch.cuda.synchronize()
+        assert ra["status"] == rb["status"] == mf.PCG_NOT_CONVERGED and ra["iters"] == 7
+        assert torch.equal(xa, xb) and np.array_equal(ra["hist"], rb["hist"])
+        xg7, x1h = to_host(xa), to_host(x1)
+    finally:
+        mf.pcg_destroy(h)
+    # seven fixed steps against the oracle's, with the bounds of the solve
+    # comparisons: x within rel-L2 1e-9, the history within max(1e-6, 10x the
+    # oracle's spread under an ulp-level perturbation of b).  A cycle's
+    # rounding is not that of a perturbed b: the residual t = f - A z cancels
+    # terms ~1e4 times larger than itself and the coarse columns are far
+    # worse conditioned than the fine ones, so two correct cycles differ by
+    # up to a few 1e-10 relative (measured 4.6e-10 in x after 7 steps, 7.6e-8
+    # in the 7th residual norm, while the perturbed-b spread is 2e-16)
+    ref = oracle.pcg_mg(gp, b, tol=0.0, maxit=7)
+    u = np.random.default_rng(4242).uniform(-1.0, 1.0, size=b.shape)
+    sp = oracle.pcg_mg(gp, b * (1.0 + 2.0 ** -52 * u), tol=0.0, maxit=7)
+    nx_ = np.linalg.norm(ref["x"])
+    dx, sx = np.linalg.norm(xg7 - ref["x"]) / nx_, np.linalg.norm(sp["x"] - ref["x"]) / nx_
+    dh = np.max(np.abs(ra["hist"] - ref["hist"]) / ref["hist"])
+    sh = np.max(np.abs(sp["hist"] - ref["hist"]) / ref["hist"])
+    print(f"7 steps: x {dx:.2e} (oracle spread {sx:.2e}), history {dh:.2e} (spread {sh:.2e})")
+    assert dx <= max(1e-9, 10 * sx), (dx, sx)
+    assert dh <= max(1e-6, 10 * sh), (dh, sh)
+    full = oracle.pcg_mg(gp, b, x0=x0, tol=1e-10, maxit=200)
+    assert abs(warm["iters"] - full["iters"]) <= 1, (warm["iters"], full["iters"])
+    assert np.linalg.norm(x1h - full["x"]) <= 1e-9 * np.linalg.norm(full["x"])
