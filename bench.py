@@ -98,6 +98,16 @@ def mg_cycle_bytes(level_points, k, nu=1):
     return tot
 
 
+def step_class(variant, kernel, k):
+    """Launches of a pass with the same work per point: the first step, and
+    (interleaved stencil pass) odd / even steps, else the rest."""
+    if k == 0:
+        return "first"
+    if variant in ("interleaved", "f32", "mixed") and kernel == "fused_spmv":
+        return "odd" if k % 2 else "even"
+    return "rest"
+
+
 def mg_pass_bytes(level_points, iters):
     """Total algorithmic bytes and count of the timed V-cycles (k = 0..K)."""
     tot = cnt = 0

@@ -1,0 +1,55 @@
+"""The benchmark's byte models and step classes (CPU): the per-launch
+algorithmic bytes of each variant average to the documented bytes per point
+per step, and the committed counter summary is found by the traffic lookup
+when it was taken on the current kernel source."""
+import hashlib
+import json
+import os
+
+import pytest
+
+import bench
+
+N = 1024 * 1024 * 128
+
+
+@pytest.mark.parametrize("variant,per_point", [("interleaved", 84), ("interleaved_no_q", 72), ("f32", 42),
+                                               ("mixed", 76)])
+def test_steady_state_bytes(variant, per_point):
+    # two steady-state steps (one odd, one even) of both passes
+    f = bench.BYTES_BY_VARIANT[variant][0]
+    tot = sum(f(kern, k) for kern in ("fused_prec", "fused_spmv") for k in (5, 6))
+    assert tot == 2 * per_point
+
+
+def test_step_classes_and_timed_launches():
+    assert bench.step_class("interleaved", "fused_spmv", 0) == "first"
+    assert bench.step_class("interleaved", "fused_spmv", 3) == "odd"
+    assert bench.step_class("interleaved", "fused_spmv", 4) == "even"
+    assert bench.step_class("interleaved", "fused_prec", 4) == "rest"
+    # a solve of K steps times K+1 preconditioner passes and K stencil passes
+    assert len(list(bench.timed_steps("fused_prec", [10, 7]))) == 19
+    assert len(list(bench.timed_steps("fused_spmv", [10, 7]))) == 17
+    tot, cnt = bench.pass_bytes("interleaved", "fused_spmv", [3], 1)
+    assert (tot, cnt) == (24 + 40 + 64, 3)
+
+
+def test_mg_cycle_bytes():
+    pts = [N // 4 ** l for l in range(11)]          # 1024^2 x 128 down to one column
+    per = bench.mg_cycle_bytes(pts, 1) / N
+    assert 114.0 < per < 115.5
+    # level 0 alone: 32 + 24 + 32 per point and 16 per coarse point
+    assert bench.mg_cycle_bytes([N, N // 4], 1) == 88 * N + 16 * (N // 4) + 16 * (N // 4)
+    tot, cnt = bench.mg_pass_bytes(pts, [2])
+    assert cnt == 3 and tot == bench.mg_cycle_bytes(pts, 0) + 2 * bench.mg_cycle_bytes(pts, 1)
+
+
+def test_traffic_record_matches_source_or_is_ignored():
+    rec = json.load(open(bench.TRAFFIC_FILE))
+    sha = hashlib.sha256(open(bench.KERNEL_SOURCE, "rb").read()).hexdigest()
+    t = bench.measured_traffic("fused_spmv", "varying-1024x1024x128", "interleaved", [927])
+    if rec.get("source_sha256") == sha:
+        assert t is not None and 6.5e9 < t < 8.5e9
+    else:
+        assert t is None
+    assert bench.measured_traffic("fused_spmv", "other-workload", "interleaved", [927]) is None
