@@ -220,6 +220,12 @@ def cpu_baseline(w, steps, variant="interleaved"):
     (its set-up pass r0 = b - A x0, z0 = M^-1 r0 is not counted)."""
     import oracle
     from matrix_free_pcg_amd.workloads import GeneralProblem
+    cpu = _host_cpu()
+    # one core, as the pages' single-core CPU figures (affinity of this
+    # process only, restored afterwards)
+    old_aff = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    if old_aff:
+        os.sched_setaffinity(0, {min(old_aff)})
     t0 = time.perf_counter()
     if variant == "mg":
         gp = w.problem if isinstance(w.problem, GeneralProblem) else _as_general(w.problem)
@@ -237,10 +243,25 @@ def cpu_baseline(w, steps, variant="interleaved"):
         total = time.perf_counter() - t0
         per = res["loop_seconds"] / max(1, res["iters"])
         how = "timed around the step loop"
+    if old_aff:
+        os.sched_setaffinity(0, old_aff)
     return {"value": round(1.0 / per, 4), "unit": "iterations/s", "cores": 1, "kind": "oracle",
             "sample": f"{res['iters']} CG steps of the {w.name} workload (single-threaded C, "
-                      f"-O2), {how}; {total:.1f} s of CPU time in all",
-            "s_per_iteration": round(per, 3)}
+                      f"-O2, pinned to one core), {how}; {total:.1f} s of CPU time in all",
+            "s_per_iteration": round(per, 3), "host_cpu": cpu["model"], "host_nproc": cpu["nproc"]}
+
+
+def _host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "nproc": os.cpu_count()}
 
 
 def _as_general(prob):
@@ -342,9 +363,16 @@ def main():
     log(f"[bench] {w.name}: inputs generated in {time.perf_counter() - t:.1f}s")
     n = prob.n
     vdtype = np.float32 if args.variant == "f32" else np.float64
+    # outside the timed region, listed separately: host-to-device copy of b
+    # and the set-up (handle: coefficient tables and Thomas multipliers)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
     b = torch.from_numpy(w.rhs.astype(vdtype)).to(dev)
+    torch.cuda.synchronize()
+    t_h2d = time.perf_counter() - t
     x = torch.zeros_like(b)
     stream = torch.cuda.current_stream()
+    t = time.perf_counter()
     h = mf.pcg_create(prob, stream)
     tol, maxit = (1e-5 if args.variant == "f32" else w.tol), w.maxit
     if args.fixed_iterations > 0:
@@ -352,6 +380,9 @@ def main():
     level_points = None
     if args.variant == "mg":
         mf.pcg_mg_setup(h, nu=1, omega=0.8)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t
+    if args.variant == "mg":
         level_points = [mf.pcg_mg_level(h, l)[0] * mf.pcg_mg_level(h, l)[1] * prob.nz
                         for l in range(mf.pcg_mg_num_levels(h))]
         ws = torch.empty(mf.pcg_mg_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
@@ -371,11 +402,14 @@ def main():
     mf.pcg_profile_reset(h)
     mf.pcg_profile_enable(h, True)
     iters = []
+    solve_s = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        ts = time.perf_counter()
         x.zero_()
-        res = solve(h, b, x, tol, maxit, ws)
+        res = solve(h, b, x, tol, maxit, ws)   # returns after the solve has finished
+        solve_s.append(time.perf_counter() - ts)
         iters.append(res["iters"])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -426,12 +460,18 @@ def main():
     roofline = None
     if dom is not None:
         ach = kern[dom]["GBps"]
+        traffic = measured_traffic(dom, w.name, args.variant, iters)
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(dom, w.name, args.variant, iters),
+                    "traffic": traffic,
                     "traffic_unit": "bytes per launch", "kernel": dom,
                     "bytes_per_launch": round(kern[dom]["bytes_per_launch"]),
                     "avg_launch_ms": round(kern[dom]["avg_ms"], 4)}
+        if traffic is not None:
+            # counter-measured bytes (calibrated HBM read + write) over this run's launch time
+            cg = traffic / (kern[dom]["avg_ms"] * 1e-3) / 1e9
+            roofline["traffic_GBps"] = round(cg, 1)
+            roofline["traffic_frac"] = round(cg / HBM_PEAK_GBS, 4)
 
     out = {
         "metric": METRIC,
@@ -446,6 +486,9 @@ def main():
         "vs_baseline": None,
         "dtype": {"f32": "f32", "mixed": "f64 (preconditioner f32)"}.get(args.variant, "f64"),
         "s_per_solve": round(elapsed / args.steps, 4),
+        "median_s_per_solve": round(float(np.median(solve_s)), 4),
+        "setup_s": round(t_setup, 4),
+        "h2d_s": round(t_h2d, 4),
         "data": "synthetic",
         "config": {"workload": w.name, "nx": prob.nx, "ny": prob.ny, "nz": prob.nz,
                    "tol": tol, "maxit": maxit, "variant": args.variant,
