@@ -146,20 +146,31 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def kernel_source_digest(path=None) -> str:
+    """sha256 of the kernel source with // and /* */ comments removed and
+    whitespace collapsed: a counter record stays valid across comment edits
+    and is dropped once the code changes."""
+    import hashlib
+    import re
+    src = open(path or KERNEL_SOURCE, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()
+
+
 def measured_traffic(kernel: str, workload: str, variant: str, iters):
     """HBM bytes per launch of a pass from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE per dispatch, calibrated on a plain copy,
     per step class), averaged over the same launches as the timing; None when
-    that summary was taken on a different kernel source, variant or workload."""
-    import hashlib
+    that summary was taken on different kernel code, variant or workload."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        with open(KERNEL_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        digest = kernel_source_digest()
     except OSError:
         return None
-    if rec.get("source_sha256") != sha or rec.get("variant") != variant or rec.get("workload") != workload:
+    if rec.get("code_digest") != digest or rec.get("variant") != variant or rec.get("workload") != workload:
         return None
     classes = rec.get("passes", {}).get(kernel)
     if not classes:

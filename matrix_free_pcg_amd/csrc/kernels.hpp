@@ -287,7 +287,7 @@ enum : int { MG_NONE = 0, MG_FIRST = 1, MG_CORR = 2, MG_POST = 3 };
 
 struct MgArgs {
     const double *zc;   // coarse correction (coarse layout), or null
-    const double *f;    // the level's right-hand side (dot products of MG_CORR)
+    const double *f;    // the level's right-hand side (dot products of MG_CORR, MG_POST)
     double omega;       // damping of the smoother
     int ncx, fx, fy;    // coarse row length, coarsening factors in i and j
 };
@@ -850,8 +850,9 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         if constexpr (MG == MG_FIRST)
             zv = (TZ)mg.omega * zv;
         if constexpr (MG == MG_CORR || MG == MG_POST) {
-            // the iterate (plus the coarse correction) and f, loaded here,
-            // after the solve, to keep the registers of the sweep low
+            // MG_POST loads the iterate (plus the coarse correction) and f
+            // here, after the solve: its load phase holds the coarse
+            // stencil's operands
             double zq, fv;
             if constexpr (MG == MG_CORR) {
                 zq = zb[t];

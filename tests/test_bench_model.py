@@ -2,7 +2,6 @@
 algorithmic bytes of each variant average to the documented bytes per point
 per step, and the committed counter summary is found by the traffic lookup
 when it was taken on the current kernel source."""
-import hashlib
 import json
 import os
 
@@ -44,11 +43,20 @@ def test_mg_cycle_bytes():
     assert cnt == 3 and tot == bench.mg_cycle_bytes(pts, 0) + 2 * bench.mg_cycle_bytes(pts, 1)
 
 
+def test_kernel_digest_ignores_comments_only(tmp_path):
+    src = open(bench.KERNEL_SOURCE, encoding="utf-8").read()
+    p1, p2, p3 = tmp_path / "a.hpp", tmp_path / "b.hpp", tmp_path / "c.hpp"
+    p1.write_text(src)
+    p2.write_text("// a new comment\n" + src.replace("{", "{ /* note */", 1) + "\n\n")
+    p3.write_text(src.replace("kWave = 64", "kWave = 32", 1))
+    assert bench.kernel_source_digest(str(p1)) == bench.kernel_source_digest(str(p2))
+    assert bench.kernel_source_digest(str(p1)) != bench.kernel_source_digest(str(p3))
+
+
 def test_traffic_record_matches_source_or_is_ignored():
     rec = json.load(open(bench.TRAFFIC_FILE))
-    sha = hashlib.sha256(open(bench.KERNEL_SOURCE, "rb").read()).hexdigest()
     t = bench.measured_traffic("fused_spmv", "varying-1024x1024x128", "interleaved", [927])
-    if rec.get("source_sha256") == sha:
+    if rec.get("code_digest") == bench.kernel_source_digest():
         assert t is not None and 6.5e9 < t < 8.5e9
     else:
         assert t is None
