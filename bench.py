@@ -108,6 +108,25 @@ def step_class(variant, kernel, k):
     return "rest"
 
 
+# standard: the non-interleaved loop (one pass per BLAS-1 step, each fused
+# with its dot product).  Per step k >= 1: q = A p with <p,q> (read p, write
+# q: 16 B), x += alpha p with r -= alpha q and <r,r> (read x, p, r, q, write
+# x, r: 48), z = M^-1 r with <r,z> (16), p = z + beta p (read z, p, write p:
+# 24): 104 B per point per step; before the loop z = M^-1 r0 (16) and p = z
+# (16).  The passes after the last stop test are launched but return at once
+# (no bytes).  Totals per timed launch class over solves of K steps:
+def standard_bytes(kind, iters, n):
+    tot = 0
+    for K in iters:
+        if kind == "apply_A":
+            tot += 16 * K
+        elif kind == "precond":
+            tot += 16 * K
+        elif kind == "vector":
+            tot += 16 + 48 * K + 24 * max(K - 1, 0)
+    return tot * n
+
+
 def mg_pass_bytes(level_points, iters):
     """Total algorithmic bytes and count of the timed V-cycles (k = 0..K)."""
     tot = cnt = 0
@@ -444,6 +463,11 @@ def main():
                 ent["bytes_per_launch"] = tot / nl
                 ent["GBps"] = tot / (ms * 1e-3) / 1e9
                 ent["note"] = f"one V(1,1) cycle over {len(level_points)} levels: every kernel of the cycle"
+            elif args.variant == "standard" and name in ("apply_A", "precond", "vector"):
+                tot = standard_bytes(name, iters, n)
+                ent["bytes_total"] = tot
+                ent["GBps"] = tot / (ms * 1e-3) / 1e9
+                ent["note"] = "algorithmic bytes of all timed launches / their total time"
             elif has_bytes and name in ("fused_prec", "fused_spmv"):
                 tot, nl = pass_bytes(args.variant, name, iters, n)
                 if nl != cnt:
@@ -464,12 +488,20 @@ def main():
     # every timed pass's algorithmic bytes over the whole timed region
     if args.variant == "mg":
         all_bytes = pass_bytes(args.variant, "fused_spmv", iters, n)[0] + mg_pass_bytes(level_points, iters)[0]
+    elif args.variant == "standard":
+        all_bytes = sum(standard_bytes(kind, iters, n) for kind in ("apply_A", "precond", "vector"))
     else:
         all_bytes = (sum(pass_bytes(args.variant, kname, iters, n)[0] for kname in ("fused_prec", "fused_spmv"))
                      if has_bytes else None)
     dom = max((k for k in kern if "GBps" in kern[k]), key=lambda k: kern[k]["total_ms"], default=None)
     roofline = None
-    if dom is not None:
+    if dom is not None and "bytes_per_launch" not in kern[dom]:
+        # standard loop: totals per launch class
+        ach = kern[dom]["GBps"]
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "traffic_unit": "bytes per launch",
+                    "kernel": dom, "avg_launch_ms": round(kern[dom]["avg_ms"], 4)}
+    elif dom is not None:
         ach = kern[dom]["GBps"]
         traffic = measured_traffic(dom, w.name, args.variant, iters)
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -508,9 +540,10 @@ def main():
         # algorithmic bytes of both passes over the whole timed region / its wall time
         "hbm_GBps_whole_solve": round(all_bytes / elapsed / 1e9, 1) if all_bytes else None,
         "hbm_frac_whole_solve": round(all_bytes / elapsed / 1e9 / HBM_PEAK_GBS, 4) if all_bytes else None,
-        "bytes_per_point_per_iteration": (BYTES_BY_VARIANT[args.variant][1] if args.variant != "mg"
-                                          else round(52 + mg_cycle_bytes(level_points, 1) / n, 2))
-                                         if has_bytes else None,
+        "bytes_per_point_per_iteration": (104 if args.variant == "standard" else
+                                          (BYTES_BY_VARIANT[args.variant][1] if args.variant != "mg"
+                                           else round(52 + mg_cycle_bytes(level_points, 1) / n, 2))
+                                          if has_bytes else None),
         "kernels": kern,
         "roofline": roofline,
         "cpu_baseline": None,

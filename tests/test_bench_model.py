@@ -61,3 +61,12 @@ def test_traffic_record_matches_source_or_is_ignored():
     else:
         assert t is None
     assert bench.measured_traffic("fused_spmv", "other-workload", "interleaved", [927]) is None
+
+
+def test_standard_bytes():
+    # K steps: 104 B per point per step, plus 32 before the loop (z = M^-1 r0,
+    # p = z), minus the column solve and p update of step K (launched after
+    # the stop test, they return at once)
+    for K in (1, 5, 40):
+        tot = sum(bench.standard_bytes(kind, [K], 1) for kind in ("apply_A", "precond", "vector"))
+        assert tot == 104 * K + 32 - 16 - 24
