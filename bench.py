@@ -82,15 +82,18 @@ BYTES_BY_VARIANT = {"interleaved": (_bytes_interleaved, 84), "interleaved_no_q":
 #   restriction   read f, z, write t: 24 per point; write f_c: 8 per coarse point
 #   correction    read t, z (and f for the dot products on level 0), write z:
 #                 24, level 0: 32; read z_c: 8 per coarse point
-# and on a coarsest level of one column the exact column solve: 16.
-def mg_cycle_bytes(level_points, k, nu=1):
+# and on the coarsest level: one column, the exact column solve (16);
+# several, cs sweeps from z = 0 (coarse_sweeps = cs): the first 16, each
+# further one a residual pass (read f, z, write w: 24) and a corrected column
+# solve (read w, z, write z: 24).
+def mg_cycle_bytes(level_points, k, nu=1, coarse_sweeps=0):
     if nu != 1:
         raise ValueError("the byte model covers V(1,1) cycles")
     tot = 0
     for l, nl in enumerate(level_points):
         nc = level_points[l + 1] if l + 1 < len(level_points) else 0
         if nc == 0:
-            tot += 16 * nl
+            tot += (16 + 48 * max(coarse_sweeps - 1, 0)) * nl
             continue
         first = 32 if (l == 0 and k > 0) else 16
         corr = 32 if l == 0 else 24
@@ -127,12 +130,12 @@ def standard_bytes(kind, iters, n):
     return tot * n
 
 
-def mg_pass_bytes(level_points, iters):
+def mg_pass_bytes(level_points, iters, coarse_sweeps=0):
     """Total algorithmic bytes and count of the timed V-cycles (k = 0..K)."""
     tot = cnt = 0
     for K in iters:
         for k in range(K + 1):
-            tot += mg_cycle_bytes(level_points, k)
+            tot += mg_cycle_bytes(level_points, k, coarse_sweeps=coarse_sweeps)
             cnt += 1
     return tot, cnt
 
@@ -215,7 +218,11 @@ def parse():
                     choices=["interleaved", "interleaved_no_q", "standard", "f32", "mixed", "mg"],
                     help="f32: every vector in binary32, to tol 1e-5 (the workload's 1e-10 is below "
                          "binary32 rounding); mixed: binary64 with the preconditioner in binary32; "
-                         "mg: one multigrid V(1,1) cycle (omega 0.8) as the preconditioner")
+                         "mg: one multigrid V(1,1) cycle as the preconditioner (--mg-* options)")
+    ap.add_argument("--mg-omega", type=float, default=0.9, help="mg: damping of the column smoother")
+    ap.add_argument("--mg-levels", type=int, default=5,
+                    help="mg: levels of the hierarchy (0: down to one column); 5 ends at 64x64 columns at 1024^2")
+    ap.add_argument("--mg-coarse-sweeps", type=int, default=64, help="mg: sweeps on the coarsest level")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -244,7 +251,7 @@ def copy_calibration():
                       "copy_ms": dt * 1e3, "copy_GBps": 2 * n * 8 / dt / 1e9}), flush=True)
 
 
-def cpu_baseline(w, steps, variant="interleaved"):
+def cpu_baseline(w, steps, variant="interleaved", mg_params=None):
     """The CPU oracle (single thread) on a bounded sample of the same workload:
     `steps` CG steps of the full problem, timed around the oracle's step loop
     (its set-up pass r0 = b - A x0, z0 = M^-1 r0 is not counted)."""
@@ -259,7 +266,7 @@ def cpu_baseline(w, steps, variant="interleaved"):
     t0 = time.perf_counter()
     if variant == "mg":
         gp = w.problem if isinstance(w.problem, GeneralProblem) else _as_general(w.problem)
-        res = oracle.pcg_mg(gp, w.rhs, tol=0.0, maxit=steps)
+        res = oracle.pcg_mg(gp, w.rhs, tol=0.0, maxit=steps, **(mg_params or {}))
         total = time.perf_counter() - t0
         per = total / (res["iters"] + 1)
         how = "multigrid PCG, timed around the whole call, its set-up pass counted as one more step"
@@ -408,13 +415,17 @@ def main():
     if args.fixed_iterations > 0:
         tol, maxit = 0.0, args.fixed_iterations
     level_points = None
+    mg_params = None
     if args.variant == "mg":
-        mf.pcg_mg_setup(h, nu=1, omega=0.8)
+        mg_params = dict(nu=1, omega=args.mg_omega, max_levels=args.mg_levels, coarse_sweeps=args.mg_coarse_sweeps)
+        mf.pcg_mg_setup(h, **mg_params)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t
     if args.variant == "mg":
         level_points = [mf.pcg_mg_level(h, l)[0] * mf.pcg_mg_level(h, l)[1] * prob.nz
                         for l in range(mf.pcg_mg_num_levels(h))]
+        # sweeps on the coarsest level (0: one column, solved exactly)
+        mg_cs = 0 if level_points[-1] == prob.nz else mg_params["coarse_sweeps"]
         ws = torch.empty(mf.pcg_mg_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
     else:
         ws = torch.empty(mf.pcg_solve_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
@@ -457,7 +468,7 @@ def main():
             avg = ms / cnt
             ent = {"launches": cnt, "avg_ms": avg, "total_ms": ms}
             if name == "mg_vcycle":
-                tot, nl = mg_pass_bytes(level_points, iters)
+                tot, nl = mg_pass_bytes(level_points, iters, mg_cs)
                 if nl != cnt:
                     raise SystemExit(f"{name}: {cnt} timed cycles, expected {nl}")
                 ent["bytes_per_launch"] = tot / nl
@@ -487,7 +498,7 @@ def main():
     it_s = total_iters / elapsed
     # every timed pass's algorithmic bytes over the whole timed region
     if args.variant == "mg":
-        all_bytes = pass_bytes(args.variant, "fused_spmv", iters, n)[0] + mg_pass_bytes(level_points, iters)[0]
+        all_bytes = pass_bytes(args.variant, "fused_spmv", iters, n)[0] + mg_pass_bytes(level_points, iters, mg_cs)[0]
     elif args.variant == "standard":
         all_bytes = sum(standard_bytes(kind, iters, n) for kind in ("apply_A", "precond", "vector"))
     else:
@@ -536,13 +547,14 @@ def main():
         "config": {"workload": w.name, "nx": prob.nx, "ny": prob.ny, "nz": prob.nz,
                    "tol": tol, "maxit": maxit, "variant": args.variant,
                    "iterations_per_solve": iters, "status": res["status"],
-                   "final_rel_res": res["final_rel_res"], "true_rel_res": true_rel},
+                   "final_rel_res": res["final_rel_res"], "true_rel_res": true_rel,
+                   **({"mg": mg_params} if mg_params else {})},
         # algorithmic bytes of both passes over the whole timed region / its wall time
         "hbm_GBps_whole_solve": round(all_bytes / elapsed / 1e9, 1) if all_bytes else None,
         "hbm_frac_whole_solve": round(all_bytes / elapsed / 1e9 / HBM_PEAK_GBS, 4) if all_bytes else None,
         "bytes_per_point_per_iteration": (104 if args.variant == "standard" else
                                           (BYTES_BY_VARIANT[args.variant][1] if args.variant != "mg"
-                                           else round(52 + mg_cycle_bytes(level_points, 1) / n, 2))
+                                           else round(52 + mg_cycle_bytes(level_points, 1, coarse_sweeps=mg_cs) / n, 2))
                                           if has_bytes else None),
         "kernels": kern,
         "roofline": roofline,
@@ -550,7 +562,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         t = time.perf_counter()
-        out["cpu_baseline"] = cpu_baseline(w, 1 if args.variant == "mg" else args.cpu_steps, args.variant)
+        out["cpu_baseline"] = cpu_baseline(w, 1 if args.variant == "mg" else args.cpu_steps, args.variant,
+                                           mg_params)
         log(f"[bench] cpu baseline in {time.perf_counter() - t:.1f}s")
     print(json.dumps(out), flush=True)
 

@@ -70,3 +70,10 @@ def test_standard_bytes():
     for K in (1, 5, 40):
         tot = sum(bench.standard_bytes(kind, [K], 1) for kind in ("apply_A", "precond", "vector"))
         assert tot == 104 * K + 32 - 16 - 24
+
+
+def test_mg_cycle_bytes_with_coarse_sweeps():
+    pts = [N // 4 ** l for l in range(5)]            # 1024^2 down to 64^2 columns
+    base = bench.mg_cycle_bytes(pts, 1)              # coarsest treated as one exact solve
+    with_cs = bench.mg_cycle_bytes(pts, 1, coarse_sweeps=64)
+    assert with_cs - base == 48 * 63 * pts[-1]
