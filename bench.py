@@ -84,16 +84,18 @@ BYTES_BY_VARIANT = {"interleaved": (_bytes_interleaved, 84), "interleaved_no_q":
 #                 24, level 0: 32; read z_c: 8 per coarse point
 # and on the coarsest level: one column, the exact column solve (16);
 # several, cs sweeps from z = 0 (coarse_sweeps = cs): the first 16, each
-# further one a residual pass (read f, z, write w: 24) and a corrected column
-# solve (read w, z, write z: 24).
-def mg_cycle_bytes(level_points, k, nu=1, coarse_sweeps=0):
+# further one 24 (read f, z, write z: one pass forming the residual from z
+# and its neighbours), or 48 where the segments are longer than 8 levels
+# (nz > 128), which run it as a residual pass (read f, z, write w) and a
+# corrected column solve (read w, z, write z).
+def mg_cycle_bytes(level_points, k, nu=1, coarse_sweeps=0, two_pass_sweeps=False):
     if nu != 1:
         raise ValueError("the byte model covers V(1,1) cycles")
     tot = 0
     for l, nl in enumerate(level_points):
         nc = level_points[l + 1] if l + 1 < len(level_points) else 0
         if nc == 0:
-            tot += (16 + 48 * max(coarse_sweeps - 1, 0)) * nl
+            tot += (16 + (48 if two_pass_sweeps else 24) * max(coarse_sweeps - 1, 0)) * nl
             continue
         first = 32 if (l == 0 and k > 0) else 16
         corr = 32 if l == 0 else 24
@@ -130,12 +132,12 @@ def standard_bytes(kind, iters, n):
     return tot * n
 
 
-def mg_pass_bytes(level_points, iters, coarse_sweeps=0):
+def mg_pass_bytes(level_points, iters, coarse_sweeps=0, two_pass_sweeps=False):
     """Total algorithmic bytes and count of the timed V-cycles (k = 0..K)."""
     tot = cnt = 0
     for K in iters:
         for k in range(K + 1):
-            tot += mg_cycle_bytes(level_points, k, coarse_sweeps=coarse_sweeps)
+            tot += mg_cycle_bytes(level_points, k, coarse_sweeps=coarse_sweeps, two_pass_sweeps=two_pass_sweeps)
             cnt += 1
     return tot, cnt
 
@@ -426,6 +428,7 @@ def main():
                         for l in range(mf.pcg_mg_num_levels(h))]
         # sweeps on the coarsest level (0: one column, solved exactly)
         mg_cs = 0 if level_points[-1] == prob.nz else mg_params["coarse_sweeps"]
+        mg_two = prob.nz > 128   # segments longer than 8 levels: two-pass sweeps
         ws = torch.empty(mf.pcg_mg_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
     else:
         ws = torch.empty(mf.pcg_solve_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
@@ -468,7 +471,7 @@ def main():
             avg = ms / cnt
             ent = {"launches": cnt, "avg_ms": avg, "total_ms": ms}
             if name == "mg_vcycle":
-                tot, nl = mg_pass_bytes(level_points, iters, mg_cs)
+                tot, nl = mg_pass_bytes(level_points, iters, mg_cs, mg_two)
                 if nl != cnt:
                     raise SystemExit(f"{name}: {cnt} timed cycles, expected {nl}")
                 ent["bytes_per_launch"] = tot / nl
@@ -498,7 +501,8 @@ def main():
     it_s = total_iters / elapsed
     # every timed pass's algorithmic bytes over the whole timed region
     if args.variant == "mg":
-        all_bytes = pass_bytes(args.variant, "fused_spmv", iters, n)[0] + mg_pass_bytes(level_points, iters, mg_cs)[0]
+        all_bytes = (pass_bytes(args.variant, "fused_spmv", iters, n)[0]
+                     + mg_pass_bytes(level_points, iters, mg_cs, mg_two)[0])
     elif args.variant == "standard":
         all_bytes = sum(standard_bytes(kind, iters, n) for kind in ("apply_A", "precond", "vector"))
     else:
@@ -554,7 +558,8 @@ def main():
         "hbm_frac_whole_solve": round(all_bytes / elapsed / 1e9 / HBM_PEAK_GBS, 4) if all_bytes else None,
         "bytes_per_point_per_iteration": (104 if args.variant == "standard" else
                                           (BYTES_BY_VARIANT[args.variant][1] if args.variant != "mg"
-                                           else round(52 + mg_cycle_bytes(level_points, 1, coarse_sweeps=mg_cs) / n, 2))
+                                           else round(52 + mg_cycle_bytes(level_points, 1, coarse_sweeps=mg_cs,
+                                                                          two_pass_sweeps=mg_two) / n, 2))
                                           if has_bytes else None),
         "kernels": kern,
         "roofline": roofline,

@@ -206,7 +206,7 @@ typedef struct {
     int32_t nu;            /* sweeps before and after the coarse correction, 1..16 */
     double omega;          /* damping of the smoother, 0 < omega <= 1 */
     int32_t max_levels;    /* 0: as many levels as the grid allows; else 1..64 */
-    int32_t coarse_sweeps; /* sweeps on a coarsest level of several columns, 1..64 */
+    int32_t coarse_sweeps; /* sweeps on a coarsest level of several columns, 1..1024 */
 } pcg_mg_params;
 
 /* Build (or rebuild) the level hierarchy: the coarse levels' coefficient

@@ -280,10 +280,13 @@ enum : int { UPD_NONE = 0, UPD_Q = 1, UPD_AP = 2 };
 //             restriction; z = (q + P zc) + omega y: the sweep after the
 //             coarse correction, with the residual of q + P zc formed from t
 //             and the coarse correction alone (no neighbour reads of q)
+//   MG_SWEEP  with UPD_AP: rr = rin - A q with q's neighbours read here (the
+//             recomputed-product path with alpha = 1), z = q + omega y: one
+//             whole sweep in one pass; no dot products
 // P zc is the value of the coarse parent.  Binary64 only.  The dot products
 // of MG_CORR and MG_POST are <f, f> and <f, z> (f: the level's right-hand
 // side); in every MG form they are skipped when partials is null.
-enum : int { MG_NONE = 0, MG_FIRST = 1, MG_CORR = 2, MG_POST = 3 };
+enum : int { MG_NONE = 0, MG_FIRST = 1, MG_CORR = 2, MG_POST = 3, MG_SWEEP = 4 };
 
 struct MgArgs {
     const double *zc;   // coarse correction (coarse layout), or null
@@ -309,9 +312,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     static_assert((UPD != UPD_AP && !STORED) ||
                       (std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
                   "the stored-matrix and recomputed-Ap forms are binary64 only");
-    static_assert(MG == MG_NONE || (UPD != UPD_AP && !STORED && std::is_same<TV, double>::value &&
-                                    std::is_same<TZ, double>::value),
+    static_assert(MG == MG_NONE || ((UPD != UPD_AP || MG == MG_SWEEP) && !STORED &&
+                                    std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
                   "the multigrid forms are binary64 only");
+    static_assert(MG != MG_SWEEP || UPD == UPD_AP, "MG_SWEEP forms its residual on the recomputed-product path");
     static_assert(MG != MG_POST || UPD == UPD_NONE, "MG_POST reads its residual as it is");
     __shared__ TZ sh_a[kMaxThreads];
     __shared__ TZ sh_b[kMaxThreads];
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     const int len = active ? min(L, o.nz - k0) : 0;
     const size_t base = lin(o, ic, j, 0);
     const size_t ks = (size_t)o.nx;
-    const TV alpha = (UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0;
+    const TV alpha = MG == MG_SWEEP ? (TV)1 : ((UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0);
 
     // The segment's vertical face coefficients: face(t) couples levels
     // k0+t-1 and k0+t (face(0) below the segment, face(len) above it).  With
@@ -379,6 +383,12 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     TV rr[L];
     TZ iD[L], zp[L];
     double r2 = 0.0;
+    double zsw[MG == MG_SWEEP ? L : 1];   // MG_SWEEP: the iterate at the column's levels
+    if constexpr (MG == MG_SWEEP) {
+#pragma unroll
+        for (int t = 0; t < L; ++t)
+            zsw[t] = 0.0;
+    }
     if constexpr (UPD == UPD_AP) {
         // q = p; (A p) at the segment's levels.  Load phase first (r, p at
         // levels k0-1..k0+L clamped to the grid, p at j-1 and j+1; with 64
@@ -430,6 +440,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
                                                       pym[t], pyp[t], pv[t], pv[t + 2]);
                 if (ok)
                     v = v - alpha * Ap;
+                if constexpr (MG == MG_SWEEP)
+                    zsw[t] = pc;
             }
             rr[t] = v;
             r2 += v * v;
@@ -501,7 +513,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
             r2 += (double)v * (double)v;
         }
     }
-    if (UPD != UPD_NONE && !first && ok) {
+    if (MG != MG_SWEEP && UPD != UPD_NONE && !first && ok) {
 #pragma unroll
         for (int t = 0; t < L; ++t)
             if (t < len)
@@ -583,6 +595,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
             TZ zv = zp[t] + ztop * H;
             if constexpr (MG == MG_FIRST)
                 zv = (TZ)mg.omega * zv;
+            if constexpr (MG == MG_SWEEP)
+                zv = zsw[t] + mg.omega * zv;
             if constexpr (MG == MG_CORR || MG == MG_POST) {
                 // the iterate (plus the coarse correction) and f, loaded here,
                 // after the solve, to keep the registers of the sweep low
@@ -641,9 +655,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
 {
     static_assert(UPD != UPD_AP || (std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
                   "the recomputed-Ap form is binary64 only");
-    static_assert(MG == MG_NONE || (UPD != UPD_AP && std::is_same<TV, double>::value &&
+    static_assert(MG == MG_NONE || ((UPD != UPD_AP || MG == MG_SWEEP) && std::is_same<TV, double>::value &&
                                     std::is_same<TZ, double>::value),
                   "the multigrid forms are binary64 only");
+    static_assert(MG != MG_SWEEP || UPD == UPD_AP, "MG_SWEEP forms its residual on the recomputed-product path");
     static_assert(MG != MG_POST || UPD == UPD_NONE, "MG_POST reads its residual as it is");
     constexpr int kSeg = kMaxThreads / kWave;
     __shared__ Pair<TZ> sh_ab[kMaxThreads];
@@ -665,13 +680,14 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     const unsigned cv = (unsigned)i * (unsigned)sizeof(TV);   // lane's byte offset in a TV row
     const unsigned cz = (unsigned)i * (unsigned)sizeof(TZ);   // ... in a TZ row
     const size_t row0 = ((size_t)j * o.nz + k0) * nx;   // level k0 of row j (uniform)
-    const TV alpha = (UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0;
+    const TV alpha = MG == MG_SWEEP ? (TV)1 : ((UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0);
     const double *az = o.az + k0;                       // az[t]: face below level k0+t
     // area-scaled vertical couplings: vz(t) couples levels k0+t-1 and k0+t
     auto vz = [&](int t) -> TZ { return fz.area * (TZ)az[t]; };
 
     TV rr[L];
     double r2 = 0.0;
+    double zsw[MG == MG_SWEEP ? L : 1];   // MG_SWEEP: the iterate at the column's levels
     if (UPD == UPD_Q && !first) {
         TV qv[L];
 #pragma unroll
@@ -717,6 +733,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
                                                   fc.area * az[t], fc.area * az[t + 1], pc, pl, pr, pym[t],
                                                   pyp[t], pv[t], pv[t + 2]);
             rr[t] = rr[t] - alpha * Ap;
+            if constexpr (MG == MG_SWEEP)
+                zsw[t] = pc;
         }
     } else if constexpr (MG == MG_POST) {
         // rr = t - A (P zc): the coarse parents of the column (levels k0-1 ..
@@ -772,7 +790,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
 #pragma unroll
     for (int t = 0; t < L; ++t)
         r2 += (double)rr[t] * (double)rr[t];
-    if (UPD != UPD_NONE && !first) {
+    if (MG != MG_SWEEP && UPD != UPD_NONE && !first) {
 #pragma unroll
         for (int t = 0; t < L; ++t)
             st_at(rout + row0 + (size_t)t * nx, cv, rr[t]);
@@ -849,6 +867,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         TZ zv = zp[t] + ztop * H;
         if constexpr (MG == MG_FIRST)
             zv = (TZ)mg.omega * zv;
+        if constexpr (MG == MG_SWEEP)
+            zv = zsw[t] + mg.omega * zv;
         if constexpr (MG == MG_CORR || MG == MG_POST) {
             // MG_POST loads the iterate (plus the coarse correction) and f
             // here, after the solve: its load phase holds the coarse

@@ -993,7 +993,14 @@ void launch_mg_column_l(pcg_handle *h, const double *rin, const double *q, doubl
     dim3 grid(h->col_tiles), block(h->col_threads);
     const Op &o = h->op;
     const bool fused_q = MG == MG_FIRST && upd == UPD_Q;
-    if (h->col_full) {
+    if constexpr (MG == MG_SWEEP) {
+        if (h->col_full)
+            k_column_full<L, UPD_AP, true, double, double, MG_SWEEP><<<grid, block, 0, h->stream>>>(
+                rin, q, rout, z, o, st, 0, nullptr, h->d_phib, a);
+        else
+            k_column_solve<L, kWave, UPD_AP, true, false, double, double, MG_SWEEP><<<grid, block, 0, h->stream>>>(
+                rin, q, rout, z, o, st, 0, nullptr, nullptr, h->d_phib, a);
+    } else if (h->col_full) {
         if (fused_q)
             k_column_full<L, UPD_Q, true, double, double, MG_FIRST><<<grid, block, 0, h->stream>>>(
                 rin, q, rout, z, o, st, first, partials, h->d_phib, a);
@@ -1029,6 +1036,8 @@ void mg_column(pcg_handle *h, int mode, const double *rin, const double *q, doub
         launch_mg_column<MG_FIRST>(h, rin, q, rout, z, st, first, partials, upd, a);
     else if (mode == MG_CORR)
         launch_mg_column<MG_CORR>(h, rin, q, rout, z, st, first, partials, upd, a);
+    else if (mode == MG_SWEEP)
+        launch_mg_column<MG_SWEEP>(h, rin, q, rout, z, st, first, partials, upd, a);
     else
         launch_mg_column<MG_POST>(h, rin, q, rout, z, st, first, partials, upd, a);
 }
@@ -1067,7 +1076,9 @@ void mg_restrict(pcg_handle *h, int fx, int fy, const double *f, const double *z
 // (partials).  The result lands in V; after the first sweep every sweep
 // writes the buffer that does not hold the current iterate:
 //   first sweep   z = omega M^{-1} f
-//   sweep         w = f - A z (stencil pass), z' = z + omega M^{-1} w
+//   sweep         z' = z + omega M^{-1} (f - A z), one column pass reading z's
+//                 neighbours (the last sweep of level 0, which forms the dot
+//                 products: a stencil pass for w = f - A z, then the column pass)
 //   restriction   t = f - A z, f_c = P^T t
 //   correction    z' = (z + P z_c) + omega M^{-1} (t - A P z_c), one column
 //                 pass over the buffer of t
@@ -1082,6 +1093,11 @@ void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const 
     double *V = mw.V[(size_t)l], *U = mw.U[(size_t)l];
     const MgArgs a{nullptr, f, h0->mg_omega, 0, 1, 1};
     auto sweep = [&](double *cur, double *oth, double *parts) {
+        if (!parts && h->op.L <= 8) {   // one pass: the residual formed in the column kernel
+                                         // (longer segments would spill its registers)
+            mg_column(h, MG_SWEEP, f, cur, nullptr, oth, st, 0, nullptr, UPD_AP, a);
+            return;
+        }
         stencil<double, double>(h, SP_RESID, cur, f, nullptr, nullptr, oth, nullptr, nullptr);
         mg_column(h, MG_CORR, oth, cur, nullptr, oth, st, 0, parts, UPD_NONE, a);
     };
@@ -1337,8 +1353,8 @@ int pcg_mg_setup(pcg_handle *h, const pcg_mg_params *p)
         return fail(h, PCG_ERR_INVALID, "%s: omega = %g must be in (0, 1]", who, p->omega);
     if (p->max_levels < 0 || p->max_levels > 64)
         return fail(h, PCG_ERR_INVALID, "%s: max_levels = %d must be in 0..64", who, p->max_levels);
-    if (p->coarse_sweeps < 1 || p->coarse_sweeps > 64)
-        return fail(h, PCG_ERR_INVALID, "%s: coarse_sweeps = %d must be in 1..64", who, p->coarse_sweeps);
+    if (p->coarse_sweeps < 1 || p->coarse_sweeps > 1024)
+        return fail(h, PCG_ERR_INVALID, "%s: coarse_sweeps = %d must be in 1..1024", who, p->coarse_sweeps);
     if (h->op.C != kWave)
         return fail(h, PCG_ERR_UNSUPPORTED, "%s: the multigrid sweeps need 64-column column tiles", who);
     int rc = set_device(h);

@@ -75,5 +75,5 @@ def test_standard_bytes():
 def test_mg_cycle_bytes_with_coarse_sweeps():
     pts = [N // 4 ** l for l in range(5)]            # 1024^2 down to 64^2 columns
     base = bench.mg_cycle_bytes(pts, 1)              # coarsest treated as one exact solve
-    with_cs = bench.mg_cycle_bytes(pts, 1, coarse_sweeps=64)
-    assert with_cs - base == 48 * 63 * pts[-1]
+    assert bench.mg_cycle_bytes(pts, 1, coarse_sweeps=64) - base == 24 * 63 * pts[-1]
+    assert bench.mg_cycle_bytes(pts, 1, coarse_sweeps=64, two_pass_sweeps=True) - base == 48 * 63 * pts[-1]
