@@ -47,6 +47,9 @@ GRIDS = [
     ("random-1x1x7", lambda: random_general(1, 1, 7, seed=24)),
     ("random-5x3x4", lambda: random_general(5, 3, 4, seed=25)),
     ("general-64x64x128", lambda: W.general_problem(64, 64, 128, 6)),
+    # 16- and 32-level segments (nz > 128): the two-pass sweeps
+    ("general-64x8x256", lambda: W.general_problem(64, 8, 256, 6)),
+    ("random-4x4x300", lambda: random_general(4, 4, 300, seed=26)),
 ]
 PARAMS = [
     dict(nu=1, omega=0.8, max_levels=0, coarse_sweeps=2),
