@@ -19,8 +19,10 @@ field does not depend on the memory order it is stored in.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -68,13 +70,35 @@ def _cell_counters(nx: int, ny: int, nz: int, j0: int, j1: int) -> np.ndarray:
     return i + np.uint64(nx) * (j + np.uint64(ny) * k)
 
 
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def _chunked_field(nx, ny, nz, fn, rows_per_chunk=None):
+    """Fill a (ny, nz, nx) field block of rows by block of rows.  Each block
+    depends only on its own counters, so the blocks are computed by a pool of
+    threads (numpy releases the interpreter lock inside its loops) and the
+    result does not depend on the number of threads."""
     out = np.empty((ny, nz, nx), dtype=np.float64)
     if rows_per_chunk is None:
         rows_per_chunk = max(1, (1 << 22) // max(1, nx * nz))
-    for j0 in range(0, ny, rows_per_chunk):
-        j1 = min(ny, j0 + rows_per_chunk)
+    blocks = [(j0, min(ny, j0 + rows_per_chunk)) for j0 in range(0, ny, rows_per_chunk)]
+
+    def fill(blk):
+        j0, j1 = blk
         out[j0:j1] = fn(_cell_counters(nx, ny, nz, j0, j1))
+
+    nw = min(_workers(), len(blocks))
+    if nw <= 1:
+        for blk in blocks:
+            fill(blk)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(nw) as pool:
+            list(pool.map(fill, blocks))
     return out
 
 
