@@ -55,7 +55,10 @@ struct Op {
     const double *area;    // ny*nx: |T| per column
     const double *ex;      // ny*nx: edge coefficient between (i, j) and (i+1 mod nx, j)
     const double *ey;      // ny*nx: edge coefficient between (i, j) and (i, j+1 mod ny)
-    const double *phib;    // (P-1)*ny*nx: Thomas multiplier phi at k = s*L-1
+    const double *phib;    // Thomas multiplier phi at the boundaries of a table's segments
+    int pst;               // segments of the multiplier table per column segment: segment s
+                           //   starts at table boundary s*pst (a table of shorter segments
+                           //   holds every boundary of a longer segmentation too)
 };
 
 // Scalar state of one solve, in device memory (one writer: the reduce kernels).
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     // Local forward sweep: pivots from the true incoming phi, z'' with zero
     // inflow; the right-hand side rounded to TZ.
     const size_t ncol = (size_t)o.nx * o.ny;
-    TZ phi = (s > 0 && active) ? ld_s(phib_tab + (size_t)(s - 1) * ncol + (size_t)j * o.nx + ic) : (TZ)0;
+    TZ phi = (s > 0 && active) ? ld_s(phib_tab + (size_t)(s * o.pst - 1) * ncol + (size_t)j * o.nx + ic) : (TZ)0;
     TZ zpp = 0, mu = 1;
 #pragma unroll
     for (int t = 0; t < L; ++t) {
@@ -810,7 +813,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     // Local forward sweep: pivots from the true incoming phi, z'' with zero
     // inflow; the right-hand side rounded to TZ.
     const size_t ncol = (size_t)nx * o.ny;
-    TZ phi = s > 0 ? ld_s(phib + (size_t)(s - 1) * ncol + (size_t)j * nx + i) : (TZ)0;
+    TZ phi = s > 0 ? ld_s(phib + (size_t)(s * o.pst - 1) * ncol + (size_t)j * nx + i) : (TZ)0;
     TZ iD[L], zp[L];
     TZ zpp = 0, mu = 1;
 #pragma unroll

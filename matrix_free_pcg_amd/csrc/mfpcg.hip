@@ -37,6 +37,9 @@ struct pcg_handle {
     int col_tiles = 0;     // workgroups of a column pass
     int col_threads = 0;   // threads per column-pass workgroup
     bool col_full = false; // every column tile whole (nx % 64 == 0, nz % L == 0, 64 columns)
+    int colf_L = 0;        // column passes without a stored table: segment length (a multiple of L)
+    int colf_threads = 0;  // ... threads per workgroup
+    bool colf_full = false;// ... every tile whole
     int pt_tiles = 0;      // workgroups of a point pass
     bool pt_full = false;  // every sweep tile whole (nx % 64 == 0, nz % (Ws * Ls) == 0)
     size_t n = 0;          // nx*ny*nz
@@ -101,6 +104,7 @@ int env_int(const char *name, int dflt)
 
 struct Geometry {
     int L, C, Ls, Ws;
+    int Lf;   // segment length of the column passes that need no stored table (a multiple of L)
 };
 
 bool choose_geometry(int nz, Geometry *g, std::string *why)
@@ -117,6 +121,20 @@ bool choose_geometry(int nz, Geometry *g, std::string *why)
     if (l != 4 && l != 8 && l != 16 && l != 32) { *why = "MFPCG_COL_L must be 4, 8, 16 or 32"; return false; }
     if ((size_t)g->C * ((nz + l - 1) / l) > (size_t)kMaxThreads) { *why = "column workgroup exceeds 1024 threads"; return false; }
     g->L = l;
+    // Segments of 16 levels measured faster than 8 for the fused and the
+    // stand-alone column passes at nz = 32..128 (their threads keep more loads
+    // in flight; the multigrid sweeps need 8, so the table stays at L).
+    // Whole segments are preferred: nz a multiple of 8 but not 16 keeps 8.
+    int lf = env_int("MFPCG_COL_LF", 0);
+    if (lf == 0) {
+        lf = l;
+        if (l == 8 && nz >= 16 && (nz % 16 == 0 || nz % 8 != 0) &&
+            (size_t)g->C * ((nz + 15) / 16) <= (size_t)kMaxThreads)
+            lf = 16;
+    }
+    if (lf != l && lf != 2 * l && lf != 4 * l) { *why = "MFPCG_COL_LF must be 1, 2 or 4 times the segment length"; return false; }
+    if (lf > 32) { *why = "MFPCG_COL_LF must be at most 32"; return false; }
+    g->Lf = lf;
     g->Ls = env_int("MFPCG_ST_L", 4);
     if (g->Ls != 1 && g->Ls != 2 && g->Ls != 4 && g->Ls != 8) { *why = "MFPCG_ST_L must be 1, 2, 4 or 8"; return false; }
     const int need = (nz + g->Ls - 1) / g->Ls;
@@ -241,17 +259,41 @@ template <> const float *phib_of<float>(const pcg_handle *h) { return h->d_phib3
 template <typename TV, typename TZ>
 constexpr bool kBinary64 = std::is_same<TV, double>::value && std::is_same<TZ, double>::value;
 
+// Segmentation of one column pass: the operator with its segment length,
+// segment count and multiplier-table stride, and the workgroup shape.
+struct ColGeo {
+    Op o;
+    int threads;
+    bool full;
+};
+
+// The passes with a stored column matrix use the handle's segments (their
+// multiplier table is computed for them); the others use colf_L, reading
+// the handle's table at every (colf_L / L)-th boundary.
+ColGeo col_geo(const pcg_handle *h, bool stored)
+{
+    ColGeo g{h->op, h->col_threads, h->col_full};
+    if (!stored && h->colf_L != h->op.L) {
+        g.o.L = h->colf_L;
+        g.o.P = (h->op.nz + h->colf_L - 1) / h->colf_L;
+        g.o.pst = h->colf_L / h->op.L;
+        g.threads = h->colf_threads;
+        g.full = h->colf_full;
+    }
+    return g;
+}
+
 template <int L, int C, typename TV, typename TZ>
-void launch_column_lc(pcg_handle *h, const TV *rin, const TV *q, TV *rout, TZ *z,
+void launch_column_lc(pcg_handle *h, const ColGeo &g, const TV *rin, const TV *q, TV *rout, TZ *z,
                       const SolveState *st, int first, double *partials, int upd, bool dots,
                       const double *tri)
 {
-    dim3 grid(h->col_tiles), block(h->col_threads);
-    const Op &o = h->op;
+    dim3 grid(h->col_tiles), block(g.threads);
+    const Op &o = g.o;
     const TZ *phib = phib_of<TZ>(h);
     constexpr bool kD = kBinary64<TV, TZ>;
     if constexpr (C == kWave) {
-        if (!tri && h->col_full) {
+        if (!tri && g.full) {
             if (upd == UPD_Q)
                 k_column_full<L, UPD_Q, true, TV, TZ><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, phib, MgArgs{});
             else if (!dots)
@@ -291,11 +333,12 @@ void launch_column_c(pcg_handle *h, const TV *rin, const TV *q, TV *rout, TZ *z,
                      const SolveState *st, int first, double *partials, int upd, bool dots,
                      const double *tri)
 {
-    switch (h->op.L) {
-    case 4: launch_column_lc<4, C>(h, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
-    case 8: launch_column_lc<8, C>(h, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
-    case 16: launch_column_lc<16, C>(h, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
-    default: launch_column_lc<32, C>(h, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
+    const ColGeo g = col_geo(h, tri != nullptr);
+    switch (g.o.L) {
+    case 4: launch_column_lc<4, C>(h, g, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
+    case 8: launch_column_lc<8, C>(h, g, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
+    case 16: launch_column_lc<16, C>(h, g, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
+    default: launch_column_lc<32, C>(h, g, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
     }
 }
 
@@ -631,6 +674,9 @@ void init_geometry(pcg_handle *h, int nx, int ny, int nz, const Geometry &g)
     h->col_tiles = (int)(ntc * ny);
     h->col_threads = ((C * P + kWave - 1) / kWave) * kWave;
     h->col_full = C == kWave && nx % kWave == 0 && nz % L == 0 && env_int("MFPCG_COL_FULL", 1) != 0;
+    h->colf_L = g.Lf;
+    h->colf_threads = ((C * ((nz + g.Lf - 1) / g.Lf) + kWave - 1) / kWave) * kWave;
+    h->colf_full = C == kWave && nx % kWave == 0 && nz % g.Lf == 0 && env_int("MFPCG_COL_FULL", 1) != 0;
     h->pt_tiles = (int)(ntx * nkt * ny);
     h->pt_full = nx % kWave == 0 && nz % (g.Ls * g.Ws) == 0 && env_int("MFPCG_ST_FULL", 1) != 0;
     h->n = ncol * (size_t)nz;
@@ -640,6 +686,7 @@ void init_geometry(pcg_handle *h, int nx, int ny, int nz, const Geometry &g)
     h->op.L = L;
     h->op.P = P;
     h->op.C = C;
+    h->op.pst = 1;
     h->op.ntc = (int)ntc;
     h->csr.hx = nx == 1 ? 0 : (nx == 2 ? 1 : 2);
     h->csr.hy = ny == 1 ? 0 : (ny == 2 ? 1 : 2);
@@ -1297,7 +1344,7 @@ int create_coarse(pcg_handle *h, int fx, int fy, pcg_handle **out)
     pcg_handle *c = new pcg_handle();
     c->device = h->device;
     c->stream = h->stream;
-    const Geometry g{h->op.L, h->op.C, h->op.Ls, h->op.Ws};
+    const Geometry g{h->op.L, h->op.C, h->op.Ls, h->op.Ws, h->op.L};
     const int nz = h->op.nz;
     init_geometry(c, h->op.nx / fx, h->op.ny / fy, nz, g);
     int rc = alloc_tables(c, who, false);

@@ -28,7 +28,8 @@ GRIDS = [
     ("cfg2-3x1x2", lambda: W.config_problem(2, scale_xy=(3, 1), nz=2)),
     ("cfg4-64x2x33", lambda: W.config_problem(4, scale_xy=(64, 2), nz=33)),
     # whole tiles (nx a multiple of 64, nz of the segment length): the
-    # straight-line kernels, with 16, 1, 16 and 16 segments of 8, 8, 16, 32 levels
+    # straight-line kernels, with 8, 1, 16 and 16 segments of 16, 8, 16, 32
+    # levels (the first over the multiplier table of 8-level segments)
     ("cfg4-128x3x128", lambda: W.config_problem(4, scale_xy=(128, 3), nz=128)),
     ("cfg4-64x1x8", lambda: W.config_problem(4, scale_xy=(64, 1), nz=8)),
     ("cfg2-192x2x256", lambda: W.config_problem(2, scale_xy=(192, 2), nz=256)),
@@ -336,3 +337,57 @@ def test_whole_tile_kernels_match_generic(dev, monkeypatch):
         xb, hb = b[name]
         assert np.allclose(ha, hb, rtol=1e-12, atol=0), name
         assert np.linalg.norm(xa - xb) <= 1e-12 * np.linalg.norm(xb), name
+
+
+# (label, problem, segment lengths compared): nz = 64 and 128 take 16-level
+# segments over the 8-level table by default; 40 keeps 8 by default (whole
+# segments) and is forced to 16 (a ragged last segment); 200 and 130 have
+# 16-level tables and are forced to 32
+SEGMENT_CASES = [
+    ("cfg4-128x6x64", lambda: W.config_problem(4, scale_xy=(128, 6), nz=64), 8, 16),
+    ("cfg4-64x4x128", lambda: W.config_problem(4, scale_xy=(64, 4), nz=128), 8, 16),
+    ("cfg4-70x5x40", lambda: W.config_problem(4, scale_xy=(70, 5), nz=40), 8, 16),
+    ("cfg4-64x3x200", lambda: W.config_problem(4, scale_xy=(64, 3), nz=200), 16, 32),
+    ("cfg4-65x4x130", lambda: W.config_problem(4, scale_xy=(65, 4), nz=130), 16, 32),
+]
+
+
+@pytest.mark.parametrize("label,make,short,long_", SEGMENT_CASES, ids=[c[0] for c in SEGMENT_CASES])
+def test_column_segment_lengths_agree(dev, monkeypatch, label, make, short, long_):
+    """MFPCG_COL_LF (read at pcg_create) sets the segment length of the column
+    passes that use no stored matrix; longer segments start at every
+    (long/short)-th boundary of the multiplier table computed for the short
+    ones.  Same elimination either way: precond matches the oracle and the
+    first 5 steps of each solve agree to rounding."""
+    import torch
+    prob = make()
+    r = W.gaussian_field(prob.nx, prob.ny, prob.nz, 31)
+    b = W.uniform_field(prob.nx, prob.ny, prob.nz, 32)
+    ref = oracle.precond(prob, r)
+
+    def run(lf):
+        monkeypatch.setenv("MFPCG_COL_LF", str(lf))
+        h = mf.pcg_create(prob)
+        try:
+            rd = to_dev(r, dev)
+            zd = torch.full_like(rd, float("nan"))
+            mf.pcg_precond(h, rd, zd)
+            out = {"z": to_host(zd)}
+            for name, fn in SOLVERS.items():
+                bd = to_dev(b, dev)
+                xs = torch.zeros_like(bd)
+                res = fn(h, bd, xs, 0.0, 5)
+                out[name] = (to_host(xs), res["hist"])
+            torch.cuda.synchronize()
+            return out
+        finally:
+            mf.pcg_destroy(h)
+
+    a, c = run(short), run(long_)
+    for o in (a, c):
+        assert np.abs(o["z"] - ref).max() <= precond_tol(prob, ref), label
+    for name in SOLVERS:
+        xa, ha = a[name]
+        xc, hc = c[name]
+        assert np.allclose(ha, hc, rtol=1e-11, atol=0), (label, name)
+        assert np.linalg.norm(xa - xc) <= 1e-11 * np.linalg.norm(xa), (label, name)
