@@ -11,6 +11,8 @@ Prints one JSON line (see the "roofline" and "cpu_baseline" objects).
   python bench.py [--gpus 1] [--steps K] [--warmup W]
 Options for profiling helpers:
   --copy-calibration   run only a plain 1 GiB device copy (counter calibration)
+  --stream-probe       run only the streaming-bandwidth probe (lib/libmfprobe.so): the GB/s a
+                       plain kernel reaches for the solver's read/write stream mixes
   --no-cpu-baseline    skip timing the CPU oracle
 """
 from __future__ import annotations
@@ -228,6 +230,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--stream-probe", action="store_true")
     ap.add_argument("--fixed-iterations", type=int, default=0,
                     help="run exactly N CG steps per solve (tol 0) instead of solving to 1e-10")
     return ap.parse_args()
@@ -251,6 +254,60 @@ def copy_calibration():
     dt = (time.perf_counter() - t) / reps
     print(json.dumps({"copy_bytes_read": n * 8, "copy_bytes_written": n * 8,
                       "copy_ms": dt * 1e3, "copy_GBps": 2 * n * 8 / dt / 1e9}), flush=True)
+
+
+# (reads, writes, pass it stands for)
+PROBE_MIXES = [(1, 1, "copy"), (2, 1, "residual r = b - A x"), (2, 2, "column pass (r, q -> r, z)"),
+               (3, 2, "stencil pass, odd steps (z, p, q -> p, q)"),
+               (5, 3, "stencil pass, even steps (z, p, q, x, p' -> p, q, x)")]
+
+
+def stream_probe(n=1 << 27, reps=20):
+    """GB/s of a plain streaming kernel (every element read / written once,
+    loads batched before stores) for each stream mix of the solver's passes,
+    with non-temporal and with ordinary loads and stores, on vectors of n
+    float64 (1 GiB at the default): the best over 1, 2, 4 or 8 elements per
+    thread and 256- or 1024-thread workgroups.  The solver's passes add what a
+    stream kernel does not have (neighbour reads, the column recurrences), so
+    these rates are the measured ceiling for each mix, beside the published
+    peak."""
+    import ctypes
+    import torch
+    from matrix_free_pcg_amd import build as hipbuild
+    if not os.path.exists(hipbuild.PROBE_LIB):
+        raise SystemExit(f"{hipbuild.PROBE_LIB} is not built (python -m matrix_free_pcg_amd.build)")
+    lib = ctypes.CDLL(hipbuild.PROBE_LIB)
+    lib.mfprobe_stream.restype = ctypes.c_int
+    lib.mfprobe_stream.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_int64,
+                                   ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                   ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
+    vec = [torch.full((n,), 1.0 + k, dtype=torch.float64, device="cuda") for k in range(8)]
+    torch.cuda.synchronize()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = []
+    for r, w, what in PROBE_MIXES:
+        ins = (ctypes.c_void_p * r)(*[vec[k].data_ptr() for k in range(r)])
+        outs = (ctypes.c_void_p * w)(*[vec[5 + k].data_ptr() for k in range(w)])
+        row = {"reads": r, "writes": w, "stands_for": what}
+        for nt in (1, 0):
+            best = None
+            for elems in (1, 2, 4, 8):
+                for block in (256, 1024):
+                    ms = ctypes.c_double(0.0)
+                    rc = lib.mfprobe_stream(r, w, nt, elems, block, n, ins, outs, reps, stream, ctypes.byref(ms))
+                    if rc != 0:
+                        raise SystemExit(f"mfprobe_stream({r}, {w}, nt={nt}, {elems}, {block}) returned {rc}")
+                    gbps = (r + w) * n * 8 / (ms.value * 1e-3) / 1e9
+                    if best is None or gbps > best[0]:
+                        best = (gbps, elems, block)
+            key = "nontemporal" if nt else "ordinary"
+            row[key + "_GBps"] = round(best[0], 1)
+            row[key + "_shape"] = f"{best[1]} elements x {best[2]} threads"
+        out.append(row)
+        print(json.dumps(row), flush=True)
+    torch.cuda.synchronize()
+    print(json.dumps({"stream_probe": out, "vector_bytes": n * 8, "reps": reps}), flush=True)
 
 
 def cpu_baseline(w, steps, variant="interleaved", mg_params=None):
@@ -383,6 +440,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.stream_probe:
+        stream_probe()
         return
 
     if args.config == 5:

@@ -2,7 +2,9 @@
 
 The library is a plain shared object with a C ABI (include/mfpcg.h); the
 Python binding loads it with ctypes.  Building writes
-``matrix_free_pcg_amd/lib/libmfpcg.so`` in the source tree.
+``matrix_free_pcg_amd/lib/libmfpcg.so`` in the source tree, and
+``lib/libmfprobe.so``, the streaming-bandwidth probe that bench.py
+--stream-probe runs (a measurement tool, not part of the solver).
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmfpcg.so")
 SOURCES = [os.path.join(CSRC, "mfpcg.hip")]
+PROBE_SRC = os.path.join(CSRC, "stream_probe.hip")
+PROBE_LIB = os.path.join(LIBDIR, "libmfprobe.so")
 DEPENDS = SOURCES + [os.path.join(CSRC, "kernels.hpp"), os.path.join(INCLUDE, "mfpcg.h")]
 
 ARCH = os.environ.get("MFPCG_OFFLOAD_ARCH", "gfx950")
@@ -42,15 +46,20 @@ def hipcc() -> str:
     raise FileNotFoundError("hipcc not found (ROCm is required to build libmfpcg.so)")
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile every HIP source into LIB (always recompiles)."""
-    os.makedirs(LIBDIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-o", tmp, *SOURCES]
+def _compile(sources, out, verbose, extra):
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile the library into LIB and the probe into PROBE_LIB (always recompiles)."""
+    os.makedirs(LIBDIR, exist_ok=True)
+    _compile(SOURCES, LIB, verbose, extra)
+    _compile([PROBE_SRC], PROBE_LIB, verbose, extra)
     return LIB
 
 

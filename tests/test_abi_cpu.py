@@ -170,3 +170,27 @@ def test_mg_entry_points_reject_null_handle(lib):
     assert lib.pcg_mg_workspace_bytes(None, 10) == 0
     assert lib.pcg_mg_vcycle(None, None, None, None, 0) == _abi.PCG_ERR_INVALID
     assert lib.pcg_solve_mg(None, None, None, 1e-8, 10, None, 0, None, None, None, None) == _abi.PCG_ERR_INVALID
+
+
+def test_stream_probe_rejects_bad_arguments():
+    """The bandwidth probe that bench.py --stream-probe loads (a measurement
+    tool beside the solver) rejects invalid stream counts and sizes on the host
+    (return -1, nothing launched)."""
+    if not os.path.exists(hipbuild.PROBE_LIB):
+        hipbuild.build()
+    probe = ctypes.CDLL(hipbuild.PROBE_LIB)
+    f = probe.mfprobe_stream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                  ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
+    ins = (ctypes.c_void_p * 5)(*([ctypes.c_void_p(4096)] * 5))
+    outs = (ctypes.c_void_p * 3)(*([ctypes.c_void_p(8192)] * 3))
+    ms = ctypes.c_double(0.0)
+    for r, w, e, b, n, reps in [(0, 1, 4, 256, 1024, 1), (6, 1, 4, 256, 1024, 1), (1, 0, 4, 256, 1024, 1),
+                                (1, 4, 4, 256, 1024, 1), (1, 1, 3, 256, 1024, 1), (1, 1, 4, 100, 1024, 1),
+                                (1, 1, 4, 2048, 8192, 1), (1, 1, 4, 256, 1000, 1), (1, 1, 4, 256, 0, 1),
+                                (1, 1, 4, 256, 1024, 0)]:
+        assert f(r, w, 1, e, b, n, ins, outs, reps, None, ctypes.byref(ms)) == -1, (r, w, e, b, n, reps)
+    nulls = (ctypes.c_void_p * 5)()
+    assert f(2, 1, 1, 4, 256, 1024, nulls, outs, 1, None, ctypes.byref(ms)) == -1
