@@ -56,6 +56,8 @@ struct Op {
     const double *ex;      // ny*nx: edge coefficient between (i, j) and (i+1 mod nx, j)
     const double *ey;      // ny*nx: edge coefficient between (i, j) and (i, j+1 mod ny)
     const double *phib;    // Thomas multiplier phi at the boundaries of a table's segments
+    int jt;                // sweep passes: rows per tile (1: the waves split the levels; > 1:
+                           //   wave w takes row j0 + w, Ws = jt, nkt = nz / Ls)
     int pst;               // segments of the multiplier table per column segment: segment s
                            //   starts at table boundary s*pst (a table of shorter segments
                            //   holds every boundary of a longer segmentation too)
@@ -985,22 +987,32 @@ struct Sweep {
 };
 
 // Wave w of the workgroup sweeps levels [k0, k0 + len) of column i of row j.
+// JT = 1: the tile is one row, its waves split the levels; JT > 1: the tile is
+// JT rows of Ls levels, wave w takes row j0 + w (o.jt = JT, o.ny % JT == 0).
+template <int JT = 1>
 __device__ __forceinline__ Sweep sweep_of_thread(const Op &o, int Ls)
 {
     Sweep sw;
     sw.tile = tile_of_block(blockIdx.x, gridDim.x);
     // strip g holds i-tiles [g*sg, g*sg + gw); the last strip may be narrower
-    const int per_strip = o.sg * o.ny * o.nkt;
+    const int nj = JT > 1 ? o.ny / JT : o.ny;
+    const int per_strip = o.sg * nj * o.nkt;
     const int g = sw.tile / per_strip;
     const int rem = sw.tile - g * per_strip;
     const int gw = min(o.sg, o.ntx - g * o.sg);
     const int kt = rem % o.nkt;
     const int r = rem / o.nkt;
-    sw.j = r / gw;
-    const int it = g * o.sg + (r - sw.j * gw);
+    const int jb = r / gw;
+    const int it = g * o.sg + (r - jb * gw);
     sw.i = it * kWave + (threadIdx.x & (kWave - 1));
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    sw.k0 = (kt * o.Ws + w) * Ls;
+    if constexpr (JT > 1) {
+        sw.j = jb * JT + w;
+        sw.k0 = kt * Ls;
+    } else {
+        sw.j = jb;
+        sw.k0 = (kt * o.Ws + w) * Ls;
+    }
     sw.len = max(0, min(Ls, o.nz - sw.k0));
     sw.ok = sw.i < o.nx;
     sw.ic = sw.ok ? sw.i : o.nx - 1;
@@ -1034,7 +1046,11 @@ enum : int {
 // FULL: every tile is whole (nx a multiple of 64, nz a multiple of Ws * Ls),
 // so no level or column guard is needed and the two edge lanes of a wave load
 // their outside neighbours (i-1 for lane 0, i+1 for lane 63) with one load.
-template <int Ls, int MODE, bool FULL, typename TV = double, typename TI = double>
+// JT > 1 (whole tiles only): a tile is JT rows of Ls levels, one wave per row;
+// each wave puts its z rows in LDS and takes z at j-1 and j+1 from the waves
+// of the rows beside it, so only the tile's first and last waves load a
+// neighbour row from memory.
+template <int Ls, int MODE, bool FULL, typename TV = double, typename TI = double, int JT = 1>
 __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ zin,
                                                          const TV *__restrict__ bvec,
                                                          TV *__restrict__ u,
@@ -1047,6 +1063,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
     static_assert((MODE != SP_FIRST_AP && MODE != SP_FUSED_AP) ||
                       (std::is_same<TV, double>::value && std::is_same<TI, double>::value),
                   "the q-free forms are binary64 only");
+    static_assert(JT == 1 || (FULL && MODE != SP_FIRST_AP && MODE != SP_FUSED_AP),
+                  "row tiles: whole tiles, one operand");
     __shared__ double sh_red[kMaxThreads / kWave][1];
     TV alpha = 0, beta = 0;
     bool fixup_only = false;
@@ -1070,7 +1088,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
         if (kX2)
             alpha_prev = (TV)st->alpha_prev;
     }
-    const Sweep sw = sweep_of_thread(o, Ls);
+    const Sweep sw = sweep_of_thread<JT>(o, Ls);
     const size_t ks = (size_t)o.nx;
     const size_t base = lin(o, sw.ic, sw.j, 0);
 
@@ -1111,6 +1129,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
         const bool needR = FULL ? lane == kWave - 1 : (lane == kWave - 1 || sw.ic + 1 >= o.nx);
         const size_t bxe = needL ? bxm : bxp;   // FULL: the edge lanes' outside neighbour
         auto lev = [&](int k) { return (size_t)min(max(k, 0), o.nz - 1) * ks; };
+        const int wj = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // JT > 1: the tile's row
 
         // Load phase: every value of the wave's Ls levels is requested before
         // any is used, so a wave waits for one memory round trip, not Ls.
@@ -1128,8 +1147,14 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
 #pragma unroll
         for (int t = 0; t < Ls; ++t) {
             const size_t off = lev(k0 + t);
-            zyp[t] = (TV)zin[byp + off];
-            zym[t] = (TV)zin[bym + off];
+            if constexpr (JT > 1) {
+                // rows j +- 1 inside the tile come from LDS below
+                zyp[t] = wj == JT - 1 ? (TV)zin[byp + off] : (TV)0;
+                zym[t] = wj == 0 ? (TV)zin[bym + off] : (TV)0;
+            } else {
+                zyp[t] = (TV)zin[byp + off];
+                zym[t] = (TV)zin[bym + off];
+            }
             if constexpr (FULL) {
                 zxl[t] = (needL || needR) ? (TV)zin[bxe + off] : (TV)0;
                 zxr[t] = zxl[t];
@@ -1158,6 +1183,20 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
                 qo[t] = ld_s(y + base + off);
             if constexpr (MODE == SP_RESID)
                 qo[t] = ld_s(bvec + base + off);
+        }
+        if constexpr (JT > 1) {
+            __shared__ TV sh_z[JT][Ls][kWave];   // each wave's z rows
+#pragma unroll
+            for (int t = 0; t < Ls; ++t)
+                sh_z[wj][t][lane] = zv[t + 1];
+            __syncthreads();
+#pragma unroll
+            for (int t = 0; t < Ls; ++t) {
+                if (wj > 0)
+                    zym[t] = sh_z[wj - 1][t][lane];
+                if (wj < JT - 1)
+                    zyp[t] = sh_z[wj + 1][t][lane];
+            }
         }
 
         // Compute phase.

@@ -42,6 +42,8 @@ struct pcg_handle {
     bool colf_full = false;// ... every tile whole
     int pt_tiles = 0;      // workgroups of a point pass
     bool pt_full = false;  // every sweep tile whole (nx % 64 == 0, nz % (Ws * Ls) == 0)
+    int st_jt = 4;         // sweep passes on whole tiles: rows per tile of the fused passes
+                           //   (1: one row; the operator-only passes then take 2)
     size_t n = 0;          // nx*ny*nz
     double *d_az = nullptr, *d_phib = nullptr;
     double *d_coef = nullptr;         // lev_a, lev_d (nz each), area, ex, ey (ny*nx each)
@@ -393,17 +395,65 @@ void launch_stencil_f(pcg_handle *h, const Op &o, int mode, const TI *zin, const
     }
 }
 
+// Whole tiles of JT rows x Ls levels, one wave per row (k_stencil with JT).
+template <int Ls, int JT, typename TV, typename TI>
+void launch_stencil_jt(pcg_handle *h, const Op &o, int mode, const TI *zin, const TV *b, TV *u, TV *p,
+                       TV *y, const SolveState *st, double *partials, TV *p_out)
+{
+    constexpr bool kSame = std::is_same<TV, TI>::value;
+    dim3 grid(h->pt_tiles), block(kWave * JT);
+    if constexpr (Ls == 4) {   // the fused passes
+        switch (mode) {
+        case SP_FIRST: k_stencil<Ls, SP_FIRST, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+        case SP_FUSED_NOX: k_stencil<Ls, SP_FUSED_NOX, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+        case SP_FUSED_X2: k_stencil<Ls, SP_FUSED_X2, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+        default: break;
+        }
+    } else if constexpr (kSame) {   // the operator-only passes
+        switch (mode) {
+        case SP_APPLY: k_stencil<Ls, SP_APPLY, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+        case SP_RESID: k_stencil<Ls, SP_RESID, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+        case SP_APPLY_DOT: k_stencil<Ls, SP_APPLY_DOT, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+        default: break;
+        }
+    }
+}
+
 // The passes that apply the operator alone (y = A x, q = A p with <p,q>,
 // r = b - A x) move one stream in and one out; with 4 levels per wave they
 // are latency-bound, so they sweep 8 levels per wave with half the waves
 // (the same tiles, so the same partial sums and tile order): 13 % faster at
 // 1024 x 1024 x 128.
+// Row tiles (st_jt > 1, whole tiles, 4 waves): the same number of tiles
+// (JT rows x Ls levels against one row x Ws * Ls levels), so the same partial
+// count; the fused passes take 4 rows x 4 levels (ny a multiple of 4), the
+// operator-only ones 2 x 8 (ny even).  The rows j +- 1 inside a tile come
+// through LDS instead of the L2: the fused pass 1.222 -> 1.170 ms and
+// y = A x 0.541 -> 0.475 ms at 1024 x 1024 x 128.
 template <int Ls, typename TV, typename TI>
 void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, TV *p, TV *y,
                     const SolveState *st, double *partials, TV *p_out)
 {
     if constexpr (Ls == 4) {
         const bool op_only = mode == SP_APPLY || mode == SP_APPLY_DOT || mode == SP_RESID;
+        const bool fused_rows = mode == SP_FIRST || mode == SP_FUSED_NOX || mode == SP_FUSED_X2;
+        if (h->st_jt > 1 && h->pt_full && h->op.Ws == 4) {
+            Op o2 = h->op;
+            if (fused_rows && h->op.ny % 4 == 0) {
+                o2.jt = 4;
+                o2.nkt = h->op.nz / 4;
+                launch_stencil_jt<4, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+                return;
+            }
+            if (op_only && h->op.ny % 2 == 0) {
+                o2.Ls = 8;
+                o2.Ws = 2;
+                o2.jt = 2;
+                o2.nkt = h->op.nz / 8;
+                launch_stencil_jt<8, 2>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+                return;
+            }
+        }
         if (op_only && h->op.Ws % 2 == 0) {
             Op o2 = h->op;
             o2.Ls = 8;
@@ -679,6 +729,7 @@ void init_geometry(pcg_handle *h, int nx, int ny, int nz, const Geometry &g)
     h->colf_full = C == kWave && nx % kWave == 0 && nz % g.Lf == 0 && env_int("MFPCG_COL_FULL", 1) != 0;
     h->pt_tiles = (int)(ntx * nkt * ny);
     h->pt_full = nx % kWave == 0 && nz % (g.Ls * g.Ws) == 0 && env_int("MFPCG_ST_FULL", 1) != 0;
+    h->st_jt = env_int("MFPCG_ST_JT", 4) == 1 ? 1 : 4;   // MFPCG_ST_JT=1: one-row tiles (see launch_stencil)
     h->n = ncol * (size_t)nz;
     h->op.nx = nx;
     h->op.ny = ny;
@@ -687,6 +738,7 @@ void init_geometry(pcg_handle *h, int nx, int ny, int nz, const Geometry &g)
     h->op.P = P;
     h->op.C = C;
     h->op.pst = 1;
+    h->op.jt = 1;
     h->op.ntc = (int)ntc;
     h->csr.hx = nx == 1 ? 0 : (nx == 2 ? 1 : 2);
     h->csr.hy = ny == 1 ? 0 : (ny == 2 ? 1 : 2);

@@ -56,3 +56,21 @@ def precond_tol(prob, z_ref):
     """Both sides run a backward-stable elimination of each column matrix;
     their difference is bounded by 64 eps cond(M_T) ||z||_inf."""
     return 64 * EPS * column_cond_bound(prob) * np.abs(z_ref).max()
+
+
+def gen_scale(gp, x):
+    """Bound on the sum of the term magnitudes of the general stencil in any
+    cell, |T| a + d (sum of the cell's edges) + 4 |T| beta, times ||x||_inf."""
+    T = gp.area
+    hor = gp.d.max() * (gp.alpha_x + np.roll(gp.alpha_x, 1, axis=1) + gp.alpha_y + np.roll(gp.alpha_y, 1, axis=0)).max()
+    return (T.max() * gp.a.max() + hor + 4 * T.max() * gp.beta_face.max()) * np.abs(x).max()
+
+
+def gen_column_cond(gp):
+    """Gershgorin bound of the condition number of the general operator's
+    column matrices."""
+    aT = gp.alpha_x + np.roll(gp.alpha_x, 1, axis=1) + gp.alpha_y + np.roll(gp.alpha_y, 1, axis=0)
+    lo = (gp.area[:, None, :] * gp.a[None, :, None] + gp.d[None, :, None] * aT[:, None, :]).min()
+    vert = gp.beta_face[:-1] + gp.beta_face[1:]
+    hi = (gp.area[:, None, :] * (gp.a + 2 * vert)[None, :, None] + gp.d[None, :, None] * aT[:, None, :]).max()
+    return hi / lo

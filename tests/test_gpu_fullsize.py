@@ -210,7 +210,7 @@ def test_general_full_size(dev):
     stencil and column solve against the oracle, and the full solve's true
     residual evaluated by the oracle's general stencil."""
     import torch
-    from test_gpu_general import gen_column_cond, gen_scale
+    from gpu_helpers import gen_column_cond, gen_scale
     t = time.time()
     w = W.make_workload(6)
     gp = w.problem

@@ -15,7 +15,7 @@ import pytest
 
 import matrix_free_pcg_amd as mf
 import oracle
-from gpu_helpers import EPS, require_gpu, to_dev, to_host
+from gpu_helpers import EPS, gen_column_cond, gen_scale, require_gpu, to_dev, to_host
 from matrix_free_pcg_amd import workloads as W
 from oracle_pins import dense_from_apply_gen, random_general
 
@@ -36,20 +36,6 @@ GRIDS = [
     ("random-2x2x2", lambda: random_general(2, 2, 2, seed=3)),
     ("random-64x2x512", lambda: random_general(64, 2, 512, seed=4)),
 ]
-
-
-def gen_scale(gp, x):
-    T = gp.area
-    hor = gp.d.max() * (gp.alpha_x + np.roll(gp.alpha_x, 1, axis=1) + gp.alpha_y + np.roll(gp.alpha_y, 1, axis=0)).max()
-    return (T.max() * gp.a.max() + hor + 4 * T.max() * gp.beta_face.max()) * np.abs(x).max()
-
-
-def gen_column_cond(gp):
-    aT = gp.alpha_x + np.roll(gp.alpha_x, 1, axis=1) + gp.alpha_y + np.roll(gp.alpha_y, 1, axis=0)
-    lo = (gp.area[:, None, :] * gp.a[None, :, None] + gp.d[None, :, None] * aT[:, None, :]).min()
-    vert = gp.beta_face[:-1] + gp.beta_face[1:]
-    hi = (gp.area[:, None, :] * (gp.a + 2 * vert)[None, :, None] + gp.d[None, :, None] * aT[:, None, :]).max()
-    return hi / lo
 
 
 @pytest.mark.parametrize("label,make", GRIDS, ids=[g[0] for g in GRIDS])

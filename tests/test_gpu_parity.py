@@ -9,7 +9,7 @@ import pytest
 
 import matrix_free_pcg_amd as mf
 import oracle
-from gpu_helpers import apply_tol, precond_tol, require_gpu, to_dev, to_host
+from gpu_helpers import apply_tol, gen_scale, precond_tol, require_gpu, to_dev, to_host
 from matrix_free_pcg_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -391,3 +391,60 @@ def test_column_segment_lengths_agree(dev, monkeypatch, label, make, short, long
         xc, hc = c[name]
         assert np.allclose(ha, hc, rtol=1e-11, atol=0), (label, name)
         assert np.linalg.norm(xa - xc) <= 1e-11 * np.linalg.norm(xa), (label, name)
+
+
+# grids of whole tiles: ny a multiple of 4 (row tiles in every stencil pass),
+# ny = 6 (in the operator-only passes only), a general operator
+ROW_TILE_CASES = [
+    ("cfg4-128x24x64", lambda: W.config_problem(4, scale_xy=(128, 24), nz=64)),
+    ("cfg4-64x6x32", lambda: W.config_problem(4, scale_xy=(64, 6), nz=32)),
+    ("general-64x8x48", lambda: W.general_problem(64, 8, 48, 6)),
+]
+
+
+@pytest.mark.parametrize("label,make", ROW_TILE_CASES, ids=[c[0] for c in ROW_TILE_CASES])
+def test_row_tiles_match_one_row_tiles(dev, monkeypatch, label, make):
+    """On whole tiles the stencil passes take tiles of several rows j whose
+    waves pass z through LDS (default); MFPCG_ST_JT=1 (read at pcg_create)
+    takes one-row tiles.  Same stencil: apply_A matches the oracle either way
+    and the first 5 steps of every solve agree to rounding (the dot products'
+    per-tile partial sums group differently)."""
+    import torch
+    prob = make()
+    general = isinstance(prob, W.GeneralProblem)
+    x = W.uniform_field(prob.nx, prob.ny, prob.nz, 41)
+    b = W.uniform_field(prob.nx, prob.ny, prob.nz, 42)
+    ref = oracle.apply_A_gen(prob, x) if general else oracle.apply_A(prob, x)
+
+    def run(jt):
+        monkeypatch.setenv("MFPCG_ST_JT", str(jt))
+        h = mf.pcg_create(prob)
+        try:
+            xd = to_dev(x, dev)
+            yd = torch.full_like(xd, float("nan"))
+            mf.pcg_apply_A(h, xd, yd)
+            out = {"y": to_host(yd)}
+            for name, fn in SOLVERS.items():
+                bd = to_dev(b, dev)
+                xs = torch.zeros_like(bd)
+                res = fn(h, bd, xs, 0.0, 5)
+                out[name] = (to_host(xs), res["hist"])
+            torch.cuda.synchronize()
+            return out
+        finally:
+            mf.pcg_destroy(h)
+
+    a, c = run(4), run(1)
+    for o in (a, c):
+        assert np.isfinite(o["y"]).all()
+    if general:
+        tol = 16 * np.finfo(float).eps * gen_scale(prob, x)
+    else:
+        tol = apply_tol(prob, x)
+    assert np.abs(a["y"] - ref).max() <= tol, label
+    assert np.abs(c["y"] - ref).max() <= tol, label
+    for name in SOLVERS:
+        xa, ha = a[name]
+        xc, hc = c[name]
+        assert np.allclose(ha, hc, rtol=1e-11, atol=0), (label, name)
+        assert np.linalg.norm(xa - xc) <= 1e-11 * np.linalg.norm(xc), (label, name)
