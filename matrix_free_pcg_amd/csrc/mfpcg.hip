@@ -42,8 +42,9 @@ struct pcg_handle {
     bool colf_full = false;// ... every tile whole
     int pt_tiles = 0;      // workgroups of a point pass
     bool pt_full = false;  // every sweep tile whole (nx % 64 == 0, nz % (Ws * Ls) == 0)
-    int st_jt = 4;         // sweep passes on whole tiles: rows per tile of the fused passes
-                           //   (1: one row; the operator-only passes then take 2)
+    int st_jt = 0;         // sweep passes on whole tiles: rows per tile of the fused passes
+                           //   (0: 4 in binary64, 8 in binary32; 1: one row, and the
+                           //   operator-only passes then take one row too)
     size_t n = 0;          // nx*ny*nz
     double *d_az = nullptr, *d_phib = nullptr;
     double *d_coef = nullptr;         // lev_a, lev_d (nz each), area, ex, ey (ny*nx each)
@@ -401,7 +402,7 @@ void launch_stencil_jt(pcg_handle *h, const Op &o, int mode, const TI *zin, cons
                        TV *y, const SolveState *st, double *partials, TV *p_out)
 {
     constexpr bool kSame = std::is_same<TV, TI>::value;
-    dim3 grid(h->pt_tiles), block(kWave * JT);
+    dim3 grid((unsigned)((size_t)o.ntx * o.nkt * (o.ny / JT))), block(kWave * JT);
     if constexpr (Ls == 4) {   // the fused passes
         switch (mode) {
         case SP_FIRST: k_stencil<Ls, SP_FIRST, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
@@ -430,6 +431,26 @@ void launch_stencil_jt(pcg_handle *h, const Op &o, int mode, const TI *zin, cons
 // operator-only ones 2 x 8 (ny even).  The rows j +- 1 inside a tile come
 // through LDS instead of the L2: the fused pass 1.222 -> 1.170 ms and
 // y = A x 0.541 -> 0.475 ms at 1024 x 1024 x 128.
+// Rows per tile of the fused stencil passes (SP_FIRST, SP_FUSED_NOX,
+// SP_FUSED_X2) on this handle, 0 when they take one-row tiles.  Measured at
+// 1024 x 1024 x 128: 4 rows best in binary64 and the mixed solve (8 rows:
+// 1.2 % and 6 % slower), 8 rows in binary32 (2.5 % faster than 4).
+int fused_rows_jt(const pcg_handle *h, bool binary32)
+{
+    const Op &o = h->op;
+    const int jt = h->st_jt ? h->st_jt : (binary32 ? 8 : 4);
+    return jt > 1 && h->pt_full && o.Ls == 4 && o.Ws == 4 && o.ny % jt == 0 ? jt : 0;
+}
+
+// Partial sums (tiles) of a stencil pass of this mode.
+int stencil_tiles(const pcg_handle *h, int mode, bool binary32)
+{
+    const int jt = fused_rows_jt(h, binary32);
+    if (jt && (mode == SP_FIRST || mode == SP_FUSED_NOX || mode == SP_FUSED_X2))
+        return (int)((size_t)h->op.ntx * (h->op.nz / 4) * (h->op.ny / jt));
+    return h->pt_tiles;
+}
+
 template <int Ls, typename TV, typename TI>
 void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, TV *p, TV *y,
                     const SolveState *st, double *partials, TV *p_out)
@@ -437,14 +458,20 @@ void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, 
     if constexpr (Ls == 4) {
         const bool op_only = mode == SP_APPLY || mode == SP_APPLY_DOT || mode == SP_RESID;
         const bool fused_rows = mode == SP_FIRST || mode == SP_FUSED_NOX || mode == SP_FUSED_X2;
-        if (h->st_jt > 1 && h->pt_full && h->op.Ws == 4) {
+        const int jt = fused_rows_jt(h, std::is_same<TV, float>::value && std::is_same<TI, float>::value);
+        if (fused_rows && jt) {
             Op o2 = h->op;
-            if (fused_rows && h->op.ny % 4 == 0) {
-                o2.jt = 4;
-                o2.nkt = h->op.nz / 4;
+            o2.jt = jt;
+            o2.Ws = jt;
+            o2.nkt = h->op.nz / 4;
+            if (jt == 8)
+                launch_stencil_jt<4, 8>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+            else
                 launch_stencil_jt<4, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
-                return;
-            }
+            return;
+        }
+        if (h->st_jt != 1 && h->pt_full && h->op.Ws == 4) {
+            Op o2 = h->op;
             if (op_only && h->op.ny % 2 == 0) {
                 o2.Ls = 8;
                 o2.Ws = 2;
@@ -729,7 +756,10 @@ void init_geometry(pcg_handle *h, int nx, int ny, int nz, const Geometry &g)
     h->colf_full = C == kWave && nx % kWave == 0 && nz % g.Lf == 0 && env_int("MFPCG_COL_FULL", 1) != 0;
     h->pt_tiles = (int)(ntx * nkt * ny);
     h->pt_full = nx % kWave == 0 && nz % (g.Ls * g.Ws) == 0 && env_int("MFPCG_ST_FULL", 1) != 0;
-    h->st_jt = env_int("MFPCG_ST_JT", 4) == 1 ? 1 : 4;   // MFPCG_ST_JT=1: one-row tiles (see launch_stencil)
+    {   // MFPCG_ST_JT: rows per fused-pass tile, 1 (one-row tiles), 4 or 8 (see launch_stencil)
+        const int jt = env_int("MFPCG_ST_JT", 0);
+        h->st_jt = (jt == 1 || jt == 4 || jt == 8) ? jt : 0;
+    }
     h->n = ncol * (size_t)nz;
     h->op.nx = nx;
     h->op.ny = ny;
@@ -1312,7 +1342,8 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
             }
         }
         // a6: sigma, alpha
-        red = fold_partials(h, w, h->pt_tiles, &nred);
+        const int smode = ap ? SP_FUSED_AP : (k == 0 ? SP_FIRST : ((k & 1) ? SP_FUSED_NOX : SP_FUSED_X2));
+        red = fold_partials(h, w, stencil_tiles(h, smode, std::is_same<TV, float>::value), &nred);
         k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k, !ap && (k & 1));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) {

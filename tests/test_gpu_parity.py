@@ -393,8 +393,8 @@ def test_column_segment_lengths_agree(dev, monkeypatch, label, make, short, long
         assert np.linalg.norm(xa - xc) <= 1e-11 * np.linalg.norm(xa), (label, name)
 
 
-# grids of whole tiles: ny a multiple of 4 (row tiles in every stencil pass),
-# ny = 6 (in the operator-only passes only), a general operator
+# grids of whole tiles: ny a multiple of 8 (row tiles of 4 or 8 rows in every
+# stencil pass), ny = 6 (in the operator-only passes only), a general operator
 ROW_TILE_CASES = [
     ("cfg4-128x24x64", lambda: W.config_problem(4, scale_xy=(128, 24), nz=64)),
     ("cfg4-64x6x32", lambda: W.config_problem(4, scale_xy=(64, 6), nz=32)),
@@ -405,10 +405,11 @@ ROW_TILE_CASES = [
 @pytest.mark.parametrize("label,make", ROW_TILE_CASES, ids=[c[0] for c in ROW_TILE_CASES])
 def test_row_tiles_match_one_row_tiles(dev, monkeypatch, label, make):
     """On whole tiles the stencil passes take tiles of several rows j whose
-    waves pass z through LDS (default); MFPCG_ST_JT=1 (read at pcg_create)
-    takes one-row tiles.  Same stencil: apply_A matches the oracle either way
-    and the first 5 steps of every solve agree to rounding (the dot products'
-    per-tile partial sums group differently)."""
+    waves pass z through LDS (default; MFPCG_ST_JT=4 or 8 rows for the fused
+    passes, read at pcg_create); MFPCG_ST_JT=1 takes one-row tiles.  Same
+    stencil: apply_A matches the oracle every way and the first 5 steps of
+    every solve agree to rounding (the dot products' per-tile partial sums
+    group differently)."""
     import torch
     prob = make()
     general = isinstance(prob, W.GeneralProblem)
@@ -434,17 +435,18 @@ def test_row_tiles_match_one_row_tiles(dev, monkeypatch, label, make):
         finally:
             mf.pcg_destroy(h)
 
-    a, c = run(4), run(1)
-    for o in (a, c):
+    a, c, e = run(4), run(1), run(8)
+    for o in (a, c, e):
         assert np.isfinite(o["y"]).all()
     if general:
         tol = 16 * np.finfo(float).eps * gen_scale(prob, x)
     else:
         tol = apply_tol(prob, x)
-    assert np.abs(a["y"] - ref).max() <= tol, label
-    assert np.abs(c["y"] - ref).max() <= tol, label
+    for o in (a, c, e):
+        assert np.abs(o["y"] - ref).max() <= tol, label
     for name in SOLVERS:
-        xa, ha = a[name]
         xc, hc = c[name]
-        assert np.allclose(ha, hc, rtol=1e-11, atol=0), (label, name)
-        assert np.linalg.norm(xa - xc) <= 1e-11 * np.linalg.norm(xc), (label, name)
+        for o in (a, e):
+            xa, ha = o[name]
+            assert np.allclose(ha, hc, rtol=1e-11, atol=0), (label, name)
+            assert np.linalg.norm(xa - xc) <= 1e-11 * np.linalg.norm(xc), (label, name)
