@@ -1599,9 +1599,14 @@ __global__ __launch_bounds__(kMaxThreads) void k_csr_assemble(Op o, CsrShape cs,
 
 enum : int { CSR_APPLY = 0, CSR_RESID = 1, CSR_APPLY_DOT = 2 };
 
-// y = A x from the CSR matrix (one row per thread, sweep geometry); RESID:
-// y = b - A x; APPLY_DOT: also <x, y> per workgroup.
-template <int Ls, int MODE>
+// y = A x from the CSR matrix; RESID: y = b - A x; APPLY_DOT: also <x, y> per
+// workgroup.  A workgroup covers the rows of one sweep tile (64 columns x
+// Ws * Ls levels of one row j: the sweep passes' tiles, so the same partial
+// sums) and gives each row a group of kCsrG lanes: the lanes of a group read
+// the row's entries side by side (a wave reads 8 consecutive rows' entries in
+// one contiguous run) and add their products in a 3-step butterfly.
+constexpr int kCsrG = 8;
+template <int MODE>
 __global__ __launch_bounds__(kMaxThreads) void k_csr_spmv(const int64_t *__restrict__ row_ptr,
                                                           const int32_t *__restrict__ col,
                                                           const double *__restrict__ val,
@@ -1614,24 +1619,67 @@ __global__ __launch_bounds__(kMaxThreads) void k_csr_spmv(const int64_t *__restr
     __shared__ double sh_red[kMaxThreads / kWave][1];
     if (MODE == CSR_APPLY_DOT && st->done)
         return;
-    const Sweep sw = sweep_of_thread(o, Ls);
+    const int tile = tile_of_block(blockIdx.x, gridDim.x);
+    const int per_strip = o.sg * o.ny * o.nkt;
+    const int g = tile / per_strip;
+    const int rem = tile - g * per_strip;
+    const int gw = min(o.sg, o.ntx - g * o.sg);
+    const int kt = rem % o.nkt;
+    const int r = rem / o.nkt;
+    const int j = r / gw;
+    const int i0 = (g * o.sg + (r - j * gw)) * kWave;
+    const int k0 = kt * o.Ws * o.Ls;
+    const int q = threadIdx.x & (kCsrG - 1);            // lane in the row's group
+    const int grp = threadIdx.x / kCsrG;
+    const int ngrp = blockDim.x / kCsrG;
+    const int rows = kWave * o.Ws * o.Ls;               // the tile's rows: (level, column) pairs
+    // kCsrU rows per group at a time, so that their dependent loads (row
+    // pointers, then entries, then x) are in flight together; rows / ngrp =
+    // 8 * Ls is a multiple of kCsrU, so every group runs the same trip count
+    constexpr int kCsrU = 4;
     double acc = 0.0;
-    if (sw.ok) {
-        const size_t base = lin(o, sw.i, sw.j, 0);
-        for (int t = 0; t < sw.len; ++t) {
-            const size_t l = base + (size_t)(sw.k0 + t) * o.nx;
-            const int64_t e0 = row_ptr[l], e1 = row_ptr[l + 1];
-            double s = 0.0;
-            // val / col lines are shared by the 64 rows of a wave over the
-            // loop's iterations: ordinary (cached) loads
-            for (int64_t e = e0; e < e1; ++e)
-                s += val[e] * x[col[e]];
-            if (MODE == CSR_RESID) {
-                st_s(y + l, ld_s(bvec + l) - s);
-            } else {
-                st_s(y + l, s);
-                if (MODE == CSR_APPLY_DOT)
-                    acc += x[l] * s;
+    for (int t0 = grp; t0 < rows; t0 += ngrp * kCsrU) {
+        size_t l[kCsrU];
+        bool in[kCsrU];
+        int64_t e0[kCsrU], e1[kCsrU];
+#pragma unroll
+        for (int u = 0; u < kCsrU; ++u) {
+            const int t = t0 + u * ngrp;
+            const int i = i0 + (t & (kWave - 1)), k = k0 + t / kWave;
+            in[u] = i < o.nx && k < o.nz;
+            l[u] = in[u] ? lin(o, i, j, k) : 0;
+            e0[u] = in[u] ? row_ptr[l[u]] : 0;
+            e1[u] = in[u] ? row_ptr[l[u] + 1] : 0;
+        }
+        double v[kCsrU];
+        int c[kCsrU];
+#pragma unroll
+        for (int u = 0; u < kCsrU; ++u) {
+            const int64_t e = e0[u] + q;
+            const bool has = e < e1[u];
+            v[u] = has ? val[e] : 0.0;
+            c[u] = has ? col[e] : -1;
+        }
+        double sum[kCsrU];
+#pragma unroll
+        for (int u = 0; u < kCsrU; ++u)
+            sum[u] = c[u] >= 0 ? v[u] * x[c[u]] : 0.0;
+#pragma unroll
+        for (int u = 0; u < kCsrU; ++u) {
+            for (int64_t e = e0[u] + q + kCsrG; e < e1[u]; e += kCsrG)   // rows of more than kCsrG entries
+                sum[u] += val[e] * x[col[e]];
+            double s = sum[u];
+            s += __shfl_xor(s, 4, kCsrG);
+            s += __shfl_xor(s, 2, kCsrG);
+            s += __shfl_xor(s, 1, kCsrG);
+            if (in[u] && q == 0) {
+                if (MODE == CSR_RESID) {
+                    st_s(y + l[u], ld_s(bvec + l[u]) - s);
+                } else {
+                    st_s(y + l[u], s);
+                    if (MODE == CSR_APPLY_DOT)
+                        acc += x[l[u]] * s;
+                }
             }
         }
     }
@@ -1640,7 +1688,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_csr_spmv(const int64_t *__restr
         double out[1];
         block_sum<1>(v, sh_red, out);
         if (threadIdx.x == 0)
-            partials[2 * (size_t)sw.tile] = out[0];
+            partials[2 * (size_t)tile] = out[0];
     }
 }
 

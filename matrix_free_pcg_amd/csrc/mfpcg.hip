@@ -544,28 +544,16 @@ void update_p(pcg_handle *h, double *p, const double *z, const SolveState *st, i
     vec(h, 1, nullptr, nullptr, p, z, st, nullptr, first);
 }
 
-template <int Ls>
-void launch_csr(pcg_handle *h, int mode, const int64_t *rp, const int32_t *col, const double *val,
-                const double *x, const double *b, double *y, const SolveState *st, double *partials)
-{
-    dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
-    if (mode == CSR_APPLY)
-        k_csr_spmv<Ls, CSR_APPLY><<<grid, block, 0, h->stream>>>(rp, col, val, x, b, y, h->op, st, partials);
-    else if (mode == CSR_RESID)
-        k_csr_spmv<Ls, CSR_RESID><<<grid, block, 0, h->stream>>>(rp, col, val, x, b, y, h->op, st, partials);
-    else
-        k_csr_spmv<Ls, CSR_APPLY_DOT><<<grid, block, 0, h->stream>>>(rp, col, val, x, b, y, h->op, st, partials);
-}
-
 void csr_spmv(pcg_handle *h, int mode, const int64_t *rp, const int32_t *col, const double *val,
               const double *x, const double *b, double *y, const SolveState *st, double *partials)
 {
-    switch (h->op.Ls) {
-    case 1: launch_csr<1>(h, mode, rp, col, val, x, b, y, st, partials); break;
-    case 2: launch_csr<2>(h, mode, rp, col, val, x, b, y, st, partials); break;
-    case 4: launch_csr<4>(h, mode, rp, col, val, x, b, y, st, partials); break;
-    default: launch_csr<8>(h, mode, rp, col, val, x, b, y, st, partials); break;
-    }
+    dim3 grid(h->pt_tiles), block(kWave * h->op.Ws);
+    if (mode == CSR_APPLY)
+        k_csr_spmv<CSR_APPLY><<<grid, block, 0, h->stream>>>(rp, col, val, x, b, y, h->op, st, partials);
+    else if (mode == CSR_RESID)
+        k_csr_spmv<CSR_RESID><<<grid, block, 0, h->stream>>>(rp, col, val, x, b, y, h->op, st, partials);
+    else
+        k_csr_spmv<CSR_APPLY_DOT><<<grid, block, 0, h->stream>>>(rp, col, val, x, b, y, h->op, st, partials);
 }
 
 void csr_assemble(pcg_handle *h, int64_t *rp, int32_t *col, double *val)
