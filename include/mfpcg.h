@@ -325,7 +325,10 @@ int pcg_tridiag_factor(pcg_handle *h, const double *tri_dev);
 int pcg_tridiag_precond(pcg_handle *h, const double *tri_dev, const double *r_dev, double *z_dev);
 
 /* Standard PCG (section 4.1) with the CSR matrix and the stored column
- * matrices; arguments and results as pcg_solve. */
+ * matrices; arguments and results as pcg_solve.  The matrix must have the
+ * layout pcg_csr_assemble writes (every row stores its diagonal entry; the
+ * values may differ): sigma = <p, A p> takes p at each row's point from the
+ * diagonal entry's column. */
 int pcg_solve_csr(pcg_handle *h, const int64_t *row_ptr_dev, const int32_t *col_dev,
                   const double *val_dev, const double *tri_dev, const double *b_dev,
                   double *x_dev, double tol, int32_t maxit, void *workspace_dev,

@@ -1660,25 +1660,38 @@ __global__ __launch_bounds__(kMaxThreads) void k_csr_spmv(const int64_t *__restr
             v[u] = has ? val[e] : 0.0;
             c[u] = has ? col[e] : -1;
         }
-        double sum[kCsrU];
-#pragma unroll
-        for (int u = 0; u < kCsrU; ++u)
-            sum[u] = c[u] >= 0 ? v[u] * x[c[u]] : 0.0;
+        double sum[kCsrU], xd[kCsrU];   // APPLY_DOT: x at the row's own point, from the gathers
 #pragma unroll
         for (int u = 0; u < kCsrU; ++u) {
-            for (int64_t e = e0[u] + q + kCsrG; e < e1[u]; e += kCsrG)   // rows of more than kCsrG entries
-                sum[u] += val[e] * x[col[e]];
+            const double xc = c[u] >= 0 ? x[c[u]] : 0.0;
+            sum[u] = v[u] * xc;
+            xd[u] = (MODE == CSR_APPLY_DOT && c[u] >= 0 && (size_t)c[u] == l[u]) ? xc : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kCsrU; ++u) {
+            for (int64_t e = e0[u] + q + kCsrG; e < e1[u]; e += kCsrG) {   // rows of more than kCsrG entries
+                const double xc = x[col[e]];
+                sum[u] += val[e] * xc;
+                if (MODE == CSR_APPLY_DOT && (size_t)col[e] == l[u])
+                    xd[u] = xc;
+            }
             double s = sum[u];
             s += __shfl_xor(s, 4, kCsrG);
             s += __shfl_xor(s, 2, kCsrG);
             s += __shfl_xor(s, 1, kCsrG);
+            double xl = xd[u];   // one lane of the group holds x at the row's point, the others 0
+            if (MODE == CSR_APPLY_DOT) {
+                xl += __shfl_xor(xl, 4, kCsrG);
+                xl += __shfl_xor(xl, 2, kCsrG);
+                xl += __shfl_xor(xl, 1, kCsrG);
+            }
             if (in[u] && q == 0) {
                 if (MODE == CSR_RESID) {
                     st_s(y + l[u], ld_s(bvec + l[u]) - s);
                 } else {
                     st_s(y + l[u], s);
                     if (MODE == CSR_APPLY_DOT)
-                        acc += x[l[u]] * s;
+                        acc += xl * s;
                 }
             }
         }
