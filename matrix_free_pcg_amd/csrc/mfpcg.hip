@@ -410,7 +410,8 @@ void launch_stencil_jt(pcg_handle *h, const Op &o, int mode, const TI *zin, cons
         case SP_FUSED_X2: k_stencil<Ls, SP_FUSED_X2, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
         default: break;
         }
-    } else if constexpr (kSame) {   // the operator-only passes
+    }
+    if constexpr (kSame && Ls == 8) {   // the operator-only passes
         switch (mode) {
         case SP_APPLY: k_stencil<Ls, SP_APPLY, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
         case SP_RESID: k_stencil<Ls, SP_RESID, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
@@ -420,17 +421,16 @@ void launch_stencil_jt(pcg_handle *h, const Op &o, int mode, const TI *zin, cons
     }
 }
 
-// The passes that apply the operator alone (y = A x, q = A p with <p,q>,
-// r = b - A x) move one stream in and one out; with 4 levels per wave they
-// are latency-bound, so they sweep 8 levels per wave with half the waves
-// (the same tiles, so the same partial sums and tile order): 13 % faster at
-// 1024 x 1024 x 128.
-// Row tiles (st_jt > 1, whole tiles, 4 waves): the same number of tiles
-// (JT rows x Ls levels against one row x Ws * Ls levels), so the same partial
-// count; the fused passes take 4 rows x 4 levels (ny a multiple of 4), the
-// operator-only ones 2 x 8 (ny even).  The rows j +- 1 inside a tile come
-// through LDS instead of the L2: the fused pass 1.222 -> 1.170 ms and
-// y = A x 0.541 -> 0.475 ms at 1024 x 1024 x 128.
+// Tiles of the sweep passes.  On whole tiles (4 waves of 4 levels by
+// default) the passes take row tiles, one wave per row j, the rows j +- 1
+// inside a tile coming through LDS instead of the L2 (the fused pass
+// 1.222 -> 1.170 ms at 1024 x 1024 x 128); otherwise one-row tiles of
+// Ws x Ls levels.  The passes that apply the operator alone (y = A x,
+// q = A p with <p,q>, r = b - A x) move one stream in and one out; with 4
+// levels per wave they are latency-bound, so they sweep 8 levels per wave
+// (13 % faster on one-row tiles).  stencil_tiles gives each pass's partial
+// count.
+
 // Rows per tile of the fused stencil passes (SP_FIRST, SP_FUSED_NOX,
 // SP_FUSED_X2) on this handle, 0 when they take one-row tiles.  Measured at
 // 1024 x 1024 x 128: 4 rows best in binary64 and the mixed solve (8 rows:
@@ -442,12 +442,26 @@ int fused_rows_jt(const pcg_handle *h, bool binary32)
     return jt > 1 && h->pt_full && o.Ls == 4 && o.Ws == 4 && o.ny % jt == 0 ? jt : 0;
 }
 
+// Rows per tile of the operator-only passes (SP_APPLY, SP_APPLY_DOT,
+// SP_RESID; 8 levels per wave) on this handle, 0 when they take one-row
+// tiles.  y = A x at 1024 x 1024 x 128: one row 0.541 ms, 2 rows 0.471 ms,
+// 4 rows 0.439 ms.
+int op_rows_jt(const pcg_handle *h)
+{
+    const Op &o = h->op;
+    if (h->st_jt == 1 || !h->pt_full || o.Ls != 4 || o.Ws != 4)
+        return 0;
+    return o.ny % 4 == 0 ? 4 : (o.ny % 2 == 0 ? 2 : 0);
+}
+
 // Partial sums (tiles) of a stencil pass of this mode.
 int stencil_tiles(const pcg_handle *h, int mode, bool binary32)
 {
     const int jt = fused_rows_jt(h, binary32);
     if (jt && (mode == SP_FIRST || mode == SP_FUSED_NOX || mode == SP_FUSED_X2))
         return (int)((size_t)h->op.ntx * (h->op.nz / 4) * (h->op.ny / jt));
+    if (mode == SP_APPLY_DOT && op_rows_jt(h) == 4)
+        return (int)((size_t)h->op.ntx * (h->op.nz / 8) * (h->op.ny / 4));
     return h->pt_tiles;
 }
 
@@ -470,16 +484,18 @@ void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, 
                 launch_stencil_jt<4, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
             return;
         }
-        if (h->st_jt != 1 && h->pt_full && h->op.Ws == 4) {
+        const int ojt = op_rows_jt(h);
+        if (op_only && ojt) {
             Op o2 = h->op;
-            if (op_only && h->op.ny % 2 == 0) {
-                o2.Ls = 8;
-                o2.Ws = 2;
-                o2.jt = 2;
-                o2.nkt = h->op.nz / 8;
+            o2.Ls = 8;
+            o2.Ws = ojt;
+            o2.jt = ojt;
+            o2.nkt = h->op.nz / 8;
+            if (ojt == 4)
+                launch_stencil_jt<8, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+            else
                 launch_stencil_jt<8, 2>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
-                return;
-            }
+            return;
         }
         if (op_only && h->op.Ws % 2 == 0) {
             Op o2 = h->op;
@@ -1652,7 +1668,7 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
             else
                 stencil<double, double>(h, SP_APPLY_DOT, w.p, nullptr, nullptr, nullptr, w.q, w.state, w.partials);
         }
-        red = fold_partials(h, w, h->pt_tiles, &nred);
+        red = fold_partials(h, w, ex ? h->pt_tiles : stencil_tiles(h, SP_APPLY_DOT, false), &nred);
         k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k - 1, 0);
         {   // x += alpha p ; r -= alpha q ; <r,r>
             Timed t(h, PCG_KID_VECTOR, k);
