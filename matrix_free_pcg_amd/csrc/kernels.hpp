@@ -1057,8 +1057,10 @@ enum : int {
 // there; p_out holds it on entry and receives the new one (each point is read
 // before it is written by the same thread, and p has no neighbour reads here).
 // FULL: every tile is whole (nx a multiple of 64, nz a multiple of Ws * Ls),
-// so no level or column guard is needed and the two edge lanes of a wave load
-// their outside neighbours (i-1 for lane 0, i+1 for lane 63) with one load.
+// so no level or column guard is needed, and a wave fetches the outside
+// neighbours of its two edge lanes (i-1 for lane 0, i+1 for lane 63) at all
+// its levels with one load over 2 * Ls lanes, then hands them out with
+// readlane.
 // JT > 1 (whole tiles only): a tile is JT rows of Ls levels, one wave per row;
 // each wave puts its z rows in LDS and takes z at j-1 and j+1 from the waves
 // of the rows beside it, so only the tile's first and last waves load a
