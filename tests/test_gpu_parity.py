@@ -450,3 +450,54 @@ def test_row_tiles_match_one_row_tiles(dev, monkeypatch, label, make):
             xa, ha = o[name]
             assert np.allclose(ha, hc, rtol=1e-11, atol=0), (label, name)
             assert np.linalg.norm(xa - xc) <= 1e-11 * np.linalg.norm(xc), (label, name)
+
+
+def _random_shapes(count=24, seed=20261202):
+    """Seeded grid shapes that mix whole and ragged tiles in every direction:
+    nx a multiple of 64 or not, ny a multiple of 8, 4, 2 or odd, nz a multiple
+    of 16 or not (1..200)."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for n in range(count):
+        nx = int(rng.choice([64, 128, 192])) if n % 2 == 0 else int(rng.integers(1, 150))
+        ny = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16]))
+        nz = int(rng.choice([16, 32, 48, 64, 128])) if n % 3 != 2 else int(rng.integers(1, 200))
+        shapes.append((nx, ny, nz))
+    return shapes
+
+
+@pytest.mark.parametrize("nx,ny,nz", _random_shapes(), ids=lambda v: str(v))
+def test_random_shapes_match_oracle(dev, nx, ny, nz):
+    """apply_A, precond and the first 3 steps of the interleaved and the
+    standard solve against the oracle on seeded grid shapes (the launch
+    geometry the library picks for each: row tiles, 16-level segments, ragged
+    tiles)."""
+    import torch
+    prob = W.config_problem(4, scale_xy=(nx, ny), nz=nz)
+    x = W.uniform_field(nx, ny, nz, 51)
+    r = W.gaussian_field(nx, ny, nz, 52)
+    b = W.uniform_field(nx, ny, nz, 53)
+    h = mf.pcg_create(prob)
+    try:
+        xd, rd = to_dev(x, dev), to_dev(r, dev)
+        yd, zd = torch.full_like(xd, float("nan")), torch.full_like(xd, float("nan"))
+        mf.pcg_apply_A(h, xd, yd)
+        mf.pcg_precond(h, rd, zd)
+        y, z = to_host(yd), to_host(zd)
+        runs = {}
+        for name in ("interleaved", "standard"):
+            bd = to_dev(b, dev)
+            xs = torch.zeros_like(bd)
+            res = SOLVERS[name](h, bd, xs, 0.0, 3)
+            runs[name] = (to_host(xs), res)
+        torch.cuda.synchronize()
+    finally:
+        mf.pcg_destroy(h)
+    assert np.abs(y - oracle.apply_A(prob, x)).max() <= apply_tol(prob, x)
+    zo = oracle.precond(prob, r)
+    assert np.abs(z - zo).max() <= precond_tol(prob, zo)
+    ref = oracle.pcg(prob, b, tol=0.0, maxit=3)
+    for name, (xg, res) in runs.items():
+        assert res["iters"] == ref["iters"] == 3, name
+        assert np.allclose(res["hist"], ref["hist"], rtol=1e-11, atol=0), name
+        assert np.linalg.norm(xg - ref["x"]) <= 1e-11 * np.linalg.norm(ref["x"]), name
