@@ -164,3 +164,40 @@ def test_general_explicit_solve_matches_oracle(dev):
     ref = oracle.pcg_gen(gp, b, tol=1e-10, maxit=5000)
     assert res["status"] == 0 and abs(res["iters"] - ref["iters"]) <= 1, (res["iters"], ref["iters"])
     assert np.linalg.norm(xg - ref["x"]) <= 1e-9 * np.linalg.norm(ref["x"])
+
+
+RANDOM_SHAPES = [(64, 4, 64), (24, 16, 16), (128, 12, 33), (55, 16, 48), (64, 8, 16), (109, 6, 128),
+                 (128, 8, 64), (192, 4, 116)]
+
+
+@pytest.mark.parametrize("nx,ny,nz", RANDOM_SHAPES, ids=lambda v: str(v))
+def test_general_random_shapes(dev, nx, ny, nz):
+    """The general operator with random coefficients on grid shapes that mix
+    whole and ragged tiles: apply_A and precond against the oracle's general
+    functions, and 3 fixed steps of the interleaved solve against
+    oracle.pcg_gen."""
+    import torch
+    gp = random_general(nx, ny, nz, seed=nx + ny + nz)
+    x = W.uniform_field(nx, ny, nz, 71)
+    r = W.gaussian_field(nx, ny, nz, 72)
+    b = W.uniform_field(nx, ny, nz, 73)
+    h = mf.pcg_create(gp)
+    try:
+        xd, rd = to_dev(x, dev), to_dev(r, dev)
+        yd, zd = torch.full_like(xd, float("nan")), torch.full_like(xd, float("nan"))
+        mf.pcg_apply_A(h, xd, yd)
+        mf.pcg_precond(h, rd, zd)
+        bd = to_dev(b, dev)
+        xs = torch.zeros_like(bd)
+        res = mf.pcg_solve(h, bd, xs, 0.0, 3)
+        torch.cuda.synchronize()
+        y, z, xg = to_host(yd), to_host(zd), to_host(xs)
+    finally:
+        mf.pcg_destroy(h)
+    assert np.abs(y - oracle.apply_A_gen(gp, x)).max() <= 16 * EPS * gen_scale(gp, x)
+    zo = oracle.precond_gen(gp, r)
+    assert np.abs(z - zo).max() <= 64 * EPS * gen_column_cond(gp) * np.abs(zo).max()
+    ref = oracle.pcg_gen(gp, b, tol=0.0, maxit=3)
+    assert res["iters"] == ref["iters"] == 3
+    assert np.allclose(res["hist"], ref["hist"], rtol=1e-11, atol=0)
+    assert np.linalg.norm(xg - ref["x"]) <= 1e-11 * np.linalg.norm(ref["x"])

@@ -265,3 +265,27 @@ def test_f32_edge_cases(dev):
         assert res["status"] == mf.PCG_ERR_BREAKDOWN
     finally:
         mf.pcg_destroy(h)
+
+
+RANDOM_SHAPES = [(64, 4, 64), (24, 16, 16), (128, 12, 33), (55, 16, 48), (64, 8, 16), (109, 6, 128),
+                 (128, 8, 64), (192, 4, 116)]
+
+
+@pytest.mark.parametrize("nx,ny,nz", RANDOM_SHAPES, ids=lambda v: str(v))
+def test_f32_and_mixed_random_shapes(dev, nx, ny, nz):
+    """Two fixed steps of the binary32 and mixed solves against the oracle's
+    on grid shapes that mix whole and ragged tiles (the binary32 stencil
+    passes take 8-row tiles where ny allows, the others 4), within the
+    binary32 rounding bound of the other fixed-step tests."""
+    prob = W.config_problem(4, scale_xy=(nx, ny), nz=nz)
+    b64 = W.uniform_field(nx, ny, nz, 61)
+    b32 = b64.astype(np.float32)
+    bound = max(1e-4, 10 * precond_f32_forward_error(prob, b32))
+    res, xg = _gpu_solve(mf.pcg_solve_f32, prob, b32, 0.0, 2, dev, to_dev32)
+    ref = oracle.pcg_f32(prob, b32, tol=0.0, maxit=2)
+    assert res["iters"] == ref["iters"] == 2
+    assert np.linalg.norm(xg - ref["x"]) <= bound * np.linalg.norm(ref["x"]), "f32"
+    res, xg = _gpu_solve(mf.pcg_solve_mixed, prob, b64, 0.0, 2, dev, to_dev64)
+    ref = oracle.pcg_mixed(prob, b64, tol=0.0, maxit=2)
+    assert res["iters"] == ref["iters"] == 2
+    assert np.linalg.norm(xg - ref["x"]) <= bound * np.linalg.norm(ref["x"]), "mixed"
