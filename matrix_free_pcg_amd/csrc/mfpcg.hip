@@ -411,6 +411,10 @@ void launch_stencil_jt(pcg_handle *h, const Op &o, int mode, const TI *zin, cons
         default: break;
         }
     }
+    if constexpr (Ls == 8 && JT == 4 && kBinary64<TV, TI>) {   // the binary64 odd-step pass
+        if (mode == SP_FUSED_NOX)
+            k_stencil<Ls, SP_FUSED_NOX, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+    }
     if constexpr (kSame && Ls == 8) {   // the operator-only passes
         switch (mode) {
         case SP_APPLY: k_stencil<Ls, SP_APPLY, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
@@ -454,12 +458,30 @@ int op_rows_jt(const pcg_handle *h)
     return o.ny % 4 == 0 ? 4 : (o.ny % 2 == 0 ? 2 : 0);
 }
 
-// Partial sums (tiles) of a stencil pass of this mode.
-int stencil_tiles(const pcg_handle *h, int mode, bool binary32)
+// Row-tile shape of a fused pass: levels per wave and rows (0 rows: one-row
+// tiles).  In binary64 the odd-step pass takes 8 levels per wave (4 x 8
+// tiles: 0.5 % faster than 4 x 4; in the mixed solve 1.8 % slower).
+struct RowShape {
+    int Ls, jt;
+};
+RowShape fused_shape(const pcg_handle *h, int mode, bool binary64, bool binary32)
 {
     const int jt = fused_rows_jt(h, binary32);
-    if (jt && (mode == SP_FIRST || mode == SP_FUSED_NOX || mode == SP_FUSED_X2))
-        return (int)((size_t)h->op.ntx * (h->op.nz / 4) * (h->op.ny / jt));
+    if (!jt)
+        return {4, 0};
+    if (binary64 && jt == 4 && mode == SP_FUSED_NOX)
+        return {8, 4};
+    return {4, jt};
+}
+
+// Partial sums (tiles) of a stencil pass of this mode.
+int stencil_tiles(const pcg_handle *h, int mode, bool binary64, bool binary32)
+{
+    if (mode == SP_FIRST || mode == SP_FUSED_NOX || mode == SP_FUSED_X2) {
+        const RowShape rs = fused_shape(h, mode, binary64, binary32);
+        if (rs.jt)
+            return (int)((size_t)h->op.ntx * (h->op.nz / rs.Ls) * (h->op.ny / rs.jt));
+    }
     if (mode == SP_APPLY_DOT && op_rows_jt(h) == 4)
         return (int)((size_t)h->op.ntx * (h->op.nz / 8) * (h->op.ny / 4));
     return h->pt_tiles;
@@ -472,13 +494,18 @@ void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, 
     if constexpr (Ls == 4) {
         const bool op_only = mode == SP_APPLY || mode == SP_APPLY_DOT || mode == SP_RESID;
         const bool fused_rows = mode == SP_FIRST || mode == SP_FUSED_NOX || mode == SP_FUSED_X2;
-        const int jt = fused_rows_jt(h, std::is_same<TV, float>::value && std::is_same<TI, float>::value);
-        if (fused_rows && jt) {
+        const RowShape rs = fused_rows ? fused_shape(h, mode, kBinary64<TV, TI>,
+                                                     std::is_same<TV, float>::value && std::is_same<TI, float>::value)
+                                       : RowShape{4, 0};
+        if (rs.jt) {
             Op o2 = h->op;
-            o2.jt = jt;
-            o2.Ws = jt;
-            o2.nkt = h->op.nz / 4;
-            if (jt == 8)
+            o2.Ls = rs.Ls;
+            o2.jt = rs.jt;
+            o2.Ws = rs.jt;
+            o2.nkt = h->op.nz / rs.Ls;
+            if (rs.Ls == 8)
+                launch_stencil_jt<8, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+            else if (rs.jt == 8)
                 launch_stencil_jt<4, 8>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
             else
                 launch_stencil_jt<4, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
@@ -1347,7 +1374,7 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
         }
         // a6: sigma, alpha
         const int smode = ap ? SP_FUSED_AP : (k == 0 ? SP_FIRST : ((k & 1) ? SP_FUSED_NOX : SP_FUSED_X2));
-        red = fold_partials(h, w, stencil_tiles(h, smode, std::is_same<TV, float>::value), &nred);
+        red = fold_partials(h, w, stencil_tiles(h, smode, kBinary64<TV, TZ>, std::is_same<TV, float>::value), &nred);
         k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k, !ap && (k & 1));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) {
@@ -1668,7 +1695,7 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
             else
                 stencil<double, double>(h, SP_APPLY_DOT, w.p, nullptr, nullptr, nullptr, w.q, w.state, w.partials);
         }
-        red = fold_partials(h, w, ex ? h->pt_tiles : stencil_tiles(h, SP_APPLY_DOT, false), &nred);
+        red = fold_partials(h, w, ex ? h->pt_tiles : stencil_tiles(h, SP_APPLY_DOT, true, false), &nred);
         k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k - 1, 0);
         {   // x += alpha p ; r -= alpha q ; <r,r>
             Timed t(h, PCG_KID_VECTOR, k);
