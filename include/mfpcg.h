@@ -352,8 +352,10 @@ int pcg_profile_reset(pcg_handle *h);
 int pcg_profile_read(const pcg_handle *h, int32_t kernel_id, double *ms_total,
                      int64_t *launches);
 
-/* Human-readable description of the last error on this handle (or of the
- * last failed pcg_create when h is NULL).  Never NULL. */
+/* Human-readable description of the last error on this handle (or, when h
+ * is NULL, of the last failed pcg_create / pcg_create_general on the calling
+ * thread).  Never NULL; valid until the next call that fails on the same
+ * handle (or thread). */
 const char *pcg_last_error(const pcg_handle *h);
 
 /* Library version string. */
