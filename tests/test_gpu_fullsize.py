@@ -128,8 +128,11 @@ def test_cfg4_full_solve_true_residual(dev, cfg4):
 
 
 def test_cfg3_manufactured_full(dev):
-    """512x512x128, b = A x_true: the solve recovers x_true to within the
-    condition-number bound of tol, and its true residual is small."""
+    """512x512x128, b = A x_true: the first 3 steps against the oracle's
+    (1e-11), and the full solve against the oracle's full solve: iterations
+    within 1, and the GPU iterate as close to x_true (the exact solution) as
+    the oracle's (within a factor 2) and within the condition-number bound of
+    tol; its true residual small."""
     import torch
     w = W.make_workload(3)
     prob = w.problem
@@ -138,17 +141,30 @@ def test_cfg3_manufactured_full(dev):
     try:
         bd = to_dev(b, dev)
         xd = torch.zeros_like(bd)
+        first = mf.pcg_solve(h, bd, xd, 0.0, 3)
+        torch.cuda.synchronize()
+        x3 = to_host(xd)
+        xd.zero_()
         res = mf.pcg_solve(h, bd, xd, w.tol, w.maxit)
         torch.cuda.synchronize()
         xg = to_host(xd)
         del bd, xd
     finally:
         mf.pcg_destroy(h)
+    ref3 = oracle.pcg(prob, b, tol=0.0, maxit=3)
+    assert np.allclose(first["hist"], ref3["hist"], rtol=1e-11, atol=0)
+    assert np.linalg.norm(x3 - ref3["x"]) <= 1e-11 * np.linalg.norm(ref3["x"])
     assert res["status"] == mf.PCG_OK, res
-    err = np.linalg.norm(xg - w.x_true) / np.linalg.norm(w.x_true)
+    ref = oracle.pcg(prob, b, tol=w.tol, maxit=w.maxit)
+    assert ref["status"] == 0 and abs(res["iters"] - ref["iters"]) <= 1, (res["iters"], ref["iters"])
+    nt = np.linalg.norm(w.x_true)
+    err = np.linalg.norm(xg - w.x_true) / nt
+    err_orc = np.linalg.norm(ref["x"] - w.x_true) / nt
     kappa = (prob.delta + 8 * 1.0 + 4 * prob.alpha_z_face.max()) / prob.delta
     tr = _true_residual(prob, b, xg)
-    print(f"[cfg3] iters={res['iters']} err={err:.3e} true-res={tr:.3e}", flush=True)
+    print(f"[cfg3] iters gpu={res['iters']} oracle={ref['iters']} err to x_true gpu={err:.3e} "
+          f"oracle={err_orc:.3e} true-res={tr:.3e}", flush=True)
+    assert err <= 2.0 * err_orc
     assert err <= kappa * w.tol
     assert tr <= 1e-8
 
