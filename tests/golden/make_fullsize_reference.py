@@ -1,0 +1,60 @@
+"""Write fullsize_<workload>.json: the oracle's complete solve of a full-size
+workload, for the GPU tests that cannot wait for it (about an hour and a half
+for varying-1024x1024x128 on one core of this machine class).
+
+Stored: the step count and status, the whole residual history ||r_k||_2, the
+2-norm of the final iterate and its values at 4096 seeded positions (numpy
+default_rng(20261202) over the field's linear indices).  Calls only oracle/
+(the solver) and matrix_free_pcg_amd.workloads (the seeded inputs).
+
+    python tests/golden/make_fullsize_reference.py 4      # varying-1024x1024x128
+"""
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+import oracle  # noqa: E402
+from matrix_free_pcg_amd import workloads as W  # noqa: E402
+
+SAMPLES = 4096
+SAMPLE_SEED = 20261202
+
+
+def sample_indices(n: int) -> np.ndarray:
+    return np.sort(np.random.default_rng(SAMPLE_SEED).choice(n, size=SAMPLES, replace=False))
+
+
+def main(cfg: int) -> str:
+    w = W.make_workload(cfg)
+    p = w.problem
+    t = time.time()
+    if isinstance(p, W.GeneralProblem):
+        ref = oracle.pcg_gen(p, w.rhs, tol=w.tol, maxit=w.maxit)
+    else:
+        ref = oracle.pcg(p, w.rhs, tol=w.tol, maxit=w.maxit)
+    x = ref["x"].reshape(-1)
+    idx = sample_indices(x.size)
+    out = {
+        "workload": w.name, "tol": w.tol, "maxit": w.maxit,
+        "iters": int(ref["iters"]), "status": int(ref["status"]),
+        "hist": [float(v) for v in ref["hist"]],
+        "x_norm2": float(np.linalg.norm(x)),
+        "sample_seed": SAMPLE_SEED, "sample_index": [int(i) for i in idx],
+        "x_sample": [float(v) for v in x[idx]],
+        "oracle_seconds": round(time.time() - t, 1),
+    }
+    path = os.path.join(HERE, f"fullsize_{w.name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f)
+    return path
+
+
+if __name__ == "__main__":
+    for a in sys.argv[1:] or ["4"]:
+        print(main(int(a)), flush=True)

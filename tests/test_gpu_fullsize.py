@@ -4,8 +4,9 @@ benchmark times (1024x1024x128 with graded alpha_z and varying alpha_h;
 
 The oracle cannot finish a full solve at these sizes within a test, so the
 solve is checked by what it can compute: the whole stencil and column solve
-(one pass each), the first CG steps exactly, and the true residual
-||b - A x|| of the GPU solution evaluated by the oracle's stencil.
+(one pass each), the first CG steps exactly, the true residual ||b - A x|| of
+the GPU solution evaluated by the oracle's stencil, and (for the 1024^2 x 128
+workload) the oracle's complete solve stored by a committed script.
 """
 import time
 
@@ -256,3 +257,54 @@ def test_general_full_size(dev):
     tr = np.linalg.norm(w.rhs - oracle.apply_A_gen(gp, xg)) / np.linalg.norm(w.rhs)
     print(f"[general] iters={res['iters']} recursive={res['final_rel_res']:.3e} true={tr:.3e}", flush=True)
     assert tr <= 1e-8, tr
+
+
+def _reference(name):
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", f"fullsize_{name}.json")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not written (tests/golden/make_fullsize_reference.py)")
+    with open(path) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("cfg", [4])
+def test_full_solve_against_oracle_reference(dev, cfg4, cfg):
+    """The whole benchmark solve at full size against the oracle's complete
+    solve of the same workload (tests/golden/fullsize_<workload>.json, written
+    by tests/golden/make_fullsize_reference.py, which calls only the oracle):
+    step counts within 1; the residual histories within 1e-6 relative while
+    ||r_k|| >= 1e-6 ||r_0|| (the tail is rounding-dominated, as in the
+    smaller solve tests); the final iterate within rel-L2 1e-9 of the
+    oracle's on 4096 seeded positions, and its 2-norm within 1e-9."""
+    import torch
+    ref = _reference(W.CONFIG_NAMES[cfg])
+    w = cfg4 if cfg == 4 else W.make_workload(cfg)
+    assert ref["workload"] == w.name and ref["status"] == 0
+    h = mf.pcg_create(w.problem)
+    try:
+        bd = to_dev(w.rhs, dev)
+        xd = torch.zeros_like(bd)
+        res = mf.pcg_solve(h, bd, xd, w.tol, w.maxit)
+        torch.cuda.synchronize()
+        xg = to_host(xd).reshape(-1)
+        del bd, xd
+    finally:
+        mf.pcg_destroy(h)
+    assert res["status"] == mf.PCG_OK, res
+    assert abs(res["iters"] - ref["iters"]) <= 1, (res["iters"], ref["iters"])
+    ho = np.asarray(ref["hist"])
+    n = min(len(ho), len(res["hist"]))
+    hg, ho = res["hist"][:n], ho[:n]
+    big = ho >= 1e-6 * ho[0]
+    dev_hist = np.max(np.abs(hg[big] - ho[big]) / ho[big])
+    idx = np.asarray(ref["sample_index"])
+    xs, xo = xg[idx], np.asarray(ref["x_sample"])
+    rel = np.linalg.norm(xs - xo) / np.linalg.norm(xo)
+    rel_norm = abs(np.linalg.norm(xg) - ref["x_norm2"]) / ref["x_norm2"]
+    print(f"[{w.name}] iters gpu={res['iters']} oracle={ref['iters']} history {dev_hist:.2e} "
+          f"samples rel-L2 {rel:.2e} norm {rel_norm:.2e}", flush=True)
+    assert dev_hist <= 1e-6
+    assert rel <= 1e-9
+    assert rel_norm <= 1e-9
