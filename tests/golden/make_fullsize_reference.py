@@ -4,10 +4,13 @@ for varying-1024x1024x128 on one core of this machine class).
 
 Stored: the step count and status, the whole residual history ||r_k||_2, the
 2-norm of the final iterate and its values at 4096 seeded positions (numpy
-default_rng(20261202) over the field's linear indices).  Calls only oracle/
+default_rng(20261202) over the field's linear indices).  With the suffix m the
+solve is the multigrid-preconditioned one (general operator; the cycle
+parameters of the benchmark).  Calls only oracle/
 (the solver) and matrix_free_pcg_amd.workloads (the seeded inputs).
 
     python tests/golden/make_fullsize_reference.py 4      # varying-1024x1024x128
+    python tests/golden/make_fullsize_reference.py 6m     # general-1024x1024x128, multigrid
 """
 import json
 import os
@@ -30,11 +33,17 @@ def sample_indices(n: int) -> np.ndarray:
     return np.sort(np.random.default_rng(SAMPLE_SEED).choice(n, size=SAMPLES, replace=False))
 
 
-def main(cfg: int) -> str:
+# the multigrid-preconditioned solve with the benchmark's cycle parameters
+MG_PARAMS = dict(nu=1, omega=0.9, max_levels=5, coarse_sweeps=64)
+
+
+def main(cfg: int, mg: bool = False) -> str:
     w = W.make_workload(cfg)
     p = w.problem
     t = time.time()
-    if isinstance(p, W.GeneralProblem):
+    if mg:
+        ref = oracle.pcg_mg(p, w.rhs, tol=w.tol, maxit=w.maxit, **MG_PARAMS)
+    elif isinstance(p, W.GeneralProblem):
         ref = oracle.pcg_gen(p, w.rhs, tol=w.tol, maxit=w.maxit)
     else:
         ref = oracle.pcg(p, w.rhs, tol=w.tol, maxit=w.maxit)
@@ -49,7 +58,9 @@ def main(cfg: int) -> str:
         "x_sample": [float(v) for v in x[idx]],
         "oracle_seconds": round(time.time() - t, 1),
     }
-    path = os.path.join(HERE, f"fullsize_{w.name}.json")
+    if mg:
+        out["mg"] = MG_PARAMS
+    path = os.path.join(HERE, f"fullsize_{w.name}{'_mg' if mg else ''}.json")
     with open(path, "w") as f:
         json.dump(out, f)
     return path
@@ -57,4 +68,4 @@ def main(cfg: int) -> str:
 
 if __name__ == "__main__":
     for a in sys.argv[1:] or ["4"]:
-        print(main(int(a)), flush=True)
+        print(main(int(a.rstrip("m")), mg=a.endswith("m")), flush=True)

@@ -308,3 +308,43 @@ def test_full_solve_against_oracle_reference(dev, cfg4, cfg):
     assert dev_hist <= 1e-6
     assert rel <= 1e-9
     assert rel_norm <= 1e-9
+
+
+def test_mg_full_solve_against_oracle_reference(dev):
+    """The multigrid-preconditioned solve of general-1024x1024x128 with the
+    benchmark's cycle against the oracle's complete multigrid solve, stored
+    by tests/golden/make_fullsize_reference.py: step counts within 1, the
+    residual histories within 1e-6 relative while ||r_k|| >= 1e-6 ||r_0||,
+    the final iterate within rel-L2 1e-9 on 4096 seeded positions and its
+    2-norm within 1e-9 (the bars of the smaller multigrid solve tests)."""
+    import torch
+    ref = _reference(W.CONFIG_NAMES[6] + "_mg")
+    w = W.make_workload(6)
+    assert ref["workload"] == w.name and ref["status"] == 0
+    h = mf.pcg_create(w.problem)
+    try:
+        mf.pcg_mg_setup(h, **ref["mg"])
+        bd = to_dev(w.rhs, dev)
+        xd = torch.zeros_like(bd)
+        res = mf.pcg_solve_mg(h, bd, xd, w.tol, w.maxit)
+        torch.cuda.synchronize()
+        xg = to_host(xd).reshape(-1)
+        del bd, xd
+    finally:
+        mf.pcg_destroy(h)
+    assert res["status"] == mf.PCG_OK, res
+    assert abs(res["iters"] - ref["iters"]) <= 1, (res["iters"], ref["iters"])
+    ho = np.asarray(ref["hist"])
+    n = min(len(ho), len(res["hist"]))
+    hg, ho = res["hist"][:n], ho[:n]
+    big = ho >= 1e-6 * ho[0]
+    dev_hist = np.max(np.abs(hg[big] - ho[big]) / ho[big])
+    idx = np.asarray(ref["sample_index"])
+    xs, xo = xg[idx], np.asarray(ref["x_sample"])
+    rel = np.linalg.norm(xs - xo) / np.linalg.norm(xo)
+    rel_norm = abs(np.linalg.norm(xg) - ref["x_norm2"]) / ref["x_norm2"]
+    print(f"[{w.name} mg] iters gpu={res['iters']} oracle={ref['iters']} history {dev_hist:.2e} "
+          f"samples rel-L2 {rel:.2e} norm {rel_norm:.2e}", flush=True)
+    assert dev_hist <= 1e-6
+    assert rel <= 1e-9
+    assert rel_norm <= 1e-9
