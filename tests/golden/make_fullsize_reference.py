@@ -6,11 +6,13 @@ Stored: the step count and status, the whole residual history ||r_k||_2, the
 2-norm of the final iterate and its values at 4096 seeded positions (numpy
 default_rng(20261202) over the field's linear indices).  With the suffix m the
 solve is the multigrid-preconditioned one (general operator; the cycle
-parameters of the benchmark).  Calls only oracle/
+parameters of the benchmark); with the suffix f it is the binary32 solve to
+tol 1e-5.  Calls only oracle/
 (the solver) and matrix_free_pcg_amd.workloads (the seeded inputs).
 
     python tests/golden/make_fullsize_reference.py 4      # varying-1024x1024x128
     python tests/golden/make_fullsize_reference.py 6m     # general-1024x1024x128, multigrid
+    python tests/golden/make_fullsize_reference.py 4f     # varying-1024x1024x128, binary32
 """
 import json
 import os
@@ -37,20 +39,27 @@ def sample_indices(n: int) -> np.ndarray:
 MG_PARAMS = dict(nu=1, omega=0.9, max_levels=5, coarse_sweeps=64)
 
 
-def main(cfg: int, mg: bool = False) -> str:
+# the binary32 solve: the right-hand side rounded to binary32, the benchmark's
+# tolerance for it (1e-10 is below binary32 rounding)
+F32_TOL = 1e-5
+
+
+def main(cfg: int, mg: bool = False, f32: bool = False) -> str:
     w = W.make_workload(cfg)
     p = w.problem
     t = time.time()
-    if mg:
+    if f32:
+        ref = oracle.pcg_f32(p, w.rhs.astype(np.float32), tol=F32_TOL, maxit=w.maxit)
+    elif mg:
         ref = oracle.pcg_mg(p, w.rhs, tol=w.tol, maxit=w.maxit, **MG_PARAMS)
     elif isinstance(p, W.GeneralProblem):
         ref = oracle.pcg_gen(p, w.rhs, tol=w.tol, maxit=w.maxit)
     else:
         ref = oracle.pcg(p, w.rhs, tol=w.tol, maxit=w.maxit)
-    x = ref["x"].reshape(-1)
+    x = ref["x"].reshape(-1).astype(np.float64)
     idx = sample_indices(x.size)
     out = {
-        "workload": w.name, "tol": w.tol, "maxit": w.maxit,
+        "workload": w.name, "tol": F32_TOL if f32 else w.tol, "maxit": w.maxit,
         "iters": int(ref["iters"]), "status": int(ref["status"]),
         "hist": [float(v) for v in ref["hist"]],
         "x_norm2": float(np.linalg.norm(x)),
@@ -60,7 +69,8 @@ def main(cfg: int, mg: bool = False) -> str:
     }
     if mg:
         out["mg"] = MG_PARAMS
-    path = os.path.join(HERE, f"fullsize_{w.name}{'_mg' if mg else ''}.json")
+    suffix = "_mg" if mg else ("_f32" if f32 else "")
+    path = os.path.join(HERE, f"fullsize_{w.name}{suffix}.json")
     with open(path, "w") as f:
         json.dump(out, f)
     return path
@@ -68,4 +78,4 @@ def main(cfg: int, mg: bool = False) -> str:
 
 if __name__ == "__main__":
     for a in sys.argv[1:] or ["4"]:
-        print(main(int(a.rstrip("m")), mg=a.endswith("m")), flush=True)
+        print(main(int(a.rstrip("mf")), mg=a.endswith("m"), f32=a.endswith("f")), flush=True)

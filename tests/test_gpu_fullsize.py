@@ -269,9 +269,11 @@ def _reference(name):
         return json.load(f)
 
 
+@pytest.mark.parametrize("solver", ["interleaved", "standard", "no_q"])
 @pytest.mark.parametrize("cfg", [4])
-def test_full_solve_against_oracle_reference(dev, cfg4, cfg):
-    """The whole benchmark solve at full size against the oracle's complete
+def test_full_solve_against_oracle_reference(dev, cfg4, cfg, solver):
+    """The whole benchmark solve at full size (and the standard and q-free
+    loops, which compute the same iterates) against the oracle's complete
     solve of the same workload (tests/golden/fullsize_<workload>.json, written
     by tests/golden/make_fullsize_reference.py, which calls only the oracle):
     step counts within 1; the residual histories within 1e-6 relative while
@@ -286,7 +288,8 @@ def test_full_solve_against_oracle_reference(dev, cfg4, cfg):
     try:
         bd = to_dev(w.rhs, dev)
         xd = torch.zeros_like(bd)
-        res = mf.pcg_solve(h, bd, xd, w.tol, w.maxit)
+        fn = {"interleaved": mf.pcg_solve, "standard": mf.pcg_solve_standard, "no_q": mf.pcg_solve_no_q}[solver]
+        res = fn(h, bd, xd, w.tol, w.maxit)
         torch.cuda.synchronize()
         xg = to_host(xd).reshape(-1)
         del bd, xd
@@ -303,7 +306,7 @@ def test_full_solve_against_oracle_reference(dev, cfg4, cfg):
     xs, xo = xg[idx], np.asarray(ref["x_sample"])
     rel = np.linalg.norm(xs - xo) / np.linalg.norm(xo)
     rel_norm = abs(np.linalg.norm(xg) - ref["x_norm2"]) / ref["x_norm2"]
-    print(f"[{w.name}] iters gpu={res['iters']} oracle={ref['iters']} history {dev_hist:.2e} "
+    print(f"[{w.name} {solver}] iters gpu={res['iters']} oracle={ref['iters']} history {dev_hist:.2e} "
           f"samples rel-L2 {rel:.2e} norm {rel_norm:.2e}", flush=True)
     assert dev_hist <= 1e-6
     assert rel <= 1e-9
