@@ -7,12 +7,15 @@ Stored: the step count and status, the whole residual history ||r_k||_2, the
 default_rng(20261202) over the field's linear indices).  With the suffix m the
 solve is the multigrid-preconditioned one (general operator; the cycle
 parameters of the benchmark); with the suffix f it is the binary32 solve to
-tol 1e-5.  Calls only oracle/
+tol 1e-5; with the suffix x it is the binary64 solve with the binary32 column solve
+(the mixed-precision solve).  --out DIR writes there instead of beside this script.
+Calls only oracle/
 (the solver) and matrix_free_pcg_amd.workloads (the seeded inputs).
 
     python tests/golden/make_fullsize_reference.py 4      # varying-1024x1024x128
     python tests/golden/make_fullsize_reference.py 6m     # general-1024x1024x128, multigrid
     python tests/golden/make_fullsize_reference.py 4f     # varying-1024x1024x128, binary32
+    python tests/golden/make_fullsize_reference.py 4x     # varying-1024x1024x128, mixed
 """
 import json
 import os
@@ -44,12 +47,14 @@ MG_PARAMS = dict(nu=1, omega=0.9, max_levels=5, coarse_sweeps=64)
 F32_TOL = 1e-5
 
 
-def main(cfg: int, mg: bool = False, f32: bool = False) -> str:
+def main(cfg: int, mg: bool = False, f32: bool = False, mixed: bool = False, out_dir: str = HERE) -> str:
     w = W.make_workload(cfg)
     p = w.problem
     t = time.time()
     if f32:
         ref = oracle.pcg_f32(p, w.rhs.astype(np.float32), tol=F32_TOL, maxit=w.maxit)
+    elif mixed:
+        ref = oracle.pcg_mixed(p, w.rhs, tol=w.tol, maxit=w.maxit)
     elif mg:
         ref = oracle.pcg_mg(p, w.rhs, tol=w.tol, maxit=w.maxit, **MG_PARAMS)
     elif isinstance(p, W.GeneralProblem):
@@ -69,13 +74,20 @@ def main(cfg: int, mg: bool = False, f32: bool = False) -> str:
     }
     if mg:
         out["mg"] = MG_PARAMS
-    suffix = "_mg" if mg else ("_f32" if f32 else "")
-    path = os.path.join(HERE, f"fullsize_{w.name}{suffix}.json")
+    suffix = "_mg" if mg else ("_f32" if f32 else ("_mixed" if mixed else ""))
+    path = os.path.join(out_dir, f"fullsize_{w.name}{suffix}.json")
     with open(path, "w") as f:
         json.dump(out, f)
     return path
 
 
 if __name__ == "__main__":
-    for a in sys.argv[1:] or ["4"]:
-        print(main(int(a.rstrip("mf")), mg=a.endswith("m"), f32=a.endswith("f")), flush=True)
+    args = sys.argv[1:]
+    out_dir = HERE
+    if "--out" in args:
+        i = args.index("--out")
+        out_dir = args[i + 1]
+        del args[i:i + 2]
+    for a in args or ["4"]:
+        print(main(int(a.rstrip("mfx")), mg=a.endswith("m"), f32=a.endswith("f"), mixed=a.endswith("x"),
+                   out_dir=out_dir), flush=True)

@@ -400,3 +400,41 @@ def test_f32_full_solve_against_oracle_reference(dev, cfg4):
           flush=True)
     assert dev_hist <= max(1e-4, 10 * f)
     assert err_g <= 1.5 * err_o + 1e-6
+
+
+def test_mixed_full_solve_against_oracle_reference(dev, cfg4):
+    """The mixed-precision solve (binary64 CG, binary32 column solve) of
+    varying-1024x1024x128 against the oracle's complete mixed solve, stored
+    by the committed script, with the bars of the smaller mixed solve tests:
+    converged with the true residual ||b - A x||/||b|| <= 10 tol (evaluated
+    by the oracle's binary64 stencil), the step count within 20 % + 2 of the
+    oracle's mixed and binary64 counts, and the iterate at the 4096 stored
+    positions within 1e-8 rel-L2 of the oracle's mixed iterate.  The two
+    column solves round differently (segmented scans against one sequential
+    sweep), so the trajectories are not compared step by step."""
+    import torch
+    ref = _reference(W.CONFIG_NAMES[4] + "_mixed")
+    ref64 = _reference(W.CONFIG_NAMES[4])
+    w = cfg4
+    h = mf.pcg_create(w.problem)
+    try:
+        bd = to_dev(w.rhs, dev)
+        xd = torch.zeros_like(bd)
+        res = mf.pcg_solve_mixed(h, bd, xd, w.tol, w.maxit)
+        torch.cuda.synchronize()
+        xg = to_host(xd).reshape(-1)
+        del bd, xd
+    finally:
+        mf.pcg_destroy(h)
+    assert res["status"] == mf.PCG_OK == ref["status"], (res, ref["status"])
+    lo, hi = min(ref["iters"], ref64["iters"]), max(ref["iters"], ref64["iters"])
+    assert 0.8 * lo - 2 <= res["iters"] <= 1.2 * hi + 2, (res["iters"], ref["iters"], ref64["iters"])
+    tr = _true_residual(w.problem, w.rhs, xg.reshape(w.rhs.shape))
+    idx = np.asarray(ref["sample_index"])
+    xo = np.asarray(ref["x_sample"])
+    rel = np.linalg.norm(xg[idx] - xo) / np.linalg.norm(xo)
+    nrm = abs(np.linalg.norm(xg) - ref["x_norm2"]) / ref["x_norm2"]
+    print(f"[{w.name} mixed] iters gpu={res['iters']} oracle={ref['iters']} (binary64 {ref64['iters']}) "
+          f"true residual {tr:.2e} samples rel-L2 {rel:.2e} norm {nrm:.2e}", flush=True)
+    assert tr <= 10 * w.tol, tr
+    assert rel <= 1e-8 and nrm <= 1e-8, (rel, nrm)
