@@ -7,7 +7,9 @@ Stored: the step count and status, the whole residual history ||r_k||_2, the
 default_rng(20261202) over the field's linear indices).  With the suffix m the
 solve is the multigrid-preconditioned one (general operator; the cycle
 parameters of the benchmark); with the suffix f it is the binary32 solve to
-tol 1e-5; with the suffix x it is the binary64 solve with the binary32 column solve
+tol 1e-5, and the script also stores the oracle's history for b perturbed at
+binary32's rounding level, (b (1 + 2^-23 u)) rounded to binary32 with u uniform in [-1, 1]
+(default_rng(4242)): the spread of two correct binary32 runs; with the suffix x it is the binary64 solve with the binary32 column solve
 (the mixed-precision solve).  --out DIR writes there instead of beside this script.
 Calls only oracle/
 (the solver) and matrix_free_pcg_amd.workloads (the seeded inputs).
@@ -45,6 +47,19 @@ MG_PARAMS = dict(nu=1, omega=0.9, max_levels=5, coarse_sweeps=64)
 # the binary32 solve: the right-hand side rounded to binary32, the benchmark's
 # tolerance for it (1e-10 is below binary32 rounding)
 F32_TOL = 1e-5
+SPREAD_SEED = 4242
+
+
+def _f32_solves(p, b, maxit):
+    """The binary32 solve of b and of b perturbed at binary32's rounding
+    level, side by side (each is one call into the oracle's C code)."""
+    from concurrent.futures import ThreadPoolExecutor
+    u = np.random.default_rng(SPREAD_SEED).uniform(-1.0, 1.0, size=b.shape)
+    bs = (b * (1.0 + 2.0 ** -23 * u)).astype(np.float32)
+    with ThreadPoolExecutor(2) as ex:
+        f0 = ex.submit(oracle.pcg_f32, p, b.astype(np.float32), tol=F32_TOL, maxit=maxit)
+        f1 = ex.submit(oracle.pcg_f32, p, bs, tol=F32_TOL, maxit=maxit)
+        return f0.result(), f1.result()
 
 
 def main(cfg: int, mg: bool = False, f32: bool = False, mixed: bool = False, out_dir: str = HERE) -> str:
@@ -52,7 +67,7 @@ def main(cfg: int, mg: bool = False, f32: bool = False, mixed: bool = False, out
     p = w.problem
     t = time.time()
     if f32:
-        ref = oracle.pcg_f32(p, w.rhs.astype(np.float32), tol=F32_TOL, maxit=w.maxit)
+        ref, spread = _f32_solves(p, w.rhs, w.maxit)
     elif mixed:
         ref = oracle.pcg_mixed(p, w.rhs, tol=w.tol, maxit=w.maxit)
     elif mg:
@@ -74,6 +89,9 @@ def main(cfg: int, mg: bool = False, f32: bool = False, mixed: bool = False, out
     }
     if mg:
         out["mg"] = MG_PARAMS
+    if f32:
+        out["spread_seed"] = SPREAD_SEED
+        out["hist_spread"] = [float(v) for v in spread["hist"]]
     suffix = "_mg" if mg else ("_f32" if f32 else ("_mixed" if mixed else ""))
     path = os.path.join(out_dir, f"fullsize_{w.name}{suffix}.json")
     with open(path, "w") as f:

@@ -356,14 +356,17 @@ def test_mg_full_solve_against_oracle_reference(dev):
 def test_f32_full_solve_against_oracle_reference(dev, cfg4):
     """The binary32 solve of varying-1024x1024x128 (tol 1e-5) against the
     oracle's complete binary32 solve, stored by the committed script: step
-    counts within 2 and the residual histories within max(1e-4, 10 f) while
-    ||r_k|| >= 1e-3 ||r_0||, f the binary32 column solve's forward error on
-    b; at the 4096 stored positions, the iterate's distance to the binary64
-    solution (the oracle's stored binary64 solve) at most 1.5 times the
-    oracle's binary32 iterate's plus 1e-6 -- the bars of the smaller binary32
-    solve tests.  Two correct binary32 runs round differently, so their
-    iterates agree only to the accuracy that binary32 reaches; an error in
-    the operator or the column solve shows far above these bars."""
+    counts within 2; at the 4096 stored positions, the iterate's distance to
+    the binary64 solution (the oracle's stored binary64 solve) at most 1.5
+    times the oracle's binary32 iterate's plus 1e-6 (the bars of the smaller
+    binary32 solve tests); the residual histories, while ||r_k|| >= 1e-3
+    ||r_0||, within max(1e-4, 10 f, 10 s), f the binary32 column solve's
+    forward error on b and s the oracle's own deviation when b is perturbed
+    at binary32's rounding level (stored beside its history).  Over the 373
+    steps the rounding differences of two correct binary32 runs compound to
+    about 1e-2 in the history, more than the 10 f that bounds the shorter
+    solves; an error in the operator or the column solve shows far above
+    these bars."""
     import torch
     ref = _reference(W.CONFIG_NAMES[4] + "_f32")
     ref64 = _reference(W.CONFIG_NAMES[4])
@@ -389,6 +392,11 @@ def test_f32_full_solve_against_oracle_reference(dev, cfg4):
     hg, ho = np.asarray(res["hist"][:n]), ho[:n]
     big = ho >= 1e-3 * ho[0]
     dev_hist = np.max(np.abs(hg[big] - ho[big]) / ho[big])
+    hs = np.asarray(ref["hist_spread"])
+    m = min(n, len(hs))
+    bs = big[:m]
+    spread = np.max(np.abs(hs[:m][bs] - ho[:m][bs]) / ho[:m][bs])
+    bar = max(1e-4, 10 * f, 10 * spread)
     idx = np.asarray(ref["sample_index"])
     assert np.array_equal(idx, np.asarray(ref64["sample_index"]))
     xs64 = np.asarray(ref64["x_sample"])
@@ -396,9 +404,9 @@ def test_f32_full_solve_against_oracle_reference(dev, cfg4):
     err_g = np.linalg.norm(xg[idx] - xs64) / nrm
     err_o = np.linalg.norm(np.asarray(ref["x_sample"]) - xs64) / nrm
     print(f"[{w.name} f32] iters gpu={res['iters']} oracle={ref['iters']} history {dev_hist:.2e} "
-          f"(bar {max(1e-4, 10 * f):.2e}) distance to binary64 x: gpu {err_g:.2e} oracle {err_o:.2e}",
+          f"(f {f:.2e}, oracle's spread {spread:.2e}) distance to binary64 x: gpu {err_g:.2e} oracle {err_o:.2e}",
           flush=True)
-    assert dev_hist <= max(1e-4, 10 * f)
+    assert dev_hist <= bar, (dev_hist, bar)
     assert err_g <= 1.5 * err_o + 1e-6
 
 
