@@ -13,6 +13,7 @@ Options for profiling helpers:
   --copy-calibration   run only a plain 1 GiB device copy (counter calibration)
   --stream-probe       run only the streaming-bandwidth probe (lib/libmfprobe.so): the GB/s a
                        plain kernel reaches for the solver's read/write stream mixes
+                       (--stream-probe-dtype f32: with 4-byte elements, the binary32 passes)
   --no-cpu-baseline    skip timing the CPU oracle
 """
 from __future__ import annotations
@@ -231,6 +232,9 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--stream-probe", action="store_true")
+    ap.add_argument("--stream-probe-dtype", choices=["f64", "f32"], default="f64",
+                    help="element of the probe's vectors: f64 (8-byte accesses, the binary64 passes) or "
+                         "f32 (4-byte, the binary32 passes); 1 GiB vectors either way")
     ap.add_argument("--fixed-iterations", type=int, default=0,
                     help="run exactly N CG steps per solve (tol 0) instead of solving to 1e-10")
     return ap.parse_args()
@@ -262,11 +266,11 @@ PROBE_MIXES = [(1, 1, "copy"), (2, 1, "residual r = b - A x"), (2, 2, "column pa
                (5, 3, "stencil pass, even steps (z, p, q, x, p' -> p, q, x)")]
 
 
-def stream_probe(n=1 << 27, reps=20):
+def stream_probe(dtype="f64", vector_bytes=1 << 30, reps=20):
     """GB/s of a plain streaming kernel (every element read / written once,
     loads batched before stores) for each stream mix of the solver's passes,
-    with non-temporal and with ordinary loads and stores, on vectors of n
-    float64 (1 GiB at the default): the best over 1, 2, 4 or 8 elements per
+    with non-temporal and with ordinary loads and stores, on vectors of
+    float64 or float32 elements (`dtype`, 1 GiB each at the default): the best over 1, 2, 4 or 8 elements per
     thread and 256- or 1024-thread workgroups.  The solver's passes add what a
     stream kernel does not have (neighbour reads, the column recurrences), so
     these rates are the measured ceiling for each mix, beside the published
@@ -277,12 +281,16 @@ def stream_probe(n=1 << 27, reps=20):
     if not os.path.exists(hipbuild.PROBE_LIB):
         raise SystemExit(f"{hipbuild.PROBE_LIB} is not built (python -m matrix_free_pcg_amd.build)")
     lib = ctypes.CDLL(hipbuild.PROBE_LIB)
-    lib.mfprobe_stream.restype = ctypes.c_int
-    lib.mfprobe_stream.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+    fn = lib.mfprobe_stream_f32 if dtype == "f32" else lib.mfprobe_stream
+    esize = 4 if dtype == "f32" else 8
+    n = vector_bytes // esize
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int32, ctypes.c_int64,
                                    ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                    ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
-    vec = [torch.full((n,), 1.0 + k, dtype=torch.float64, device="cuda") for k in range(8)]
+    tdt = torch.float32 if dtype == "f32" else torch.float64
+    vec = [torch.full((n,), 1.0 + k, dtype=tdt, device="cuda") for k in range(8)]
     torch.cuda.synchronize()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     out = []
@@ -295,10 +303,10 @@ def stream_probe(n=1 << 27, reps=20):
             for elems in (1, 2, 4, 8):
                 for block in (256, 1024):
                     ms = ctypes.c_double(0.0)
-                    rc = lib.mfprobe_stream(r, w, nt, elems, block, n, ins, outs, reps, stream, ctypes.byref(ms))
+                    rc = fn(r, w, nt, elems, block, n, ins, outs, reps, stream, ctypes.byref(ms))
                     if rc != 0:
-                        raise SystemExit(f"mfprobe_stream({r}, {w}, nt={nt}, {elems}, {block}) returned {rc}")
-                    gbps = (r + w) * n * 8 / (ms.value * 1e-3) / 1e9
+                        raise SystemExit(f"mfprobe_stream[{dtype}]({r}, {w}, nt={nt}, {elems}, {block}) returned {rc}")
+                    gbps = (r + w) * n * esize / (ms.value * 1e-3) / 1e9
                     if best is None or gbps > best[0]:
                         best = (gbps, elems, block)
             key = "nontemporal" if nt else "ordinary"
@@ -307,7 +315,7 @@ def stream_probe(n=1 << 27, reps=20):
         out.append(row)
         print(json.dumps(row), flush=True)
     torch.cuda.synchronize()
-    print(json.dumps({"stream_probe": out, "vector_bytes": n * 8, "reps": reps}), flush=True)
+    print(json.dumps({"stream_probe": out, "dtype": dtype, "vector_bytes": n * esize, "reps": reps}), flush=True)
 
 
 def cpu_baseline(w, steps, variant="interleaved", mg_params=None):
@@ -444,7 +452,7 @@ def main():
         copy_calibration()
         return
     if args.stream_probe:
-        stream_probe()
+        stream_probe(args.stream_probe_dtype)
         return
 
     if args.config == 5:

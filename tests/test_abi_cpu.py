@@ -179,18 +179,18 @@ def test_stream_probe_rejects_bad_arguments():
     if not os.path.exists(hipbuild.PROBE_LIB):
         hipbuild.build()
     probe = ctypes.CDLL(hipbuild.PROBE_LIB)
-    f = probe.mfprobe_stream
-    f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                  ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
-                  ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
-    ins = (ctypes.c_void_p * 5)(*([ctypes.c_void_p(4096)] * 5))
-    outs = (ctypes.c_void_p * 3)(*([ctypes.c_void_p(8192)] * 3))
-    ms = ctypes.c_double(0.0)
-    for r, w, e, b, n, reps in [(0, 1, 4, 256, 1024, 1), (6, 1, 4, 256, 1024, 1), (1, 0, 4, 256, 1024, 1),
-                                (1, 4, 4, 256, 1024, 1), (1, 1, 3, 256, 1024, 1), (1, 1, 4, 100, 1024, 1),
-                                (1, 1, 4, 2048, 8192, 1), (1, 1, 4, 256, 1000, 1), (1, 1, 4, 256, 0, 1),
-                                (1, 1, 4, 256, 1024, 0)]:
-        assert f(r, w, 1, e, b, n, ins, outs, reps, None, ctypes.byref(ms)) == -1, (r, w, e, b, n, reps)
-    nulls = (ctypes.c_void_p * 5)()
-    assert f(2, 1, 1, 4, 256, 1024, nulls, outs, 1, None, ctypes.byref(ms)) == -1
+    for f in (probe.mfprobe_stream, probe.mfprobe_stream_f32):   # float64 and float32 elements
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                      ctypes.c_int64, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                      ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
+        ins = (ctypes.c_void_p * 5)(*([ctypes.c_void_p(4096)] * 5))
+        outs = (ctypes.c_void_p * 3)(*([ctypes.c_void_p(8192)] * 3))
+        ms = ctypes.c_double(0.0)
+        for r, w, e, b, n, reps in [(0, 1, 4, 256, 1024, 1), (6, 1, 4, 256, 1024, 1), (1, 0, 4, 256, 1024, 1),
+                                    (1, 4, 4, 256, 1024, 1), (1, 1, 3, 256, 1024, 1), (1, 1, 4, 100, 1024, 1),
+                                    (1, 1, 4, 2048, 8192, 1), (1, 1, 4, 256, 1000, 1), (1, 1, 4, 256, 0, 1),
+                                    (1, 1, 4, 256, 1024, 0)]:
+            assert f(r, w, 1, e, b, n, ins, outs, reps, None, ctypes.byref(ms)) == -1, (r, w, e, b, n, reps)
+        nulls = (ctypes.c_void_p * 5)()
+        assert f(2, 1, 1, 4, 256, 1024, nulls, outs, 1, None, ctypes.byref(ms)) == -1
