@@ -15,11 +15,16 @@ Facts used (source: Mueller, Guo, Scheichl, Shi 2013, sections 3-4):
   K4  symmetry, positivity, Gershgorin bound; the energy (quadratic form)
       written face by face with the mean face coefficient;
   K5  M^{-1} inverts exactly A's diagonal column block (dense solve);
-  K6  converged PCG equals a dense Cholesky solve;
+  K6  converged PCG equals a dense Cholesky solve of A assembled face by face
+      from the operator's definition (not from apply_A);
   K7  finite termination: steps <= number of distinct eigenvalues of M^{-1}A;
   K8  CG invariants: M^{-1}-orthogonal residuals, A-conjugate directions,
       monotone A-norm error;
-  K9  manufactured solution recovered to within cond(A)*tol.
+  K9  manufactured solution recovered to within cond(A)*tol;
+  D1  the binary64 dot is a compensated sum: with exactly representable
+      products it is within one rounding of the exact sum (math.fsum) even
+      under cancellation that loses every digit of a plain running sum, and
+      for general operands within the rounding of the products.
 Binary32 and mixed-precision functions (section 7 runs the solver in single
 precision as well):
   F1  on dyadic coefficients and integer fields every binary32 operation of
@@ -206,6 +211,41 @@ def dense_from_apply(orc, prob):
     return A
 
 
+def dense_from_formula(prob):
+    """A assembled face by face from the operator's definition: delta on the
+    diagonal; for every horizontal face the mean of the two cells' alpha_h,
+    for every interior vertical face f (between levels f-1 and f) alpha_z[f],
+    each added to the diagonal of both cells and subtracted from their
+    coupling; i and j wrap periodically, faces 0 and nz carry nothing.  A face
+    whose two cells coincide (a periodic direction of one cell) contributes
+    nothing, as u - u = 0."""
+    nx, ny, nz = prob.nx, prob.ny, prob.nz
+    ah = prob.alpha_h_field()
+    az = prob.alpha_z_face
+    A = np.zeros((prob.n, prob.n))
+
+    def at(i, j, k):
+        return i + nx * (k + nz * j)
+
+    def face(l, m, c):
+        A[l, l] += c
+        A[m, m] += c
+        A[l, m] -= c
+        A[m, l] -= c
+
+    for j in range(ny):
+        for k in range(nz):
+            for i in range(nx):
+                l = at(i, j, k)
+                A[l, l] += prob.delta
+                # each face once: the one towards i+1, j+1 and k+1
+                face(l, at((i + 1) % nx, j, k), 0.5 * (ah[j, i] + ah[j, (i + 1) % nx]))
+                face(l, at(i, (j + 1) % ny, k), 0.5 * (ah[j, i] + ah[(j + 1) % ny, i]))
+                if k + 1 < nz:
+                    face(l, at(i, j, k + 1), az[k + 1])
+    return A
+
+
 def pin_k5_column_block(orc):
     """M^{-1} inverts A's diagonal column block: for r supported on one column,
     z = M^{-1} r is supported on that column and (A z) on it equals r; and z
@@ -242,8 +282,11 @@ def pin_k6_cholesky(orc):
     cases = [((3, 4, 5), 0.1, 5.0), ((4, 4, 4), 0.1, 10.0), ((6, 5, 3), 0.3, 2.0), ((4, 3, 6), 1e-3, 1e3)]
     for (nx, ny, nz), delta, azs in cases:
         prob = varying_problem(nx, ny, nz, delta=delta, seed=nx + ny, az_scale=azs)
-        A = dense_from_apply(orc, prob)
-        assert np.abs(A - A.T).max() <= 1e-14 * np.abs(A).max(), "K6 symmetric"
+        A = dense_from_formula(prob)
+        # the oracle's stencil applied to unit vectors gives the same matrix (each
+        # entry is one face value or a sum of a few: rounding order only)
+        Aa = dense_from_apply(orc, prob)
+        assert np.abs(Aa - A).max() <= 16 * EPS * np.abs(A).max(), "K6 stencil = formula"
         c = sla.cho_factor(A)
         b = _rand((ny, nz, nx), 99 + nx)
         xc = sla.cho_solve(c, b.ravel()).reshape(b.shape)
@@ -261,6 +304,42 @@ def pin_k6_cholesky(orc):
         assert abs(res0["hist"][0] - np.linalg.norm(r0)) <= 1e-12 * np.linalg.norm(r0), "K6 warm r0"
         err0 = np.linalg.norm(res0["x"] - xc) / np.linalg.norm(xc)
         assert err0 <= max(1e-11, 100 * cond * EPS), ("K6 warm", (nx, ny, nz), err0, cond)
+
+
+def pin_d1_dot(orc):
+    from fractions import Fraction
+    rng = np.random.default_rng(2024)
+    # integer-valued operands: every product is exact, so the exact dot is the
+    # exact sum of the products, and a compensated sum lands within one
+    # rounding of it.  Large terms that cancel leave a small exact sum that a
+    # plain running sum loses entirely.
+    for n in [1, 2, 9, 1000, 4096]:
+        big = rng.integers(-2 ** 26, 2 ** 26, size=n).astype(np.float64) * 2.0 ** 24
+        a = np.concatenate([big, -big, rng.integers(-9, 10, size=n).astype(np.float64)])
+        b = np.concatenate([np.ones(n), np.ones(n), rng.integers(-9, 10, size=n).astype(np.float64)])
+        perm = rng.permutation(a.size)
+        a, b = a[perm], b[perm]
+        exact = math.fsum(float(u) * float(v) for u, v in zip(a, b))
+        got = orc.dot(a, b)
+        assert abs(got - exact) <= EPS * abs(exact), ("D1 cancellation", n, got, exact)
+    # the classic case that also separates Neumaier's branch from Kahan's
+    a = np.array([1.0, 1e100, 1.0, -1e100])
+    assert orc.dot(a, np.ones(4)) == 2.0, "D1 Neumaier"
+    # a small term after a large one of the opposite trend
+    a = np.array([2.0 ** 53, 1.0, -(2.0 ** 53), 0.5])
+    assert orc.dot(a, np.ones(4)) == 1.5, "D1 order"
+    # general operands: the products round (half an ulp each), the sum does not
+    for n in [3, 257, 5000]:
+        a = rng.uniform(-1e3, 1e3, size=n)
+        b = rng.uniform(-1, 1, size=n)
+        exact = float(sum(Fraction(float(u)) * Fraction(float(v)) for u, v in zip(a, b)))
+        scale = math.fsum(abs(float(u) * float(v)) for u, v in zip(a, b))
+        got = orc.dot(a, b)
+        assert abs(got - exact) <= 0.5 * EPS * scale + EPS * abs(exact), ("D1 general", n, got, exact)
+    # both operands count: <a, b> differs from <a, a> and <b, b>
+    a = np.array([3.0, -1.0, 2.0])
+    b = np.array([0.5, 4.0, -2.0])
+    assert orc.dot(a, b) == -6.5 and orc.dot(b, a) == -6.5, "D1 operands"
 
 
 def pin_k7_finite_termination(orc):
@@ -712,7 +791,7 @@ def pin_m5_convergence(orc):
 
 ALL_PINS = [pin_k1_eigenmodes, pin_k2_constants, pin_k3_no_horizontal, pin_k4_symmetry_energy,
             pin_k5_column_block, pin_k6_cholesky, pin_k7_finite_termination, pin_k8_invariants,
-            pin_k9_manufactured, pin_stop_rule_and_breakdown, pin_f1_stencil_f32, pin_f2_precond_f32,
+            pin_k9_manufactured, pin_stop_rule_and_breakdown, pin_d1_dot, pin_f1_stencil_f32, pin_f2_precond_f32,
             pin_f3_dot_f32, pin_f4_pcg_f32, pin_f5_pcg_mixed, pin_g1_special_case, pin_g2_eigenmodes,
             pin_g3_constants, pin_g4_symmetry_energy, pin_g5_column_block_cholesky, pin_m1_galerkin,
             pin_m2_coarse_space, pin_m3_textbook_recursion, pin_m4_spd, pin_m5_convergence]

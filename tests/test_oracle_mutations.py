@@ -13,6 +13,10 @@ import oracle
 import oracle_pins as P
 
 MUTATIONS = {
+    "dot_no_compensation": ("    return s + c;\n}", "    (void)c;\n    return s;\n}"),
+    "dot_kahan_branch": ("        if (fabs(s) >= fabs(t))\n            c += (s - u) + t;\n        else\n            c += (t - u) + s;",
+                         "        c += (s - u) + t;"),
+    "dot_wrong_operand": ("        double t = a[l] * b[l];\n        double u = s + t;", "        double t = a[l] * a[l];\n        double u = s + t;"),
     "stencil_drop_ym": ("acc += face_ym(nx, ny, ah, i, j) * (u - x[at(nx, nz, i, jm, k)]);", ""),
     "stencil_vertical_sign": ("acc += az[k + 1] * (u - x[at(nx, nz, i, j, k + 1)]);",
                               "acc -= az[k + 1] * (u - x[at(nx, nz, i, j, k + 1)]);"),
