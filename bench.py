@@ -230,6 +230,8 @@ def parse():
     ap.add_argument("--mg-coarse-sweeps", type=int, default=64, help="mg: sweeps on the coarsest level")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
+    ap.add_argument("--cpu-steps-cfg5", type=int, default=1,
+                    help="--config 5: CG steps of the oracle's CPU baseline at 2048x2048x128")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--stream-probe", action="store_true")
     ap.add_argument("--stream-probe-dtype", choices=["f64", "f32"], default="f64",
@@ -435,6 +437,15 @@ def explicit_comparison(args):
                    "csr_ms": round(a_csr, 4), "csr_GBps": round(CSR_BYTES_PER_ROW * n / a_csr / 1e6, 1),
                    "speedup_matrix_free": round(a_csr / a_mf, 2)}
     mf.pcg_destroy(h)
+    del C, tri, ws, b, x, y
+    if not args.no_cpu_baseline:
+        # the oracle on one CG step of the same 2048x2048x128 problem (its
+        # 50-step solve takes about 20 minutes on one core)
+        t = time.perf_counter()
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_steps_cfg5)
+        out["cpu_baseline"]["matrix_free_speedup_vs_oracle"] = round(
+            out["matrix_free"]["iterations_per_s"] / out["cpu_baseline"]["value"], 1)
+        log(f"[bench] cpu baseline in {time.perf_counter() - t:.1f}s")
     print(json.dumps(out), flush=True)
 
 
@@ -503,6 +514,7 @@ def main():
         mf.pcg_mg_setup(h, **mg_params)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t
+    overrides = mf.pcg_tuning_overrides(h)   # MFPCG_* launch-shape variables set at creation (0: none)
     if args.variant == "mg":
         level_points = [mf.pcg_mg_level(h, l)[0] * mf.pcg_mg_level(h, l)[1] * prob.nz
                         for l in range(mf.pcg_mg_num_levels(h))]
@@ -632,6 +644,7 @@ def main():
                    "tol": tol, "maxit": maxit, "variant": args.variant,
                    "iterations_per_solve": iters, "status": res["status"],
                    "final_rel_res": res["final_rel_res"], "true_rel_res": true_rel,
+                   "tuning_overrides": overrides,
                    **({"mg": mg_params} if mg_params else {})},
         # algorithmic bytes of both passes over the whole timed region / its wall time
         "hbm_GBps_whole_solve": round(all_bytes / elapsed / 1e9, 1) if all_bytes else None,

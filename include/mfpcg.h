@@ -26,9 +26,16 @@
  *
  * Memory: every pointer named *_dev is device memory on the device that was
  * current when the handle was created; *_host pointers are host memory.  The
- * caller owns all vectors and the solve workspace.  The handle owns only
- * small coefficient tables: O(nz + (1 + ceil(nz/L)) * nx*ny) doubles,
- * allocated at pcg_create and freed at pcg_destroy.
+ * library allocates no device memory: the caller owns all vectors, the
+ * handle's coefficient tables (pcg_handle_bytes), the multigrid levels'
+ * tables (pcg_mg_setup_bytes), the stored column matrices
+ * (pcg_tridiag_bytes) and every solve workspace, and each buffer must stay
+ * allocated while the handle uses it (until pcg_destroy for the tables).
+ * Device buffers passed as tables or workspace must be 256-byte aligned
+ * (torch's allocations are).  Besides its host-side object the handle holds
+ * one 32-byte word of pinned host memory, to which the device writes each
+ * step's stop decision (hipHostMalloc at creation, freed at pcg_destroy),
+ * and one HIP event.
  *
  * Streams: every call is ordered on the handle's HIP stream (the one passed
  * to pcg_create, or pcg_set_stream).  pcg_apply_A and pcg_precond are
@@ -68,6 +75,36 @@ typedef struct {
     int32_t nx, ny, nz;
 } pcg_grid;
 
+/* Tuning variables.  pcg_create, pcg_create_general and pcg_handle_bytes
+ * read these environment variables; each changes the launch geometry (and
+ * with it the number of partial sums, so the last bits of dot products and
+ * of iterates), never the operator.  Unset or empty means the default.  They
+ * are measurement and test hooks: set them only to compare launch shapes.
+ *   MFPCG_COL_C      columns per column-pass workgroup, 32 or 64 (64)
+ *   MFPCG_COL_L      segment length of the column solve, 4/8/16/32 (the
+ *                    smallest of 8, 16, 32 that fits 1024 threads)
+ *   MFPCG_COL_LF     segment length of the column passes without a stored
+ *                    matrix, 1, 2 or 4 times MFPCG_COL_L, at most 32
+ *   MFPCG_ST_L       levels per wave of the stencil passes, 1/2/4/8 (4)
+ *   MFPCG_ST_W       waves per stencil workgroup, 1..16 (min(4, nz/4))
+ *   MFPCG_COL_FULL   0: never use the straight-line whole-tile column kernel
+ *   MFPCG_ST_FULL    0: never use the whole-tile stencil kernels
+ *   MFPCG_ST_JT      rows per fused stencil tile, 1, 4 or 8
+ *   MFPCG_COL_STRIP, MFPCG_ST_STRIP  i-tiles per strip of the tile order
+ *                    (one strip per XCD)
+ * pcg_tuning_overrides reports which of them were set when a handle was
+ * created, as a mask of these bits (0: every default): */
+#define PCG_TUNE_COL_C 0x001
+#define PCG_TUNE_COL_L 0x002
+#define PCG_TUNE_COL_LF 0x004
+#define PCG_TUNE_ST_L 0x008
+#define PCG_TUNE_ST_W 0x010
+#define PCG_TUNE_COL_FULL 0x020
+#define PCG_TUNE_ST_FULL 0x040
+#define PCG_TUNE_ST_JT 0x080
+#define PCG_TUNE_COL_STRIP 0x100
+#define PCG_TUNE_ST_STRIP 0x200
+
 /* Operator coefficients (section 3, eqs. (5)-(8); section 4.2, eq. (17)).
  *   delta         zero-order term, > 0
  *   alpha_z_face  HOST, nz+1 entries; face f lies between cells f-1 and f;
@@ -85,15 +122,27 @@ typedef struct {
     const double *alpha_h_field;
 } pcg_coeffs;
 
+/* Bytes of device memory the handle's tables need for this grid: the nz+1
+ * vertical faces, a and d per level, |T| and the two edge coefficients per
+ * column, and the Thomas multipliers at the column segments' boundaries in
+ * binary64 and binary32, O(nz + (3 + 1.5 (ceil(nz/L) - 1)) nx*ny) doubles
+ * (L: the segment length, 8 up to nz = 128).  0 for an invalid grid. */
+size_t pcg_handle_bytes(const pcg_grid *grid);
+
 /* Create a handle for one grid and operator (section 6: the coefficient
  * vectors are copied to the device once).  The operator is the special case
  * of the general form below with |T| = 1, a_k = delta, d_k = 1, beta = alpha_z
- * and the edge coefficient between two cells the mean of their alpha_h.  hip_stream: a hipStream_t, or
- * NULL for the null stream.  Returns PCG_ERR_INVALID for bad arguments,
- * PCG_ERR_UNSUPPORTED for nz > 512, PCG_ERR_HIP if a table allocation fails.
- * *out is NULL on failure. */
+ * and the edge coefficient between two cells the mean of their alpha_h.
+ *   hip_stream   a hipStream_t, or NULL for the null stream
+ *   tables_dev   caller-owned device memory of >= pcg_handle_bytes(grid)
+ *                bytes, 256-byte aligned, on the current device; the handle
+ *                writes its tables there and reads them until pcg_destroy
+ * Blocks until the tables are written.  Returns PCG_ERR_INVALID for bad
+ * arguments (also a missing, misaligned or short table buffer),
+ * PCG_ERR_UNSUPPORTED for nz > 512, PCG_ERR_HIP on a runtime error.  *out is
+ * NULL on failure. */
 int pcg_create(const pcg_grid *grid, const pcg_coeffs *coeffs, void *hip_stream,
-               pcg_handle **out);
+               void *tables_dev, size_t tables_bytes, pcg_handle **out);
 
 /* The operator with general tensor-product coefficients (section 3,
  * eqs. (5)-(8), with the signs of a symmetric positive definite operator):
@@ -120,13 +169,19 @@ typedef struct {
     const double *alpha_y;
 } pcg_coeffs_general;
 
-/* As pcg_create, for general coefficients.  Every other entry point works
- * on the handle unchanged (binary64, binary32, mixed, explicit path). */
+/* As pcg_create, for general coefficients (tables_dev: pcg_handle_bytes(grid)
+ * bytes as there).  Every other entry point works on the handle unchanged
+ * (binary64, binary32, mixed, explicit path). */
 int pcg_create_general(const pcg_grid *grid, const pcg_coeffs_general *coeffs, void *hip_stream,
-                       pcg_handle **out);
+                       void *tables_dev, size_t tables_bytes, pcg_handle **out);
 
-/* Release the handle and its tables (waits for its stream).  NULL is a no-op. */
+/* Release the handle (waits for its stream).  The table buffers stay the
+ * caller's, free to reuse after this returns.  NULL is a no-op. */
 int pcg_destroy(pcg_handle *h);
+
+/* The PCG_TUNE_* bits of the tuning variables that were set when the handle
+ * was created (0: every launch-geometry default; 0 for NULL). */
+int32_t pcg_tuning_overrides(const pcg_handle *h);
 
 /* Change the stream later calls are ordered on. */
 int pcg_set_stream(pcg_handle *h, void *hip_stream);
@@ -209,12 +264,21 @@ typedef struct {
     int32_t coarse_sweeps; /* sweeps on a coarsest level of several columns, 1..1024 */
 } pcg_mg_params;
 
+/* Bytes of device memory the coarse levels' tables need for these
+ * parameters (only max_levels matters; one pcg_handle_bytes-sized set of
+ * tables per coarse level, about a third of the handle's in all).  0 when
+ * the hierarchy has no coarse level, or for bad arguments. */
+size_t pcg_mg_setup_bytes(const pcg_handle *h, const pcg_mg_params *params);
+
 /* Build (or rebuild) the level hierarchy: the coarse levels' coefficient
- * tables are computed on the device from the handle's and owned by the
- * handle until pcg_destroy or the next pcg_mg_setup.  Blocks until done.
- * Returns PCG_ERR_INVALID for bad parameters, PCG_ERR_UNSUPPORTED when the
- * column tiles are not 64 columns wide, PCG_ERR_HIP on allocation failure. */
-int pcg_mg_setup(pcg_handle *h, const pcg_mg_params *params);
+ * tables are computed on the device from the handle's, in levels_dev
+ * (caller-owned device memory, >= pcg_mg_setup_bytes(h, params) bytes,
+ * 256-byte aligned; may be NULL when that is 0), which the handle reads until
+ * pcg_destroy or the next pcg_mg_setup.  Blocks until done.  Returns
+ * PCG_ERR_INVALID for bad parameters or a short buffer, PCG_ERR_UNSUPPORTED
+ * when the column tiles are not 64 columns wide, PCG_ERR_HIP on a runtime
+ * error. */
+int pcg_mg_setup(pcg_handle *h, const pcg_mg_params *params, void *levels_dev, size_t levels_bytes);
 
 /* Number of levels of the hierarchy built by pcg_mg_setup (1 = none coarser
  * than the grid).  PCG_ERR_INVALID before pcg_mg_setup. */
@@ -310,30 +374,36 @@ int pcg_csr_assemble(pcg_handle *h, int64_t *row_ptr_dev, int32_t *col_dev, doub
 int pcg_csr_spmv(pcg_handle *h, const int64_t *row_ptr_dev, const int32_t *col_dev,
                  const double *val_dev, const double *x_dev, double *y_dev);
 
-/* Assemble M's column matrices as tri_dev = [sub | diag | sup] (3N doubles,
- * each in field layout; sub is 0 at k = 0 and sup at k = nz-1) and factor
- * them (pcg_tridiag_factor).  Asynchronous. */
-int pcg_tridiag_assemble(pcg_handle *h, double *tri_dev);
+/* Bytes of a stored set of column matrices: tri_dev = [sub | diag | sup |
+ * phi], the three diagonals (N doubles each, field layout; sub is 0 at k = 0
+ * and sup at k = nz-1) followed by their Thomas multipliers at the column
+ * segments' boundaries ((ceil(nz/L) - 1) * nx*ny doubles, at least nx*ny). */
+size_t pcg_tridiag_bytes(const pcg_handle *h);
 
-/* Compute the handle's segment-boundary multipliers of the stored column
- * matrices tri_dev; call again after changing tri_dev.  Allocates a table of
- * (ceil(nz/L)-1)*nx*ny doubles in the handle on first use.  Asynchronous. */
-int pcg_tridiag_factor(pcg_handle *h, const double *tri_dev);
+/* Assemble M's column matrices into tri_dev (>= pcg_tridiag_bytes(h) bytes,
+ * 256-byte aligned) and factor them (pcg_tridiag_factor).  Asynchronous. */
+int pcg_tridiag_assemble(pcg_handle *h, double *tri_dev, size_t tri_bytes);
 
-/* z = M^{-1} r with the stored column matrices (factored first).
- * Asynchronous. */
-int pcg_tridiag_precond(pcg_handle *h, const double *tri_dev, const double *r_dev, double *z_dev);
+/* Compute the segment-boundary multipliers of the column matrices in
+ * tri_dev's diagonals into its phi part; call again after changing the
+ * diagonals.  Asynchronous. */
+int pcg_tridiag_factor(pcg_handle *h, double *tri_dev, size_t tri_bytes);
 
-/* Standard PCG (section 4.1) with the CSR matrix and the stored column
- * matrices; arguments and results as pcg_solve.  The matrix must have the
+/* z = M^{-1} r with the stored (factored) column matrices.  Asynchronous. */
+int pcg_tridiag_precond(pcg_handle *h, const double *tri_dev, size_t tri_bytes, const double *r_dev,
+                        double *z_dev);
+
+/* Standard PCG (section 4.1) with the CSR matrix and the stored (factored)
+ * column matrices (tri_dev, tri_bytes as above); arguments and results as
+ * pcg_solve.  The matrix must have the
  * layout pcg_csr_assemble writes (every row stores its diagonal entry; the
  * values may differ): sigma = <p, A p> takes p at each row's point from the
  * diagonal entry's column. */
 int pcg_solve_csr(pcg_handle *h, const int64_t *row_ptr_dev, const int32_t *col_dev,
-                  const double *val_dev, const double *tri_dev, const double *b_dev,
-                  double *x_dev, double tol, int32_t maxit, void *workspace_dev,
-                  size_t workspace_bytes, int32_t *iters_out, double *hist_host,
-                  int32_t *hist_len_out, double *final_rel_res);
+                  const double *val_dev, const double *tri_dev, size_t tri_bytes,
+                  const double *b_dev, double *x_dev, double tol, int32_t maxit,
+                  void *workspace_dev, size_t workspace_bytes, int32_t *iters_out,
+                  double *hist_host, int32_t *hist_len_out, double *final_rel_res);
 
 /* Per-kernel timing with HIP events on the handle's stream (off by default).
  * While enabled, every launch of the kernels below is bracketed by events;

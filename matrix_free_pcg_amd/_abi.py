@@ -35,17 +35,24 @@ PCG_KID_CSR_SPMV = 5
 PCG_KID_MG_VCYCLE = 6
 PCG_KID_COUNT = 7
 
-EXPORTED = [
-    "pcg_create", "pcg_destroy", "pcg_set_stream", "pcg_apply_A", "pcg_precond",
+EXPORTED = sorted([
+    "pcg_handle_bytes", "pcg_create", "pcg_destroy", "pcg_set_stream", "pcg_tuning_overrides",
+    "pcg_apply_A", "pcg_precond",
     "pcg_solve_workspace_bytes", "pcg_solve", "pcg_solve_standard", "pcg_solve_no_q",
     "pcg_profile_enable",
     "pcg_profile_reset", "pcg_profile_read", "pcg_last_error", "pcg_version",
-    "pcg_csr_nnz", "pcg_csr_assemble", "pcg_csr_spmv", "pcg_tridiag_assemble",
+    "pcg_csr_nnz", "pcg_csr_assemble", "pcg_csr_spmv", "pcg_tridiag_bytes", "pcg_tridiag_assemble",
     "pcg_tridiag_factor", "pcg_tridiag_precond", "pcg_solve_csr",
     "pcg_apply_A_f32", "pcg_precond_f32", "pcg_solve_f32", "pcg_solve_mixed", "pcg_create_general",
-    "pcg_mg_setup", "pcg_mg_num_levels", "pcg_mg_level", "pcg_mg_workspace_bytes", "pcg_mg_vcycle",
-    "pcg_solve_mg",
-]
+    "pcg_mg_setup_bytes", "pcg_mg_setup", "pcg_mg_num_levels", "pcg_mg_level", "pcg_mg_workspace_bytes",
+    "pcg_mg_vcycle", "pcg_solve_mg",
+])
+
+PCG_TUNE_NAMES = {
+    0x001: "MFPCG_COL_C", 0x002: "MFPCG_COL_L", 0x004: "MFPCG_COL_LF", 0x008: "MFPCG_ST_L",
+    0x010: "MFPCG_ST_W", 0x020: "MFPCG_COL_FULL", 0x040: "MFPCG_ST_FULL", 0x080: "MFPCG_ST_JT",
+    0x100: "MFPCG_COL_STRIP", 0x200: "MFPCG_ST_STRIP",
+}
 
 
 class PcgError(RuntimeError):
@@ -102,11 +109,21 @@ def load():
         dp = ctypes.POINTER(ctypes.c_double)
         i32p = ctypes.POINTER(ctypes.c_int32)
         H = ctypes.c_void_p
-        lib.pcg_create.argtypes = [ctypes.POINTER(pcg_grid), ctypes.POINTER(pcg_coeffs), vp, ctypes.POINTER(H)]
+        sz = ctypes.c_size_t
+        lib.pcg_handle_bytes.argtypes = [ctypes.POINTER(pcg_grid)]
+        lib.pcg_handle_bytes.restype = sz
+        lib.pcg_create.argtypes = [ctypes.POINTER(pcg_grid), ctypes.POINTER(pcg_coeffs), vp, vp, sz,
+                                   ctypes.POINTER(H)]
         lib.pcg_create.restype = ctypes.c_int
         lib.pcg_create_general.argtypes = [ctypes.POINTER(pcg_grid), ctypes.POINTER(pcg_coeffs_general), vp,
-                                           ctypes.POINTER(H)]
+                                           vp, sz, ctypes.POINTER(H)]
         lib.pcg_create_general.restype = ctypes.c_int
+        lib.pcg_tuning_overrides.argtypes = [H]
+        lib.pcg_tuning_overrides.restype = ctypes.c_int32
+        lib.pcg_mg_setup_bytes.argtypes = [H, ctypes.POINTER(pcg_mg_params)]
+        lib.pcg_mg_setup_bytes.restype = sz
+        lib.pcg_tridiag_bytes.argtypes = [H]
+        lib.pcg_tridiag_bytes.restype = sz
         lib.pcg_destroy.argtypes = [H]
         lib.pcg_destroy.restype = ctypes.c_int
         lib.pcg_set_stream.argtypes = [H, vp]
@@ -121,7 +138,7 @@ def load():
         lib.pcg_apply_A_f32.restype = ctypes.c_int
         lib.pcg_precond_f32.argtypes = [H, vp, vp]
         lib.pcg_precond_f32.restype = ctypes.c_int
-        lib.pcg_mg_setup.argtypes = [H, ctypes.POINTER(pcg_mg_params)]
+        lib.pcg_mg_setup.argtypes = [H, ctypes.POINTER(pcg_mg_params), vp, sz]
         lib.pcg_mg_setup.restype = ctypes.c_int
         lib.pcg_mg_num_levels.argtypes = [H, i32p]
         lib.pcg_mg_num_levels.restype = ctypes.c_int
@@ -153,13 +170,13 @@ def load():
         lib.pcg_csr_assemble.restype = ctypes.c_int
         lib.pcg_csr_spmv.argtypes = [H, vp, vp, vp, vp, vp]
         lib.pcg_csr_spmv.restype = ctypes.c_int
-        lib.pcg_tridiag_assemble.argtypes = [H, vp]
+        lib.pcg_tridiag_assemble.argtypes = [H, vp, sz]
         lib.pcg_tridiag_assemble.restype = ctypes.c_int
-        lib.pcg_tridiag_factor.argtypes = [H, vp]
+        lib.pcg_tridiag_factor.argtypes = [H, vp, sz]
         lib.pcg_tridiag_factor.restype = ctypes.c_int
-        lib.pcg_tridiag_precond.argtypes = [H, vp, vp, vp]
+        lib.pcg_tridiag_precond.argtypes = [H, vp, sz, vp, vp]
         lib.pcg_tridiag_precond.restype = ctypes.c_int
-        lib.pcg_solve_csr.argtypes = [H, vp, vp, vp, vp, vp, vp, ctypes.c_double, ctypes.c_int32,
+        lib.pcg_solve_csr.argtypes = [H, vp, vp, vp, vp, sz, vp, vp, ctypes.c_double, ctypes.c_int32,
                                       vp, ctypes.c_size_t, i32p, dp, i32p, dp]
         lib.pcg_solve_csr.restype = ctypes.c_int
         _lib = lib
@@ -199,16 +216,37 @@ def _check(h, rc: int, allow=(PCG_OK,)) -> int:
 
 
 class Handle:
-    """An open pcg_handle plus the grid it was created for."""
+    """An open pcg_handle plus the grid it was created for and the device
+    buffers it reads (its tables, and the multigrid levels' tables), which
+    the caller owns: they live as long as this object."""
 
-    def __init__(self, ptr: int, nx: int, ny: int, nz: int, device):
+    def __init__(self, ptr: int, nx: int, ny: int, nz: int, device, tables=None):
         self.ptr = ptr
         self.nx, self.ny, self.nz = nx, ny, nz
         self.n = nx * ny * nz
         self.device = device
+        self.tables = tables
+        self.mg_tables = None
 
     def __repr__(self):
         return f"Handle({self.nx}x{self.ny}x{self.nz})"
+
+
+def pcg_handle_bytes(nx: int, ny: int, nz: int) -> int:
+    """Device bytes of a handle's tables for this grid (0 for an invalid grid)."""
+    g = pcg_grid(int(nx), int(ny), int(nz))
+    return int(load().pcg_handle_bytes(ctypes.byref(g)))
+
+
+def _tables(g: pcg_grid):
+    """A caller-owned (torch) device buffer for a handle's tables."""
+    import torch
+    need = int(load().pcg_handle_bytes(ctypes.byref(g)))
+    return torch.empty(max(need, 256), dtype=torch.uint8, device=torch.device("cuda", torch.cuda.current_device()))
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
 
 
 def _create_general(problem, stream) -> Handle:
@@ -226,12 +264,13 @@ def _create_general(problem, stream) -> Handle:
         keep.append(v)
         setattr(c, name, v.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     out = ctypes.c_void_p()
+    tables = _tables(g)
     rc = lib.pcg_create_general(ctypes.byref(g), ctypes.byref(c), ctypes.c_void_p(_stream_ptr(stream)),
-                                ctypes.byref(out))
+                                tables.data_ptr(), _nbytes(tables), ctypes.byref(out))
     del keep
     if rc != PCG_OK:
         raise PcgError(rc, pcg_last_error(None))
-    return Handle(out.value, problem.nx, problem.ny, problem.nz, torch.cuda.current_device())
+    return Handle(out.value, problem.nx, problem.ny, problem.nz, torch.cuda.current_device(), tables)
 
 
 def pcg_create(problem, stream=None) -> Handle:
@@ -264,18 +303,25 @@ def pcg_create(problem, stream=None) -> Handle:
         c.alpha_h_const = 0.0
         c.alpha_h_field = ah.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
     out = ctypes.c_void_p()
+    tables = _tables(g)
     rc = lib.pcg_create(ctypes.byref(g), ctypes.byref(c), ctypes.c_void_p(_stream_ptr(stream)),
-                        ctypes.byref(out))
+                        tables.data_ptr(), _nbytes(tables), ctypes.byref(out))
     del keep
     if rc != PCG_OK:
         raise PcgError(rc, pcg_last_error(None))
-    return Handle(out.value, problem.nx, problem.ny, problem.nz, torch.cuda.current_device())
+    return Handle(out.value, problem.nx, problem.ny, problem.nz, torch.cuda.current_device(), tables)
 
 
 def pcg_destroy(h: Handle) -> None:
     if h is not None and h.ptr:
         load().pcg_destroy(h.ptr)
         h.ptr = None
+        h.tables = h.mg_tables = None
+
+
+def pcg_tuning_overrides(h: Handle) -> int:
+    """PCG_TUNE_* bits of the tuning variables set when the handle was created."""
+    return int(load().pcg_tuning_overrides(h.ptr))
 
 
 def pcg_set_stream(h: Handle, stream) -> None:
@@ -361,11 +407,22 @@ def pcg_solve_mixed(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> 
 
 # ---- tensor-product multigrid preconditioner ----------------------------------
 
+def pcg_mg_setup_bytes(h: Handle, nu: int = 1, omega: float = 0.8, max_levels: int = 0,
+                       coarse_sweeps: int = 2) -> int:
+    p = pcg_mg_params(int(nu), float(omega), int(max_levels), int(coarse_sweeps))
+    return int(load().pcg_mg_setup_bytes(h.ptr, ctypes.byref(p)))
+
+
 def pcg_mg_setup(h: Handle, nu: int = 1, omega: float = 0.8, max_levels: int = 0,
                  coarse_sweeps: int = 2) -> None:
-    """Build the level hierarchy (device tables owned by the handle)."""
+    """Build the level hierarchy; its tables go to a (torch) device buffer
+    kept on the handle object."""
+    import torch
     p = pcg_mg_params(int(nu), float(omega), int(max_levels), int(coarse_sweeps))
-    _check(h.ptr, load().pcg_mg_setup(h.ptr, ctypes.byref(p)))
+    need = int(load().pcg_mg_setup_bytes(h.ptr, ctypes.byref(p)))
+    buf = torch.empty(max(need, 256), dtype=torch.uint8, device=torch.device("cuda", h.device))
+    _check(h.ptr, load().pcg_mg_setup(h.ptr, ctypes.byref(p), buf.data_ptr(), _nbytes(buf)))
+    h.mg_tables = buf
 
 
 def pcg_mg_num_levels(h: Handle) -> int:
@@ -473,31 +530,41 @@ def pcg_csr_spmv(h: Handle, A: Csr, x, y) -> None:
     _check(h.ptr, load().pcg_csr_spmv(h.ptr, rp, col, val, _dev_ptr(x, h.n, "x"), _dev_ptr(y, h.n, "y")))
 
 
+def pcg_tridiag_bytes(h: Handle) -> int:
+    return int(load().pcg_tridiag_bytes(h.ptr))
+
+
+def _tri_ptr(h: Handle, tri):
+    n = pcg_tridiag_bytes(h) // 8
+    return _dev_tensor(tri, n, "float64", "tri"), n * 8
+
+
 def pcg_tridiag_assemble(h: Handle, device=None):
-    """Allocate (torch, 3N doubles = [sub | diag | sup]) and assemble + factor M's column matrices."""
+    """Allocate (torch, pcg_tridiag_bytes: [sub | diag | sup | phi]) and
+    assemble + factor M's column matrices."""
     import torch
     dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
-    tri = torch.empty(3 * h.n, dtype=torch.float64, device=dev)
-    _check(h.ptr, load().pcg_tridiag_assemble(h.ptr, tri.data_ptr()))
+    tri = torch.empty(pcg_tridiag_bytes(h) // 8, dtype=torch.float64, device=dev)
+    _check(h.ptr, load().pcg_tridiag_assemble(h.ptr, tri.data_ptr(), _nbytes(tri)))
     return tri
 
 
 def pcg_tridiag_factor(h: Handle, tri) -> None:
-    _check(h.ptr, load().pcg_tridiag_factor(h.ptr, _dev_tensor(tri, 3 * h.n, "float64", "tri")))
+    _check(h.ptr, load().pcg_tridiag_factor(h.ptr, *_tri_ptr(h, tri)))
 
 
 def pcg_tridiag_precond(h: Handle, tri, r, z) -> None:
     """z = M^{-1} r with the stored column matrices (asynchronous)."""
-    _check(h.ptr, load().pcg_tridiag_precond(h.ptr, _dev_tensor(tri, 3 * h.n, "float64", "tri"),
-                                             _dev_ptr(r, h.n, "r"), _dev_ptr(z, h.n, "z")))
+    _check(h.ptr, load().pcg_tridiag_precond(h.ptr, *_tri_ptr(h, tri), _dev_ptr(r, h.n, "r"),
+                                             _dev_ptr(z, h.n, "z")))
 
 
 def pcg_solve_csr(h: Handle, A: Csr, tri, b, x, tol: float, maxit: int, workspace=None) -> dict:
     """Standard PCG with the CSR matrix and the stored column matrices."""
     lib = load()
     rp, col, val = _csr_ptrs(h, A)
-    tp = _dev_tensor(tri, 3 * h.n, "float64", "tri")
+    tp, tb = _tri_ptr(h, tri)
 
     def fn(hp, bp, xp, tol_, maxit_, wsp, wsb, it, hist, hlen, rel):
-        return lib.pcg_solve_csr(hp, rp, col, val, tp, bp, xp, tol_, maxit_, wsp, wsb, it, hist, hlen, rel)
+        return lib.pcg_solve_csr(hp, rp, col, val, tp, tb, bp, xp, tol_, maxit_, wsp, wsb, it, hist, hlen, rel)
     return _solve(fn, h, b, x, tol, maxit, workspace)

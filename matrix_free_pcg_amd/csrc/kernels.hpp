@@ -292,10 +292,10 @@ enum : int { UPD_NONE = 0, UPD_Q = 1, UPD_AP = 2 };
 // semi-coarsening, the column solve as damped block-Jacobi smoother), with
 // y = M^{-1} rr:
 //   MG_FIRST  rr from the UPD mode, z = omega y    (first sweep from z = 0)
-//   MG_CORR   rr = rin, a residual f - A q computed by a stencil pass;
-//             z = q + omega y                      (further sweeps)
-//   MG_POST   rr = rin - A (P zc), rin the residual t = f - A q kept by the
-//             restriction; z = (q + P zc) + omega y: the sweep after the
+//   MG_CORR   rr = w, a residual f - A q computed by a stencil pass into
+//             z's buffer; z = q + omega y          (further sweeps)
+//   MG_POST   rr = t - A (P zc), t = f - A q the residual the restriction
+//             kept in z's buffer; z = (q + P zc) + omega y: the sweep after the
 //             coarse correction, with the residual of q + P zc formed from t
 //             and the coarse correction alone (no neighbour reads of q)
 //   MG_SWEEP  with UPD_AP: rr = rin - A q with q's neighbours read here (the
@@ -313,6 +313,24 @@ struct MgArgs {
     int ncx, fx, fy;    // coarse row length, coarsening factors in i and j
 };
 
+// Where a column pass reads its residual.  The pointer arguments of the
+// column kernels are restrict-qualified, so no two of them may name the same
+// vector: in the solve's in-place update r -= alpha q the residual is read
+// and written through rout, and in the multigrid corrected sweeps (MG_CORR,
+// MG_POST) it is read through z, whose buffer then receives the new iterate
+// (each thread reads its own elements before it writes them); rin is null in
+// those forms and is read only in the others.
+template <int UPD, int MG, typename TV, typename TZ>
+__device__ __forceinline__ const TV *residual_source(const TV *rin, TV *rout, TZ *z)
+{
+    if constexpr (MG != MG_SWEEP && UPD != UPD_NONE)
+        return rout;
+    else if constexpr (MG == MG_CORR || MG == MG_POST)
+        return (const TV *)z;
+    else
+        return rin;
+}
+
 // Index of the coarse parent of fine cell (i, j, k): (i / fx, j / fy, k).
 __device__ __forceinline__ size_t mg_parent(const MgArgs &m, int nz, int i, int j, int k)
 {
@@ -327,6 +345,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     double *__restrict__ partials, const double *__restrict__ tri,
     const TZ *__restrict__ phib_tab, MgArgs mg)
 {
+    const TV *rsrc = residual_source<UPD, MG>(rin, rout, z);
     static_assert((UPD != UPD_AP && !STORED) ||
                       (std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
                   "the stored-matrix and recomputed-Ap forms are binary64 only");
@@ -442,7 +461,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         for (int t = 0; t < L; ++t) {
             double v = 0.0;
             if (t < len && ok)
-                v = ld_s(rin + base + (size_t)(k0 + t) * ks);
+                v = ld_s(rsrc + base + (size_t)(k0 + t) * ks);
             if (do_ap && t < len) {
                 const double pc = pv[t + 1];
                 double pl = pxl[t], pr = pxr[t];
@@ -500,7 +519,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         for (int t = 0; t < L; ++t) {
             double v = 0.0;
             if (t < len && ok)
-                v = ld_s(rin + base + (size_t)(k0 + t) * ks);
+                v = ld_s(rsrc + base + (size_t)(k0 + t) * ks);
             if (do_it && t < len) {
                 const double c = cv[t + 1];
                 double xl = cxl[t], xr = cxr[t];
@@ -523,7 +542,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
             TV v = (TV)0;
             if (t < len && ok) {
                 const size_t l = base + (size_t)(k0 + t) * ks;
-                v = ld_s(rin + l);
+                v = ld_s(rsrc + l);
                 if (UPD == UPD_Q && !first)
                     v = v - alpha * ld_s(q + l);
             }
@@ -671,6 +690,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     TZ *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
     double *__restrict__ partials, const TZ *__restrict__ phib, MgArgs mg)
 {
+    const TV *rsrc = residual_source<UPD, MG>(rin, rout, z);
     static_assert(UPD != UPD_AP || (std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
                   "the recomputed-Ap form is binary64 only");
     static_assert(MG == MG_NONE || ((UPD != UPD_AP || MG == MG_SWEEP) && std::is_same<TV, double>::value &&
@@ -710,7 +730,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         TV qv[L];
 #pragma unroll
         for (int t = 0; t < L; ++t) {
-            rr[t] = ld_at(rin + row0 + (size_t)t * nx, cv);
+            rr[t] = ld_at(rsrc + row0 + (size_t)t * nx, cv);
             qv[t] = ld_at(q + row0 + (size_t)t * nx, cv);
         }
 #pragma unroll
@@ -734,7 +754,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         pv[L + 1] = ld_at(q + row0 + (size_t)ka * nx, cv);
 #pragma unroll
         for (int t = 0; t < L; ++t) {
-            rr[t] = ld_at(rin + row0 + (size_t)t * nx, cv);
+            rr[t] = ld_at(rsrc + row0 + (size_t)t * nx, cv);
             pv[t + 1] = ld_at(q + row0 + (size_t)t * nx, cv);
             pyp[t] = ld_at(q + rowp + (size_t)t * nx, cv);
             pym[t] = ld_at(q + rowm + (size_t)t * nx, cv);
@@ -779,7 +799,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         cc[L + 1] = ld_at(zcc + (size_t)ka * ksc, pl);
 #pragma unroll
         for (int t = 0; t < L; ++t) {
-            rr[t] = ld_at(rin + row0 + (size_t)t * nx, cv);
+            rr[t] = ld_at(rsrc + row0 + (size_t)t * nx, cv);
             cc[t + 1] = ld_at(zcc + (size_t)t * ksc, pl);
             cy[t] = (om || op) ? ld_at(zyo + (size_t)t * ksc, pl) : 0.0;
             ce[t] = edge ? ld_at(zcc + (size_t)t * ksc, pe) : 0.0;
@@ -803,7 +823,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     } else {
 #pragma unroll
         for (int t = 0; t < L; ++t)
-            rr[t] = ld_at(rin + row0 + (size_t)t * nx, cv);
+            rr[t] = ld_at(rsrc + row0 + (size_t)t * nx, cv);
     }
 #pragma unroll
     for (int t = 0; t < L; ++t)

@@ -46,12 +46,16 @@ struct pcg_handle {
                            //   (0: 4 in binary64, 8 in binary32; 1: one row, and the
                            //   operator-only passes then take one row too)
     size_t n = 0;          // nx*ny*nz
+    // device tables, carved from the caller's buffer (pcg_handle_bytes; for a
+    // coarse level, from the buffer given to pcg_mg_setup): the library
+    // allocates no device memory
     double *d_az = nullptr, *d_phib = nullptr;
     double *d_coef = nullptr;         // lev_a, lev_d (nz each), area, ex, ey (ny*nx each)
-    double *d_phib_tri = nullptr;     // boundary multipliers of the last factored stored tridiagonal
     float *d_phib32 = nullptr;        // boundary multipliers in binary32 (single-precision solves)
+    int32_t overrides = 0;            // PCG_TUNE_* bits: tuning variables that changed the geometry
     CsrShape csr{};
     HostStatus *h_status = nullptr;   // pinned host memory written by the reduce kernels
+    hipEvent_t loop_ev = nullptr;     // marks the stop decision of a step (created once)
     std::string err = "no error";
     bool profiling = false;
     double prof_ms[PCG_KID_COUNT] = {};
@@ -92,6 +96,7 @@ int fail(pcg_handle *h, int code, const char *fmt, ...)
 
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
+
 // Column-pass geometry: C columns per workgroup and the segment length L
 // (default: the smallest of 8, 16, 32 with C * ceil(nz / L) <= 1024).
 // Sweep-pass geometry: Ls levels per wave (1, 2, 4 or 8), Ws waves per
@@ -99,22 +104,31 @@ inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 // and MFPCG_ST_W override the choice (tuning); MFPCG_COL_FULL=0 and MFPCG_ST_FULL=0
 // disable the whole-tile kernels; MFPCG_COL_STRIP and MFPCG_ST_STRIP set the
 // i-strip widths of the tile order (default: one strip per XCD).
-int env_int(const char *name, int dflt)
+// The value of a tuning variable, or dflt when it is unset or empty; a set
+// variable adds its PCG_TUNE_* bit to *seen (when seen is not null).
+int env_int(const char *name, int dflt, int32_t *seen = nullptr, int32_t bit = 0)
 {
     const char *v = getenv(name);
-    return (v && *v) ? atoi(v) : dflt;
+    if (!(v && *v))
+        return dflt;
+    if (seen)
+        *seen |= bit;
+    return atoi(v);
 }
 
 struct Geometry {
     int L, C, Ls, Ws;
     int Lf;   // segment length of the column passes that need no stored table (a multiple of L)
+    int32_t overrides;   // PCG_TUNE_* bits of the variables read
 };
 
 bool choose_geometry(int nz, Geometry *g, std::string *why)
 {
-    g->C = env_int("MFPCG_COL_C", 64);
+    g->overrides = 0;
+    int32_t *ov = &g->overrides;
+    g->C = env_int("MFPCG_COL_C", 64, ov, PCG_TUNE_COL_C);
     if (g->C != 32 && g->C != 64) { *why = "MFPCG_COL_C must be 32 or 64"; return false; }
-    int l = env_int("MFPCG_COL_L", 0);
+    int l = env_int("MFPCG_COL_L", 0, ov, PCG_TUNE_COL_L);
     if (l == 0) {
         for (int cand : {8, 16, 32}) {
             if ((size_t)g->C * ((nz + cand - 1) / cand) <= (size_t)kMaxThreads) { l = cand; break; }
@@ -128,7 +142,7 @@ bool choose_geometry(int nz, Geometry *g, std::string *why)
     // stand-alone column passes at nz = 32..128 (their threads keep more loads
     // in flight; the multigrid sweeps need 8, so the table stays at L).
     // Whole segments are preferred: nz a multiple of 8 but not 16 keeps 8.
-    int lf = env_int("MFPCG_COL_LF", 0);
+    int lf = env_int("MFPCG_COL_LF", 0, ov, PCG_TUNE_COL_LF);
     if (lf == 0) {
         lf = l;
         if (l == 8 && nz >= 16 && (nz % 16 == 0 || nz % 8 != 0) &&
@@ -138,10 +152,10 @@ bool choose_geometry(int nz, Geometry *g, std::string *why)
     if (lf != l && lf != 2 * l && lf != 4 * l) { *why = "MFPCG_COL_LF must be 1, 2 or 4 times the segment length"; return false; }
     if (lf > 32) { *why = "MFPCG_COL_LF must be at most 32"; return false; }
     g->Lf = lf;
-    g->Ls = env_int("MFPCG_ST_L", 4);
+    g->Ls = env_int("MFPCG_ST_L", 4, ov, PCG_TUNE_ST_L);
     if (g->Ls != 1 && g->Ls != 2 && g->Ls != 4 && g->Ls != 8) { *why = "MFPCG_ST_L must be 1, 2, 4 or 8"; return false; }
     const int need = (nz + g->Ls - 1) / g->Ls;
-    g->Ws = env_int("MFPCG_ST_W", std::min(4, need));
+    g->Ws = env_int("MFPCG_ST_W", std::min(4, need), ov, PCG_TUNE_ST_W);
     if (g->Ws < 1 || g->Ws > 16) { *why = "MFPCG_ST_W must be in 1..16"; return false; }
     return true;
 }
@@ -313,9 +327,9 @@ void launch_column_lc(pcg_handle *h, const ColGeo &g, const TV *rin, const TV *q
     if constexpr (kD) {
         if (tri) {
             if (dots)
-                k_column_solve<L, C, UPD_NONE, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri, MgArgs{});
+                k_column_solve<L, C, UPD_NONE, true, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, tri + 3 * h->n, MgArgs{});
             else
-                k_column_solve<L, C, UPD_NONE, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, h->d_phib_tri, MgArgs{});
+                k_column_solve<L, C, UPD_NONE, false, true><<<grid, block, 0, h->stream>>>(rin, q, rout, z, o, st, first, partials, tri, tri + 3 * h->n, MgArgs{});
             return;
         }
     }
@@ -728,6 +742,11 @@ const char *pcg_last_error(const pcg_handle *h)
     return h ? h->err.c_str() : g_create_error.c_str();
 }
 
+int32_t pcg_tuning_overrides(const pcg_handle *h)
+{
+    return h ? h->overrides : 0;
+}
+
 }   // extern "C"
 
 namespace {
@@ -781,14 +800,17 @@ void init_geometry(pcg_handle *h, int nx, int ny, int nz, const Geometry &g)
     const int P = (nz + L - 1) / L;
     h->col_tiles = (int)(ntc * ny);
     h->col_threads = ((C * P + kWave - 1) / kWave) * kWave;
-    h->col_full = C == kWave && nx % kWave == 0 && nz % L == 0 && env_int("MFPCG_COL_FULL", 1) != 0;
+    int32_t ov = g.overrides;
+    const bool col_whole = env_int("MFPCG_COL_FULL", 1, &ov, PCG_TUNE_COL_FULL) != 0;
+    h->col_full = C == kWave && nx % kWave == 0 && nz % L == 0 && col_whole;
     h->colf_L = g.Lf;
     h->colf_threads = ((C * ((nz + g.Lf - 1) / g.Lf) + kWave - 1) / kWave) * kWave;
-    h->colf_full = C == kWave && nx % kWave == 0 && nz % g.Lf == 0 && env_int("MFPCG_COL_FULL", 1) != 0;
+    h->colf_full = C == kWave && nx % kWave == 0 && nz % g.Lf == 0 && col_whole;
     h->pt_tiles = (int)(ntx * nkt * ny);
-    h->pt_full = nx % kWave == 0 && nz % (g.Ls * g.Ws) == 0 && env_int("MFPCG_ST_FULL", 1) != 0;
+    h->pt_full = nx % kWave == 0 && nz % (g.Ls * g.Ws) == 0 &&
+                 env_int("MFPCG_ST_FULL", 1, &ov, PCG_TUNE_ST_FULL) != 0;
     {   // MFPCG_ST_JT: rows per fused-pass tile, 1 (one-row tiles), 4 or 8 (see launch_stencil)
-        const int jt = env_int("MFPCG_ST_JT", 0);
+        const int jt = env_int("MFPCG_ST_JT", 0, &ov, PCG_TUNE_ST_JT);
         h->st_jt = (jt == 1 || jt == 4 || jt == 8) ? jt : 0;
     }
     h->n = ncol * (size_t)nz;
@@ -809,37 +831,52 @@ void init_geometry(pcg_handle *h, int nx, int ny, int nz, const Geometry &g)
     h->op.nkt = (int)nkt;
     h->op.ntx = (int)ntx;
     // one strip of i-tiles per XCD (MFPCG_ST_STRIP overrides; 1 = i-tile slowest)
-    h->op.sg = std::max(1, std::min((int)ntx, env_int("MFPCG_ST_STRIP", (int)((ntx + kXcds - 1) / kXcds))));
-    h->op.csg = std::max(1, std::min((int)ntc, env_int("MFPCG_COL_STRIP", (int)((ntc + kXcds - 1) / kXcds))));
+    h->op.sg = std::max(1, std::min((int)ntx, env_int("MFPCG_ST_STRIP", (int)((ntx + kXcds - 1) / kXcds),
+                                                      &ov, PCG_TUNE_ST_STRIP)));
+    h->op.csg = std::max(1, std::min((int)ntc, env_int("MFPCG_COL_STRIP", (int)((ntc + kXcds - 1) / kXcds),
+                                                       &ov, PCG_TUNE_COL_STRIP)));
+    h->overrides = ov;
 }
 
-// Device tables of a level (faces, per-level and per-column coefficients,
-// boundary multipliers) and, for a handle the caller sees, the pinned status
-// word; the Op pointers are set to them.
-int alloc_tables(pcg_handle *h, const char *who, bool host_status)
+// Device tables of a level: the nz+1 vertical faces, per-level a and d and
+// per-column |T| and the two edge coefficients, the segment-boundary Thomas
+// multipliers in binary64 and binary32; each part 256-byte aligned.  Returns
+// the bytes; with base and h set, points h's tables (and its Op) into base.
+size_t table_layout(int nx, int ny, int nz, int P, char *base, pcg_handle *h)
 {
-    const int nz = h->op.nz, P = h->op.P;
-    const size_t ncol = (size_t)h->op.nx * h->op.ny;
-    const size_t ncoef = 2 * (size_t)nz + 3 * ncol;
-    hipError_t e;
-    if ((e = hipMalloc(&h->d_az, sizeof(double) * (nz + 1))) != hipSuccess ||
-        (e = hipMalloc(&h->d_coef, sizeof(double) * ncoef)) != hipSuccess ||
-        (e = hipMalloc(&h->d_phib, sizeof(double) * ncol * (size_t)(P > 1 ? P - 1 : 1))) != hipSuccess ||
-        (e = hipMalloc(&h->d_phib32, sizeof(float) * ncol * (size_t)(P > 1 ? P - 1 : 1))) != hipSuccess ||
-        (host_status &&
-         (e = hipHostMalloc((void **)&h->h_status, sizeof(HostStatus), hipHostMallocCoherent)) != hipSuccess)) {
-        h->err = std::string(who) + ": allocation failed: " + hipGetErrorString(e);
-        return PCG_ERR_HIP;
+    const size_t ncol = (size_t)nx * ny;
+    const size_t nb = ncol * (size_t)(P > 1 ? P - 1 : 1);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    const size_t o_az = take(sizeof(double) * ((size_t)nz + 1));
+    const size_t o_coef = take(sizeof(double) * (2 * (size_t)nz + 3 * ncol));
+    const size_t o_phib = take(sizeof(double) * nb);
+    const size_t o_phib32 = take(sizeof(float) * nb);
+    if (base && h) {
+        h->d_az = (double *)(base + o_az);
+        h->d_coef = (double *)(base + o_coef);
+        h->d_phib = (double *)(base + o_phib);
+        h->d_phib32 = (float *)(base + o_phib32);
+        h->op.az = h->d_az;
+        h->op.lev_a = h->d_coef;
+        h->op.lev_d = h->d_coef + nz;
+        h->op.area = h->d_coef + 2 * (size_t)nz;
+        h->op.ex = h->op.area + ncol;
+        h->op.ey = h->op.ex + ncol;
+        h->op.phib = h->d_phib;
     }
-    if (h->h_status)
-        memset(h->h_status, 0, sizeof(HostStatus));
-    h->op.az = h->d_az;
-    h->op.lev_a = h->d_coef;
-    h->op.lev_d = h->d_coef + nz;
-    h->op.area = h->d_coef + 2 * (size_t)nz;
-    h->op.ex = h->op.area + ncol;
-    h->op.ey = h->op.ex + ncol;
-    h->op.phib = h->d_phib;
+    return off;
+}
+
+// Check a caller-provided device buffer of at least `need` bytes.
+int check_buffer(pcg_handle *h, const char *who, const char *what, const void *buf, size_t bytes, size_t need)
+{
+    if (!buf)
+        return fail(h, PCG_ERR_INVALID, "%s: %s is NULL", who, what);
+    if (((uintptr_t)buf & 255u) != 0)
+        return fail(h, PCG_ERR_INVALID, "%s: %s must be 256-byte aligned", who, what);
+    if (bytes < need)
+        return fail(h, PCG_ERR_INVALID, "%s: %s has %zu bytes, needs %zu", who, what, bytes, need);
     return PCG_OK;
 }
 
@@ -862,13 +899,18 @@ int setup_multipliers(pcg_handle *h, const char *who)
     return PCG_OK;
 }
 
-// Allocate the handle, copy the coefficients and compute the Thomas
-// multipliers at the segment boundaries (binary64 and binary32 tables).
+// Create the handle in the caller's table buffer, copy the coefficients and
+// compute the Thomas multipliers at the segment boundaries (binary64 and
+// binary32 tables).
 int create_handle(const char *who, const pcg_grid *grid, const Geometry &g, const HostCoeffs &hc,
-                  void *hip_stream, pcg_handle **out)
+                  void *hip_stream, void *tables, size_t tables_bytes, pcg_handle **out)
 {
     const int nx = grid->nx, ny = grid->ny, nz = grid->nz;
     const size_t ncol = (size_t)nx * ny;
+    const size_t need = table_layout(nx, ny, nz, (nz + g.L - 1) / g.L, nullptr, nullptr);
+    int rc = check_buffer(nullptr, who, "tables_dev", tables, tables_bytes, need);
+    if (rc != PCG_OK)
+        return rc;
     pcg_handle *h = new pcg_handle();
     auto bail = [&](int code) {
         g_create_error = h->err;
@@ -881,15 +923,20 @@ int create_handle(const char *who, const pcg_grid *grid, const Geometry &g, cons
     }
     h->stream = (hipStream_t)hip_stream;
     init_geometry(h, nx, ny, nz, g);
-    int rc = alloc_tables(h, who, true);
-    if (rc != PCG_OK)
-        return bail(rc);
+    table_layout(nx, ny, nz, h->op.P, (char *)tables, h);
+    hipError_t e;
+    if ((e = hipHostMalloc((void **)&h->h_status, sizeof(HostStatus), hipHostMallocCoherent)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&h->loop_ev, hipEventDisableTiming)) != hipSuccess) {
+        h->h_status = nullptr;
+        h->err = std::string(who) + ": pinned status word / event: " + hipGetErrorString(e);
+        return bail(PCG_ERR_HIP);
+    }
+    memset(h->h_status, 0, sizeof(HostStatus));
     const size_t ncoef = 2 * (size_t)nz + 3 * ncol;
     std::vector<double> coef;
     coef.reserve(ncoef);
     for (const auto *v : {&hc.a, &hc.d, &hc.area, &hc.ex, &hc.ey})
         coef.insert(coef.end(), v->begin(), v->end());
-    hipError_t e;
     if ((e = hipMemcpy(h->d_az, hc.beta.data(), sizeof(double) * (nz + 1), hipMemcpyHostToDevice)) != hipSuccess ||
         (e = hipMemcpy(h->d_coef, coef.data(), sizeof(double) * ncoef, hipMemcpyHostToDevice)) != hipSuccess) {
         h->err = std::string(who) + ": copy failed: " + hipGetErrorString(e);
@@ -905,7 +952,21 @@ int create_handle(const char *who, const pcg_grid *grid, const Geometry &g, cons
 
 extern "C" {
 
-int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_handle **out)
+size_t pcg_handle_bytes(const pcg_grid *grid)
+{
+    if (!grid)
+        return 0;
+    Geometry g{};
+    const std::string keep = g_create_error;
+    if (check_grid("pcg_handle_bytes", grid, &g) != PCG_OK) {
+        g_create_error = keep;
+        return 0;
+    }
+    return table_layout(grid->nx, grid->ny, grid->nz, (grid->nz + g.L - 1) / g.L, nullptr, nullptr);
+}
+
+int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, void *tables,
+               size_t tables_bytes, pcg_handle **out)
 {
     const char *who = "pcg_create";
     if (!out)
@@ -953,11 +1014,11 @@ int pcg_create(const pcg_grid *grid, const pcg_coeffs *c, void *hip_stream, pcg_
             hc.ex[t] = 0.5 * (ah[t] + ah[(size_t)j * nx + (i + 1 == nx ? 0 : i + 1)]);
             hc.ey[t] = 0.5 * (ah[t] + ah[(size_t)(j + 1 == ny ? 0 : j + 1) * nx + i]);
         }
-    return create_handle(who, grid, g, hc, hip_stream, out);
+    return create_handle(who, grid, g, hc, hip_stream, tables, tables_bytes, out);
 }
 
 int pcg_create_general(const pcg_grid *grid, const pcg_coeffs_general *c, void *hip_stream,
-                       pcg_handle **out)
+                       void *tables, size_t tables_bytes, pcg_handle **out)
 {
     const char *who = "pcg_create_general";
     if (!out)
@@ -987,7 +1048,7 @@ int pcg_create_general(const pcg_grid *grid, const pcg_coeffs_general *c, void *
     hc.area.assign(c->area, c->area + ncol);
     hc.ex.assign(c->alpha_x, c->alpha_x + ncol);
     hc.ey.assign(c->alpha_y, c->alpha_y + ncol);
-    return create_handle(who, grid, g, hc, hip_stream, out);
+    return create_handle(who, grid, g, hc, hip_stream, tables, tables_bytes, out);
 }
 
 int pcg_destroy(pcg_handle *h)
@@ -1003,15 +1064,11 @@ int pcg_destroy(pcg_handle *h)
     }
     for (auto e : h->free_events)
         (void)hipEventDestroy(e);
-    if (h->d_az) (void)hipFree(h->d_az);
-    if (h->d_coef) (void)hipFree(h->d_coef);
-    if (h->d_phib) (void)hipFree(h->d_phib);
-    if (h->d_phib32) (void)hipFree(h->d_phib32);
-    if (h->d_phib_tri) (void)hipFree(h->d_phib_tri);
+    if (h->loop_ev) (void)hipEventDestroy(h->loop_ev);
     if (h->h_status) (void)hipHostFree(h->h_status);
     for (auto *c : h->mg_levels)
         pcg_destroy(c);
-    delete h;
+    delete h;   // the device tables belong to the caller
     return PCG_OK;
 }
 
@@ -1259,7 +1316,7 @@ void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const 
             return;
         }
         stencil<double, double>(h, SP_RESID, cur, f, nullptr, nullptr, oth, nullptr, nullptr);
-        mg_column(h, MG_CORR, oth, cur, nullptr, oth, st, 0, parts, UPD_NONE, a);
+        mg_column(h, MG_CORR, nullptr, cur, nullptr, oth, st, 0, parts, UPD_NONE, a);
     };
     if (l == nlev - 1) {
         if ((size_t)h->op.nx * h->op.ny == 1) {
@@ -1288,7 +1345,7 @@ void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const 
     mg_restrict(h, fx, fy, f, cur, oth, mw.f[(size_t)l + 1], c->op.nx, st);
     mg_cycle(h0, mw, l + 1, mw.f[(size_t)l + 1], nullptr, nullptr, UPD_NONE, st, 0, nullptr);
     const MgArgs ap{mw.V[(size_t)l + 1], f, h0->mg_omega, c->op.nx, fx, fy};
-    mg_column(h, MG_POST, oth, cur, nullptr, oth, st, 0, nu == 1 ? partials : nullptr, UPD_NONE, ap);
+    mg_column(h, MG_POST, nullptr, cur, nullptr, oth, st, 0, nu == 1 ? partials : nullptr, UPD_NONE, ap);
     std::swap(cur, oth);
     for (int sw = 1; sw < nu; ++sw) {
         sweep(cur, oth, sw == nu - 1 ? partials : nullptr);
@@ -1330,8 +1387,7 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
     k_init_state<<<1, 64, 0, h->stream>>>(w.state);
     // a2: r0 = b - A x0
     stencil<TV, TV>(h, SP_RESID, x, b, nullptr, nullptr, r, nullptr, nullptr);
-    hipEvent_t ev = nullptr;
-    HIP_TRY(h, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    hipEvent_t ev = h->loop_ev;
     int last = 0;
     for (int k = 0; k <= maxit; ++k) {
         int nred = 0;
@@ -1345,12 +1401,12 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
         if constexpr (kD) {
             if (mg) {
                 Timed t(h, PCG_KID_MG_VCYCLE, k);
-                mg_cycle(h, *mg, 0, r, pin, r, UPD_Q, w.state, k == 0, w.partials);
+                mg_cycle(h, *mg, 0, nullptr, pin, r, UPD_Q, w.state, k == 0, w.partials);
             }
         }
         if (!mg) {
             Timed t(h, PCG_KID_FUSED_PREC, k);
-            column<TV, TZ>(h, r, pin, r, z, w.state, k == 0, w.partials, ap ? UPD_AP : UPD_Q, true);
+            column<TV, TZ>(h, nullptr, pin, r, z, w.state, k == 0, w.partials, ap ? UPD_AP : UPD_Q, true);
         }
         // a4: ||r_k||, stop test, beta
         red = fold_partials(h, w, h->col_tiles, &nred);
@@ -1377,20 +1433,15 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
         red = fold_partials(h, w, stencil_tiles(h, smode, kBinary64<TV, TZ>, std::is_same<TV, float>::value), &nred);
         k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k, !ap && (k & 1));
         hipError_t e = hipGetLastError();
-        if (e != hipSuccess) {
-            (void)hipEventDestroy(ev);
+        if (e != hipSuccess)
             return fail(h, PCG_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
-        }
         e = hipEventSynchronize(ev);
-        if (e != hipSuccess) {
-            (void)hipEventDestroy(ev);
+        if (e != hipSuccess)
             return fail(h, PCG_ERR_HIP, "%s: hipEventSynchronize: %s", who, hipGetErrorString(e));
-        }
         last = k;
         if (((volatile HostStatus *)h->h_status)->done)
             break;
     }
-    (void)hipEventDestroy(ev);
     return solve_epilogue(h, a, w, PCG_KID_FUSED_SPMV, last);
 }
 
@@ -1446,37 +1497,38 @@ int pcg_solve_mixed(pcg_handle *h, const double *b, double *x, double tol, int32
     return interleaved_loop<double, float>(h, a, w, false, "pcg_solve_mixed");
 }
 
+
 }   // extern "C"
 
 namespace {
 
-// One coarse level from the fine level h (factors fx, fy): its tables on the
-// device, the coefficients by Galerkin coarsening, the Thomas multipliers.
-int create_coarse(pcg_handle *h, int fx, int fy, pcg_handle **out)
+// One coarse level from the fine level h (factors fx, fy): its tables in
+// `tables` (table_layout bytes), the coefficients by Galerkin coarsening, the
+// Thomas multipliers.
+int create_coarse(pcg_handle *h, int fx, int fy, char *tables, pcg_handle **out)
 {
     const char *who = "pcg_mg_setup";
     pcg_handle *c = new pcg_handle();
     c->device = h->device;
     c->stream = h->stream;
-    const Geometry g{h->op.L, h->op.C, h->op.Ls, h->op.Ws, h->op.L};
+    const Geometry g{h->op.L, h->op.C, h->op.Ls, h->op.Ws, h->op.L, 0};
     const int nz = h->op.nz;
     init_geometry(c, h->op.nx / fx, h->op.ny / fy, nz, g);
-    int rc = alloc_tables(c, who, false);
-    if (rc == PCG_OK) {
-        hipError_t e;
-        if ((e = hipMemcpyAsync(c->d_az, h->d_az, sizeof(double) * (nz + 1), hipMemcpyDeviceToDevice,
-                                h->stream)) != hipSuccess ||
-            (e = hipMemcpyAsync(c->d_coef, h->d_coef, sizeof(double) * 2 * (size_t)nz,
-                                hipMemcpyDeviceToDevice, h->stream)) != hipSuccess) {
-            c->err = std::string(who) + ": copy failed: " + hipGetErrorString(e);
-            rc = PCG_ERR_HIP;
-        } else {
-            const size_t ncol = (size_t)c->op.nx * c->op.ny;
-            double *area = c->d_coef + 2 * (size_t)nz;
-            k_mg_coarsen<<<dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, h->stream>>>(
-                h->op, c->op.nx, c->op.ny, fx, fy, area, area + ncol, area + 2 * ncol);
-            rc = setup_multipliers(c, who);
-        }
+    table_layout(c->op.nx, c->op.ny, nz, c->op.P, tables, c);
+    int rc = PCG_OK;
+    hipError_t e;
+    if ((e = hipMemcpyAsync(c->d_az, h->d_az, sizeof(double) * (nz + 1), hipMemcpyDeviceToDevice,
+                            h->stream)) != hipSuccess ||
+        (e = hipMemcpyAsync(c->d_coef, h->d_coef, sizeof(double) * 2 * (size_t)nz,
+                            hipMemcpyDeviceToDevice, h->stream)) != hipSuccess) {
+        c->err = std::string(who) + ": copy failed: " + hipGetErrorString(e);
+        rc = PCG_ERR_HIP;
+    } else {
+        const size_t ncol = (size_t)c->op.nx * c->op.ny;
+        double *area = c->d_coef + 2 * (size_t)nz;
+        k_mg_coarsen<<<dim3((unsigned)((ncol + 255) / 256)), dim3(256), 0, h->stream>>>(
+            h->op, c->op.nx, c->op.ny, fx, fy, area, area + ncol, area + 2 * ncol);
+        rc = setup_multipliers(c, who);
     }
     if (rc != PCG_OK) {
         h->err = c->err;
@@ -1485,6 +1537,28 @@ int create_coarse(pcg_handle *h, int fx, int fy, pcg_handle **out)
     }
     *out = c;
     return PCG_OK;
+}
+
+// The coarsening factors of the hierarchy pcg_mg_setup builds for these
+// parameters (one (fx, fy) pair per coarse level) and the bytes of the
+// coarse levels' tables.
+size_t mg_plan(const pcg_handle *h, int max_levels, std::vector<int> *fxs, std::vector<int> *fys)
+{
+    int nx = h->op.nx, ny = h->op.ny, nlev = 1;
+    size_t bytes = 0;
+    while ((max_levels == 0 || nlev < max_levels) && (size_t)nx * ny > 1) {
+        const int fx = (nx > 1 && nx % 2 == 0) ? 2 : 1;
+        const int fy = (ny > 1 && ny % 2 == 0) ? 2 : 1;
+        if (fx == 1 && fy == 1)
+            break;
+        nx /= fx;
+        ny /= fy;
+        ++nlev;
+        bytes += table_layout(nx, ny, h->op.nz, h->op.P, nullptr, nullptr);
+        if (fxs) fxs->push_back(fx);
+        if (fys) fys->push_back(fy);
+    }
+    return bytes;
 }
 
 void mg_clear(pcg_handle *h)
@@ -1501,7 +1575,14 @@ void mg_clear(pcg_handle *h)
 
 extern "C" {
 
-int pcg_mg_setup(pcg_handle *h, const pcg_mg_params *p)
+size_t pcg_mg_setup_bytes(const pcg_handle *h, const pcg_mg_params *p)
+{
+    if (!h || !p || p->max_levels < 0 || p->max_levels > 64)
+        return 0;
+    return mg_plan(h, p->max_levels, nullptr, nullptr);
+}
+
+int pcg_mg_setup(pcg_handle *h, const pcg_mg_params *p, void *levels, size_t levels_bytes)
 {
     const char *who = "pcg_mg_setup";
     if (!h)
@@ -1518,32 +1599,30 @@ int pcg_mg_setup(pcg_handle *h, const pcg_mg_params *p)
         return fail(h, PCG_ERR_INVALID, "%s: coarse_sweeps = %d must be in 1..1024", who, p->coarse_sweeps);
     if (h->op.C != kWave)
         return fail(h, PCG_ERR_UNSUPPORTED, "%s: the multigrid sweeps need 64-column column tiles", who);
-    int rc = set_device(h);
-    if (rc != PCG_OK)
+    std::vector<int> fxs, fys;
+    const size_t need = mg_plan(h, p->max_levels, &fxs, &fys);
+    int rc = PCG_OK;
+    if (need > 0 && (rc = check_buffer(h, who, "levels_dev", levels, levels_bytes, need)) != PCG_OK)
+        return rc;
+    if ((rc = set_device(h)) != PCG_OK)
         return rc;
     HIP_TRY(h, hipStreamSynchronize(h->stream));
     mg_clear(h);
     pcg_handle *cur = h;
-    int nx = h->op.nx, ny = h->op.ny, nlev = 1;
-    while ((p->max_levels == 0 || nlev < p->max_levels) && (size_t)nx * ny > 1) {
-        const int fx = (nx > 1 && nx % 2 == 0) ? 2 : 1;
-        const int fy = (ny > 1 && ny % 2 == 0) ? 2 : 1;
-        if (fx == 1 && fy == 1)
-            break;
+    char *base = (char *)levels;
+    for (size_t l = 0; l < fxs.size(); ++l) {
         pcg_handle *c = nullptr;
-        if ((rc = create_coarse(cur, fx, fy, &c)) != PCG_OK) {
+        if ((rc = create_coarse(cur, fxs[l], fys[l], base, &c)) != PCG_OK) {
             if (cur != h)
                 h->err = cur->err;
             mg_clear(h);
             return rc;
         }
+        base += table_layout(c->op.nx, c->op.ny, c->op.nz, c->op.P, nullptr, nullptr);
         h->mg_levels.push_back(c);
-        h->mg_fx.push_back(fx);
-        h->mg_fy.push_back(fy);
+        h->mg_fx.push_back(fxs[l]);
+        h->mg_fy.push_back(fys[l]);
         cur = c;
-        nx /= fx;
-        ny /= fy;
-        ++nlev;
     }
     h->mg_nu = p->nu;
     h->mg_omega = p->omega;
@@ -1660,8 +1739,7 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
     HostStatus *hs = nullptr;
     HIP_TRY(h, hipHostGetDevicePointer((void **)&hs, h->h_status, 0));
     h->h_status->done = 0;
-    hipEvent_t ev = nullptr;
-    HIP_TRY(h, hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    hipEvent_t ev = h->loop_ev;
     const double *b = (const double *)a.b;
     double *x = (double *)a.x;
     const int32_t maxit = a.maxit;
@@ -1719,7 +1797,6 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
             e = hipEventSynchronize(ev);
         done = (e == hipSuccess) && ((volatile HostStatus *)h->h_status)->done;
     }
-    (void)hipEventDestroy(ev);
     if (e != hipSuccess)
         return fail(h, PCG_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
     return solve_epilogue(h, a, w, -1, -2);
@@ -1736,8 +1813,6 @@ int check_explicit(pcg_handle *h, const Explicit &ex, const char *who)
 {
     if (!ex.row_ptr || !ex.col || !ex.val || !ex.tri)
         return fail(h, PCG_ERR_INVALID, "%s: null CSR or tridiagonal pointer", who);
-    if (!h->d_phib_tri && h->op.P > 1)
-        return fail(h, PCG_ERR_INVALID, "%s: the stored tridiagonal has not been factored (pcg_tridiag_factor)", who);
     return csr_supported(h, who);
 }
 
@@ -1801,53 +1876,56 @@ int pcg_csr_spmv(pcg_handle *h, const int64_t *row_ptr, const int32_t *col, cons
     return PCG_OK;
 }
 
-int pcg_tridiag_factor(pcg_handle *h, const double *tri)
+size_t pcg_tridiag_bytes(const pcg_handle *h)
 {
     if (!h)
+        return 0;
+    const size_t ncol = (size_t)h->op.nx * h->op.ny;
+    return sizeof(double) * (3 * h->n + ncol * (size_t)(h->op.P > 1 ? h->op.P - 1 : 1));
+}
+
+int pcg_tridiag_factor(pcg_handle *h, double *tri, size_t tri_bytes)
+{
+    const char *who = "pcg_tridiag_factor";
+    if (!h)
         return PCG_ERR_INVALID;
-    if (!tri)
-        return fail(h, PCG_ERR_INVALID, "pcg_tridiag_factor: null pointer");
-    int rc = set_device(h);
-    if (rc != PCG_OK)
+    int rc = check_buffer(h, who, "tri_dev", tri, tri_bytes, pcg_tridiag_bytes(h));
+    if (rc != PCG_OK || (rc = set_device(h)) != PCG_OK)
         return rc;
     const size_t ncol = (size_t)h->op.nx * h->op.ny;
-    if (!h->d_phib_tri)
-        HIP_TRY(h, hipMalloc(&h->d_phib_tri, sizeof(double) * ncol * (size_t)(h->op.P > 1 ? h->op.P - 1 : 1)));
     if (h->op.P > 1) {
         const int threads = 256;
-        k_setup_phib_stored<<<dim3((unsigned)((ncol + threads - 1) / threads)), dim3(threads), 0, h->stream>>>(h->op, tri, h->d_phib_tri);
+        k_setup_phib_stored<<<dim3((unsigned)((ncol + threads - 1) / threads)), dim3(threads), 0, h->stream>>>(
+            h->op, tri, tri + 3 * h->n);
     }
     HIP_TRY(h, hipGetLastError());
     return PCG_OK;
 }
 
-int pcg_tridiag_assemble(pcg_handle *h, double *tri)
+int pcg_tridiag_assemble(pcg_handle *h, double *tri, size_t tri_bytes)
 {
+    const char *who = "pcg_tridiag_assemble";
     if (!h)
         return PCG_ERR_INVALID;
-    if (!tri)
-        return fail(h, PCG_ERR_INVALID, "pcg_tridiag_assemble: null pointer");
-    int rc = set_device(h);
-    if (rc != PCG_OK)
+    int rc = check_buffer(h, who, "tri_dev", tri, tri_bytes, pcg_tridiag_bytes(h));
+    if (rc != PCG_OK || (rc = set_device(h)) != PCG_OK)
         return rc;
     const size_t ncol = (size_t)h->op.nx * h->op.ny;
     const int threads = 256;
     k_tridiag_assemble<<<dim3((unsigned)((ncol + threads - 1) / threads)), dim3(threads), 0, h->stream>>>(h->op, tri);
     HIP_TRY(h, hipGetLastError());
-    return pcg_tridiag_factor(h, tri);
+    return pcg_tridiag_factor(h, tri, tri_bytes);
 }
 
-int pcg_tridiag_precond(pcg_handle *h, const double *tri, const double *r, double *z)
+int pcg_tridiag_precond(pcg_handle *h, const double *tri, size_t tri_bytes, const double *r, double *z)
 {
+    const char *who = "pcg_tridiag_precond";
     if (!h)
         return PCG_ERR_INVALID;
-    int rc = check_vectors(h, r, z, "pcg_tridiag_precond");
-    if (rc != PCG_OK || (rc = set_device(h)) != PCG_OK)
+    int rc = check_vectors(h, r, z, who);
+    if (rc != PCG_OK || (rc = check_buffer(h, who, "tri_dev", tri, tri_bytes, pcg_tridiag_bytes(h))) != PCG_OK ||
+        (rc = set_device(h)) != PCG_OK)
         return rc;
-    if (!tri)
-        return fail(h, PCG_ERR_INVALID, "pcg_tridiag_precond: null pointer");
-    if (!h->d_phib_tri && h->op.P > 1)
-        return fail(h, PCG_ERR_INVALID, "pcg_tridiag_precond: call pcg_tridiag_factor first");
     {
         Timed t(h, PCG_KID_PRECOND, -1);
         column<double, double>(h, r, nullptr, nullptr, z, nullptr, 0, nullptr, UPD_NONE, false, tri);
@@ -1857,8 +1935,8 @@ int pcg_tridiag_precond(pcg_handle *h, const double *tri, const double *r, doubl
 }
 
 int pcg_solve_csr(pcg_handle *h, const int64_t *row_ptr, const int32_t *col, const double *val,
-                  const double *tri, const double *b, double *x, double tol, int32_t maxit,
-                  void *ws, size_t ws_bytes, int32_t *iters_out, double *hist_host,
+                  const double *tri, size_t tri_bytes, const double *b, double *x, double tol,
+                  int32_t maxit, void *ws, size_t ws_bytes, int32_t *iters_out, double *hist_host,
                   int32_t *hist_len_out, double *final_rel)
 {
     SolveArgs a{b, x, sizeof(double), tol, maxit, ws, ws_bytes, iters_out, hist_host, hist_len_out, final_rel};
@@ -1866,7 +1944,8 @@ int pcg_solve_csr(pcg_handle *h, const int64_t *row_ptr, const int32_t *col, con
         return PCG_ERR_INVALID;
     Explicit ex{row_ptr, col, val, tri};
     int rc = check_explicit(h, ex, "pcg_solve_csr");
-    if (rc != PCG_OK)
+    if (rc != PCG_OK ||
+        (rc = check_buffer(h, "pcg_solve_csr", "tri_dev", tri, tri_bytes, pcg_tridiag_bytes(h))) != PCG_OK)
         return rc;
     Workspace w{};
     rc = solve_prologue(h, a, &w, "pcg_solve_csr");

@@ -46,7 +46,12 @@ def test_version_and_error_strings(lib):
     assert isinstance(_abi.pcg_last_error(None), str)
 
 
-def _create(lib, nx, ny, nz, delta, az, kind=0, hconst=1.0, field=None):
+# a stand-in for a device table buffer: 256-byte aligned and large enough;
+# never dereferenced (every case below fails before any HIP call)
+FAKE_TABLES = 1 << 40
+
+
+def _create(lib, nx, ny, nz, delta, az, kind=0, hconst=1.0, field=None, tables=FAKE_TABLES, tbytes=1 << 30):
     g = _abi.pcg_grid(nx, ny, nz)
     c = _abi.pcg_coeffs()
     c.delta = delta
@@ -58,7 +63,7 @@ def _create(lib, nx, ny, nz, delta, az, kind=0, hconst=1.0, field=None):
         field = np.ascontiguousarray(field, dtype=np.float64)
         c.alpha_h_field = field.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
     out = ctypes.c_void_p()
-    rc = lib.pcg_create(ctypes.byref(g), ctypes.byref(c), None, ctypes.byref(out))
+    rc = lib.pcg_create(ctypes.byref(g), ctypes.byref(c), None, tables, tbytes, ctypes.byref(out))
     return rc, out.value, (az, field)
 
 
@@ -74,6 +79,9 @@ def _create(lib, nx, ny, nz, delta, az, kind=0, hconst=1.0, field=None):
     ("field_negative", _abi.PCG_ERR_INVALID),
     ("field_null", _abi.PCG_ERR_INVALID),
     ("bad_kind", _abi.PCG_ERR_INVALID),
+    ("tables_null", _abi.PCG_ERR_INVALID),
+    ("tables_misaligned", _abi.PCG_ERR_INVALID),
+    ("tables_short", _abi.PCG_ERR_INVALID),
 ])
 def test_create_rejects_invalid_arguments(lib, case, expect):
     nz = 8
@@ -106,10 +114,58 @@ def test_create_rejects_invalid_arguments(lib, case, expect):
         args.update(kind=1)
     elif case == "bad_kind":
         args.update(kind=7)
+    elif case == "tables_null":
+        args.update(tables=None)
+    elif case == "tables_misaligned":
+        args.update(tables=FAKE_TABLES + 8)
+    elif case == "tables_short":
+        g = _abi.pcg_grid(4, 4, nz)
+        args.update(tbytes=lib.pcg_handle_bytes(ctypes.byref(g)) - 1)
     rc, h, _keep = _create(lib, **args)
     assert rc == expect
     assert h is None
     assert len(_abi.pcg_last_error(None)) > 0
+    if case.startswith("tables"):
+        assert "tables_dev" in _abi.pcg_last_error(None)
+
+
+def test_handle_bytes_covers_the_tables(lib):
+    """pcg_handle_bytes: the handle's device tables (faces, a and d per level,
+    |T| and two edges per column, binary64 and binary32 multipliers at the
+    segment boundaries, each part rounded up to 256 bytes), 0 for an invalid
+    grid; no device memory is allocated by the library."""
+    def a256(b):
+        return (b + 255) // 256 * 256
+    for nx, ny, nz in [(32, 32, 16), (1024, 1024, 128), (5, 3, 7), (64, 8, 300)]:
+        g = _abi.pcg_grid(nx, ny, nz)
+        L = 8 if nz <= 128 else (16 if nz <= 256 else 32)
+        P = -(-nz // L)
+        ncol = nx * ny
+        nb = ncol * max(P - 1, 1)
+        want = a256(8 * (nz + 1)) + a256(8 * (2 * nz + 3 * ncol)) + a256(8 * nb) + a256(4 * nb)
+        assert lib.pcg_handle_bytes(ctypes.byref(g)) == want, (nx, ny, nz)
+    for bad in [(0, 4, 4), (4, -1, 4), (4, 4, 0), (4, 4, 513)]:
+        g = _abi.pcg_grid(*bad)
+        assert lib.pcg_handle_bytes(ctypes.byref(g)) == 0
+    assert lib.pcg_handle_bytes(None) == 0
+
+
+def test_no_device_allocation_in_the_library():
+    """The library's source makes no device allocation: no hipMalloc /
+    hipFree / hipMallocAsync / hipExtMalloc call in the host code (the pinned
+    status word is hipHostMalloc'ed host memory)."""
+    import re as _re
+    src = open(os.path.join(hipbuild.CSRC, "mfpcg.hip")).read()
+    src = _re.sub(r"//[^\n]*", "", src)
+    for name in ("hipMalloc(", "hipMallocManaged", "hipMallocAsync", "hipExtMallocWithFlags", "hipFree("):
+        assert name not in src, name
+
+
+def test_size_queries_without_gpu(lib):
+    assert lib.pcg_tuning_overrides(None) == 0
+    assert lib.pcg_tridiag_bytes(None) == 0
+    p = _abi.pcg_mg_params(1, 0.8, 0, 2)
+    assert lib.pcg_mg_setup_bytes(None, ctypes.byref(p)) == 0
 
 
 def test_null_handle_calls_are_invalid(lib):
@@ -155,7 +211,7 @@ def test_create_general_rejects_invalid_arguments(lib, case):
         setattr(c, name, v.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     g = _abi.pcg_grid(nx, ny, nz)
     out = ctypes.c_void_p()
-    rc = lib.pcg_create_general(ctypes.byref(g), ctypes.byref(c), None, ctypes.byref(out))
+    rc = lib.pcg_create_general(ctypes.byref(g), ctypes.byref(c), None, FAKE_TABLES, 1 << 30, ctypes.byref(out))
     assert rc == _abi.PCG_ERR_INVALID
     assert out.value is None
     assert "pcg_create_general" in _abi.pcg_last_error(None)
@@ -163,7 +219,7 @@ def test_create_general_rejects_invalid_arguments(lib, case):
 
 def test_mg_entry_points_reject_null_handle(lib):
     p = _abi.pcg_mg_params(1, 0.8, 0, 2)
-    assert lib.pcg_mg_setup(None, ctypes.byref(p)) == _abi.PCG_ERR_INVALID
+    assert lib.pcg_mg_setup(None, ctypes.byref(p), None, 0) == _abi.PCG_ERR_INVALID
     n = ctypes.c_int32(0)
     assert lib.pcg_mg_num_levels(None, ctypes.byref(n)) == _abi.PCG_ERR_INVALID
     assert lib.pcg_mg_level(None, 0, None, None, None, None, None) == _abi.PCG_ERR_INVALID

@@ -133,15 +133,45 @@ def test_csr_fixed_steps_match_oracle(dev):
     assert np.linalg.norm(xg - ref["x"]) <= 1e-11 * np.linalg.norm(ref["x"])
 
 
-def test_stored_precond_needs_factor(dev):
+def test_stored_matrices_keep_their_own_factors(dev):
+    """The segment-boundary multipliers of stored column matrices live in
+    the tri buffer itself: factoring a second, different set of matrices
+    leaves the first one's solve unchanged, each solve satisfies its own
+    matrices (backward error per row), and a buffer of only the three
+    diagonals is refused before any work is queued."""
+    import ctypes
     import torch
+    from matrix_free_pcg_amd import _abi
     prob = W.config_problem(4, scale_xy=(8, 8), nz=40)
+    n = prob.n
+    r = W.uniform_field(prob.nx, prob.ny, prob.nz, 77)
     h = mf.pcg_create(prob)
     try:
-        tri = torch.zeros(3 * prob.n, dtype=torch.float64, device=dev)
-        r = torch.ones(prob.n, dtype=torch.float64, device=dev)
-        z = torch.empty_like(r)
-        with pytest.raises(mf.PcgError):
-            mf.pcg_tridiag_precond(h, tri, r, z)
+        tri1 = mf.pcg_tridiag_assemble(h)
+        tri2 = tri1.clone()
+        tri2[n:2 * n] *= 2.0     # another diagonally dominant set of column matrices
+        mf.pcg_tridiag_factor(h, tri2)
+        rd = to_dev(r, dev)
+        z1 = torch.empty_like(rd)
+        z2 = torch.empty_like(rd)
+        mf.pcg_tridiag_precond(h, tri1, rd, z1)
+        mf.pcg_tridiag_precond(h, tri2, rd, z2)
+        short = torch.zeros(3 * n, dtype=torch.float64, device=dev)
+        rc = _abi.load().pcg_tridiag_precond(h.ptr, short.data_ptr(), ctypes.c_size_t(3 * n * 8),
+                                             rd.data_ptr(), z1.data_ptr())
+        assert rc == mf.PCG_ERR_INVALID and "tri_dev" in mf.pcg_last_error(h.ptr)
+        torch.cuda.synchronize()
+        z1h, z2h, t2 = to_host(z1), to_host(z2), to_host(tri2)
     finally:
         mf.pcg_destroy(h)
+    zo = oracle.precond(prob, r)
+    assert np.abs(z1h - zo).max() <= precond_tol(prob, zo)
+    sub, dia, sup = (t2[m * n:(m + 1) * n].reshape(r.shape) for m in range(3))
+    zm = np.zeros_like(z2h)
+    zp = np.zeros_like(z2h)
+    zm[:, 1:, :] = z2h[:, :-1, :]
+    zp[:, :-1, :] = z2h[:, 1:, :]
+    Mz = sub * zm + dia * z2h + sup * zp
+    scale = np.abs(sub * zm) + np.abs(dia * z2h) + np.abs(sup * zp) + np.abs(r)
+    assert np.all(np.abs(Mz - r) <= 64 * EPS * scale)
+    assert np.abs(z2h - z1h).max() > 1e-3 * np.abs(z1h).max()   # the second matrices really differ
