@@ -35,7 +35,8 @@
  * (torch's allocations are).  Besides its host-side object the handle holds
  * one 32-byte word of pinned host memory, to which the device writes each
  * step's stop decision (hipHostMalloc at creation, freed at pcg_destroy),
- * and one HIP event.
+ * and one HIP event.  pcg_solve_static uses a fixed device array that the
+ * library's code object holds (see there).
  *
  * Streams: every call is ordered on the handle's HIP stream (the one passed
  * to pcg_create, or pcg_set_stream).  pcg_apply_A and pcg_precond are
@@ -345,6 +346,27 @@ int pcg_solve_f32(pcg_handle *h, const float *b_dev, float *x_dev, double tol, i
 int pcg_solve_mixed(pcg_handle *h, const double *b_dev, double *x_dev, double tol, int32_t maxit,
                     void *workspace_dev, size_t workspace_bytes, int32_t *iters_out,
                     double *hist_host, int32_t *hist_len_out, double *final_rel_res);
+
+/* ---- The no-allocation solve --------------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture set-up, tight serving loops, harnesses that forbid
+ * allocation.  pcg_solve with its workspace in a fixed array that the
+ * library's device code object holds (pcg_solve_static_max_bytes bytes, 64
+ * MiB: each device the library runs on keeps one until the process ends).
+ * The call allocates nothing (no hipMalloc, no event, no allocating library
+ * routine); the caller still passes b, x and the host results.  The grid and
+ * maxit must fit the array: pcg_solve_workspace_bytes(h, maxit) <= the
+ * maximum (about 1.6 million points), else PCG_ERR_INVALID with the sizes in
+ * pcg_last_error.  Every call on one device shares that device's array, and
+ * each call leaves its state there: calls that overlap in time on one device
+ * (two host threads, or two handles' streams) race and give wrong results.
+ * Per-kernel timing (pcg_profile_enable) is not recorded during the call.
+ * Arguments, results and errors otherwise as pcg_solve; the same kernels,
+ * so the results equal pcg_solve's bit for bit. */
+size_t pcg_solve_static_max_bytes(void);
+int pcg_solve_static(pcg_handle *h, const double *b_dev, double *x_dev, double tol, int32_t maxit,
+                     int32_t *iters_out, double *hist_host, int32_t *hist_len_out,
+                     double *final_rel_res);
 
 /* Same contract as pcg_solve, computed by the standard (non-interleaved)
  * PCG of section 4.1: separate stencil, preconditioner and vector-update

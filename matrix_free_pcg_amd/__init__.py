@@ -17,7 +17,8 @@ from ._abi import (PCG_ERR_BREAKDOWN, PCG_ERR_HIP, PCG_ERR_INVALID, PCG_ERR_UNSU
                    pcg_apply_A_f32, pcg_precond_f32, pcg_solve_f32, pcg_solve_mixed,
                    PCG_KID_MG_VCYCLE, pcg_mg_setup, pcg_mg_num_levels, pcg_mg_level,
                    pcg_mg_workspace_bytes, pcg_mg_vcycle, pcg_solve_mg, pcg_handle_bytes,
-                   pcg_tuning_overrides, pcg_mg_setup_bytes, pcg_tridiag_bytes)
+                   pcg_tuning_overrides, pcg_solve_static, pcg_solve_static_max_bytes,
+                   pcg_mg_setup_bytes, pcg_tridiag_bytes)
 
 __all__ = [
     "workloads", "Handle", "PcgError", "pcg_create", "pcg_destroy", "pcg_set_stream",
@@ -27,5 +28,6 @@ __all__ = [
     "pcg_csr_assemble", "pcg_csr_spmv", "pcg_tridiag_assemble", "pcg_tridiag_factor",
     "pcg_tridiag_precond", "pcg_solve_csr", "pcg_apply_A_f32", "pcg_precond_f32", "pcg_solve_f32",
     "pcg_solve_mixed", "pcg_mg_setup", "pcg_mg_num_levels", "pcg_mg_level", "pcg_mg_workspace_bytes",
-    "pcg_mg_vcycle", "pcg_solve_mg", "pcg_handle_bytes", "pcg_tuning_overrides", "pcg_mg_setup_bytes", "pcg_tridiag_bytes",
+    "pcg_mg_vcycle", "pcg_solve_mg", "pcg_handle_bytes", "pcg_tuning_overrides", "pcg_solve_static",
+    "pcg_solve_static_max_bytes", "pcg_mg_setup_bytes", "pcg_tridiag_bytes",
 ]

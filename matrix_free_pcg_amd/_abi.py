@@ -39,6 +39,7 @@ EXPORTED = sorted([
     "pcg_handle_bytes", "pcg_create", "pcg_destroy", "pcg_set_stream", "pcg_tuning_overrides",
     "pcg_apply_A", "pcg_precond",
     "pcg_solve_workspace_bytes", "pcg_solve", "pcg_solve_standard", "pcg_solve_no_q",
+    "pcg_solve_static", "pcg_solve_static_max_bytes",
     "pcg_profile_enable",
     "pcg_profile_reset", "pcg_profile_read", "pcg_last_error", "pcg_version",
     "pcg_csr_nnz", "pcg_csr_assemble", "pcg_csr_spmv", "pcg_tridiag_bytes", "pcg_tridiag_assemble",
@@ -120,6 +121,10 @@ def load():
         lib.pcg_create_general.restype = ctypes.c_int
         lib.pcg_tuning_overrides.argtypes = [H]
         lib.pcg_tuning_overrides.restype = ctypes.c_int32
+        lib.pcg_solve_static.argtypes = [H, vp, vp, ctypes.c_double, ctypes.c_int32, i32p, dp, i32p, dp]
+        lib.pcg_solve_static.restype = ctypes.c_int
+        lib.pcg_solve_static_max_bytes.argtypes = []
+        lib.pcg_solve_static_max_bytes.restype = sz
         lib.pcg_mg_setup_bytes.argtypes = [H, ctypes.POINTER(pcg_mg_params)]
         lib.pcg_mg_setup_bytes.restype = sz
         lib.pcg_tridiag_bytes.argtypes = [H]
@@ -376,6 +381,26 @@ def pcg_solve(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
 def pcg_solve_no_q(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:
     """Interleaved PCG without storing q (A p recomputed; 72 B per point per iteration)."""
     return _solve(load().pcg_solve_no_q, h, b, x, tol, maxit, workspace)
+
+
+def pcg_solve_static_max_bytes() -> int:
+    return int(load().pcg_solve_static_max_bytes())
+
+
+def pcg_solve_static(h: Handle, b, x, tol: float, maxit: int) -> dict:
+    """pcg_solve with its workspace in the library's fixed device array (no
+    allocation in the library or here beyond the host history array)."""
+    hist = np.zeros(max(1, maxit + 1), dtype=np.float64)
+    iters = ctypes.c_int32(0)
+    hlen = ctypes.c_int32(0)
+    rel = ctypes.c_double(0.0)
+    rc = load().pcg_solve_static(h.ptr, _dev_ptr(b, h.n, "b"), _dev_ptr(x, h.n, "x"), float(tol), int(maxit),
+                                 ctypes.byref(iters), hist.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                 ctypes.byref(hlen), ctypes.byref(rel))
+    _check(h.ptr, rc, allow=(PCG_OK, PCG_NOT_CONVERGED, PCG_ERR_BREAKDOWN))
+    return dict(status=rc, iters=iters.value, hist=hist[: hlen.value].copy(),
+                final_rel_res=rel.value,
+                error=pcg_last_error(h.ptr) if rc == PCG_ERR_BREAKDOWN else "")
 
 
 def pcg_solve_standard(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dict:

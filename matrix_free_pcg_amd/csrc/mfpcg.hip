@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 #include <vector>
@@ -96,6 +97,44 @@ int fail(pcg_handle *h, int code, const char *fmt, ...)
 
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
+// ---- the fixed scratch array of pcg_solve_static ------------------------------
+// A file-scope device array that serves as the workspace of the solve entry
+// point that allocates nothing.  Each device that loads the library holds its
+// own copy until the process ends.  On the host the array's name is not a
+// device address: host code uses only the address hipGetSymbolAddress
+// returns, resolved once per device (with that device current) when the
+// first handle on the device is created.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Resolve the array's address on `device`, which must be current.
+int scratch_setup(int device)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return fail(nullptr, PCG_ERR_UNSUPPORTED, "device %d: at most %d devices are supported", device, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device])
+        return PCG_OK;
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+        return fail(nullptr, PCG_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", device,
+                    hipGetErrorString(e));
+    g_scratch_ptr[device] = ptr;
+    return PCG_OK;
+}
+
+void *scratch_of(int device)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_ptr[device];
+}
 
 // Column-pass geometry: C columns per workgroup and the segment length L
 // (default: the smallest of 8, 16, 32 with C * ceil(nz / L) <= 1024).
@@ -932,6 +971,10 @@ int create_handle(const char *who, const pcg_grid *grid, const Geometry &g, cons
         return bail(PCG_ERR_HIP);
     }
     memset(h->h_status, 0, sizeof(HostStatus));
+    if ((rc = scratch_setup(h->device)) != PCG_OK) {
+        h->err = g_create_error;
+        return bail(rc);
+    }
     const size_t ncoef = 2 * (size_t)nz + 3 * ncol;
     std::vector<double> coef;
     coef.reserve(ncoef);
@@ -1497,6 +1540,37 @@ int pcg_solve_mixed(pcg_handle *h, const double *b, double *x, double tol, int32
     return interleaved_loop<double, float>(h, a, w, false, "pcg_solve_mixed");
 }
 
+size_t pcg_solve_static_max_bytes(void) { return kScratchBytes; }
+
+int pcg_solve_static(pcg_handle *h, const double *b, double *x, double tol, int32_t maxit,
+                     int32_t *iters_out, double *hist_host, int32_t *hist_len_out, double *final_rel)
+{
+    const char *who = "pcg_solve_static";
+    if (!h)
+        return PCG_ERR_INVALID;
+    if (maxit < 0)
+        return fail(h, PCG_ERR_INVALID, "%s: maxit must be >= 0", who);
+    void *ws = scratch_of(h->device);
+    if (!ws)
+        return fail(h, PCG_ERR_HIP, "%s: the scratch array has no address on device %d", who, h->device);
+    const size_t need = workspace_layout(h, maxit, nullptr, nullptr);
+    if (need > kScratchBytes)
+        return fail(h, PCG_ERR_INVALID,
+                    "%s: grid %d x %d x %d with maxit %d needs %zu bytes of workspace; the fixed scratch "
+                    "array holds %zu (use pcg_solve with a workspace)",
+                    who, h->op.nx, h->op.ny, h->op.nz, maxit, need, kScratchBytes);
+    SolveArgs a{b, x, sizeof(double), tol, maxit, ws, kScratchBytes, iters_out, hist_host, hist_len_out, final_rel};
+    Workspace w{};
+    int rc = solve_prologue(h, a, &w, who);
+    if (rc != PCG_OK)
+        return rc;
+    // per-kernel timing would create events on first use: not recorded here
+    const bool profiling = h->profiling;
+    h->profiling = false;
+    rc = interleaved_loop<double, double>(h, a, w, false, who);
+    h->profiling = profiling;
+    return rc;
+}
 
 }   // extern "C"
 

@@ -161,7 +161,9 @@ def test_no_device_allocation_in_the_library():
         assert name not in src, name
 
 
-def test_size_queries_without_gpu(lib):
+def test_static_solve_contract_without_gpu(lib):
+    assert lib.pcg_solve_static_max_bytes() == 64 << 20
+    assert lib.pcg_solve_static(None, None, None, 1e-8, 10, None, None, None, None) == _abi.PCG_ERR_INVALID
     assert lib.pcg_tuning_overrides(None) == 0
     assert lib.pcg_tridiag_bytes(None) == 0
     p = _abi.pcg_mg_params(1, 0.8, 0, 2)
