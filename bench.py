@@ -347,10 +347,13 @@ def cpu_baseline(w, steps, variant="interleaved", mg_params=None):
         per = total / (res["iters"] + 1)
         how = "timed around the whole call, its set-up pass counted as one more step"
     else:
-        res = oracle.pcg(w.problem, rhs, tol=0.0, maxit=steps)
+        # one step more than timed: the last step of a call skips its
+        # preconditioner application, so only the complete steps before it count
+        res = oracle.pcg(w.problem, rhs, tol=0.0, maxit=steps + 1)
         total = time.perf_counter() - t0
-        per = res["loop_seconds"] / max(1, res["iters"])
-        how = "timed around the step loop"
+        per = res["full_steps_seconds"] / max(1, res["full_steps"])
+        how = (f"timed over its first {res['full_steps']} complete step(s) (stencil, preconditioner, "
+               f"dots, updates; the call ran one more)")
     if old_aff:
         os.sched_setaffinity(0, old_aff)
     return {"value": round(1.0 / per, 4), "unit": "iterations/s", "cores": 1, "kind": "oracle",

@@ -74,6 +74,8 @@ class Oracle:
         lib.orc_pcg.restype = i
         lib.orc_last_loop_seconds.argtypes = []
         lib.orc_last_loop_seconds.restype = d
+        lib.orc_last_full_steps_seconds.argtypes = [ctypes.POINTER(ctypes.c_int)]
+        lib.orc_last_full_steps_seconds.restype = d
         fp = ctypes.POINTER(ctypes.c_float)
         f = ctypes.c_float
         ip = ctypes.POINTER(ctypes.c_int)
@@ -305,8 +307,11 @@ class Oracle:
         st = self.lib.orc_pcg(prob.nx, prob.ny, prob.nz, prob.delta, _ptr(az), _ptr(ah), _ptr(b),
                               _ptr(x), float(tol), int(maxit), _ptr(hist), ctypes.byref(iters), ntr,
                               _ptr(tr[0]), _ptr(tr[1]), _ptr(tr[2]))
+        nfull = ctypes.c_int(0)
+        full_s = self.lib.orc_last_full_steps_seconds(ctypes.byref(nfull))
         out = dict(x=x, iters=iters.value, hist=hist[: iters.value + 1].copy(), status=st,
-                   loop_seconds=self.lib.orc_last_loop_seconds())
+                   loop_seconds=self.lib.orc_last_loop_seconds(),
+                   full_steps=nfull.value, full_steps_seconds=full_s)
         if ntr > 0:
             out.update(trace_r=tr[0], trace_z=tr[1], trace_p=tr[2])
         return out

@@ -153,6 +153,17 @@ int orc_precond(int nx, int ny, int nz, double delta, const double *az,
 static double g_loop_seconds = 0.0;
 double orc_last_loop_seconds(void) { return g_loop_seconds; }
 
+/* Wall time of the complete CG steps of the last orc_pcg call (each with its
+ * preconditioner application: the last step of a call skips it) and their
+ * number; timing only. */
+static double g_full_seconds = 0.0;
+static int g_full_steps = 0;
+double orc_last_full_steps_seconds(int *steps)
+{
+    if (steps) *steps = g_full_steps;
+    return g_full_seconds;
+}
+
 static double now_seconds(void)
 {
     struct timespec ts;
@@ -225,8 +236,12 @@ int orc_pcg(int nx, int ny, int nz, double delta, const double *az, const double
 
     t_loop = now_seconds();
     g_loop_seconds = 0.0;
+    g_full_seconds = 0.0;
+    g_full_steps = 0;
     for (int k = 1; k <= maxit; ++k) {
         g_loop_seconds = now_seconds() - t_loop;
+        g_full_seconds = g_loop_seconds;
+        g_full_steps = k - 1;
         orc_apply_A(nx, ny, nz, delta, az, ah, p, q);
         double sigma = orc_dot(n, p, q);
         if (!(sigma > 0.0) || !isfinite(sigma)) { status = ORC_ERR_BREAKDOWN; goto done; }

@@ -18,6 +18,8 @@ Calls only oracle/
     python tests/golden/make_fullsize_reference.py 6m     # general-1024x1024x128, multigrid
     python tests/golden/make_fullsize_reference.py 4f     # varying-1024x1024x128, binary32
     python tests/golden/make_fullsize_reference.py 4x     # varying-1024x1024x128, mixed
+    python tests/golden/make_fullsize_reference.py 5      # csr-vs-mf-2048x2048x128: its 50 fixed
+                                                          # steps (tol 0; 18 minutes, 26 GB of RAM)
 """
 import json
 import os

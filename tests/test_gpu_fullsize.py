@@ -15,7 +15,7 @@ import pytest
 
 import matrix_free_pcg_amd as mf
 import oracle
-from gpu_helpers import EPS, apply_tol, precond_tol, require_gpu, to_dev, to_host
+from gpu_helpers import EPS, apply_tol, check_mixed_against_oracle, precond_tol, require_gpu, to_dev, to_host
 from matrix_free_pcg_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -131,9 +131,12 @@ def test_cfg4_full_solve_true_residual(dev, cfg4):
 def test_cfg3_manufactured_full(dev):
     """512x512x128, b = A x_true: the first 3 steps against the oracle's
     (1e-11), and the full solve against the oracle's full solve: iterations
-    within 1, and the GPU iterate as close to x_true (the exact solution) as
-    the oracle's (within a factor 2) and within the condition-number bound of
-    tol; its true residual small."""
+    within 1 and the final iterates within rel-L2 1e-9 -- unless the oracle's
+    own solve of b perturbed at the rounding level (b (1 + 2^-52 u)) moves
+    its iterate by more than 1e-9, in which case the GPU iterate must instead
+    be as close to x_true (the exact solution) as the oracle's (within a
+    factor 2); in both cases within the condition-number bound of tol of
+    x_true, and its true residual small."""
     import torch
     w = W.make_workload(3)
     prob = w.problem
@@ -163,9 +166,20 @@ def test_cfg3_manufactured_full(dev):
     err_orc = np.linalg.norm(ref["x"] - w.x_true) / nt
     kappa = (prob.delta + 8 * 1.0 + 4 * prob.alpha_z_face.max()) / prob.delta
     tr = _true_residual(prob, b, xg)
-    print(f"[cfg3] iters gpu={res['iters']} oracle={ref['iters']} err to x_true gpu={err:.3e} "
-          f"oracle={err_orc:.3e} true-res={tr:.3e}", flush=True)
-    assert err <= 2.0 * err_orc
+    rel = np.linalg.norm(xg - ref["x"]) / np.linalg.norm(ref["x"])
+    spread = None
+    if rel > 1e-9:
+        u = np.random.default_rng(4242).uniform(-1.0, 1.0, size=b.shape)
+        refp = oracle.pcg(prob, b * (1.0 + 2.0 ** -52 * u), tol=w.tol, maxit=w.maxit)
+        spread = np.linalg.norm(refp["x"] - ref["x"]) / np.linalg.norm(ref["x"])
+    print(f"[cfg3] iters gpu={res['iters']} oracle={ref['iters']} rel-L2 gpu-oracle={rel:.3e} "
+          f"(oracle spread {spread}) err to x_true gpu={err:.3e} oracle={err_orc:.3e} true-res={tr:.3e}",
+          flush=True)
+    if spread is None:
+        assert rel <= 1e-9
+    else:
+        assert spread > 1e-9, (rel, spread)
+        assert err <= 2.0 * err_orc
     assert err <= kappa * w.tol
     assert tr <= 1e-8
 
@@ -174,8 +188,13 @@ def test_cfg5_explicit_path_full(dev):
     """2048x2048x128 with the 1024^2 operator: the CSR matrix applied to a field
     against the oracle's stencil (every element), the first 2 explicit CG steps
     against the oracle, and the 50-step iterates of the matrix-free
-    (interleaved) and explicit (CSR + stored tridiagonal) solves."""
+    (interleaved) and explicit (CSR + stored tridiagonal) solves each against
+    the oracle's 50-step solve stored by tests/golden/make_fullsize_reference.py
+    (residual histories within 1e-9 relative, x at 4096 seeded positions
+    within rel-L2 1e-9, its 2-norm within 1e-9) and against each other."""
     import torch
+    ref50 = _reference(W.CONFIG_NAMES[5])
+    assert ref50["iters"] == 50 and ref50["tol"] == 0.0
     t = time.time()
     w = W.make_workload(5)
     prob = w.problem
@@ -203,6 +222,9 @@ def test_cfg5_explicit_path_full(dev):
         resc = mf.pcg_solve_csr(h, C, tri, bd, xc, 0.0, 50, ws)
         torch.cuda.synchronize()
         d50 = float(torch.linalg.vector_norm(xm - xc) / torch.linalg.vector_norm(xc))
+        idx = torch.as_tensor(ref50["sample_index"], dtype=torch.int64, device=dev)
+        samples = {k: to_host(v.reshape(-1)[idx]) for k, v in (("mf", xm), ("csr", xc))}
+        norms = {k: float(torch.linalg.vector_norm(v)) for k, v in (("mf", xm), ("csr", xc))}
         del xm, xc, ws, bd, C, tri
     finally:
         mf.pcg_destroy(h)
@@ -211,6 +233,16 @@ def test_cfg5_explicit_path_full(dev):
     assert resm["iters"] == resc["iters"] == 50
     assert d50 <= 1e-10
     assert np.allclose(resm["hist"], resc["hist"], rtol=1e-8, atol=0)
+    ho = np.asarray(ref50["hist"])
+    xo = np.asarray(ref50["x_sample"])
+    for name, res in (("mf", resm), ("csr", resc)):
+        dh = np.max(np.abs(res["hist"] - ho) / ho)
+        rel = np.linalg.norm(samples[name] - xo) / np.linalg.norm(xo)
+        rn = abs(norms[name] - ref50["x_norm2"]) / ref50["x_norm2"]
+        print(f"[cfg5] {name} vs oracle 50 steps: history {dh:.2e} samples rel-L2 {rel:.2e} norm {rn:.2e}",
+              flush=True)
+        assert len(res["hist"]) == len(ho) == 51
+        assert dh <= 1e-9 and rel <= 1e-9 and rn <= 1e-9, (name, dh, rel, rn)
     t = time.time()
     yref = oracle.apply_A(prob, w.rhs)
     assert np.abs(y - yref).max() <= apply_tol(prob, w.rhs)
@@ -418,13 +450,13 @@ def test_f32_full_solve_against_oracle_reference(dev, cfg4):
 def test_mixed_full_solve_against_oracle_reference(dev, cfg4):
     """The mixed-precision solve (binary64 CG, binary32 column solve) of
     varying-1024x1024x128 against the oracle's complete mixed solve, stored
-    by the committed script, with the bars of the smaller mixed solve tests:
-    converged with the true residual ||b - A x||/||b|| <= 10 tol (evaluated
-    by the oracle's binary64 stencil), the step count within 20 % + 2 of the
-    oracle's mixed and binary64 counts, and the iterate at the 4096 stored
-    positions within 1e-8 rel-L2 of the oracle's mixed iterate.  The two
-    column solves round differently (segmented scans against one sequential
-    sweep), so the trajectories are not compared step by step."""
+    by the committed script, with the bars of the smaller mixed solve tests
+    (gpu_helpers.check_mixed_against_oracle: histories while ||r|| >= 1e-8
+    ||r_0||, crossings of 1e-6..1e-8 within one step, the step count between
+    the binary64 and the oracle's mixed count); converged with the true
+    residual ||b - A x||/||b|| <= 10 tol (evaluated by the oracle's binary64
+    stencil); the iterate at the 4096 stored positions within 1e-8 rel-L2 of
+    the oracle's mixed iterate."""
     import torch
     ref = _reference(W.CONFIG_NAMES[4] + "_mixed")
     ref64 = _reference(W.CONFIG_NAMES[4])
@@ -440,8 +472,8 @@ def test_mixed_full_solve_against_oracle_reference(dev, cfg4):
     finally:
         mf.pcg_destroy(h)
     assert res["status"] == mf.PCG_OK == ref["status"], (res, ref["status"])
-    lo, hi = min(ref["iters"], ref64["iters"]), max(ref["iters"], ref64["iters"])
-    assert 0.8 * lo - 2 <= res["iters"] <= 1.2 * hi + 2, (res["iters"], ref["iters"], ref64["iters"])
+    check_mixed_against_oracle(w.name, res["hist"], res["iters"], ref["hist"], ref["iters"], ref64["hist"],
+                               ref64["iters"])
     tr = _true_residual(w.problem, w.rhs, xg.reshape(w.rhs.shape))
     idx = np.asarray(ref["sample_index"])
     xo = np.asarray(ref["x_sample"])

@@ -70,10 +70,16 @@ def test_mg_levels_match_oracle(dev, label, make):
     finally:
         mf.pcg_destroy(h)
     assert nlev == oracle.mg_num_levels(gp.nx, gp.ny), (label, nlev)
-    # coarsen the GPU's own level-0 tables on the oracle: the sums are then
-    # of identical binary64 values in identical order
-    _, _, area0, ax0, ay0 = levels[0]
-    cur = W.GeneralProblem(gp.nx, gp.ny, gp.nz, gp.a, gp.d, gp.beta_face, area0, ax0, ay0)
+    # level 0 is the operator in general form as the oracle's side builds it
+    # (edge = mean of the two cells' alpha_h: one addition and one halving,
+    # identical in binary64), and every coarser level is the oracle's
+    # coarsening of the level above, bit for bit (the same additions in the
+    # same order)
+    nx0, ny0, area0, ax0, ay0 = levels[0]
+    assert (nx0, ny0) == (gp.nx, gp.ny), label
+    assert np.array_equal(area0, gp.area) and np.array_equal(ax0, gp.alpha_x) and \
+        np.array_equal(ay0, gp.alpha_y), label
+    cur = gp
     for l in range(1, nlev):
         cur = oracle.mg_coarsen(cur)
         nx, ny, area, ax, ay = levels[l]

@@ -33,7 +33,7 @@ import pytest
 
 import matrix_free_pcg_amd as mf
 import oracle
-from gpu_helpers import require_gpu, stencil_scale, to_host
+from gpu_helpers import check_mixed_against_oracle, require_gpu, stencil_scale, to_host
 from matrix_free_pcg_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -207,9 +207,8 @@ def test_solve_mixed_matches_oracle(dev, label, make):
     ref = oracle.pcg_mixed(prob, w.rhs, tol=tol, maxit=w.maxit)
     r64 = oracle.pcg(prob, w.rhs, tol=tol, maxit=w.maxit)
     assert res["status"] == ref["status"] == 0, (label, res, ref["status"])
-    lo = min(ref["iters"], r64["iters"])
-    hi = max(ref["iters"], r64["iters"])
-    assert 0.8 * lo - 2 <= res["iters"] <= 1.2 * hi + 2, (label, res["iters"], ref["iters"], r64["iters"])
+    check_mixed_against_oracle(label, res["hist"], res["iters"], ref["hist"], ref["iters"], r64["hist"],
+                               r64["iters"])
     tr = np.linalg.norm(w.rhs - oracle.apply_A(prob, xg)) / np.linalg.norm(w.rhs)
     rel = np.linalg.norm(xg - ref["x"]) / np.linalg.norm(ref["x"])
     print(f"{label} mixed: iters gpu {res['iters']} oracle {ref['iters']} (binary64 {r64['iters']}); "
