@@ -237,6 +237,12 @@ def parse():
     ap.add_argument("--stream-probe-dtype", choices=["f64", "f32"], default="f64",
                     help="element of the probe's vectors: f64 (8-byte accesses, the binary64 passes) or "
                          "f32 (4-byte, the binary32 passes); 1 GiB vectors either way")
+    ap.add_argument("--counter-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write the HBM counter record of the fused passes from four rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE of a --fixed-iterations solve; the same of --copy-calibration)")
+    ap.add_argument("--counter-steps", type=int, default=10, help="--counter-summary: the solve's fixed steps")
+    ap.add_argument("--counter-commands", default="", help="--counter-summary: the commands, ';'-separated")
+    ap.add_argument("--counter-out", default=None, help="--counter-summary: directory to write to (default profiles/)")
     ap.add_argument("--fixed-iterations", type=int, default=0,
                     help="run exactly N CG steps per solve (tol 0) instead of solving to 1e-10")
     return ap.parse_args()
@@ -260,6 +266,122 @@ def copy_calibration():
     dt = (time.perf_counter() - t) / reps
     print(json.dumps({"copy_bytes_read": n * 8, "copy_bytes_written": n * 8,
                       "copy_ms": dt * 1e3, "copy_GBps": 2 * n * 8 / dt / 1e9}), flush=True)
+
+
+def _counter_rows(run_dir):
+    """(dispatch id, kernel name, counter name, value) of every row of the
+    rocprofv3 counter-collection CSV files under run_dir."""
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    """{dispatch id: (kernel name, summed counter value)} in dispatch order."""
+    out = {}
+    for d, k, c, v in rows:
+        if c == counter:
+            name, tot = out.get(d, (k, 0.0))
+            out[d] = (name, tot + v)
+    return dict(sorted(out.items()))
+
+
+def _short_kernel(name):
+    """`k_stencil<4, 8, true, double, double, 4>` from a demangled kernel name."""
+    base = name.split("(")[0].replace("void ", "").replace("mfpcg::", "")
+    return base.strip()
+
+
+def counter_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, steps, commands, out_dir=None):
+    """Write the HBM counter record of the binary64 fused passes (the JSON the
+    roofline's `traffic` reads, and its Markdown summary) from four rocprofv3
+    runs: FETCH_SIZE and WRITE_SIZE of a solve of `steps` fixed steps of
+    varying-1024x1024x128 (bench.py --steps 1 --warmup 0 --fixed-iterations
+    steps), and of the 1 GiB copy (bench.py --copy-calibration)."""
+    import hashlib
+    n = 1024 * 1024 * 128
+    copy_bytes = 1 << 30
+    cf = [v for _, (k, v) in _per_dispatch(_counter_rows(copy_fetch_dir), "FETCH_SIZE").items() if "copyBuffer" in k]
+    cw = [v for _, (k, v) in _per_dispatch(_counter_rows(copy_write_dir), "WRITE_SIZE").items() if "copyBuffer" in k]
+    if not cf or not cw:
+        raise SystemExit("no copy dispatch in the calibration runs")
+    f_kib, w_kib = sorted(cf)[len(cf) // 2], sorted(cw)[len(cw) // 2]     # the median dispatch
+    fetch_scale, write_scale = copy_bytes / (f_kib * 1024), copy_bytes / (w_kib * 1024)
+    fetch = _per_dispatch(_counter_rows(fetch_dir), "FETCH_SIZE")
+    write = _per_dispatch(_counter_rows(write_dir), "WRITE_SIZE")
+
+    def classify(fetch_or_write):
+        """Dispatch values of the two passes by step class, in launch order."""
+        prec, spmv = [], []
+        for _, (k, v) in fetch_or_write.items():
+            short = _short_kernel(k)
+            if short.startswith("k_column_full<16, 1, true, double, double, 0>"):
+                prec.append((short, v))
+            elif short.startswith("k_stencil<") and short.split(",")[1].strip() in ("0", "7", "8"):
+                spmv.append((short, v))
+        if len(prec) != steps + 1 or len(spmv) != steps + 1:
+            raise SystemExit(f"expected {steps + 1} launches of each pass, found {len(prec)} and {len(spmv)}")
+        spmv = spmv[:-1]   # the last stencil launch only applies the pending x update
+        out = {"fused_prec": {"first": [prec[0]], "rest": prec[1:]}, "fused_spmv": {"first": [], "odd": [], "even": []}}
+        for kk, e in enumerate(spmv):
+            out["fused_spmv"]["first" if kk == 0 else ("odd" if kk % 2 else "even")].append(e)
+        return out
+
+    cf_, cw_ = classify(fetch), classify(write)
+    alg = {("fused_prec", "first"): 16, ("fused_prec", "rest"): 32, ("fused_spmv", "first"): 24,
+           ("fused_spmv", "odd"): 40, ("fused_spmv", "even"): 64}
+    passes = {}
+    lines = []
+    for kern in ("fused_prec", "fused_spmv"):
+        passes[kern] = {}
+        for cls, fl in cf_[kern].items():
+            wl = cw_[kern][cls]
+            rb = sum(v for _, v in fl) / len(fl) * 1024 * fetch_scale
+            wb = sum(v for _, v in wl) / len(wl) * 1024 * write_scale
+            passes[kern][cls] = {"kernel": fl[0][0], "dispatches": len(fl), "read_bytes": rb, "write_bytes": wb,
+                                 "traffic_bytes": rb + wb, "algorithmic_bytes": alg[(kern, cls)] * n}
+            lines.append(f"| {kern} | {cls} | `{fl[0][0]}` | {len(fl)} | {rb / n:.2f} | {wb / n:.2f} | "
+                         f"{(rb + wb) / 1e9:.3f} | {alg[(kern, cls)] * n / 1e9:.3f} |")
+    src = KERNEL_SOURCE
+    rec = {"variant": "interleaved", "source": "matrix_free_pcg_amd/csrc/kernels.hpp",
+           "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "code_digest": kernel_source_digest(),
+           "code_digest_note": "sha256 of kernels.hpp with comments removed and whitespace collapsed "
+                               "(bench.kernel_source_digest)",
+           "workload": "varying-1024x1024x128", "steps_profiled": steps,
+           "calibration": {"copy_bytes": copy_bytes, "FETCH_SIZE_KiB_per_dispatch": f_kib,
+                           "WRITE_SIZE_KiB_per_dispatch": w_kib, "fetch_scale": fetch_scale,
+                           "write_scale": write_scale},
+           "passes": passes}
+    out_json = TRAFFIC_FILE if out_dir is None else os.path.join(out_dir, os.path.basename(TRAFFIC_FILE))
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    md = os.path.join(out_dir or os.path.join(ROOT, "profiles"), "hbm_counters_fused_passes_varying-1024x1024x128.md")
+    with open(md, "w") as f:
+        f.write("# HBM traffic of the fused passes, varying-1024x1024x128 (fp64), variant `interleaved`\n\n")
+        f.write("Commands (from /tmp, TMPDIR=/tmp; one counter per run), then the summary written by the last one:\n\n```\n")
+        f.write("\n".join(commands) + "\n```\n\n")
+        f.write(f"Calibration: a plain 1 GiB device copy (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = {f_kib:.1f} KiB "
+                f"and WRITE_SIZE = {w_kib:.1f} KiB per dispatch for 1048576 KiB moved each way, so read counts are "
+                f"scaled by {fetch_scale:.4f} and write counts by {write_scale:.4f}.\n\n")
+        f.write(f"Kernel source: `matrix_free_pcg_amd/csrc/kernels.hpp`, sha256 `{rec['source_sha256']}`.\n\n")
+        f.write(f"A {steps}-step solve; dispatches grouped by the step class they belong to (the stencil pass "
+                "alternates between a form that defers the x update and one that applies two). The stencil launch "
+                "after the last step, which only applies the pending x update, is left out.\n\n")
+        f.write("| pass | step class | kernel | dispatches | read B/point | write B/point | traffic GB per launch | "
+                "algorithmic GB per launch |\n|---|---|---|---:|---:|---:|---:|---:|\n")
+        f.write("\n".join(lines) + "\n\nN = 134217728 points.  Reads above the algorithmic count: in the stencil "
+                "pass the i-halo lines at the edges of each XCD's strip of tiles (and a few j / k halo lines that "
+                "miss L2); in the preconditioner pass the per-column Thomas multipliers at the boundaries of its "
+                "16-level segments and the per-column coefficient tables (area and the two edge fields).\n")
+    print(json.dumps({"written": [out_json, md]}), flush=True)
 
 
 # (reads, writes, pass it stands for)
@@ -462,6 +584,11 @@ def main():
     import numpy as np
     import torch
 
+    if args.counter_summary:
+        counter_summary(*args.counter_summary, steps=args.counter_steps,
+                        commands=[c.strip() for c in args.counter_commands.split(";") if c.strip()],
+                        out_dir=args.counter_out)
+        return
     if args.copy_calibration:
         copy_calibration()
         return

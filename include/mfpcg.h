@@ -292,8 +292,8 @@ int pcg_mg_level(pcg_handle *h, int32_t level, int32_t *nx, int32_t *ny, double 
                  double *alpha_x_host, double *alpha_y_host);
 
 /* Bytes of device workspace of pcg_solve_mg with this maxit (those of
- * pcg_solve, one more N-vector, and three vectors per coarse level: about
- * seven N-vectors for a full hierarchy).  0 before pcg_mg_setup. */
+ * pcg_solve, two more N-vectors, and four vectors per coarse level: about
+ * 8.3 N-vectors for a full hierarchy).  0 before pcg_mg_setup. */
 size_t pcg_mg_workspace_bytes(const pcg_handle *h, int32_t maxit);
 
 /* z = B r, one V-cycle.  r_dev, z_dev: N doubles each, must not overlap each

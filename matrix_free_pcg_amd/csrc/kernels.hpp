@@ -292,10 +292,10 @@ enum : int { UPD_NONE = 0, UPD_Q = 1, UPD_AP = 2 };
 // semi-coarsening, the column solve as damped block-Jacobi smoother), with
 // y = M^{-1} rr:
 //   MG_FIRST  rr from the UPD mode, z = omega y    (first sweep from z = 0)
-//   MG_CORR   rr = w, a residual f - A q computed by a stencil pass into
-//             z's buffer; z = q + omega y          (further sweeps)
-//   MG_POST   rr = t - A (P zc), t = f - A q the residual the restriction
-//             kept in z's buffer; z = (q + P zc) + omega y: the sweep after the
+//   MG_CORR   rr = rin, a residual f - A q computed by a stencil pass;
+//             z = q + omega y                      (further sweeps)
+//   MG_POST   rr = rin - A (P zc), rin the residual t = f - A q kept by the
+//             restriction; z = (q + P zc) + omega y: the sweep after the
 //             coarse correction, with the residual of q + P zc formed from t
 //             and the coarse correction alone (no neighbour reads of q)
 //   MG_SWEEP  with UPD_AP: rr = rin - A q with q's neighbours read here (the
@@ -316,17 +316,14 @@ struct MgArgs {
 // Where a column pass reads its residual.  The pointer arguments of the
 // column kernels are restrict-qualified, so no two of them may name the same
 // vector: in the solve's in-place update r -= alpha q the residual is read
-// and written through rout, and in the multigrid corrected sweeps (MG_CORR,
-// MG_POST) it is read through z, whose buffer then receives the new iterate
-// (each thread reads its own elements before it writes them); rin is null in
-// those forms and is read only in the others.
+// and written through rout (each thread reads its own elements before it
+// writes them) and rin is null; every other form reads rin, a vector none of
+// the other arguments names.
 template <int UPD, int MG, typename TV, typename TZ>
-__device__ __forceinline__ const TV *residual_source(const TV *rin, TV *rout, TZ *z)
+__device__ __forceinline__ const TV *residual_source(const TV *rin, TV *rout, TZ *)
 {
     if constexpr (MG != MG_SWEEP && UPD != UPD_NONE)
         return rout;
-    else if constexpr (MG == MG_CORR || MG == MG_POST)
-        return (const TV *)z;
     else
         return rin;
 }
@@ -782,10 +779,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         // Parent rows are wave-uniform; a lane adds the byte offset of its parent.
         const int jp = (j + 1 == o.ny) ? 0 : j + 1;
         const int jm = (j == 0) ? o.ny - 1 : j - 1;
-        const int ie = lane == 0 ? (i == 0 ? nx - 1 : i - 1) : (i + 1 == nx ? 0 : i + 1);
-        const bool edge = lane == 0 || lane == kWave - 1;
         const size_t ksc = (size_t)mg.ncx;
-        const unsigned pl = (unsigned)(i / mg.fx) * 8u, pe = (unsigned)(ie / mg.fx) * 8u;
+        const unsigned pl = (unsigned)(i / mg.fx) * 8u;
         const int J = j / mg.fy;
         const bool om = jm / mg.fy != J, op = jp / mg.fy != J;   // neighbour rows with another parent
         auto prow = [&](int jj) { return mg.zc + ksc * ((size_t)o.nz * (size_t)(jj / mg.fy) + (size_t)k0); };
@@ -794,15 +789,26 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         const double *zy2 = prow(jp);
         const int kb = k0 > 0 ? -1 : 0;                      // level below, clamped
         const int ka = k0 + L < o.nz ? L : L - 1;            // level above, clamped
-        double cc[L + 2], cy[L], ce[L];
+        double cc[L + 2], cy[L];
         cc[0] = ld_at(zcc + (ptrdiff_t)kb * (ptrdiff_t)ksc, pl);
         cc[L + 1] = ld_at(zcc + (size_t)ka * ksc, pl);
+        // the parents of the tile's two outside columns at the segment's
+        // levels in one load: lane e < L takes the left one's at level k0 + e,
+        // lane L + e the right one's (handed to lanes 0 and 63 by readlane)
+        double ev = 0.0;
+        {
+            static_assert(2 * L <= kWave, "edge parents in one load");
+            const int t0 = i - lane;
+            const int io = lane < L ? (t0 == 0 ? nx - 1 : t0 - 1) : (t0 + kWave == nx ? 0 : t0 + kWave);
+            const int e = lane < L ? lane : lane - L;
+            if (lane < 2 * L)
+                ev = ld_at(zcc + (size_t)e * ksc, (unsigned)(io / mg.fx) * 8u);
+        }
 #pragma unroll
         for (int t = 0; t < L; ++t) {
             rr[t] = ld_at(rsrc + row0 + (size_t)t * nx, cv);
             cc[t + 1] = ld_at(zcc + (size_t)t * ksc, pl);
             cy[t] = (om || op) ? ld_at(zyo + (size_t)t * ksc, pl) : 0.0;
-            ce[t] = edge ? ld_at(zcc + (size_t)t * ksc, pe) : 0.0;
         }
         const Faces fc = column_faces(o, i, j);
 #pragma unroll
@@ -810,8 +816,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
             const double c = cc[t + 1];
             const double l_s = __shfl_up(c, 1, kWave);
             const double r_s = __shfl_down(c, 1, kWave);
-            const double xl = lane == 0 ? ce[t] : l_s;
-            const double xr = lane == kWave - 1 ? ce[t] : r_s;
+            const double xl = lane == 0 ? lane_value(ev, t) : l_s;
+            const double xr = lane == kWave - 1 ? lane_value(ev, L + t) : r_s;
             const double ym = om ? cy[t] : c;
             double yp = c;
             if (op)   // wave-uniform; both rows differ only when fy = 1
@@ -910,7 +916,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         if constexpr (MG == MG_CORR || MG == MG_POST) {
             // MG_POST loads the iterate (plus the coarse correction) and f
             // here, after the solve: its load phase holds the coarse
-            // stencil's operands
+            // stencil's operands (issued all together here, they spill)
             double zq, fv;
             if constexpr (MG == MG_CORR) {
                 zq = zb[t];

@@ -1209,10 +1209,12 @@ namespace {
 pcg_handle *mg_level(pcg_handle *h, int l) { return l == 0 ? h : h->mg_levels[(size_t)l - 1]; }
 
 // Per level: the right-hand side f (levels >= 1; level 0 works on the
-// solve's residual) and the two iterate buffers U, V (the cycle's result
-// lands in V; level 0's V is the solve's z).
+// solve's residual), the two iterate buffers U, V (the cycle's result lands
+// in V; level 0's V is the solve's z) and W, which holds a residual (the
+// restriction's t = f - A z, or w = f - A z of a two-pass sweep) that the
+// next column pass reads while it writes an iterate buffer.
 struct MgWork {
-    std::vector<double *> f, U, V;
+    std::vector<double *> f, U, V, W;
 };
 
 size_t mg_layout(const pcg_handle *h, int32_t maxit, char *base, Workspace *w, MgWork *mw)
@@ -1226,19 +1228,22 @@ size_t mg_layout(const pcg_handle *h, int32_t maxit, char *base, Workspace *w, M
         mw->f.assign(nl, nullptr);
         mw->U.assign(nl, nullptr);
         mw->V.assign(nl, nullptr);
+        mw->W.assign(nl, nullptr);
     }
-    const size_t o0 = take(h->n * sizeof(double));
+    const size_t o0 = take(h->n * sizeof(double)), ow0 = take(h->n * sizeof(double));
     if (mw && base) {
         mw->U[0] = (double *)(base + o0);
         mw->V[0] = wl->z;
+        mw->W[0] = (double *)(base + ow0);
     }
     for (size_t l = 1; l < nl; ++l) {
         const size_t bytes = h->mg_levels[l - 1]->n * sizeof(double);
-        const size_t of = take(bytes), ou = take(bytes), ov = take(bytes);
+        const size_t of = take(bytes), ou = take(bytes), ov = take(bytes), ow = take(bytes);
         if (mw && base) {
             mw->f[l] = (double *)(base + of);
             mw->U[l] = (double *)(base + ou);
             mw->V[l] = (double *)(base + ov);
+            mw->W[l] = (double *)(base + ow);
         }
     }
     return off;
@@ -1350,7 +1355,7 @@ void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const 
     pcg_handle *h = mg_level(h0, l);
     const int nlev = 1 + (int)h0->mg_levels.size();
     const double *f = (upd != UPD_NONE) ? rout : rin;
-    double *V = mw.V[(size_t)l], *U = mw.U[(size_t)l];
+    double *V = mw.V[(size_t)l], *U = mw.U[(size_t)l], *Wr = mw.W[(size_t)l];
     const MgArgs a{nullptr, f, h0->mg_omega, 0, 1, 1};
     auto sweep = [&](double *cur, double *oth, double *parts) {
         if (!parts && h->op.L <= 8) {   // one pass: the residual formed in the column kernel
@@ -1358,8 +1363,8 @@ void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const 
             mg_column(h, MG_SWEEP, f, cur, nullptr, oth, st, 0, nullptr, UPD_AP, a);
             return;
         }
-        stencil<double, double>(h, SP_RESID, cur, f, nullptr, nullptr, oth, nullptr, nullptr);
-        mg_column(h, MG_CORR, nullptr, cur, nullptr, oth, st, 0, parts, UPD_NONE, a);
+        stencil<double, double>(h, SP_RESID, cur, f, nullptr, nullptr, Wr, nullptr, nullptr);
+        mg_column(h, MG_CORR, Wr, cur, nullptr, oth, st, 0, parts, UPD_NONE, a);
     };
     if (l == nlev - 1) {
         if ((size_t)h->op.nx * h->op.ny == 1) {
@@ -1385,10 +1390,10 @@ void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const 
     }
     pcg_handle *c = mg_level(h0, l + 1);
     const int fx = h0->mg_fx[(size_t)l], fy = h0->mg_fy[(size_t)l];
-    mg_restrict(h, fx, fy, f, cur, oth, mw.f[(size_t)l + 1], c->op.nx, st);
+    mg_restrict(h, fx, fy, f, cur, Wr, mw.f[(size_t)l + 1], c->op.nx, st);
     mg_cycle(h0, mw, l + 1, mw.f[(size_t)l + 1], nullptr, nullptr, UPD_NONE, st, 0, nullptr);
     const MgArgs ap{mw.V[(size_t)l + 1], f, h0->mg_omega, c->op.nx, fx, fy};
-    mg_column(h, MG_POST, nullptr, cur, nullptr, oth, st, 0, nu == 1 ? partials : nullptr, UPD_NONE, ap);
+    mg_column(h, MG_POST, Wr, cur, nullptr, oth, st, 0, nu == 1 ? partials : nullptr, UPD_NONE, ap);
     std::swap(cur, oth);
     for (int sw = 1; sw < nu; ++sw) {
         sweep(cur, oth, sw == nu - 1 ? partials : nullptr);
