@@ -396,8 +396,9 @@ def test_f32_full_solve_against_oracle_reference(dev, cfg4):
     solve's forward error on b.  Every application of the two column solves
     (segmented scans against one sequential sweep) differs by up to f, and
     to first order these differences add up over the steps; the shorter
-    solves' bar 10 f is the same bound at k = 10.  Measured: 1.1e-2 at step
-    135 against a bar of 0.14, growing with k from 1e-4 at step 1.  The
+    solves' bar 10 f is the same bound at k = 10.  Measured: at most 2.9e-3,
+    0.02 of the bar (1.1e-2 at step 135 while the column kernels summed the
+    pivots' diagonal in another order than the oracle).  The
     oracle's own deviation when b is perturbed at binary32's rounding level
     (stored beside its history, printed) stays near 5e-6: the divergence
     comes from the column solve's rounding, not from b."""

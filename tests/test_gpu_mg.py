@@ -7,16 +7,24 @@ Tolerances:
   * coarse coefficients: bit-exact (both sides sum the same binary64 values
     in the same order, additions only);
   * one V-cycle z = B r: every sweep is a stencil pass and a column solve
-    whose GPU and oracle results differ by rounding (16 eps S and 64 eps
-    kappa ||z|| per pass, as in the single-pass tests); a cycle composes a
-    few such passes per level, so |z_gpu - z_orc| <= 1e-9 ||z_orc||_inf
-    (measured differences are below 1e-12 relative);
+    whose GPU and oracle results differ by rounding, and the coarsest
+    single column (no horizontal coupling left: |T| (a_k + vertical
+    Laplacian), condition ~4e7 for the general operators) turns a pivot
+    rounded differently into a difference of eps * kappa.  The bar is
+    therefore the oracle's own spread when every coefficient is perturbed
+    by one ulp (the GPU's result is that of a problem rounded a few ulps
+    apart): |z_gpu - z_orc| <= max(1e-11, 8 spread) ||z_orc||_inf.  The
+    full-depth cycles measure 4e-10 to 1.3e-9 for that spread (1e-16 for
+    a perturbed r: the sensitivity is the matrix's, not the input's) and
+    4e-10 to 1.4e-9 for the GPU; the others 1e-13 and below 6e-13;
   * solves: as the other solve tests (iterations within 1, final iterates
     within rel-L2 1e-9, residual histories within 10x the oracle's own
     spread under an ulp-level perturbation of b, floor 1e-6);
   * at full size, where the oracle is too slow, properties that hold at any
     size: B is symmetric (<B u, v> = <u, B v>) and positive, and the solve
     converges with a true residual within 10 tol."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -36,6 +44,24 @@ def dev():
 
 def as_general(prob):
     return prob if isinstance(prob, W.GeneralProblem) else general_from_special(prob)
+
+
+def coefficient_spread(gp, r, mg, seeds=(700, 701)):
+    """Largest relative change of the oracle's V-cycle when every
+    coefficient (a, d, beta, |T|, alpha_x, alpha_y) is multiplied by
+    1 + 2^-52 u, u uniform in [-1, 1]: how far apart two correct cycles on
+    operators rounded one ulp apart lie."""
+    zo = oracle.mg_vcycle(gp, r, **mg)
+    spread = 0.0
+    for seed in seeds:
+        rng = np.random.default_rng(seed)
+        kw = {}
+        for name in ("a", "d", "beta_face", "area", "alpha_x", "alpha_y"):
+            v = np.asarray(getattr(gp, name), dtype=np.float64)
+            kw[name] = np.ascontiguousarray(v * (1.0 + 2.0 ** -52 * rng.uniform(-1.0, 1.0, size=v.shape)))
+        zp = oracle.mg_vcycle(dataclasses.replace(gp, **kw), r, **mg)
+        spread = max(spread, float(np.abs(zp - zo).max() / np.abs(zo).max()))
+    return zo, spread
 
 
 GRIDS = [
@@ -111,10 +137,11 @@ def test_vcycle_matches_oracle(dev, label, make, pi):
         z, z2 = to_host(zd), to_host(zd2)
     finally:
         mf.pcg_destroy(h)
-    zo = oracle.mg_vcycle(gp, r, **mg)
+    zo, spread = coefficient_spread(gp, r, mg)
     err = np.abs(z - zo).max() / np.abs(zo).max()
-    print(f"{label} {mg}: rel max err {err:.2e}")
-    assert np.all(np.isfinite(z)) and err <= 1e-9, (label, mg, err)
+    bar = max(1e-11, 8.0 * spread)
+    print(f"{label} {mg}: rel max err {err:.2e} (coefficient spread {spread:.2e}, bar {bar:.2e})")
+    assert np.all(np.isfinite(z)) and err <= bar, (label, mg, err, spread)
     assert np.array_equal(z, z2), label
 
 
