@@ -93,8 +93,14 @@ typedef struct {
  *   MFPCG_ST_JT      rows per fused stencil tile, 1, 4 or 8
  *   MFPCG_COL_STRIP, MFPCG_ST_STRIP  i-tiles per strip of the tile order
  *                    (one strip per XCD)
+ * and pcg_mg_setup reads
+ *   MFPCG_MG_COARSE_C  columns per column-pass workgroup on the coarsest
+ *                    level, 16, 32 or 64 (the widest of 64, 32, 16 that
+ *                    gives at least 256 workgroups, else 16; 64 for a
+ *                    single column or segments longer than 8 levels)
  * pcg_tuning_overrides reports which of them were set when a handle was
- * created, as a mask of these bits (0: every default): */
+ * created (or its hierarchy set up), as a mask of these bits (0: every
+ * default): */
 #define PCG_TUNE_COL_C 0x001
 #define PCG_TUNE_COL_L 0x002
 #define PCG_TUNE_COL_LF 0x004
@@ -105,6 +111,7 @@ typedef struct {
 #define PCG_TUNE_ST_JT 0x080
 #define PCG_TUNE_COL_STRIP 0x100
 #define PCG_TUNE_ST_STRIP 0x200
+#define PCG_TUNE_MG_COARSE_C 0x400
 
 /* Operator coefficients (section 3, eqs. (5)-(8); section 4.2, eq. (17)).
  *   delta         zero-order term, > 0

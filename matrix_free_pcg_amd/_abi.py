@@ -52,7 +52,7 @@ EXPORTED = sorted([
 PCG_TUNE_NAMES = {
     0x001: "MFPCG_COL_C", 0x002: "MFPCG_COL_L", 0x004: "MFPCG_COL_LF", 0x008: "MFPCG_ST_L",
     0x010: "MFPCG_ST_W", 0x020: "MFPCG_COL_FULL", 0x040: "MFPCG_ST_FULL", 0x080: "MFPCG_ST_JT",
-    0x100: "MFPCG_COL_STRIP", 0x200: "MFPCG_ST_STRIP",
+    0x100: "MFPCG_COL_STRIP", 0x200: "MFPCG_ST_STRIP", 0x400: "MFPCG_MG_COARSE_C",
 }
 
 

@@ -37,6 +37,7 @@ namespace mfpcg {
 constexpr int kWave = 64;
 constexpr int kMaxThreads = 1024;
 constexpr int kXcds = 8;
+constexpr int kCus = 256;   // compute units (32 per XCD)
 
 // Operator and launch geometry, passed by value to every kernel.
 struct Op {
@@ -151,9 +152,14 @@ __device__ __forceinline__ Faces column_faces(const Op &o, int i, int j)
 // edges f: the diagonal's zero-order and horizontal part |T| a_k + d_k alpha_T,
 // and the vertical couplings lo = |T| beta_k (to k-1), up = |T| beta_{k+1}.
 template <typename T>
+__device__ __forceinline__ T diag_base_of(const FacesT<T> &f, T aT, double a_k, double d_k)
+{
+    return f.area * (T)a_k + (T)d_k * aT;
+}
+template <typename T>
 __device__ __forceinline__ T diag_base(const Op &o, const FacesT<T> &f, T aT, int k)
 {
-    return f.area * (T)o.lev_a[k] + (T)o.lev_d[k] * aT;
+    return diag_base_of(f, aT, o.lev_a[k], o.lev_d[k]);
 }
 
 // Thomas pivot of level k (section 4.2, eq. (19); Appendix A, Algorithm 3):
@@ -339,9 +345,15 @@ __device__ __forceinline__ size_t mg_parent(const MgArgs &m, int nz, int i, int 
     return (size_t)(i / m.fx) + (size_t)m.ncx * ((size_t)k + (size_t)nz * (size_t)(j / m.fy));
 }
 
+// Threads per workgroup a column-solve instantiation is compiled for: the
+// multigrid forms on narrow tiles (a coarsest level) have at most 16
+// segments per column, the rest up to 1024 threads.
+template <int C, int MG>
+constexpr int col_bound() { return (MG != MG_NONE && C < kWave) ? 16 * C : kMaxThreads; }
+
 template <int L, int C, int UPD, bool DOTS, bool STORED, typename TV = double, typename TZ = double,
           int MG = MG_NONE>
-__global__ __launch_bounds__(kMaxThreads) void k_column_solve(
+__global__ __launch_bounds__((col_bound<C, MG>())) void k_column_solve(
     const TV *__restrict__ rin, const TV *__restrict__ q, TV *__restrict__ rout,
     TZ *__restrict__ z, Op o, const SolveState *__restrict__ st, int first,
     double *__restrict__ partials, const double *__restrict__ tri,
@@ -381,6 +393,11 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     const size_t base = lin(o, ic, j, 0);
     const size_t ks = (size_t)o.nx;
     const TV alpha = MG == MG_SWEEP ? (TV)1 : ((UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0);
+    // the Thomas multiplier at the segment's lower boundary (set-up table),
+    // requested before the segment's other loads
+    const TZ phi_in = (s > 0 && active)
+                          ? ld_s(phib_tab + (size_t)(s * o.pst - 1) * ((size_t)o.nx * o.ny) + (size_t)j * o.nx + ic)
+                          : (TZ)0;
 
     // The segment's vertical face coefficients: face(t) couples levels
     // k0+t-1 and k0+t (face(0) below the segment, face(len) above it).  With
@@ -390,7 +407,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     if constexpr (C != kWave) {
 #pragma unroll
         for (int t = 0; t <= L; ++t)
-            fz[t] = (t <= len) ? (TZ)o.az[k0 + t] : (TZ)0;
+        {
+            const TZ fv = (TZ)o.az[min(k0 + t, o.nz)];   // faces 0..nz
+            fz[t] = (t <= len) ? fv : (TZ)0;
+        }
     }
     // area-scaled vertical coupling across face(t)
     auto face = [&](int t) -> TZ {
@@ -422,6 +442,27 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     TV rr[L];
     TZ iD[L], zp[L];
     double r2 = 0.0;
+    // Segments of up to 8 levels request a_k, d_k and r of all their levels
+    // (clamped: in bounds for every thread) with the first loads, so no load
+    // is left inside the per-level loops below, whose branches would wait
+    // for each one in turn (one memory round trip per level); longer
+    // segments load them where they are used, to keep their registers.
+    constexpr bool kPre = L <= 8 && !STORED;
+    double la[kPre ? L : 1], ldv[kPre ? L : 1];
+    if constexpr (kPre) {
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            const int kk = min(k0 + t, o.nz - 1);
+            la[t] = o.lev_a[kk];
+            ldv[t] = o.lev_d[kk];
+        }
+    }
+    auto a_at = [&](int t) -> double {
+        if constexpr (kPre) return la[t]; else return o.lev_a[k0 + t];
+    };
+    auto d_at = [&](int t) -> double {
+        if constexpr (kPre) return ldv[t]; else return o.lev_d[k0 + t];
+    };
     double zsw[MG == MG_SWEEP ? L : 1];   // MG_SWEEP: the iterate at the column's levels
     if constexpr (MG == MG_SWEEP) {
 #pragma unroll
@@ -446,6 +487,12 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         const bool needR = !kShfl || lane == kWave - 1 || ic + 1 >= o.nx;
         auto lev = [&](int k) { return (size_t)min(max(k, 0), o.nz - 1) * ks; };
         double pv[L + 2], pyp[L], pym[L], pxl[L], pxr[L];
+        double ra[kPre ? L : 1];   // r at the segment's levels (kPre: with the operands)
+        if constexpr (kPre) {
+#pragma unroll
+            for (int t = 0; t < L; ++t)
+                ra[t] = ld_s(rsrc + base + (size_t)min(k0 + t, o.nz - 1) * ks);
+        }
         if (do_ap) {
 #pragma unroll
             for (int t = 0; t < L + 2; ++t)
@@ -462,7 +509,9 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
 #pragma unroll
         for (int t = 0; t < L; ++t) {
             double v = 0.0;
-            if (t < len && ok)
+            if constexpr (kPre)
+                v = (t < len && ok) ? ra[t] : 0.0;
+            else if (t < len && ok)
                 v = ld_s(rsrc + base + (size_t)(k0 + t) * ks);
             if (do_ap && t < len) {
                 const double pc = pv[t + 1];
@@ -474,8 +523,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
                     pr = needR ? pr : pr_s;
                 }
                 const double lo = face(t), up = face(t + 1);
-                const int k = k0 + t;
-                const double Ap = stencil_row<double>(fc, fc.area * o.lev_a[k], o.lev_d[k], lo, up, pc, pl, pr,
+                const double Ap = stencil_row<double>(fc, fc.area * a_at(t), d_at(t), lo, up, pc, pl, pr,
                                                       pym[t], pyp[t], pv[t], pv[t + 2]);
                 if (ok)
                     v = v - alpha * Ap;
@@ -517,10 +565,18 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
                 cxr[t] = needR ? mg.zc[pxp + off] : 0.0;
             }
         }
+        double ra[kPre ? L : 1];   // as in the UPD_AP form
+        if constexpr (kPre) {
+#pragma unroll
+            for (int t = 0; t < L; ++t)
+                ra[t] = ld_s(rsrc + base + (size_t)min(k0 + t, o.nz - 1) * ks);
+        }
 #pragma unroll
         for (int t = 0; t < L; ++t) {
             double v = 0.0;
-            if (t < len && ok)
+            if constexpr (kPre)
+                v = (t < len && ok) ? ra[t] : 0.0;
+            else if (t < len && ok)
                 v = ld_s(rsrc + base + (size_t)(k0 + t) * ks);
             if (do_it && t < len) {
                 const double c = cv[t + 1];
@@ -531,22 +587,39 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
                     xl = needL ? xl : l_s;
                     xr = needR ? xr : r_s;
                 }
-                const int k = k0 + t;
-                const double APz = stencil_row<double>(fc, fc.area * o.lev_a[k], o.lev_d[k], face(t), face(t + 1),
+                const double APz = stencil_row<double>(fc, fc.area * a_at(t), d_at(t), face(t), face(t + 1),
                                                        c, xl, xr, cym[t], cyp[t], cv[t], cv[t + 2]);
                 v = v - APz;
             }
             rr[t] = v;
         }
     } else {
+        // kPre: all of the segment's loads first (clamped levels), then the selects
+        TV ra[kPre ? L : 1], qa[kPre ? L : 1];
+        if constexpr (kPre) {
+#pragma unroll
+            for (int t = 0; t < L; ++t)
+                ra[t] = ld_s(rsrc + base + (size_t)min(k0 + t, o.nz - 1) * ks);
+            if (UPD == UPD_Q && !first) {
+#pragma unroll
+                for (int t = 0; t < L; ++t)
+                    qa[t] = ld_s(q + base + (size_t)min(k0 + t, o.nz - 1) * ks);
+            }
+        }
 #pragma unroll
         for (int t = 0; t < L; ++t) {
             TV v = (TV)0;
             if (t < len && ok) {
-                const size_t l = base + (size_t)(k0 + t) * ks;
-                v = ld_s(rsrc + l);
-                if (UPD == UPD_Q && !first)
-                    v = v - alpha * ld_s(q + l);
+                if constexpr (kPre) {
+                    v = ra[t];
+                    if (UPD == UPD_Q && !first)
+                        v = v - alpha * qa[t];
+                } else {
+                    const size_t l = base + (size_t)(k0 + t) * ks;
+                    v = ld_s(rsrc + l);
+                    if (UPD == UPD_Q && !first)
+                        v = v - alpha * ld_s(q + l);
+                }
             }
             rr[t] = v;
             r2 += (double)v * (double)v;
@@ -561,8 +634,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
 
     // Local forward sweep: pivots from the true incoming phi, z'' with zero
     // inflow; the right-hand side rounded to TZ.
-    const size_t ncol = (size_t)o.nx * o.ny;
-    TZ phi = (s > 0 && active) ? ld_s(phib_tab + (size_t)(s * o.pst - 1) * ncol + (size_t)j * o.nx + ic) : (TZ)0;
+    TZ phi = phi_in;
     TZ zpp = 0, mu = 1;
 #pragma unroll
     for (int t = 0; t < L; ++t) {
@@ -572,7 +644,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
             if constexpr (STORED)
                 D = sdg[t] + lo * phi;
             else
-                D = thomas_pivot(diag_base(o, fc, aT, k0 + t), lo, up, phi);
+                D = thomas_pivot(diag_base_of(fc, aT, a_at(t), d_at(t)), lo, up, phi);
             const TZ inv = (TZ)1 / D;
             iD[t] = inv;
             phi = -up * inv;
@@ -587,9 +659,15 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
         sh_b[s * C + c] = mu;
     }
     __syncthreads();
+    // Both scans run over the largest segment count of the instantiation with
+    // a select, so their LDS reads do not wait behind the recurrence.
+    constexpr int kSegMax = col_bound<C, MG>() / C;
     TZ zin = 0;
-    for (int w = 0; w < s && active; ++w)
-        zin = sh_a[w * C + c] + sh_b[w * C + c] * zin;
+#pragma unroll
+    for (int w = 0; w < kSegMax - 1; ++w) {
+        const TZ nz_ = sh_a[w * C + c] + sh_b[w * C + c] * zin;
+        zin = w < s ? nz_ : zin;
+    }
 
     // Forward sweep again with the true inflow: z'_k of the serial algorithm.
     TZ prev = zin;
@@ -620,9 +698,11 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_solve(
     }
     __syncthreads();
     TZ ztop = 0;
-    if (active)
-        for (int w = P - 1; w > s; --w)
-            ztop = sh_a[w * C + c] + sh_b[w * C + c] * ztop;
+#pragma unroll
+    for (int w = kSegMax - 1; w > 0; --w) {
+        const TZ nt = sh_a[w * C + c] + sh_b[w * C + c] * ztop;
+        ztop = (w > s && w < P) ? nt : ztop;
+    }
 
     double kap = 0.0, r2mg = 0.0;
     H = 1;

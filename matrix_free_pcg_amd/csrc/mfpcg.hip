@@ -1249,8 +1249,22 @@ size_t mg_layout(const pcg_handle *h, int32_t maxit, char *base, Workspace *w, M
     return off;
 }
 
-// Multigrid forms of the column solve (64-column tiles).  DOTS is
-// instantiated on; the kernels skip the dot products when partials is null.
+// Multigrid forms of the column solve on a coarsest level of 16 or 32
+// columns per workgroup (at most 8 levels per segment; never the fused r
+// update, which only level 0 applies).
+template <int MG, int L, int C>
+void launch_mg_column_narrow(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
+                             const SolveState *st, double *partials, const MgArgs &a)
+{
+    dim3 grid(h->col_tiles), block(h->col_threads);   // <= 16 C threads: P <= 16 (mg_coarse_columns)
+    constexpr int UPD = MG == MG_SWEEP ? UPD_AP : UPD_NONE;
+    k_column_solve<L, C, UPD, true, false, double, double, MG><<<grid, block, 0, h->stream>>>(
+        rin, q, rout, z, h->op, st, 0, MG == MG_SWEEP ? nullptr : partials, nullptr, h->d_phib, a);
+}
+
+// Multigrid forms of the column solve (64-column tiles, or the narrow tiles
+// of a coarsest level).  DOTS is instantiated on; the kernels skip the dot
+// products when partials is null.
 template <int MG, int L>
 void launch_mg_column_l(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
                         const SolveState *st, int first, double *partials, int upd, const MgArgs &a)
@@ -1258,6 +1272,16 @@ void launch_mg_column_l(pcg_handle *h, const double *rin, const double *q, doubl
     dim3 grid(h->col_tiles), block(h->col_threads);
     const Op &o = h->op;
     const bool fused_q = MG == MG_FIRST && upd == UPD_Q;
+    if constexpr (L <= 8) {
+        if (h->op.C == 16) {
+            launch_mg_column_narrow<MG, L, 16>(h, rin, q, rout, z, st, partials, a);
+            return;
+        }
+        if (h->op.C == 32) {
+            launch_mg_column_narrow<MG, L, 32>(h, rin, q, rout, z, st, partials, a);
+            return;
+        }
+    }
     if constexpr (MG == MG_SWEEP) {
         if (h->col_full)
             k_column_full<L, UPD_AP, true, double, double, MG_SWEEP><<<grid, block, 0, h->stream>>>(
@@ -1584,13 +1608,13 @@ namespace {
 // One coarse level from the fine level h (factors fx, fy): its tables in
 // `tables` (table_layout bytes), the coefficients by Galerkin coarsening, the
 // Thomas multipliers.
-int create_coarse(pcg_handle *h, int fx, int fy, char *tables, pcg_handle **out)
+int create_coarse(pcg_handle *h, int fx, int fy, int C, char *tables, pcg_handle **out)
 {
     const char *who = "pcg_mg_setup";
     pcg_handle *c = new pcg_handle();
     c->device = h->device;
     c->stream = h->stream;
-    const Geometry g{h->op.L, h->op.C, h->op.Ls, h->op.Ws, h->op.L, 0};
+    const Geometry g{h->op.L, C, h->op.Ls, h->op.Ws, h->op.L, 0};
     const int nz = h->op.nz;
     init_geometry(c, h->op.nx / fx, h->op.ny / fy, nz, g);
     table_layout(c->op.nx, c->op.ny, nz, c->op.P, tables, c);
@@ -1615,6 +1639,32 @@ int create_coarse(pcg_handle *h, int fx, int fy, char *tables, pcg_handle **out)
         return rc;
     }
     *out = c;
+    return PCG_OK;
+}
+
+// Columns per workgroup of the coarsest level's column passes.  Its
+// coarse_sweeps sweeps run back to back on a small grid: with 64-column tiles
+// the 64 x 64 coarsest level of a 1024 x 1024 grid is 64 workgroups, a
+// quarter of the chip, and each sweep's time is set by the per-CU work of
+// the CUs in use.  Halve the tile width (down to 16) while the level has
+// fewer tiles than the chip has CUs.  Segments of at most 8 levels, at most
+// 16 per column (the narrow forms are instantiated and bounded for those);
+// a single column keeps 64 (its exact solve is one tile either way).
+// MFPCG_MG_COARSE_C (16, 32 or 64) overrides the choice.
+int mg_coarse_columns(pcg_handle *h, int nx, int ny, int *C)
+{
+    *C = kWave;
+    if (h->op.L > 8 || h->op.P > 16 || (size_t)nx * ny == 1)
+        return PCG_OK;
+    const int v = env_int("MFPCG_MG_COARSE_C", 0, &h->overrides, PCG_TUNE_MG_COARSE_C);
+    if (v != 0) {
+        if (v != 16 && v != 32 && v != 64)
+            return fail(h, PCG_ERR_INVALID, "pcg_mg_setup: MFPCG_MG_COARSE_C must be 16, 32 or 64");
+        *C = v;
+        return PCG_OK;
+    }
+    while (*C > 16 && (size_t)((nx + *C - 1) / *C) * ny < (size_t)kCus)
+        *C /= 2;
     return PCG_OK;
 }
 
@@ -1691,7 +1741,13 @@ int pcg_mg_setup(pcg_handle *h, const pcg_mg_params *p, void *levels, size_t lev
     char *base = (char *)levels;
     for (size_t l = 0; l < fxs.size(); ++l) {
         pcg_handle *c = nullptr;
-        if ((rc = create_coarse(cur, fxs[l], fys[l], base, &c)) != PCG_OK) {
+        int C = kWave;
+        if (l + 1 == fxs.size() &&
+            (rc = mg_coarse_columns(h, cur->op.nx / fxs[l], cur->op.ny / fys[l], &C)) != PCG_OK) {
+            mg_clear(h);
+            return rc;
+        }
+        if ((rc = create_coarse(cur, fxs[l], fys[l], C, base, &c)) != PCG_OK) {
             if (cur != h)
                 h->err = cur->err;
             mg_clear(h);
