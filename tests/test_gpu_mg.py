@@ -145,6 +145,53 @@ def test_vcycle_matches_oracle(dev, label, make, pi):
     assert np.array_equal(z, z2), label
 
 
+
+@pytest.mark.parametrize("width", ["16", "32", "64", "48"])
+def test_coarsest_tile_width(dev, monkeypatch, width):
+    """The coarsest level's tile width (MFPCG_MG_COARSE_C, read by
+    pcg_mg_setup): 16, 32 and 64 columns per workgroup give the oracle's
+    V-cycle within the V-cycle bar, the width the default rule picks (16 on
+    this 32 x 16-column coarsest level, which has fewer tiles than the chip
+    has CUs) gives the default's bits, the handle reports the override, and
+    any other width is refused."""
+    import torch
+    prob = W.general_problem(128, 64, 16, 6)
+    mg = dict(nu=1, omega=0.8, max_levels=3, coarse_sweeps=5)
+    r = W.gaussian_field(prob.nx, prob.ny, prob.nz, 304)
+
+    def cycle(env):
+        if env is None:
+            monkeypatch.delenv("MFPCG_MG_COARSE_C", raising=False)
+        else:
+            monkeypatch.setenv("MFPCG_MG_COARSE_C", env)
+        h = mf.pcg_create(prob)
+        try:
+            mf.pcg_mg_setup(h, **mg)
+            rd = to_dev(r, dev)
+            zd = torch.full_like(rd, float("nan"))
+            mf.pcg_mg_vcycle(h, rd, zd)
+            torch.cuda.synchronize()
+            return to_host(zd), mf.pcg_tuning_overrides(h)
+        finally:
+            mf.pcg_destroy(h)
+            monkeypatch.delenv("MFPCG_MG_COARSE_C", raising=False)
+
+    if width == "48":
+        with pytest.raises(mf.PcgError) as e:
+            cycle(width)
+        assert e.value.code == mf.PCG_ERR_INVALID
+        return
+    z_def, ov_def = cycle(None)
+    z, ov = cycle(width)
+    assert ov_def == 0 and ov & 0x400, (ov_def, ov)
+    zo, spread = coefficient_spread(prob, r, mg)
+    err = np.abs(z - zo).max() / np.abs(zo).max()
+    bar = max(1e-11, 8.0 * spread)
+    print(f"coarsest tiles of {width} columns: rel max err {err:.2e} (bar {bar:.2e})")
+    assert np.all(np.isfinite(z)) and err <= bar, (width, err, bar)
+    if width == "16":
+        assert np.array_equal(z, z_def)
+
 SOLVES = [
     ("general-128x64x16", lambda: W.general_problem(128, 64, 16, 6), 6),
     ("varying-96x40x12", lambda: W.config_problem(4, scale_xy=(96, 40), nz=12), 4),
