@@ -85,7 +85,8 @@ typedef struct {
  *   MFPCG_COL_L      segment length of the column solve, 4/8/16/32 (the
  *                    smallest of 8, 16, 32 that fits 1024 threads)
  *   MFPCG_COL_LF     segment length of the column passes without a stored
- *                    matrix, 1, 2 or 4 times MFPCG_COL_L, at most 32
+ *                    matrix (except pcg_solve_no_q's, which keep
+ *                    MFPCG_COL_L's), 1, 2 or 4 times MFPCG_COL_L, at most 32
  *   MFPCG_ST_L       levels per wave of the stencil passes, 1/2/4/8 (4)
  *   MFPCG_ST_W       waves per stencil workgroup, 1..16 (min(4, nz/4))
  *   MFPCG_COL_FULL   0: never use the straight-line whole-tile column kernel

@@ -753,6 +753,13 @@ __device__ __forceinline__ T ld_at(const T *base, unsigned boff)
 {
     return ld_s((const T *)((const char *)base + boff));
 }
+// The same with an ordinary (cached) load, for lines other workgroups read
+// again (the coarse correction of the multigrid sweeps).
+template <typename T>
+__device__ __forceinline__ T ldc_at(const T *base, unsigned boff)
+{
+    return *(const T *)((const char *)base + boff);
+}
 template <typename T>
 __device__ __forceinline__ void st_at(T *base, unsigned boff, T v)
 {
@@ -875,8 +882,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         const int kb = k0 > 0 ? -1 : 0;                      // level below, clamped
         const int ka = k0 + L < o.nz ? L : L - 1;            // level above, clamped
         double cc[L + 2], cy[L];
-        cc[0] = ld_at(zcc + (ptrdiff_t)kb * (ptrdiff_t)ksc, pl);
-        cc[L + 1] = ld_at(zcc + (size_t)ka * ksc, pl);
+        cc[0] = ldc_at(zcc + (ptrdiff_t)kb * (ptrdiff_t)ksc, pl);
+        cc[L + 1] = ldc_at(zcc + (size_t)ka * ksc, pl);
         // the parents of the tile's two outside columns at the segment's
         // levels in one load: lane e < L takes the left one's at level k0 + e,
         // lane L + e the right one's (handed to lanes 0 and 63 by readlane)
@@ -887,13 +894,13 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
             const int io = lane < L ? (t0 == 0 ? nx - 1 : t0 - 1) : (t0 + kWave == nx ? 0 : t0 + kWave);
             const int e = lane < L ? lane : lane - L;
             if (lane < 2 * L)
-                ev = ld_at(zcc + (size_t)e * ksc, (unsigned)(io / mg.fx) * 8u);
+                ev = ldc_at(zcc + (size_t)e * ksc, (unsigned)(io / mg.fx) * 8u);
         }
 #pragma unroll
         for (int t = 0; t < L; ++t) {
             rr[t] = ld_at(rsrc + row0 + (size_t)t * nx, cv);
-            cc[t + 1] = ld_at(zcc + (size_t)t * ksc, pl);
-            cy[t] = (om || op) ? ld_at(zyo + (size_t)t * ksc, pl) : 0.0;
+            cc[t + 1] = ldc_at(zcc + (size_t)t * ksc, pl);
+            cy[t] = (om || op) ? ldc_at(zyo + (size_t)t * ksc, pl) : 0.0;
         }
         const Faces fc = column_faces(o, i, j);
 #pragma unroll
@@ -906,7 +913,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
             const double ym = om ? cy[t] : c;
             double yp = c;
             if (op)   // wave-uniform; both rows differ only when fy = 1
-                yp = om ? ld_at(zy2 + (size_t)t * ksc, pl) : cy[t];
+                yp = om ? ldc_at(zy2 + (size_t)t * ksc, pl) : cy[t];
             const double APz = stencil_row<double>(fc, fc.area * o.lev_a[k0 + t], o.lev_d[k0 + t], fc.area * az[t],
                                                    fc.area * az[t + 1], c, xl, xr, ym, yp, cc[t], cc[t + 2]);
             rr[t] = rr[t] - APz;
@@ -1008,8 +1015,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
                 fv = fb[t];
             } else {
                 zq = ld_at(q + row0 + (size_t)t * nx, cv) +
-                     ld_at(mg.zc + (size_t)mg.ncx * ((size_t)o.nz * (size_t)(j / mg.fy) + (size_t)(k0 + t)),
-                           (unsigned)(i / mg.fx) * 8u);
+                     ldc_at(mg.zc + (size_t)mg.ncx * ((size_t)o.nz * (size_t)(j / mg.fy) + (size_t)(k0 + t)),
+                            (unsigned)(i / mg.fx) * 8u);
                 fv = partials ? ld_at(mg.f + row0 + (size_t)t * nx, cv) : 0.0;
             }
             zv = zq + mg.omega * zv;

@@ -179,7 +179,8 @@ bool choose_geometry(int nz, Geometry *g, std::string *why)
     g->L = l;
     // Segments of 16 levels measured faster than 8 for the fused and the
     // stand-alone column passes at nz = 32..128 (their threads keep more loads
-    // in flight; the multigrid sweeps need 8, so the table stays at L).
+    // in flight; the multigrid sweeps and the recomputed-product column pass
+    // need 8, so the table stays at L).
     // Whole segments are preferred: nz a multiple of 8 but not 16 keeps 8.
     int lf = env_int("MFPCG_COL_LF", 0, ov, PCG_TUNE_COL_LF);
     if (lf == 0) {
@@ -389,7 +390,10 @@ void launch_column_c(pcg_handle *h, const TV *rin, const TV *q, TV *rout, TZ *z,
                      const SolveState *st, int first, double *partials, int upd, bool dots,
                      const double *tri)
 {
-    const ColGeo g = col_geo(h, tri != nullptr);
+    // the recomputed-product form keeps the table's segments: with 16 levels
+    // its operand arrays spill (1.65 ms per pass at 1024 x 1024 x 128, 1.18
+    // with 8)
+    const ColGeo g = col_geo(h, tri != nullptr || upd == UPD_AP);
     switch (g.o.L) {
     case 4: launch_column_lc<4, C>(h, g, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
     case 8: launch_column_lc<8, C>(h, g, rin, q, rout, z, st, first, partials, upd, dots, tri); break;
