@@ -393,6 +393,68 @@ def test_column_segment_lengths_agree(dev, monkeypatch, label, make, short, long
         assert np.linalg.norm(xa - xc) <= 1e-11 * np.linalg.norm(xa), (label, name)
 
 
+
+# (columns per column-pass workgroup, segment length): the generic column
+# kernel at every shape its tuning variables allow on these grids
+COLUMN_SHAPES = [(32, 8), (64, 4), (32, 4), (32, 16)]
+COLUMN_SHAPE_GRIDS = [
+    ("cfg4-70x45x40", lambda: W.config_problem(4, scale_xy=(70, 45), nz=40)),
+    ("cfg4-128x24x64", lambda: W.config_problem(4, scale_xy=(128, 24), nz=64)),
+    ("cfg4-33x5x7", lambda: W.config_problem(4, scale_xy=(33, 5), nz=7)),
+]
+
+
+@pytest.mark.parametrize("shape", COLUMN_SHAPES, ids=[f"C{c}-L{l}" for c, l in COLUMN_SHAPES])
+@pytest.mark.parametrize("label,make", COLUMN_SHAPE_GRIDS, ids=[g[0] for g in COLUMN_SHAPE_GRIDS])
+def test_column_tile_shapes(dev, monkeypatch, label, make, shape):
+    """MFPCG_COL_C (32 or 64 columns per workgroup) and MFPCG_COL_L (4, 8,
+    16 or 32 levels per segment), read at pcg_create, choose the generic
+    column kernel's shape (every pass on 32-column tiles, and ragged ones,
+    runs it): precond matches the oracle within the column-solve bound, and
+    5 steps of each solve agree with the default shape's to rounding."""
+    import torch
+    cols, seg = shape
+    prob = make()
+    r = W.gaussian_field(prob.nx, prob.ny, prob.nz, 41)
+    b = W.uniform_field(prob.nx, prob.ny, prob.nz, 42)
+    ref = oracle.precond(prob, r)
+
+    def run(env):
+        for k in ("MFPCG_COL_C", "MFPCG_COL_L", "MFPCG_COL_LF"):
+            monkeypatch.delenv(k, raising=False)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
+        h = mf.pcg_create(prob)
+        try:
+            ov = mf.pcg_tuning_overrides(h)
+            rd = to_dev(r, dev)
+            zd = torch.full_like(rd, float("nan"))
+            mf.pcg_precond(h, rd, zd)
+            out = {"z": to_host(zd), "ov": ov}
+            for name, fn in SOLVERS.items():
+                bd = to_dev(b, dev)
+                xs = torch.zeros_like(bd)
+                res = fn(h, bd, xs, 0.0, 5)
+                out[name] = (to_host(xs), res["hist"])
+            torch.cuda.synchronize()
+            return out
+        finally:
+            mf.pcg_destroy(h)
+            for k in ("MFPCG_COL_C", "MFPCG_COL_L", "MFPCG_COL_LF"):
+                monkeypatch.delenv(k, raising=False)
+
+    d = run({})
+    a = run({"MFPCG_COL_C": str(cols), "MFPCG_COL_L": str(seg), "MFPCG_COL_LF": str(seg)})
+    assert d["ov"] == 0 and a["ov"] & 0x7 == 0x7, (d["ov"], a["ov"])
+    err = np.abs(a["z"] - ref).max()
+    print(f"{label} C={cols} L={seg}: precond max err {err:.2e} (bound {precond_tol(prob, ref):.2e})")
+    assert err <= precond_tol(prob, ref), (label, shape, err)
+    for name in SOLVERS:
+        xa, ha = a[name]
+        xd, hd = d[name]
+        assert np.allclose(ha, hd, rtol=1e-11, atol=0), (label, shape, name)
+        assert np.linalg.norm(xa - xd) <= 1e-11 * np.linalg.norm(xd), (label, shape, name)
+
 # grids of whole tiles: ny a multiple of 8 (row tiles of 4 or 8 rows in every
 # stencil pass), ny = 6 (in the operator-only passes only), a general operator
 ROW_TILE_CASES = [
