@@ -600,7 +600,7 @@ __global__ __launch_bounds__((col_bound<C, MG>())) void k_column_solve(
 #pragma unroll
             for (int t = 0; t < L; ++t)
                 ra[t] = ld_s(rsrc + base + (size_t)min(k0 + t, o.nz - 1) * ks);
-            if (UPD == UPD_Q && !first) {
+            if constexpr (UPD == UPD_Q) {   // on the first step too (not used then): no branch
 #pragma unroll
                 for (int t = 0; t < L; ++t)
                     qa[t] = ld_s(q + base + (size_t)min(k0 + t, o.nz - 1) * ks);
@@ -815,7 +815,22 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     TV rr[L];
     double r2 = 0.0;
     double zsw[MG == MG_SWEEP ? L : 1];   // MG_SWEEP: the iterate at the column's levels
-    if (UPD == UPD_Q && !first) {
+    if constexpr (UPD == UPD_Q && L == 16) {
+        // q is requested on the first step too (its buffer exists; the
+        // values are not used then): a branch on `first` here would split
+        // the load phase, and the compiler then waits for all of r before
+        // requesting q.  (16-level segments: at 8 levels the extra
+        // registers would cost a second workgroup per CU.)
+        TV qv[L];
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+            rr[t] = ld_at(rsrc + row0 + (size_t)t * nx, cv);
+            qv[t] = ld_at(q + row0 + (size_t)t * nx, cv);
+        }
+#pragma unroll
+        for (int t = 0; t < L; ++t)
+            rr[t] = first ? rr[t] : rr[t] - alpha * qv[t];
+    } else if (UPD == UPD_Q && !first) {
         TV qv[L];
 #pragma unroll
         for (int t = 0; t < L; ++t) {
