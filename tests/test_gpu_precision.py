@@ -150,6 +150,17 @@ def test_precond_f32_matches_oracle(dev, label, make):
     fg = np.abs(z - z64).max()
     fo = np.abs(zo - z64).max()
     assert fg <= 4 * fo + 16 * EPS32 * np.abs(z64).max(), (label, fg, fo)
+    # the two binary32 column solves against each other, per application on
+    # the same r: both sum the pivots' diagonal in the same order; they
+    # differ in the segment scans (the GPU's elimination is split into
+    # segments) and in fused multiply-adds
+    # (measured: 0.07-0.39 of the binary32 rounding |z_orc32 - z_orc64| on the
+    # variable-coefficient grids, 1.16 on the constant one, where both are at
+    # the rounding floor); a systematic difference, such as pivots summed in
+    # another order, exceeds it
+    dz = np.abs(z - zo).max()
+    print(f"{label}: |z_gpu32 - z_orc32| {dz:.2e}, |z_orc32 - z_orc64| {fo:.2e} (ratio {dz / max(fo, 1e-300):.2f})")
+    assert dz <= 2 * fo + 4 * EPS32 * np.abs(z64).max(), (label, dz, fo)
 
 
 SOLVES = [
