@@ -150,6 +150,22 @@ def test_handle_bytes_covers_the_tables(lib):
     assert lib.pcg_handle_bytes(None) == 0
 
 
+
+def test_tuning_variables_agree():
+    """The tuning variables are the same set in the header (a PCG_TUNE_*
+    bit and a line in its list each), in the binding's name table and in
+    the environment variables the library reads, each with the bit it
+    reports."""
+    header = open(HEADER).read()
+    bits = {int(v, 16): "MFPCG_" + n for n, v in re.findall(r"#define PCG_TUNE_(\w+) (0x[0-9A-Fa-f]+)", header)}
+    assert bits and bits == _abi.PCG_TUNE_NAMES
+    src = re.sub(r"//[^\n]*", "", open(os.path.join(hipbuild.CSRC, "mfpcg.hip")).read())
+    read = dict(re.findall(r'env_int\("(MFPCG_\w+)",[^;]*?PCG_TUNE_(\w+)\)', src, flags=re.S))
+    for bit, name in bits.items():
+        assert name in header.split("#define PCG_TUNE_")[0], name   # listed in the header's comment
+        assert read.get(name) == name[len("MFPCG_"):], (name, read.get(name))
+    assert set(read) == set(bits.values())
+
 def test_no_device_allocation_in_the_library():
     """The library's source makes no device allocation: no hipMalloc /
     hipFree / hipMallocAsync / hipExtMalloc call in the host code (the pinned
