@@ -368,12 +368,15 @@ def pin_k8_invariants(orc):
     m = 8
     res = orc.pcg(prob, b, tol=0.0, maxit=m, ntrace=m)
     R, Z, P = res["trace_r"], res["trace_z"], res["trace_p"]
+    assert all(np.isfinite(v).all() for v in (R, Z, P)), "K8 non-finite iterates"
     AP = [orc.apply_A(prob, P[t]) for t in range(m)]
     for a in range(m):
         for c in range(m):
             if a == c:
                 continue
-            rz = abs(np.sum(R[a] * Z[c])) / (np.linalg.norm(R[a]) * np.linalg.norm(Z[c]))
+            den = np.linalg.norm(R[a]) * np.linalg.norm(Z[c])
+            assert den > 0, ("K8 zero residual or preconditioned residual", a, c)
+            rz = abs(np.sum(R[a] * Z[c])) / den
             assert rz <= 1e-10, ("K8 r_i . z_j", a, c, rz)
             pap = abs(np.sum(P[a] * AP[c])) / math.sqrt(np.sum(P[a] * AP[a]) * np.sum(P[c] * AP[c]))
             assert pap <= 1e-10, ("K8 p_i A p_j", a, c, pap)
