@@ -135,35 +135,46 @@ def standard_bytes(kind, iters, n):
     return tot * n
 
 
-def mg_pass_bytes(level_points, iters, coarse_sweeps=0, two_pass_sweeps=False):
-    """Total algorithmic bytes and count of the timed V-cycles (k = 0..K)."""
+def mg_pass_bytes(level_points, iters, coarse_sweeps=0, two_pass_sweeps=False, period=1):
+    """Total algorithmic bytes and count of the timed V-cycles (k = 0..K;
+    with a profiling period P > 1 only those with k mod P < 2)."""
     tot = cnt = 0
     for K in iters:
         for k in range(K + 1):
+            if period > 1 and k % period >= 2:
+                continue
             tot += mg_cycle_bytes(level_points, k, coarse_sweeps=coarse_sweeps, two_pass_sweeps=two_pass_sweeps)
             cnt += 1
     return tot, cnt
 
 
-def timed_steps(kernel, iters):
+def timed_steps(kernel, iters, period=1):
     """Step index k of every timed launch of a pass, over solves of `iters`
     steps each: the preconditioner pass runs at k = 0..K, the stencil pass at
     k = 0..K-1 (its launch at k = K only applies the pending x update and is
-    not timed)."""
+    not timed); with a profiling period P > 1 the library times only the
+    steps with k mod P < 2."""
     for K in iters:
-        yield from (range(K + 1) if kernel == "fused_prec" else range(K))
+        ks = range(K + 1) if kernel == "fused_prec" else range(K)
+        yield from (k for k in ks if period <= 1 or k % period < 2)
 
 
-def pass_bytes(variant, kernel, iters, n):
+def pass_bytes(variant, kernel, iters, n, period=1):
     """Total algorithmic bytes and launch count of the timed launches of one
-    pass over solves that took `iters` steps each."""
+    pass over solves that took `iters` steps each (period: as timed_steps)."""
     f = BYTES_BY_VARIANT[variant][0]
     tot = cnt = 0
-    for k in timed_steps(kernel, iters):
+    for k in timed_steps(kernel, iters, period):
         tot += f(kernel, k) * n
         cnt += 1
     return tot, cnt
 
+
+# The solve loops' passes are timed with HIP events on two consecutive steps
+# in every PROFILE_PERIOD (both stencil-pass forms): each recorded event
+# delays the next kernel by about 5.6 us, which bracketing every pass would
+# add to the timed solves (21 ms per solve at 1024 x 1024 x 128).
+PROFILE_PERIOD = 8
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fused_passes_varying-1024x1024x128.json")
 KERNEL_SOURCE = os.path.join(ROOT, "matrix_free_pcg_amd", "csrc", "kernels.hpp")
@@ -666,7 +677,7 @@ def main():
         log(f"[bench] warmup {s}: iters={res['iters']} status={res['status']}")
 
     mf.pcg_profile_reset(h)
-    mf.pcg_profile_enable(h, True)
+    mf.pcg_profile_enable(h, PROFILE_PERIOD)
     iters = []
     solve_s = []
     torch.cuda.synchronize()
@@ -693,7 +704,7 @@ def main():
             avg = ms / cnt
             ent = {"launches": cnt, "avg_ms": avg, "total_ms": ms}
             if name == "mg_vcycle":
-                tot, nl = mg_pass_bytes(level_points, iters, mg_cs, mg_two)
+                tot, nl = mg_pass_bytes(level_points, iters, mg_cs, mg_two, PROFILE_PERIOD)
                 if nl != cnt:
                     raise SystemExit(f"{name}: {cnt} timed cycles, expected {nl}")
                 ent["bytes_per_launch"] = tot / nl
@@ -705,7 +716,7 @@ def main():
                 ent["GBps"] = tot / (ms * 1e-3) / 1e9
                 ent["note"] = "algorithmic bytes of all timed launches / their total time"
             elif has_bytes and name in ("fused_prec", "fused_spmv"):
-                tot, nl = pass_bytes(args.variant, name, iters, n)
+                tot, nl = pass_bytes(args.variant, name, iters, n, PROFILE_PERIOD)
                 if nl != cnt:
                     raise SystemExit(f"{name}: {cnt} timed launches, expected {nl}")
                 ent["bytes_per_launch"] = tot / nl          # average over the timed launches

@@ -436,9 +436,14 @@ int pcg_solve_csr(pcg_handle *h, const int64_t *row_ptr_dev, const int32_t *col_
                   double *hist_host, int32_t *hist_len_out, double *final_rel_res);
 
 /* Per-kernel timing with HIP events on the handle's stream (off by default).
- * While enabled, every launch of the kernels below is bracketed by events;
+ * While enabled, launches of the kernels below are bracketed by events;
  * pcg_profile_read returns the accumulated milliseconds and launch count of
- * one kernel id since the last pcg_profile_reset. */
+ * one kernel id since the last pcg_profile_reset.  enable = 0 turns timing
+ * off, 1 times every launch, P >= 2 times the solve loops' passes
+ * (PCG_KID_FUSED_PREC, PCG_KID_FUSED_SPMV, PCG_KID_MG_VCYCLE) only at the
+ * steps k with k mod P < 2 (each recorded event delays the next kernel by a
+ * few microseconds) and every other launch as with 1.  Negative:
+ * PCG_ERR_INVALID. */
 #define PCG_KID_FUSED_PREC 0   /* interleaved preconditioner pass          */
 #define PCG_KID_FUSED_SPMV 1   /* interleaved stencil pass                 */
 #define PCG_KID_APPLY_A 2      /* stand-alone y = A x (and standard q = A p) */

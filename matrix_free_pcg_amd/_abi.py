@@ -490,8 +490,10 @@ def pcg_solve_mg(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> dic
                   need=pcg_mg_workspace_bytes(h, maxit))
 
 
-def pcg_profile_enable(h: Handle, enable: bool = True) -> None:
-    _check(h.ptr, load().pcg_profile_enable(h.ptr, 1 if enable else 0))
+def pcg_profile_enable(h: Handle, enable=True) -> None:
+    """False/0: off; True/1: every launch; an int P >= 2: the solve loops'
+    passes at the steps k with k mod P < 2 only."""
+    _check(h.ptr, load().pcg_profile_enable(h.ptr, int(enable)))
 
 
 def pcg_profile_reset(h: Handle) -> None:

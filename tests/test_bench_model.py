@@ -77,3 +77,23 @@ def test_mg_cycle_bytes_with_coarse_sweeps():
     base = bench.mg_cycle_bytes(pts, 1)              # coarsest treated as one exact solve
     assert bench.mg_cycle_bytes(pts, 1, coarse_sweeps=64) - base == 24 * 63 * pts[-1]
     assert bench.mg_cycle_bytes(pts, 1, coarse_sweeps=64, two_pass_sweeps=True) - base == 48 * 63 * pts[-1]
+
+
+def test_sampled_profiling_steps():
+    """With a profiling period P the library times the solve loops' passes at
+    the steps k with k mod P < 2: two consecutive steps, so both stencil-pass
+    forms, in every P; the byte accounting counts the same launches."""
+    ks = list(bench.timed_steps("fused_prec", [10], period=4))
+    assert ks == [0, 1, 4, 5, 8, 9]
+    ks = list(bench.timed_steps("fused_spmv", [10, 7], period=4))
+    assert ks == [0, 1, 4, 5, 8, 9] + [0, 1, 4, 5]
+    assert list(bench.timed_steps("fused_prec", [10], period=1)) == list(range(11))
+    n = 1 << 20
+    tot8, cnt8 = bench.pass_bytes("interleaved", "fused_spmv", [927], n, period=8)
+    tot1, cnt1 = bench.pass_bytes("interleaved", "fused_spmv", [927], n)
+    assert cnt8 == len([k for k in range(927) if k % 8 < 2])
+    # the sample holds odd and even steps alike, so its mean is the whole solve's
+    assert abs(tot8 / cnt8 - tot1 / cnt1) <= 0.01 * tot1 / cnt1
+    pts = [8, 4, 2]
+    t, c = bench.mg_pass_bytes(pts, [9], period=4)
+    assert c == len([k for k in range(10) if k % 4 < 2])

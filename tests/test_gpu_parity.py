@@ -295,6 +295,15 @@ def test_profile_counts_launches(dev):
         assert ms_p > 0 and ms_s > 0 and math.isfinite(ms_p + ms_s)
         mf.pcg_profile_reset(h)
         assert mf.pcg_profile_read(h, mf.PCG_KID_FUSED_PREC) == (0.0, 0)
+        # sampled: the passes of steps k with k mod 4 < 2 only (k = 0, 1, 4, 5)
+        mf.pcg_profile_enable(h, 4)
+        xd.zero_()
+        res = mf.pcg_solve(h, bd, xd, 0.0, 7)
+        _, n_p = mf.pcg_profile_read(h, mf.PCG_KID_FUSED_PREC)
+        _, n_s = mf.pcg_profile_read(h, mf.PCG_KID_FUSED_SPMV)
+        assert (n_p, n_s) == (4, 4), (n_p, n_s)
+        with pytest.raises(mf.PcgError):
+            mf.pcg_profile_enable(h, -1)
     finally:
         mf.pcg_destroy(h)
 
