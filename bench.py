@@ -197,7 +197,7 @@ def kernel_source_digest(path=None) -> str:
     return hashlib.sha256(src.encode()).hexdigest()
 
 
-def measured_traffic(kernel: str, workload: str, variant: str, iters):
+def measured_traffic(kernel: str, workload: str, variant: str, iters, period=1):
     """HBM bytes per launch of a pass from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE per dispatch, calibrated on a plain copy,
     per step class), averaged over the same launches as the timing; None when
@@ -214,7 +214,7 @@ def measured_traffic(kernel: str, workload: str, variant: str, iters):
     if not classes:
         return None
     tot = cnt = 0
-    for k in timed_steps(kernel, iters):
+    for k in timed_steps(kernel, iters, period):
         c = classes.get(step_class(variant, kernel, k))
         if c is None:
             return None
@@ -751,7 +751,7 @@ def main():
                     "kernel": dom, "avg_launch_ms": round(kern[dom]["avg_ms"], 4)}
     elif dom is not None:
         ach = kern[dom]["GBps"]
-        traffic = measured_traffic(dom, w.name, args.variant, iters)
+        traffic = measured_traffic(dom, w.name, args.variant, iters, PROFILE_PERIOD)
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4),
                     "traffic": traffic,
