@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <chrono>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -250,6 +251,42 @@ const double *fold_partials(pcg_handle *h, const Workspace &w, int n, int *n_out
     k_sum_stage<<<dim3(nb), dim3(kRedThreads), 0, h->stream>>>(w.partials, n, kStagePer, w.stage);
     *n_out = nb;
     return w.stage;
+}
+
+// Waits until a reduce kernel has published step k's stop decision in the
+// pinned status block.  The kernel writes the block with system-scope stores,
+// each finished before the next, the step index last; so once the host reads
+// an index >= k, the decision beside it is that step's.  The caller must know
+// that no earlier solve can still publish (the first step of a solve waits on
+// an event instead, which drains everything queued before it).  The host
+// spins; after 50 ms without the index, and every 50 ms after that, it asks
+// the stream whether it failed, or drained without publishing (an error).
+// Recording an event per step instead would hold the next kernel back by
+// about 5.6 us (the runtime's marker packet).
+int wait_published(pcg_handle *h, int k, const char *who)
+{
+    volatile HostStatus *vs = (volatile HostStatus *)h->h_status;
+    if (vs->k >= k)
+        return PCG_OK;
+    const auto t0 = std::chrono::steady_clock::now();
+    auto next = std::chrono::milliseconds(50);
+    for (;;) {
+        for (int i = 0; i < 4096; ++i) {
+            if (vs->k >= k)
+                return PCG_OK;
+            __builtin_ia32_pause();
+        }
+        if (std::chrono::steady_clock::now() - t0 < next)
+            continue;
+        const hipError_t e = hipStreamQuery(h->stream);
+        if (vs->k >= k)
+            return PCG_OK;
+        if (e == hipSuccess)
+            return fail(h, PCG_ERR_HIP, "%s: the stream drained without publishing step %d", who, k);
+        if (e != hipErrorNotReady)
+            return fail(h, PCG_ERR_HIP, "%s: step %d: %s", who, k, hipGetErrorString(e));
+        next += std::chrono::milliseconds(50);
+    }
 }
 
 // ---- per-kernel event timing ------------------------------------------------
@@ -1500,7 +1537,8 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
         // a4: ||r_k||, stop test, beta
         red = fold_partials(h, w, h->col_tiles, &nred);
         k_reduce_rz<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, w.hist, k, maxit, tol, hs);
-        (void)hipEventRecord(ev, h->stream);
+        if (k == 0)
+            (void)hipEventRecord(ev, h->stream);
         // a5: x += alpha p; p = z + beta p; q = A z + beta q (or A p_new on the
         //     fly); partial <p,q>  (Algorithm 2); only x += alpha p once the
         //     stop test has passed (a7)
@@ -1524,9 +1562,15 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return fail(h, PCG_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
-        e = hipEventSynchronize(ev);
-        if (e != hipSuccess)
-            return fail(h, PCG_ERR_HIP, "%s: hipEventSynchronize: %s", who, hipGetErrorString(e));
+        if (k == 0) {
+            e = hipEventSynchronize(ev);
+            if (e != hipSuccess)
+                return fail(h, PCG_ERR_HIP, "%s: hipEventSynchronize: %s", who, hipGetErrorString(e));
+        } else {
+            const int rc = wait_published(h, k, who);
+            if (rc != PCG_OK)
+                return rc;
+        }
         last = k;
         if (((volatile HostStatus *)h->h_status)->done)
             break;
@@ -1933,7 +1977,6 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
         }
         red = fold_partials(h, w, h->pt_tiles, &nred);
         k_reduce_rr<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, w.hist, k, maxit, tol, hs);
-        (void)hipEventRecord(ev, h->stream);
         {   // z = M^{-1} r ; kappa = <r,z>
             Timed t(h, PCG_KID_PRECOND, k);
             column<double, double>(h, w.r, nullptr, nullptr, w.z, w.state, 1, w.partials, UPD_NONE, true, tri);
@@ -1945,9 +1988,12 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
             update_p(h, w.p, w.z, w.state, 0);
         }
         e = hipGetLastError();
-        if (e == hipSuccess)
-            e = hipEventSynchronize(ev);
-        done = (e == hipSuccess) && ((volatile HostStatus *)h->h_status)->done;
+        if (e != hipSuccess)
+            break;
+        const int rc = wait_published(h, k, who);
+        if (rc != PCG_OK)
+            return rc;
+        done = ((volatile HostStatus *)h->h_status)->done;
     }
     if (e != hipSuccess)
         return fail(h, PCG_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
