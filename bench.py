@@ -34,26 +34,28 @@ METRIC = "PCG iterations/s + achieved HBM GB/s (% roofline), fp64 1024×1024×12
 # Algorithmic bytes per grid point of each launch of a pass (float64 = 8 B;
 # each vector read or written once per pass; stencil halos and coefficients
 # not counted), as a function of the step k the launch belongs to.
-#   interleaved: Algorithms 2-3, x updated every second step.
+#   interleaved: Algorithms 2-3, x updated every fourth step.
 #     fused_prec  k = 0: read r, write z (16); k >= 1: read r, q, write r, z (32)
-#     fused_spmv  k = 0: read z, write p, q (24); odd k: read z, p, q, write p, q
-#                 (40); even k >= 2: also read x and the previous p, write x (64)
-#     -> 84 B per point per step in steady state
+#     fused_spmv  k = 0: read z, write p, q (24); k mod 4 != 0: read z, p, q,
+#                 write p, q (40); k mod 4 == 0, k >= 4: also read x and the
+#                 three older directions, write x (80)
+#     -> 82 B per point per step in steady state
 #   interleaved_no_q: q never stored.
 #     fused_prec  k = 0: 16; k >= 1: read r, p, write r, z (32)
 #     fused_spmv  k = 0: read z, write p (16); k >= 1: read x, p, z, write x, p (40)
 #     -> 72 B per point per step
 #   f32: the interleaved loop with every vector in binary32 (4 B): half of
-#     the interleaved figures -> 42 B per point per step
+#     the interleaved figures -> 41 B per point per step
 #   mixed: binary64 vectors, z in binary32:
 #     fused_prec  k = 0: read r, write z (12); k >= 1: read r, q, write r, z (28)
-#     fused_spmv  k = 0: read z, write p, q (20); odd k: read z, p, q, write p, q
-#                 (36); even k: also read x and the older p, write x (60)
-#     -> 76 B per point per step
+#     fused_spmv  k = 0: read z, write p, q (20); k mod 4 != 0: read z, p, q,
+#                 write p, q (36); k mod 4 == 0: also read x and the three
+#                 older directions, write x (76)
+#     -> 74 B per point per step
 def _bytes_interleaved(kernel, k):
     if kernel == "fused_prec":
         return 16 if k == 0 else 32
-    return 24 if k == 0 else (40 if k % 2 else 64)
+    return 24 if k == 0 else (80 if k % 4 == 0 else 40)
 
 
 def _bytes_no_q(kernel, k):
@@ -69,11 +71,11 @@ def _bytes_f32(kernel, k):
 def _bytes_mixed(kernel, k):
     if kernel == "fused_prec":
         return 12 if k == 0 else 28
-    return 20 if k == 0 else (36 if k % 2 else 60)
+    return 20 if k == 0 else (76 if k % 4 == 0 else 36)
 
 
-BYTES_BY_VARIANT = {"interleaved": (_bytes_interleaved, 84), "interleaved_no_q": (_bytes_no_q, 72),
-                    "f32": (_bytes_f32, 42), "mixed": (_bytes_mixed, 76), "mg": (_bytes_interleaved, None)}
+BYTES_BY_VARIANT = {"interleaved": (_bytes_interleaved, 82), "interleaved_no_q": (_bytes_no_q, 72),
+                    "f32": (_bytes_f32, 41), "mixed": (_bytes_mixed, 74), "mg": (_bytes_interleaved, None)}
 
 
 # mg: the interleaved loop with one multigrid V-cycle as the preconditioner
@@ -108,11 +110,12 @@ def mg_cycle_bytes(level_points, k, nu=1, coarse_sweeps=0, two_pass_sweeps=False
 
 def step_class(variant, kernel, k):
     """Launches of a pass with the same work per point: the first step, and
-    (interleaved stencil pass) odd / even steps, else the rest."""
+    (interleaved stencil pass) the steps that defer the x update ("nox") and
+    every fourth one, which applies four ("x4"), else the rest."""
     if k == 0:
         return "first"
     if variant in ("interleaved", "f32", "mixed") and kernel == "fused_spmv":
-        return "odd" if k % 2 else "even"
+        return "x4" if k % 4 == 0 else "nox"
     return "rest"
 
 
@@ -137,11 +140,11 @@ def standard_bytes(kind, iters, n):
 
 def mg_pass_bytes(level_points, iters, coarse_sweeps=0, two_pass_sweeps=False, period=1):
     """Total algorithmic bytes and count of the timed V-cycles (k = 0..K;
-    with a profiling period P > 1 only those with k mod P < 2)."""
+    with a profiling period P > 1 only those with k mod P < PROFILE_WINDOW)."""
     tot = cnt = 0
     for K in iters:
         for k in range(K + 1):
-            if period > 1 and k % period >= 2:
+            if period > 1 and k % period >= PROFILE_WINDOW:
                 continue
             tot += mg_cycle_bytes(level_points, k, coarse_sweeps=coarse_sweeps, two_pass_sweeps=two_pass_sweeps)
             cnt += 1
@@ -151,12 +154,12 @@ def mg_pass_bytes(level_points, iters, coarse_sweeps=0, two_pass_sweeps=False, p
 def timed_steps(kernel, iters, period=1):
     """Step index k of every timed launch of a pass, over solves of `iters`
     steps each: the preconditioner pass runs at k = 0..K, the stencil pass at
-    k = 0..K-1 (its launch at k = K only applies the pending x update and is
-    not timed); with a profiling period P > 1 the library times only the
-    steps with k mod P < 2."""
+    k = 0..K-1 (its launch at k = K, made before the stop test was read,
+    returns at once and is not timed); with a profiling period P > 1 the
+    library times only the steps with k mod P < PROFILE_WINDOW."""
     for K in iters:
         ks = range(K + 1) if kernel == "fused_prec" else range(K)
-        yield from (k for k in ks if period <= 1 or k % period < 2)
+        yield from (k for k in ks if period <= 1 or k % period < PROFILE_WINDOW)
 
 
 def pass_bytes(variant, kernel, iters, n, period=1):
@@ -170,11 +173,13 @@ def pass_bytes(variant, kernel, iters, n, period=1):
     return tot, cnt
 
 
-# The solve loops' passes are timed with HIP events on two consecutive steps
-# in every PROFILE_PERIOD (both stencil-pass forms): each recorded event
-# delays the next kernel by about 5.6 us, which bracketing every pass would
-# add to the timed solves (21 ms per solve at 1024 x 1024 x 128).
-PROFILE_PERIOD = 8
+# The solve loops' passes are timed with HIP events on PROFILE_WINDOW
+# consecutive steps in every PROFILE_PERIOD (the stencil pass's two forms as
+# often as in a whole solve): each recorded event delays the next kernel by
+# about 5.6 us, which bracketing every pass would add to the timed solves
+# (21 ms per solve at 1024 x 1024 x 128).  The window is the library's.
+PROFILE_WINDOW = 4
+PROFILE_PERIOD = 16
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_fused_passes_varying-1024x1024x128.json")
 KERNEL_SOURCE = os.path.join(ROOT, "matrix_free_pcg_amd", "csrc", "kernels.hpp")
@@ -335,19 +340,19 @@ def counter_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, steps,
             short = _short_kernel(k)
             if short.startswith("k_column_full<16, 1, true, double, double, 0>"):
                 prec.append((short, v))
-            elif short.startswith("k_stencil<") and short.split(",")[1].strip() in ("0", "7", "8"):
+            elif short.startswith("k_stencil<") and short.split(",")[1].strip() in ("0", "7", "9"):
                 spmv.append((short, v))
         if len(prec) != steps + 1 or len(spmv) != steps + 1:
             raise SystemExit(f"expected {steps + 1} launches of each pass, found {len(prec)} and {len(spmv)}")
-        spmv = spmv[:-1]   # the last stencil launch only applies the pending x update
-        out = {"fused_prec": {"first": [prec[0]], "rest": prec[1:]}, "fused_spmv": {"first": [], "odd": [], "even": []}}
+        spmv = spmv[:-1]   # the last stencil launch returns at once (the stop test had passed)
+        out = {"fused_prec": {"first": [prec[0]], "rest": prec[1:]}, "fused_spmv": {"first": [], "nox": [], "x4": []}}
         for kk, e in enumerate(spmv):
-            out["fused_spmv"]["first" if kk == 0 else ("odd" if kk % 2 else "even")].append(e)
+            out["fused_spmv"][step_class("interleaved", "fused_spmv", kk)].append(e)
         return out
 
     cf_, cw_ = classify(fetch), classify(write)
     alg = {("fused_prec", "first"): 16, ("fused_prec", "rest"): 32, ("fused_spmv", "first"): 24,
-           ("fused_spmv", "odd"): 40, ("fused_spmv", "even"): 64}
+           ("fused_spmv", "nox"): 40, ("fused_spmv", "x4"): 80}
     passes = {}
     lines = []
     for kern in ("fused_prec", "fused_spmv"):
@@ -384,8 +389,8 @@ def counter_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, steps,
                 f"scaled by {fetch_scale:.4f} and write counts by {write_scale:.4f}.\n\n")
         f.write(f"Kernel source: `matrix_free_pcg_amd/csrc/kernels.hpp`, sha256 `{rec['source_sha256']}`.\n\n")
         f.write(f"A {steps}-step solve; dispatches grouped by the step class they belong to (the stencil pass "
-                "alternates between a form that defers the x update and one that applies two). The stencil launch "
-                "after the last step, which only applies the pending x update, is left out.\n\n")
+                "defers the x update on three steps, `nox`, and applies the four pending terms on every fourth, "
+                "`x4`). The stencil launch after the last step, which returns at once, is left out.\n\n")
         f.write("| pass | step class | kernel | dispatches | read B/point | write B/point | traffic GB per launch | "
                 "algorithmic GB per launch |\n|---|---|---|---:|---:|---:|---:|---:|\n")
         f.write("\n".join(lines) + "\n\nN = 134217728 points.  Reads above the algorithmic count: in the stencil "
@@ -397,8 +402,8 @@ def counter_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, steps,
 
 # (reads, writes, pass it stands for)
 PROBE_MIXES = [(1, 1, "copy"), (2, 1, "residual r = b - A x"), (2, 2, "column pass (r, q -> r, z)"),
-               (3, 2, "stencil pass, odd steps (z, p, q -> p, q)"),
-               (5, 3, "stencil pass, even steps (z, p, q, x, p' -> p, q, x)")]
+               (3, 2, "stencil pass deferring x (z, p, q -> p, q)"),
+               (7, 3, "stencil pass of every fourth step (z, p, q, x and three older p -> p, q, x)")]
 
 
 def stream_probe(dtype="f64", vector_bytes=1 << 30, reps=20):
@@ -425,13 +430,13 @@ def stream_probe(dtype="f64", vector_bytes=1 << 30, reps=20):
                                    ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                    ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]
     tdt = torch.float32 if dtype == "f32" else torch.float64
-    vec = [torch.full((n,), 1.0 + k, dtype=tdt, device="cuda") for k in range(8)]
+    vec = [torch.full((n,), 1.0 + k, dtype=tdt, device="cuda") for k in range(10)]
     torch.cuda.synchronize()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     out = []
     for r, w, what in PROBE_MIXES:
         ins = (ctypes.c_void_p * r)(*[vec[k].data_ptr() for k in range(r)])
-        outs = (ctypes.c_void_p * w)(*[vec[5 + k].data_ptr() for k in range(w)])
+        outs = (ctypes.c_void_p * w)(*[vec[7 + k].data_ptr() for k in range(w)])
         row = {"reads": r, "writes": w, "stands_for": what}
         for nt in (1, 0):
             best = None

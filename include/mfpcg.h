@@ -205,7 +205,7 @@ int pcg_apply_A(pcg_handle *h, const double *x_dev, double *y_dev);
  * Asynchronous. */
 int pcg_precond(pcg_handle *h, const double *r_dev, double *z_dev);
 
-/* Bytes of device workspace a solve with this maxit needs (five N-vectors,
+/* Bytes of device workspace a solve with this maxit needs (seven N-vectors,
  * per-workgroup partial sums, the scalar state and the residual history). */
 size_t pcg_solve_workspace_bytes(const pcg_handle *h, int32_t maxit);
 
@@ -213,13 +213,15 @@ size_t pcg_solve_workspace_bytes(const pcg_handle *h, int32_t maxit);
  * (Algorithm 1): per iteration one fused preconditioner pass (Appendix A,
  * Algorithm 3: r -= alpha q, z = M^{-1} r, <r,r>, <r,z>) and one fused
  * stencil pass (Algorithm 2: x += alpha p, p = z + beta p, q = A z + beta q,
- * <p,q>), each followed by a deterministic reduction.  The x update of every
- * odd step is deferred to the next stencil pass, which applies both terms
- * (x + alpha_{k-1} p_{k-1} + alpha_k p_k, the same sum as two updates), so x
- * is read and written every second step; the two latest directions live in
- * two workspace vectors.  84 bytes per point per step (preconditioner pass:
- * read r, q, write r, z; stencil pass: read z, p, q, write p, q, and every
- * second step also read x and the older p, write x).
+ * <p,q>), each followed by a deterministic reduction.  The x updates of
+ * three steps are deferred to the stencil pass of the fourth, which applies
+ * the four terms one after the other (the same sums as four updates), so x
+ * is read and written every fourth step; the four latest directions live in
+ * four workspace vectors, and the updates still pending when the loop stops
+ * are applied before the call returns.  82 bytes per point per step
+ * (preconditioner pass: read r, q, write r, z; stencil pass: read z, p, q,
+ * write p, q, and every fourth step also read x and the three older
+ * directions, write x).
  *   b_dev          right-hand side, N doubles
  *   x_dev          in: initial guess x0; out: the last iterate.  Must not
  *                  alias b_dev or the workspace.
@@ -364,7 +366,7 @@ int pcg_solve_mixed(pcg_handle *h, const double *b_dev, double *x_dev, double to
  * The call allocates nothing (no hipMalloc, no event, no allocating library
  * routine); the caller still passes b, x and the host results.  The grid and
  * maxit must fit the array: pcg_solve_workspace_bytes(h, maxit) <= the
- * maximum (about 1.6 million points), else PCG_ERR_INVALID with the sizes in
+ * maximum (about 1.2 million points), else PCG_ERR_INVALID with the sizes in
  * pcg_last_error.  Every call on one device shares that device's array, and
  * each call leaves its state there: calls that overlap in time on one device
  * (two host threads, or two handles' streams) race and give wrong results.
@@ -441,9 +443,10 @@ int pcg_solve_csr(pcg_handle *h, const int64_t *row_ptr_dev, const int32_t *col_
  * one kernel id since the last pcg_profile_reset.  enable = 0 turns timing
  * off, 1 times every launch, P >= 2 times the solve loops' passes
  * (PCG_KID_FUSED_PREC, PCG_KID_FUSED_SPMV, PCG_KID_MG_VCYCLE) only at the
- * steps k with k mod P < 2 (each recorded event delays the next kernel by a
- * few microseconds) and every other launch as with 1.  Negative:
- * PCG_ERR_INVALID. */
+ * steps k with k mod P < 4 (four consecutive steps in every P: the stencil
+ * pass's forms as often as in a whole solve; each recorded event delays the
+ * next kernel by a few microseconds) and every other launch as with 1.
+ * Negative: PCG_ERR_INVALID. */
 #define PCG_KID_FUSED_PREC 0   /* interleaved preconditioner pass          */
 #define PCG_KID_FUSED_SPMV 1   /* interleaved stencil pass                 */
 #define PCG_KID_APPLY_A 2      /* stand-alone y = A x (and standard q = A p) */

@@ -65,9 +65,13 @@ struct Op {
 };
 
 // Scalar state of one solve, in device memory (one writer: the reduce kernels).
+// alpha is the newest step length, alpha_prev .. alpha_prev3 the three before
+// it (the deferred x updates need them); x holds x_0 + sum of alpha_i p_i over
+// i < x_steps.
 struct SolveState {
-    double alpha, beta, kappa_old, R0, R, sigma, kappa, alpha_prev;
-    int32_t k, done, fixup, status, iters, pad1, pad2, pad3;
+    double alpha, beta, kappa_old, R0, R, sigma, kappa;
+    double alpha_prev, alpha_prev2, alpha_prev3;
+    int32_t k, done, x_steps, status, iters, pad1, pad2, pad3;
 };
 
 // Copy of the stop decision that the reduce kernel writes to pinned host memory.
@@ -1175,8 +1179,15 @@ enum : int {
     SP_FUSED_AP = 6,  // x += alpha p, p_new = z + beta p, <p_new, A z + beta A p>  (no q stored)
     SP_FUSED_NOX = 7, // Algorithm 2 with the x update deferred: p_new = z + beta p (to
                       //   p_out), q = A z + beta q, <p_new, q>
-    SP_FUSED_X2 = 8   // SP_FUSED_NOX plus both pending x updates:
-                      //   x += alpha_prev p_prev (read from p_out) + alpha p
+    SP_FUSED_X4 = 9   // SP_FUSED_NOX plus the four pending x updates of p_{k-4}
+                      //   (p_out), p_{k-3}, p_{k-2} (older.a, older.b) and p_{k-1} (p)
+};
+
+// The two directions between p_out and p that SP_FUSED_X4 reads (p_{k-3},
+// p_{k-2}); null in every other mode.
+template <typename T>
+struct Older {
+    const T *a, *b;
 };
 
 // Stencil passes (section 4.2, eq. (18)): the 7-point operator recomputed in
@@ -1185,11 +1196,13 @@ enum : int {
 // SP_FIRST_AP / SP_FUSED_AP read the old search direction from p (with its
 // neighbours) and write the new one to p_out, a different buffer: an in-place
 // update would let a neighbour read an already-updated value.
-// SP_FUSED_NOX / SP_FUSED_X2 update x every second step (the stencil pass of
-// an odd step skips it, the next one applies both terms in one read and write
-// of x): p alternates between two buffers so that the older direction is still
-// there; p_out holds it on entry and receives the new one (each point is read
-// before it is written by the same thread, and p has no neighbour reads here).
+// SP_FUSED_NOX / SP_FUSED_X4 update x every fourth step (the stencil passes
+// of three steps skip it, the fourth applies the four terms in one read and
+// write of x): p rotates over four buffers so that the older directions are
+// still there; p_out holds p_{k-4} on entry and receives the new one (each
+// point is read before it is written by the same thread, and p has no
+// neighbour reads here).  Once the stop test has passed (st->done) every
+// form returns at once: the updates still pending are applied by k_x_fixup.
 // FULL: every tile is whole (nx a multiple of 64, nz a multiple of Ws * Ls),
 // so no level or column guard is needed, and a wave fetches the outside
 // neighbours of its two edge lanes (i-1 for lane 0, i+1 for lane 63) at all
@@ -1207,7 +1220,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
                                                          TV *__restrict__ y, Op o,
                                                          const SolveState *__restrict__ st,
                                                          double *__restrict__ partials,
-                                                         TV *__restrict__ p_out)
+                                                         TV *__restrict__ p_out, Older<TV> older)
 {
     static_assert((MODE != SP_FIRST_AP && MODE != SP_FUSED_AP) ||
                       (std::is_same<TV, double>::value && std::is_same<TI, double>::value),
@@ -1216,49 +1229,26 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
                   "row tiles: whole tiles, one operand");
     __shared__ double sh_red[kMaxThreads / kWave][1];
     TV alpha = 0, beta = 0;
-    bool fixup_only = false;
     constexpr bool kDot = MODE == SP_FIRST || MODE == SP_APPLY_DOT ||
                           MODE == SP_FIRST_AP || MODE == SP_FUSED_AP || MODE == SP_FUSED_NOX ||
-                          MODE == SP_FUSED_X2;
-    constexpr bool kFused = MODE == SP_FUSED_AP || MODE == SP_FUSED_NOX ||
-                            MODE == SP_FUSED_X2;
-    constexpr bool kX2 = MODE == SP_FUSED_X2;
-    TV alpha_prev = 0;
-    int fixup = 0;
+                          MODE == SP_FUSED_X4;
+    constexpr bool kX4 = MODE == SP_FUSED_X4;
+    constexpr bool kNox = MODE == SP_FUSED_NOX || kX4;   // p, q updates of Algorithm 2
+    TV alpha_prev = 0, alpha_prev2 = 0, alpha_prev3 = 0;
     if (kDot) {
-        if (st->done) {
-            fixup = st->fixup;
-            if (!kFused || !fixup)
-                return;
-            fixup_only = true;
-        }
+        if (st->done)
+            return;
         alpha = (TV)st->alpha;
         beta = (TV)st->beta;
-        if (kX2)
+        if (kX4) {
             alpha_prev = (TV)st->alpha_prev;
+            alpha_prev2 = (TV)st->alpha_prev2;
+            alpha_prev3 = (TV)st->alpha_prev3;
+        }
     }
     const Sweep sw = sweep_of_thread<JT>(o, Ls);
     const size_t ks = (size_t)o.nx;
     const size_t base = lin(o, sw.ic, sw.j, 0);
-
-    if (kFused && fixup_only) {
-        // The stop test passed in this iteration: only the pending update
-        // x += alpha p of the last step remains (Algorithm 1 exits before it),
-        // preceded in SP_FUSED_X2 by the deferred one of the step before
-        // (fixup 2: that deferred term alone, after a breakdown).
-        if (sw.ok) {
-            for (int t = 0; t < sw.len; ++t) {
-                const size_t l = base + (size_t)(sw.k0 + t) * ks;
-                TV v = u[l];
-                if (kX2)
-                    v = v + alpha_prev * p_out[l];
-                if (!kX2 || fixup == 1)
-                    v = v + alpha * p[l];
-                u[l] = v;
-            }
-        }
-        return;
-    }
 
     double acc = 0.0;
     if (sw.len > 0) {
@@ -1285,7 +1275,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
         constexpr bool kAp = MODE == SP_FUSED_AP;
         TV zv[Ls + 2], zyp[Ls], zym[Ls], zxl[Ls], zxr[Ls];   // the operand, widened to TV
         TV pv[kAp ? Ls + 2 : 1], pyp[kAp ? Ls : 1], pym[kAp ? Ls : 1], pxl[kAp ? Ls : 1], pxr[kAp ? Ls : 1];
-        TV uo[Ls], po[Ls], qo[Ls], p2[kX2 ? Ls : 1];
+        TV uo[Ls], po[Ls], qo[Ls], p2[kX4 ? Ls : 1], p3[kX4 ? Ls : 1], p4[kX4 ? Ls : 1];
         TV ev = 0;
         if constexpr (FULL) {
             // every outside neighbour of the wave's edge lanes in one load:
@@ -1331,13 +1321,16 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
                     pxr[t] = needR ? p[bxp + off] : 0.0;
                 }
             }
-            if constexpr (MODE == SP_FUSED_AP || kX2)
+            if constexpr (MODE == SP_FUSED_AP || kX4)
                 uo[t] = ld_s(u + base + off);
-            if constexpr (MODE == SP_FUSED_NOX || kX2)
+            if constexpr (kNox)
                 po[t] = ld_s(p + base + off);
-            if constexpr (kX2)
+            if constexpr (kX4) {
                 p2[t] = ld_s(p_out + base + off);
-            if constexpr (MODE == SP_FUSED_NOX || kX2)
+                p3[t] = ld_s(older.a + base + off);
+                p4[t] = ld_s(older.b + base + off);
+            }
+            if constexpr (kNox)
                 qo[t] = ld_s(y + base + off);
             if constexpr (MODE == SP_RESID)
                 qo[t] = ld_s(bvec + base + off);
@@ -1398,9 +1391,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_stencil(const TI *__restrict__ 
                         st_s(p + l, zc);
                         st_s(y + l, Az);
                         acc += (double)zc * (double)Az;
-                    } else if (MODE == SP_FUSED_NOX || kX2) {
-                        if constexpr (kX2)
-                            st_s(u + l, (uo[t] + alpha_prev * p2[t]) + alpha * po[t]);
+                    } else if (kNox) {
+                        if constexpr (kX4)   // in the order of the steps, as one update a step
+                            st_s(u + l, (((uo[t] + alpha_prev3 * p2[t]) + alpha_prev2 * p3[t]) +
+                                         alpha_prev * p4[t]) + alpha * po[t]);
                         const TV pn = zc + beta * po[t];
                         const TV qn = Az + beta * qo[t];
                         st_s(p_out + l, pn);
@@ -1908,11 +1902,10 @@ __device__ __forceinline__ void sum_partials(const double *__restrict__ partials
         tot[a] = sh[a][0];
 }
 
-__device__ __forceinline__ void finish(SolveState *st, int32_t status, int32_t fixup)
+__device__ __forceinline__ void finish(SolveState *st, int32_t status)
 {
     st->done = 1;
     st->status = status;
-    st->fixup = fixup;
 }
 
 __device__ __forceinline__ void publish(const SolveState *st, HostStatus *hs, int k)
@@ -1954,13 +1947,13 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce_rz(const double *__restr
         st->iters = 0;
         st->alpha = 0.0;
         if (!isfinite(R))
-            finish(st, ST_BREAKDOWN, 0);
+            finish(st, ST_BREAKDOWN);
         else if (R == 0.0)
-            finish(st, ST_OK, 0);
+            finish(st, ST_OK);
         else if (maxit == 0)
-            finish(st, ST_NOT_CONVERGED, 0);
+            finish(st, ST_NOT_CONVERGED);
         else if (!(kappa > 0.0) || !isfinite(kappa))
-            finish(st, ST_BREAKDOWN, 0);
+            finish(st, ST_BREAKDOWN);
         else {
             st->beta = 0.0;
             st->kappa_old = kappa;
@@ -1968,13 +1961,13 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce_rz(const double *__restr
     } else {
         st->iters = k;
         if (!isfinite(R))
-            finish(st, ST_BREAKDOWN, 1);
+            finish(st, ST_BREAKDOWN);
         else if (R == 0.0 || R / st->R0 < tol)
-            finish(st, ST_OK, 1);
+            finish(st, ST_OK);
         else if (k == maxit)
-            finish(st, ST_NOT_CONVERGED, 1);
+            finish(st, ST_NOT_CONVERGED);
         else if (!(kappa > 0.0) || !isfinite(kappa))
-            finish(st, ST_BREAKDOWN, 1);
+            finish(st, ST_BREAKDOWN);
         else {
             st->beta = kappa / st->kappa_old;
             st->kappa_old = kappa;
@@ -1983,34 +1976,31 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce_rz(const double *__restr
     publish(st, hs, k);
 }
 
-// After the stencil pass: sigma = <p, A p>, alpha = kappa / sigma (the
-// previous alpha is kept for a deferred x update).  deferred != 0: the x
-// update of this step was deferred (see SP_FUSED_NOX), so a breakdown here
-// leaves fixup = 2 for the next stencil pass to apply it alone.
+// After the stencil pass: sigma = <p, A p>, alpha = kappa / sigma (the three
+// alphas before it are kept for the deferred x updates).  x_steps >= 0: the
+// pass brought x up to x_0 + sum of alpha_i p_i over i < x_steps.  After a
+// breakdown here the alphas stay as they were, so that k_x_fixup finds the
+// step lengths of the pending updates, and this step's is never applied.
 __global__ __launch_bounds__(kRedThreads) void k_reduce_sigma(const double *__restrict__ partials,
                                                               int nparts, SolveState *st,
-                                                              int iters_if_breakdown, int deferred)
+                                                              int iters_if_breakdown, int x_steps)
 {
-    if (st->done) {
-        if (threadIdx.x == 0)
-            st->fixup = 0;
+    if (st->done)
         return;
-    }
     double tot[1];
     sum_partials<1>(partials, nparts, 0, tot);
     if (threadIdx.x != 0)
         return;
     const double sigma = tot[0];
     st->sigma = sigma;
+    if (x_steps >= 0)
+        st->x_steps = x_steps;
     if (!(sigma > 0.0) || !isfinite(sigma)) {
         st->iters = iters_if_breakdown;
-        if (deferred) {
-            st->alpha_prev = st->alpha;
-            finish(st, ST_BREAKDOWN, 2);
-        } else {
-            finish(st, ST_BREAKDOWN, 0);
-        }
+        finish(st, ST_BREAKDOWN);
     } else {
+        st->alpha_prev3 = st->alpha_prev2;
+        st->alpha_prev2 = st->alpha_prev;
         st->alpha_prev = st->alpha;
         st->alpha = st->kappa_old / sigma;
     }
@@ -2036,11 +2026,11 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce_rr(const double *__restr
     hist[k] = R;
     st->iters = k;
     if (!isfinite(R))
-        finish(st, ST_BREAKDOWN, 0);
+        finish(st, ST_BREAKDOWN);
     else if (R == 0.0 || R / st->R0 < tol)
-        finish(st, ST_OK, 0);
+        finish(st, ST_OK);
     else if (k == maxit)
-        finish(st, ST_NOT_CONVERGED, 0);
+        finish(st, ST_NOT_CONVERGED);
     publish(st, hs, k);
 }
 
@@ -2057,10 +2047,40 @@ __global__ __launch_bounds__(kRedThreads) void k_reduce_kappa(const double *__re
     const double kappa = tot[0];
     st->kappa = kappa;
     if (!(kappa > 0.0) || !isfinite(kappa)) {
-        finish(st, ST_BREAKDOWN, 0);
+        finish(st, ST_BREAKDOWN);
     } else {
         st->beta = kappa / st->kappa_old;
         st->kappa_old = kappa;
+    }
+}
+
+// The search directions of the last steps of an interleaved solve: p_i is in
+// p[i mod 4] (a two-buffer rotation passes its buffers twice).
+template <typename T>
+struct DirRing {
+    const T *p[4];
+};
+
+// After the last step of an interleaved solve (Algorithm 1 leaves the loop
+// once the stop test passes): the x updates the stencil passes deferred,
+// x += alpha_i p_i for x_steps <= i < iters, one after the other in the order
+// of i.  alpha_{iters-1} is st->alpha, the ones before it alpha_prev ..
+// alpha_prev3; at most four updates are pending (the deferral is at most
+// four steps).  Every element is read and written by one thread.
+template <typename TV>
+__global__ __launch_bounds__(256) void k_x_fixup(TV *__restrict__ x, DirRing<TV> ring,
+                                                 const SolveState *__restrict__ st, size_t n)
+{
+    const int K = st->iters, A = st->x_steps;
+    if (K <= A || K - A > 4)
+        return;
+    const TV al[4] = {(TV)st->alpha, (TV)st->alpha_prev, (TV)st->alpha_prev2, (TV)st->alpha_prev3};
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t l = (size_t)blockIdx.x * blockDim.x + threadIdx.x; l < n; l += stride) {
+        TV v = x[l];
+        for (int i = A; i < K; ++i)
+            v = v + al[K - 1 - i] * ring.p[i & 3][l];
+        x[l] = v;
     }
 }
 

@@ -210,7 +210,7 @@ constexpr int kStagePer = 1024;
 int stage_blocks(int nparts) { return nparts <= kDirect ? 0 : (nparts + kStagePer - 1) / kStagePer; }
 
 struct Workspace {
-    double *r, *z, *p, *q, *p2, *partials, *stage, *hist;
+    double *r, *z, *p, *q, *p2, *p3, *p4, *partials, *stage, *hist;
     SolveState *state;
 };
 
@@ -221,6 +221,7 @@ size_t workspace_layout(const pcg_handle *h, int32_t maxit, char *base, Workspac
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     size_t o_r = take(vec), o_z = take(vec), o_p = take(vec), o_q = take(vec), o_p2 = take(vec);
+    size_t o_p3 = take(vec), o_p4 = take(vec);
     size_t o_part = take((size_t)np * 2 * sizeof(double));
     size_t o_stage = take((size_t)std::max(1, stage_blocks(np)) * 2 * sizeof(double));
     size_t o_state = take(sizeof(SolveState));
@@ -231,6 +232,8 @@ size_t workspace_layout(const pcg_handle *h, int32_t maxit, char *base, Workspac
         w->p = (double *)(base + o_p);
         w->q = (double *)(base + o_q);
         w->p2 = (double *)(base + o_p2);
+        w->p3 = (double *)(base + o_p3);
+        w->p4 = (double *)(base + o_p4);
         w->partials = (double *)(base + o_part);
         w->stage = (double *)(base + o_stage);
         w->state = (SolveState *)(base + o_state);
@@ -305,14 +308,16 @@ hipEvent_t take_event(pcg_handle *h)
 
 // A recorded event shows on the GPU's timeline as a gap of about 5.6 us
 // before the next kernel, so with a period P > 1 the passes of the solve
-// loops (tags >= 0: the step) are timed on two consecutive steps in every P
-// (both stencil-pass forms), the other launches every time.
+// loops (tags >= 0: the step) are timed on four consecutive steps in every P
+// (the stencil pass's forms in the proportion of a whole solve: x is updated
+// every fourth step), the other launches every time.
+constexpr int kProfileWindow = 4;
 bool timed_launch(const pcg_handle *h, int kid, int tag)
 {
     if (!h->profiling)
         return false;
     const bool loop_pass = kid == PCG_KID_FUSED_PREC || kid == PCG_KID_FUSED_SPMV || kid == PCG_KID_MG_VCYCLE;
-    return !loop_pass || tag < 0 || h->profile_period <= 1 || tag % h->profile_period < 2;
+    return !loop_pass || tag < 0 || h->profile_period <= 1 || tag % h->profile_period < kProfileWindow;
 }
 
 struct Timed {
@@ -339,7 +344,7 @@ struct Timed {
 
 // Fold the recorded event pairs into the totals (the stream must be idle).
 // Launches tagged `skip_tag` of kernel `skip_kid` are dropped (the final
-// stencil pass of a solve, which only applies the pending x update).
+// stencil pass of a solve, launched before the stop test was read: it returns at once).
 void drain_events(pcg_handle *h, int skip_kid = -1, int skip_tag = -2)
 {
     for (auto &e : h->pending) {
@@ -471,34 +476,34 @@ void column(pcg_handle *h, const TV *rin, const TV *q, TV *rout, TZ *z,
 // the solve with a binary32 preconditioner.
 template <int Ls, bool FULL, typename TV, typename TI>
 void launch_stencil_f(pcg_handle *h, const Op &o, int mode, const TI *zin, const TV *b, TV *u, TV *p, TV *y,
-                      const SolveState *st, double *partials, TV *p_out)
+                      const SolveState *st, double *partials, TV *p_out, Older<TV> older)
 {
     dim3 grid(h->pt_tiles), block(kWave * o.Ws);
     constexpr bool kSame = std::is_same<TV, TI>::value;
     constexpr bool kD = kBinary64<TV, TI>;
     switch (mode) {
-    case SP_FIRST: k_stencil<Ls, SP_FIRST, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_FUSED_NOX: k_stencil<Ls, SP_FUSED_NOX, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-    case SP_FUSED_X2: k_stencil<Ls, SP_FUSED_X2, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+    case SP_FIRST: k_stencil<Ls, SP_FIRST, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older); break;
+    case SP_FUSED_NOX: k_stencil<Ls, SP_FUSED_NOX, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older); break;
+    case SP_FUSED_X4: k_stencil<Ls, SP_FUSED_X4, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older); break;
     case SP_APPLY:
         if constexpr (kSame)
-            k_stencil<Ls, SP_APPLY, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+            k_stencil<Ls, SP_APPLY, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older);
         break;
     case SP_RESID:
         if constexpr (kSame)
-            k_stencil<Ls, SP_RESID, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+            k_stencil<Ls, SP_RESID, FULL, TV, TI><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older);
         break;
     case SP_APPLY_DOT:
         if constexpr (kD)
-            k_stencil<Ls, SP_APPLY_DOT, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+            k_stencil<Ls, SP_APPLY_DOT, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older);
         break;
     case SP_FIRST_AP:
         if constexpr (kD)
-            k_stencil<Ls, SP_FIRST_AP, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+            k_stencil<Ls, SP_FIRST_AP, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older);
         break;
     default:
         if constexpr (kD)
-            k_stencil<Ls, SP_FUSED_AP, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+            k_stencil<Ls, SP_FUSED_AP, FULL><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older);
         break;
     }
 }
@@ -506,27 +511,27 @@ void launch_stencil_f(pcg_handle *h, const Op &o, int mode, const TI *zin, const
 // Whole tiles of JT rows x Ls levels, one wave per row (k_stencil with JT).
 template <int Ls, int JT, typename TV, typename TI>
 void launch_stencil_jt(pcg_handle *h, const Op &o, int mode, const TI *zin, const TV *b, TV *u, TV *p,
-                       TV *y, const SolveState *st, double *partials, TV *p_out)
+                       TV *y, const SolveState *st, double *partials, TV *p_out, Older<TV> older)
 {
     constexpr bool kSame = std::is_same<TV, TI>::value;
     dim3 grid((unsigned)((size_t)o.ntx * o.nkt * (o.ny / JT))), block(kWave * JT);
     if constexpr (Ls == 4) {   // the fused passes
         switch (mode) {
-        case SP_FIRST: k_stencil<Ls, SP_FIRST, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-        case SP_FUSED_NOX: k_stencil<Ls, SP_FUSED_NOX, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-        case SP_FUSED_X2: k_stencil<Ls, SP_FUSED_X2, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+        case SP_FIRST: k_stencil<Ls, SP_FIRST, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older); break;
+        case SP_FUSED_NOX: k_stencil<Ls, SP_FUSED_NOX, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older); break;
+        case SP_FUSED_X4: k_stencil<Ls, SP_FUSED_X4, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older); break;
         default: break;
         }
     }
-    if constexpr (Ls == 8 && JT == 4 && kBinary64<TV, TI>) {   // the binary64 odd-step pass
+    if constexpr (Ls == 8 && JT == 4 && kBinary64<TV, TI>) {   // the binary64 pass that defers x
         if (mode == SP_FUSED_NOX)
-            k_stencil<Ls, SP_FUSED_NOX, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out);
+            k_stencil<Ls, SP_FUSED_NOX, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older);
     }
     if constexpr (kSame && Ls == 8) {   // the operator-only passes
         switch (mode) {
-        case SP_APPLY: k_stencil<Ls, SP_APPLY, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-        case SP_RESID: k_stencil<Ls, SP_RESID, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
-        case SP_APPLY_DOT: k_stencil<Ls, SP_APPLY_DOT, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out); break;
+        case SP_APPLY: k_stencil<Ls, SP_APPLY, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older); break;
+        case SP_RESID: k_stencil<Ls, SP_RESID, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older); break;
+        case SP_APPLY_DOT: k_stencil<Ls, SP_APPLY_DOT, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older); break;
         default: break;
         }
     }
@@ -543,7 +548,7 @@ void launch_stencil_jt(pcg_handle *h, const Op &o, int mode, const TI *zin, cons
 // count.
 
 // Rows per tile of the fused stencil passes (SP_FIRST, SP_FUSED_NOX,
-// SP_FUSED_X2) on this handle, 0 when they take one-row tiles.  Measured at
+// SP_FUSED_X4) on this handle, 0 when they take one-row tiles.  Measured at
 // 1024 x 1024 x 128: 4 rows best in binary64 and the mixed solve (8 rows:
 // 1.2 % and 6 % slower), 8 rows in binary32 (2.5 % faster than 4).
 int fused_rows_jt(const pcg_handle *h, bool binary32)
@@ -584,7 +589,7 @@ RowShape fused_shape(const pcg_handle *h, int mode, bool binary64, bool binary32
 // Partial sums (tiles) of a stencil pass of this mode.
 int stencil_tiles(const pcg_handle *h, int mode, bool binary64, bool binary32)
 {
-    if (mode == SP_FIRST || mode == SP_FUSED_NOX || mode == SP_FUSED_X2) {
+    if (mode == SP_FIRST || mode == SP_FUSED_NOX || mode == SP_FUSED_X4) {
         const RowShape rs = fused_shape(h, mode, binary64, binary32);
         if (rs.jt)
             return (int)((size_t)h->op.ntx * (h->op.nz / rs.Ls) * (h->op.ny / rs.jt));
@@ -596,11 +601,11 @@ int stencil_tiles(const pcg_handle *h, int mode, bool binary64, bool binary32)
 
 template <int Ls, typename TV, typename TI>
 void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, TV *p, TV *y,
-                    const SolveState *st, double *partials, TV *p_out)
+                    const SolveState *st, double *partials, TV *p_out, Older<TV> older)
 {
     if constexpr (Ls == 4) {
         const bool op_only = mode == SP_APPLY || mode == SP_APPLY_DOT || mode == SP_RESID;
-        const bool fused_rows = mode == SP_FIRST || mode == SP_FUSED_NOX || mode == SP_FUSED_X2;
+        const bool fused_rows = mode == SP_FIRST || mode == SP_FUSED_NOX || mode == SP_FUSED_X4;
         const RowShape rs = fused_rows ? fused_shape(h, mode, kBinary64<TV, TI>,
                                                      std::is_same<TV, float>::value && std::is_same<TI, float>::value)
                                        : RowShape{4, 0};
@@ -611,11 +616,11 @@ void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, 
             o2.Ws = rs.jt;
             o2.nkt = h->op.nz / rs.Ls;
             if (rs.Ls == 8)
-                launch_stencil_jt<8, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+                launch_stencil_jt<8, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
             else if (rs.jt == 8)
-                launch_stencil_jt<4, 8>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+                launch_stencil_jt<4, 8>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
             else
-                launch_stencil_jt<4, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+                launch_stencil_jt<4, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
             return;
         }
         const int ojt = op_rows_jt(h);
@@ -626,9 +631,9 @@ void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, 
             o2.jt = ojt;
             o2.nkt = h->op.nz / 8;
             if (ojt == 4)
-                launch_stencil_jt<8, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+                launch_stencil_jt<8, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
             else
-                launch_stencil_jt<8, 2>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+                launch_stencil_jt<8, 2>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
             return;
         }
         if (op_only && h->op.Ws % 2 == 0) {
@@ -636,27 +641,27 @@ void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, 
             o2.Ls = 8;
             o2.Ws = h->op.Ws / 2;
             if (h->pt_full)
-                launch_stencil_f<8, true>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+                launch_stencil_f<8, true>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
             else
-                launch_stencil_f<8, false>(h, o2, mode, zin, b, u, p, y, st, partials, p_out);
+                launch_stencil_f<8, false>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
             return;
         }
     }
     if (h->pt_full)
-        launch_stencil_f<Ls, true>(h, h->op, mode, zin, b, u, p, y, st, partials, p_out);
+        launch_stencil_f<Ls, true>(h, h->op, mode, zin, b, u, p, y, st, partials, p_out, older);
     else
-        launch_stencil_f<Ls, false>(h, h->op, mode, zin, b, u, p, y, st, partials, p_out);
+        launch_stencil_f<Ls, false>(h, h->op, mode, zin, b, u, p, y, st, partials, p_out, older);
 }
 
 template <typename TV, typename TI>
 void stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, TV *p, TV *y,
-             const SolveState *st, double *partials, TV *p_out = nullptr)
+             const SolveState *st, double *partials, TV *p_out = nullptr, Older<TV> older = {})
 {
     switch (h->op.Ls) {
-    case 1: launch_stencil<1>(h, mode, zin, b, u, p, y, st, partials, p_out); break;
-    case 2: launch_stencil<2>(h, mode, zin, b, u, p, y, st, partials, p_out); break;
-    case 4: launch_stencil<4>(h, mode, zin, b, u, p, y, st, partials, p_out); break;
-    default: launch_stencil<8>(h, mode, zin, b, u, p, y, st, partials, p_out); break;
+    case 1: launch_stencil<1>(h, mode, zin, b, u, p, y, st, partials, p_out, older); break;
+    case 2: launch_stencil<2>(h, mode, zin, b, u, p, y, st, partials, p_out, older); break;
+    case 4: launch_stencil<4>(h, mode, zin, b, u, p, y, st, partials, p_out, older); break;
+    default: launch_stencil<8>(h, mode, zin, b, u, p, y, st, partials, p_out, older); break;
     }
 }
 
@@ -1481,10 +1486,12 @@ void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const 
 
 // The interleaved loop of section 4.3, Algorithm 1.  ap = false: Algorithms 2
 // and 3 as printed (q = A z + beta q stored by the stencil pass, r -= alpha q
-// in the preconditioner pass), with the x update of every odd step deferred to
-// the next stencil pass, which applies both terms (x is read and written every
-// second step: 84 instead of 88 bytes per point per step); the directions
-// alternate between p and p2 so that the deferred one is still there.
+// in the preconditioner pass), with the x updates of three steps deferred to
+// the stencil pass of the fourth, which applies the four terms in the order of
+// the steps (x is read and written every fourth step, the three older
+// directions read then: 82 instead of 88 bytes per point per step); the
+// directions rotate over four buffers so that the deferred ones are still
+// there, and k_x_fixup applies what is pending when the loop stops.
 // ap = true: q is never stored -- the preconditioner pass recomputes A p from
 // p and the stencil pass forms <p_new, A z + beta A p_old>; p alternates
 // between two buffers (the stencil pass reads the old direction around each
@@ -1509,7 +1516,12 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
     // the front of each slot
     TV *r = (TV *)w.r, *q = (TV *)w.q;
     TZ *z = (TZ *)w.z;
-    TV *pbuf[2] = {(TV *)w.p, ap ? (TV *)w.q : (TV *)w.p2};
+    // p_i lives in pbuf[i mod 4]: four buffers with q stored (x is updated
+    // every fourth step), two on the q-free path (the stencil pass reads the
+    // old direction around each point while it writes the new one), each
+    // named twice
+    TV *pbuf[4] = {(TV *)w.p, ap ? (TV *)w.q : (TV *)w.p2, ap ? (TV *)w.p : (TV *)w.p3,
+                   ap ? (TV *)w.q : (TV *)w.p4};
     k_init_state<<<1, 64, 0, h->stream>>>(w.state);
     // a2: r0 = b - A x0
     stencil<TV, TV>(h, SP_RESID, x, b, nullptr, nullptr, r, nullptr, nullptr);
@@ -1521,8 +1533,13 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
         // search direction read this iteration (written by the previous one)
         // and the buffer of the new one
         TV *pin = ap ? pbuf[(k + 1) & 1] : q;
-        TV *pcur = pbuf[(k + 1) & 1];
-        TV *pnext = pbuf[k & 1];
+        TV *pcur = pbuf[(k + 3) & 3];    // p_{k-1}
+        TV *pnext = pbuf[k & 3];         // p_{k-4} (q-free: p_{k-2}) on entry, p_k on exit
+        const Older<TV> older{pbuf[(k + 1) & 3], pbuf[(k + 2) & 3]};   // p_{k-3}, p_{k-2}
+        // the stencil pass's form and whether it brings x up to date
+        const bool xstep = ap ? k > 0 : (k > 0 && k % 4 == 0);
+        const int smode = ap ? (k == 0 ? SP_FIRST_AP : SP_FUSED_AP)
+                             : (k == 0 ? SP_FIRST : (xstep ? SP_FUSED_X4 : SP_FUSED_NOX));
         // a3: r -= alpha q (or alpha A p); z = M^{-1} r; partial <r,r>, <r,z>  (Algorithm 3)
         if constexpr (kD) {
             if (mg) {
@@ -1546,19 +1563,16 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
             Timed t(h, PCG_KID_FUSED_SPMV, k);
             if (ap) {
                 if constexpr (kD)
-                    stencil<TV, TZ>(h, k == 0 ? SP_FIRST_AP : SP_FUSED_AP, z, nullptr, x, pcur, nullptr,
-                                    w.state, w.partials, pnext);
+                    stencil<TV, TZ>(h, smode, z, nullptr, x, pcur, nullptr, w.state, w.partials, pnext);
             } else if (k == 0) {
                 stencil<TV, TZ>(h, SP_FIRST, z, nullptr, x, pnext, q, w.state, w.partials);
             } else {
-                stencil<TV, TZ>(h, (k & 1) ? SP_FUSED_NOX : SP_FUSED_X2, z, nullptr, x, pcur, q, w.state,
-                                w.partials, pnext);
+                stencil<TV, TZ>(h, smode, z, nullptr, x, pcur, q, w.state, w.partials, pnext, older);
             }
         }
         // a6: sigma, alpha
-        const int smode = ap ? SP_FUSED_AP : (k == 0 ? SP_FIRST : ((k & 1) ? SP_FUSED_NOX : SP_FUSED_X2));
         red = fold_partials(h, w, stencil_tiles(h, smode, kBinary64<TV, TZ>, std::is_same<TV, float>::value), &nred);
-        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k, !ap && (k & 1));
+        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k, xstep ? k : -1);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return fail(h, PCG_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -1575,6 +1589,10 @@ int interleaved_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, bool
         if (((volatile HostStatus *)h->h_status)->done)
             break;
     }
+    // a7: the x updates still pending when the loop stopped
+    const DirRing<TV> ring{{pbuf[0], pbuf[1], pbuf[2], pbuf[3]}};
+    const size_t nb = std::min<size_t>((h->n + 255) / 256, 8192);
+    k_x_fixup<TV><<<dim3((unsigned)std::max<size_t>(nb, 1)), dim3(256), 0, h->stream>>>(x, ring, w.state, h->n);
     return solve_epilogue(h, a, w, PCG_KID_FUSED_SPMV, last);
 }
 
@@ -1970,7 +1988,7 @@ int standard_loop(pcg_handle *h, const SolveArgs &a, const Workspace &w, const E
                 stencil<double, double>(h, SP_APPLY_DOT, w.p, nullptr, nullptr, nullptr, w.q, w.state, w.partials);
         }
         red = fold_partials(h, w, ex ? h->pt_tiles : stencil_tiles(h, SP_APPLY_DOT, true, false), &nred);
-        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k - 1, 0);
+        k_reduce_sigma<<<1, kRedThreads, 0, h->stream>>>(red, nred, w.state, k - 1, -1);
         {   // x += alpha p ; r -= alpha q ; <r,r>
             Timed t(h, PCG_KID_VECTOR, k);
             update_xr(h, x, w.p, w.r, w.q, w.state, w.partials);

@@ -1,8 +1,8 @@
 // stream_probe.hip - a measurement tool, not part of the solver: the HBM
 // bandwidth that a plain streaming kernel reaches on this GPU when it reads
 // R and writes W vectors once per element, the stream mixes of the solver's
-// passes (column pass: 2 in / 2 out; stencil pass: 3 / 2 on odd steps, 5 / 3
-// on even steps), in float64 (8 bytes per lane access) and float32 (4 bytes,
+// passes (column pass: 2 in / 2 out; stencil pass: 3 / 2 on the steps that
+// defer the x update, 7 / 3 on every fourth step), in float64 (8 bytes per lane access) and float32 (4 bytes,
 // the binary32 solve's element).  It gives the measured ceiling beside the
 // published peak for those mixes.  C ABI, loaded by bench.py --stream-probe.
 #include <hip/hip_runtime.h>
@@ -14,7 +14,7 @@ constexpr int kMaxBlock = 1024;
 
 template <typename T>
 struct Streams {
-    const T *in[5];
+    const T *in[7];
     T *out[3];
 };
 
@@ -87,12 +87,14 @@ using Launcher = void (*)(bool, int, const Streams<T> &, unsigned, unsigned, hip
 template <typename T>
 Launcher<T> pick(int r, int w)
 {
-    static const Launcher<T> table[5][3] = {
+    static const Launcher<T> table[7][3] = {
         {launch<T, 1, 1>, launch<T, 1, 2>, launch<T, 1, 3>},
         {launch<T, 2, 1>, launch<T, 2, 2>, launch<T, 2, 3>},
         {launch<T, 3, 1>, launch<T, 3, 2>, launch<T, 3, 3>},
         {launch<T, 4, 1>, launch<T, 4, 2>, launch<T, 4, 3>},
-        {launch<T, 5, 1>, launch<T, 5, 2>, launch<T, 5, 3>}};
+        {launch<T, 5, 1>, launch<T, 5, 2>, launch<T, 5, 3>},
+        {launch<T, 6, 1>, launch<T, 6, 2>, launch<T, 6, 3>},
+        {launch<T, 7, 1>, launch<T, 7, 2>, launch<T, 7, 3>}};
     return table[r - 1][w - 1];
 }
 
@@ -101,7 +103,7 @@ template <typename T>
 int run(int32_t reads, int32_t writes, int32_t nontemporal, int32_t elems, int32_t block, int64_t n,
         const T *const *in_dev, T *const *out_dev, int32_t reps, void *stream, double *ms_per_launch)
 {
-    if (reads < 1 || reads > 5 || writes < 1 || writes > 3 ||
+    if (reads < 1 || reads > 7 || writes < 1 || writes > 3 ||
         (elems != 1 && elems != 2 && elems != 4 && elems != 8) || block < 64 || block > kMaxBlock ||
         block % 64 != 0 || n <= 0 || n % ((int64_t)block * elems) != 0 ||
         n / ((int64_t)block * elems) > 0x7fffffff || !in_dev || !out_dev || reps < 1 || !ms_per_launch)
@@ -156,7 +158,7 @@ extern "C" {
 // Time `reps` launches of the (reads, writes) streaming kernel on `stream`
 // (a hipStream_t, NULL for the null stream) after 3 untimed ones, and store
 // the average milliseconds per launch in *ms_per_launch.
-//   reads 1..5, writes 1..3; elems (per thread) 1, 2, 4 or 8; block 64..1024,
+//   reads 1..7, writes 1..3; elems (per thread) 1, 2, 4 or 8; block 64..1024,
 //   a multiple of 64; n > 0 a multiple of block * elems; in_dev / out_dev:
 //   HOST arrays of `reads` / `writes` device pointers to n doubles each
 //   (n floats for mfprobe_stream_f32), the outputs distinct from each other

@@ -261,7 +261,7 @@ def test_stream_probe_rejects_bad_arguments():
         ins = (ctypes.c_void_p * 5)(*([ctypes.c_void_p(4096)] * 5))
         outs = (ctypes.c_void_p * 3)(*([ctypes.c_void_p(8192)] * 3))
         ms = ctypes.c_double(0.0)
-        for r, w, e, b, n, reps in [(0, 1, 4, 256, 1024, 1), (6, 1, 4, 256, 1024, 1), (1, 0, 4, 256, 1024, 1),
+        for r, w, e, b, n, reps in [(0, 1, 4, 256, 1024, 1), (8, 1, 4, 256, 1024, 1), (1, 0, 4, 256, 1024, 1),
                                     (1, 4, 4, 256, 1024, 1), (1, 1, 3, 256, 1024, 1), (1, 1, 4, 100, 1024, 1),
                                     (1, 1, 4, 2048, 8192, 1), (1, 1, 4, 256, 1000, 1), (1, 1, 4, 256, 0, 1),
                                     (1, 1, 4, 256, 1024, 0)]:

@@ -12,25 +12,28 @@ import bench
 N = 1024 * 1024 * 128
 
 
-@pytest.mark.parametrize("variant,per_point", [("interleaved", 84), ("interleaved_no_q", 72), ("f32", 42),
-                                               ("mixed", 76)])
+@pytest.mark.parametrize("variant,per_point", [("interleaved", 82), ("interleaved_no_q", 72), ("f32", 41),
+                                               ("mixed", 74)])
 def test_steady_state_bytes(variant, per_point):
-    # two steady-state steps (one odd, one even) of both passes
+    # four steady-state steps (three that defer the x update, one that
+    # applies four) of both passes
     f = bench.BYTES_BY_VARIANT[variant][0]
-    tot = sum(f(kern, k) for kern in ("fused_prec", "fused_spmv") for k in (5, 6))
-    assert tot == 2 * per_point
+    tot = sum(f(kern, k) for kern in ("fused_prec", "fused_spmv") for k in (5, 6, 7, 8))
+    assert tot == 4 * per_point
+    assert bench.BYTES_BY_VARIANT[variant][1] == per_point
 
 
 def test_step_classes_and_timed_launches():
     assert bench.step_class("interleaved", "fused_spmv", 0) == "first"
-    assert bench.step_class("interleaved", "fused_spmv", 3) == "odd"
-    assert bench.step_class("interleaved", "fused_spmv", 4) == "even"
+    assert bench.step_class("interleaved", "fused_spmv", 3) == "nox"
+    assert bench.step_class("interleaved", "fused_spmv", 4) == "x4"
+    assert bench.step_class("interleaved", "fused_spmv", 6) == "nox"
     assert bench.step_class("interleaved", "fused_prec", 4) == "rest"
     # a solve of K steps times K+1 preconditioner passes and K stencil passes
     assert len(list(bench.timed_steps("fused_prec", [10, 7]))) == 19
     assert len(list(bench.timed_steps("fused_spmv", [10, 7]))) == 17
-    tot, cnt = bench.pass_bytes("interleaved", "fused_spmv", [3], 1)
-    assert (tot, cnt) == (24 + 40 + 64, 3)
+    tot, cnt = bench.pass_bytes("interleaved", "fused_spmv", [5], 1)
+    assert (tot, cnt) == (24 + 40 + 40 + 40 + 80, 5)
 
 
 def test_mg_cycle_bytes():
@@ -81,19 +84,22 @@ def test_mg_cycle_bytes_with_coarse_sweeps():
 
 def test_sampled_profiling_steps():
     """With a profiling period P the library times the solve loops' passes at
-    the steps k with k mod P < 2: two consecutive steps, so both stencil-pass
-    forms, in every P; the byte accounting counts the same launches."""
-    ks = list(bench.timed_steps("fused_prec", [10], period=4))
-    assert ks == [0, 1, 4, 5, 8, 9]
-    ks = list(bench.timed_steps("fused_spmv", [10, 7], period=4))
-    assert ks == [0, 1, 4, 5, 8, 9] + [0, 1, 4, 5]
+    the steps k with k mod P < 4: four consecutive steps, so the stencil
+    pass's two forms as often as in a whole solve, in every P; the byte
+    accounting counts the same launches."""
+    assert bench.PROFILE_WINDOW == 4
+    ks = list(bench.timed_steps("fused_prec", [18], period=8))
+    assert ks == [0, 1, 2, 3, 8, 9, 10, 11, 16, 17, 18]
+    ks = list(bench.timed_steps("fused_spmv", [18, 7], period=8))
+    assert ks == [0, 1, 2, 3, 8, 9, 10, 11, 16, 17] + [0, 1, 2, 3]
     assert list(bench.timed_steps("fused_prec", [10], period=1)) == list(range(11))
     n = 1 << 20
-    tot8, cnt8 = bench.pass_bytes("interleaved", "fused_spmv", [927], n, period=8)
+    totp, cntp = bench.pass_bytes("interleaved", "fused_spmv", [927], n, period=16)
     tot1, cnt1 = bench.pass_bytes("interleaved", "fused_spmv", [927], n)
-    assert cnt8 == len([k for k in range(927) if k % 8 < 2])
-    # the sample holds odd and even steps alike, so its mean is the whole solve's
-    assert abs(tot8 / cnt8 - tot1 / cnt1) <= 0.01 * tot1 / cnt1
+    assert cntp == len([k for k in range(927) if k % 16 < 4])
+    # one step in four of the sample applies the x updates, as in the whole
+    # solve, so its mean is the whole solve's
+    assert abs(totp / cntp - tot1 / cnt1) <= 0.01 * tot1 / cnt1
     pts = [8, 4, 2]
-    t, c = bench.mg_pass_bytes(pts, [9], period=4)
-    assert c == len([k for k in range(10) if k % 4 < 2])
+    t, c = bench.mg_pass_bytes(pts, [9], period=8)
+    assert c == len([k for k in range(10) if k % 8 < 4])

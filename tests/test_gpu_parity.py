@@ -189,9 +189,11 @@ def test_solve_matches_oracle(dev, label, make, drift, variant):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-@pytest.mark.parametrize("steps", [0, 1, 2, 5])
+@pytest.mark.parametrize("steps", [0, 1, 2, 3, 4, 5, 7, 8])
 def test_first_steps_match_oracle(dev, steps, variant):
-    """Fixed step counts (tol = 0): iterate and history after k steps, tight."""
+    """Fixed step counts (tol = 0): iterate and history after k steps, tight.
+    The interleaved loop applies the x updates every fourth step, so these
+    counts stop it with 1, 2, 3 and 4 updates pending."""
     w = W.make_workload(4, scale_xy=(70, 45), nz=40)
     res, xg, ref = _solve_both(w.problem, w.rhs, 0.0, steps, dev, variant)
     assert res["status"] == ref["status"] == 1
@@ -291,17 +293,18 @@ def test_profile_counts_launches(dev):
         ms_p, n_p = mf.pcg_profile_read(h, mf.PCG_KID_FUSED_PREC)
         ms_s, n_s = mf.pcg_profile_read(h, mf.PCG_KID_FUSED_SPMV)
         assert res["iters"] == 7
-        assert n_p == 8 and n_s == 7     # the last stencil pass (x update only) is not counted
+        assert n_p == 8 and n_s == 7     # the last stencil pass (launched before the stop test was read) is not counted
         assert ms_p > 0 and ms_s > 0 and math.isfinite(ms_p + ms_s)
         mf.pcg_profile_reset(h)
         assert mf.pcg_profile_read(h, mf.PCG_KID_FUSED_PREC) == (0.0, 0)
-        # sampled: the passes of steps k with k mod 4 < 2 only (k = 0, 1, 4, 5)
-        mf.pcg_profile_enable(h, 4)
+        # sampled: the passes of steps k with k mod 8 < 4 only (k = 0..3, 8..11;
+        # the stencil pass of the last step, k = 11, is not counted)
+        mf.pcg_profile_enable(h, 8)
         xd.zero_()
-        res = mf.pcg_solve(h, bd, xd, 0.0, 7)
+        res = mf.pcg_solve(h, bd, xd, 0.0, 11)
         _, n_p = mf.pcg_profile_read(h, mf.PCG_KID_FUSED_PREC)
         _, n_s = mf.pcg_profile_read(h, mf.PCG_KID_FUSED_SPMV)
-        assert (n_p, n_s) == (4, 4), (n_p, n_s)
+        assert (n_p, n_s) == (8, 7), (n_p, n_s)
         with pytest.raises(mf.PcgError):
             mf.pcg_profile_enable(h, -1)
     finally:

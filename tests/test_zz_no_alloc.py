@@ -48,7 +48,7 @@ def test_static_solve_matches_workspace_solve_twice():
 def test_static_solve_refuses_grids_beyond_the_array():
     import torch
     dev = require_gpu()
-    prob = W.config_problem(2, (512, 512), 64)   # 16.8 M points: 5 vectors > 64 MiB
+    prob = W.config_problem(2, (512, 512), 64)   # 16.8 M points: 7 vectors > 64 MiB
     h = mf.pcg_create(prob)
     try:
         b = torch.zeros(h.n, dtype=torch.float64, device=dev)
