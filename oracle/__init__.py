@@ -100,7 +100,7 @@ class Oracle:
         lib.orc_mg_coarsen.restype = i
         lib.orc_mg_num_levels.argtypes = [i, i, i]
         lib.orc_mg_num_levels.restype = i
-        mg = [i, d, i, i]
+        mg = [i, d, i, i, d]
         lib.orc_mg_vcycle.argtypes = gen + mg + [dp, dp]
         lib.orc_mg_vcycle.restype = i
         lib.orc_pcg_mg.argtypes = gen + mg + [dp, dp, d, i, dp, ip]
@@ -263,19 +263,20 @@ class Oracle:
         return self.lib.orc_mg_num_levels(int(nx), int(ny), int(max_levels))
 
     def mg_vcycle(self, gp, r, nu: int = 1, omega: float = 0.8, max_levels: int = 0,
-                  coarse_sweeps: int = 2) -> np.ndarray:
-        """z = B r: one V(nu, nu) cycle of the multigrid hierarchy."""
+                  coarse_sweeps: int = 2, coarse_lo: float = 0.0) -> np.ndarray:
+        """z = B r: one V(nu, nu) cycle of the multigrid hierarchy (coarse_lo > 0:
+        Chebyshev-accelerated coarsest sweeps on [coarse_lo, 2])."""
         r = self._field(r, gp)
         args, keep = self._gen_args(gp)
         z = np.empty_like(r)
         st = self.lib.orc_mg_vcycle(*args, int(nu), float(omega), int(max_levels), int(coarse_sweeps),
-                                    _ptr(r), _ptr(z))
+                                    float(coarse_lo), _ptr(r), _ptr(z))
         if st != OK:
             raise FloatingPointError(f"V-cycle failed ({st})")
         return z
 
     def pcg_mg(self, gp, b, x0=None, tol: float = 1e-10, maxit: int = 500, nu: int = 1,
-               omega: float = 0.8, max_levels: int = 0, coarse_sweeps: int = 2):
+               omega: float = 0.8, max_levels: int = 0, coarse_sweeps: int = 2, coarse_lo: float = 0.0):
         """Textbook PCG with one V-cycle per step.  Returns dict(x, iters, hist, status)."""
         b = self._field(b, gp)
         x = np.zeros_like(b) if x0 is None else self._field(x0, gp).copy()
@@ -283,7 +284,8 @@ class Oracle:
         hist = np.zeros(max(1, maxit + 1))
         iters = ctypes.c_int(0)
         st = self.lib.orc_pcg_mg(*args, int(nu), float(omega), int(max_levels), int(coarse_sweeps),
-                                 _ptr(b), _ptr(x), float(tol), int(maxit), _ptr(hist), ctypes.byref(iters))
+                                 float(coarse_lo), _ptr(b), _ptr(x), float(tol), int(maxit), _ptr(hist),
+                                 ctypes.byref(iters))
         return dict(x=x, iters=iters.value, hist=hist[: iters.value + 1].copy(), status=st)
 
     def dot(self, a, b) -> float:
@@ -388,9 +390,9 @@ def mg_num_levels(nx, ny, max_levels=0):
     return default().mg_num_levels(nx, ny, max_levels)
 
 
-def mg_vcycle(gp, r, nu=1, omega=0.8, max_levels=0, coarse_sweeps=2):
-    return default().mg_vcycle(gp, r, nu, omega, max_levels, coarse_sweeps)
+def mg_vcycle(gp, r, nu=1, omega=0.8, max_levels=0, coarse_sweeps=2, coarse_lo=0.0):
+    return default().mg_vcycle(gp, r, nu, omega, max_levels, coarse_sweeps, coarse_lo)
 
 
-def pcg_mg(gp, b, x0=None, tol=1e-10, maxit=500, nu=1, omega=0.8, max_levels=0, coarse_sweeps=2):
-    return default().pcg_mg(gp, b, x0, tol, maxit, nu, omega, max_levels, coarse_sweeps)
+def pcg_mg(gp, b, x0=None, tol=1e-10, maxit=500, nu=1, omega=0.8, max_levels=0, coarse_sweeps=2, coarse_lo=0.0):
+    return default().pcg_mg(gp, b, x0, tol, maxit, nu, omega, max_levels, coarse_sweeps, coarse_lo)

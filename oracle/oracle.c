@@ -670,7 +670,16 @@ done:
  *    z <- z + omega M^{-1} (f - A z);
  *  - cycle: V(nu, nu): nu sweeps from z = 0, the coarse correction, nu
  *    sweeps; on the coarsest level z = M^{-1} f when it is one column (exact,
- *    its edges being zero), else coarse_sweeps sweeps from z = 0.
+ *    its edges being zero), else coarse_sweeps sweeps from z = 0;
+ *  - coarsest sweeps: with coarse_lo = 0 the damped sweeps above; with
+ *    coarse_lo > 0 the same sweeps accelerated by Chebyshev polynomials on
+ *    the interval [coarse_lo, 2] (Chebyshev semi-iteration, Golub and Varga
+ *    1961; Saad, Iterative Methods for Sparse Linear Systems, 2nd ed., 12.3).
+ *    The eigenvalues of M^{-1} A lie in (0, 2) here (M + N is diagonally
+ *    dominant when A = M - N, N >= 0 holding the couplings between
+ *    columns), so with the upper end 2 the result is q(M^{-1} A) M^{-1} f
+ *    for a polynomial q that is positive on the whole spectrum, whatever
+ *    coarse_lo: a symmetric positive definite coarse solve.
  * ====================================================================== */
 
 /* Coarsening factors of an nx x ny level (1 or 2 each); 0 if neither
@@ -805,9 +814,55 @@ static int mg_smooth(const mg_level *L, int nz, const double *a, const double *d
     return ORC_OK;
 }
 
+/* The coarsest level with coarse_lo > 0: m = coarse_sweeps steps of the
+ * Chebyshev semi-iteration for M^{-1} A z = M^{-1} f from z_0 = 0 on the
+ * interval [lo, hi] = [coarse_lo, 2] (readings above).  With
+ * theta = (hi + lo) / 2, delta = (hi - lo) / 2, s = theta / delta:
+ *   z_1 = M^{-1} f / theta,  rho_0 = 1 / s,
+ *   rho_k = 1 / (2 s - rho_{k-1}),
+ *   z_{k+1} = z_k + rho_k rho_{k-1} (z_k - z_{k-1})
+ *             + (2 rho_k / delta) M^{-1} (f - A z_k),   k = 1 .. m-1.
+ * The residual f - A z_k is formed afresh at every step. */
+static int mg_chebyshev(const mg_level *L, int nz, const double *a, const double *d, const double *beta,
+                        int m, double lo, const double *f, double *z)
+{
+    const size_t n = (size_t)L->nx * L->ny * nz;
+    const double hi = 2.0;
+    const double theta = 0.5 * (hi + lo), delta = 0.5 * (hi - lo), s = theta / delta;
+    if (orc_precond_gen(L->nx, L->ny, nz, a, d, beta, L->area, L->ax, L->ay, f, L->y) != ORC_OK)
+        return ORC_ERR_BREAKDOWN;
+    for (size_t l = 0; l < n; ++l)
+        z[l] = L->y[l] / theta;
+    if (m < 2)
+        return ORC_OK;
+    double *zold = (double *)calloc(n, sizeof(double));   /* z_{k-1}; z_0 = 0 */
+    double *znew = (double *)malloc(n * sizeof(double));
+    if (!zold || !znew) { free(zold); free(znew); return ORC_ERR_INVALID; }
+    int st = ORC_OK;
+    double rho_prev = 1.0 / s;
+    for (int k = 1; k < m; ++k) {
+        const double rho = 1.0 / (2.0 * s - rho_prev);
+        orc_apply_A_gen(L->nx, L->ny, nz, a, d, beta, L->area, L->ax, L->ay, z, L->t);
+        for (size_t l = 0; l < n; ++l)
+            L->t[l] = f[l] - L->t[l];
+        if (orc_precond_gen(L->nx, L->ny, nz, a, d, beta, L->area, L->ax, L->ay, L->t, L->y) != ORC_OK) {
+            st = ORC_ERR_BREAKDOWN;
+            break;
+        }
+        for (size_t l = 0; l < n; ++l)
+            znew[l] = (z[l] + (rho * rho_prev) * (z[l] - zold[l])) + (2.0 * rho / delta) * L->y[l];
+        memcpy(zold, z, n * sizeof(double));
+        memcpy(z, znew, n * sizeof(double));
+        rho_prev = rho;
+    }
+    free(zold);
+    free(znew);
+    return st;
+}
+
 /* z = B_l f: one V(nu, nu) cycle from level l down (readings above). */
 static int mg_vcycle(const mg_level *lv, int nlev, int l, int nz, const double *a, const double *d,
-                     const double *beta, int nu, double omega, int coarse_sweeps,
+                     const double *beta, int nu, double omega, int coarse_sweeps, double coarse_lo,
                      const double *f, double *z)
 {
     const mg_level *L = &lv[l];
@@ -817,6 +872,8 @@ static int mg_vcycle(const mg_level *lv, int nlev, int l, int nz, const double *
     if (l == nlev - 1) {
         if (nx * ny == 1)
             return orc_precond_gen(nx, ny, nz, a, d, beta, L->area, L->ax, L->ay, f, z);
+        if (coarse_lo > 0.0)
+            return mg_chebyshev(L, nz, a, d, beta, coarse_sweeps, coarse_lo, f, z);
         for (int s = 0; s < coarse_sweeps; ++s)
             if (mg_smooth(L, nz, a, d, beta, omega, f, z) != ORC_OK)
                 return ORC_ERR_BREAKDOWN;
@@ -836,7 +893,7 @@ static int mg_vcycle(const mg_level *lv, int nlev, int l, int nz, const double *
         for (int k = 0; k < nz; ++k)
             for (int i = 0; i < nx; ++i)
                 C->f[at(C->nx, nz, i / fx, j / fy, k)] += L->t[at(nx, nz, i, j, k)];
-    if (mg_vcycle(lv, nlev, l + 1, nz, a, d, beta, nu, omega, coarse_sweeps, C->f, C->z) != ORC_OK)
+    if (mg_vcycle(lv, nlev, l + 1, nz, a, d, beta, nu, omega, coarse_sweeps, coarse_lo, C->f, C->z) != ORC_OK)
         return ORC_ERR_BREAKDOWN;
     /* z += P z_c */
     for (int j = 0; j < ny; ++j)
@@ -852,13 +909,13 @@ static int mg_vcycle(const mg_level *lv, int nlev, int l, int nz, const double *
 /* z = B r, one V-cycle of the hierarchy of the general operator. */
 int orc_mg_vcycle(int nx, int ny, int nz, const double *a, const double *d, const double *beta,
                   const double *area, const double *ax, const double *ay, int nu, double omega,
-                  int max_levels, int coarse_sweeps, const double *r, double *z)
+                  int max_levels, int coarse_sweeps, double coarse_lo, const double *r, double *z)
 {
     int nlev = 0;
     mg_level *lv = mg_build(nx, ny, nz, area, ax, ay, max_levels, &nlev);
     if (!lv)
         return ORC_ERR_INVALID;
-    int st = mg_vcycle(lv, nlev, 0, nz, a, d, beta, nu, omega, coarse_sweeps, r, z);
+    int st = mg_vcycle(lv, nlev, 0, nz, a, d, beta, nu, omega, coarse_sweeps, coarse_lo, r, z);
     mg_free(lv, nlev);
     return st;
 }
@@ -866,7 +923,7 @@ int orc_mg_vcycle(int nx, int ny, int nz, const double *a, const double *d, cons
 /* Textbook PCG (as orc_pcg_gen) with one V-cycle as the preconditioner. */
 int orc_pcg_mg(int nx, int ny, int nz, const double *a, const double *d, const double *beta,
                const double *area, const double *ax, const double *ay, int nu, double omega,
-               int max_levels, int coarse_sweeps, const double *b, double *x, double tol, int maxit,
+               int max_levels, int coarse_sweeps, double coarse_lo, const double *b, double *x, double tol, int maxit,
                double *hist, int *iters_out)
 {
     size_t n = (size_t)nx * ny * nz;
@@ -889,7 +946,7 @@ int orc_pcg_mg(int nx, int ny, int nz, const double *a, const double *d, const d
     hist[0] = R0;
     if (!isfinite(R0)) { status = ORC_ERR_BREAKDOWN; goto done; }
     if (R0 == 0.0) { status = ORC_OK; goto done; }
-    if (mg_vcycle(lv, nlev, 0, nz, a, d, beta, nu, omega, coarse_sweeps, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+    if (mg_vcycle(lv, nlev, 0, nz, a, d, beta, nu, omega, coarse_sweeps, coarse_lo, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
     memcpy(p, z, sizeof(double) * n);
     double rho = orc_dot(n, r, z);
     if (!(rho > 0.0) || !isfinite(rho)) { status = ORC_ERR_BREAKDOWN; goto done; }
@@ -906,7 +963,7 @@ int orc_pcg_mg(int nx, int ny, int nz, const double *a, const double *d, const d
         if (!isfinite(R)) { status = ORC_ERR_BREAKDOWN; goto done; }
         if (R == 0.0 || R / R0 < tol) { status = ORC_OK; goto done; }
         if (k == maxit) break;
-        if (mg_vcycle(lv, nlev, 0, nz, a, d, beta, nu, omega, coarse_sweeps, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
+        if (mg_vcycle(lv, nlev, 0, nz, a, d, beta, nu, omega, coarse_sweeps, coarse_lo, r, z) != ORC_OK) { status = ORC_ERR_BREAKDOWN; goto done; }
         double rho_new = orc_dot(n, r, z);
         if (!(rho_new > 0.0) || !isfinite(rho_new)) { status = ORC_ERR_BREAKDOWN; goto done; }
         double beta_cg = rho_new / rho;

@@ -699,7 +699,22 @@ def dense_vcycle(orc, gp):
     return B
 
 
-def textbook_vcycle(A, nx, ny, nz, nu, omega, max_levels, cs, level=0):
+def chebyshev_error(K, m, lo, hi=2.0):
+    """The error operator of m Chebyshev steps on [lo, hi] for K z = g from
+    z = 0: T_m(X) / T_m(s) with X = (hi + lo - 2 K) / (hi - lo) and
+    s = (hi + lo) / (hi - lo), the Chebyshev polynomial of the first kind by
+    its own recurrence T_{k+1} = 2 X T_k - T_{k-1} (dense)."""
+    n = K.shape[0]
+    I = np.eye(n)
+    X = ((hi + lo) * I - 2.0 * K) / (hi - lo)
+    s = (hi + lo) / (hi - lo)
+    Tm1, T = I, X
+    for _ in range(m - 1):
+        Tm1, T = T, 2.0 * X @ T - Tm1
+    return T / math.cosh(m * math.acosh(s))
+
+
+def textbook_vcycle(A, nx, ny, nz, nu, omega, max_levels, cs, level=0, coarse_lo=0.0):
     """B of the V-cycle from the recursion of its error operator (dense)."""
     n = A.shape[0]
     I = np.eye(n)
@@ -710,11 +725,14 @@ def textbook_vcycle(A, nx, ny, nz, nu, omega, max_levels, cs, level=0):
     if last:
         if nx * ny == 1:
             return np.linalg.inv(M)
-        E = np.linalg.matrix_power(S, cs)
+        if coarse_lo > 0.0:
+            E = chebyshev_error(np.linalg.solve(M, A), cs, coarse_lo)
+        else:
+            E = np.linalg.matrix_power(S, cs)
     else:
         ncx, ncy = nx // fx, ny // fy
         P = prolongation(nx, ny, nz, ncx, ncy)
-        Bc = textbook_vcycle(P.T @ A @ P, ncx, ncy, nz, nu, omega, max_levels, cs, level + 1)
+        Bc = textbook_vcycle(P.T @ A @ P, ncx, ncy, nz, nu, omega, max_levels, cs, level + 1, coarse_lo)
         Sn = np.linalg.matrix_power(S, nu)
         E = Sn @ (I - P @ Bc @ P.T @ A) @ Sn
     return np.linalg.solve(A.T, (I - E).T).T
@@ -792,9 +810,70 @@ def pin_m5_convergence(orc):
     assert err <= 1e-8, ("M5 solution", err)
 
 
+def pin_m6_chebyshev_coarsest(orc):
+    """The V-cycle whose coarsest level takes Chebyshev-accelerated sweeps
+    (coarse_lo > 0) equals the textbook recursion with the Chebyshev
+    polynomial's error operator on that level: one level alone (the whole
+    solve is the Chebyshev iteration) and inside hierarchies."""
+    cases = [((4, 3, 3), dict(nu=1, omega=0.8, max_levels=1, coarse_sweeps=1, coarse_lo=0.1)),
+             ((4, 3, 3), dict(nu=1, omega=0.8, max_levels=1, coarse_sweeps=2, coarse_lo=0.05)),
+             ((2, 5, 2), dict(nu=1, omega=0.8, max_levels=1, coarse_sweeps=5, coarse_lo=0.02)),
+             ((6, 4, 2), dict(nu=1, omega=0.8, max_levels=1, coarse_sweeps=9, coarse_lo=0.3)),
+             ((4, 4, 3), dict(nu=1, omega=0.9, max_levels=2, coarse_sweeps=6, coarse_lo=0.05)),
+             ((8, 4, 2), dict(nu=2, omega=0.7, max_levels=3, coarse_sweeps=4, coarse_lo=0.02))]
+    for (nx, ny, nz), mg in cases:
+        gp = random_general(nx, ny, nz, seed=3 * nx + 5 * ny + nz, az_scale=5.0)
+        gp.mg = mg
+        B = dense_vcycle(orc, gp)
+        A = dense_from_apply_gen(orc, gp)
+        Bt = textbook_vcycle(A, nx, ny, nz, mg["nu"], mg["omega"], mg["max_levels"], mg["coarse_sweeps"],
+                             coarse_lo=mg["coarse_lo"])
+        err = np.abs(B - Bt).max() / np.abs(Bt).max()
+        assert err <= 1e-10, ("M6", (nx, ny, nz), mg, err)
+
+
+def pin_m7_chebyshev_bounds(orc):
+    """The reading behind the upper end 2: the column smoother's M^{-1} A has
+    its eigenvalues in (0, 2) (on random operators and on their Galerkin
+    coarse operators); with it the Chebyshev coarsest solve keeps B symmetric
+    positive definite whatever coarse_lo, and m steps reduce the A-norm error
+    by at least 1 / T_m((2 + lo) / (2 - lo)) when lo is at or below the
+    smallest eigenvalue."""
+    for (nx, ny, nz) in [(4, 6, 3), (6, 4, 2), (8, 2, 3), (3, 5, 4)]:
+        gp = random_general(nx, ny, nz, seed=7 * nx + ny, az_scale=20.0)
+        for g in (gp, orc.mg_coarsen(gp)):
+            if g is None:
+                continue
+            A = dense_from_apply_gen(orc, g)
+            lam = np.linalg.eigvals(np.linalg.solve(column_blocks(A, g.nx, g.ny, g.nz), A)).real
+            assert 0.0 < lam.min() and lam.max() < 2.0, ("M7 spectrum", (g.nx, g.ny), lam.min(), lam.max())
+    for (nx, ny, nz), mg in [((4, 6, 3), dict(nu=1, omega=0.9, max_levels=2, coarse_sweeps=5, coarse_lo=0.9)),
+                             ((6, 4, 2), dict(nu=1, omega=0.8, max_levels=0, coarse_sweeps=3, coarse_lo=1e-4)),
+                             ((4, 4, 2), dict(nu=1, omega=0.5, max_levels=2, coarse_sweeps=16, coarse_lo=0.02))]:
+        gp = random_general(nx, ny, nz, seed=nx + 3 * ny, az_scale=20.0)
+        gp.mg = mg
+        B = dense_vcycle(orc, gp)
+        A = dense_from_apply_gen(orc, gp)
+        assert np.abs(B - B.T).max() <= 1e-12 * np.abs(B).max(), ("M7 symmetry", mg)
+        assert np.linalg.eigvalsh(0.5 * (B + B.T)).min() > 0.0, ("M7 definite", mg)
+    gp = random_general(6, 4, 3, seed=41, az_scale=20.0)
+    A = dense_from_apply_gen(orc, gp)
+    lam = np.linalg.eigvals(np.linalg.solve(column_blocks(A, 6, 4, 3), A)).real
+    lo = 0.95 * lam.min()
+    f = _rand((4, 3, 6), 93)
+    xs = np.linalg.solve(A, f.ravel())
+    for m in (3, 8, 20):
+        z = orc.mg_vcycle(gp, f, nu=1, omega=0.8, max_levels=1, coarse_sweeps=m, coarse_lo=lo).ravel()
+        e, e0 = z - xs, xs
+        ratio = math.sqrt(e @ (A @ e)) / math.sqrt(e0 @ (A @ e0))
+        bound = 1.0 / math.cosh(m * math.acosh((2.0 + lo) / (2.0 - lo)))
+        assert ratio <= bound * (1.0 + 1e-6) + 1e-13, ("M7 Chebyshev bound", m, ratio, bound)
+
+
 ALL_PINS = [pin_k1_eigenmodes, pin_k2_constants, pin_k3_no_horizontal, pin_k4_symmetry_energy,
             pin_k5_column_block, pin_k6_cholesky, pin_k7_finite_termination, pin_k8_invariants,
             pin_k9_manufactured, pin_stop_rule_and_breakdown, pin_d1_dot, pin_f1_stencil_f32, pin_f2_precond_f32,
             pin_f3_dot_f32, pin_f4_pcg_f32, pin_f5_pcg_mixed, pin_g1_special_case, pin_g2_eigenmodes,
             pin_g3_constants, pin_g4_symmetry_energy, pin_g5_column_block_cholesky, pin_m1_galerkin,
-            pin_m2_coarse_space, pin_m3_textbook_recursion, pin_m4_spd, pin_m5_convergence]
+            pin_m2_coarse_space, pin_m3_textbook_recursion, pin_m4_spd, pin_m5_convergence,
+            pin_m6_chebyshev_coarsest, pin_m7_chebyshev_bounds]

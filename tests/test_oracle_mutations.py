@@ -67,6 +67,14 @@ MUTATIONS = {
     for (int s = 0; s < 0; ++s)"""),
     "mg_coarsest_not_exact": ("        if (nx * ny == 1)\n            return orc_precond_gen(",
                               "        if (nx * ny == 0)\n            return orc_precond_gen("),
+    "mg_cheb_momentum_sign": ("znew[l] = (z[l] + (rho * rho_prev) * (z[l] - zold[l]))",
+                              "znew[l] = (z[l] - (rho * rho_prev) * (z[l] - zold[l]))"),
+    "mg_cheb_rho_recurrence": ("const double rho = 1.0 / (2.0 * s - rho_prev);",
+                               "const double rho = 1.0 / (2.0 * s + rho_prev);"),
+    "mg_cheb_first_step_unscaled": ("        z[l] = L->y[l] / theta;", "        z[l] = L->y[l];"),
+    "mg_cheb_stale_residual": ("            L->t[l] = f[l] - L->t[l];\n        if (orc_precond_gen(L->nx, L->ny, nz, a, d, beta, L->area, L->ax, L->ay, L->t, L->y) != ORC_OK) {",
+                               "            L->t[l] = f[l];\n        if (orc_precond_gen(L->nx, L->ny, nz, a, d, beta, L->area, L->ax, L->ay, L->t, L->y) != ORC_OK) {"),
+    "mg_cheb_interval_width": ("theta = 0.5 * (hi + lo), delta = 0.5 * (hi - lo)", "theta = 0.5 * (hi + lo), delta = (hi - lo)"),
 }
 
 
