@@ -92,15 +92,19 @@ BYTES_BY_VARIANT = {"interleaved": (_bytes_interleaved, 82), "interleaved_no_q":
 # further one 24 (read f, z, write z: one pass forming the residual from z
 # and its neighbours), or 48 where the segments are longer than 8 levels
 # (nz > 128), which run it as a residual pass (read f, z, write w) and a
-# corrected column solve (read w, z, write z).
-def mg_cycle_bytes(level_points, k, nu=1, coarse_sweeps=0, two_pass_sweeps=False):
+# corrected column solve (read w, z, write z).  Chebyshev-accelerated
+# sweeps (chebyshev=True) also read z_{k-1} from the second one on: 32 (56).
+def mg_cycle_bytes(level_points, k, nu=1, coarse_sweeps=0, two_pass_sweeps=False, chebyshev=False):
     if nu != 1:
         raise ValueError("the byte model covers V(1,1) cycles")
     tot = 0
     for l, nl in enumerate(level_points):
         nc = level_points[l + 1] if l + 1 < len(level_points) else 0
         if nc == 0:
-            tot += (16 + (48 if two_pass_sweeps else 24) * max(coarse_sweeps - 1, 0)) * nl
+            per = 48 if two_pass_sweeps else 24
+            further = max(coarse_sweeps - 1, 0)
+            extra = 8 * max(further - 1, 0) if chebyshev else 0
+            tot += (16 + per * further + extra) * nl
             continue
         first = 32 if (l == 0 and k > 0) else 16
         corr = 32 if l == 0 else 24
@@ -138,7 +142,7 @@ def standard_bytes(kind, iters, n):
     return tot * n
 
 
-def mg_pass_bytes(level_points, iters, coarse_sweeps=0, two_pass_sweeps=False, period=1):
+def mg_pass_bytes(level_points, iters, coarse_sweeps=0, two_pass_sweeps=False, period=1, chebyshev=False):
     """Total algorithmic bytes and count of the timed V-cycles (k = 0..K;
     with a profiling period P > 1 only those with k mod P < PROFILE_WINDOW)."""
     tot = cnt = 0
@@ -146,7 +150,8 @@ def mg_pass_bytes(level_points, iters, coarse_sweeps=0, two_pass_sweeps=False, p
         for k in range(K + 1):
             if period > 1 and k % period >= PROFILE_WINDOW:
                 continue
-            tot += mg_cycle_bytes(level_points, k, coarse_sweeps=coarse_sweeps, two_pass_sweeps=two_pass_sweeps)
+            tot += mg_cycle_bytes(level_points, k, coarse_sweeps=coarse_sweeps, two_pass_sweeps=two_pass_sweeps,
+                                  chebyshev=chebyshev)
             cnt += 1
     return tot, cnt
 
@@ -243,7 +248,9 @@ def parse():
     ap.add_argument("--mg-omega", type=float, default=0.9, help="mg: damping of the column smoother")
     ap.add_argument("--mg-levels", type=int, default=5,
                     help="mg: levels of the hierarchy (0: down to one column); 5 ends at 64x64 columns at 1024^2")
-    ap.add_argument("--mg-coarse-sweeps", type=int, default=64, help="mg: sweeps on the coarsest level")
+    ap.add_argument("--mg-coarse-sweeps", type=int, default=16, help="mg: sweeps on the coarsest level")
+    ap.add_argument("--mg-coarse-lo", type=float, default=0.02,
+                    help="mg: lower end of the Chebyshev interval [lo, 2] of the coarsest sweeps (0: damped sweeps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--cpu-steps-cfg5", type=int, default=1,
@@ -656,7 +663,8 @@ def main():
     level_points = None
     mg_params = None
     if args.variant == "mg":
-        mg_params = dict(nu=1, omega=args.mg_omega, max_levels=args.mg_levels, coarse_sweeps=args.mg_coarse_sweeps)
+        mg_params = dict(nu=1, omega=args.mg_omega, max_levels=args.mg_levels, coarse_sweeps=args.mg_coarse_sweeps,
+                         coarse_lo=args.mg_coarse_lo)
         mf.pcg_mg_setup(h, **mg_params)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t
@@ -667,6 +675,7 @@ def main():
         # sweeps on the coarsest level (0: one column, solved exactly)
         mg_cs = 0 if level_points[-1] == prob.nz else mg_params["coarse_sweeps"]
         mg_two = prob.nz > 128   # segments longer than 8 levels: two-pass sweeps
+        mg_cheb = mg_params["coarse_lo"] > 0.0
         ws = torch.empty(mf.pcg_mg_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
     else:
         ws = torch.empty(mf.pcg_solve_workspace_bytes(h, maxit), dtype=torch.uint8, device=dev)
@@ -709,7 +718,7 @@ def main():
             avg = ms / cnt
             ent = {"launches": cnt, "avg_ms": avg, "total_ms": ms}
             if name == "mg_vcycle":
-                tot, nl = mg_pass_bytes(level_points, iters, mg_cs, mg_two, PROFILE_PERIOD)
+                tot, nl = mg_pass_bytes(level_points, iters, mg_cs, mg_two, PROFILE_PERIOD, mg_cheb)
                 if nl != cnt:
                     raise SystemExit(f"{name}: {cnt} timed cycles, expected {nl}")
                 ent["bytes_per_launch"] = tot / nl
@@ -740,7 +749,7 @@ def main():
     # every timed pass's algorithmic bytes over the whole timed region
     if args.variant == "mg":
         all_bytes = (pass_bytes(args.variant, "fused_spmv", iters, n)[0]
-                     + mg_pass_bytes(level_points, iters, mg_cs, mg_two)[0])
+                     + mg_pass_bytes(level_points, iters, mg_cs, mg_two, chebyshev=mg_cheb)[0])
     elif args.variant == "standard":
         all_bytes = sum(standard_bytes(kind, iters, n) for kind in ("apply_A", "precond", "vector"))
     else:
@@ -797,8 +806,9 @@ def main():
         "hbm_frac_whole_solve": round(all_bytes / elapsed / 1e9 / HBM_PEAK_GBS, 4) if all_bytes else None,
         "bytes_per_point_per_iteration": (104 if args.variant == "standard" else
                                           (BYTES_BY_VARIANT[args.variant][1] if args.variant != "mg"
-                                           else round(52 + mg_cycle_bytes(level_points, 1, coarse_sweeps=mg_cs,
-                                                                          two_pass_sweeps=mg_two) / n, 2))
+                                           else round(50 + mg_cycle_bytes(level_points, 1, coarse_sweeps=mg_cs,
+                                                                          two_pass_sweeps=mg_two,
+                                                                          chebyshev=mg_cheb) / n, 2))
                                           if has_bytes else None),
         "kernels": kern,
         "roofline": roofline,

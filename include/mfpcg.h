@@ -266,13 +266,21 @@ int pcg_solve_no_q(pcg_handle *h, const double *b_dev, double *x_dev, double tol
  * column solve of eq. (19) as damped block Jacobi, z <- z + omega M^{-1}
  * (f - A z); the cycle is V(nu, nu) from z = 0; the coarsest level is solved
  * exactly by the column solve when it is one column, else by coarse_sweeps
- * sweeps from z = 0.  B (one cycle) is symmetric positive definite for
- * 0 < omega <= 1, so CG with B is PCG. */
+ * sweeps from z = 0.  With coarse_lo > 0 those sweeps are accelerated by
+ * Chebyshev polynomials on [coarse_lo, 2] (the Chebyshev semi-iteration of
+ * Golub and Varga; the eigenvalues of M^{-1} A lie in (0, 2) for these
+ * operators): z_1 = M^{-1} f / theta, then z_{k+1} = z_k + rho_k rho_{k-1}
+ * (z_k - z_{k-1}) + (2 rho_k / delta) M^{-1} (f - A z_k), theta and delta
+ * the interval's centre and half-width, rho_0 = delta / theta and
+ * rho_k = 1 / (2 theta / delta - rho_{k-1}).  B (one cycle) is symmetric
+ * positive definite for 0 < omega <= 1 and any coarse_lo, so CG with B is
+ * PCG. */
 typedef struct {
     int32_t nu;            /* sweeps before and after the coarse correction, 1..16 */
     double omega;          /* damping of the smoother, 0 < omega <= 1 */
     int32_t max_levels;    /* 0: as many levels as the grid allows; else 1..64 */
     int32_t coarse_sweeps; /* sweeps on a coarsest level of several columns, 1..1024 */
+    double coarse_lo;      /* 0: damped coarsest sweeps; in (0, 2): Chebyshev on [coarse_lo, 2] */
 } pcg_mg_params;
 
 /* Bytes of device memory the coarse levels' tables need for these

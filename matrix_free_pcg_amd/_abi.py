@@ -73,7 +73,7 @@ class pcg_coeffs_general(ctypes.Structure):
 
 class pcg_mg_params(ctypes.Structure):
     _fields_ = [("nu", ctypes.c_int32), ("omega", ctypes.c_double), ("max_levels", ctypes.c_int32),
-                ("coarse_sweeps", ctypes.c_int32)]
+                ("coarse_sweeps", ctypes.c_int32), ("coarse_lo", ctypes.c_double)]
 
 
 class pcg_coeffs(ctypes.Structure):
@@ -433,17 +433,18 @@ def pcg_solve_mixed(h: Handle, b, x, tol: float, maxit: int, workspace=None) -> 
 # ---- tensor-product multigrid preconditioner ----------------------------------
 
 def pcg_mg_setup_bytes(h: Handle, nu: int = 1, omega: float = 0.8, max_levels: int = 0,
-                       coarse_sweeps: int = 2) -> int:
-    p = pcg_mg_params(int(nu), float(omega), int(max_levels), int(coarse_sweeps))
+                       coarse_sweeps: int = 2, coarse_lo: float = 0.0) -> int:
+    p = pcg_mg_params(int(nu), float(omega), int(max_levels), int(coarse_sweeps), float(coarse_lo))
     return int(load().pcg_mg_setup_bytes(h.ptr, ctypes.byref(p)))
 
 
 def pcg_mg_setup(h: Handle, nu: int = 1, omega: float = 0.8, max_levels: int = 0,
-                 coarse_sweeps: int = 2) -> None:
+                 coarse_sweeps: int = 2, coarse_lo: float = 0.0) -> None:
     """Build the level hierarchy; its tables go to a (torch) device buffer
-    kept on the handle object."""
+    kept on the handle object.  coarse_lo > 0: Chebyshev-accelerated
+    coarsest sweeps on [coarse_lo, 2]."""
     import torch
-    p = pcg_mg_params(int(nu), float(omega), int(max_levels), int(coarse_sweeps))
+    p = pcg_mg_params(int(nu), float(omega), int(max_levels), int(coarse_sweeps), float(coarse_lo))
     need = int(load().pcg_mg_setup_bytes(h.ptr, ctypes.byref(p)))
     buf = torch.empty(max(need, 256), dtype=torch.uint8, device=torch.device("cuda", h.device))
     _check(h.ptr, load().pcg_mg_setup(h.ptr, ctypes.byref(p), buf.data_ptr(), _nbytes(buf)))

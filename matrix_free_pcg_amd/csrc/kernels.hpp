@@ -316,17 +316,37 @@ enum : int { UPD_NONE = 0, UPD_Q = 1, UPD_AP = 2 };
 //   MG_SWEEP  with UPD_AP: rr = rin - A q with q's neighbours read here (the
 //             recomputed-product path with alpha = 1), z = q + omega y: one
 //             whole sweep in one pass; no dot products
+//   MG_CHEB   MG_SWEEP with the Chebyshev three-term update of a coarsest
+//             level: z holds z_{k-1} on entry (read at the thread's own
+//             points only, before they are written) and receives
+//             (q + c1 (q - z_{k-1})) + c2 y; mg.cheb == 1: z_{k-1} = 0 (the
+//             buffer is not used)
 // P zc is the value of the coarse parent.  Binary64 only.  The dot products
 // of MG_CORR and MG_POST are <f, f> and <f, z> (f: the level's right-hand
-// side); in every MG form they are skipped when partials is null.
-enum : int { MG_NONE = 0, MG_FIRST = 1, MG_CORR = 2, MG_POST = 3, MG_SWEEP = 4 };
+// side); in every MG form they are skipped when partials is null.  MG_CORR
+// with mg.cheb != 0 takes MG_CHEB's update (z_{k-1} read from z at each
+// point before it is written).
+enum : int { MG_NONE = 0, MG_FIRST = 1, MG_CORR = 2, MG_POST = 3, MG_SWEEP = 4, MG_CHEB = 5 };
+
+// The one-pass sweep forms (the residual formed from q and its neighbours).
+template <int MG>
+constexpr bool kSweepForm = MG == MG_SWEEP || MG == MG_CHEB;
 
 struct MgArgs {
     const double *zc;   // coarse correction (coarse layout), or null
     const double *f;    // the level's right-hand side (dot products of MG_CORR, MG_POST)
     double omega;       // damping of the smoother
     int ncx, fx, fy;    // coarse row length, coarsening factors in i and j
+    double c1, c2;      // Chebyshev step: z_{k+1} = (z_k + c1 (z_k - z_{k-1})) + c2 M^{-1} (f - A z_k)
+    int cheb;           // 0: the damped update; 1: Chebyshev, z_{k-1} = 0; 2: Chebyshev
 };
+
+// The Chebyshev three-term update of MG_CHEB and MG_CORR with mg.cheb != 0.
+__device__ __forceinline__ double cheb_update(const MgArgs &mg, double zk, double zold, double y)
+{
+    const double zo = mg.cheb == 2 ? zold : 0.0;
+    return (zk + mg.c1 * (zk - zo)) + mg.c2 * y;
+}
 
 // Where a column pass reads its residual.  The pointer arguments of the
 // column kernels are restrict-qualified, so no two of them may name the same
@@ -337,7 +357,7 @@ struct MgArgs {
 template <int UPD, int MG, typename TV, typename TZ>
 __device__ __forceinline__ const TV *residual_source(const TV *rin, TV *rout, TZ *)
 {
-    if constexpr (MG != MG_SWEEP && UPD != UPD_NONE)
+    if constexpr (!kSweepForm<MG> && UPD != UPD_NONE)
         return rout;
     else
         return rin;
@@ -367,10 +387,10 @@ __global__ __launch_bounds__((col_bound<C, MG>())) void k_column_solve(
     static_assert((UPD != UPD_AP && !STORED) ||
                       (std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
                   "the stored-matrix and recomputed-Ap forms are binary64 only");
-    static_assert(MG == MG_NONE || ((UPD != UPD_AP || MG == MG_SWEEP) && !STORED &&
+    static_assert(MG == MG_NONE || ((UPD != UPD_AP || kSweepForm<MG>) && !STORED &&
                                     std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
                   "the multigrid forms are binary64 only");
-    static_assert(MG != MG_SWEEP || UPD == UPD_AP, "MG_SWEEP forms its residual on the recomputed-product path");
+    static_assert(!kSweepForm<MG> || UPD == UPD_AP, "MG_SWEEP forms its residual on the recomputed-product path");
     static_assert(MG != MG_POST || UPD == UPD_NONE, "MG_POST reads its residual as it is");
     __shared__ TZ sh_a[kMaxThreads];
     __shared__ TZ sh_b[kMaxThreads];
@@ -396,7 +416,7 @@ __global__ __launch_bounds__((col_bound<C, MG>())) void k_column_solve(
     const int len = active ? min(L, o.nz - k0) : 0;
     const size_t base = lin(o, ic, j, 0);
     const size_t ks = (size_t)o.nx;
-    const TV alpha = MG == MG_SWEEP ? (TV)1 : ((UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0);
+    const TV alpha = kSweepForm<MG> ? (TV)1 : ((UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0);
     // the Thomas multiplier at the segment's lower boundary (set-up table),
     // requested before the segment's other loads
     const TZ phi_in = (s > 0 && active)
@@ -467,8 +487,9 @@ __global__ __launch_bounds__((col_bound<C, MG>())) void k_column_solve(
     auto d_at = [&](int t) -> double {
         if constexpr (kPre) return ldv[t]; else return o.lev_d[k0 + t];
     };
-    double zsw[MG == MG_SWEEP ? L : 1];   // MG_SWEEP: the iterate at the column's levels
-    if constexpr (MG == MG_SWEEP) {
+    double zsw[kSweepForm<MG> ? L : 1];   // MG_SWEEP, MG_CHEB: the iterate at the column's levels
+    double zo[MG == MG_CHEB ? L : 1];     // MG_CHEB: z_{k-1} at the column's levels
+    if constexpr (kSweepForm<MG>) {
 #pragma unroll
         for (int t = 0; t < L; ++t)
             zsw[t] = 0.0;
@@ -496,6 +517,11 @@ __global__ __launch_bounds__((col_bound<C, MG>())) void k_column_solve(
 #pragma unroll
             for (int t = 0; t < L; ++t)
                 ra[t] = ld_s(rsrc + base + (size_t)min(k0 + t, o.nz - 1) * ks);
+        }
+        if constexpr (MG == MG_CHEB) {   // z_{k-1}, with the operands (used only when mg.cheb == 2)
+#pragma unroll
+            for (int t = 0; t < L; ++t)
+                zo[t] = ld_s(z + base + (size_t)min(k0 + t, o.nz - 1) * ks);
         }
         if (do_ap) {
 #pragma unroll
@@ -531,7 +557,7 @@ __global__ __launch_bounds__((col_bound<C, MG>())) void k_column_solve(
                                                       pym[t], pyp[t], pv[t], pv[t + 2]);
                 if (ok)
                     v = v - alpha * Ap;
-                if constexpr (MG == MG_SWEEP)
+                if constexpr (kSweepForm<MG>)
                     zsw[t] = pc;
             }
             rr[t] = v;
@@ -629,7 +655,7 @@ __global__ __launch_bounds__((col_bound<C, MG>())) void k_column_solve(
             r2 += (double)v * (double)v;
         }
     }
-    if (MG != MG_SWEEP && UPD != UPD_NONE && !first && ok) {
+    if (!kSweepForm<MG> && UPD != UPD_NONE && !first && ok) {
 #pragma unroll
         for (int t = 0; t < L; ++t)
             if (t < len)
@@ -720,6 +746,8 @@ __global__ __launch_bounds__((col_bound<C, MG>())) void k_column_solve(
                 zv = (TZ)mg.omega * zv;
             if constexpr (MG == MG_SWEEP)
                 zv = zsw[t] + mg.omega * zv;
+            if constexpr (MG == MG_CHEB)
+                zv = cheb_update(mg, zsw[t], zo[t], zv);
             if constexpr (MG == MG_CORR || MG == MG_POST) {
                 // the iterate (plus the coarse correction) and f, loaded here,
                 // after the solve, to keep the registers of the sweep low
@@ -727,7 +755,10 @@ __global__ __launch_bounds__((col_bound<C, MG>())) void k_column_solve(
                 double zq = ok ? ld_s(q + l) : 0.0;
                 if constexpr (MG == MG_POST)
                     zq = zq + mg.zc[mg_parent(mg, o.nz, ic, j, k0 + t)];
-                zv = zq + mg.omega * zv;
+                if (MG == MG_CORR && mg.cheb != 0)
+                    zv = cheb_update(mg, zq, (ok && mg.cheb == 2) ? ld_s(z + l) : 0.0, zv);
+                else
+                    zv = zq + mg.omega * zv;
                 const double fv = (ok && partials) ? ld_s(mg.f + l) : 0.0;
                 kap += fv * zv;
                 r2mg += fv * fv;
@@ -786,10 +817,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     const TV *rsrc = residual_source<UPD, MG>(rin, rout, z);
     static_assert(UPD != UPD_AP || (std::is_same<TV, double>::value && std::is_same<TZ, double>::value),
                   "the recomputed-Ap form is binary64 only");
-    static_assert(MG == MG_NONE || ((UPD != UPD_AP || MG == MG_SWEEP) && std::is_same<TV, double>::value &&
+    static_assert(MG == MG_NONE || ((UPD != UPD_AP || kSweepForm<MG>) && std::is_same<TV, double>::value &&
                                     std::is_same<TZ, double>::value),
                   "the multigrid forms are binary64 only");
-    static_assert(MG != MG_SWEEP || UPD == UPD_AP, "MG_SWEEP forms its residual on the recomputed-product path");
+    static_assert(!kSweepForm<MG> || UPD == UPD_AP, "MG_SWEEP forms its residual on the recomputed-product path");
     static_assert(MG != MG_POST || UPD == UPD_NONE, "MG_POST reads its residual as it is");
     constexpr int kSeg = kMaxThreads / kWave;
     __shared__ Pair<TZ> sh_ab[kMaxThreads];
@@ -811,14 +842,15 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
     const unsigned cv = (unsigned)i * (unsigned)sizeof(TV);   // lane's byte offset in a TV row
     const unsigned cz = (unsigned)i * (unsigned)sizeof(TZ);   // ... in a TZ row
     const size_t row0 = ((size_t)j * o.nz + k0) * nx;   // level k0 of row j (uniform)
-    const TV alpha = MG == MG_SWEEP ? (TV)1 : ((UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0);
+    const TV alpha = kSweepForm<MG> ? (TV)1 : ((UPD != UPD_NONE && !first) ? (TV)st->alpha : (TV)0);
     const double *az = o.az + k0;                       // az[t]: face below level k0+t
     // area-scaled vertical couplings: vz(t) couples levels k0+t-1 and k0+t
     auto vz = [&](int t) -> TZ { return fz.area * (TZ)az[t]; };
 
     TV rr[L];
     double r2 = 0.0;
-    double zsw[MG == MG_SWEEP ? L : 1];   // MG_SWEEP: the iterate at the column's levels
+    double zsw[kSweepForm<MG> ? L : 1];   // MG_SWEEP, MG_CHEB: the iterate at the column's levels
+    double zo[MG == MG_CHEB ? L : 1];     // MG_CHEB: z_{k-1} at the column's levels
     if constexpr (UPD == UPD_Q && L == 16) {
         // q is requested on the first step too (its buffer exists; the
         // values are not used then): a branch on `first` here would split
@@ -862,6 +894,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
         pv[L + 1] = ld_at(q + row0 + (size_t)ka * nx, cv);
 #pragma unroll
         for (int t = 0; t < L; ++t) {
+            if constexpr (MG == MG_CHEB)   // z_{k-1} (used only when mg.cheb == 2)
+                zo[t] = ld_at(z + row0 + (size_t)t * nx, cz);
             rr[t] = ld_at(rsrc + row0 + (size_t)t * nx, cv);
             pv[t + 1] = ld_at(q + row0 + (size_t)t * nx, cv);
             pyp[t] = ld_at(q + rowp + (size_t)t * nx, cv);
@@ -879,7 +913,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
                                                   fc.area * az[t], fc.area * az[t + 1], pc, pl, pr, pym[t],
                                                   pyp[t], pv[t], pv[t + 2]);
             rr[t] = rr[t] - alpha * Ap;
-            if constexpr (MG == MG_SWEEP)
+            if constexpr (kSweepForm<MG>)
                 zsw[t] = pc;
         }
     } else if constexpr (MG == MG_POST) {
@@ -945,7 +979,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
 #pragma unroll
     for (int t = 0; t < L; ++t)
         r2 += (double)rr[t] * (double)rr[t];
-    if (MG != MG_SWEEP && UPD != UPD_NONE && !first) {
+    if (!kSweepForm<MG> && UPD != UPD_NONE && !first) {
 #pragma unroll
         for (int t = 0; t < L; ++t)
             st_at(rout + row0 + (size_t)t * nx, cv, rr[t]);
@@ -1024,6 +1058,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
             zv = (TZ)mg.omega * zv;
         if constexpr (MG == MG_SWEEP)
             zv = zsw[t] + mg.omega * zv;
+        if constexpr (MG == MG_CHEB)
+            zv = cheb_update(mg, zsw[t], zo[t], zv);
         if constexpr (MG == MG_CORR || MG == MG_POST) {
             // MG_POST loads the iterate (plus the coarse correction) and f
             // here, after the solve: its load phase holds the coarse
@@ -1038,7 +1074,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_column_full(
                             (unsigned)(i / mg.fx) * 8u);
                 fv = partials ? ld_at(mg.f + row0 + (size_t)t * nx, cv) : 0.0;
             }
-            zv = zq + mg.omega * zv;
+            if (MG == MG_CORR && mg.cheb != 0)
+                zv = cheb_update(mg, zq, mg.cheb == 2 ? ld_at(z + row0 + (size_t)t * nx, cz) : 0.0, zv);
+            else
+                zv = zq + mg.omega * zv;
             kap += fv * zv;
             r2mg += fv * fv;
         } else {

@@ -72,6 +72,7 @@ struct pcg_handle {
     std::vector<int> mg_fx, mg_fy;
     int mg_nu = 0, mg_coarse_sweeps = 0;
     double mg_omega = 0.0;
+    double mg_coarse_lo = 0.0;        // > 0: Chebyshev-accelerated coarsest sweeps on [lo, 2]
 };
 
 namespace {
@@ -1316,9 +1317,9 @@ void launch_mg_column_narrow(pcg_handle *h, const double *rin, const double *q, 
                              const SolveState *st, double *partials, const MgArgs &a)
 {
     dim3 grid(h->col_tiles), block(h->col_threads);   // <= 16 C threads: P <= 16 (mg_coarse_columns)
-    constexpr int UPD = MG == MG_SWEEP ? UPD_AP : UPD_NONE;
+    constexpr int UPD = kSweepForm<MG> ? UPD_AP : UPD_NONE;
     k_column_solve<L, C, UPD, true, false, double, double, MG><<<grid, block, 0, h->stream>>>(
-        rin, q, rout, z, h->op, st, 0, MG == MG_SWEEP ? nullptr : partials, nullptr, h->d_phib, a);
+        rin, q, rout, z, h->op, st, 0, kSweepForm<MG> ? nullptr : partials, nullptr, h->d_phib, a);
 }
 
 // Multigrid forms of the column solve (64-column tiles, or the narrow tiles
@@ -1341,12 +1342,12 @@ void launch_mg_column_l(pcg_handle *h, const double *rin, const double *q, doubl
             return;
         }
     }
-    if constexpr (MG == MG_SWEEP) {
+    if constexpr (kSweepForm<MG>) {
         if (h->col_full)
-            k_column_full<L, UPD_AP, true, double, double, MG_SWEEP><<<grid, block, 0, h->stream>>>(
+            k_column_full<L, UPD_AP, true, double, double, MG><<<grid, block, 0, h->stream>>>(
                 rin, q, rout, z, o, st, 0, nullptr, h->d_phib, a);
         else
-            k_column_solve<L, kWave, UPD_AP, true, false, double, double, MG_SWEEP><<<grid, block, 0, h->stream>>>(
+            k_column_solve<L, kWave, UPD_AP, true, false, double, double, MG><<<grid, block, 0, h->stream>>>(
                 rin, q, rout, z, o, st, 0, nullptr, nullptr, h->d_phib, a);
     } else if (h->col_full) {
         if (fused_q)
@@ -1386,6 +1387,8 @@ void mg_column(pcg_handle *h, int mode, const double *rin, const double *q, doub
         launch_mg_column<MG_CORR>(h, rin, q, rout, z, st, first, partials, upd, a);
     else if (mode == MG_SWEEP)
         launch_mg_column<MG_SWEEP>(h, rin, q, rout, z, st, first, partials, upd, a);
+    else if (mode == MG_CHEB)
+        launch_mg_column<MG_CHEB>(h, rin, q, rout, z, st, first, partials, upd, a);
     else
         launch_mg_column<MG_POST>(h, rin, q, rout, z, st, first, partials, upd, a);
 }
@@ -1431,7 +1434,10 @@ void mg_restrict(pcg_handle *h, int fx, int fy, const double *f, const double *z
 //   correction    z' = (z + P z_c) + omega M^{-1} (t - A P z_c), one column
 //                 pass over the buffer of t
 // On the coarsest level: the exact column solve for one column, else
-// coarse_sweeps sweeps from z = 0.
+// coarse_sweeps sweeps from z = 0; with a lower end coarse_lo > 0 those
+// sweeps are the steps of the Chebyshev semi-iteration on [coarse_lo, 2]
+// (first z_1 = M^{-1} f / theta, then the three-term update, each step's
+// z_{k+1} written over z_{k-1}).
 void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const double *q, double *rout,
               int upd, const SolveState *st, int first, double *partials)
 {
@@ -1457,6 +1463,31 @@ void mg_cycle(pcg_handle *h0, const MgWork &mw, int l, const double *rin, const 
         const int cs = h0->mg_coarse_sweeps;
         double *cur = ((cs - 1) % 2 == 0) ? V : U;
         double *oth = (cur == V) ? U : V;
+        if (h0->mg_coarse_lo > 0.0) {
+            const double lo = h0->mg_coarse_lo, hi = 2.0;
+            const double theta = 0.5 * (hi + lo), delta = 0.5 * (hi - lo), s = theta / delta;
+            MgArgs a1 = a;
+            a1.omega = 1.0 / theta;
+            mg_column(h, MG_FIRST, rin, q, rout, cur, st, first, cs == 1 ? partials : nullptr, upd, a1);
+            double rho_prev = 1.0 / s;
+            for (int k = 1; k < cs; ++k) {
+                const double rho = 1.0 / (2.0 * s - rho_prev);
+                MgArgs ak = a;
+                ak.c1 = rho * rho_prev;
+                ak.c2 = 2.0 * rho / delta;
+                ak.cheb = k == 1 ? 1 : 2;
+                double *parts = k == cs - 1 ? partials : nullptr;
+                if (!parts && h->op.L <= 8) {
+                    mg_column(h, MG_CHEB, f, cur, nullptr, oth, st, 0, nullptr, UPD_AP, ak);
+                } else {
+                    stencil<double, double>(h, SP_RESID, cur, f, nullptr, nullptr, Wr, nullptr, nullptr);
+                    mg_column(h, MG_CORR, Wr, cur, nullptr, oth, st, 0, parts, UPD_NONE, ak);
+                }
+                std::swap(cur, oth);
+                rho_prev = rho;
+            }
+            return;
+        }
         mg_column(h, MG_FIRST, rin, q, rout, cur, st, first, cs == 1 ? partials : nullptr, upd, a);
         for (int sw = 1; sw < cs; ++sw) {
             sweep(cur, oth, sw == cs - 1 ? partials : nullptr);
@@ -1805,6 +1836,8 @@ int pcg_mg_setup(pcg_handle *h, const pcg_mg_params *p, void *levels, size_t lev
         return fail(h, PCG_ERR_INVALID, "%s: max_levels = %d must be in 0..64", who, p->max_levels);
     if (p->coarse_sweeps < 1 || p->coarse_sweeps > 1024)
         return fail(h, PCG_ERR_INVALID, "%s: coarse_sweeps = %d must be in 1..1024", who, p->coarse_sweeps);
+    if (!(p->coarse_lo >= 0.0 && p->coarse_lo < 2.0))
+        return fail(h, PCG_ERR_INVALID, "%s: coarse_lo = %g must be in [0, 2)", who, p->coarse_lo);
     if (h->op.C != kWave)
         return fail(h, PCG_ERR_UNSUPPORTED, "%s: the multigrid sweeps need 64-column column tiles", who);
     std::vector<int> fxs, fys;
@@ -1841,6 +1874,7 @@ int pcg_mg_setup(pcg_handle *h, const pcg_mg_params *p, void *levels, size_t lev
     h->mg_nu = p->nu;
     h->mg_omega = p->omega;
     h->mg_coarse_sweeps = p->coarse_sweeps;
+    h->mg_coarse_lo = p->coarse_lo;
     return PCG_OK;
 }
 

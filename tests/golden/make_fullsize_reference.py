@@ -5,8 +5,10 @@ for varying-1024x1024x128 on one core of this machine class).
 Stored: the step count and status, the whole residual history ||r_k||_2, the
 2-norm of the final iterate and its values at 4096 seeded positions (numpy
 default_rng(20261202) over the field's linear indices).  With the suffix m the
-solve is the multigrid-preconditioned one (general operator; the cycle
-parameters of the benchmark); with the suffix f it is the binary32 solve to
+solve is the multigrid-preconditioned one (general operator, damped coarsest
+sweeps: 64 on 64x64 columns); with the suffix c the same with the
+benchmark's Chebyshev-accelerated coarsest sweeps (16 on [0.02, 2]); with
+the suffix f it is the binary32 solve to
 tol 1e-5, and the script also stores the oracle's history for b perturbed at
 binary32's rounding level, (b (1 + 2^-23 u)) rounded to binary32 with u uniform in [-1, 1]
 (default_rng(4242)): the spread of two correct binary32 runs; with the suffix x it is the binary64 solve with the binary32 column solve
@@ -16,6 +18,7 @@ Calls only oracle/
 
     python tests/golden/make_fullsize_reference.py 4      # varying-1024x1024x128
     python tests/golden/make_fullsize_reference.py 6m     # general-1024x1024x128, multigrid
+    python tests/golden/make_fullsize_reference.py 6c     # the same, Chebyshev coarsest sweeps
     python tests/golden/make_fullsize_reference.py 4f     # varying-1024x1024x128, binary32
     python tests/golden/make_fullsize_reference.py 4x     # varying-1024x1024x128, mixed
     python tests/golden/make_fullsize_reference.py 5      # csr-vs-mf-2048x2048x128: its 50 fixed
@@ -42,8 +45,10 @@ def sample_indices(n: int) -> np.ndarray:
     return np.sort(np.random.default_rng(SAMPLE_SEED).choice(n, size=SAMPLES, replace=False))
 
 
-# the multigrid-preconditioned solve with the benchmark's cycle parameters
+# the multigrid-preconditioned solve: damped coarsest sweeps, and the
+# benchmark's Chebyshev-accelerated ones
 MG_PARAMS = dict(nu=1, omega=0.9, max_levels=5, coarse_sweeps=64)
+MG_CHEB_PARAMS = dict(nu=1, omega=0.9, max_levels=5, coarse_sweeps=16, coarse_lo=0.02)
 
 
 # the binary32 solve: the right-hand side rounded to binary32, the benchmark's
@@ -64,7 +69,9 @@ def _f32_solves(p, b, maxit):
         return f0.result(), f1.result()
 
 
-def main(cfg: int, mg: bool = False, f32: bool = False, mixed: bool = False, out_dir: str = HERE) -> str:
+def main(cfg: int, mg: bool = False, f32: bool = False, mixed: bool = False, out_dir: str = HERE,
+         cheb: bool = False) -> str:
+    mgp = MG_CHEB_PARAMS if cheb else MG_PARAMS
     w = W.make_workload(cfg)
     p = w.problem
     t = time.time()
@@ -73,7 +80,7 @@ def main(cfg: int, mg: bool = False, f32: bool = False, mixed: bool = False, out
     elif mixed:
         ref = oracle.pcg_mixed(p, w.rhs, tol=w.tol, maxit=w.maxit)
     elif mg:
-        ref = oracle.pcg_mg(p, w.rhs, tol=w.tol, maxit=w.maxit, **MG_PARAMS)
+        ref = oracle.pcg_mg(p, w.rhs, tol=w.tol, maxit=w.maxit, **mgp)
     elif isinstance(p, W.GeneralProblem):
         ref = oracle.pcg_gen(p, w.rhs, tol=w.tol, maxit=w.maxit)
     else:
@@ -90,11 +97,11 @@ def main(cfg: int, mg: bool = False, f32: bool = False, mixed: bool = False, out
         "oracle_seconds": round(time.time() - t, 1),
     }
     if mg:
-        out["mg"] = MG_PARAMS
+        out["mg"] = mgp
     if f32:
         out["spread_seed"] = SPREAD_SEED
         out["hist_spread"] = [float(v) for v in spread["hist"]]
-    suffix = "_mg" if mg else ("_f32" if f32 else ("_mixed" if mixed else ""))
+    suffix = ("_mg_cheb" if cheb else "_mg") if mg else ("_f32" if f32 else ("_mixed" if mixed else ""))
     path = os.path.join(out_dir, f"fullsize_{w.name}{suffix}.json")
     with open(path, "w") as f:
         json.dump(out, f)
@@ -109,5 +116,5 @@ if __name__ == "__main__":
         out_dir = args[i + 1]
         del args[i:i + 2]
     for a in args or ["4"]:
-        print(main(int(a.rstrip("mfx")), mg=a.endswith("m"), f32=a.endswith("f"), mixed=a.endswith("x"),
-                   out_dir=out_dir), flush=True)
+        print(main(int(a.rstrip("mfxc")), mg=a.endswith("m") or a.endswith("c"), f32=a.endswith("f"),
+                   mixed=a.endswith("x"), out_dir=out_dir, cheb=a.endswith("c")), flush=True)

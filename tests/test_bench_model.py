@@ -80,6 +80,12 @@ def test_mg_cycle_bytes_with_coarse_sweeps():
     base = bench.mg_cycle_bytes(pts, 1)              # coarsest treated as one exact solve
     assert bench.mg_cycle_bytes(pts, 1, coarse_sweeps=64) - base == 24 * 63 * pts[-1]
     assert bench.mg_cycle_bytes(pts, 1, coarse_sweeps=64, two_pass_sweeps=True) - base == 48 * 63 * pts[-1]
+    # Chebyshev steps: the first like a damped sweep, every later one also
+    # reads z_{k-1}
+    assert bench.mg_cycle_bytes(pts, 1, coarse_sweeps=16, chebyshev=True) - base == (24 + 32 * 14) * pts[-1]
+    assert bench.mg_cycle_bytes(pts, 1, coarse_sweeps=16, two_pass_sweeps=True, chebyshev=True) - base == \
+        (48 + 56 * 14) * pts[-1]
+    assert bench.mg_cycle_bytes(pts, 1, coarse_sweeps=1, chebyshev=True) == bench.mg_cycle_bytes(pts, 1, coarse_sweeps=1)
 
 
 def test_sampled_profiling_steps():

@@ -345,15 +345,18 @@ def test_full_solve_against_oracle_reference(dev, cfg4, cfg, solver):
     assert rel_norm <= 1e-9
 
 
-def test_mg_full_solve_against_oracle_reference(dev):
-    """The multigrid-preconditioned solve of general-1024x1024x128 with the
-    benchmark's cycle against the oracle's complete multigrid solve, stored
-    by tests/golden/make_fullsize_reference.py: step counts within 1, the
-    residual histories within 1e-6 relative while ||r_k|| >= 1e-6 ||r_0||,
-    the final iterate within rel-L2 1e-9 on 4096 seeded positions and its
-    2-norm within 1e-9 (the bars of the smaller multigrid solve tests)."""
+@pytest.mark.parametrize("suffix", ["_mg", "_mg_cheb"], ids=["damped-coarsest", "chebyshev-coarsest"])
+def test_mg_full_solve_against_oracle_reference(dev, suffix):
+    """The multigrid-preconditioned solve of general-1024x1024x128 against
+    the oracle's complete multigrid solve, stored by
+    tests/golden/make_fullsize_reference.py with the cycle parameters it
+    records (64 damped coarsest sweeps; the benchmark's 16 Chebyshev-
+    accelerated ones): step counts within 1, the residual histories within
+    1e-6 relative while ||r_k|| >= 1e-6 ||r_0||, the final iterate within
+    rel-L2 1e-9 on 4096 seeded positions and its 2-norm within 1e-9 (the bars
+    of the smaller multigrid solve tests)."""
     import torch
-    ref = _reference(W.CONFIG_NAMES[6] + "_mg")
+    ref = _reference(W.CONFIG_NAMES[6] + suffix)
     w = W.make_workload(6)
     assert ref["workload"] == w.name and ref["status"] == 0
     h = mf.pcg_create(w.problem)

@@ -1,7 +1,7 @@
 """GPU parity of the tensor-product multigrid preconditioner (horizontal
 Galerkin coarsening with piecewise-constant transfers, damped column-block
-smoother, V(nu, nu) cycle) against the oracle's multigrid functions (pinned by
-M1-M5).
+smoother, V(nu, nu) cycle, damped or Chebyshev-accelerated coarsest sweeps)
+against the oracle's multigrid functions (pinned by M1-M7).
 
 Tolerances:
   * coarse coefficients: bit-exact (both sides sum the same binary64 values
@@ -81,7 +81,19 @@ PARAMS = [
     dict(nu=1, omega=0.8, max_levels=0, coarse_sweeps=2),
     dict(nu=2, omega=0.7, max_levels=3, coarse_sweeps=3),
     dict(nu=1, omega=1.0, max_levels=2, coarse_sweeps=1),
+    # Chebyshev-accelerated coarsest sweeps on [coarse_lo, 2]: a three-level
+    # hierarchy, the grid alone (every step of the solve is the Chebyshev
+    # iteration, its last step forming the dot products) and nu = 2
+    dict(nu=1, omega=0.9, max_levels=3, coarse_sweeps=8, coarse_lo=0.02),
+    dict(nu=1, omega=0.9, max_levels=1, coarse_sweeps=6, coarse_lo=0.1),
+    dict(nu=2, omega=0.8, max_levels=2, coarse_sweeps=16, coarse_lo=0.02),
 ]
+
+
+def _pid(i):
+    p = PARAMS[i]
+    tag = "nu{nu}-w{omega}-L{max_levels}-cs{coarse_sweeps}".format(**p)
+    return tag + (f"-lo{p['coarse_lo']}" if p.get("coarse_lo") else "")
 
 
 @pytest.mark.parametrize("label,make", GRIDS, ids=[g[0] for g in GRIDS])
@@ -115,7 +127,7 @@ def test_mg_levels_match_oracle(dev, label, make):
     assert cur.nx * cur.ny == 1 or oracle.mg_coarsen(cur) is None, label
 
 
-@pytest.mark.parametrize("pi", range(len(PARAMS)), ids=lambda i: "nu{nu}-w{omega}-L{max_levels}-cs{coarse_sweeps}".format(**PARAMS[i]))
+@pytest.mark.parametrize("pi", range(len(PARAMS)), ids=_pid)
 @pytest.mark.parametrize("label,make", GRIDS, ids=[g[0] for g in GRIDS])
 def test_vcycle_matches_oracle(dev, label, make, pi):
     import torch
@@ -200,7 +212,7 @@ SOLVES = [
 ]
 
 
-@pytest.mark.parametrize("pi", [0, 1], ids=["default", "nu2-L3"])
+@pytest.mark.parametrize("pi", [0, 1, 3, 4], ids=["default", "nu2-L3", "cheb-L3", "cheb-L1"])
 @pytest.mark.parametrize("label,make,seed", SOLVES, ids=[c[0] for c in SOLVES])
 def test_solve_mg_matches_oracle(dev, label, make, seed, pi):
     import torch
@@ -245,7 +257,8 @@ def test_mg_setup_rejects_and_requires(dev):
         xd = torch.zeros_like(bd)
         with pytest.raises(mf.PcgError):
             mf.pcg_solve_mg(h, bd, xd, 1e-8, 10, workspace=torch.empty(1 << 20, dtype=torch.uint8, device=dev))
-        for bad in (dict(nu=0), dict(omega=0.0), dict(omega=1.5), dict(max_levels=-1), dict(coarse_sweeps=0)):
+        for bad in (dict(nu=0), dict(omega=0.0), dict(omega=1.5), dict(max_levels=-1), dict(coarse_sweeps=0),
+                    dict(coarse_lo=-0.1), dict(coarse_lo=2.0), dict(coarse_lo=float("nan"))):
             with pytest.raises(mf.PcgError) as e:
                 mf.pcg_mg_setup(h, **bad)
             assert e.value.code == mf.PCG_ERR_INVALID
