@@ -524,7 +524,10 @@ void launch_stencil_jt(pcg_handle *h, const Op &o, int mode, const TI *zin, cons
         default: break;
         }
     }
-    if constexpr (Ls == 8 && JT == 4 && kBinary64<TV, TI>) {   // the binary64 pass that defers x
+    // the pass that defers x with 8 levels per wave: binary64 on 4 rows,
+    // binary32 on 4 or 8
+    if constexpr (Ls == 8 && ((JT == 4 && kBinary64<TV, TI>) ||
+                              (std::is_same<TV, float>::value && kSame && (JT == 4 || JT == 8)))) {
         if (mode == SP_FUSED_NOX)
             k_stencil<Ls, SP_FUSED_NOX, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older);
     }
@@ -572,8 +575,10 @@ int op_rows_jt(const pcg_handle *h)
 }
 
 // Row-tile shape of a fused pass: levels per wave and rows (0 rows: one-row
-// tiles).  In binary64 the odd-step pass takes 8 levels per wave (4 x 8
-// tiles: 0.5 % faster than 4 x 4; in the mixed solve 1.8 % slower).
+// tiles).  The pass that defers x takes 8 levels per wave in binary64 (4 x 8
+// tiles: 0.5 % faster than 4 x 4; in the mixed solve 1.8 % slower) and in
+// binary32 (8 x 8 tiles: the binary32 solve 1.8 % faster than with 8 x 4;
+// 8 levels on 4 rows gain 0.3 %).
 struct RowShape {
     int Ls, jt;
 };
@@ -584,6 +589,8 @@ RowShape fused_shape(const pcg_handle *h, int mode, bool binary64, bool binary32
         return {4, 0};
     if (binary64 && jt == 4 && mode == SP_FUSED_NOX)
         return {8, 4};
+    if (binary32 && (jt == 4 || jt == 8) && mode == SP_FUSED_NOX)
+        return {8, jt};
     return {4, jt};
 }
 
@@ -616,7 +623,9 @@ void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, 
             o2.jt = rs.jt;
             o2.Ws = rs.jt;
             o2.nkt = h->op.nz / rs.Ls;
-            if (rs.Ls == 8)
+            if (rs.Ls == 8 && rs.jt == 8)
+                launch_stencil_jt<8, 8>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
+            else if (rs.Ls == 8)
                 launch_stencil_jt<8, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
             else if (rs.jt == 8)
                 launch_stencil_jt<4, 8>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
