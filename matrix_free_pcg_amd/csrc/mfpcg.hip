@@ -524,9 +524,8 @@ void launch_stencil_jt(pcg_handle *h, const Op &o, int mode, const TI *zin, cons
         default: break;
         }
     }
-    // the pass that defers x with 8 levels per wave: binary64 on 4 rows,
-    // binary32 on 4 or 8
-    if constexpr (Ls == 8 && ((JT == 4 && kBinary64<TV, TI>) ||
+    // the pass that defers x with 8 levels per wave, on 4 or 8 rows
+    if constexpr (Ls == 8 && (((JT == 4 || JT == 8) && kBinary64<TV, TI>) ||
                               (std::is_same<TV, float>::value && kSame && (JT == 4 || JT == 8)))) {
         if (mode == SP_FUSED_NOX)
             k_stencil<Ls, SP_FUSED_NOX, true, TV, TI, JT><<<grid, block, 0, h->stream>>>(zin, b, u, p, y, o, st, partials, p_out, older);
@@ -576,7 +575,9 @@ int op_rows_jt(const pcg_handle *h)
 
 // Row-tile shape of a fused pass: levels per wave and rows (0 rows: one-row
 // tiles).  The pass that defers x takes 8 levels per wave in binary64 (4 x 8
-// tiles: 0.5 % faster than 4 x 4; in the mixed solve 1.8 % slower) and in
+// tiles: 0.5 % faster than 4 x 4; in the mixed solve 1.8 % slower; on 8 rows
+// where ny allows and no row count is forced, the binary64 solve another
+// 0.5 % faster, while 8 rows for the fourth-step form cost 0.8 %) and in
 // binary32 (8 x 8 tiles: the binary32 solve 1.8 % faster than with 8 x 4;
 // 8 levels on 4 rows gain 0.3 %).
 struct RowShape {
@@ -588,7 +589,7 @@ RowShape fused_shape(const pcg_handle *h, int mode, bool binary64, bool binary32
     if (!jt)
         return {4, 0};
     if (binary64 && jt == 4 && mode == SP_FUSED_NOX)
-        return {8, 4};
+        return {8, (!h->st_jt && h->op.ny % 8 == 0) ? 8 : 4};
     if (binary32 && (jt == 4 || jt == 8) && mode == SP_FUSED_NOX)
         return {8, jt};
     return {4, jt};
