@@ -564,13 +564,13 @@ int fused_rows_jt(const pcg_handle *h, bool binary32)
 // Rows per tile of the operator-only passes (SP_APPLY, SP_APPLY_DOT,
 // SP_RESID; 8 levels per wave) on this handle, 0 when they take one-row
 // tiles.  y = A x at 1024 x 1024 x 128: one row 0.541 ms, 2 rows 0.471 ms,
-// 4 rows 0.439 ms.
+// 4 rows 0.439 ms (later 0.407), 8 rows 0.394 ms.
 int op_rows_jt(const pcg_handle *h)
 {
     const Op &o = h->op;
     if (h->st_jt == 1 || !h->pt_full || o.Ls != 4 || o.Ws != 4)
         return 0;
-    return o.ny % 4 == 0 ? 4 : (o.ny % 2 == 0 ? 2 : 0);
+    return o.ny % 8 == 0 ? 8 : (o.ny % 4 == 0 ? 4 : (o.ny % 2 == 0 ? 2 : 0));
 }
 
 // Row-tile shape of a fused pass: levels per wave and rows (0 rows: one-row
@@ -603,8 +603,8 @@ int stencil_tiles(const pcg_handle *h, int mode, bool binary64, bool binary32)
         if (rs.jt)
             return (int)((size_t)h->op.ntx * (h->op.nz / rs.Ls) * (h->op.ny / rs.jt));
     }
-    if (mode == SP_APPLY_DOT && op_rows_jt(h) == 4)
-        return (int)((size_t)h->op.ntx * (h->op.nz / 8) * (h->op.ny / 4));
+    if (mode == SP_APPLY_DOT && op_rows_jt(h) >= 4)
+        return (int)((size_t)h->op.ntx * (h->op.nz / 8) * (h->op.ny / op_rows_jt(h)));
     return h->pt_tiles;
 }
 
@@ -641,7 +641,9 @@ void launch_stencil(pcg_handle *h, int mode, const TI *zin, const TV *b, TV *u, 
             o2.Ws = ojt;
             o2.jt = ojt;
             o2.nkt = h->op.nz / 8;
-            if (ojt == 4)
+            if (ojt == 8)
+                launch_stencil_jt<8, 8>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
+            else if (ojt == 4)
                 launch_stencil_jt<8, 4>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
             else
                 launch_stencil_jt<8, 2>(h, o2, mode, zin, b, u, p, y, st, partials, p_out, older);
