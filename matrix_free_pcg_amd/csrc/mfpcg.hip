@@ -1382,6 +1382,22 @@ template <int MG>
 void launch_mg_column(pcg_handle *h, const double *rin, const double *q, double *rout, double *z,
                       const SolveState *st, int first, double *partials, int upd, const MgArgs &a)
 {
+    if constexpr (MG == MG_FIRST) {
+        // The first sweep holds no operands beyond r (and q): on a level whose
+        // column passes take longer segments than its table (the finest), it
+        // takes them too, as the PCG's own column pass does.
+        if (h->colf_L == 16 && h->colf_L != h->op.L && h->colf_full) {
+            const ColGeo g = col_geo(h, false);
+            dim3 grid(h->col_tiles), block(g.threads);
+            if (upd == UPD_Q)
+                k_column_full<16, UPD_Q, true, double, double, MG_FIRST><<<grid, block, 0, h->stream>>>(
+                    rin, q, rout, z, g.o, st, first, partials, h->d_phib, a);
+            else
+                k_column_full<16, UPD_NONE, true, double, double, MG_FIRST><<<grid, block, 0, h->stream>>>(
+                    rin, q, rout, z, g.o, st, first, partials, h->d_phib, a);
+            return;
+        }
+    }
     switch (h->op.L) {
     case 4: launch_mg_column_l<MG, 4>(h, rin, q, rout, z, st, first, partials, upd, a); break;
     case 8: launch_mg_column_l<MG, 8>(h, rin, q, rout, z, st, first, partials, upd, a); break;
