@@ -158,6 +158,49 @@ def test_vcycle_matches_oracle(dev, label, make, pi):
 
 
 
+
+def test_first_sweep_segments_agree(dev, monkeypatch):
+    """On the finest level the first sweep takes the 16-level segments of the
+    column passes (nz = 128 over the 8-level multiplier table); with
+    MFPCG_COL_LF=8 (read at pcg_create) it takes the table's 8-level ones.
+    The same elimination either way: a V-cycle (first sweep without q) and 5
+    steps of the multigrid solve (first sweep with r -= alpha q) agree to
+    rounding."""
+    import torch
+    prob = W.general_problem(128, 64, 128, 8)
+    mg = dict(nu=1, omega=0.9, max_levels=3, coarse_sweeps=8, coarse_lo=0.02)
+    r = W.gaussian_field(prob.nx, prob.ny, prob.nz, 305)
+    b = W.uniform_field(prob.nx, prob.ny, prob.nz, 306)
+
+    def run(lf):
+        if lf is None:
+            monkeypatch.delenv("MFPCG_COL_LF", raising=False)
+        else:
+            monkeypatch.setenv("MFPCG_COL_LF", lf)
+        h = mf.pcg_create(prob)
+        try:
+            mf.pcg_mg_setup(h, **mg)
+            rd = to_dev(r, dev)
+            zd = torch.full_like(rd, float("nan"))
+            mf.pcg_mg_vcycle(h, rd, zd)
+            bd = to_dev(b, dev)
+            xd = torch.zeros_like(bd)
+            res = mf.pcg_solve_mg(h, bd, xd, 0.0, 5)
+            torch.cuda.synchronize()
+            return to_host(zd), to_host(xd), np.asarray(res["hist"]), mf.pcg_tuning_overrides(h)
+        finally:
+            mf.pcg_destroy(h)
+            monkeypatch.delenv("MFPCG_COL_LF", raising=False)
+
+    z16, x16, h16, ov16 = run(None)
+    z8, x8, h8, ov8 = run("8")
+    assert ov16 == 0 and ov8 & 0x004, (ov16, ov8)
+    dz = np.abs(z16 - z8).max() / np.abs(z8).max()
+    print(f"first sweep 16 vs 8 levels: V-cycle {dz:.2e}, histories {np.abs(h16 / h8 - 1).max():.2e}")
+    assert np.isfinite(z16).all() and dz <= 1e-11, dz
+    assert np.allclose(h16, h8, rtol=1e-11, atol=0)
+    assert np.linalg.norm(x16 - x8) <= 1e-11 * np.linalg.norm(x8)
+
 @pytest.mark.parametrize("width", ["16", "32", "64", "48"])
 def test_coarsest_tile_width(dev, monkeypatch, width):
     """The coarsest level's tile width (MFPCG_MG_COARSE_C, read by
